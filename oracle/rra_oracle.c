@@ -1,0 +1,649 @@
+/*
+ * CPU oracle for the fused residual-add/RMSNorm/SiLU/RoPE/quant path.
+ *
+ * TEST INFRASTRUCTURE ONLY: the plain definition the HIP library is checked
+ * against.  Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg load it.  It shares nothing with rope_residual_add_amd/.
+ *
+ * Page abbreviations used in the citations below:
+ *   [FUSION]  vLLM design page "Fusion torch.compile passes"
+ *   [TUNING]  blog "Making vLLM fast: configuration, internals, and the places
+ *             worth touching code", section "PagedAttention"
+ *   [OFP8]    OCP 8-bit Floating Point Specification, E4M3 format
+ *
+ * Readings taken where the pages are silent are stated at each function.
+ */
+#include "rra_oracle.h"
+
+#include <fenv.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ======================================================================= */
+/* Codecs                                                                   */
+/* ======================================================================= */
+
+/* bf16: 1 sign, 8 exponent (bias 127), 7 fraction bits; the upper half of an
+ * IEEE binary32.  Largest finite value (2 - 2^-7) * 2^127. */
+static const double kBf16Max = 3.3895313892515355e38;
+
+/* Round a double to the nearest bf16, ties to even, overflow to infinity
+ * (IEEE round-to-nearest-even semantics), NaN to a quiet NaN of the same sign.
+ * Method: the representable neighbours of |v| are integer multiples of the
+ * quantum 2^(E-7) of |v|'s binade E (clamped to the smallest normal binade,
+ * which subnormals share); nearbyint() in the default rounding mode rounds
+ * half to even. */
+uint16_t orc_bf16_encode(double v) {
+  const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+  double a = fabs(v);
+  if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e); /* a in [2^(e-1), 2^e) */
+  int E = e - 1;
+  if (E < -126) E = -126;
+  const double quantum = ldexp(1.0, E - 7);
+  const double n = nearbyint(a / quantum);
+  const double r = n * quantum;
+  if (r > kBf16Max) return (uint16_t)(sign | 0x7F80u);
+  const float f = (float)r; /* exact: r is a bf16 value */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | (uint16_t)(u >> 16));
+}
+
+double orc_bf16_decode(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+float orc_fp32_round(double v) { return (float)v; /* RNE in FE_TONEAREST */ }
+
+/* [OFP8] E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits.
+ * Exponent field 0 encodes subnormals m * 2^-9; S.1111.111 is NaN; there is
+ * no infinity, so S.1111.110 = 448 is the largest finite magnitude. */
+double orc_e4m3fn_decode(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 0xF, m = c & 0x7;
+  double mag;
+  if (e == 0xF && m == 0x7) return s ? -NAN : NAN;
+  if (e == 0)
+    mag = ldexp((double)m, -9);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+/* The 127 non-negative finite E4M3 values, indexed by code 0x00..0x7E, in
+ * increasing order (the encoding is monotonic in the code). */
+static double g_e4m3_values[127];
+
+__attribute__((constructor)) static void build_e4m3_table(void) {
+  for (int c = 0; c < 127; ++c) g_e4m3_values[c] = orc_e4m3fn_decode((uint8_t)c);
+}
+
+/* Encode to E4M3 by search over the decoded value table: the nearest finite
+ * value, ties to the even code (the code's last bit is the mantissa's last
+ * bit), magnitudes at or above 448 saturate to 448 (reading: the quantizer
+ * saturates rather than producing NaN), NaN maps to S.1111.111, and the sign
+ * of zero is kept. */
+uint8_t orc_e4m3fn_encode(double v) {
+  const uint8_t sign = signbit(v) ? 0x80u : 0u;
+  if (isnan(v)) return (uint8_t)(sign | 0x7Fu);
+  const double a = fabs(v);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);
+  int lo = 0, hi = 126; /* invariant: table[lo] <= a < table[hi] */
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (g_e4m3_values[mid] <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  if (a == g_e4m3_values[lo]) return (uint8_t)(sign | lo);
+  const double midpoint = 0.5 * (g_e4m3_values[lo] + g_e4m3_values[hi]); /* exact */
+  int k;
+  if (a < midpoint)
+    k = lo;
+  else if (a > midpoint)
+    k = hi;
+  else
+    k = (lo % 2 == 0) ? lo : hi;
+  return (uint8_t)(sign | k);
+}
+
+/* A second E4M3 encoder built a different way, used only to cross-check the
+ * first: scale |v| by the quantum of its binade (2^(E-3), or 2^-9 below the
+ * smallest normal binade 2^-6), round half to even with nearbyint(), clamp to
+ * 448, then assemble the bit fields from frexp(). */
+uint8_t orc_e4m3fn_encode_arith(double v) {
+  const uint8_t sign = signbit(v) ? 0x80u : 0u;
+  if (isnan(v)) return (uint8_t)(sign | 0x7Fu);
+  double a = fabs(v);
+  if (isinf(a)) return (uint8_t)(sign | 0x7Eu);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);
+  int E = e - 1;
+  if (E < -6) E = -6;
+  const double q = ldexp(1.0, E - 3);
+  double r = nearbyint(a / q) * q;
+  if (r > 448.0) r = 448.0;
+  if (r < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)(r * 512.0)); /* m * 2^-9 */
+  int e2;
+  const double f = frexp(r, &e2); /* r = f * 2^e2, f in [0.5, 1) */
+  const int biased = (e2 - 1) + 7;
+  const int m = (int)((2.0 * f - 1.0) * 8.0);
+  return (uint8_t)(sign | (biased << 3) | m);
+}
+
+void orc_bf16_encode_f32_array(const float* in, uint16_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_encode((double)in[i]);
+}
+
+void orc_e4m3fn_encode_f32_array(const float* in, uint8_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3fn_encode((double)in[i]);
+}
+
+void orc_e4m3fn_decode_array(const uint8_t* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3fn_decode(in[i]);
+}
+
+int64_t orc_e4m3fn_cross_check(uint64_t begin, uint64_t end) {
+  int64_t bad = 0;
+  const int64_t b = (int64_t)begin, n = (int64_t)end;
+#pragma omp parallel for reduction(+ : bad) schedule(static)
+  for (int64_t i = b; i < n; ++i) {
+    const uint32_t u = (uint32_t)i;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    if (orc_e4m3fn_encode((double)f) != orc_e4m3fn_encode_arith((double)f)) ++bad;
+  }
+  return bad;
+}
+
+/* ======================================================================= */
+/* Threading                                                                */
+/* ======================================================================= */
+
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int orc_get_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ======================================================================= */
+/* Row building blocks                                                      */
+/* ======================================================================= */
+
+static int quant_args_ok(int mode, int group_size, int64_t H, int allow_none) {
+  switch (mode) {
+    case ORC_Q_NONE:
+      return allow_none;
+    case ORC_Q_STATIC:
+    case ORC_Q_PER_TOKEN:
+      return 1;
+    case ORC_Q_PER_GROUP:
+      return group_size > 0 && H % group_size == 0;
+    default:
+      return 0;
+  }
+}
+
+/* RMSNorm of one row.  The pages name the op (rms_norm) without a formula;
+ * the reading is the usual one: y_j = z_j / sqrt(mean_j(z_j^2) + eps) * w_j,
+ * with eps inside the root and a multiplicative weight.
+ * [FUSION] sections "RMSNorm + Quantization" and "MLA Dual RMSNorm". */
+static void rms_norm_row(const double* z, const uint16_t* w, float eps, int64_t H, double* y) {
+  double ss = 0.0;
+  for (int64_t j = 0; j < H; ++j) ss += z[j] * z[j];
+  const double rho = 1.0 / sqrt(ss / (double)H + (double)eps);
+  for (int64_t j = 0; j < H; ++j) y[j] = z[j] * rho * orc_bf16_decode(w[j]);
+}
+
+/* One scale from an amax: s = amax / 448 rounded to fp32 (448 is E4M3's
+ * largest finite value).  Reading: no floor and no cap, so an all-zero slice
+ * gets s = 0. */
+static float dynamic_scale(double amax) { return orc_fp32_round(amax / 448.0); }
+
+/* Code of one value for a stored fp32 scale s.  Reading: quantize with the
+ * stored scale so that dequantization is decode(code) * s; s = 0 (all-zero
+ * slice) gives +0 codes. */
+static uint8_t quant_one(double y, float s) {
+  if (s == 0.0f) return 0;
+  return orc_e4m3fn_encode(y / (double)s);
+}
+
+/* FP8 quantization of one row y[0..H).  Static: the given per-tensor scale;
+ * per-token: one dynamic scale per row; per-group: one dynamic scale per
+ * contiguous slice of group_size elements, scales laid out [row, H/g].
+ * [FUSION] sections "RMSNorm + Quantization" (static per-tensor, dynamic
+ * per-token, dynamic per-token-group 128/64) and "SiLU+Mul + Quantization". */
+static void quant_row(const double* y, int64_t H, int mode, int group_size, float static_scale,
+                      uint8_t* out, float* scales_row) {
+  if (mode == ORC_Q_STATIC) {
+    for (int64_t j = 0; j < H; ++j) out[j] = quant_one(y[j], static_scale);
+  } else if (mode == ORC_Q_PER_TOKEN) {
+    double amax = 0.0;
+    for (int64_t j = 0; j < H; ++j) amax = fmax(amax, fabs(y[j]));
+    const float s = dynamic_scale(amax);
+    scales_row[0] = s;
+    for (int64_t j = 0; j < H; ++j) out[j] = quant_one(y[j], s);
+  } else { /* ORC_Q_PER_GROUP */
+    for (int64_t g0 = 0, k = 0; g0 < H; g0 += group_size, ++k) {
+      double amax = 0.0;
+      for (int64_t j = g0; j < g0 + group_size; ++j) amax = fmax(amax, fabs(y[j]));
+      const float s = dynamic_scale(amax);
+      scales_row[k] = s;
+      for (int64_t j = g0; j < g0 + group_size; ++j) out[j] = quant_one(y[j], s);
+    }
+  }
+}
+
+static float* scales_row_ptr(float* scales, int mode, int group_size, int64_t H, int64_t t) {
+  if (mode == ORC_Q_PER_TOKEN) return scales + t;
+  if (mode == ORC_Q_PER_GROUP) return scales + t * (H / group_size);
+  return NULL;
+}
+
+static int static_scale_ok(int mode, float s) {
+  return mode != ORC_Q_STATIC || (isfinite(s) && s > 0.0f);
+}
+
+/* ======================================================================= */
+/* Residual add + RMSNorm + FP8 quant                                       */
+/* ======================================================================= */
+
+/* Fused-add RMSNorm followed by FP8 quantization, one pass, no intermediate
+ * tensor; the residual is overwritten with the sum.
+ * [FUSION] section "RMSNorm + Quantization (fuse_norm_quant)": the two fused
+ * variants are rms_norm(x) -> quant and fused_add_rms_norm(x, residual) ->
+ * quant with the residual updated in place.
+ * Readings: z = bf16(x + residual) is both the stored residual and the norm
+ * input; y is never rounded before the single FP8 rounding. */
+int orc_fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint16_t* residual,
+                                int64_t res_stride, const uint16_t* weight, float eps,
+                                int quant_mode, int group_size, float static_scale,
+                                uint8_t* out, int64_t out_stride, float* scales, int64_t T,
+                                int64_t H) {
+  if (T < 0 || H <= 0 || !quant_args_ok(quant_mode, group_size, H, 0)) return ORC_EARG;
+  if (!static_scale_ok(quant_mode, static_scale)) return ORC_ECONTRACT;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* z = (double*)malloc((size_t)H * sizeof(double));
+    double* y = (double*)malloc((size_t)H * sizeof(double));
+    for (int64_t j = 0; j < H; ++j) {
+      const double xv = orc_bf16_decode(x[t * x_stride + j]);
+      if (residual) {
+        /* the sum of two bf16 values is exact in double */
+        const uint16_t zb = orc_bf16_encode(xv + orc_bf16_decode(residual[t * res_stride + j]));
+        residual[t * res_stride + j] = zb;
+        z[j] = orc_bf16_decode(zb);
+      } else {
+        z[j] = xv;
+      }
+    }
+    rms_norm_row(z, weight, eps, H, y);
+    quant_row(y, H, quant_mode, group_size, static_scale, out + t * out_stride,
+              scales_row_ptr(scales, quant_mode, group_size, H, t));
+    free(z);
+    free(y);
+  }
+  return ORC_OK;
+}
+
+/* The unfused composition the fusion replaces: fused_add_rms_norm writes the
+ * residual and a bf16 normalized tensor, then a separate quant op reads that
+ * bf16 tensor and derives its scale from it.  [FUSION] section "RMSNorm +
+ * Quantization". */
+int orc_unfused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint16_t* residual,
+                                  int64_t res_stride, const uint16_t* weight, float eps,
+                                  int quant_mode, int group_size, float static_scale,
+                                  uint8_t* out, int64_t out_stride, float* scales, int64_t T,
+                                  int64_t H) {
+  if (T < 0 || H <= 0 || !quant_args_ok(quant_mode, group_size, H, 0)) return ORC_EARG;
+  if (!static_scale_ok(quant_mode, static_scale)) return ORC_ECONTRACT;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* z = (double*)malloc((size_t)H * sizeof(double));
+    double* y = (double*)malloc((size_t)H * sizeof(double));
+    /* step 1: the residual add, stored */
+    for (int64_t j = 0; j < H; ++j) {
+      double v = orc_bf16_decode(x[t * x_stride + j]);
+      if (residual) {
+        const uint16_t zb = orc_bf16_encode(v + orc_bf16_decode(residual[t * res_stride + j]));
+        residual[t * res_stride + j] = zb;
+        v = orc_bf16_decode(zb);
+      }
+      z[j] = v;
+    }
+    /* step 2: rms_norm materializes a bf16 tensor */
+    rms_norm_row(z, weight, eps, H, y);
+    for (int64_t j = 0; j < H; ++j) y[j] = orc_bf16_decode(orc_bf16_encode(y[j]));
+    /* step 3: quant_fp8 of that tensor */
+    quant_row(y, H, quant_mode, group_size, static_scale, out + t * out_stride,
+              scales_row_ptr(scales, quant_mode, group_size, H, t));
+    free(z);
+    free(y);
+  }
+  return ORC_OK;
+}
+
+/* ======================================================================= */
+/* SiLU-and-Mul + FP8 quant                                                 */
+/* ======================================================================= */
+
+/* silu(g) * u in double.  Reading: silu(x) = x * sigmoid(x) = x / (1 + e^-x);
+ * the gate is the first half of the gate-up projection row and up the second.
+ * [FUSION] section "SiLU+Mul + Quantization (fuse_act_quant)". */
+static double silu_mul(double g, double u) { return g / (1.0 + exp(-g)) * u; }
+
+/* silu_and_mul followed by FP8 quantization without materializing the
+ * activation.  [FUSION] section "SiLU+Mul + Quantization": static per-tensor
+ * and dynamic per-group (128/64) variants. */
+int orc_silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_mode, int group_size,
+                       float static_scale, uint8_t* out, int64_t out_stride, float* scales,
+                       int64_t T, int64_t I) {
+  if (T < 0 || I <= 0 || !quant_args_ok(quant_mode, group_size, I, 0)) return ORC_EARG;
+  if (!static_scale_ok(quant_mode, static_scale)) return ORC_ECONTRACT;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* a = (double*)malloc((size_t)I * sizeof(double));
+    const uint16_t* row = in + t * in_stride;
+    for (int64_t j = 0; j < I; ++j)
+      a[j] = silu_mul(orc_bf16_decode(row[j]), orc_bf16_decode(row[I + j]));
+    quant_row(a, I, quant_mode, group_size, static_scale, out + t * out_stride,
+              scales_row_ptr(scales, quant_mode, group_size, I, t));
+    free(a);
+  }
+  return ORC_OK;
+}
+
+/* The unfused composition: silu_and_mul writes a bf16 activation tensor, the
+ * quant op reads it back.  [FUSION] section "SiLU+Mul + Quantization". */
+int orc_unfused_silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_mode,
+                               int group_size, float static_scale, uint8_t* out,
+                               int64_t out_stride, float* scales, int64_t T, int64_t I) {
+  if (T < 0 || I <= 0 || !quant_args_ok(quant_mode, group_size, I, 0)) return ORC_EARG;
+  if (!static_scale_ok(quant_mode, static_scale)) return ORC_ECONTRACT;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* a = (double*)malloc((size_t)I * sizeof(double));
+    const uint16_t* row = in + t * in_stride;
+    for (int64_t j = 0; j < I; ++j)
+      a[j] = orc_bf16_decode(
+          orc_bf16_encode(silu_mul(orc_bf16_decode(row[j]), orc_bf16_decode(row[I + j]))));
+    quant_row(a, I, quant_mode, group_size, static_scale, out + t * out_stride,
+              scales_row_ptr(scales, quant_mode, group_size, I, t));
+    free(a);
+  }
+  return ORC_OK;
+}
+
+/* ======================================================================= */
+/* RoPE + paged KV-cache write                                              */
+/* ======================================================================= */
+
+static int rope_args_ok(int64_t T, int Hq, int Hkv, int D, int rot_dim, int block_size,
+                        int64_t num_blocks, int is_neox) {
+  return T >= 0 && Hq > 0 && Hkv > 0 && D > 0 && rot_dim > 0 && rot_dim % 2 == 0 &&
+         rot_dim <= D && block_size > 0 && num_blocks > 0 && (is_neox == 0 || is_neox == 1);
+}
+
+static int cmp_i64(const void* a, const void* b) {
+  const int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* Data contract of the cache write: every position inside the rotary table,
+ * every non-negative slot inside the cache, and no two tokens on one slot
+ * (with duplicates several final cache states would be "correct"). */
+static int rope_contract_ok(const int64_t* positions, int64_t max_pos,
+                            const int64_t* slot_mapping, int64_t T, int block_size,
+                            int64_t num_blocks) {
+  const int64_t n_slots = (int64_t)block_size * num_blocks;
+  int64_t* s = (int64_t*)malloc((size_t)(T > 0 ? T : 1) * sizeof(int64_t));
+  int64_t n = 0;
+  int ok = 1;
+  for (int64_t t = 0; t < T && ok; ++t) {
+    if (positions[t] < 0 || positions[t] >= max_pos) ok = 0;
+    if (slot_mapping[t] >= n_slots) ok = 0;
+    if (slot_mapping[t] >= 0) s[n++] = slot_mapping[t];
+  }
+  if (ok) {
+    qsort(s, (size_t)n, sizeof(int64_t), cmp_i64);
+    for (int64_t i = 1; i < n; ++i)
+      if (s[i] == s[i - 1]) ok = 0;
+  }
+  free(s);
+  return ok;
+}
+
+/* cos and sin of the rotation angles of one position.  Reading (the pages
+ * give no RoPE formula): the RoFormer frequencies inv_i = theta^(-2i/rot_dim)
+ * for i < rot_dim/2, angle = pos * inv_i, evaluated in double. */
+static void rope_angles(int64_t pos, double theta, int rot_dim, double* c, double* s) {
+  for (int i = 0; i < rot_dim / 2; ++i) {
+    const double inv = pow(theta, -2.0 * (double)i / (double)rot_dim);
+    const double ang = (double)pos * inv;
+    c[i] = cos(ang);
+    s[i] = sin(ang);
+  }
+}
+
+/* Rotate one head of D values.  Pairs are (i, i + rot_dim/2) in the GPT-NeoX
+ * layout and (2i, 2i+1) in the GPT-J layout; each pair (a, b) becomes
+ * (a cos - b sin, b cos + a sin).  Dimensions at and past rot_dim pass
+ * through.  The head is read completely before it is written, so out may
+ * alias in. */
+static void rotate_head(const uint16_t* in, uint16_t* out, const double* c, const double* s,
+                        int D, int rot_dim, int is_neox) {
+  double* x = (double*)malloc((size_t)D * sizeof(double));
+  uint16_t* keep = (uint16_t*)malloc((size_t)D * sizeof(uint16_t));
+  for (int d = 0; d < D; ++d) {
+    x[d] = orc_bf16_decode(in[d]);
+    keep[d] = in[d];
+  }
+  const int half = rot_dim / 2;
+  for (int i = 0; i < half; ++i) {
+    const int a = is_neox ? i : 2 * i;
+    const int b = is_neox ? i + half : 2 * i + 1;
+    out[a] = orc_bf16_encode(x[a] * c[i] - x[b] * s[i]);
+    out[b] = orc_bf16_encode(x[b] * c[i] + x[a] * s[i]);
+  }
+  for (int d = rot_dim; d < D; ++d) out[d] = keep[d];
+  free(x);
+  free(keep);
+}
+
+/* Address of head h of a slot in a paged cache laid out
+ * [num_blocks, block_size, Hkv, D].  [TUNING] section "PagedAttention": the
+ * cache is cut into fixed-size blocks and a request's logical token positions
+ * map to physical blocks through its block table.  Reading: the slot of a
+ * token is block * block_size + offset, as the caller's slot mapping gives. */
+static uint16_t* cache_head(uint16_t* cache, int64_t slot, int block_size, int Hkv, int D,
+                            int h) {
+  const int64_t blk = slot / block_size, off = slot % block_size;
+  return cache + (((blk * block_size + off) * Hkv + h) * (int64_t)D);
+}
+
+/* Rotary embedding fused with the KV-cache scatter: rotated q is written to
+ * q_out (which may alias q), rotated k and the unmodified v go straight into
+ * the slot of each token; k is not written anywhere else, and tokens with a
+ * negative slot (padding, a reading) write no cache.
+ * [FUSION] section "RoPE + KV-Cache Update (fuse_rope_kvcache)". */
+int orc_rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_stride,
+                      uint16_t* q_out, int64_t q_out_stride, const uint16_t* k,
+                      int64_t k_stride, const uint16_t* v, int64_t v_stride, double theta,
+                      int64_t max_pos, const int64_t* slot_mapping, uint16_t* key_cache,
+                      uint16_t* value_cache, int64_t T, int Hq, int Hkv, int D, int rot_dim,
+                      int block_size, int64_t num_blocks, int is_neox) {
+  if (!rope_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox)) return ORC_EARG;
+  if (!rope_contract_ok(positions, max_pos, slot_mapping, T, block_size, num_blocks))
+    return ORC_ECONTRACT;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* c = (double*)malloc((size_t)rot_dim / 2 * sizeof(double));
+    double* s = (double*)malloc((size_t)rot_dim / 2 * sizeof(double));
+    rope_angles(positions[t], theta, rot_dim, c, s);
+    for (int h = 0; h < Hq; ++h)
+      rotate_head(q + t * q_stride + (int64_t)h * D, q_out + t * q_out_stride + (int64_t)h * D,
+                  c, s, D, rot_dim, is_neox);
+    const int64_t slot = slot_mapping[t];
+    if (slot >= 0) {
+      for (int h = 0; h < Hkv; ++h) {
+        rotate_head(k + t * k_stride + (int64_t)h * D,
+                    cache_head(key_cache, slot, block_size, Hkv, D, h), c, s, D, rot_dim,
+                    is_neox);
+        memcpy(cache_head(value_cache, slot, block_size, Hkv, D, h),
+               v + t * v_stride + (int64_t)h * D, (size_t)D * sizeof(uint16_t));
+      }
+    }
+    free(c);
+    free(s);
+  }
+  return ORC_OK;
+}
+
+/* The unfused pair the fusion replaces: the rotary_embedding op writes
+ * rotated q and k back as tensors, then the KV-cache update op re-reads k and
+ * v and writes the slots.  [FUSION] section "RoPE + KV-Cache Update". */
+int orc_unfused_rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_stride,
+                              uint16_t* q_out, int64_t q_out_stride, const uint16_t* k,
+                              int64_t k_stride, uint16_t* k_out, const uint16_t* v,
+                              int64_t v_stride, double theta, int64_t max_pos,
+                              const int64_t* slot_mapping, uint16_t* key_cache,
+                              uint16_t* value_cache, int64_t T, int Hq, int Hkv, int D,
+                              int rot_dim, int block_size, int64_t num_blocks, int is_neox) {
+  if (!rope_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox)) return ORC_EARG;
+  if (!rope_contract_ok(positions, max_pos, slot_mapping, T, block_size, num_blocks))
+    return ORC_ECONTRACT;
+  /* op 1: rotary embedding of q and k */
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* c = (double*)malloc((size_t)rot_dim / 2 * sizeof(double));
+    double* s = (double*)malloc((size_t)rot_dim / 2 * sizeof(double));
+    rope_angles(positions[t], theta, rot_dim, c, s);
+    for (int h = 0; h < Hq; ++h)
+      rotate_head(q + t * q_stride + (int64_t)h * D, q_out + t * q_out_stride + (int64_t)h * D,
+                  c, s, D, rot_dim, is_neox);
+    for (int h = 0; h < Hkv; ++h)
+      rotate_head(k + t * k_stride + (int64_t)h * D, k_out + (t * Hkv + h) * (int64_t)D, c, s,
+                  D, rot_dim, is_neox);
+    free(c);
+    free(s);
+  }
+  /* op 2: KV-cache update from the materialized k and the input v */
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    for (int h = 0; h < Hkv; ++h) {
+      memcpy(cache_head(key_cache, slot, block_size, Hkv, D, h),
+             k_out + (t * Hkv + h) * (int64_t)D, (size_t)D * sizeof(uint16_t));
+      memcpy(cache_head(value_cache, slot, block_size, Hkv, D, h),
+             v + t * v_stride + (int64_t)h * D, (size_t)D * sizeof(uint16_t));
+    }
+  }
+  return ORC_OK;
+}
+
+/* ======================================================================= */
+/* MLA dual RMSNorm (+ FP8 quant of the q latent)                           */
+/* ======================================================================= */
+
+/* Normalize one row (no residual) and emit it as bf16 (mode NONE) or as FP8
+ * codes with scales. */
+static void norm_emit_row(const uint16_t* src, const uint16_t* w, float eps, int64_t H,
+                          int mode, int group_size, void* dst, float* scales_row) {
+  if (H <= 0) return;
+  double* z = (double*)calloc((size_t)H, sizeof(double));
+  double* y = (double*)calloc((size_t)H, sizeof(double));
+  for (int64_t j = 0; j < H; ++j) z[j] = orc_bf16_decode(src[j]);
+  rms_norm_row(z, w, eps, H, y);
+  if (mode == ORC_Q_NONE) {
+    uint16_t* o = (uint16_t*)dst;
+    for (int64_t j = 0; j < H; ++j) o[j] = orc_bf16_encode(y[j]);
+  } else {
+    quant_row(y, H, mode, group_size, 0.0f, (uint8_t*)dst, scales_row);
+  }
+  free(z);
+  free(y);
+}
+
+static int dual_args_ok(int64_t T, int64_t Hq, int64_t Hkv, int mode, int group_size) {
+  return T >= 0 && Hq > 0 && Hkv > 0 && mode != ORC_Q_STATIC &&
+         quant_args_ok(mode, group_size, Hq, 1);
+}
+
+/* The paired q_a / kv_a RMSNorms of an MLA layer in one op, each with its own
+ * weight and epsilon; optionally the q latent is FP8-quantized (per token or
+ * per group) while the kv latent stays bf16.
+ * [FUSION] section "MLA Dual RMSNorm (fuse_mla_dual_rms_norm)", including its
+ * FP8 per-token-quant variant. */
+int orc_dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_w,
+                           float eps_q, const uint16_t* kv, int64_t kv_stride,
+                           const uint16_t* kv_w, float eps_kv, int q_quant_mode,
+                           int group_size, void* q_out, int64_t q_out_stride, float* q_scales,
+                           uint16_t* kv_out, int64_t kv_out_stride, int64_t T, int64_t Hq,
+                           int64_t Hkv) {
+  if (!dual_args_ok(T, Hq, Hkv, q_quant_mode, group_size)) return ORC_EARG;
+  const size_t q_elem = q_quant_mode == ORC_Q_NONE ? sizeof(uint16_t) : sizeof(uint8_t);
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    norm_emit_row(q + t * q_stride, q_w, eps_q, Hq, q_quant_mode, group_size,
+                  (char*)q_out + (size_t)(t * q_out_stride) * q_elem,
+                  scales_row_ptr(q_scales, q_quant_mode, group_size, Hq, t));
+    norm_emit_row(kv + t * kv_stride, kv_w, eps_kv, Hkv, ORC_Q_NONE, 0,
+                  kv_out + t * kv_out_stride, NULL);
+  }
+  return ORC_OK;
+}
+
+/* The unfused form: two separate norm calls.  When q is quantized the q side
+ * is the single-row norm+dynamic-quant op (the residual-free case of
+ * orc_fused_add_rmsnorm_quant) and kv is a plain rms_norm.
+ * [FUSION] section "MLA Dual RMSNorm", both unfused listings. */
+int orc_unfused_dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_w,
+                                   float eps_q, const uint16_t* kv, int64_t kv_stride,
+                                   const uint16_t* kv_w, float eps_kv, int q_quant_mode,
+                                   int group_size, void* q_out, int64_t q_out_stride,
+                                   float* q_scales, uint16_t* kv_out, int64_t kv_out_stride,
+                                   int64_t T, int64_t Hq, int64_t Hkv) {
+  if (!dual_args_ok(T, Hq, Hkv, q_quant_mode, group_size)) return ORC_EARG;
+  int rc;
+  if (q_quant_mode == ORC_Q_NONE) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+      norm_emit_row(q + t * q_stride, q_w, eps_q, Hq, ORC_Q_NONE, 0,
+                    (uint16_t*)q_out + t * q_out_stride, NULL);
+    rc = ORC_OK;
+  } else {
+    rc = orc_fused_add_rmsnorm_quant(q, q_stride, NULL, 0, q_w, eps_q, q_quant_mode, group_size,
+                                     0.0f, (uint8_t*)q_out, q_out_stride, q_scales, T, Hq);
+  }
+  if (rc != ORC_OK) return rc;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    norm_emit_row(kv + t * kv_stride, kv_w, eps_kv, Hkv, ORC_Q_NONE, 0,
+                  kv_out + t * kv_out_stride, NULL);
+  return ORC_OK;
+}

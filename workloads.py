@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for the four fused kernels.
+
+Shared by the tests, the benchmark and the smoke check, and by both the HIP
+path and the CPU oracle.  It holds none of the method's arithmetic: it only
+draws random numbers (numpy ``default_rng``) and stores them as bf16 bit
+patterns (torch's float32 -> bfloat16 conversion, round-to-nearest-even).
+
+Layer shapes are those of Llama-3-8B (hidden 4096, intermediate 14336, 32 query
+/ 8 key-value heads of 128, rope theta 500000) and of DeepSeek-V3's MLA
+(q_lora_rank 1536, kv_lora_rank 512).  No weights or datasets are involved.
+
+Seeding: every tensor comes from ``default_rng((tag, T, index, salt))`` where
+``tag`` names the workload, ``T`` is the token count, ``index`` numbers the
+tensor within the workload and ``salt`` lets callers draw independent copies
+(the benchmark's rotating buffer sets).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+_TAGS = {"norm_static": 0, "norm_token": 1, "silu": 2, "rope": 3, "mla": 4,
+         "qknorm": 5, "pad": 6, "mla_rope": 7}
+
+
+@dataclasses.dataclass(frozen=True)
+class NormCfg:
+    """Residual add + RMSNorm + FP8 quant."""
+    name: str
+    H: int
+    eps: float
+    quant: str  # "static" | "per_token" | "per_group"
+    group_size: int = 0
+    static_scale: float = 0.05
+    Ts: tuple = ()
+
+
+@dataclasses.dataclass(frozen=True)
+class SiluCfg:
+    """SiLU-and-Mul + FP8 quant."""
+    name: str
+    I: int
+    quant: str
+    group_size: int = 128
+    static_scale: float = 0.05
+    Ts: tuple = ()
+
+
+@dataclasses.dataclass(frozen=True)
+class RopeCfg:
+    """Neox RoPE + paged KV-cache write."""
+    name: str
+    Hq: int = 32
+    Hkv: int = 8
+    D: int = 128
+    rot_dim: int = 128
+    theta: float = 500000.0
+    max_pos: int = 8192
+    num_blocks: int = 4096
+    block_size: int = 16
+    is_neox: bool = True
+    Ts: tuple = ()
+
+
+@dataclasses.dataclass(frozen=True)
+class MlaCfg:
+    """MLA dual RMSNorm with per-group FP8 quant of the q latent."""
+    name: str
+    Hq: int = 1536
+    Hkv: int = 512
+    eps_q: float = 1e-6
+    eps_kv: float = 1e-6
+    quant: str = "per_group"
+    group_size: int = 128
+    Ts: tuple = ()
+
+
+# The five workloads and their token-count sets; T = 8192 is the headline
+# point for every kernel.
+NORM_STATIC = NormCfg("norm_static", H=1024, eps=1e-6, quant="static", static_scale=0.05,
+                      Ts=(16, 8192))
+NORM_TOKEN = NormCfg("norm_token", H=4096, eps=1e-5, quant="per_token", Ts=(1, 32, 512, 8192))
+SILU = SiluCfg("silu", I=14336, quant="per_group", group_size=128, Ts=(1, 64, 1024, 8192))
+ROPE = RopeCfg("rope", Ts=(16, 2048, 8192, 16384))
+MLA = MlaCfg("mla", Ts=(1, 1024, 8192, 16384))
+
+HEADLINE_T = 8192
+
+
+def _rng(tag: str, T: int, index: int, salt: int = 0) -> np.random.Generator:
+    return np.random.default_rng((_TAGS[tag], int(T), int(index), int(salt)))
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round-to-nearest-even, via torch."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_normal(rng: np.random.Generator, shape, mean: float = 0.0, std: float = 1.0):
+    a = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    if mean != 0.0:
+        a += np.float32(mean)
+    return to_bf16_bits(a)
+
+
+def norm_inputs(T: int, H: int, salt: int = 0, tag: str = "norm_token"):
+    """x, residual ~ N(0,1) [T,H]; weight ~ N(1, 0.1) [H]."""
+    return dict(
+        x=bf16_normal(_rng(tag, T, 0, salt), (T, H)),
+        residual=bf16_normal(_rng(tag, T, 1, salt), (T, H)),
+        weight=bf16_normal(_rng(tag, 0, 2, salt), (H,), mean=1.0, std=0.1),
+    )
+
+
+def silu_inputs(T: int, I: int, salt: int = 0):
+    """gate | up halves of one [T, 2I] row block, ~ N(0, 2) (std 2)."""
+    return dict(inp=bf16_normal(_rng("silu", T, 0, salt), (T, 2 * I), std=2.0))
+
+
+def rope_inputs(T: int, cfg: RopeCfg = ROPE, salt: int = 0, with_cache: bool = True):
+    """q [T,Hq,D], k, v [T,Hkv,D] ~ N(0,1); positions uniform in [0, max_pos);
+    slot_mapping = the first T entries of a seeded permutation of all cache slots
+    (distinct); caches filled with a seeded random bf16 sentinel pattern."""
+    n_slots = cfg.num_blocks * cfg.block_size
+    if T > n_slots:
+        raise ValueError("more tokens than cache slots")
+    d = dict(
+        q=bf16_normal(_rng("rope", T, 0, salt), (T, cfg.Hq, cfg.D)),
+        k=bf16_normal(_rng("rope", T, 1, salt), (T, cfg.Hkv, cfg.D)),
+        v=bf16_normal(_rng("rope", T, 2, salt), (T, cfg.Hkv, cfg.D)),
+        positions=_rng("rope", T, 3, salt).integers(0, cfg.max_pos, T, dtype=np.int64),
+        slot_mapping=_rng("rope", T, 4, salt).permutation(n_slots)[:T].astype(np.int64),
+    )
+    if with_cache:
+        shape = (cfg.num_blocks, cfg.block_size, cfg.Hkv, cfg.D)
+        d["key_cache"] = sentinel_cache(shape, 5, salt)
+        d["value_cache"] = sentinel_cache(shape, 6, salt)
+    return d
+
+
+def sentinel_cache(shape, index: int, salt: int = 0) -> np.ndarray:
+    """Random bf16 bit patterns (finite: exponent field below all-ones)."""
+    r = _rng("rope", 0, index, salt).integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    return (r & np.uint16(0xBFFF)).astype(np.uint16)  # clear the top exponent bit
+
+
+def mla_inputs(T: int, cfg: MlaCfg = MLA, salt: int = 0):
+    """q latent [T,1536], kv latent [T,512] ~ N(0,1); weights ~ N(1, 0.1)."""
+    return dict(
+        q=bf16_normal(_rng("mla", T, 0, salt), (T, cfg.Hq)),
+        kv=bf16_normal(_rng("mla", T, 1, salt), (T, cfg.Hkv)),
+        q_w=bf16_normal(_rng("mla", 0, 2, salt), (cfg.Hq,), mean=1.0, std=0.1),
+        kv_w=bf16_normal(_rng("mla", 0, 3, salt), (cfg.Hkv,), mean=1.0, std=0.1),
+    )
