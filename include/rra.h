@@ -1,0 +1,201 @@
+/*
+ * rra.h - C ABI of the fused residual-add / RMSNorm / SiLU / RoPE / FP8-quant
+ * kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the fused patterns described on the vLLM design page
+ * "Fusion torch.compile passes"; each entry point below names the section that
+ * defines it.  Every entry point is a plain C function taking raw device
+ * pointers, element strides and sizes.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - Types: bf16 tensors are passed as uint16_t bit patterns; FP8 outputs are
+ *   OCP e4m3fn bytes (largest finite value 448, round-to-nearest-even,
+ *   saturating); scales are fp32; token indices are int64.
+ * - Layout: 2-D tensors are row-major [T, width] with an arbitrary row stride
+ *   (in elements) and contiguous rows, so column slices ("split" views of a
+ *   wider projection) are valid inputs.
+ * - Alignment: every bf16 pointer must be 16-byte aligned and every bf16 row
+ *   stride a multiple of 8 elements; FP8 outputs 8-byte aligned with strides a
+ *   multiple of 8; scale pointers 4-byte aligned.
+ * - Ownership: the caller allocates and owns every buffer.  The library
+ *   allocates nothing, keeps no mutable state, never synchronizes, and only
+ *   enqueues work on `stream` (a hipStream_t; NULL = the null stream).  Calls
+ *   are therefore reentrant and may be captured into a HIP graph.
+ * - Errors: each function returns RRA_OK (0) or a negative rra_status.  All
+ *   argument checks run on the host before anything is launched, so an error
+ *   return means nothing was enqueued.  T == 0 returns RRA_OK without a launch.
+ *   RRA_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).
+ * - Device-data contract (not checked: checking would need a host sync):
+ *   inputs are finite; a static scale is finite and > 0; positions lie in
+ *   [0, max_pos); non-negative slots lie below num_blocks * block_size and are
+ *   pairwise distinct.  Breaking it gives unspecified outputs (no memory is
+ *   written outside the documented output ranges except through an
+ *   out-of-range slot or position, which is undefined behaviour).
+ */
+#ifndef RRA_H
+#define RRA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RRA_ABI_VERSION 1
+
+enum rra_status {
+  RRA_OK = 0,
+  RRA_ERR_NULL = -1,        /* a required pointer is NULL */
+  RRA_ERR_SHAPE = -2,       /* negative or inconsistent sizes */
+  RRA_ERR_ALIGN = -3,       /* pointer or stride breaks the alignment rules */
+  RRA_ERR_UNSUPPORTED = -4, /* valid but not implemented (mode, size, layout) */
+  RRA_ERR_LAUNCH = -5       /* the kernel launch failed */
+};
+
+enum rra_quant_mode {
+  RRA_Q_NONE = 0,      /* no quantization: bf16 output */
+  RRA_Q_STATIC = 1,    /* one per-tensor scale given by the caller */
+  RRA_Q_PER_TOKEN = 2, /* scale[t] = amax over the row / 448 */
+  RRA_Q_PER_GROUP = 3  /* scale[t, k] = amax over columns [k*g, (k+1)*g) / 448 */
+};
+
+/* Version of this ABI (RRA_ABI_VERSION of the built library). */
+int rra_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* rra_status_string(int status);
+
+/*
+ * Residual add + RMSNorm + FP8 quant.
+ * Section "RMSNorm + Quantization (fuse_norm_quant)": rms_norm(x) -> quant and
+ * fused_add_rms_norm(x, residual) -> quant as one kernel, with the residual
+ * updated in place and no full-precision intermediate in memory.
+ *
+ *   z      = bf16(x + residual)           (z = x when residual is NULL)
+ *   residual <- z                         (in place, when residual != NULL)
+ *   y      = z / sqrt(mean(z^2) + eps) * weight
+ *   out    = e4m3fn(y / s)
+ * with s = *static_scale (RRA_Q_STATIC), s = fp32(amax(|y| over the row)/448)
+ * written to scales[t] (RRA_Q_PER_TOKEN), or one such scale per contiguous
+ * group of group_size columns written to scales[t * (H / group_size) + k]
+ * (RRA_Q_PER_GROUP).  A zero amax gives s = 0 and all-zero codes.
+ *
+ * x          [T, H] bf16, row stride x_stride.
+ * residual   [T, H] bf16, row stride residual_stride, read and overwritten; or
+ *            NULL for plain RMSNorm + quant.
+ * weight     [H] bf16, contiguous.
+ * quant_mode RRA_Q_STATIC, RRA_Q_PER_TOKEN or RRA_Q_PER_GROUP.
+ * group_size 64 or 128 with RRA_Q_PER_GROUP (H % group_size == 0), else 0.
+ * static_scale  device pointer to one fp32 scale (RRA_Q_STATIC only).
+ * out        [T, H] e4m3fn, row stride out_stride.
+ * scales     [T] or [T, H/group_size] fp32 contiguous; NULL for RRA_Q_STATIC.
+ * Limits: H % 8 == 0 and 8 <= H <= 8192.
+ */
+int fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint16_t* residual,
+                            int64_t residual_stride, const uint16_t* weight, float eps,
+                            int quant_mode, int group_size, const float* static_scale,
+                            uint8_t* out, int64_t out_stride, float* scales, int64_t T,
+                            int64_t H, void* stream);
+
+/*
+ * SiLU-and-Mul + FP8 quant.
+ * Section "SiLU+Mul + Quantization (fuse_act_quant)": the gate-up activation
+ * silu_and_mul followed by quantization without materializing the activation.
+ *
+ *   a[t, j] = silu(in[t, j]) * in[t, I + j],   silu(g) = g / (1 + exp(-g))
+ *   out     = e4m3fn(a / s)
+ * with s = *static_scale (RRA_Q_STATIC) or one scale per group of group_size
+ * columns, s = fp32(amax/448), written to scales[t * (I / group_size) + k]
+ * (RRA_Q_PER_GROUP).
+ *
+ * in     [T, 2I] bf16 (gate half, then up half), row stride in_stride.
+ * out    [T, I] e4m3fn, row stride out_stride.
+ * scales [T, I/group_size] fp32 contiguous; NULL for RRA_Q_STATIC.
+ * Limits: I % 8 == 0; group_size 64 or 128 dividing I.
+ */
+int silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_mode, int group_size,
+                   const float* static_scale, uint8_t* out, int64_t out_stride,
+                   float* scales, int64_t T, int64_t I, void* stream);
+
+/*
+ * Rotary cos/sin table used by rope_kv_write.
+ * cos_sin[p, i] = cos(p * theta^(-2i/rot_dim)) and
+ * cos_sin[p, rot_dim/2 + i] = sin(same angle), for p < max_pos and
+ * i < rot_dim/2, evaluated in double precision and rounded to fp32.
+ * cos_sin: [max_pos, rot_dim] fp32, contiguous, 16-byte aligned.
+ * Limits: rot_dim even, 16 <= rot_dim <= 1024; theta > 0.
+ */
+int rope_cos_sin_cache(float* cos_sin, int64_t max_pos, int rot_dim, double theta,
+                       void* stream);
+
+/*
+ * Rotary embedding + paged KV-cache write.
+ * Section "RoPE + KV-Cache Update (fuse_rope_kvcache)": the rotary embedding
+ * and the KV-cache scatter in one kernel, so k and v are read once and k is
+ * never written back.  The cache is paged as in the PagedAttention section of
+ * "Making vLLM fast: configuration, internals, and the places worth touching
+ * code": fixed-size blocks addressed through a per-token slot.
+ *
+ * For token t at position p = positions[t], every q head and k head of D
+ * values is rotated pairwise, (a, b) -> (a cos - b sin, b cos + a sin), with
+ * pairs (i, i + rot_dim/2) (GPT-NeoX layout, is_neox = 1) and the angles of
+ * row p of cos_sin.  Rotated q goes to q_out (q_out may equal q: in-place).
+ * With s = slot_mapping[t] >= 0, rotated k goes to key_cache[s / block_size,
+ * s % block_size, :, :] and v, unchanged, to value_cache at the same place.
+ * Tokens with s < 0 (padding) write no cache.  Nothing else is written.
+ *
+ * positions    [T] int64.
+ * q            [T, Hq, D] bf16, token stride q_stride, heads contiguous.
+ * q_out        [T, Hq, D] bf16, token stride q_out_stride (may alias q).
+ * k, v         [T, Hkv, D] bf16, token strides k_stride, v_stride.
+ * cos_sin      [max_pos, rot_dim] fp32 (see rope_cos_sin_cache).
+ * slot_mapping [T] int64.
+ * key_cache, value_cache [num_blocks, block_size, Hkv, D] bf16, contiguous.
+ * Limits: D in {64, 128, 256}; rot_dim == D; is_neox == 1 (the GPT-J pair
+ * layout is RRA_ERR_UNSUPPORTED); Hq, Hkv >= 1; block_size >= 1.
+ */
+int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_stride,
+                  uint16_t* q_out, int64_t q_out_stride, const uint16_t* k, int64_t k_stride,
+                  const uint16_t* v, int64_t v_stride, const float* cos_sin, int64_t max_pos,
+                  const int64_t* slot_mapping, uint16_t* key_cache, uint16_t* value_cache,
+                  int64_t T, int Hq, int Hkv, int D, int rot_dim, int block_size,
+                  int64_t num_blocks, int is_neox, void* stream);
+
+/*
+ * MLA dual RMSNorm (+ FP8 quant of the q latent).
+ * Section "MLA Dual RMSNorm (fuse_mla_dual_rms_norm)": the paired q_a and kv_a
+ * RMSNorms of an MLA layer in one launch, each with its own weight and
+ * epsilon; in the FP8 variant only the q latent is quantized and kv stays
+ * bf16.
+ *
+ *   q_out  = RMSNorm(q; q_weight, eps_q)   as bf16 (RRA_Q_NONE) or e4m3fn
+ *            codes with per-token or per-group scales in q_scales
+ *   kv_out = RMSNorm(kv; kv_weight, eps_kv) as bf16
+ *
+ * q        [T, Hq] bf16, row stride q_stride;  kv [T, Hkv], row stride kv_stride.
+ * q_out    [T, Hq] bf16 (RRA_Q_NONE) or e4m3fn, row stride q_out_stride.
+ * q_scales [T] or [T, Hq/group_size] fp32 contiguous; NULL for RRA_Q_NONE.
+ * kv_out   [T, Hkv] bf16, row stride kv_out_stride.
+ * Limits: q_quant_mode NONE, PER_TOKEN or PER_GROUP (64/128 dividing Hq);
+ * Hq and Hkv multiples of 8 with Hq <= 2048 and Hkv <= 1024.
+ */
+int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_weight,
+                       float eps_q, const uint16_t* kv, int64_t kv_stride,
+                       const uint16_t* kv_weight, float eps_kv, int q_quant_mode,
+                       int group_size, void* q_out, int64_t q_out_stride, float* q_scales,
+                       uint16_t* kv_out, int64_t kv_out_stride, int64_t T, int64_t Hq,
+                       int64_t Hkv, void* stream);
+
+/*
+ * Diagnostic: out[i] = e4m3fn(in[i]) for n fp32 values, using the same device
+ * conversion every quantizing kernel above uses (round-to-nearest-even,
+ * saturating to +-448).  NaN inputs give unspecified codes.
+ * in: [n] fp32, 16-byte aligned; out: [n] bytes, 4-byte aligned.
+ */
+int rra_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RRA_H */

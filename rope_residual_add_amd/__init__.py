@@ -1,0 +1,271 @@
+"""Fused residual-add / RMSNorm / SiLU / RoPE / FP8-quant kernels for AMD MI355X.
+
+Python binding of ``librra.so`` (hand-written HIP for gfx950).  Every function
+here only marshals torch tensors into the C ABI declared in ``include/rra.h``
+and raises ``RRAError`` on a non-zero status; all computation happens in the
+library's kernels, on the tensors' device and the current torch stream.  PyTorch
+is used only for device memory and streams.
+
+The library must be built first (``python -m rope_residual_add_amd.build`` or
+``__graft_entry__.build()``); importing this package without it fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported first so that librra.so binds to torch's HIP runtime
+
+from .build import SO as LIBRARY_PATH
+
+Q_NONE, Q_STATIC, Q_PER_TOKEN, Q_PER_GROUP = 0, 1, 2, 3
+_QUANT_NAMES = {"none": Q_NONE, "static": Q_STATIC, "per_token": Q_PER_TOKEN,
+                "per_group": Q_PER_GROUP}
+
+EXPORTS = ("rra_abi_version", "rra_status_string", "fused_add_rmsnorm_quant", "silu_mul_quant",
+           "rope_cos_sin_cache", "rope_kv_write", "dual_rmsnorm_quant", "rra_e4m3fn_encode")
+
+
+class RRAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+_p, _i64, _i32, _f32, _f64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float,
+                              ctypes.c_double)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librra.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY_PATH):
+            raise ImportError(f"{LIBRARY_PATH} is missing: build it with "
+                              "`python -m rope_residual_add_amd.build`")
+        L = ctypes.CDLL(LIBRARY_PATH)
+        L.rra_abi_version.restype = _i32
+        L.rra_status_string.restype = ctypes.c_char_p
+        L.rra_status_string.argtypes = [_i32]
+        L.fused_add_rmsnorm_quant.argtypes = [_p, _i64, _p, _i64, _p, _f32, _i32, _i32, _p, _p,
+                                              _i64, _p, _i64, _i64, _p]
+        L.silu_mul_quant.argtypes = [_p, _i64, _i32, _i32, _p, _p, _i64, _p, _i64, _i64, _p]
+        L.rope_cos_sin_cache.argtypes = [_p, _i64, _i32, _f64, _p]
+        L.rope_kv_write.argtypes = [_p, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p,
+                                    _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _p]
+        L.dual_rmsnorm_quant.argtypes = [_p, _i64, _p, _f32, _p, _i64, _p, _f32, _i32, _i32, _p,
+                                         _i64, _p, _p, _i64, _i64, _i64, _i64, _p]
+        L.rra_e4m3fn_encode.argtypes = [_p, _p, _i64, _p]
+        for name in EXPORTS[2:]:
+            getattr(L, name).restype = _i32
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return int(lib().rra_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib().rra_status_string(int(status)).decode()
+
+
+# ---- marshalling helpers -----------------------------------------------------
+
+def _mode(m) -> int:
+    return _QUANT_NAMES[m] if isinstance(m, str) else int(m)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need_cuda(name: str, t: torch.Tensor, dtypes) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+
+
+def _vector(name: str, t: torch.Tensor, n: int) -> None:
+    _need_cuda(name, t, (torch.bfloat16,))
+    if t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [{n}] bf16 tensor")
+
+
+def _rows(name: str, t: torch.Tensor, dtypes, width: int | None = None) -> int:
+    """Check a [T, width] tensor with contiguous rows; return its row stride."""
+    _need_cuda(name, t, dtypes)
+    if t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    if width is not None and t.shape[1] != width:
+        raise ValueError(f"{name} must have {width} columns, got {t.shape[1]}")
+    return t.stride(0)
+
+
+def _heads(name: str, t: torch.Tensor, H: int, D: int) -> int:
+    """Check a [T, H, D] (or [T, H*D]) tensor whose heads are contiguous."""
+    _need_cuda(name, t, (torch.bfloat16,))
+    if t.dim() == 3:
+        if tuple(t.shape[1:]) != (H, D) or (t.numel() > 0 and (t.stride(2) != 1 or t.stride(1) != D)):
+            raise ValueError(f"{name} must be [T, {H}, {D}] with contiguous heads")
+        return t.stride(0)
+    return _rows(name, t, (torch.bfloat16,), H * D)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise RRAError(fn, status)
+
+
+_BF16 = (torch.bfloat16,)
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _scales_shape(mode: int, T: int, H: int, g: int):
+    if mode == Q_PER_TOKEN:
+        return (T,)
+    if mode == Q_PER_GROUP:
+        return (T, H // g)
+    return None
+
+
+# ---- the fused ops -------------------------------------------------------------
+
+def fused_add_rmsnorm_quant(x, residual, weight, eps, quant_mode, group_size=0,
+                            static_scale=None, out=None, scales=None):
+    """Residual add + RMSNorm + FP8 quant (residual updated in place).
+
+    x, residual: [T, H] bf16 (residual may be None); weight: [H] bf16;
+    static_scale: [1] fp32 device tensor (static mode).  Returns (out, scales):
+    out [T, H] float8_e4m3fn, scales [T] / [T, H/g] fp32 or None."""
+    mode = _mode(quant_mode)
+    T, H = x.shape
+    xs = _rows("x", x, _BF16)
+    rs = _rows("residual", residual, _BF16, H) if residual is not None else 0
+    _vector("weight", weight, H)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=x.device)
+    os_ = _rows("out", out, _FP8, H)
+    shape = _scales_shape(mode, T, H, group_size or 1)
+    if scales is None and shape is not None:
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        st = lib().fused_add_rmsnorm_quant(
+            _ptr(x), xs, _ptr(residual), rs, _ptr(weight), float(eps), mode,
+            int(group_size), _ptr(static_scale), _ptr(out), os_, _ptr(scales), T, H, _stream(x))
+    _check("fused_add_rmsnorm_quant", st)
+    return out, scales
+
+
+def silu_mul_quant(inp, quant_mode, group_size=0, static_scale=None, out=None, scales=None):
+    """SiLU-and-Mul + FP8 quant.  inp: [T, 2I] bf16 (gate | up).
+    Returns (out [T, I] float8_e4m3fn, scales [T, I/g] fp32 or None)."""
+    mode = _mode(quant_mode)
+    T, two_i = inp.shape
+    I = two_i // 2
+    s = _rows("inp", inp, _BF16)
+    if out is None:
+        out = torch.empty((T, I), dtype=torch.float8_e4m3fn, device=inp.device)
+    os_ = _rows("out", out, _FP8, I)
+    shape = _scales_shape(mode, T, I, group_size or 1)
+    if scales is None and shape is not None:
+        scales = torch.empty(shape, dtype=torch.float32, device=inp.device)
+    with torch.cuda.device(inp.device):
+        st = lib().silu_mul_quant(_ptr(inp), s, mode, int(group_size), _ptr(static_scale),
+                                  _ptr(out), os_, _ptr(scales), T, I, _stream(inp))
+    _check("silu_mul_quant", st)
+    return out, scales
+
+
+def rope_cos_sin_cache(max_pos: int, rot_dim: int, theta: float, device="cuda", out=None):
+    """[max_pos, rot_dim] fp32 table: cos of the rot_dim/2 angles, then sin."""
+    if out is None:
+        out = torch.empty((max_pos, rot_dim), dtype=torch.float32, device=device)
+    _need_cuda("out", out, (torch.float32,))
+    with torch.cuda.device(out.device):
+        st = lib().rope_cos_sin_cache(_ptr(out), int(max_pos), int(rot_dim), float(theta),
+                                      _stream(out))
+    _check("rope_cos_sin_cache", st)
+    return out
+
+
+def rope_kv_write(positions, q, k, v, cos_sin, slot_mapping, key_cache, value_cache,
+                  q_out=None, is_neox=True):
+    """Neox RoPE of q and k + paged KV-cache write of rotated k and v.
+
+    q: [T, Hq, D], k, v: [T, Hkv, D] bf16; cos_sin: [max_pos, rot_dim] fp32;
+    positions, slot_mapping: [T] int64 (slot < 0 = padding);
+    caches: [num_blocks, block_size, Hkv, D] bf16.  q_out defaults to q
+    (in place).  Returns q_out."""
+    T = positions.shape[0]
+    num_blocks, block_size, Hkv, D = key_cache.shape
+    Hq = q.shape[1] if q.dim() == 3 else q.shape[1] // D
+    _need_cuda("positions", positions, (torch.int64,))
+    _need_cuda("slot_mapping", slot_mapping, (torch.int64,))
+    _need_cuda("cos_sin", cos_sin, (torch.float32,))
+    for name, c in (("key_cache", key_cache), ("value_cache", value_cache)):
+        _need_cuda(name, c, _BF16)
+        if not c.is_contiguous() or tuple(c.shape) != (num_blocks, block_size, Hkv, D):
+            raise ValueError(f"{name} must be a contiguous [num_blocks, block_size, Hkv, D] tensor")
+    if not (positions.is_contiguous() and slot_mapping.is_contiguous() and cos_sin.is_contiguous()):
+        raise ValueError("positions, slot_mapping and cos_sin must be contiguous")
+    if q_out is None:
+        q_out = q
+    qs, qos = _heads("q", q, Hq, D), _heads("q_out", q_out, Hq, D)
+    ks, vs = _heads("k", k, Hkv, D), _heads("v", v, Hkv, D)
+    max_pos, rot_dim = cos_sin.shape
+    with torch.cuda.device(q.device):
+        st = lib().rope_kv_write(
+            _ptr(positions), _ptr(q), qs, _ptr(q_out), qos, _ptr(k), ks, _ptr(v), vs,
+            _ptr(cos_sin), max_pos, _ptr(slot_mapping), _ptr(key_cache), _ptr(value_cache), T,
+            Hq, Hkv, D, rot_dim, block_size, num_blocks, int(bool(is_neox)), _stream(q))
+    _check("rope_kv_write", st)
+    return q_out
+
+
+def dual_rmsnorm_quant(q, q_weight, eps_q, kv, kv_weight, eps_kv, q_quant_mode="none",
+                       group_size=0, q_out=None, q_scales=None, kv_out=None):
+    """MLA dual RMSNorm of the q and kv latents in one launch; the q side is
+    optionally FP8-quantized.  Returns (q_out, q_scales or None, kv_out)."""
+    mode = _mode(q_quant_mode)
+    T, Hq = q.shape
+    Hkv = kv.shape[1]
+    qs = _rows("q", q, _BF16)
+    kvs = _rows("kv", kv, _BF16)
+    _vector("q_weight", q_weight, Hq)
+    _vector("kv_weight", kv_weight, Hkv)
+    if q_out is None:
+        dt = torch.bfloat16 if mode == Q_NONE else torch.float8_e4m3fn
+        q_out = torch.empty((T, Hq), dtype=dt, device=q.device)
+    qos = _rows("q_out", q_out, _BF16 if mode == Q_NONE else _FP8, Hq)
+    shape = _scales_shape(mode, T, Hq, group_size or 1)
+    if q_scales is None and shape is not None:
+        q_scales = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if kv_out is None:
+        kv_out = torch.empty((T, Hkv), dtype=torch.bfloat16, device=q.device)
+    kvos = _rows("kv_out", kv_out, _BF16, Hkv)
+    with torch.cuda.device(q.device):
+        st = lib().dual_rmsnorm_quant(
+            _ptr(q), qs, _ptr(q_weight), float(eps_q), _ptr(kv), kvs,
+            _ptr(kv_weight), float(eps_kv), mode, int(group_size), _ptr(q_out), qos,
+            _ptr(q_scales), _ptr(kv_out), kvos, T, Hq, Hkv, _stream(q))
+    _check("dual_rmsnorm_quant", st)
+    return q_out, q_scales, kv_out
+
+
+def e4m3fn_encode(x, out=None):
+    """fp32 -> e4m3fn codes with the kernels' device conversion (diagnostic)."""
+    _need_cuda("x", x, (torch.float32,))
+    x = x.contiguous()
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        st = lib().rra_e4m3fn_encode(_ptr(x), _ptr(out), x.numel(), _stream(x))
+    _check("rra_e4m3fn_encode", st)
+    return out

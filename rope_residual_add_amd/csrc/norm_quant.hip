@@ -1,0 +1,370 @@
+// Residual add + RMSNorm + FP8 quant, and the MLA dual RMSNorm (+ FP8 quant
+// of the q latent), for gfx950.
+//
+// Operations: vLLM design page "Fusion torch.compile passes", sections
+// "RMSNorm + Quantization (fuse_norm_quant)" (rms_norm / fused_add_rms_norm
+// followed by static, per-token or per-token-group FP8 quant, residual updated
+// in place) and "MLA Dual RMSNorm (fuse_mla_dual_rms_norm)" (the q_a and kv_a
+// norms in one launch; in the FP8 variant only q is quantized).
+//
+// Mapping: one wavefront per row.  A row of H bf16 values is spread over the
+// 64 lanes as 16-byte vectors: lane l holds vectors l, l + 64, l + 128, ... so
+// every vector load of the wave reads 1 KiB of contiguous memory.  The whole
+// row stays in VGPRs between the read and the write, so each element crosses
+// HBM once in each direction.  Row reductions (sum of squares, amax) are
+// wave-local DPP reductions: no LDS and no barrier.  A quantization group of
+// 128 (64) columns is exactly 16 (8) consecutive lanes of one vector, so group
+// amaxes are DPP row reductions as well.
+#include "rra_device.hpp"
+#include "rra_host.hpp"
+
+namespace rra {
+
+// This lane's share of one row: vector i covers columns (i*64 + lane)*8 .. +8.
+template <int NV>
+struct RowVecs {
+  u32x4 v[NV];
+};
+
+template <int NV, bool kStream>
+__device__ __forceinline__ void load_row(RowVecs<NV>& r, const uint16_t* base, int nvec,
+                                         int lane) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = i * kWave + lane;
+    if (idx < nvec)
+      r.v[i] = kStream ? ld_stream(base + idx * 8) : ld_cached(base + idx * 8);
+    else
+      r.v[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void store_row(uint16_t* base, const RowVecs<NV>& r, int nvec,
+                                         int lane) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = i * kWave + lane;
+    if (idx < nvec) st_stream(base + idx * 8, r.v[i]);
+  }
+}
+
+// t = z * w for the 8 columns of one vector.
+__device__ __forceinline__ void zw8(u32x4 z, u32x4 w, float t[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    t[2 * k] = bf16_lo(z[k]) * bf16_lo(w[k]);
+    t[2 * k + 1] = bf16_hi(z[k]) * bf16_hi(w[k]);
+  }
+}
+
+__device__ __forceinline__ float absmax8(const float t[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t[j]));
+  return m;
+}
+
+__device__ __forceinline__ u32x2 codes8(const float t[8], float f) {
+  return u32x2{pack_e4m3x4(t[0] * f, t[1] * f, t[2] * f, t[3] * f),
+               pack_e4m3x4(t[4] * f, t[5] * f, t[6] * f, t[7] * f)};
+}
+
+// RMSNorm of one row held in registers, then the row's output:
+//   y = z * w * rho,  rho = 1/sqrt(mean(z^2) + eps)
+// mode NONE writes bf16(y) to out (uint16_t*); the quantizing modes write
+// e4m3fn(y / s) to out (uint8_t*) and s to scale_row.
+// Because rho > 0 is one number per row, max|y| = max|z*w| * rho exactly
+// (rounding is monotonic), so the amax needs no extra pass over y; the codes
+// are t * (rho / s) with t = z * w.
+template <int NV>
+__device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs<NV>& w,
+                                             float eps, int H, int nvec, int lane, int mode,
+                                             int group, float static_inv, void* out,
+                                             float* scale_row) {
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float a = bf16_lo(z.v[i][k]), b = bf16_hi(z.v[i][k]);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  const float rho = rsqrtf(ss / static_cast<float>(H) + eps);
+
+  if (mode == RRA_Q_NONE) {
+    uint16_t* o = static_cast<uint16_t*>(out);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = i * kWave + lane;
+      float t[8];
+      zw8(z.v[i], w.v[i], t);
+      const u32x4 packed{pack_bf16x2(t[0] * rho, t[1] * rho), pack_bf16x2(t[2] * rho, t[3] * rho),
+                         pack_bf16x2(t[4] * rho, t[5] * rho), pack_bf16x2(t[6] * rho, t[7] * rho)};
+      if (idx < nvec) st_stream(o + idx * 8, packed);
+    }
+    return;
+  }
+
+  uint8_t* o = static_cast<uint8_t*>(out);
+  if (mode == RRA_Q_PER_GROUP) {
+    const int lanes_per_group = group / 8;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = i * kWave + lane;
+      float t[8];
+      zw8(z.v[i], w.v[i], t);
+      float m = absmax8(t);
+      m = group == 128 ? max16(m) : max8(m);
+      const float s = (m * rho) / 448.0f;
+      const float f = rho * inv_scale(s);
+      if (idx < nvec) {
+        if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = s;
+        st_stream(o + idx * 8, codes8(t, f));
+      }
+    }
+    return;
+  }
+
+  float f;
+  if (mode == RRA_Q_PER_TOKEN) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float t[8];
+      zw8(z.v[i], w.v[i], t);
+      m = fmaxf(m, absmax8(t));
+    }
+    m = wave_max(m);
+    const float s = (m * rho) / 448.0f;
+    f = rho * inv_scale(s);
+    if (lane == 0) scale_row[0] = s;
+  } else {  // RRA_Q_STATIC
+    f = rho * static_inv;
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = i * kWave + lane;
+    float t[8];
+    zw8(z.v[i], w.v[i], t);
+    if (idx < nvec) st_stream(o + idx * 8, codes8(t, f));
+  }
+}
+
+template <int NV, bool kResidual>
+__global__ void __launch_bounds__(kBlock)
+    add_rmsnorm_quant_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
+                             uint16_t* __restrict__ residual, int64_t res_stride,
+                             const uint16_t* __restrict__ weight, float eps, int mode,
+                             int group, const float* __restrict__ static_scale,
+                             uint8_t* __restrict__ out, int64_t out_stride,
+                             float* __restrict__ scales, int64_t T, int H) {
+  const int lane = lane_id();
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
+  if (row >= T) return;
+  const int nvec = H >> 3;
+
+  RowVecs<NV> a, r, w;
+  load_row<NV, true>(a, x + row * x_stride, nvec, lane);
+  if (kResidual) load_row<NV, true>(r, residual + row * res_stride, nvec, lane);
+  load_row<NV, false>(w, weight, nvec, lane);
+  const float static_inv = mode == RRA_Q_STATIC ? 1.0f / static_scale[0] : 0.0f;
+
+  if (kResidual) {
+    // z = bf16(x + residual): the fp32 sum of two bf16 values rounds once.
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        a.v[i][k] = pack_bf16x2(bf16_lo(a.v[i][k]) + bf16_lo(r.v[i][k]),
+                                bf16_hi(a.v[i][k]) + bf16_hi(r.v[i][k]));
+    }
+    store_row(residual + row * res_stride, a, nvec, lane);
+  }
+
+  float* scale_row = nullptr;
+  if (mode == RRA_Q_PER_TOKEN) scale_row = scales + row;
+  if (mode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / group);
+  rmsnorm_emit<NV>(a, w, eps, H, nvec, lane, mode, group, static_inv, out + row * out_stride,
+                   scale_row);
+}
+
+template <int NVQ, int NVKV>
+__global__ void __launch_bounds__(kBlock)
+    dual_rmsnorm_quant_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
+                              const uint16_t* __restrict__ q_w, float eps_q,
+                              const uint16_t* __restrict__ kv, int64_t kv_stride,
+                              const uint16_t* __restrict__ kv_w, float eps_kv, int mode,
+                              int group, void* __restrict__ q_out, int64_t q_out_stride,
+                              float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
+                              int64_t kv_out_stride, int64_t T, int Hq, int Hkv) {
+  const int lane = lane_id();
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
+  if (row >= T) return;
+  const int nq = Hq >> 3, nkv = Hkv >> 3;
+
+  // Issue every load of the token before either reduction.
+  RowVecs<NVQ> zq, wq;
+  RowVecs<NVKV> zkv, wkv;
+  load_row<NVQ, true>(zq, q + row * q_stride, nq, lane);
+  load_row<NVKV, true>(zkv, kv + row * kv_stride, nkv, lane);
+  load_row<NVQ, false>(wq, q_w, nq, lane);
+  load_row<NVKV, false>(wkv, kv_w, nkv, lane);
+
+  void* qo;
+  float* scale_row = nullptr;
+  if (mode == RRA_Q_NONE) {
+    qo = static_cast<uint16_t*>(q_out) + row * q_out_stride;
+  } else {
+    qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
+    scale_row = mode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / group);
+  }
+  rmsnorm_emit<NVQ>(zq, wq, eps_q, Hq, nq, lane, mode, group, 0.0f, qo, scale_row);
+  rmsnorm_emit<NVKV>(zkv, wkv, eps_kv, Hkv, nkv, lane, RRA_Q_NONE, 0, 0.0f,
+                     kv_out + row * kv_out_stride, nullptr);
+}
+
+template <bool kResidual>
+static int launch_add_rmsnorm(int nv, dim3 grid, hipStream_t st, const uint16_t* x,
+                              int64_t xs, uint16_t* res, int64_t rs, const uint16_t* w,
+                              float eps, int mode, int group, const float* sscale, uint8_t* out,
+                              int64_t os, float* scales, int64_t T, int H) {
+#define RRA_NORM_CASE(N)                                                                   \
+  case N:                                                                                  \
+    hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, kResidual>), grid, dim3(kBlock), 0, st, \
+                       x, xs, res, rs, w, eps, mode, group, sscale, out, os, scales, T, H); \
+    break;
+  switch (nv) {
+    RRA_NORM_CASE(1)
+    RRA_NORM_CASE(2)
+    RRA_NORM_CASE(3)
+    RRA_NORM_CASE(4)
+    RRA_NORM_CASE(5)
+    RRA_NORM_CASE(6)
+    RRA_NORM_CASE(7)
+    RRA_NORM_CASE(8)
+    RRA_NORM_CASE(9)
+    RRA_NORM_CASE(10)
+    RRA_NORM_CASE(11)
+    RRA_NORM_CASE(12)
+    RRA_NORM_CASE(13)
+    RRA_NORM_CASE(14)
+    RRA_NORM_CASE(15)
+    RRA_NORM_CASE(16)
+    default:
+      return RRA_ERR_UNSUPPORTED;
+  }
+#undef RRA_NORM_CASE
+  return launch_status();
+}
+
+}  // namespace rra
+
+using namespace rra;
+
+extern "C" int fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint16_t* residual,
+                                       int64_t residual_stride, const uint16_t* weight,
+                                       float eps, int quant_mode, int group_size,
+                                       const float* static_scale, uint8_t* out,
+                                       int64_t out_stride, float* scales, int64_t T, int64_t H,
+                                       void* stream) {
+  RRA_REQUIRE(T >= 0 && H > 0, RRA_ERR_SHAPE);
+  RRA_REQUIRE(x && weight && out, RRA_ERR_NULL);
+  RRA_REQUIRE(x_stride >= H && out_stride >= H, RRA_ERR_SHAPE);
+  RRA_REQUIRE(!residual || residual_stride >= H, RRA_ERR_SHAPE);
+  RRA_REQUIRE(H % 8 == 0 && H <= 8192, RRA_ERR_UNSUPPORTED);
+  switch (quant_mode) {
+    case RRA_Q_STATIC:
+      RRA_REQUIRE(static_scale, RRA_ERR_NULL);
+      RRA_REQUIRE(aligned(static_scale, 4), RRA_ERR_ALIGN);
+      break;
+    case RRA_Q_PER_TOKEN:
+      RRA_REQUIRE(scales, RRA_ERR_NULL);
+      break;
+    case RRA_Q_PER_GROUP:
+      RRA_REQUIRE(group_ok(group_size), RRA_ERR_UNSUPPORTED);
+      RRA_REQUIRE(H % group_size == 0, RRA_ERR_SHAPE);
+      RRA_REQUIRE(scales, RRA_ERR_NULL);
+      break;
+    default:
+      return RRA_ERR_UNSUPPORTED;
+  }
+  RRA_REQUIRE(vec_ok(x, x_stride) && aligned(weight, 16), RRA_ERR_ALIGN);
+  RRA_REQUIRE(!residual || vec_ok(residual, residual_stride), RRA_ERR_ALIGN);
+  RRA_REQUIRE(aligned(out, 8) && out_stride % 8 == 0, RRA_ERR_ALIGN);
+  RRA_REQUIRE(!scales || aligned(scales, 4), RRA_ERR_ALIGN);
+  if (T == 0) return RRA_OK;
+
+  const int nv = static_cast<int>(ceil_div(H, 8 * kWave));
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock)));
+  const int g = quant_mode == RRA_Q_PER_GROUP ? group_size : 0;
+  if (residual)
+    return launch_add_rmsnorm<true>(nv, grid, as_stream(stream), x, x_stride, residual,
+                                    residual_stride, weight, eps, quant_mode, g, static_scale,
+                                    out, out_stride, scales, T, static_cast<int>(H));
+  return launch_add_rmsnorm<false>(nv, grid, as_stream(stream), x, x_stride, nullptr, 0, weight,
+                                   eps, quant_mode, g, static_scale, out, out_stride, scales, T,
+                                   static_cast<int>(H));
+}
+
+extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_weight,
+                                  float eps_q, const uint16_t* kv, int64_t kv_stride,
+                                  const uint16_t* kv_weight, float eps_kv, int q_quant_mode,
+                                  int group_size, void* q_out, int64_t q_out_stride,
+                                  float* q_scales, uint16_t* kv_out, int64_t kv_out_stride,
+                                  int64_t T, int64_t Hq, int64_t Hkv, void* stream) {
+  RRA_REQUIRE(T >= 0 && Hq > 0 && Hkv > 0, RRA_ERR_SHAPE);
+  RRA_REQUIRE(q && q_weight && kv && kv_weight && q_out && kv_out, RRA_ERR_NULL);
+  RRA_REQUIRE(q_stride >= Hq && kv_stride >= Hkv && q_out_stride >= Hq && kv_out_stride >= Hkv,
+              RRA_ERR_SHAPE);
+  RRA_REQUIRE(Hq % 8 == 0 && Hkv % 8 == 0 && Hq <= 2048 && Hkv <= 1024, RRA_ERR_UNSUPPORTED);
+  switch (q_quant_mode) {
+    case RRA_Q_NONE:
+      RRA_REQUIRE(vec_ok(q_out, q_out_stride), RRA_ERR_ALIGN);
+      break;
+    case RRA_Q_PER_TOKEN:
+      RRA_REQUIRE(q_scales, RRA_ERR_NULL);
+      RRA_REQUIRE(aligned(q_out, 8) && q_out_stride % 8 == 0, RRA_ERR_ALIGN);
+      break;
+    case RRA_Q_PER_GROUP:
+      RRA_REQUIRE(group_ok(group_size), RRA_ERR_UNSUPPORTED);
+      RRA_REQUIRE(Hq % group_size == 0, RRA_ERR_SHAPE);
+      RRA_REQUIRE(q_scales, RRA_ERR_NULL);
+      RRA_REQUIRE(aligned(q_out, 8) && q_out_stride % 8 == 0, RRA_ERR_ALIGN);
+      break;
+    default:
+      return RRA_ERR_UNSUPPORTED;
+  }
+  RRA_REQUIRE(vec_ok(q, q_stride) && vec_ok(kv, kv_stride) && vec_ok(kv_out, kv_out_stride),
+              RRA_ERR_ALIGN);
+  RRA_REQUIRE(aligned(q_weight, 16) && aligned(kv_weight, 16), RRA_ERR_ALIGN);
+  RRA_REQUIRE(!q_scales || aligned(q_scales, 4), RRA_ERR_ALIGN);
+  if (T == 0) return RRA_OK;
+
+  const int nvq = static_cast<int>(ceil_div(Hq, 8 * kWave));
+  const int nvkv = static_cast<int>(ceil_div(Hkv, 8 * kWave));
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock)));
+  const hipStream_t st = as_stream(stream);
+  const int g = q_quant_mode == RRA_Q_PER_GROUP ? group_size : 0;
+#define RRA_DUAL_CASE(A, B)                                                                   \
+  if (nvq == A && nvkv == B) {                                                                \
+    hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B>), grid, dim3(kBlock), 0, st, q,       \
+                       q_stride, q_weight, eps_q, kv, kv_stride, kv_weight, eps_kv,            \
+                       q_quant_mode, g, q_out, q_out_stride, q_scales, kv_out, kv_out_stride, \
+                       T, static_cast<int>(Hq), static_cast<int>(Hkv));                       \
+    return launch_status();                                                                   \
+  }
+  RRA_DUAL_CASE(1, 1)
+  RRA_DUAL_CASE(2, 1)
+  RRA_DUAL_CASE(3, 1)
+  RRA_DUAL_CASE(4, 1)
+  RRA_DUAL_CASE(1, 2)
+  RRA_DUAL_CASE(2, 2)
+  RRA_DUAL_CASE(3, 2)
+  RRA_DUAL_CASE(4, 2)
+#undef RRA_DUAL_CASE
+  return RRA_ERR_UNSUPPORTED;
+}

@@ -1,0 +1,40 @@
+// Host-side argument checks shared by the C-ABI entry points.  Everything here
+// runs before a launch; a failed check returns an rra_status and enqueues
+// nothing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rra.h"
+
+namespace rra {
+
+inline bool aligned(const void* p, uintptr_t bytes) {
+  return (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+
+// A bf16 tensor accessed with 16-byte vectors: base 16-byte aligned and a row
+// stride that keeps every row 16-byte aligned.
+inline bool vec_ok(const void* p, int64_t stride_elems) {
+  return aligned(p, 16) && stride_elems % 8 == 0;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? RRA_OK : RRA_ERR_LAUNCH;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Per-group scales are reduced inside one 16-lane row (group 128 = 16 lanes x
+// 8 values) or one 8-lane half row (group 64).
+inline bool group_ok(int g) { return g == 64 || g == 128; }
+
+}  // namespace rra
+
+#define RRA_REQUIRE(cond, status) \
+  do {                            \
+    if (!(cond)) return (status); \
+  } while (0)

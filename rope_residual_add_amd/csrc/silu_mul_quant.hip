@@ -1,0 +1,146 @@
+// SiLU-and-Mul + FP8 quant for gfx950.
+//
+// Operation: vLLM design page "Fusion torch.compile passes", section
+// "SiLU+Mul + Quantization (fuse_act_quant)": the gate-up activation
+// silu(gate) * up followed by static or per-group FP8 quantization, without
+// writing the activation to memory.
+//
+// Mapping: each wavefront owns one chunk of NV*512 output columns of one row.
+// Lane l handles vectors l, l + 64, ... of the chunk (8 columns each) and loads
+// the matching 16-byte vectors of the gate half and of the up half, so every
+// load instruction of the wave reads 1 KiB of contiguous memory.  A group of
+// 128 (64) outputs is 16 (8) consecutive lanes of one vector: the group amax is
+// a DPP row reduction.
+//
+// Arithmetic budget: at the HBM roofline this kernel has about 25 VALU slots
+// per output element on MI355X (256 CUs x 64 lanes x 2.4 GHz against 10 bytes
+// of traffic per element at 8 TB/s).  A correctly rounded expf and fp32 divide
+// would use more than that, so silu uses the hardware exp2 and reciprocal:
+// silu(g) * u = g * u * rcp(1 + exp2(-g * log2(e))), relative error ~1e-6,
+// which moves an FP8 code only for values within that distance of a rounding
+// midpoint.
+#include "rra_device.hpp"
+#include "rra_host.hpp"
+
+namespace rra {
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ void silu8(u32x4 g, u32x4 u, float a[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    a[2 * k] = silu_mul(bf16_lo(g[k]), bf16_lo(u[k]));
+    a[2 * k + 1] = silu_mul(bf16_hi(g[k]), bf16_hi(u[k]));
+  }
+}
+
+template <int NV>
+__global__ void __launch_bounds__(kBlock)
+    silu_mul_quant_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int mode,
+                          int group, const float* __restrict__ static_scale,
+                          uint8_t* __restrict__ out, int64_t out_stride,
+                          float* __restrict__ scales, int64_t T, int I, int chunks) {
+  const int lane = lane_id();
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
+  const int64_t row = wid / chunks;
+  if (row >= T) return;
+  const int chunk = static_cast<int>(wid - row * chunks);
+  const int nvec = I >> 3;
+  const uint16_t* gate = in + row * in_stride;
+  const uint16_t* up = gate + I;
+
+  u32x4 g[NV], u[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = (chunk * NV + i) * kWave + lane;
+    if (idx < nvec) {
+      g[i] = ld_stream(gate + idx * 8);
+      u[i] = ld_stream(up + idx * 8);
+    } else {
+      g[i] = u32x4{0u, 0u, 0u, 0u};
+      u[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  uint8_t* o = out + row * out_stride;
+  if (mode == RRA_Q_STATIC) {
+    const float f = 1.0f / static_scale[0];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = (chunk * NV + i) * kWave + lane;
+      float a[8];
+      silu8(g[i], u[i], a);
+      if (idx < nvec)
+        st_stream(o + idx * 8,
+                  u32x2{pack_e4m3x4(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
+                        pack_e4m3x4(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
+    }
+    return;
+  }
+
+  // RRA_Q_PER_GROUP
+  float* scale_row = scales + row * (I / group);
+  const int lanes_per_group = group / 8;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = (chunk * NV + i) * kWave + lane;
+    float a[8];
+    silu8(g[i], u[i], a);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(a[j]));
+    m = group == 128 ? max16(m) : max8(m);
+    const float s = m / 448.0f;
+    const float f = inv_scale(s);
+    if (idx < nvec) {
+      if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = s;
+      st_stream(o + idx * 8, u32x2{pack_e4m3x4(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
+                                   pack_e4m3x4(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
+    }
+  }
+}
+
+constexpr int kSiluNV = 4;  // 2048 output columns per wavefront
+
+}  // namespace rra
+
+using namespace rra;
+
+extern "C" int silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_mode,
+                              int group_size, const float* static_scale, uint8_t* out,
+                              int64_t out_stride, float* scales, int64_t T, int64_t I,
+                              void* stream) {
+  RRA_REQUIRE(T >= 0 && I > 0, RRA_ERR_SHAPE);
+  RRA_REQUIRE(in && out, RRA_ERR_NULL);
+  RRA_REQUIRE(in_stride >= 2 * I && out_stride >= I, RRA_ERR_SHAPE);
+  RRA_REQUIRE(I % 8 == 0 && I <= (int64_t(1) << 30), RRA_ERR_UNSUPPORTED);
+  switch (quant_mode) {
+    case RRA_Q_STATIC:
+      RRA_REQUIRE(static_scale, RRA_ERR_NULL);
+      RRA_REQUIRE(aligned(static_scale, 4), RRA_ERR_ALIGN);
+      break;
+    case RRA_Q_PER_GROUP:
+      RRA_REQUIRE(group_ok(group_size), RRA_ERR_UNSUPPORTED);
+      RRA_REQUIRE(I % group_size == 0, RRA_ERR_SHAPE);
+      RRA_REQUIRE(scales, RRA_ERR_NULL);
+      RRA_REQUIRE(aligned(scales, 4), RRA_ERR_ALIGN);
+      break;
+    default:
+      return RRA_ERR_UNSUPPORTED;
+  }
+  RRA_REQUIRE(vec_ok(in, in_stride), RRA_ERR_ALIGN);
+  RRA_REQUIRE(aligned(out, 8) && out_stride % 8 == 0, RRA_ERR_ALIGN);
+  if (T == 0) return RRA_OK;
+
+  const int64_t chunks = ceil_div(I, 8 * kWave * kSiluNV);
+  const int64_t blocks = ceil_div(T * chunks, kWavesPerBlock);
+  RRA_REQUIRE(blocks <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
+  hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kBlock), 0, as_stream(stream), in, in_stride, quant_mode,
+                     quant_mode == RRA_Q_PER_GROUP ? group_size : 0, static_scale, out,
+                     out_stride, scales, T, static_cast<int>(I), static_cast<int>(chunks));
+  return launch_status();
+}

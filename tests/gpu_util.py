@@ -1,0 +1,99 @@
+"""Helpers for the GPU parity tests: host <-> device transfer of bit patterns
+and the acceptance bars.
+
+Bars: FP8 codes may differ from the oracle by at most one code (adjacent
+values) on at most 1e-4 of all codes; bf16 outputs and fp32 scales within
+rtol 1e-2 (bf16 outputs also atol 1e-5, for values that cancel to near zero);
+integer and index work (which slots are written, bit copies) bit-exact."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+from helpers import bf16_to_f64, code_ulp_diff
+
+CODE_MISMATCH_BUDGET = 1e-4
+RTOL = 1e-2
+ATOL_BF16 = 1e-5
+
+
+def torch_mod():
+    import torch
+
+    return torch
+
+
+def require_gpu():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(msg: str) -> None:
+    """Name the case on stdout before it touches the GPU."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(a: np.ndarray):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(a: np.ndarray):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host_bf16(t) -> np.ndarray:
+    torch = torch_mod()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_u8(t) -> np.ndarray:
+    torch = torch_mod()
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
+def host_f32(t) -> np.ndarray:
+    return t.contiguous().cpu().numpy()
+
+
+def assert_codes(gpu: np.ndarray, ref: np.ndarray, what: str) -> dict:
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    d = code_ulp_diff(gpu, ref)
+    n = d.size
+    bad = int(np.count_nonzero(d))
+    stats = dict(what=what, codes=n, mismatches=bad, max_ulp=int(d.max()) if n else 0)
+    print(stats, flush=True)
+    assert stats["max_ulp"] <= 1, stats
+    assert bad <= CODE_MISMATCH_BUDGET * n, stats
+    return stats
+
+
+def assert_scales(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
+    assert gpu.shape == ref.shape
+    ok = np.isclose(gpu.astype(np.float64), ref.astype(np.float64), rtol=RTOL, atol=0)
+    assert ok.all(), (what, np.argwhere(~ok)[:5])
+    exact = np.mean(gpu.view(np.uint32) == ref.view(np.uint32)) if gpu.size else 1.0
+    print(dict(what=what, scales=gpu.size, bit_exact_fraction=float(exact)), flush=True)
+
+
+def assert_bf16(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
+    assert gpu.shape == ref.shape
+    g, r = bf16_to_f64(gpu), bf16_to_f64(ref)
+    ok = np.isclose(g, r, rtol=RTOL, atol=ATOL_BF16)
+    assert ok.all(), (what, np.argwhere(~ok)[:5], g[~ok][:5], r[~ok][:5])
+    exact = float(np.mean(gpu == ref)) if gpu.size else 1.0
+    print(dict(what=what, values=gpu.size, bit_exact_fraction=exact), flush=True)
+
+
+def sample_rows(T: int, n: int = 256, seed: int = 0) -> np.ndarray:
+    """Sorted sample of row indices (always the first and last row)."""
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(T, size=n - 2, replace=False)
+    return np.unique(np.concatenate([[0, T - 1], idx]))

@@ -1,0 +1,138 @@
+"""GPU parity: fused_add_rmsnorm_quant against the CPU oracle.
+
+Covers the static-scale workload (H=1024, eps 1e-6, scale 0.05, T in {16,
+8192}), the per-token workload (Llama-3-8B width 4096, eps 1e-5, T in {1, 32,
+512, 8192}), per-group 128/64, no residual, ragged widths that leave masked
+lanes, strided views and T = 0.  At T = 8192 the oracle checks a sample of
+rows; properties that hold at any size (residual = bf16(x + residual), a row
+amax of exactly 448) are checked on every row."""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import (assert_codes, assert_scales, dev_bf16, host_bf16, host_f32, host_u8,
+                      require_gpu, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rra():
+    require_gpu()
+    import rope_residual_add_amd as r
+
+    r.lib()
+    return r
+
+
+def _strided(a: np.ndarray, pad_left: int, pad_right: int):
+    """Device bf16 view [T, H] inside a wider [T, pad_left + H + pad_right] buffer."""
+    T, H = a.shape
+    wide = np.zeros((T, pad_left + H + pad_right), np.uint16)
+    wide[:, pad_left:pad_left + H] = a
+    return dev_bf16(wide)[:, pad_left:pad_left + H]
+
+
+def run(rra, oracle, T, H, mode, g=0, eps=1e-5, static=0.05, residual=True, tag="norm_token",
+        strided=False):
+    import torch
+
+    say(f"[norm] T={T} H={H} mode={mode} g={g} residual={residual} strided={strided}")
+    d = workloads.norm_inputs(T, H, tag=tag)
+    if strided:
+        x = _strided(d["x"], 32, 40)
+        r = _strided(d["residual"], 8, 0) if residual else None
+        out_wide = torch.empty((T, H + 16), dtype=torch.float8_e4m3fn, device="cuda")
+        out = out_wide[:, 8:8 + H]
+    else:
+        x = dev_bf16(d["x"])
+        r = dev_bf16(d["residual"]) if residual else None
+        out = None
+    r_before = r.clone() if residual else None
+    w = dev_bf16(d["weight"])
+    ss = torch.tensor([static], dtype=torch.float32, device="cuda") if mode == 1 else None
+    out, scales = rra.fused_add_rmsnorm_quant(x, r, w, eps, mode, g, ss, out=out)
+    torch.cuda.synchronize()
+
+    rows = sample_rows(T)
+    ref_codes, ref_scales, ref_res = oracle.fused_add_rmsnorm_quant(
+        d["x"][rows], d["residual"][rows] if residual else None, d["weight"], eps, mode, g, static)
+    assert_codes(host_u8(out)[rows], ref_codes, f"codes T={T} H={H} mode={mode}")
+    if scales is not None:
+        assert_scales(host_f32(scales)[rows], ref_scales, "scales")
+    if residual:
+        assert np.array_equal(host_bf16(r)[rows], ref_res)
+        # any size: the stored residual is bf16(x + old residual) on every row
+        full = (x.float() + r_before.float()).to(torch.bfloat16)
+        assert torch.equal(full.view(torch.int16), r.view(torch.int16))
+    if mode == 2 and T:
+        # any size: every row reaches the largest code
+        amax = out.float().abs().amax(dim=1)
+        assert torch.all(amax == 448.0)
+    return out, scales
+
+
+@pytest.mark.parametrize("T", workloads.NORM_STATIC.Ts)
+def test_static_workload(rra, oracle, T):
+    c = workloads.NORM_STATIC
+    run(rra, oracle, T, c.H, 1, eps=c.eps, static=c.static_scale, tag="norm_static")
+
+
+@pytest.mark.parametrize("T", workloads.NORM_TOKEN.Ts)
+def test_per_token_workload(rra, oracle, T):
+    c = workloads.NORM_TOKEN
+    run(rra, oracle, T, c.H, 2, eps=c.eps)
+
+
+@pytest.mark.parametrize("T,g", [(7, 128), (8192, 128), (33, 64), (512, 64)])
+def test_per_group(rra, oracle, T, g):
+    run(rra, oracle, T, 4096, 3, g)
+
+
+@pytest.mark.parametrize("mode,g", [(1, 0), (2, 0), (3, 128)])
+def test_no_residual(rra, oracle, mode, g):
+    run(rra, oracle, 33, 4096, mode, g, residual=False)
+
+
+@pytest.mark.parametrize("H,mode,g", [(8, 2, 0), (1000, 1, 0), (2880, 2, 0), (2880, 3, 64),
+                                      (5120, 3, 128), (8192, 2, 0), (7168, 3, 128)])
+def test_widths(rra, oracle, H, mode, g):
+    run(rra, oracle, 65, H, mode, g)
+
+
+@pytest.mark.parametrize("mode,g", [(2, 0), (3, 128), (1, 0)])
+def test_strided_views(rra, oracle, mode, g):
+    run(rra, oracle, 19, 1024, mode, g, strided=True)
+
+
+def test_empty(rra):
+    import torch
+
+    say("[norm] T=0")
+    x = torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(1024, dtype=torch.bfloat16, device="cuda")
+    out, scales = rra.fused_add_rmsnorm_quant(x, x.clone(), w, 1e-6, 2)
+    assert out.shape == (0, 1024) and scales.shape == (0,)
+
+
+def test_zero_rows(rra):
+    """An all-zero row gets scale 0 and all-zero codes (no NaN)."""
+    import torch
+
+    say("[norm] zero rows")
+    x = torch.zeros((8, 512), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(512, dtype=torch.bfloat16, device="cuda")
+    for mode, g in ((2, 0), (3, 64)):
+        out, scales = rra.fused_add_rmsnorm_quant(x, None, w, 1e-6, mode, g)
+        torch.cuda.synchronize()
+        assert torch.all(scales == 0)
+        assert torch.all((out.view(torch.uint8) & 0x7F) == 0)
+
+
+def test_error_is_raised(rra):
+    import torch
+
+    x = torch.zeros((4, 1000), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(1000, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rra.RRAError):
+        rra.fused_add_rmsnorm_quant(x, None, w, 1e-6, 3, 128)

@@ -1,0 +1,158 @@
+"""The C-ABI library: it loads, exports every function include/rra.h declares,
+and rejects bad arguments on the host before anything is launched.
+
+These tests make no compute call: every call below either fails validation
+(NULL, misaligned or out-of-range arguments, with fake pointers that are never
+dereferenced) or has T == 0, which returns before any HIP call."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rra.h")
+
+OK, ENULL, ESHAPE, EALIGN, EUNSUP = 0, -1, -2, -3, -4
+A = 0x10000  # a 16-byte aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def rra():
+    import rope_residual_add_amd as r
+
+    if not os.path.exists(r.LIBRARY_PATH):
+        from rope_residual_add_amd import build
+
+        build.build()
+    r.lib()
+    return r
+
+
+def declared_functions() -> list:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fused_add_rmsnorm_quant", "silu_mul_quant", "rope_kv_write", "dual_rmsnorm_quant",
+              "rope_cos_sin_cache", "rra_e4m3fn_encode", "rra_abi_version", "rra_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(rra):
+    out = subprocess.run(["nm", "-D", "--defined-only", rra.LIBRARY_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+    assert set(rra.EXPORTS) == set(declared_functions())
+
+
+def test_version_and_status_strings(rra):
+    assert rra.abi_version() == 1
+    for s in (OK, ENULL, ESHAPE, EALIGN, EUNSUP, -5):
+        assert rra.status_string(s) and rra.status_string(s) != "unknown status"
+    assert rra.status_string(-99) == "unknown status"
+
+
+def norm(L, **kw):
+    a = dict(x=A, xs=4096, res=A, rs=4096, w=A, eps=1e-5, mode=2, g=0, ss=None, out=A, os=4096,
+             sc=A, T=4, H=4096)
+    a.update(kw)
+    return L.fused_add_rmsnorm_quant(a["x"], a["xs"], a["res"], a["rs"], a["w"], a["eps"],
+                                     a["mode"], a["g"], a["ss"], a["out"], a["os"], a["sc"],
+                                     a["T"], a["H"], None)
+
+
+def test_norm_validation(rra):
+    L = rra.lib()
+    assert norm(L, T=0) == OK
+    assert norm(L, x=None) == ENULL
+    assert norm(L, sc=None) == ENULL  # per-token needs scales
+    assert norm(L, mode=1, ss=None, T=0) == ENULL  # static needs the scale pointer
+    assert norm(L, T=-1) == ESHAPE
+    assert norm(L, xs=100) == ESHAPE
+    assert norm(L, H=4100, xs=4104, rs=4104, os=4104) == EUNSUP  # H % 8
+    assert norm(L, H=8200, xs=8200, rs=8200, os=8200) == EUNSUP  # above the register cap
+    assert norm(L, mode=3, g=96) == EUNSUP
+    assert norm(L, mode=3, g=128, H=4032, xs=4032, rs=4032, os=4032) == ESHAPE  # g does not divide H
+    assert norm(L, mode=0) == EUNSUP
+    assert norm(L, mode=7) == EUNSUP
+    assert norm(L, x=A + 8) == EALIGN
+    assert norm(L, xs=4100) == EALIGN
+    assert norm(L, out=A + 4) == EALIGN
+    assert norm(L, res=None, rs=0, T=0) == OK
+
+
+def test_silu_validation(rra):
+    L = rra.lib()
+    f = lambda **k: L.silu_mul_quant(k.get("inp", A), k.get("s", 28672), k.get("mode", 3),
+                                     k.get("g", 128), k.get("ss", None), k.get("out", A),
+                                     k.get("os", 14336), k.get("sc", A), k.get("T", 2),
+                                     k.get("I", 14336), None)
+    assert f(T=0) == OK
+    assert f(inp=None) == ENULL
+    assert f(sc=None) == ENULL
+    assert f(s=14336) == ESHAPE
+    assert f(g=32) == EUNSUP
+    assert f(mode=2) == EUNSUP  # per-token is not offered for this op
+    assert f(I=1000, s=2000, os=1000) == ESHAPE  # 128 does not divide 1000
+    assert f(inp=A + 2) == EALIGN
+    assert f(mode=1, ss=None) == ENULL
+
+
+def test_rope_validation(rra):
+    L = rra.lib()
+
+    def f(**k):
+        a = dict(pos=A, q=A, qs=4096, qo=A, qos=4096, k=A, ks=1024, v=A, vs=1024, cs=A, mp=8192,
+                 sm=A, kc=A, vc=A, T=4, Hq=32, Hkv=8, D=128, rd=128, bs=16, nb=4096, neox=1)
+        a.update(k)
+        return L.rope_kv_write(a["pos"], a["q"], a["qs"], a["qo"], a["qos"], a["k"], a["ks"],
+                               a["v"], a["vs"], a["cs"], a["mp"], a["sm"], a["kc"], a["vc"],
+                               a["T"], a["Hq"], a["Hkv"], a["D"], a["rd"], a["bs"], a["nb"],
+                               a["neox"], None)
+
+    assert f(T=0) == OK
+    assert f(sm=None) == ENULL
+    assert f(qs=2048) == ESHAPE
+    assert f(D=96, qs=3072, qos=3072, ks=768, vs=768, rd=96) == EUNSUP
+    assert f(rd=64) == EUNSUP
+    assert f(neox=0) == EUNSUP
+    assert f(kc=A + 2) == EALIGN
+    assert f(pos=A + 4) == EALIGN
+    assert f(bs=0) == ESHAPE
+    assert L.rope_cos_sin_cache(None, 8192, 128, 5e5, None) == ENULL
+    assert L.rope_cos_sin_cache(A, 8192, 127, 5e5, None) == ESHAPE
+    assert L.rope_cos_sin_cache(A, 8192, 128, -1.0, None) == EUNSUP
+    assert L.rope_cos_sin_cache(A, 0, 128, 5e5, None) == OK
+
+
+def test_dual_validation(rra):
+    L = rra.lib()
+
+    def f(**k):
+        a = dict(q=A, qs=1536, qw=A, eq=1e-6, kv=A, kvs=512, kvw=A, ekv=1e-6, mode=3, g=128,
+                 qo=A, qos=1536, sc=A, kvo=A, kvos=512, T=2, Hq=1536, Hkv=512)
+        a.update(k)
+        return L.dual_rmsnorm_quant(a["q"], a["qs"], a["qw"], a["eq"], a["kv"], a["kvs"],
+                                    a["kvw"], a["ekv"], a["mode"], a["g"], a["qo"], a["qos"],
+                                    a["sc"], a["kvo"], a["kvos"], a["T"], a["Hq"], a["Hkv"], None)
+
+    assert f(T=0) == OK
+    assert f(kvo=None) == ENULL
+    assert f(sc=None) == ENULL
+    assert f(mode=1) == EUNSUP
+    assert f(Hq=4096, qs=4096, qos=4096) == EUNSUP
+    assert f(kv=A + 8, T=0) == EALIGN  # alignment is checked before the T == 0 early return
+    assert f(g=64, Hq=1000, qs=1000, qos=1000) == ESHAPE  # 64 does not divide 1000
+
+
+def test_e4m3_diag_validation(rra):
+    L = rra.lib()
+    assert L.rra_e4m3fn_encode(None, A, 4, None) == ENULL
+    assert L.rra_e4m3fn_encode(A + 4, A, 4, None) == EALIGN
+    assert L.rra_e4m3fn_encode(A, A, 0, None) == OK
