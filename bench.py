@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Throughput of the four fused kernels on one MI355X.
+
+One step is one pass over the whole fused path at T tokens (default 8192):
+  fused_add_rmsnorm_quant  residual add + RMSNorm + per-token FP8, hidden 4096 (Llama-3-8B)
+  silu_mul_quant           SiLU-and-Mul + per-group-128 FP8, intermediate 14336 (Llama-3-8B)
+  rope_kv_write            neox RoPE (32 q / 8 kv heads of 128, theta 5e5) + paged KV write
+                           into a [4096, 16, 8, 128] bf16 cache through a slot mapping
+  dual_rmsnorm_quant       MLA q (1536, per-group-128 FP8) / kv (512, bf16) RMSNorm (DeepSeek-V3)
+on seeded synthetic inputs already resident in HBM.  The step streams about
+1.1 GB, several times the 256 MB last-level cache, so every kernel starts on
+cold data.
+
+Bandwidth is counted in ALGORITHMIC bytes: each input read once and each
+output written once (per token: 7H + 4 for the norm, 5I + 4I/128 for SiLU,
+24592 for RoPE + KV write, 6704 for the MLA norm; plus the weights once per
+launch).  Per-kernel durations come from HIP events recorded on the stream the
+kernels run on, around every launch of the timed region.
+
+Prints ONE JSON line on stdout (everything else goes to stderr).  With
+--sweep it also times each kernel alone at several token counts, rotating
+over enough buffer sets that every launch reads cold data, and adds the table
+under "sweep".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+METRIC = "achieved HBM GB/s (% of MI355X peak) and tokens/s per fused kernel, T=8192"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---- algorithmic bytes ---------------------------------------------------------
+
+H_NORM, I_SILU, G = 4096, 14336, 128
+ROPE_HQ, ROPE_HKV, ROPE_D = 32, 8, 128
+MLA_HQ, MLA_HKV = 1536, 512
+
+BYTES_PER_TOKEN = {
+    "fused_add_rmsnorm_quant": 7 * H_NORM + 4,
+    "silu_mul_quant": 5 * I_SILU + 4 * (I_SILU // G),
+    "rope_kv_write": 2 * 2 * ROPE_HQ * ROPE_D + 2 * 2 * ROPE_HKV * ROPE_D + 2 * 2 * ROPE_HKV * ROPE_D
+    + 16,
+    "dual_rmsnorm_quant": 2 * MLA_HQ + 2 * MLA_HKV + MLA_HQ + 4 * (MLA_HQ // G) + 2 * MLA_HKV,
+}
+BYTES_PER_LAUNCH = {  # weights, read once per launch
+    "fused_add_rmsnorm_quant": 2 * H_NORM,
+    "silu_mul_quant": 0,
+    "rope_kv_write": 0,
+    "dual_rmsnorm_quant": 2 * (MLA_HQ + MLA_HKV),
+}
+KERNELS = tuple(BYTES_PER_TOKEN)
+
+
+def algo_bytes(name: str, T: int) -> int:
+    return BYTES_PER_TOKEN[name] * T + BYTES_PER_LAUNCH[name]
+
+
+# ---- GPU side ------------------------------------------------------------------
+
+def make_launchers(T: int, salt: int = 0, rope_state=None, only=KERNELS):
+    """Allocate one input/output set at T tokens for each kernel in `only` and
+    return {name: zero-argument launch function}.  `rope_state` = (key_cache,
+    value_cache, cos_sin) shares one cache pair and table across sets."""
+    import torch
+
+    import rope_residual_add_amd as rra
+    import workloads
+
+    dev = "cuda"
+    L = {}
+
+    if "fused_add_rmsnorm_quant" in only:
+        d = workloads.device_norm_inputs(T, H_NORM, dev, salt)
+        out = torch.empty((T, H_NORM), dtype=torch.float8_e4m3fn, device=dev)
+        sc = torch.empty((T,), dtype=torch.float32, device=dev)
+        L["fused_add_rmsnorm_quant"] = lambda d=d, out=out, sc=sc: rra.fused_add_rmsnorm_quant(
+            d["x"], d["residual"], d["weight"], 1e-5, rra.Q_PER_TOKEN, 0, None, out, sc)
+
+    if "silu_mul_quant" in only:
+        d = workloads.device_silu_inputs(T, I_SILU, dev, salt)
+        out = torch.empty((T, I_SILU), dtype=torch.float8_e4m3fn, device=dev)
+        sc = torch.empty((T, I_SILU // G), dtype=torch.float32, device=dev)
+        L["silu_mul_quant"] = lambda d=d, out=out, sc=sc: rra.silu_mul_quant(
+            d["inp"], rra.Q_PER_GROUP, G, None, out, sc)
+
+    if "rope_kv_write" in only:
+        cfg = workloads.ROPE
+        d = workloads.device_rope_inputs(T, cfg, dev, salt, with_cache=rope_state is None)
+        if rope_state is None:
+            cs = rra.rope_cos_sin_cache(cfg.max_pos, cfg.rot_dim, cfg.theta, device=dev)
+            rope_state = (d["key_cache"], d["value_cache"], cs)
+        kc, vc, cs = rope_state
+        L["rope_kv_write"] = lambda d=d, kc=kc, vc=vc, cs=cs: rra.rope_kv_write(
+            d["positions"], d["q"], d["k"], d["v"], cs, d["slot_mapping"], kc, vc)
+        L["_rope_state"] = rope_state
+
+    if "dual_rmsnorm_quant" in only:
+        d = workloads.device_mla_inputs(T, workloads.MLA, dev, salt)
+        qo = torch.empty((T, MLA_HQ), dtype=torch.float8_e4m3fn, device=dev)
+        qs = torch.empty((T, MLA_HQ // G), dtype=torch.float32, device=dev)
+        kvo = torch.empty((T, MLA_HKV), dtype=torch.bfloat16, device=dev)
+        L["dual_rmsnorm_quant"] = lambda d=d, qo=qo, qs=qs, kvo=kvo: rra.dual_rmsnorm_quant(
+            d["q"], d["q_w"], 1e-6, d["kv"], d["kv_w"], 1e-6, rra.Q_PER_GROUP, G, qo, qs, kvo)
+    torch.cuda.synchronize()
+    return L
+
+
+def run_steps(launch, steps: int, warmup: int):
+    """Warm up, then time `steps` passes over the four kernels.  Returns
+    (wall seconds for the timed steps, {kernel: [per-launch ms]})."""
+    import torch
+
+    for _ in range(warmup):
+        for n in KERNELS:
+            launch[n]()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        e = ev[s]
+        e[0].record()
+        for i, n in enumerate(KERNELS):
+            launch[n]()
+            e[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]
+           for i, n in enumerate(KERNELS)}
+    return wall, per
+
+
+def sweep(Ts, launches_per_point: int = 30):
+    """Each kernel alone at each T, rotating over buffer sets of that kernel
+    that total at least 1 GiB of algorithmic traffic (four times the 256 MB
+    last-level cache), so every launch reads cold data."""
+    import torch
+
+    rows = []
+    rope_state = None
+    for T in Ts:
+        for n in KERNELS:
+            n_sets = max(2, min(256, -(-(1 << 30) // algo_bytes(n, T))))
+            sets = []
+            for salt in range(n_sets):
+                L = make_launchers(T, salt, rope_state, only=(n,))
+                rope_state = L.get("_rope_state", rope_state)
+                sets.append(L)
+            for s in sets:  # warm-up: one launch per set
+                s[n]()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(launches_per_point)]
+            for j, (a, b) in enumerate(ev):
+                a.record()
+                sets[j % n_sets][n]()
+                b.record()
+            torch.cuda.synchronize()
+            ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+            gbps = algo_bytes(n, T) / (ms * 1e-3) / 1e9
+            rows.append(dict(kernel=n, T=T, us=round(ms * 1e3, 2), gbps=round(gbps, 1),
+                             frac=round(gbps / PEAK_HBM_GBPS, 4),
+                             tokens_per_s=round(T / (ms * 1e-3), 1), buffer_sets=n_sets))
+            log(f"sweep {n:26s} T={T:6d} {ms * 1e3:9.2f} us {gbps:8.1f} GB/s "
+                f"({100 * gbps / PEAK_HBM_GBPS:5.1f}% of peak), {n_sets} buffer sets")
+            del sets
+            torch.cuda.empty_cache()
+    return rows
+
+
+# ---- CPU baseline: the oracle on a bounded sample --------------------------------
+
+def cpu_baseline(sample_T: int):
+    import oracle
+    import workloads
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    oracle.set_threads(cores)
+    cfg = workloads.ROPE
+    n = sample_T
+    dn = workloads.norm_inputs(n, H_NORM)
+    ds = workloads.silu_inputs(n, I_SILU)
+    dr = workloads.rope_inputs(n, cfg)
+    dm = workloads.mla_inputs(n)
+    calls = {
+        "fused_add_rmsnorm_quant": lambda: oracle.fused_add_rmsnorm_quant(
+            dn["x"], dn["residual"], dn["weight"], 1e-5, oracle.Q_PER_TOKEN),
+        "silu_mul_quant": lambda: oracle.silu_mul_quant(ds["inp"], oracle.Q_PER_GROUP, G),
+        "rope_kv_write": lambda: oracle.rope_kv_write(
+            dr["positions"], dr["q"], dr["k"], dr["v"], cfg.theta, cfg.max_pos,
+            dr["slot_mapping"], dr["key_cache"], dr["value_cache"], cfg.Hq, cfg.Hkv, cfg.D),
+        "dual_rmsnorm_quant": lambda: oracle.dual_rmsnorm_quant(
+            dm["q"], dm["q_w"], 1e-6, dm["kv"], dm["kv_w"], 1e-6, oracle.Q_PER_GROUP, G),
+    }
+    secs = {}
+    for name, f in calls.items():
+        f()  # warm-up
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        secs[name] = statistics.median(ts)
+        log(f"oracle {name:26s} T={n} {secs[name] * 1e3:8.1f} ms on {oracle.get_threads()} threads")
+    total_bytes = sum(algo_bytes(k, n) for k in KERNELS)
+    total_s = sum(secs.values())
+    return dict(value=round(total_bytes / total_s / 1e9, 4), unit="GB/s",
+                cores=int(oracle.get_threads()), kind="oracle",
+                sample=f"T={n} tokens of each of the four kernels' workloads (the GPU step "
+                       f"uses T=8192); fp64 C oracle, OpenMP over rows, median of 3 calls "
+                       f"after one warm-up; bytes counted as for the GPU",
+                per_kernel_ms={k: round(v * 1e3, 2) for k, v in secs.items()})
+
+
+# ---- main ------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--T", type=int, default=8192, help="tokens per step")
+    ap.add_argument("--cpu-sample", type=int, default=1024,
+                    help="tokens per kernel for the oracle baseline (0 = skip)")
+    ap.add_argument("--sweep", default="", help="comma-separated token counts for the "
+                                                "per-kernel cold-cache sweep")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the four kernels are row-independent and "
+              f"need no exchange, so --gpus {args.gpus} has nothing further to show here.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import rope_residual_add_amd as rra
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        return 1
+    rra.lib()  # fail loudly if the HIP library is missing
+    T = args.T
+    log(f"device: {torch.cuda.get_device_name(0)}; T={T}; steps={args.steps}; "
+        f"warmup={args.warmup}")
+    launch = make_launchers(T)
+    wall, per = run_steps(launch, args.steps, args.warmup)
+
+    kern = {}
+    for n in KERNELS:
+        ms = statistics.fmean(per[n])
+        b = algo_bytes(n, T)
+        gbps = b / (ms * 1e-3) / 1e9
+        kern[n] = dict(us=round(ms * 1e3, 2), us_median=round(statistics.median(per[n]) * 1e3, 2),
+                       bytes=b, gbps=round(gbps, 1), frac_of_peak=round(gbps / PEAK_HBM_GBPS, 4),
+                       tokens_per_s=round(T / (ms * 1e-3), 1))
+        log(f"{n:26s} {ms * 1e3:9.2f} us  {gbps:8.1f} GB/s  "
+            f"{100 * gbps / PEAK_HBM_GBPS:5.1f}% of 8 TB/s  {T / (ms * 1e-3):.3e} tokens/s")
+
+    step_bytes = sum(algo_bytes(n, T) for n in KERNELS)
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+    dom = max(KERNELS, key=lambda n: kern[n]["us"])
+    roofline = dict(bound="hbm", kernel=dom, achieved=kern[dom]["gbps"], peak=PEAK_HBM_GBPS,
+                    unit="GB/s", frac=kern[dom]["frac_of_peak"], traffic=None)
+
+    result = dict(
+        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="fp32", data="synthetic",
+        config=dict(workload=f"fused layer ops at T={T}: residual-add+RMSNorm->FP8 per-token "
+                             f"(H=4096), SiLU-and-Mul->FP8 group-128 (I=14336), neox RoPE->paged "
+                             f"KV write (32/8 heads x 128, cache 4096x16x8x128), MLA dual RMSNorm "
+                             f"(1536 FP8 group-128 / 512 bf16)",
+                    T=T, io="bf16 in; e4m3fn codes + fp32 scales / bf16 out; fp32 arithmetic",
+                    step_bytes=step_bytes),
+        kernels=kern, roofline=roofline,
+    )
+    if args.sweep:
+        result["sweep"] = sweep([int(t) for t in args.sweep.split(",") if t])
+    if args.cpu_sample > 0:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_sample)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

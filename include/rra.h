@@ -24,7 +24,9 @@
  *   are therefore reentrant and may be captured into a HIP graph.
  * - Errors: each function returns RRA_OK (0) or a negative rra_status.  All
  *   argument checks run on the host before anything is launched, so an error
- *   return means nothing was enqueued.  T == 0 returns RRA_OK without a launch.
+ *   return means nothing was enqueued.  T == 0 returns RRA_OK without a launch;
+ *   with T == 0, pointers to tensors that have T rows (or T tokens) may be NULL,
+ *   while weights, static scales, tables and caches must still be given.
  *   RRA_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).
  * - Device-data contract (not checked: checking would need a host sync):
  *   inputs are finite; a static scale is finite and > 0; positions lie in

@@ -65,45 +65,46 @@ __device__ __forceinline__ float absmax8(const float t[8]) {
   return m;
 }
 
-__device__ __forceinline__ u32x2 codes8(const float t[8], float f) {
-  return u32x2{pack_e4m3x4(t[0] * f, t[1] * f, t[2] * f, t[3] * f),
-               pack_e4m3x4(t[4] * f, t[5] * f, t[6] * f, t[7] * f)};
-}
-
 // RMSNorm of one row held in registers, then the row's output:
 //   y = z * w * rho,  rho = 1/sqrt(mean(z^2) + eps)
 // mode NONE writes bf16(y) to out (uint16_t*); the quantizing modes write
 // e4m3fn(y / s) to out (uint8_t*) and s to scale_row.
-// Because rho > 0 is one number per row, max|y| = max|z*w| * rho exactly
-// (rounding is monotonic), so the amax needs no extra pass over y; the codes
-// are t * (rho / s) with t = z * w.
+// rho and the scales are computed in double (once per row or group): the
+// sum of squares of bf16 values accumulates exactly enough in double that a
+// scale's fp32 rounding, and with it the side of every exact tie, is the one
+// the plain definition gives.  Because rho > 0 is one number per row,
+// max|y| = max|z*w| * rho, so the amax needs no extra pass over y; t = z * w
+// is exact in fp32 and the codes are e4m3fn(t * rho / s).
 template <int NV>
 __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs<NV>& w,
                                              float eps, int H, int nvec, int lane, int mode,
-                                             int group, float static_inv, void* out,
+                                             int group, float static_scale, void* out,
                                              float* scale_row) {
-  float ss = 0.0f;
+  double ss = 0.0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float a = bf16_lo(z.v[i][k]), b = bf16_hi(z.v[i][k]);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
+      ss += static_cast<double>(a * a);  // a*a is exact: a has 8 significant bits
+      ss += static_cast<double>(b * b);
     }
   }
-  ss = wave_sum(ss);
-  const float rho = rsqrtf(ss / static_cast<float>(H) + eps);
+  ss = wave_sum_f64(ss);
+  const double rho = 1.0 / sqrt(ss / static_cast<double>(H) + static_cast<double>(eps));
 
   if (mode == RRA_Q_NONE) {
+    const float rho_f = static_cast<float>(rho);
     uint16_t* o = static_cast<uint16_t*>(out);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = i * kWave + lane;
       float t[8];
       zw8(z.v[i], w.v[i], t);
-      const u32x4 packed{pack_bf16x2(t[0] * rho, t[1] * rho), pack_bf16x2(t[2] * rho, t[3] * rho),
-                         pack_bf16x2(t[4] * rho, t[5] * rho), pack_bf16x2(t[6] * rho, t[7] * rho)};
+      const u32x4 packed{pack_bf16x2(t[0] * rho_f, t[1] * rho_f),
+                         pack_bf16x2(t[2] * rho_f, t[3] * rho_f),
+                         pack_bf16x2(t[4] * rho_f, t[5] * rho_f),
+                         pack_bf16x2(t[6] * rho_f, t[7] * rho_f)};
       if (idx < nvec) st_stream(o + idx * 8, packed);
     }
     return;
@@ -119,17 +120,17 @@ __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs
       zw8(z.v[i], w.v[i], t);
       float m = absmax8(t);
       m = group == 128 ? max16(m) : max8(m);
-      const float s = (m * rho) / 448.0f;
-      const float f = rho * inv_scale(s);
+      const float s = dynamic_scale(m, rho);
+      const double g = quant_gain(rho, s);
       if (idx < nvec) {
         if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = s;
-        st_stream(o + idx * 8, codes8(t, f));
+        st_stream(o + idx * 8, quant8(t, static_cast<float>(g), g));
       }
     }
     return;
   }
 
-  float f;
+  double g;
   if (mode == RRA_Q_PER_TOKEN) {
     float m = 0.0f;
 #pragma unroll
@@ -139,18 +140,19 @@ __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs
       m = fmaxf(m, absmax8(t));
     }
     m = wave_max(m);
-    const float s = (m * rho) / 448.0f;
-    f = rho * inv_scale(s);
+    const float s = dynamic_scale(m, rho);
+    g = quant_gain(rho, s);
     if (lane == 0) scale_row[0] = s;
   } else {  // RRA_Q_STATIC
-    f = rho * static_inv;
+    g = rho / static_cast<double>(static_scale);
   }
+  const float f = static_cast<float>(g);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = i * kWave + lane;
     float t[8];
     zw8(z.v[i], w.v[i], t);
-    if (idx < nvec) st_stream(o + idx * 8, codes8(t, f));
+    if (idx < nvec) st_stream(o + idx * 8, quant8(t, f, g));
   }
 }
 
@@ -171,7 +173,7 @@ __global__ void __launch_bounds__(kBlock)
   load_row<NV, true>(a, x + row * x_stride, nvec, lane);
   if (kResidual) load_row<NV, true>(r, residual + row * res_stride, nvec, lane);
   load_row<NV, false>(w, weight, nvec, lane);
-  const float static_inv = mode == RRA_Q_STATIC ? 1.0f / static_scale[0] : 0.0f;
+  const float sscale = mode == RRA_Q_STATIC ? static_scale[0] : 0.0f;
 
   if (kResidual) {
     // z = bf16(x + residual): the fp32 sum of two bf16 values rounds once.
@@ -188,7 +190,7 @@ __global__ void __launch_bounds__(kBlock)
   float* scale_row = nullptr;
   if (mode == RRA_Q_PER_TOKEN) scale_row = scales + row;
   if (mode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / group);
-  rmsnorm_emit<NV>(a, w, eps, H, nvec, lane, mode, group, static_inv, out + row * out_stride,
+  rmsnorm_emit<NV>(a, w, eps, H, nvec, lane, mode, group, sscale, out + row * out_stride,
                    scale_row);
 }
 
@@ -272,7 +274,9 @@ extern "C" int fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint
                                        int64_t out_stride, float* scales, int64_t T, int64_t H,
                                        void* stream) {
   RRA_REQUIRE(T >= 0 && H > 0, RRA_ERR_SHAPE);
-  RRA_REQUIRE(x && weight && out, RRA_ERR_NULL);
+  // Tensors of T rows may be NULL when T == 0 (an empty torch tensor has no storage).
+  const bool rows_ok = T == 0 || (x && out);
+  RRA_REQUIRE(rows_ok && weight, RRA_ERR_NULL);
   RRA_REQUIRE(x_stride >= H && out_stride >= H, RRA_ERR_SHAPE);
   RRA_REQUIRE(!residual || residual_stride >= H, RRA_ERR_SHAPE);
   RRA_REQUIRE(H % 8 == 0 && H <= 8192, RRA_ERR_UNSUPPORTED);
@@ -282,12 +286,12 @@ extern "C" int fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint
       RRA_REQUIRE(aligned(static_scale, 4), RRA_ERR_ALIGN);
       break;
     case RRA_Q_PER_TOKEN:
-      RRA_REQUIRE(scales, RRA_ERR_NULL);
+      RRA_REQUIRE(scales || T == 0, RRA_ERR_NULL);
       break;
     case RRA_Q_PER_GROUP:
       RRA_REQUIRE(group_ok(group_size), RRA_ERR_UNSUPPORTED);
       RRA_REQUIRE(H % group_size == 0, RRA_ERR_SHAPE);
-      RRA_REQUIRE(scales, RRA_ERR_NULL);
+      RRA_REQUIRE(scales || T == 0, RRA_ERR_NULL);
       break;
     default:
       return RRA_ERR_UNSUPPORTED;
@@ -317,7 +321,8 @@ extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uin
                                   float* q_scales, uint16_t* kv_out, int64_t kv_out_stride,
                                   int64_t T, int64_t Hq, int64_t Hkv, void* stream) {
   RRA_REQUIRE(T >= 0 && Hq > 0 && Hkv > 0, RRA_ERR_SHAPE);
-  RRA_REQUIRE(q && q_weight && kv && kv_weight && q_out && kv_out, RRA_ERR_NULL);
+  const bool rows_ok = T == 0 || (q && kv && q_out && kv_out);
+  RRA_REQUIRE(rows_ok && q_weight && kv_weight, RRA_ERR_NULL);
   RRA_REQUIRE(q_stride >= Hq && kv_stride >= Hkv && q_out_stride >= Hq && kv_out_stride >= Hkv,
               RRA_ERR_SHAPE);
   RRA_REQUIRE(Hq % 8 == 0 && Hkv % 8 == 0 && Hq <= 2048 && Hkv <= 1024, RRA_ERR_UNSUPPORTED);
@@ -326,13 +331,13 @@ extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uin
       RRA_REQUIRE(vec_ok(q_out, q_out_stride), RRA_ERR_ALIGN);
       break;
     case RRA_Q_PER_TOKEN:
-      RRA_REQUIRE(q_scales, RRA_ERR_NULL);
+      RRA_REQUIRE(q_scales || T == 0, RRA_ERR_NULL);
       RRA_REQUIRE(aligned(q_out, 8) && q_out_stride % 8 == 0, RRA_ERR_ALIGN);
       break;
     case RRA_Q_PER_GROUP:
       RRA_REQUIRE(group_ok(group_size), RRA_ERR_UNSUPPORTED);
       RRA_REQUIRE(Hq % group_size == 0, RRA_ERR_SHAPE);
-      RRA_REQUIRE(q_scales, RRA_ERR_NULL);
+      RRA_REQUIRE(q_scales || T == 0, RRA_ERR_NULL);
       RRA_REQUIRE(aligned(q_out, 8) && q_out_stride % 8 == 0, RRA_ERR_ALIGN);
       break;
     default:

@@ -166,9 +166,9 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   RRA_REQUIRE(T >= 0 && Hq > 0 && Hkv > 0 && D > 0 && rot_dim > 0 && block_size > 0 &&
                   num_blocks > 0 && max_pos > 0,
               RRA_ERR_SHAPE);
-  RRA_REQUIRE(positions && q && q_out && k && v && cos_sin && slot_mapping && key_cache &&
-                  value_cache,
-              RRA_ERR_NULL);
+  // Tensors of T tokens may be NULL when T == 0 (an empty torch tensor has no storage).
+  const bool tokens_ok = T == 0 || (positions && q && q_out && k && v && slot_mapping);
+  RRA_REQUIRE(tokens_ok && cos_sin && key_cache && value_cache, RRA_ERR_NULL);
   RRA_REQUIRE(q_stride >= int64_t(Hq) * D && q_out_stride >= int64_t(Hq) * D &&
                   k_stride >= int64_t(Hkv) * D && v_stride >= int64_t(Hkv) * D,
               RRA_ERR_SHAPE);

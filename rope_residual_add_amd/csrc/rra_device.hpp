@@ -65,6 +65,57 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return static_cast<uint32_t>(w);
 }
 
+// ---- correctly rounded quantization ------------------------------------------
+// A code is e4m3fn(q) of the exact quotient q = y / s.  Dynamic scales make
+// exact ties common: y / s = 448 * t / m * (1 + d), where t and m (products of
+// two bf16 values) often stand in a short ratio such as 3/8 that puts
+// 448 * t / m exactly on an e4m3 rounding midpoint, and only the tiny offset d
+// left by rounding s to fp32 decides the side.  An fp32 quotient cannot see d.
+// So each value is first rounded as v = fp32(t * f) (within two fp32 ulps of
+// q); where v lies within 4 ulps of a midpoint, or in the e4m3 subnormal
+// range, q is recomputed in double and narrowed to fp32 with round-to-odd,
+// after which the single hardware rounding to e4m3 is the correct rounding of
+// q (fp32 keeps 20 more fraction bits than e4m3; round-to-odd makes the
+// double rounding innocuous).
+
+// True when v (an fp32 estimate of q) may round differently from q.
+__device__ __forceinline__ bool e4m3_near_tie(float v) {
+  const uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
+  // e4m3 normals: a midpoint has the 20 fraction bits below e4m3's 3 equal
+  // to 0x80000 (one half of the e4m3 quantum).
+  const bool near_mid = ((b & 0xFFFFFu) - 0x7FFFCu) <= 8u;
+  // below 2^-6 (e4m3 subnormals) the quantum is fixed: resolve exactly.
+  return near_mid || (b < 0x3C800000u && b != 0u);
+}
+
+// double -> fp32 rounding to odd: truncate toward zero, set the last bit if
+// anything was discarded.
+__device__ __forceinline__ float f32_round_odd(double q) {
+  const float v = static_cast<float>(q);  // to nearest even
+  const double back = static_cast<double>(v);
+  if (back == q) return v;
+  uint32_t b = __float_as_uint(v);
+  if (fabs(back) > fabs(q)) b -= 1u;  // rounded away from zero: step back
+  return __uint_as_float(b | 1u);
+}
+
+// Eight codes e4m3fn(t[j] * g), with f = fp32(g) for the fast path.
+__device__ __forceinline__ u32x2 quant8(const float t[8], float f, double g) {
+  float v[8];
+  bool exact = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v[j] = t[j] * f;
+    exact |= e4m3_near_tie(v[j]);
+  }
+  if (exact) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (e4m3_near_tie(v[j])) v[j] = f32_round_odd(static_cast<double>(t[j]) * g);
+  }
+  return u32x2{pack_e4m3x4(v[0], v[1], v[2], v[3]), pack_e4m3x4(v[4], v[5], v[6], v[7])};
+}
+
 // ---- wavefront reductions ---------------------------------------------------
 // DPP moves within 16-lane rows: quad_perm [1,0,3,2] (0xB1), quad_perm
 // [2,3,0,1] (0x4E), row_half_mirror (0x141), row_mirror (0x140); across rows:
@@ -112,6 +163,32 @@ __device__ __forceinline__ float wave_sum(float v) {
   return readlane63(v);
 }
 
+// Sum of doubles over the whole wave, with the same DPP pattern applied to
+// both 32-bit halves; wave-uniform result.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(u & 0xFFFFFFFFu), kCtrl, kRowMask, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(u >> 32), kCtrl, kRowMask, 0xF, false));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  v += dpp_f64<0x142, 0xA>(v);
+  v += dpp_f64<0x143, 0xC>(v);
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(u & 0xFFFFFFFFu), 63));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), 63));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
 // Max over the whole wave (inputs >= 0); wave-uniform result.
 __device__ __forceinline__ float wave_max(float v) {
   v = max16(v);
@@ -130,5 +207,16 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 // 1/s for a quantization scale, with s = 0 (all-zero slice) mapped to 0 so
 // that every code of the slice is +0.
 __device__ __forceinline__ float inv_scale(float s) { return s > 0.0f ? 1.0f / s : 0.0f; }
+
+// Dynamic scale from an amax given as m * rho (m >= 0 exact in fp32, rho in
+// double): s = fp32(m * rho / 448), 448 being e4m3fn's largest finite value.
+__device__ __forceinline__ float dynamic_scale(float m, double rho) {
+  return static_cast<float>(static_cast<double>(m) * rho / 448.0);
+}
+
+// rho / s in double, 0 for s = 0.
+__device__ __forceinline__ double quant_gain(double rho, float s) {
+  return s > 0.0f ? rho / static_cast<double>(s) : 0.0;
+}
 
 }  // namespace rra

@@ -114,7 +114,7 @@ extern "C" int silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_m
                               int64_t out_stride, float* scales, int64_t T, int64_t I,
                               void* stream) {
   RRA_REQUIRE(T >= 0 && I > 0, RRA_ERR_SHAPE);
-  RRA_REQUIRE(in && out, RRA_ERR_NULL);
+  RRA_REQUIRE(T == 0 || (in && out), RRA_ERR_NULL);  // empty tensors have no storage
   RRA_REQUIRE(in_stride >= 2 * I && out_stride >= I, RRA_ERR_SHAPE);
   RRA_REQUIRE(I % 8 == 0 && I <= (int64_t(1) << 30), RRA_ERR_UNSUPPORTED);
   switch (quant_mode) {
@@ -125,7 +125,7 @@ extern "C" int silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_m
     case RRA_Q_PER_GROUP:
       RRA_REQUIRE(group_ok(group_size), RRA_ERR_UNSUPPORTED);
       RRA_REQUIRE(I % group_size == 0, RRA_ERR_SHAPE);
-      RRA_REQUIRE(scales, RRA_ERR_NULL);
+      RRA_REQUIRE(scales || T == 0, RRA_ERR_NULL);
       RRA_REQUIRE(aligned(scales, 4), RRA_ERR_ALIGN);
       break;
     default:

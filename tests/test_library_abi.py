@@ -85,6 +85,9 @@ def test_norm_validation(rra):
     assert norm(L, xs=4100) == EALIGN
     assert norm(L, out=A + 4) == EALIGN
     assert norm(L, res=None, rs=0, T=0) == OK
+    # with T == 0 the per-row tensors may be NULL (empty tensors), the weight may not
+    assert norm(L, x=None, res=None, out=None, sc=None, T=0) == OK
+    assert norm(L, w=None, T=0) == ENULL
 
 
 def test_silu_validation(rra):
@@ -102,6 +105,7 @@ def test_silu_validation(rra):
     assert f(I=1000, s=2000, os=1000) == ESHAPE  # 128 does not divide 1000
     assert f(inp=A + 2) == EALIGN
     assert f(mode=1, ss=None) == ENULL
+    assert f(inp=None, out=None, sc=None, T=0) == OK
 
 
 def test_rope_validation(rra):
@@ -122,6 +126,9 @@ def test_rope_validation(rra):
     assert f(D=96, qs=3072, qos=3072, ks=768, vs=768, rd=96) == EUNSUP
     assert f(rd=64) == EUNSUP
     assert f(neox=0) == EUNSUP
+    assert f(pos=None, q=None, qo=None, k=None, v=None, sm=None, T=0) == OK
+    assert f(kc=None, T=0) == ENULL
+    assert f(cs=None, T=0) == ENULL
     assert f(kc=A + 2) == EALIGN
     assert f(pos=A + 4) == EALIGN
     assert f(bs=0) == ESHAPE
@@ -144,6 +151,8 @@ def test_dual_validation(rra):
 
     assert f(T=0) == OK
     assert f(kvo=None) == ENULL
+    assert f(q=None, kv=None, qo=None, kvo=None, sc=None, T=0) == OK
+    assert f(qw=None, T=0) == ENULL
     assert f(sc=None) == ENULL
     assert f(mode=1) == EUNSUP
     assert f(Hq=4096, qs=4096, qos=4096) == EUNSUP

@@ -158,3 +158,68 @@ def mla_inputs(T: int, cfg: MlaCfg = MLA, salt: int = 0):
         q_w=bf16_normal(_rng("mla", 0, 2, salt), (cfg.Hq,), mean=1.0, std=0.1),
         kv_w=bf16_normal(_rng("mla", 0, 3, salt), (cfg.Hkv,), mean=1.0, std=0.1),
     )
+
+
+# ---- device-resident inputs for the benchmark --------------------------------
+# Same distributions as above, drawn directly on the GPU with torch's seeded
+# generator (the benchmark's T = 8192 tensors are too large to draw on the host
+# quickly).  Like the host generators, these only draw numbers.
+
+def _gen(device, tag: str, T: int, salt: int = 0):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(_TAGS[tag] * 1_000_003 + int(T) * 101 + int(salt))
+    return g
+
+
+def _randn(g, shape, device, mean=0.0, std=1.0):
+    import torch
+
+    a = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        a.mul_(std)
+    if mean != 0.0:
+        a.add_(mean)
+    return a.to(torch.bfloat16)
+
+
+def device_norm_inputs(T: int, H: int, device="cuda", salt: int = 0, tag: str = "norm_token"):
+    g = _gen(device, tag, T, salt)
+    return dict(x=_randn(g, (T, H), device), residual=_randn(g, (T, H), device),
+                weight=_randn(g, (H,), device, mean=1.0, std=0.1))
+
+
+def device_silu_inputs(T: int, I: int, device="cuda", salt: int = 0):
+    g = _gen(device, "silu", T, salt)
+    return dict(inp=_randn(g, (T, 2 * I), device, std=2.0))
+
+
+def device_rope_inputs(T: int, cfg: RopeCfg = ROPE, device="cuda", salt: int = 0,
+                       with_cache: bool = True):
+    import torch
+
+    g = _gen(device, "rope", T, salt)
+    n_slots = cfg.num_blocks * cfg.block_size
+    if T > n_slots:
+        raise ValueError("more tokens than cache slots")
+    d = dict(
+        q=_randn(g, (T, cfg.Hq, cfg.D), device),
+        k=_randn(g, (T, cfg.Hkv, cfg.D), device),
+        v=_randn(g, (T, cfg.Hkv, cfg.D), device),
+        positions=torch.randint(0, cfg.max_pos, (T,), generator=g, device=device,
+                                dtype=torch.int64),
+        slot_mapping=torch.randperm(n_slots, generator=g, device=device)[:T].contiguous(),
+    )
+    if with_cache:
+        cache_shape = (cfg.num_blocks, cfg.block_size, cfg.Hkv, cfg.D)
+        d["key_cache"] = _randn(g, cache_shape, device)
+        d["value_cache"] = _randn(g, cache_shape, device)
+    return d
+
+
+def device_mla_inputs(T: int, cfg: MlaCfg = MLA, device="cuda", salt: int = 0):
+    g = _gen(device, "mla", T, salt)
+    return dict(q=_randn(g, (T, cfg.Hq), device), kv=_randn(g, (T, cfg.Hkv), device),
+                q_w=_randn(g, (cfg.Hq,), device, mean=1.0, std=0.1),
+                kv_w=_randn(g, (cfg.Hkv,), device, mean=1.0, std=0.1))
