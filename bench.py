@@ -145,6 +145,50 @@ def run_steps(launch, steps: int, warmup: int):
     return wall, per
 
 
+def _blocker_cycles(target_ms: float = 5.0) -> int:
+    """Spin-kernel length (torch.cuda._sleep cycles) that keeps the GPU busy
+    for about target_ms, so that launches queued behind it run back to back
+    and the events around them time the kernels, not the host's launch rate."""
+    import torch
+
+    probe = 1_000_000
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    torch.cuda._sleep(probe)
+    b.record()
+    torch.cuda.synchronize()
+    ms = max(a.elapsed_time(b), 1e-3)
+    return int(min(probe * target_ms / ms, 2_000_000_000))
+
+
+def copy_ceiling(nbytes: int = 1 << 30, n_pairs: int = 4, reps: int = 12) -> dict:
+    """Plain device copy (torch copy_) of nbytes, rotating over n_pairs of
+    buffers (8 GiB in all) so it streams from HBM: read + write bytes / time."""
+    import torch
+
+    src = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device="cuda") for i in range(n_pairs)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n_pairs)]
+    for i in range(n_pairs):
+        dst[i].copy_(src[i])
+    cyc = _blocker_cycles()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(cyc)
+    a.record()
+    for r in range(reps):
+        dst[r % n_pairs].copy_(src[r % n_pairs])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+    log(f"copy ceiling: {nbytes >> 20} MiB copy_ {ms * 1e3:.1f} us -> {gbps:.1f} GB/s "
+        f"({100 * gbps / PEAK_HBM_GBPS:.1f}% of 8 TB/s)")
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(gbps=round(gbps, 1), frac_of_peak=round(gbps / PEAK_HBM_GBPS, 4),
+                what=f"torch copy_ of {nbytes >> 20} MiB (read + write bytes), {n_pairs} "
+                     f"rotating buffer pairs")
+
+
 def sweep(Ts, launches_per_point: int = 30):
     """Each kernel alone at each T, rotating over buffer sets of that kernel
     that total at least 1 GiB of algorithmic traffic (four times the 256 MB
@@ -153,6 +197,7 @@ def sweep(Ts, launches_per_point: int = 30):
 
     rows = []
     rope_state = None
+    cyc = _blocker_cycles()
     for T in Ts:
         for n in KERNELS:
             n_sets = max(2, min(256, -(-(1 << 30) // algo_bytes(n, T))))
@@ -166,6 +211,7 @@ def sweep(Ts, launches_per_point: int = 30):
             torch.cuda.synchronize()
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(launches_per_point)]
+            torch.cuda._sleep(cyc)  # queue the timed launches behind a spin kernel
             for j, (a, b) in enumerate(ev):
                 a.record()
                 sets[j % n_sets][n]()
@@ -295,6 +341,10 @@ def main() -> int:
                     step_bytes=step_bytes),
         kernels=kern, roofline=roofline,
     )
+    ceiling = copy_ceiling()
+    for n in KERNELS:
+        kern[n]["frac_of_copy"] = round(kern[n]["gbps"] / ceiling["gbps"], 4)
+    result["copy_ceiling"] = ceiling
     if args.sweep:
         result["sweep"] = sweep([int(t) for t in args.sweep.split(",") if t])
     if args.cpu_sample > 0:

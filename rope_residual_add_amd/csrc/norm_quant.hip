@@ -7,32 +7,36 @@
 // in place) and "MLA Dual RMSNorm (fuse_mla_dual_rms_norm)" (the q_a and kv_a
 // norms in one launch; in the FP8 variant only q is quantized).
 //
-// Mapping: one wavefront per row.  A row of H bf16 values is spread over the
-// 64 lanes as 16-byte vectors: lane l holds vectors l, l + 64, l + 128, ... so
-// every vector load of the wave reads 1 KiB of contiguous memory.  The whole
-// row stays in VGPRs between the read and the write, so each element crosses
-// HBM once in each direction.  Row reductions (sum of squares, amax) are
-// wave-local DPP reductions: no LDS and no barrier.  A quantization group of
-// 128 (64) columns is exactly 16 (8) consecutive lanes of one vector, so group
-// amaxes are DPP row reductions as well.
+// Mapping: a row of H bf16 values is spread over the lanes of kW waves as
+// 16-byte vectors: "row lane" rl = (wave within the row) * 64 + lane holds
+// vectors rl, rl + 64 kW, rl + 128 kW, ... so every vector load of a wave
+// reads 1 KiB of contiguous memory.  The row stays in VGPRs between the read
+// and the write, so each element crosses HBM once in each direction.  Each
+// wave reduces its share of the row statistics (sum of squares, amax) with
+// DPP; with kW > 1 one LDS exchange and one barrier combine the kW partials in
+// a fixed order, so every wave of the row sees bit-identical statistics.  A
+// quantization group of 128 (64) columns is exactly 16 (8) consecutive lanes
+// of one vector, so group amaxes are DPP row reductions with no exchange.
+// Rows past the end are predicated off rather than returned from, so that
+// every wave of a workgroup reaches the barrier.
 #include "rra_device.hpp"
 #include "rra_host.hpp"
 
 namespace rra {
 
-// This lane's share of one row: vector i covers columns (i*64 + lane)*8 .. +8.
+// One row lane's share of a row: vector i covers columns (i * stride + rl) * 8.
 template <int NV>
 struct RowVecs {
   u32x4 v[NV];
 };
 
 template <int NV, bool kStream>
-__device__ __forceinline__ void load_row(RowVecs<NV>& r, const uint16_t* base, int nvec,
-                                         int lane) {
+__device__ __forceinline__ void load_row(RowVecs<NV>& r, const uint16_t* base, int nvec, int rl,
+                                         int stride, bool active) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int idx = i * kWave + lane;
-    if (idx < nvec)
+    const int idx = i * stride + rl;
+    if (active && idx < nvec)
       r.v[i] = kStream ? ld_stream(base + idx * 8) : ld_cached(base + idx * 8);
     else
       r.v[i] = u32x4{0u, 0u, 0u, 0u};
@@ -40,16 +44,16 @@ __device__ __forceinline__ void load_row(RowVecs<NV>& r, const uint16_t* base, i
 }
 
 template <int NV>
-__device__ __forceinline__ void store_row(uint16_t* base, const RowVecs<NV>& r, int nvec,
-                                         int lane) {
+__device__ __forceinline__ void store_row(uint16_t* base, const RowVecs<NV>& r, int nvec, int rl,
+                                         int stride) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int idx = i * kWave + lane;
+    const int idx = i * stride + rl;
     if (idx < nvec) st_stream(base + idx * 8, r.v[i]);
   }
 }
 
-// t = z * w for the 8 columns of one vector.
+// t = z * w for the 8 columns of one vector (exact: 8-bit by 8-bit significands).
 __device__ __forceinline__ void zw8(u32x4 z, u32x4 w, float t[8]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -65,40 +69,77 @@ __device__ __forceinline__ float absmax8(const float t[8]) {
   return m;
 }
 
-// RMSNorm of one row held in registers, then the row's output:
-//   y = z * w * rho,  rho = 1/sqrt(mean(z^2) + eps)
-// mode NONE writes bf16(y) to out (uint16_t*); the quantizing modes write
-// e4m3fn(y / s) to out (uint8_t*) and s to scale_row.
-// rho and the scales are computed in double (once per row or group): the
-// sum of squares of bf16 values accumulates exactly enough in double that a
-// scale's fp32 rounding, and with it the side of every exact tie, is the one
-// the plain definition gives.  Because rho > 0 is one number per row,
-// max|y| = max|z*w| * rho, so the amax needs no extra pass over y; t = z * w
-// is exact in fp32 and the codes are e4m3fn(t * rho / s).
+// This lane's part of the row statistics: the sum of z^2 in double (each z^2
+// is exact in fp32, a bf16 having 8 significant bits, and the double sum
+// keeps enough bits that the fp32 rounding of a scale derived from it is the
+// one the plain definition gives) and, when wanted, max |z * w|.
 template <int NV>
-__device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs<NV>& w,
-                                             float eps, int H, int nvec, int lane, int mode,
-                                             int group, float static_scale, void* out,
-                                             float* scale_row) {
-  double ss = 0.0;
+__device__ __forceinline__ void row_partials(const RowVecs<NV>& z, const RowVecs<NV>& w,
+                                             bool want_max, double& ss, float& m) {
+  ss = 0.0;
+  m = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float a = bf16_lo(z.v[i][k]), b = bf16_hi(z.v[i][k]);
-      ss += static_cast<double>(a * a);  // a*a is exact: a has 8 significant bits
+      ss += static_cast<double>(a * a);
       ss += static_cast<double>(b * b);
     }
+    if (want_max) {
+      float t[8];
+      zw8(z.v[i], w.v[i], t);
+      m = fmaxf(m, absmax8(t));
+    }
   }
+}
+
+// Combine the partials of the kW waves of a row: wave-level DPP reductions,
+// then (kW > 1) an exchange through LDS slots [slot0, slot0 + kW).  Must be
+// reached by every wave of the workgroup.
+template <int kW>
+__device__ __forceinline__ void row_reduce(double& ss, float& m, double* lds_ss, float* lds_m,
+                                           int slot0, int wave_in_row) {
   ss = wave_sum_f64(ss);
+  m = wave_max(m);
+  if (kW > 1) {
+    if (lane_id() == 0) {
+      lds_ss[slot0 + wave_in_row] = ss;
+      lds_m[slot0 + wave_in_row] = m;
+    }
+    __syncthreads();
+    ss = lds_ss[slot0];
+    m = lds_m[slot0];
+#pragma unroll
+    for (int j = 1; j < kW; ++j) {
+      ss += lds_ss[slot0 + j];
+      m = fmaxf(m, lds_m[slot0 + j]);
+    }
+  }
+}
+
+// The row's output from its statistics:
+//   y = z * w * rho,  rho = 1/sqrt(ss / H + eps)
+// mode NONE writes bf16(y) to out (uint16_t*); the quantizing modes write
+// e4m3fn(y / s) to out (uint8_t*) and s to scale_row (row lane 0 for a
+// per-token scale, the first lane of each group for per-group scales).
+// Because rho > 0 is one number per row, max|y| = max|z * w| * rho, so the
+// amax needs no second pass over y; t = z * w is exact in fp32 and the codes
+// are e4m3fn(t * rho / s) (quant8 rounds them as the exact quotient would).
+template <int NV>
+__device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs<NV>& w, double ss,
+                                             float m_row, float eps, int H, int nvec, int rl,
+                                             int stride, int mode, int group, float static_scale,
+                                             void* out, float* scale_row) {
   const double rho = 1.0 / sqrt(ss / static_cast<double>(H) + static_cast<double>(eps));
+  const int lane = lane_id();
 
   if (mode == RRA_Q_NONE) {
     const float rho_f = static_cast<float>(rho);
     uint16_t* o = static_cast<uint16_t*>(out);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int idx = i * kWave + lane;
+      const int idx = i * stride + rl;
       float t[8];
       zw8(z.v[i], w.v[i], t);
       const u32x4 packed{pack_bf16x2(t[0] * rho_f, t[1] * rho_f),
@@ -115,7 +156,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs
     const int lanes_per_group = group / 8;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int idx = i * kWave + lane;
+      const int idx = i * stride + rl;
       float t[8];
       zw8(z.v[i], w.v[i], t);
       float m = absmax8(t);
@@ -132,31 +173,25 @@ __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs
 
   double g;
   if (mode == RRA_Q_PER_TOKEN) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      float t[8];
-      zw8(z.v[i], w.v[i], t);
-      m = fmaxf(m, absmax8(t));
-    }
-    m = wave_max(m);
-    const float s = dynamic_scale(m, rho);
+    const float s = dynamic_scale(m_row, rho);
     g = quant_gain(rho, s);
-    if (lane == 0) scale_row[0] = s;
+    if (rl == 0) scale_row[0] = s;
   } else {  // RRA_Q_STATIC
     g = rho / static_cast<double>(static_scale);
   }
   const float f = static_cast<float>(g);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int idx = i * kWave + lane;
+    const int idx = i * stride + rl;
     float t[8];
     zw8(z.v[i], w.v[i], t);
     if (idx < nvec) st_stream(o + idx * 8, quant8(t, f, g));
   }
 }
 
-template <int NV, bool kResidual>
+// Residual add + RMSNorm + quant.  Workgroup = kBlock lanes = kWavesPerBlock /
+// kW rows; each row lane holds NV vectors of x, residual and weight.
+template <int NV, int kW, bool kResidual>
 __global__ void __launch_bounds__(kBlock)
     add_rmsnorm_quant_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                              uint16_t* __restrict__ residual, int64_t res_stride,
@@ -164,19 +199,26 @@ __global__ void __launch_bounds__(kBlock)
                              int group, const float* __restrict__ static_scale,
                              uint8_t* __restrict__ out, int64_t out_stride,
                              float* __restrict__ scales, int64_t T, int H) {
-  const int lane = lane_id();
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
-  if (row >= T) return;
+  constexpr int kRowsPerBlock = kWavesPerBlock / kW;
+  constexpr int kStride = kW * kWave;
+  __shared__ double lds_ss[kWavesPerBlock];
+  __shared__ float lds_m[kWavesPerBlock];
+  const int wave = wave_id();
+  const int wave_in_row = wave % kW;
+  const int rl = wave_in_row * kWave + lane_id();
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave / kW;
+  const bool active = row < T;
   const int nvec = H >> 3;
 
   RowVecs<NV> a, r, w;
-  load_row<NV, true>(a, x + row * x_stride, nvec, lane);
-  if (kResidual) load_row<NV, true>(r, residual + row * res_stride, nvec, lane);
-  load_row<NV, false>(w, weight, nvec, lane);
+  load_row<NV, true>(a, x + row * x_stride, nvec, rl, kStride, active);
+  if (kResidual) load_row<NV, true>(r, residual + row * res_stride, nvec, rl, kStride, active);
+  load_row<NV, false>(w, weight, nvec, rl, kStride, true);
   const float sscale = mode == RRA_Q_STATIC ? static_scale[0] : 0.0f;
 
   if (kResidual) {
-    // z = bf16(x + residual): the fp32 sum of two bf16 values rounds once.
+    // z = bf16(x + residual): the fp32 sum of two bf16 values rounds to the
+    // same bf16 as their exact sum.
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
 #pragma unroll
@@ -184,83 +226,115 @@ __global__ void __launch_bounds__(kBlock)
         a.v[i][k] = pack_bf16x2(bf16_lo(a.v[i][k]) + bf16_lo(r.v[i][k]),
                                 bf16_hi(a.v[i][k]) + bf16_hi(r.v[i][k]));
     }
-    store_row(residual + row * res_stride, a, nvec, lane);
+    if (active) store_row(residual + row * res_stride, a, nvec, rl, kStride);
   }
+
+  double ss;
+  float m;
+  row_partials(a, w, mode == RRA_Q_PER_TOKEN, ss, m);
+  row_reduce<kW>(ss, m, lds_ss, lds_m, (wave / kW) * kW, wave_in_row);
+  if (!active) return;
 
   float* scale_row = nullptr;
   if (mode == RRA_Q_PER_TOKEN) scale_row = scales + row;
   if (mode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / group);
-  rmsnorm_emit<NV>(a, w, eps, H, nvec, lane, mode, group, sscale, out + row * out_stride,
-                   scale_row);
+  rmsnorm_emit<NV>(a, w, ss, m, eps, H, nvec, rl, kStride, mode, group, sscale,
+                   out + row * out_stride, scale_row);
 }
 
-template <int NVQ, int NVKV>
-__global__ void __launch_bounds__(kBlock)
+// MLA dual RMSNorm: one token per workgroup of (kQW + kKW) waves; the first
+// kQW waves normalize the q latent (NVQ vectors per lane), the last kKW waves
+// the kv latent, and one barrier serves both row reductions.
+template <int NVQ, int NVKV, int kQW, int kKW>
+__global__ void __launch_bounds__((kQW + kKW) * kWave)
     dual_rmsnorm_quant_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
                               const uint16_t* __restrict__ q_w, float eps_q,
                               const uint16_t* __restrict__ kv, int64_t kv_stride,
                               const uint16_t* __restrict__ kv_w, float eps_kv, int mode,
                               int group, void* __restrict__ q_out, int64_t q_out_stride,
                               float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
-                              int64_t kv_out_stride, int64_t T, int Hq, int Hkv) {
-  const int lane = lane_id();
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
-  if (row >= T) return;
-  const int nq = Hq >> 3, nkv = Hkv >> 3;
+                              int64_t kv_out_stride, int Hq, int Hkv) {
+  constexpr int NV = NVQ > NVKV ? NVQ : NVKV;
+  __shared__ double lds_ss[kQW + kKW];
+  __shared__ float lds_m[kQW + kKW];
+  const int wave = wave_id();
+  const bool is_q = wave < kQW;  // wave-uniform
+  const int64_t row = blockIdx.x;
+  // This wave's latent: width, row lane, lane stride, first LDS slot, count.
+  const int H = is_q ? Hq : Hkv;
+  const int nvec = H >> 3;
+  const int rl = (is_q ? wave : wave - kQW) * kWave + lane_id();
+  const int stride = (is_q ? kQW : kKW) * kWave;
+  const int slot0 = is_q ? 0 : kQW;
 
-  // Issue every load of the token before either reduction.
-  RowVecs<NVQ> zq, wq;
-  RowVecs<NVKV> zkv, wkv;
-  load_row<NVQ, true>(zq, q + row * q_stride, nq, lane);
-  load_row<NVKV, true>(zkv, kv + row * kv_stride, nkv, lane);
-  load_row<NVQ, false>(wq, q_w, nq, lane);
-  load_row<NVKV, false>(wkv, kv_w, nkv, lane);
-
-  void* qo;
-  float* scale_row = nullptr;
-  if (mode == RRA_Q_NONE) {
-    qo = static_cast<uint16_t*>(q_out) + row * q_out_stride;
+  RowVecs<NV> z, w;
+  if (is_q) {
+    load_row<NV, true>(z, q + row * q_stride, nvec, rl, stride, true);
+    load_row<NV, false>(w, q_w, nvec, rl, stride, true);
   } else {
-    qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
-    scale_row = mode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / group);
+    load_row<NV, true>(z, kv + row * kv_stride, nvec, rl, stride, true);
+    load_row<NV, false>(w, kv_w, nvec, rl, stride, true);
   }
-  rmsnorm_emit<NVQ>(zq, wq, eps_q, Hq, nq, lane, mode, group, 0.0f, qo, scale_row);
-  rmsnorm_emit<NVKV>(zkv, wkv, eps_kv, Hkv, nkv, lane, RRA_Q_NONE, 0, 0.0f,
+  double ss;
+  float m;
+  row_partials(z, w, is_q && mode == RRA_Q_PER_TOKEN, ss, m);
+  ss = wave_sum_f64(ss);
+  m = wave_max(m);
+  if (lane_id() == 0) {
+    lds_ss[wave] = ss;
+    lds_m[wave] = m;
+  }
+  __syncthreads();
+  const int n_slots = is_q ? kQW : kKW;
+  ss = lds_ss[slot0];
+  m = lds_m[slot0];
+  for (int j = 1; j < n_slots; ++j) {
+    ss += lds_ss[slot0 + j];
+    m = fmaxf(m, lds_m[slot0 + j]);
+  }
+
+  if (is_q) {
+    void* qo;
+    float* scale_row = nullptr;
+    if (mode == RRA_Q_NONE) {
+      qo = static_cast<uint16_t*>(q_out) + row * q_out_stride;
+    } else {
+      qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
+      scale_row = mode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / group);
+    }
+    rmsnorm_emit<NV>(z, w, ss, m, eps_q, Hq, nvec, rl, stride, mode, group, 0.0f, qo, scale_row);
+  } else {
+    rmsnorm_emit<NV>(z, w, ss, 0.0f, eps_kv, Hkv, nvec, rl, stride, RRA_Q_NONE, 0, 0.0f,
                      kv_out + row * kv_out_stride, nullptr);
+  }
 }
 
+// Waves per row for the residual-add norm: enough that each lane holds at
+// most two vectors of a row up to H = 4096 (four up to 8192).
+inline int norm_waves_per_row(int64_t H) { return H <= 1024 ? 1 : (H <= 2048 ? 2 : 4); }
+
 template <bool kResidual>
-static int launch_add_rmsnorm(int nv, dim3 grid, hipStream_t st, const uint16_t* x,
-                              int64_t xs, uint16_t* res, int64_t rs, const uint16_t* w,
-                              float eps, int mode, int group, const float* sscale, uint8_t* out,
-                              int64_t os, float* scales, int64_t T, int H) {
-#define RRA_NORM_CASE(N)                                                                   \
-  case N:                                                                                  \
-    hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, kResidual>), grid, dim3(kBlock), 0, st, \
-                       x, xs, res, rs, w, eps, mode, group, sscale, out, os, scales, T, H); \
-    break;
-  switch (nv) {
-    RRA_NORM_CASE(1)
-    RRA_NORM_CASE(2)
-    RRA_NORM_CASE(3)
-    RRA_NORM_CASE(4)
-    RRA_NORM_CASE(5)
-    RRA_NORM_CASE(6)
-    RRA_NORM_CASE(7)
-    RRA_NORM_CASE(8)
-    RRA_NORM_CASE(9)
-    RRA_NORM_CASE(10)
-    RRA_NORM_CASE(11)
-    RRA_NORM_CASE(12)
-    RRA_NORM_CASE(13)
-    RRA_NORM_CASE(14)
-    RRA_NORM_CASE(15)
-    RRA_NORM_CASE(16)
-    default:
-      return RRA_ERR_UNSUPPORTED;
+static int launch_add_rmsnorm(int64_t T, int H, hipStream_t st, const uint16_t* x, int64_t xs,
+                              uint16_t* res, int64_t rs, const uint16_t* w, float eps, int mode,
+                              int group, const float* sscale, uint8_t* out, int64_t os,
+                              float* scales) {
+  const int kw = norm_waves_per_row(H);
+  const int nv = static_cast<int>(ceil_div(H, 8 * kWave * kw));
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock / kw)));
+#define RRA_NORM_CASE(N, W)                                                                 \
+  if (nv == N && kw == W) {                                                                 \
+    hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual>), grid, dim3(kBlock), 0, st, \
+                       x, xs, res, rs, w, eps, mode, group, sscale, out, os, scales, T, H);  \
+    return launch_status();                                                                 \
   }
+  RRA_NORM_CASE(1, 1)
+  RRA_NORM_CASE(2, 1)
+  RRA_NORM_CASE(2, 2)
+  RRA_NORM_CASE(2, 4)
+  RRA_NORM_CASE(3, 4)
+  RRA_NORM_CASE(4, 4)
 #undef RRA_NORM_CASE
-  return launch_status();
+  return RRA_ERR_UNSUPPORTED;
 }
 
 }  // namespace rra
@@ -302,16 +376,14 @@ extern "C" int fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint
   RRA_REQUIRE(!scales || aligned(scales, 4), RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
 
-  const int nv = static_cast<int>(ceil_div(H, 8 * kWave));
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock)));
   const int g = quant_mode == RRA_Q_PER_GROUP ? group_size : 0;
   if (residual)
-    return launch_add_rmsnorm<true>(nv, grid, as_stream(stream), x, x_stride, residual,
-                                    residual_stride, weight, eps, quant_mode, g, static_scale,
-                                    out, out_stride, scales, T, static_cast<int>(H));
-  return launch_add_rmsnorm<false>(nv, grid, as_stream(stream), x, x_stride, nullptr, 0, weight,
-                                   eps, quant_mode, g, static_scale, out, out_stride, scales, T,
-                                   static_cast<int>(H));
+    return launch_add_rmsnorm<true>(T, static_cast<int>(H), as_stream(stream), x, x_stride,
+                                    residual, residual_stride, weight, eps, quant_mode, g,
+                                    static_scale, out, out_stride, scales);
+  return launch_add_rmsnorm<false>(T, static_cast<int>(H), as_stream(stream), x, x_stride,
+                                   nullptr, 0, weight, eps, quant_mode, g, static_scale, out,
+                                   out_stride, scales);
 }
 
 extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_weight,
@@ -349,18 +421,21 @@ extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uin
   RRA_REQUIRE(!q_scales || aligned(q_scales, 4), RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
 
-  const int nvq = static_cast<int>(ceil_div(Hq, 8 * kWave));
-  const int nvkv = static_cast<int>(ceil_div(Hkv, 8 * kWave));
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock)));
+  RRA_REQUIRE(T <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);  // one workgroup per token
+
+  // One vector per lane: ceil(Hq / 512) waves for q, ceil(Hkv / 512) for kv.
+  const int qw = static_cast<int>(ceil_div(Hq, 8 * kWave));
+  const int kvw = static_cast<int>(ceil_div(Hkv, 8 * kWave));
+  const dim3 grid(static_cast<unsigned>(T));
   const hipStream_t st = as_stream(stream);
   const int g = q_quant_mode == RRA_Q_PER_GROUP ? group_size : 0;
-#define RRA_DUAL_CASE(A, B)                                                                   \
-  if (nvq == A && nvkv == B) {                                                                \
-    hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B>), grid, dim3(kBlock), 0, st, q,       \
-                       q_stride, q_weight, eps_q, kv, kv_stride, kv_weight, eps_kv,            \
-                       q_quant_mode, g, q_out, q_out_stride, q_scales, kv_out, kv_out_stride, \
-                       T, static_cast<int>(Hq), static_cast<int>(Hkv));                       \
-    return launch_status();                                                                   \
+#define RRA_DUAL_CASE(A, B)                                                                    \
+  if (qw == A && kvw == B) {                                                                   \
+    hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<1, 1, A, B>), grid, dim3((A + B) * kWave), 0, \
+                       st, q, q_stride, q_weight, eps_q, kv, kv_stride, kv_weight, eps_kv,      \
+                       q_quant_mode, g, q_out, q_out_stride, q_scales, kv_out, kv_out_stride,  \
+                       static_cast<int>(Hq), static_cast<int>(Hkv));                           \
+    return launch_status();                                                                    \
   }
   RRA_DUAL_CASE(1, 1)
   RRA_DUAL_CASE(2, 1)

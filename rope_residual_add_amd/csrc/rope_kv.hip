@@ -9,14 +9,10 @@
 // touching code": fixed-size blocks, and every token carries the slot
 // (block * block_size + offset) it writes.
 //
-// Mapping: one wavefront per token.  A head of D values has D/2 rotation
-// pairs (i, i + D/2) (GPT-NeoX layout).  Lane l takes the 8 pairs starting at
-// column c*8 with c = l % (D/16) - one 16-byte vector from each half of the
-// head, so both members of every pair sit in the same lane and no cross-lane
-// exchange is needed - for heads l / (D/16), l / (D/16) + 64/(D/16), ...
-// Every lane uses the same position, so it reads its 8 cos and 8 sin values
-// once and applies them to all of its q and k heads.  All loads of the token
-// are issued before any store because q_out may alias q.
+// Mapping: four waves per token.  The token's work is cut into 16-byte units
+// (rotation pairs of q and k heads, plain vectors of v) spread over the 256
+// lanes so that each lane issues at most a few loads before its stores; see
+// rope_kv_write_kernel.
 #include "rra_device.hpp"
 #include "rra_host.hpp"
 
@@ -34,11 +30,17 @@ __device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, const float c[8],
   }
 }
 
-// kQBatch passes of q heads are loaded together before they are rotated and
-// stored; Hq up to kQBatch * heads-per-pass needs a single batch.
-constexpr int kQBatch = 4;
+// Work of one token, in units: a q unit or a k unit is 8 rotation pairs of one
+// head (a 16-byte vector from each half of the head), a v unit is one 16-byte
+// vector of v copied into the cache.  Units are numbered q first, then k,
+// then v; row lane rl of the token's kW waves takes units rl, rl + 64 kW, ...
+// A head has D/16 units and 64 kW is a multiple of D/16, so every q or k unit
+// of a lane starts at the same column of its head: the lane reads its 8 cos
+// and 8 sin values once.  Each lane reads a q unit before writing it back, so
+// q_out may alias q.  kU units per lane are loaded before any is stored.
+constexpr int kRopeUnitsPerPass = 2;
 
-template <int D>
+template <int D, int kW>
 __global__ void __launch_bounds__(kBlock)
     rope_kv_write_kernel(const int64_t* __restrict__ positions, const uint16_t* q,
                          int64_t q_stride, uint16_t* q_out, int64_t q_out_stride,
@@ -49,19 +51,27 @@ __global__ void __launch_bounds__(kBlock)
                          uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
                          int64_t T, int Hq, int Hkv) {
   constexpr int kHalf = D / 2;
-  constexpr int kLanesPerHead = kHalf / 8;
-  constexpr int kHeadsPerPass = kWave / kLanesPerHead;
-  const int lane = lane_id();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
-  if (t >= T) return;
-  const int col = (lane % kLanesPerHead) * 8;
-  const int head0 = lane / kLanesPerHead;
+  constexpr int kUnitsPerHead = kHalf / 8;
+  constexpr int kLanes = kW * kWave;
+  constexpr int kTokensPerBlock = kWavesPerBlock / kW;
+  constexpr int kU = kRopeUnitsPerPass;
+  static_assert(kLanes % kUnitsPerHead == 0, "a lane must keep one column");
+  const int wave = wave_id();
+  const int rl = (wave % kW) * kWave + lane_id();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + wave / kW;
+  if (t >= T) return;  // no barrier in this kernel
 
   const int64_t pos = positions[t];
   const int64_t slot = slot_mapping[t];
-  const float* cs = cos_sin + pos * D + col;
+  const int col = (rl % kUnitsPerHead) * 8;
+  const int uq = Hq * kUnitsPerHead;
+  const int uk = slot >= 0 ? Hkv * kUnitsPerHead : 0;  // padding tokens: q only
+  const int uv = slot >= 0 ? Hkv * (D / 8) : 0;
+  const int total = uq + uk + uv;
+
   float c[8], s[8];
   {
+    const float* cs = cos_sin + pos * D + col;
     const f32x4 c0 = ld_f32x4(cs), c1 = ld_f32x4(cs + 4);
     const f32x4 s0 = ld_f32x4(cs + kHalf), s1 = ld_f32x4(cs + kHalf + 4);
 #pragma unroll
@@ -72,54 +82,49 @@ __global__ void __launch_bounds__(kBlock)
       s[4 + j] = s1[j];
     }
   }
-
-  // k and v of this token (read once; written only into the cache).
-  const int kv_passes = (Hkv + kHeadsPerPass - 1) / kHeadsPerPass;
-  const int v_vecs = Hkv * D / 8;
+  const uint16_t* qt = q + t * q_stride;
+  uint16_t* qo = q_out + t * q_out_stride;
   const uint16_t* kt = k + t * k_stride;
   const uint16_t* vt = v + t * v_stride;
-
-  for (int qp0 = 0; qp0 < Hq; qp0 += kQBatch * kHeadsPerPass) {
-    u32x4 lo[kQBatch], hi[kQBatch];
-#pragma unroll
-    for (int b = 0; b < kQBatch; ++b) {
-      const int h = qp0 + b * kHeadsPerPass + head0;
-      if (h < Hq) {
-        const uint16_t* p = q + t * q_stride + h * D + col;
-        lo[b] = ld_stream(p);
-        hi[b] = ld_stream(p + kHalf);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kQBatch; ++b) {
-      const int h = qp0 + b * kHeadsPerPass + head0;
-      if (h < Hq) {
-        rotate8(lo[b], hi[b], c, s);
-        uint16_t* p = q_out + t * q_out_stride + h * D + col;
-        st_stream(p, lo[b]);
-        st_stream(p + kHalf, hi[b]);
-      }
-    }
-  }
-
-  if (slot < 0) return;  // padding token: no cache write
   // The cache is [num_blocks, block_size, Hkv, D] and contiguous, so slot
   // block * block_size + offset starts at element slot * Hkv * D.
-  uint16_t* kc = key_cache + slot * Hkv * D;
-  uint16_t* vc = value_cache + slot * Hkv * D;
+  uint16_t* kc = key_cache + (slot >= 0 ? slot : 0) * Hkv * D;
+  uint16_t* vc = value_cache + (slot >= 0 ? slot : 0) * Hkv * D;
 
-  for (int kp = 0; kp < kv_passes; ++kp) {
-    const int h = kp * kHeadsPerPass + head0;
-    if (h < Hkv) {
-      u32x4 lo = ld_stream(kt + h * D + col), hi = ld_stream(kt + h * D + col + kHalf);
-      rotate8(lo, hi, c, s);
-      st_stream(kc + h * D + col, lo);
-      st_stream(kc + h * D + col + kHalf, hi);
+  for (int u0 = 0; u0 < total; u0 += kU * kLanes) {
+    u32x4 lo[kU], hi[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int u = u0 + j * kLanes + rl;
+      if (u < uq) {
+        const uint16_t* p = qt + (u / kUnitsPerHead) * D + col;
+        lo[j] = ld_stream(p);
+        hi[j] = ld_stream(p + kHalf);
+      } else if (u < uq + uk) {
+        const uint16_t* p = kt + ((u - uq) / kUnitsPerHead) * D + col;
+        lo[j] = ld_stream(p);
+        hi[j] = ld_stream(p + kHalf);
+      } else if (u < total) {
+        lo[j] = ld_stream(vt + (u - uq - uk) * 8);
+      }
     }
-  }
-  for (int i = lane; i < v_vecs; i += kWave) {
-    const int h = i / (D / 8), off = (i % (D / 8)) * 8;
-    st_stream(vc + h * D + off, ld_stream(vt + h * D + off));
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int u = u0 + j * kLanes + rl;
+      if (u < uq) {
+        rotate8(lo[j], hi[j], c, s);
+        uint16_t* p = qo + (u / kUnitsPerHead) * D + col;
+        st_stream(p, lo[j]);
+        st_stream(p + kHalf, hi[j]);
+      } else if (u < uq + uk) {
+        rotate8(lo[j], hi[j], c, s);
+        uint16_t* p = kc + ((u - uq) / kUnitsPerHead) * D + col;
+        st_stream(p, lo[j]);
+        st_stream(p + kHalf, hi[j]);
+      } else if (u < total) {
+        st_stream(vc + (u - uq - uk) * 8, lo[j]);
+      }
+    }
   }
 }
 
@@ -182,12 +187,15 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   RRA_REQUIRE(aligned(positions, 8) && aligned(slot_mapping, 8), RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
 
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock)));
+  // Four waves (256 lanes) per token: each lane carries at most a few units.
+  constexpr int kW = 4;
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock / kW)));
+  RRA_REQUIRE(ceil_div(T, kWavesPerBlock / kW) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
   const hipStream_t st = as_stream(stream);
 #define RRA_ROPE_CASE(DD)                                                                     \
   case DD:                                                                                    \
-    hipLaunchKernelGGL((rope_kv_write_kernel<DD>), grid, dim3(kBlock), 0, st, positions, q,  \
-                       q_stride, q_out, q_out_stride, k, k_stride, v, v_stride, cos_sin,      \
+    hipLaunchKernelGGL((rope_kv_write_kernel<DD, kW>), grid, dim3(kBlock), 0, st, positions,  \
+                       q, q_stride, q_out, q_out_stride, k, k_stride, v, v_stride, cos_sin,   \
                        slot_mapping, key_cache, value_cache, T, Hq, Hkv);                     \
     break;
   switch (D) {

@@ -100,6 +100,14 @@ def test_widths(rra, oracle, H, mode, g):
     run(rra, oracle, 65, H, mode, g)
 
 
+@pytest.mark.parametrize("T,H,mode,g", [(33, 1536, 2, 0), (7, 2048, 3, 128), (3, 1024, 2, 0),
+                                        (1, 2048, 1, 0), (2, 8192, 3, 64)])
+def test_ragged_row_blocks(rra, oracle, T, H, mode, g):
+    """Token counts that leave rows of the last workgroup unused, for each
+    number of waves per row (1, 2 and 4)."""
+    run(rra, oracle, T, H, mode, g)
+
+
 @pytest.mark.parametrize("mode,g", [(2, 0), (3, 128), (1, 0)])
 def test_strided_views(rra, oracle, mode, g):
     run(rra, oracle, 19, 1024, mode, g, strided=True)
