@@ -242,71 +242,80 @@ __global__ void __launch_bounds__(kBlock)
                    out + row * out_stride, scale_row);
 }
 
-// MLA dual RMSNorm: one token per workgroup of (kQW + kKW) waves; the first
-// kQW waves normalize the q latent (NVQ vectors per lane), the last kKW waves
-// the kv latent, and one barrier serves both row reductions.
-template <int NVQ, int NVKV, int kQW, int kKW>
-__global__ void __launch_bounds__((kQW + kKW) * kWave)
+// MLA dual RMSNorm: the q and kv latents of a token are two rows handled by
+// the same kW waves (NVQ and NVKV vectors per row lane); both row reductions
+// share one LDS exchange.  Measured on MI355X at the DeepSeek-V3 shape, one
+// wave per token (four tokens per workgroup) beats spreading a token over
+// more waves: the rows are short, and a barrier per token costs more than the
+// extra vectors per lane.
+template <int NVQ, int NVKV, int kW>
+__global__ void __launch_bounds__(kBlock)
     dual_rmsnorm_quant_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
                               const uint16_t* __restrict__ q_w, float eps_q,
                               const uint16_t* __restrict__ kv, int64_t kv_stride,
                               const uint16_t* __restrict__ kv_w, float eps_kv, int mode,
                               int group, void* __restrict__ q_out, int64_t q_out_stride,
                               float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
-                              int64_t kv_out_stride, int Hq, int Hkv) {
-  constexpr int NV = NVQ > NVKV ? NVQ : NVKV;
-  __shared__ double lds_ss[kQW + kKW];
-  __shared__ float lds_m[kQW + kKW];
+                              int64_t kv_out_stride, int64_t T, int Hq, int Hkv) {
+  constexpr int kRowsPerBlock = kWavesPerBlock / kW;
+  constexpr int kStride = kW * kWave;
+  __shared__ double lds_q[kWavesPerBlock];
+  __shared__ double lds_kv[kWavesPerBlock];
+  __shared__ float lds_m[kWavesPerBlock];
   const int wave = wave_id();
-  const bool is_q = wave < kQW;  // wave-uniform
-  const int64_t row = blockIdx.x;
-  // This wave's latent: width, row lane, lane stride, first LDS slot, count.
-  const int H = is_q ? Hq : Hkv;
-  const int nvec = H >> 3;
-  const int rl = (is_q ? wave : wave - kQW) * kWave + lane_id();
-  const int stride = (is_q ? kQW : kKW) * kWave;
-  const int slot0 = is_q ? 0 : kQW;
+  const int wave_in_row = wave % kW;
+  const int rl = wave_in_row * kWave + lane_id();
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave / kW;
+  const bool active = row < T;
+  const int nq = Hq >> 3, nkv = Hkv >> 3;
 
-  RowVecs<NV> z, w;
-  if (is_q) {
-    load_row<NV, true>(z, q + row * q_stride, nvec, rl, stride, true);
-    load_row<NV, false>(w, q_w, nvec, rl, stride, true);
-  } else {
-    load_row<NV, true>(z, kv + row * kv_stride, nvec, rl, stride, true);
-    load_row<NV, false>(w, kv_w, nvec, rl, stride, true);
-  }
-  double ss;
-  float m;
-  row_partials(z, w, is_q && mode == RRA_Q_PER_TOKEN, ss, m);
-  ss = wave_sum_f64(ss);
-  m = wave_max(m);
-  if (lane_id() == 0) {
-    lds_ss[wave] = ss;
-    lds_m[wave] = m;
-  }
-  __syncthreads();
-  const int n_slots = is_q ? kQW : kKW;
-  ss = lds_ss[slot0];
-  m = lds_m[slot0];
-  for (int j = 1; j < n_slots; ++j) {
-    ss += lds_ss[slot0 + j];
-    m = fmaxf(m, lds_m[slot0 + j]);
-  }
+  // Issue every load of the token before either reduction.
+  RowVecs<NVQ> zq, wq;
+  RowVecs<NVKV> zkv, wkv;
+  load_row<NVQ, true>(zq, q + row * q_stride, nq, rl, kStride, active);
+  load_row<NVKV, true>(zkv, kv + row * kv_stride, nkv, rl, kStride, active);
+  load_row<NVQ, false>(wq, q_w, nq, rl, kStride, true);
+  load_row<NVKV, false>(wkv, kv_w, nkv, rl, kStride, true);
 
-  if (is_q) {
-    void* qo;
-    float* scale_row = nullptr;
-    if (mode == RRA_Q_NONE) {
-      qo = static_cast<uint16_t*>(q_out) + row * q_out_stride;
-    } else {
-      qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
-      scale_row = mode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / group);
+  double ss_q, ss_kv;
+  float m_q, m_kv;
+  row_partials(zq, wq, mode == RRA_Q_PER_TOKEN, ss_q, m_q);
+  row_partials(zkv, wkv, false, ss_kv, m_kv);
+  ss_q = wave_sum_f64(ss_q);
+  ss_kv = wave_sum_f64(ss_kv);
+  m_q = wave_max(m_q);
+  if (kW > 1) {
+    if (lane_id() == 0) {
+      lds_q[wave] = ss_q;
+      lds_kv[wave] = ss_kv;
+      lds_m[wave] = m_q;
     }
-    rmsnorm_emit<NV>(z, w, ss, m, eps_q, Hq, nvec, rl, stride, mode, group, 0.0f, qo, scale_row);
-  } else {
-    rmsnorm_emit<NV>(z, w, ss, 0.0f, eps_kv, Hkv, nvec, rl, stride, RRA_Q_NONE, 0, 0.0f,
-                     kv_out + row * kv_out_stride, nullptr);
+    __syncthreads();
+    const int s0 = (wave / kW) * kW;
+    ss_q = lds_q[s0];
+    ss_kv = lds_kv[s0];
+    m_q = lds_m[s0];
+#pragma unroll
+    for (int j = 1; j < kW; ++j) {
+      ss_q += lds_q[s0 + j];
+      ss_kv += lds_kv[s0 + j];
+      m_q = fmaxf(m_q, lds_m[s0 + j]);
+    }
   }
+  if (!active) return;
+
+  void* qo;
+  float* scale_row = nullptr;
+  if (mode == RRA_Q_NONE) {
+    qo = static_cast<uint16_t*>(q_out) + row * q_out_stride;
+  } else {
+    qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
+    scale_row = mode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / group);
+  }
+  rmsnorm_emit<NVQ>(zq, wq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, mode, group, 0.0f, qo,
+                    scale_row);
+  rmsnorm_emit<NVKV>(zkv, wkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kStride, RRA_Q_NONE, 0, 0.0f,
+                     kv_out + row * kv_out_stride, nullptr);
 }
 
 // Waves per row for the residual-add norm: enough that each lane holds at
@@ -421,20 +430,18 @@ extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uin
   RRA_REQUIRE(!q_scales || aligned(q_scales, 4), RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
 
-  RRA_REQUIRE(T <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);  // one workgroup per token
-
-  // One vector per lane: ceil(Hq / 512) waves for q, ceil(Hkv / 512) for kv.
-  const int qw = static_cast<int>(ceil_div(Hq, 8 * kWave));
-  const int kvw = static_cast<int>(ceil_div(Hkv, 8 * kWave));
-  const dim3 grid(static_cast<unsigned>(T));
+  // One wave per token: NVQ = ceil(Hq / 512) and NVKV = ceil(Hkv / 512) vectors per lane.
+  const int nvq = static_cast<int>(ceil_div(Hq, 8 * kWave));
+  const int nvkv = static_cast<int>(ceil_div(Hkv, 8 * kWave));
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock)));
   const hipStream_t st = as_stream(stream);
   const int g = q_quant_mode == RRA_Q_PER_GROUP ? group_size : 0;
 #define RRA_DUAL_CASE(A, B)                                                                    \
-  if (qw == A && kvw == B) {                                                                   \
-    hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<1, 1, A, B>), grid, dim3((A + B) * kWave), 0, \
-                       st, q, q_stride, q_weight, eps_q, kv, kv_stride, kv_weight, eps_kv,      \
+  if (nvq == A && nvkv == B) {                                                                 \
+    hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, 1>), grid, dim3(kBlock), 0, st, q,     \
+                       q_stride, q_weight, eps_q, kv, kv_stride, kv_weight, eps_kv,             \
                        q_quant_mode, g, q_out, q_out_stride, q_scales, kv_out, kv_out_stride,  \
-                       static_cast<int>(Hq), static_cast<int>(Hkv));                           \
+                       T, static_cast<int>(Hq), static_cast<int>(Hkv));                        \
     return launch_status();                                                                    \
   }
   RRA_DUAL_CASE(1, 1)

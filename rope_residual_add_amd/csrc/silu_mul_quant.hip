@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(kBlock)
   }
 }
 
-constexpr int kSiluNV = 2;  // 1024 output columns per wavefront
+constexpr int kSiluNV = 4;  // 2048 output columns per wavefront
 
 }  // namespace rra
 
