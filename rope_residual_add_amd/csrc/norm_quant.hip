@@ -131,7 +131,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs
                                              float m_row, float eps, int H, int nvec, int rl,
                                              int stride, int mode, int group, float static_scale,
                                              void* out, float* scale_row) {
-  const double rho = 1.0 / sqrt(ss / static_cast<double>(H) + static_cast<double>(eps));
+  const double rho = rsqrt_f64(ss / static_cast<double>(H) + static_cast<double>(eps));
   const int lane = lane_id();
 
   if (mode == RRA_Q_NONE) {
@@ -161,31 +161,24 @@ __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs
       zw8(z.v[i], w.v[i], t);
       float m = absmax8(t);
       m = group == 128 ? max16(m) : max8(m);
-      const float s = dynamic_scale(m, rho);
-      const double g = quant_gain(rho, s);
+      const QuantStep qs = quant_step(rho, dynamic_scale(m, rho));
       if (idx < nvec) {
-        if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = s;
-        st_stream(o + idx * 8, quant8(t, static_cast<float>(g), g));
+        if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = qs.s;
+        st_stream(o + idx * 8, quant8(t, qs));
       }
     }
     return;
   }
 
-  double g;
-  if (mode == RRA_Q_PER_TOKEN) {
-    const float s = dynamic_scale(m_row, rho);
-    g = quant_gain(rho, s);
-    if (rl == 0) scale_row[0] = s;
-  } else {  // RRA_Q_STATIC
-    g = rho / static_cast<double>(static_scale);
-  }
-  const float f = static_cast<float>(g);
+  const float s = mode == RRA_Q_PER_TOKEN ? dynamic_scale(m_row, rho) : static_scale;
+  if (mode == RRA_Q_PER_TOKEN && rl == 0) scale_row[0] = s;
+  const QuantStep qs = quant_step(rho, s);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = i * stride + rl;
     float t[8];
     zw8(z.v[i], w.v[i], t);
-    if (idx < nvec) st_stream(o + idx * 8, quant8(t, f, g));
+    if (idx < nvec) st_stream(o + idx * 8, quant8(t, qs));
   }
 }
 

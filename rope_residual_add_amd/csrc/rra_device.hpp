@@ -71,21 +71,19 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // two bf16 values) often stand in a short ratio such as 3/8 that puts
 // 448 * t / m exactly on an e4m3 rounding midpoint, and only the tiny offset d
 // left by rounding s to fp32 decides the side.  An fp32 quotient cannot see d.
-// So each value is first rounded as v = fp32(t * f) (within two fp32 ulps of
-// q); where v lies within 4 ulps of a midpoint, or in the e4m3 subnormal
-// range, q is recomputed in double and narrowed to fp32 with round-to-odd,
-// after which the single hardware rounding to e4m3 is the correct rounding of
-// q (fp32 keeps 20 more fraction bits than e4m3; round-to-odd makes the
-// double rounding innocuous).
+// So each value is first rounded as v = fp32(t * f) with f ~ fp32(rho / s)
+// (within 3 fp32 ulps of q); where v lies within 8 ulps of a midpoint, or in
+// the e4m3 subnormal range, q = t * rho / s is recomputed in double and
+// narrowed to fp32 with round-to-odd, after which the single hardware rounding
+// to e4m3 is the correct rounding of q (fp32 keeps 20 more fraction bits than
+// e4m3; round-to-odd makes the double rounding innocuous).
 
-// True when v (an fp32 estimate of q) may round differently from q.
+// True when v (an fp32 estimate of q) may round differently from q: its 20
+// fraction bits below e4m3's three lie within [-8, +7] ulps of 0x80000 (one
+// half of the e4m3 quantum), or |v| is below 2^-6 (e4m3 subnormals, where the
+// quantum is fixed; zero included).
 __device__ __forceinline__ bool e4m3_near_tie(float v) {
-  const uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
-  // e4m3 normals: a midpoint has the 20 fraction bits below e4m3's 3 equal
-  // to 0x80000 (one half of the e4m3 quantum).
-  const bool near_mid = ((b & 0xFFFFFu) - 0x7FFFCu) <= 8u;
-  // below 2^-6 (e4m3 subnormals) the quantum is fixed: resolve exactly.
-  return near_mid || (b < 0x3C800000u && b != 0u);
+  return ((__float_as_uint(v) + 8u) & 0xFFFF0u) == 0x80000u || fabsf(v) < 0x1p-6f;
 }
 
 // double -> fp32 rounding to odd: truncate toward zero, set the last bit if
@@ -99,19 +97,35 @@ __device__ __forceinline__ float f32_round_odd(double q) {
   return __uint_as_float(b | 1u);
 }
 
-// Eight codes e4m3fn(t[j] * g), with f = fp32(g) for the fast path.
-__device__ __forceinline__ u32x2 quant8(const float t[8], float f, double g) {
+// A quantization step: codes e4m3fn(t * rho / s).  f = fp32(rho) * rcp(s)
+// drives the fast path; rho (double) and s the exact one.  s = 0 (an all-zero
+// slice) gives f = 0 and all-zero codes.
+struct QuantStep {
+  float f;
+  float s;
+  double rho;
+};
+
+__device__ __forceinline__ QuantStep quant_step(double rho, float s) {
+  const float f = s > 0.0f ? static_cast<float>(rho) * __builtin_amdgcn_rcpf(s) : 0.0f;
+  return QuantStep{f, s, rho};
+}
+
+// Eight codes e4m3fn(t[j] * rho / s).
+__device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
   float v[8];
   bool exact = false;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    v[j] = t[j] * f;
+    v[j] = t[j] * qs.f;
     exact |= e4m3_near_tie(v[j]);
   }
-  if (exact) {
+  if (exact && qs.s > 0.0f) {
+    const double inv_s = 1.0 / static_cast<double>(qs.s);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (e4m3_near_tie(v[j])) v[j] = f32_round_odd(static_cast<double>(t[j]) * g);
+      if (e4m3_near_tie(v[j]))
+        v[j] = f32_round_odd(static_cast<double>(t[j]) * qs.rho * inv_s);
   }
   return u32x2{pack_e4m3x4(v[0], v[1], v[2], v[3]), pack_e4m3x4(v[4], v[5], v[6], v[7])};
 }
@@ -210,13 +224,23 @@ __device__ __forceinline__ float inv_scale(float s) { return s > 0.0f ? 1.0f / s
 
 // Dynamic scale from an amax given as m * rho (m >= 0 exact in fp32, rho in
 // double): s = fp32(m * rho / 448), 448 being e4m3fn's largest finite value.
+// Multiplying by the double nearest 1/448 instead of dividing changes the
+// double intermediate by at most an ulp, which moves the fp32 result only if
+// it lies within 2^-52 of an fp32 rounding boundary.
 __device__ __forceinline__ float dynamic_scale(float m, double rho) {
-  return static_cast<float>(static_cast<double>(m) * rho / 448.0);
+  return static_cast<float>(static_cast<double>(m) * rho * (1.0 / 448.0));
 }
 
-// rho / s in double, 0 for s = 0.
-__device__ __forceinline__ double quant_gain(double rho, float s) {
-  return s > 0.0f ? rho / static_cast<double>(s) : 0.0;
+// 1/sqrt(x) in double for x > 0: the hardware estimate refined by two Newton
+// steps y <- y + y/2 * (1 - x y^2), each roughly doubling the correct bits.
+__device__ __forceinline__ double rsqrt_f64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const double e = fma(-x * y, y, 1.0);
+    y = fma(0.5 * y, e, y);
+  }
+  return y;
 }
 
 }  // namespace rra
