@@ -68,6 +68,52 @@ def algo_bytes(name: str, T: int) -> int:
     return BYTES_PER_TOKEN[name] * T + BYTES_PER_LAUNCH[name]
 
 
+# ---- kernel identity: symbols and sources ----------------------------------------
+
+CSRC = os.path.join(ROOT, "rope_residual_add_amd", "csrc")
+KERNEL_SYMBOL = {
+    "fused_add_rmsnorm_quant": "add_rmsnorm_quant_kernel",
+    "silu_mul_quant": "silu_mul_quant_kernel",
+    "rope_kv_write": "rope_kv_write_kernel",
+    "dual_rmsnorm_quant": "dual_rmsnorm_quant_kernel",
+}
+KERNEL_SOURCES = {
+    "fused_add_rmsnorm_quant": ("norm_quant.hip",),
+    "dual_rmsnorm_quant": ("norm_quant.hip",),
+    "silu_mul_quant": ("silu_mul_quant.hip",),
+    "rope_kv_write": ("rope_kv.hip",),
+}
+COMMON_SOURCES = ("rra_device.hpp", "rra_host.hpp")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_kernels_T8192_hbm_traffic.md")
+
+
+def source_hash(kernel: str) -> str:
+    """sha256 (first 16 hex digits) of the sources a kernel is built from, so
+    that stored counter readings can be matched to the code they measured."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(KERNEL_SOURCES[kernel] + COMMON_SOURCES):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or the kernel's sources changed since."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    want = source_hash(kernel)
+    for line in text.splitlines():
+        cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 7 and cells[0] == kernel and cells[1] == want:
+            return int(cells[5])
+    return None
+
+
 # ---- GPU side ------------------------------------------------------------------
 
 def make_launchers(T: int, salt: int = 0, rope_state=None, only=KERNELS):
@@ -277,6 +323,87 @@ def cpu_baseline(sample_T: int):
                 per_kernel_ms={k: round(v * 1e3, 2) for k, v in secs.items()})
 
 
+# ---- profile summaries (rocprofv3 CSV -> profiles/*.md) ----------------------------
+
+def _kernel_of(symbol_name: str):
+    for k, sym in KERNEL_SYMBOL.items():
+        if f"rra::{sym}<" in symbol_name or f"rra::{sym}(" in symbol_name:
+            return k
+    return None
+
+
+def summarize_trace(stats_csv: str, out: str, command: str, T: int) -> None:
+    """Kernel-trace summary: per-kernel average duration and GB/s."""
+    import csv
+
+    lines = [f"# Kernel trace: the four fused kernels at T={T}", "",
+             "Produced by (from the repository root, after `cd /tmp && export TMPDIR=/tmp` for "
+             "the profiler):", "", "```", command, "```", "",
+             "Durations are the profiler's kernel times (AverageNs etc. of "
+             "`--stats` kernel_stats.csv). GB/s = algorithmic bytes per launch / average.", "",
+             "| kernel | symbol | calls | avg us | min us | max us | algorithmic bytes | "
+             "GB/s (avg) | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        k = _kernel_of(r["Name"])
+        if k is None:
+            continue
+        avg, mn, mx = (float(r[c]) for c in ("AverageNs", "MinNs", "MaxNs"))
+        b = algo_bytes(k, T)
+        gbps = b / avg
+        sym = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| {k} | `{sym}` | {r['Calls']} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
+                     f"{mx / 1e3:.2f} | {b} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f}% |")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, out: str, commands: str, T: int) -> None:
+    """HBM traffic per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    scaled by what the same counters read for the runtime's copy kernel on the
+    bench's 1 GiB copy (read and written bytes known)."""
+    import collections
+    import csv
+
+    def load(path, counter):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return d
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy = [n for n in fetch if "copyBuffer" in n]
+    if not copy:
+        raise SystemExit("no copy kernel in the counter run")
+    gib_kib = float(1 << 20)
+    f_copy = statistics.median(v for v in fetch[copy[0]] if v > 0.4 * gib_kib)
+    w_copy = statistics.median(v for v in write[copy[0]] if v > 0.4 * gib_kib)
+    f_scale, w_scale = gib_kib / f_copy, gib_kib / w_copy
+    lines = [f"# HBM traffic per launch at T={T} (rocprofv3 counters)", "",
+             "Produced by (from the repository root):", "", "```", commands, "```", "",
+             f"Scale factors from the runtime copy kernel (`{copy[0].split('(')[0]}`) moving "
+             f"1 GiB in the same runs: FETCH_SIZE reads {f_copy:.0f} KiB for 1 GiB read "
+             f"(x{f_scale:.4f}), WRITE_SIZE reads {w_copy:.0f} KiB for 1 GiB written "
+             f"(x{w_scale:.4f}).", "",
+             "`source` is the hash of the kernel's sources when the counters were taken "
+             "(bench.py reports `traffic` only while it matches).", "",
+             "| kernel | source | FETCH_SIZE KiB | WRITE_SIZE KiB | launches | traffic bytes | "
+             "algorithmic bytes | traffic / algorithmic |", "|---|---|---|---|---|---|---|---|"]
+    for k in KERNELS:
+        names = [n for n in fetch if _kernel_of(n) == k]
+        if not names:
+            continue
+        fv = [v for n in names for v in fetch[n]]
+        wv = [v for n in names for v in write[n]]
+        fk, wk = statistics.median(fv), statistics.median(wv)
+        traffic = int(round((fk * f_scale + wk * w_scale) * 1024))
+        b = algo_bytes(k, T)
+        lines.append(f"| {k} | `{source_hash(k)}` | {fk:.0f} | {wk:.0f} | {len(fv)} | {traffic} | "
+                     f"{b} | {traffic / b:.4f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ---- main ------------------------------------------------------------------------
 
 def main() -> int:
@@ -289,7 +416,20 @@ def main() -> int:
                     help="tokens per kernel for the oracle baseline (0 = skip)")
     ap.add_argument("--sweep", default="", help="comma-separated token counts for the "
                                                 "per-kernel cold-cache sweep")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="write a profiles/ summary from a rocprofv3 --stats run and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write a profiles/ summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--out", help="output file for --summarize-*")
+    ap.add_argument("--command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.command, args.T)
+        return 0
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.out, args.command, args.T)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the four kernels are row-independent and "
@@ -327,7 +467,8 @@ def main() -> int:
     value = step_bytes / (wall / args.steps) / 1e9
     dom = max(KERNELS, key=lambda n: kern[n]["us"])
     roofline = dict(bound="hbm", kernel=dom, achieved=kern[dom]["gbps"], peak=PEAK_HBM_GBPS,
-                    unit="GB/s", frac=kern[dom]["frac_of_peak"], traffic=None)
+                    unit="GB/s", frac=kern[dom]["frac_of_peak"], traffic=stored_traffic(dom),
+                    algorithmic_bytes=kern[dom]["bytes"])
 
     result = dict(
         metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps,
