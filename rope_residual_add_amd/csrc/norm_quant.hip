@@ -53,29 +53,20 @@ __device__ __forceinline__ void store_row(uint16_t* base, const RowVecs<NV>& r, 
   }
 }
 
-// t = z * w for the 8 columns of one vector (exact: 8-bit by 8-bit significands).
-__device__ __forceinline__ void zw8(u32x4 z, u32x4 w, float t[8]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    t[2 * k] = bf16_lo(z[k]) * bf16_lo(w[k]);
-    t[2 * k + 1] = bf16_hi(z[k]) * bf16_hi(w[k]);
-  }
-}
-
-__device__ __forceinline__ float absmax8(const float t[8]) {
-  float m = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t[j]));
-  return m;
-}
-
-// This lane's part of the row statistics: the sum of z^2 in double (each z^2
-// is exact in fp32, a bf16 having 8 significant bits, and the double sum
-// keeps enough bits that the fp32 rounding of a scale derived from it is the
-// one the plain definition gives) and, when wanted, max |z * w|.
+// A row lane's share of t = z * w in fp32 (exact: 8-bit by 8-bit
+// significands), which is all the output stage needs of z and w.
 template <int NV>
-__device__ __forceinline__ void row_partials(const RowVecs<NV>& z, const RowVecs<NV>& w,
-                                             bool want_max, double& ss, float& m) {
+struct RowT {
+  float t[NV][8];
+};
+
+// One pass over this lane's vectors: t = z * w, the sum of z^2 in double
+// (each z widened to double and squared by an fma: the sum keeps enough bits
+// that the fp32 rounding of a scale derived from it is the one the plain
+// definition gives) and, when wanted, max |t|.
+template <int NV>
+__device__ __forceinline__ void row_prepare(const RowVecs<NV>& z, const RowVecs<NV>& w,
+                                            bool want_max, RowT<NV>& t, double& ss, float& m) {
   ss = 0.0;
   m = 0.0f;
 #pragma unroll
@@ -83,13 +74,15 @@ __device__ __forceinline__ void row_partials(const RowVecs<NV>& z, const RowVecs
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float a = bf16_lo(z.v[i][k]), b = bf16_hi(z.v[i][k]);
-      ss += static_cast<double>(a * a);
-      ss += static_cast<double>(b * b);
+      const double ad = static_cast<double>(a), bd = static_cast<double>(b);
+      ss = fma(ad, ad, ss);
+      ss = fma(bd, bd, ss);
+      t.t[i][2 * k] = a * bf16_lo(w.v[i][k]);
+      t.t[i][2 * k + 1] = b * bf16_hi(w.v[i][k]);
     }
     if (want_max) {
-      float t[8];
-      zw8(z.v[i], w.v[i], t);
-      m = fmaxf(m, absmax8(t));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t.t[i][j]));
     }
   }
 }
@@ -119,17 +112,17 @@ __device__ __forceinline__ void row_reduce(double& ss, float& m, double* lds_ss,
 }
 
 // The row's output from its statistics:
-//   y = z * w * rho,  rho = 1/sqrt(ss / H + eps)
+//   y = t * rho,  rho = 1/sqrt(ss / H + eps)
 // mode NONE writes bf16(y) to out (uint16_t*); the quantizing modes write
 // e4m3fn(y / s) to out (uint8_t*) and s to scale_row (row lane 0 for a
 // per-token scale, the first lane of each group for per-group scales).
-// Because rho > 0 is one number per row, max|y| = max|z * w| * rho, so the
-// amax needs no second pass over y; t = z * w is exact in fp32 and the codes
-// are e4m3fn(t * rho / s) (quant8 rounds them as the exact quotient would).
+// Because rho > 0 is one number per row, max|y| = max|t| * rho, so the amax
+// needs no second pass over y, and the codes are e4m3fn(t * rho / s) (quant8
+// rounds them as the exact quotient would).
 template <int NV>
-__device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs<NV>& w, double ss,
-                                             float m_row, float eps, int H, int nvec, int rl,
-                                             int stride, int mode, int group, float static_scale,
+__device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float m_row,
+                                             float eps, int H, int nvec, int rl, int stride,
+                                             int mode, int group, float static_scale,
                                              void* out, float* scale_row) {
   const double rho = rsqrt_f64(ss / static_cast<double>(H) + static_cast<double>(eps));
   const int lane = lane_id();
@@ -140,12 +133,11 @@ __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = i * stride + rl;
-      float t[8];
-      zw8(z.v[i], w.v[i], t);
-      const u32x4 packed{pack_bf16x2(t[0] * rho_f, t[1] * rho_f),
-                         pack_bf16x2(t[2] * rho_f, t[3] * rho_f),
-                         pack_bf16x2(t[4] * rho_f, t[5] * rho_f),
-                         pack_bf16x2(t[6] * rho_f, t[7] * rho_f)};
+      const float* ti = t.t[i];
+      const u32x4 packed{pack_bf16x2(ti[0] * rho_f, ti[1] * rho_f),
+                         pack_bf16x2(ti[2] * rho_f, ti[3] * rho_f),
+                         pack_bf16x2(ti[4] * rho_f, ti[5] * rho_f),
+                         pack_bf16x2(ti[6] * rho_f, ti[7] * rho_f)};
       if (idx < nvec) st_stream(o + idx * 8, packed);
     }
     return;
@@ -157,14 +149,14 @@ __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = i * stride + rl;
-      float t[8];
-      zw8(z.v[i], w.v[i], t);
-      float m = absmax8(t);
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t.t[i][j]));
       m = group == 128 ? max16(m) : max8(m);
       const QuantStep qs = quant_step(rho, dynamic_scale(m, rho));
       if (idx < nvec) {
         if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = qs.s;
-        st_stream(o + idx * 8, quant8(t, qs));
+        st_stream(o + idx * 8, quant8(t.t[i], qs));
       }
     }
     return;
@@ -176,9 +168,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowVecs<NV>& z, const RowVecs
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = i * stride + rl;
-    float t[8];
-    zw8(z.v[i], w.v[i], t);
-    if (idx < nvec) st_stream(o + idx * 8, quant8(t, qs));
+    if (idx < nvec) st_stream(o + idx * 8, quant8(t.t[i], qs));
   }
 }
 
@@ -222,16 +212,17 @@ __global__ void __launch_bounds__(kBlock)
     if (active) store_row(residual + row * res_stride, a, nvec, rl, kStride);
   }
 
+  RowT<NV> t;
   double ss;
   float m;
-  row_partials(a, w, mode == RRA_Q_PER_TOKEN, ss, m);
+  row_prepare(a, w, mode == RRA_Q_PER_TOKEN, t, ss, m);
   row_reduce<kW>(ss, m, lds_ss, lds_m, (wave / kW) * kW, wave_in_row);
   if (!active) return;
 
   float* scale_row = nullptr;
   if (mode == RRA_Q_PER_TOKEN) scale_row = scales + row;
   if (mode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / group);
-  rmsnorm_emit<NV>(a, w, ss, m, eps, H, nvec, rl, kStride, mode, group, sscale,
+  rmsnorm_emit<NV>(t, ss, m, eps, H, nvec, rl, kStride, mode, group, sscale,
                    out + row * out_stride, scale_row);
 }
 
@@ -270,10 +261,12 @@ __global__ void __launch_bounds__(kBlock)
   load_row<NVQ, false>(wq, q_w, nq, rl, kStride, true);
   load_row<NVKV, false>(wkv, kv_w, nkv, rl, kStride, true);
 
+  RowT<NVQ> tq;
+  RowT<NVKV> tkv;
   double ss_q, ss_kv;
   float m_q, m_kv;
-  row_partials(zq, wq, mode == RRA_Q_PER_TOKEN, ss_q, m_q);
-  row_partials(zkv, wkv, false, ss_kv, m_kv);
+  row_prepare(zq, wq, mode == RRA_Q_PER_TOKEN, tq, ss_q, m_q);
+  row_prepare(zkv, wkv, false, tkv, ss_kv, m_kv);
   ss_q = wave_sum_f64(ss_q);
   ss_kv = wave_sum_f64(ss_kv);
   m_q = wave_max(m_q);
@@ -305,9 +298,9 @@ __global__ void __launch_bounds__(kBlock)
     qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
     scale_row = mode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / group);
   }
-  rmsnorm_emit<NVQ>(zq, wq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, mode, group, 0.0f, qo,
+  rmsnorm_emit<NVQ>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, mode, group, 0.0f, qo,
                     scale_row);
-  rmsnorm_emit<NVKV>(zkv, wkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kStride, RRA_Q_NONE, 0, 0.0f,
+  rmsnorm_emit<NVKV>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kStride, RRA_Q_NONE, 0, 0.0f,
                      kv_out + row * kv_out_stride, nullptr);
 }
 

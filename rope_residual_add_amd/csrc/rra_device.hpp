@@ -114,18 +114,19 @@ __device__ __forceinline__ QuantStep quant_step(double rho, float s) {
 // Eight codes e4m3fn(t[j] * rho / s).
 __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
   float v[8];
+  bool near[8];
   bool exact = false;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     v[j] = t[j] * qs.f;
-    exact |= e4m3_near_tie(v[j]);
+    near[j] = e4m3_near_tie(v[j]);
+    exact |= near[j];
   }
   if (exact && qs.s > 0.0f) {
-    const double inv_s = 1.0 / static_cast<double>(qs.s);
+    const double g = qs.rho / static_cast<double>(qs.s);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (e4m3_near_tie(v[j]))
-        v[j] = f32_round_odd(static_cast<double>(t[j]) * qs.rho * inv_s);
+      if (near[j]) v[j] = f32_round_odd(static_cast<double>(t[j]) * g);
   }
   return u32x2{pack_e4m3x4(v[0], v[1], v[2], v[3]), pack_e4m3x4(v[4], v[5], v[6], v[7])};
 }
@@ -217,10 +218,6 @@ __device__ __forceinline__ int wave_id() {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-
-// 1/s for a quantization scale, with s = 0 (all-zero slice) mapped to 0 so
-// that every code of the slice is +0.
-__device__ __forceinline__ float inv_scale(float s) { return s > 0.0f ? 1.0f / s : 0.0f; }
 
 // Dynamic scale from an amax given as m * rho (m >= 0 exact in fp32, rho in
 // double): s = fp32(m * rho / 448), 448 being e4m3fn's largest finite value.

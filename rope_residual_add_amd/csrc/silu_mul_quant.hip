@@ -12,10 +12,11 @@
 // 128 (64) outputs is 16 (8) consecutive lanes of one vector: the group amax is
 // a DPP row reduction.
 //
-// Arithmetic budget: at the HBM roofline this kernel has about 25 VALU slots
-// per output element on MI355X (256 CUs x 64 lanes x 2.4 GHz against 10 bytes
-// of traffic per element at 8 TB/s).  A correctly rounded expf and fp32 divide
-// would use more than that, so silu uses the hardware exp2 and reciprocal:
+// Arithmetic budget: at the HBM roofline this kernel has about 25 VALU lane
+// slots per output element on MI355X (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+// against 5 bytes of traffic per output element at 8 TB/s), and the loop
+// already needs most of them.  A correctly rounded expf and fp32 divide would
+// use more than that, so silu uses the hardware exp2 and reciprocal:
 // silu(g) * u = g * u * rcp(1 + exp2(-g * log2(e))), relative error ~1e-6,
 // which moves an FP8 code only for values within that distance of a rounding
 // midpoint.
@@ -93,8 +94,11 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(a[j]));
     m = group == 128 ? max16(m) : max8(m);
-    const float s = m / 448.0f;
-    const float f = inv_scale(s);
+    // s = amax / 448 and f = 1 / s with a multiply and the hardware
+    // reciprocal: the activation itself carries ~1e-6 relative error, so
+    // correctly rounded divisions would buy nothing here.
+    const float s = m * (1.0f / 448.0f);
+    const float f = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
     if (idx < nvec) {
       if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = s;
       st_stream(o + idx * 8, u32x2{pack_e4m3x4(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
