@@ -14,8 +14,9 @@ cold data.
 Bandwidth is counted in ALGORITHMIC bytes: each input read once and each
 output written once (per token: 7H + 4 for the norm, 5I + 4I/128 for SiLU,
 24592 for RoPE + KV write, 6704 for the MLA norm; plus the weights once per
-launch).  Per-kernel durations come from HIP events recorded on the stream the
-kernels run on, around every launch of the timed region.
+launch).  Per-kernel durations come from HIP events (created without a system
+fence) recorded on the stream the kernels run on, around every launch of the
+timed region.
 
 Prints ONE JSON line on stdout (everything else goes to stderr).  With
 --sweep it also times each kernel alone at several token counts, rotating
@@ -114,6 +115,57 @@ def stored_traffic(kernel: str):
     return None
 
 
+# ---- HIP events ----------------------------------------------------------------------
+# Kernel durations are taken with HIP events recorded on the stream the kernels
+# run on (torch's current stream, which the binding hands to the library).  The
+# events are created with hipEventDisableSystemFence: a timing marker then needs
+# no system-scope release, which otherwise adds 1-3 us to every bracketed
+# launch.  The HIP runtime is the one torch has loaded (same soname).
+
+class HipEvents:
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        self._c = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        for f in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventElapsedTime",
+                  "hipEventDestroy"):
+            getattr(self.hip, f).restype = ctypes.c_int
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def create(self, n: int) -> list:
+        out = []
+        for _ in range(n):
+            e = self._c.c_void_p()
+            self._ok(self.hip.hipEventCreateWithFlags(self._c.byref(e), self.DISABLE_SYSTEM_FENCE),
+                     "hipEventCreateWithFlags")
+            out.append(e)
+        return out
+
+    def record(self, e, stream) -> None:
+        self._ok(self.hip.hipEventRecord(e, self._c.c_void_p(stream)), "hipEventRecord")
+
+    def ms(self, a, b) -> float:
+        v = self._c.c_float()
+        self._ok(self.hip.hipEventElapsedTime(self._c.byref(v), a, b), "hipEventElapsedTime")
+        return v.value
+
+    def destroy(self, evs) -> None:
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
 # ---- GPU side ------------------------------------------------------------------
 
 def make_launchers(T: int, salt: int = 0, rope_state=None, only=KERNELS):
@@ -174,20 +226,23 @@ def run_steps(launch, steps: int, warmup: int):
             launch[n]()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)]
-          for _ in range(steps)]
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    nk = len(KERNELS)
+    ev = hip.create(steps * (nk + 1))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        e = ev[s]
-        e[0].record()
+        base = s * (nk + 1)
+        hip.record(ev[base], stream)
         for i, n in enumerate(KERNELS):
             launch[n]()
-            e[i + 1].record()
+            hip.record(ev[base + i + 1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {n: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]
+    per = {n: [hip.ms(ev[s * (nk + 1) + i], ev[s * (nk + 1) + i + 1]) for s in range(steps)]
            for i, n in enumerate(KERNELS)}
+    hip.destroy(ev)
     return wall, per
 
 
@@ -244,6 +299,8 @@ def sweep(Ts, launches_per_point: int = 30):
     rows = []
     rope_state = None
     cyc = _blocker_cycles()
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
     for T in Ts:
         for n in KERNELS:
             n_sets = max(2, min(256, -(-(1 << 30) // algo_bytes(n, T))))
@@ -255,15 +312,16 @@ def sweep(Ts, launches_per_point: int = 30):
             for s in sets:  # warm-up: one launch per set
                 s[n]()
             torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(launches_per_point)]
+            ev = hip.create(2 * launches_per_point)
             torch.cuda._sleep(cyc)  # queue the timed launches behind a spin kernel
-            for j, (a, b) in enumerate(ev):
-                a.record()
+            for j in range(launches_per_point):
+                hip.record(ev[2 * j], stream)
                 sets[j % n_sets][n]()
-                b.record()
+                hip.record(ev[2 * j + 1], stream)
             torch.cuda.synchronize()
-            ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+            ms = statistics.median(hip.ms(ev[2 * j], ev[2 * j + 1])
+                                   for j in range(launches_per_point))
+            hip.destroy(ev)
             gbps = algo_bytes(n, T) / (ms * 1e-3) / 1e9
             rows.append(dict(kernel=n, T=T, us=round(ms * 1e3, 2), gbps=round(gbps, 1),
                              frac=round(gbps / PEAK_HBM_GBPS, 4),

@@ -113,6 +113,15 @@ def test_strided_views(rra, oracle, mode, g):
     run(rra, oracle, 19, 1024, mode, g, strided=True)
 
 
+def test_static_saturation(rra, oracle):
+    """A static scale far below amax / 448 drives most |y| / s past 448: those
+    codes saturate to +-448 (0x7E / 0xFE), never NaN (0x7F / 0xFF)."""
+    out, _ = run(rra, oracle, 9, 4096, 1, static=1e-3)
+    codes = host_u8(out)
+    assert np.count_nonzero((codes & 0x7F) == 0x7E) > codes.size // 4
+    assert not np.any((codes & 0x7F) == 0x7F)
+
+
 def test_empty(rra):
     import torch
 

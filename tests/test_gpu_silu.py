@@ -60,6 +60,22 @@ def test_shapes_and_modes(rra, oracle, T, I, mode, g):
     run(rra, oracle, T, I, mode, g)
 
 
+def test_static_saturation(rra, oracle):
+    """Static scale 1e-3: most codes saturate to +-448, none become NaN."""
+    import torch
+
+    say("[silu] static saturation")
+    d = workloads.silu_inputs(5, 2048)
+    ss = torch.tensor([1e-3], dtype=torch.float32, device="cuda")
+    out, _ = rra.silu_mul_quant(dev_bf16(d["inp"]), 1, 0, ss)
+    torch.cuda.synchronize()
+    ref, _ = oracle.silu_mul_quant(d["inp"], 1, 0, 1e-3)
+    codes = host_u8(out)
+    assert_codes(codes, ref, "saturating codes")
+    assert np.count_nonzero((codes & 0x7F) == 0x7E) > codes.size // 4
+    assert not np.any((codes & 0x7F) == 0x7F)
+
+
 def test_strided(rra, oracle):
     run(rra, oracle, 9, 2048, 3, 128, strided=True)
 
