@@ -102,6 +102,17 @@ def _declare(L: ctypes.CDLL) -> None:
             _i64, _i64, _i64]
     L.orc_dual_rmsnorm_quant.argtypes = dual
     L.orc_unfused_dual_rmsnorm_quant.argtypes = dual
+    qkn = [_p, _p, _i64, _p, _p, _f32, _f64, _i64, _p, _p, _p, _i32, _i64, _i32, _i32, _i32,
+           _i32, _i32, _i64, _i32]
+    L.orc_qk_norm_rope_kv_write.argtypes = qkn
+    L.orc_unfused_qk_norm_rope_kv_write.argtypes = qkn
+    L.orc_fused_add_rmsnorm_pad.argtypes = [_p, _i64, _p, _i64, _p, _f32, _p, _i64, _i64, _i64,
+                                            _i64]
+    L.orc_mla_rope_kv_write.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _i64, _f64, _i64, _p,
+                                        _p, _i64, _i32, _i32, _i32, _i32, _i64, _i32]
+    for name in ("orc_qk_norm_rope_kv_write", "orc_unfused_qk_norm_rope_kv_write",
+                 "orc_fused_add_rmsnorm_pad", "orc_mla_rope_kv_write"):
+        getattr(L, name).restype = _i32
     for name in ("orc_fused_add_rmsnorm_quant", "orc_unfused_add_rmsnorm_quant",
                  "orc_silu_mul_quant", "orc_unfused_silu_mul_quant", "orc_rope_kv_write",
                  "orc_unfused_rope_kv_write", "orc_dual_rmsnorm_quant",
@@ -340,3 +351,88 @@ def dual_rmsnorm_quant(q, q_w, eps_q, kv, kv_w, eps_kv, q_quant_mode, group_size
 def unfused_dual_rmsnorm_quant(q, q_w, eps_q, kv, kv_w, eps_kv, q_quant_mode, group_size=0):
     return _dual("orc_unfused_dual_rmsnorm_quant", q, q_w, eps_q, kv, kv_w, eps_kv,
                  q_quant_mode, group_size)
+
+
+# ---- next rows ----------------------------------------------------------------
+
+def _qkn(fn, positions, qkv, q_weight, k_weight, eps, theta, max_pos, Hq, Hkv, D,
+         slot_mapping=None, key_cache=None, value_cache=None, write_k=False, rot_dim=None,
+         is_neox=True):
+    rot_dim = D if rot_dim is None else rot_dim
+    positions = np.ascontiguousarray(positions, dtype=np.int64)
+    T = positions.shape[0]
+    qkv = np.array(qkv, dtype=np.uint16, copy=True).reshape(T, -1)
+    qkv, qs = _rows(qkv, np.uint16)
+    slots = None if slot_mapping is None else np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    kc = vc = None
+    num_blocks, block_size = 1, 1
+    if key_cache is not None:
+        kc = np.ascontiguousarray(key_cache, dtype=np.uint16).copy()
+        vc = np.ascontiguousarray(value_cache, dtype=np.uint16).copy()
+        num_blocks, block_size = kc.shape[0], kc.shape[1]
+    rc = getattr(lib(), fn)(_ptr(positions), _ptr(qkv), qs,
+                            _ptr(np.ascontiguousarray(q_weight, np.uint16)),
+                            _ptr(np.ascontiguousarray(k_weight, np.uint16)), float(eps),
+                            float(theta), int(max_pos), _ptr(slots), _ptr(kc), _ptr(vc),
+                            int(bool(write_k)), T, Hq, Hkv, D, rot_dim, block_size, num_blocks,
+                            int(bool(is_neox)))
+    _check(fn, rc)
+    return qkv, kc, vc
+
+
+def qk_norm_rope_kv_write(positions, qkv, q_weight, k_weight, eps, theta, max_pos, Hq, Hkv, D,
+                          **kw):
+    """Per-head RMSNorm of q and k in the packed qkv rows, then RoPE; optional
+    paged cache write.  Returns (qkv', key_cache' or None, value_cache' or None);
+    the inputs are not modified."""
+    return _qkn("orc_qk_norm_rope_kv_write", positions, qkv, q_weight, k_weight, eps, theta,
+                max_pos, Hq, Hkv, D, **kw)
+
+
+def unfused_qk_norm_rope_kv_write(positions, qkv, q_weight, k_weight, eps, theta, max_pos, Hq,
+                                  Hkv, D, **kw):
+    return _qkn("orc_unfused_qk_norm_rope_kv_write", positions, qkv, q_weight, k_weight, eps,
+                theta, max_pos, Hq, Hkv, D, **kw)
+
+
+def fused_add_rmsnorm_pad(x, residual, weight, eps, H_pad):
+    """Returns (out [T, H_pad] bf16 bits, updated residual or None)."""
+    x, xs = _rows(x, np.uint16)
+    T, H = x.shape
+    res, rs = (None, 0)
+    if residual is not None:
+        res, rs = _rows(residual.copy(), np.uint16)
+    out = np.full((T, H_pad), 0xFFFF, np.uint16)  # every column must be written
+    rc = lib().orc_fused_add_rmsnorm_pad(_ptr(x), xs, _ptr(res), rs,
+                                         _ptr(np.ascontiguousarray(weight, np.uint16)),
+                                         float(eps), _ptr(out), H_pad, T, H, H_pad)
+    _check("orc_fused_add_rmsnorm_pad", rc)
+    return out, res
+
+
+def mla_rope_kv_write(positions, q, k_pe, kv_c, theta, max_pos, slot_mapping, kv_cache, Hq,
+                      rope_dim, q_head_stride=None, q_pe_offset=0, is_neox=False):
+    """q: [T, Hq * q_head_stride] bf16 rows whose heads hold their rope part at
+    columns [q_pe_offset, q_pe_offset + rope_dim); k_pe: [T, rope_dim];
+    kv_c: [T, kv_lora]; kv_cache: [num_blocks, block_size, kv_lora + rope_dim].
+    Returns (q', kv_cache'); the inputs are not modified."""
+    positions = np.ascontiguousarray(positions, dtype=np.int64)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    T = positions.shape[0]
+    q = np.array(q, dtype=np.uint16, copy=True).reshape(T, -1)
+    q, qs = _rows(q, np.uint16)
+    q_head_stride = rope_dim if q_head_stride is None else q_head_stride
+    k_pe, ks = _rows(np.ascontiguousarray(k_pe, np.uint16).reshape(T, -1), np.uint16)
+    kv_c, cs = _rows(np.ascontiguousarray(kv_c, np.uint16).reshape(T, -1), np.uint16)
+    cache = np.ascontiguousarray(kv_cache, dtype=np.uint16).copy()
+    num_blocks, block_size, width = cache.shape
+    kv_lora = kv_c.shape[1]
+    if width != kv_lora + rope_dim:
+        raise ValueError("cache width must be kv_lora + rope_dim")
+    q_view = q[:, q_pe_offset:]
+    rc = lib().orc_mla_rope_kv_write(_ptr(positions), q_view.ctypes.data, qs, q_head_stride,
+                                     _ptr(k_pe), ks, _ptr(kv_c), cs, float(theta),
+                                     int(max_pos), _ptr(slots), _ptr(cache), T, Hq, kv_lora,
+                                     rope_dim, block_size, num_blocks, int(bool(is_neox)))
+    _check("orc_mla_rope_kv_write", rc)
+    return q, cache

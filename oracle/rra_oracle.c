@@ -647,3 +647,207 @@ int orc_unfused_dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const ui
                   kv_out + t * kv_out_stride, NULL);
   return ORC_OK;
 }
+
+/* ======================================================================= */
+/* Next rows: QK norm + RoPE (+ KV write), RMSNorm + padding, MLA RoPE +    */
+/* cache concat                                                             */
+/* ======================================================================= */
+
+/* Rotate one head held in double (y[0..D)) and round once to bf16.  Pairs as
+ * in rotate_head; dimensions at and past rot_dim pass through (rounded). */
+static void rotate_head_f64(const double* y, uint16_t* out, const double* c, const double* s,
+                            int D, int rot_dim, int is_neox) {
+  const int half = rot_dim / 2;
+  for (int i = 0; i < half; ++i) {
+    const int a = is_neox ? i : 2 * i;
+    const int b = is_neox ? i + half : 2 * i + 1;
+    out[a] = orc_bf16_encode(y[a] * c[i] - y[b] * s[i]);
+    out[b] = orc_bf16_encode(y[b] * c[i] + y[a] * s[i]);
+  }
+  for (int d = rot_dim; d < D; ++d) out[d] = orc_bf16_encode(y[d]);
+}
+
+/* Per-head RMSNorm of one head of D values with a weight of D values, then
+ * the rotation.  round_between = 1 rounds the normalized head to bf16 first,
+ * as the unfused sequence materializes it; the fused op rounds once. */
+static void norm_rope_head(const uint16_t* in, const uint16_t* w, float eps, int D,
+                           const double* c, const double* s, int rot_dim, int is_neox,
+                           int round_between, uint16_t* out) {
+  double* z = (double*)calloc((size_t)D, sizeof(double));
+  double* y = (double*)calloc((size_t)D, sizeof(double));
+  for (int d = 0; d < D; ++d) z[d] = orc_bf16_decode(in[d]);
+  rms_norm_row(z, w, eps, D, y);
+  if (round_between)
+    for (int d = 0; d < D; ++d) y[d] = orc_bf16_decode(orc_bf16_encode(y[d]));
+  rotate_head_f64(y, out, c, s, D, rot_dim, is_neox);
+  free(z);
+  free(y);
+}
+
+static int qknorm_args_ok(int64_t T, int Hq, int Hkv, int D, int rot_dim, int block_size,
+                          int64_t num_blocks, int is_neox, int64_t qkv_stride) {
+  return rope_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox) &&
+         qkv_stride >= (int64_t)(Hq + 2 * Hkv) * D;
+}
+
+static int qknorm_common(const int64_t* positions, uint16_t* qkv, int64_t qkv_stride,
+                         const uint16_t* q_weight, const uint16_t* k_weight, float eps,
+                         double theta, int64_t max_pos, const int64_t* slot_mapping,
+                         uint16_t* key_cache, uint16_t* value_cache, int write_k, int64_t T,
+                         int Hq, int Hkv, int D, int rot_dim, int block_size, int64_t num_blocks,
+                         int is_neox, int round_between) {
+  if (!qknorm_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox, qkv_stride))
+    return ORC_EARG;
+  const int with_cache = slot_mapping != NULL;
+  if (with_cache && (!key_cache || !value_cache)) return ORC_EARG;
+  if (!with_cache) {
+    for (int64_t t = 0; t < T; ++t)
+      if (positions[t] < 0 || positions[t] >= max_pos) return ORC_ECONTRACT;
+  } else if (!rope_contract_ok(positions, max_pos, slot_mapping, T, block_size, num_blocks)) {
+    return ORC_ECONTRACT;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* c = (double*)malloc((size_t)rot_dim / 2 * sizeof(double));
+    double* s = (double*)malloc((size_t)rot_dim / 2 * sizeof(double));
+    uint16_t* kr = (uint16_t*)malloc((size_t)D * sizeof(uint16_t));
+    rope_angles(positions[t], theta, rot_dim, c, s);
+    uint16_t* row = qkv + t * qkv_stride;
+    uint16_t* k = row + (int64_t)Hq * D;
+    const uint16_t* v = k + (int64_t)Hkv * D;
+    for (int h = 0; h < Hq; ++h)
+      norm_rope_head(row + (int64_t)h * D, q_weight, eps, D, c, s, rot_dim, is_neox,
+                     round_between, row + (int64_t)h * D);
+    const int64_t slot = with_cache ? slot_mapping[t] : -1;
+    for (int h = 0; h < Hkv; ++h) {
+      norm_rope_head(k + (int64_t)h * D, k_weight, eps, D, c, s, rot_dim, is_neox,
+                     round_between, kr);
+      if (slot >= 0) {
+        memcpy(cache_head(key_cache, slot, block_size, Hkv, D, h), kr,
+               (size_t)D * sizeof(uint16_t));
+        memcpy(cache_head(value_cache, slot, block_size, Hkv, D, h), v + (int64_t)h * D,
+               (size_t)D * sizeof(uint16_t));
+      }
+      if (write_k) memcpy(k + (int64_t)h * D, kr, (size_t)D * sizeof(uint16_t));
+    }
+    free(c);
+    free(s);
+    free(kr);
+  }
+  return ORC_OK;
+}
+
+/* QK norm + RoPE, optionally with the paged KV-cache write.
+ * [FUSION] section "QK Norm + RoPE (enable_qk_norm_rope_fusion)": split the
+ * packed qkv row, RMSNorm every q head and every k head (each with its own
+ * weight), then the rotary embedding, as one op on qkv.  The q part of qkv is
+ * overwritten in place.  The cache write continues it the way section
+ * "RoPE + KV-Cache Update" continues plain RoPE (the fuse_qk_norm_rope_kvcache
+ * flag is only named on the pages): with slot_mapping given, the rotated k
+ * and the unchanged v go to the token's slot; write_k = 1 also writes the
+ * rotated k back into qkv.  Readings: per-head RMSNorm over the D values of a
+ * head, one weight of D values per q and per k shared by all heads, one eps;
+ * one rounding of each output. */
+int orc_qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, int64_t qkv_stride,
+                              const uint16_t* q_weight, const uint16_t* k_weight, float eps,
+                              double theta, int64_t max_pos, const int64_t* slot_mapping,
+                              uint16_t* key_cache, uint16_t* value_cache, int write_k,
+                              int64_t T, int Hq, int Hkv, int D, int rot_dim, int block_size,
+                              int64_t num_blocks, int is_neox) {
+  return qknorm_common(positions, qkv, qkv_stride, q_weight, k_weight, eps, theta, max_pos,
+                       slot_mapping, key_cache, value_cache, write_k, T, Hq, Hkv, D, rot_dim,
+                       block_size, num_blocks, is_neox, 0);
+}
+
+/* The unfused sequence of the same section: rms_norm materializes q_norm and
+ * k_norm as bf16, then rotary_embedding (and the cache update) runs on them. */
+int orc_unfused_qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv,
+                                      int64_t qkv_stride, const uint16_t* q_weight,
+                                      const uint16_t* k_weight, float eps, double theta,
+                                      int64_t max_pos, const int64_t* slot_mapping,
+                                      uint16_t* key_cache, uint16_t* value_cache, int write_k,
+                                      int64_t T, int Hq, int Hkv, int D, int rot_dim,
+                                      int block_size, int64_t num_blocks, int is_neox) {
+  return qknorm_common(positions, qkv, qkv_stride, q_weight, k_weight, eps, theta, max_pos,
+                       slot_mapping, key_cache, value_cache, write_k, T, Hq, Hkv, D, rot_dim,
+                       block_size, num_blocks, is_neox, 1);
+}
+
+/* Residual add + RMSNorm + padding.
+ * [FUSION] section "RMSNorm + Padding (fuse_act_padding)": residual add and
+ * RMSNorm, then padding of the hidden dimension to the width the next GEMM
+ * wants, as one op (GPT-OSS, hidden 2880).  Readings: the normalized row is
+ * written in bf16 to out[:, 0:H] and the pad columns out[:, H:H_pad] are +0;
+ * the residual is updated in place as in "RMSNorm + Quantization"; H_pad is
+ * the caller's choice (the pages do not give the multiple). */
+int orc_fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residual,
+                              int64_t res_stride, const uint16_t* weight, float eps,
+                              uint16_t* out, int64_t out_stride, int64_t T, int64_t H,
+                              int64_t H_pad) {
+  if (T < 0 || H <= 0 || H_pad < H || out_stride < H_pad) return ORC_EARG;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* z = (double*)malloc((size_t)H * sizeof(double));
+    double* y = (double*)malloc((size_t)H * sizeof(double));
+    const uint16_t* xr = x + t * x_stride;
+    for (int64_t j = 0; j < H; ++j) z[j] = orc_bf16_decode(xr[j]);
+    if (residual) {
+      uint16_t* rr = residual + t * res_stride;
+      for (int64_t j = 0; j < H; ++j) {
+        rr[j] = orc_bf16_encode(z[j] + orc_bf16_decode(rr[j]));
+        z[j] = orc_bf16_decode(rr[j]);
+      }
+    }
+    rms_norm_row(z, weight, eps, H, y);
+    uint16_t* o = out + t * out_stride;
+    for (int64_t j = 0; j < H; ++j) o[j] = orc_bf16_encode(y[j]);
+    for (int64_t j = H; j < H_pad; ++j) o[j] = 0;
+    free(z);
+    free(y);
+  }
+  return ORC_OK;
+}
+
+/* MLA: RoPE of the rope parts of q and k, and the MLA cache write of the
+ * concatenation [kv_c | rotated k_pe].  The fuse_rope_kvcache_cat_mla flag is
+ * only named on the pages ([LEVELS]); the reading joins the MLA split of
+ * [FUSION] section "MLA Dual RMSNorm" (kv_lora -> kv_c, k_pe) with the
+ * RoPE + KV-cache fusion of section "RoPE + KV-Cache Update": q_pe (Hq heads
+ * of rope_dim, head stride q_head_stride) is rotated in place, k_pe (one head
+ * of rope_dim shared by all q heads) is rotated, and the cache row of the
+ * token's slot, [num_blocks, block_size, kv_lora + rope_dim], receives kv_c
+ * (a bit copy: it is already normalized) followed by the rotated k_pe.  Tokens
+ * with a negative slot write no cache. */
+int orc_mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64_t q_stride,
+                          int64_t q_head_stride, const uint16_t* k_pe, int64_t k_pe_stride,
+                          const uint16_t* kv_c, int64_t kv_c_stride, double theta,
+                          int64_t max_pos, const int64_t* slot_mapping, uint16_t* kv_cache,
+                          int64_t T, int Hq, int kv_lora, int rope_dim, int block_size,
+                          int64_t num_blocks, int is_neox) {
+  if (T < 0 || Hq <= 0 || kv_lora <= 0 || rope_dim <= 0 || rope_dim % 2 != 0 ||
+      block_size <= 0 || num_blocks <= 0 || q_head_stride < rope_dim ||
+      q_stride < (int64_t)(Hq - 1) * q_head_stride + rope_dim || (is_neox != 0 && is_neox != 1))
+    return ORC_EARG;
+  if (!rope_contract_ok(positions, max_pos, slot_mapping, T, block_size, num_blocks))
+    return ORC_ECONTRACT;
+  const int64_t row_w = (int64_t)kv_lora + rope_dim;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* c = (double*)malloc((size_t)rope_dim / 2 * sizeof(double));
+    double* s = (double*)malloc((size_t)rope_dim / 2 * sizeof(double));
+    rope_angles(positions[t], theta, rope_dim, c, s);
+    for (int h = 0; h < Hq; ++h) {
+      uint16_t* qh = q_pe + t * q_stride + (int64_t)h * q_head_stride;
+      rotate_head(qh, qh, c, s, rope_dim, rope_dim, is_neox);
+    }
+    const int64_t slot = slot_mapping[t];
+    if (slot >= 0) {
+      uint16_t* dst = kv_cache + slot * row_w;  /* [num_blocks, block_size] flattened */
+      memcpy(dst, kv_c + t * kv_c_stride, (size_t)kv_lora * sizeof(uint16_t));
+      rotate_head(k_pe + t * k_pe_stride, dst + kv_lora, c, s, rope_dim, rope_dim, is_neox);
+    }
+    free(c);
+    free(s);
+  }
+  return ORC_OK;
+}

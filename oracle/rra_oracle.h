@@ -18,6 +18,8 @@
  *   [FUSION]  vLLM design page "Fusion torch.compile passes"
  *   [TUNING]  blog "Making vLLM fast: configuration, internals, and the places
  *             worth touching code" (section on PagedAttention)
+ *   [LEVELS]  blog "vLLM optimization levels explained: -O0 to -O3" (the
+ *             fusion flag names only)
  *   [OFP8]    OCP 8-bit Floating Point Specification (OFP8), E4M3 encoding
  * Where the pages leave a step open, the reading taken is stated at the
  * function.
@@ -120,6 +122,39 @@ int orc_unfused_rope_kv_write(const int64_t* positions, const uint16_t* q, int64
                               const int64_t* slot_mapping, uint16_t* key_cache,
                               uint16_t* value_cache, int64_t T, int Hq, int Hkv, int D,
                               int rot_dim, int block_size, int64_t num_blocks, int is_neox);
+
+/* ---- next rows ---------------------------------------------------------- */
+/* qkv: [T, (Hq + 2 Hkv) D], row stride qkv_stride; the q part (and with
+ * write_k the k part) is overwritten.  slot_mapping NULL: no cache write. */
+int orc_qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, int64_t qkv_stride,
+                              const uint16_t* q_weight, const uint16_t* k_weight, float eps,
+                              double theta, int64_t max_pos, const int64_t* slot_mapping,
+                              uint16_t* key_cache, uint16_t* value_cache, int write_k,
+                              int64_t T, int Hq, int Hkv, int D, int rot_dim, int block_size,
+                              int64_t num_blocks, int is_neox);
+int orc_unfused_qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv,
+                                      int64_t qkv_stride, const uint16_t* q_weight,
+                                      const uint16_t* k_weight, float eps, double theta,
+                                      int64_t max_pos, const int64_t* slot_mapping,
+                                      uint16_t* key_cache, uint16_t* value_cache, int write_k,
+                                      int64_t T, int Hq, int Hkv, int D, int rot_dim,
+                                      int block_size, int64_t num_blocks, int is_neox);
+
+/* out: [T, H_pad] bf16; columns H..H_pad are written as +0. */
+int orc_fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residual,
+                              int64_t res_stride, const uint16_t* weight, float eps,
+                              uint16_t* out, int64_t out_stride, int64_t T, int64_t H,
+                              int64_t H_pad);
+
+/* q_pe: Hq heads of rope_dim at head stride q_head_stride inside rows of
+ * q_stride, rotated in place; kv_cache: [num_blocks, block_size,
+ * kv_lora + rope_dim]. */
+int orc_mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64_t q_stride,
+                          int64_t q_head_stride, const uint16_t* k_pe, int64_t k_pe_stride,
+                          const uint16_t* kv_c, int64_t kv_c_stride, double theta,
+                          int64_t max_pos, const int64_t* slot_mapping, uint16_t* kv_cache,
+                          int64_t T, int Hq, int kv_lora, int rope_dim, int block_size,
+                          int64_t num_blocks, int is_neox);
 
 #ifdef __cplusplus
 }

@@ -88,6 +88,53 @@ MLA = MlaCfg("mla", Ts=(1, 1024, 8192, 16384))
 HEADLINE_T = 8192
 
 
+@dataclasses.dataclass(frozen=True)
+class QkNormCfg:
+    """Per-head QK RMSNorm + RoPE + paged KV write (Qwen3-8B attention shape)."""
+    name: str = "qknorm"
+    Hq: int = 32
+    Hkv: int = 8
+    D: int = 128
+    eps: float = 1e-6
+    theta: float = 1000000.0
+    max_pos: int = 8192
+    num_blocks: int = 4096
+    block_size: int = 16
+    Ts: tuple = (16, 2048, 8192)
+
+
+@dataclasses.dataclass(frozen=True)
+class PadCfg:
+    """Residual add + RMSNorm + padding (GPT-OSS hidden 2880 -> 3072)."""
+    name: str = "pad"
+    H: int = 2880
+    H_pad: int = 3072
+    eps: float = 1e-5
+    Ts: tuple = (16, 2048, 8192)
+
+
+@dataclasses.dataclass(frozen=True)
+class MlaRopeCfg:
+    """MLA q_pe / k_pe RoPE + [kv_c | k_pe] cache write (DeepSeek-V3: 128
+    heads of nope 128 + rope 64, kv_lora 512, GPT-J pairing)."""
+    name: str = "mla_rope"
+    Hq: int = 128
+    nope: int = 128
+    rope_dim: int = 64
+    kv_lora: int = 512
+    theta: float = 10000.0
+    max_pos: int = 8192
+    num_blocks: int = 1024
+    block_size: int = 64
+    is_neox: bool = False
+    Ts: tuple = (16, 2048, 8192)
+
+
+QKNORM = QkNormCfg()
+PAD = PadCfg()
+MLA_ROPE = MlaRopeCfg()
+
+
 def _rng(tag: str, T: int, index: int, salt: int = 0) -> np.random.Generator:
     return np.random.default_rng((_TAGS[tag], int(T), int(index), int(salt)))
 
@@ -148,6 +195,52 @@ def sentinel_cache(shape, index: int, salt: int = 0) -> np.ndarray:
     """Random bf16 bit patterns (finite: exponent field below all-ones)."""
     r = _rng("rope", 0, index, salt).integers(0, 1 << 16, size=shape, dtype=np.uint16)
     return (r & np.uint16(0xBFFF)).astype(np.uint16)  # clear the top exponent bit
+
+
+def qknorm_inputs(T: int, cfg: QkNormCfg = QKNORM, salt: int = 0, with_cache: bool = True):
+    """qkv [T, (Hq + 2 Hkv) D] ~ N(0,1); q and k norm weights ~ N(1, 0.1) of D;
+    positions uniform in [0, max_pos); distinct slots; sentinel caches."""
+    n_slots = cfg.num_blocks * cfg.block_size
+    if T > n_slots:
+        raise ValueError("more tokens than cache slots")
+    d = dict(
+        qkv=bf16_normal(_rng("qknorm", T, 0, salt), (T, (cfg.Hq + 2 * cfg.Hkv) * cfg.D)),
+        q_w=bf16_normal(_rng("qknorm", 0, 1, salt), (cfg.D,), mean=1.0, std=0.1),
+        k_w=bf16_normal(_rng("qknorm", 0, 2, salt), (cfg.D,), mean=1.0, std=0.1),
+        positions=_rng("qknorm", T, 3, salt).integers(0, cfg.max_pos, T, dtype=np.int64),
+        slot_mapping=_rng("qknorm", T, 4, salt).permutation(n_slots)[:T].astype(np.int64),
+    )
+    if with_cache:
+        shape = (cfg.num_blocks, cfg.block_size, cfg.Hkv, cfg.D)
+        d["key_cache"] = sentinel_cache(shape, 5, salt)
+        d["value_cache"] = sentinel_cache(shape, 6, salt)
+    return d
+
+
+def pad_inputs(T: int, cfg: PadCfg = PAD, salt: int = 0):
+    """x, residual ~ N(0,1) [T, H]; weight ~ N(1, 0.1)."""
+    return norm_inputs(T, cfg.H, salt=salt, tag="pad")
+
+
+def mla_rope_inputs(T: int, cfg: MlaRopeCfg = MLA_ROPE, salt: int = 0, with_cache: bool = True):
+    """q [T, Hq * (nope + rope_dim)], k_pe [T, rope_dim], kv_c [T, kv_lora]
+    ~ N(0,1); positions uniform; distinct slots; a sentinel cache."""
+    n_slots = cfg.num_blocks * cfg.block_size
+    if T > n_slots:
+        raise ValueError("more tokens than cache slots")
+    d = dict(
+        q=bf16_normal(_rng("mla_rope", T, 0, salt), (T, cfg.Hq * (cfg.nope + cfg.rope_dim))),
+        k_pe=bf16_normal(_rng("mla_rope", T, 1, salt), (T, cfg.rope_dim)),
+        kv_c=bf16_normal(_rng("mla_rope", T, 2, salt), (T, cfg.kv_lora)),
+        positions=_rng("mla_rope", T, 3, salt).integers(0, cfg.max_pos, T, dtype=np.int64),
+        slot_mapping=_rng("mla_rope", T, 4, salt).permutation(n_slots)[:T].astype(np.int64),
+    )
+    if with_cache:
+        r = _rng("mla_rope", 0, 5, salt).integers(
+            0, 1 << 16, size=(cfg.num_blocks, cfg.block_size, cfg.kv_lora + cfg.rope_dim),
+            dtype=np.uint16)
+        d["kv_cache"] = (r & np.uint16(0xBFFF)).astype(np.uint16)
+    return d
 
 
 def mla_inputs(T: int, cfg: MlaCfg = MLA, salt: int = 0):
