@@ -64,6 +64,26 @@ BYTES_PER_LAUNCH = {  # weights, read once per launch
 }
 KERNELS = tuple(BYTES_PER_TOKEN)
 
+# The next rows, measured beside the step (not part of it): QK norm + RoPE + KV
+# write at the Qwen3-8B attention shape, residual add + RMSNorm + padding at
+# GPT-OSS width, MLA q_pe/k_pe RoPE + [kv_c | k_pe] cache write at DeepSeek-V3.
+QK_HQ, QK_HKV, QK_D = 32, 8, 128
+PAD_H, PAD_HP = 2880, 3072
+MR_HQ, MR_NOPE, MR_ROPE, MR_LORA = 128, 128, 64, 512
+BYTES_PER_TOKEN.update({
+    "qk_norm_rope_kv_write": 2 * (QK_HQ + 2 * QK_HKV) * QK_D + 2 * QK_HQ * QK_D
+    + 2 * 2 * QK_HKV * QK_D + 16,
+    "fused_add_rmsnorm_pad": 2 * 2 * PAD_H + 2 * PAD_H + 2 * PAD_HP,
+    "mla_rope_kv_write": 2 * 2 * MR_HQ * MR_ROPE + 2 * MR_ROPE + 2 * MR_LORA
+    + 2 * (MR_LORA + MR_ROPE) + 16,
+})
+BYTES_PER_LAUNCH.update({
+    "qk_norm_rope_kv_write": 2 * 2 * QK_D,
+    "fused_add_rmsnorm_pad": 2 * PAD_H,
+    "mla_rope_kv_write": 0,
+})
+NEXT_KERNELS = ("qk_norm_rope_kv_write", "fused_add_rmsnorm_pad", "mla_rope_kv_write")
+
 
 def algo_bytes(name: str, T: int) -> int:
     return BYTES_PER_TOKEN[name] * T + BYTES_PER_LAUNCH[name]
@@ -77,12 +97,17 @@ KERNEL_SYMBOL = {
     "silu_mul_quant": "silu_mul_quant_kernel",
     "rope_kv_write": "rope_kv_write_kernel",
     "dual_rmsnorm_quant": "dual_rmsnorm_quant_kernel",
+    "qk_norm_rope_kv_write": "qk_norm_rope_kv_kernel",
+    "mla_rope_kv_write": "mla_rope_kv_kernel",
 }
 KERNEL_SOURCES = {
     "fused_add_rmsnorm_quant": ("norm_quant.hip",),
     "dual_rmsnorm_quant": ("norm_quant.hip",),
     "silu_mul_quant": ("silu_mul_quant.hip",),
     "rope_kv_write": ("rope_kv.hip",),
+    "qk_norm_rope_kv_write": ("rope_kv.hip",),
+    "fused_add_rmsnorm_pad": ("norm_quant.hip",),
+    "mla_rope_kv_write": ("rope_kv.hip",),
 }
 COMMON_SOURCES = ("rra_device.hpp", "rra_host.hpp")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_kernels_T8192_hbm_traffic.md")
@@ -205,6 +230,39 @@ def make_launchers(T: int, salt: int = 0, rope_state=None, only=KERNELS):
             d["positions"], d["q"], d["k"], d["v"], cs, d["slot_mapping"], kc, vc)
         L["_rope_state"] = rope_state
 
+    if "qk_norm_rope_kv_write" in only:
+        cfg = workloads.QKNORM
+        d = workloads.device_qknorm_inputs(T, cfg, dev, salt, with_cache=rope_state is None)
+        if rope_state is None:
+            kc, vc = d["key_cache"], d["value_cache"]
+            cs_q = rra.rope_cos_sin_cache(cfg.max_pos, cfg.D, cfg.theta, device=dev)
+        else:
+            kc, vc, cs_q = rope_state
+        L["qk_norm_rope_kv_write"] = lambda d=d, kc=kc, vc=vc, cs=cs_q: rra.qk_norm_rope_kv_write(
+            d["positions"], d["qkv"], d["q_w"], d["k_w"], cfg.eps, cs, cfg.Hq, cfg.Hkv, cfg.D,
+            slot_mapping=d["slot_mapping"], key_cache=kc, value_cache=vc)
+        L["_rope_state"] = (kc, vc, cs_q)
+
+    if "fused_add_rmsnorm_pad" in only:
+        cfg = workloads.PAD
+        d = workloads.device_pad_inputs(T, cfg, dev, salt)
+        out = torch.empty((T, cfg.H_pad), dtype=torch.bfloat16, device=dev)
+        L["fused_add_rmsnorm_pad"] = lambda d=d, out=out: rra.fused_add_rmsnorm_pad(
+            d["x"], d["residual"], d["weight"], cfg.eps, cfg.H_pad, out)
+
+    if "mla_rope_kv_write" in only:
+        cfg = workloads.MLA_ROPE
+        d = workloads.device_mla_rope_inputs(T, cfg, dev, salt, with_cache=rope_state is None)
+        if rope_state is None:
+            cache = d["kv_cache"]
+            cs_m = rra.rope_cos_sin_cache(cfg.max_pos, cfg.rope_dim, cfg.theta, device=dev)
+        else:
+            cache, cs_m = rope_state
+        L["mla_rope_kv_write"] = lambda d=d, cache=cache, cs=cs_m: rra.mla_rope_kv_write(
+            d["positions"], d["q"], d["k_pe"], d["kv_c"], cs, d["slot_mapping"], cache, cfg.Hq,
+            cfg.rope_dim, cfg.nope + cfg.rope_dim, cfg.nope, is_neox=cfg.is_neox)
+        L["_rope_state"] = (cache, cs_m)
+
     if "dual_rmsnorm_quant" in only:
         d = workloads.device_mla_inputs(T, workloads.MLA, dev, salt)
         qo = torch.empty((T, MLA_HQ), dtype=torch.float8_e4m3fn, device=dev)
@@ -290,24 +348,24 @@ def copy_ceiling(nbytes: int = 1 << 30, n_pairs: int = 4, reps: int = 12) -> dic
                      f"rotating buffer pairs")
 
 
-def sweep(Ts, launches_per_point: int = 30):
+def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS):
     """Each kernel alone at each T, rotating over buffer sets of that kernel
     that total at least 1 GiB of algorithmic traffic (four times the 256 MB
     last-level cache), so every launch reads cold data."""
     import torch
 
     rows = []
-    rope_state = None
     cyc = _blocker_cycles()
     hip = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
     for T in Ts:
-        for n in KERNELS:
+        for n in kernels:
             n_sets = max(2, min(256, -(-(1 << 30) // algo_bytes(n, T))))
             sets = []
+            state = None  # one cache (and table) shared by the kernel's buffer sets
             for salt in range(n_sets):
-                L = make_launchers(T, salt, rope_state, only=(n,))
-                rope_state = L.get("_rope_state", rope_state)
+                L = make_launchers(T, salt, state, only=(n,))
+                state = L.get("_rope_state", state)
                 sets.append(L)
             for s in sets:  # warm-up: one launch per set
                 s[n]()
@@ -474,6 +532,8 @@ def main() -> int:
                     help="tokens per kernel for the oracle baseline (0 = skip)")
     ap.add_argument("--sweep", default="", help="comma-separated token counts for the "
                                                 "per-kernel cold-cache sweep")
+    ap.add_argument("--next-rows", type=int, default=1,
+                    help="1 = also time the next-row kernels alone at T (cold, rotating sets)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="write a profiles/ summary from a rocprofv3 --stats run and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -544,6 +604,9 @@ def main() -> int:
     for n in KERNELS:
         kern[n]["frac_of_copy"] = round(kern[n]["gbps"] / ceiling["gbps"], 4)
     result["copy_ceiling"] = ceiling
+    if args.next_rows:
+        result["next_rows"] = {r["kernel"]: {k: v for k, v in r.items() if k != "kernel"}
+                               for r in sweep([T], kernels=NEXT_KERNELS)}
     if args.sweep:
         result["sweep"] = sweep([int(t) for t in args.sweep.split(",") if t])
     if args.cpu_sample > 0:

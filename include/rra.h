@@ -141,9 +141,10 @@ int rope_cos_sin_cache(float* cos_sin, int64_t max_pos, int rot_dim, double thet
  *
  * For token t at position p = positions[t], every q head and k head of D
  * values is rotated pairwise, (a, b) -> (a cos - b sin, b cos + a sin), with
- * pairs (i, i + rot_dim/2) (GPT-NeoX layout, is_neox = 1) and the angles of
- * row p of cos_sin.  Rotated q goes to q_out (q_out may equal q: in-place).
- * With s = slot_mapping[t] >= 0, rotated k goes to key_cache[s / block_size,
+ * pairs (i, i + rot_dim/2) (GPT-NeoX layout, is_neox = 1) or (2i, 2i + 1)
+ * (GPT-J layout, is_neox = 0), and the angles of row p of cos_sin.  Rotated
+ * q goes to q_out (q_out may equal q: in-place).  With
+ * s = slot_mapping[t] >= 0, rotated k goes to key_cache[s / block_size,
  * s % block_size, :, :] and v, unchanged, to value_cache at the same place.
  * Tokens with s < 0 (padding) write no cache.  Nothing else is written.
  *
@@ -154,8 +155,8 @@ int rope_cos_sin_cache(float* cos_sin, int64_t max_pos, int rot_dim, double thet
  * cos_sin      [max_pos, rot_dim] fp32 (see rope_cos_sin_cache).
  * slot_mapping [T] int64.
  * key_cache, value_cache [num_blocks, block_size, Hkv, D] bf16, contiguous.
- * Limits: D in {64, 128, 256}; rot_dim == D; is_neox == 1 (the GPT-J pair
- * layout is RRA_ERR_UNSUPPORTED); Hq, Hkv >= 1; block_size >= 1.
+ * Limits: D in {64, 128, 256}; rot_dim == D; is_neox 1 (GPT-NeoX pairs
+ * (i, i + D/2)) or 0 (GPT-J pairs (2i, 2i + 1)); Hq, Hkv >= 1; block_size >= 1.
  */
 int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_stride,
                   uint16_t* q_out, int64_t q_out_stride, const uint16_t* k, int64_t k_stride,
@@ -188,6 +189,85 @@ int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_we
                        int group_size, void* q_out, int64_t q_out_stride, float* q_scales,
                        uint16_t* kv_out, int64_t kv_out_stride, int64_t T, int64_t Hq,
                        int64_t Hkv, void* stream);
+
+/*
+ * QK norm + RoPE (+ paged KV-cache write).
+ * Section "QK Norm + RoPE (enable_qk_norm_rope_fusion)": split the packed qkv
+ * row, RMSNorm each q head and each k head over its D values, then the rotary
+ * embedding, as one op on qkv.  The cache write continues it as section
+ * "RoPE + KV-Cache Update" continues plain RoPE (the pages only name that
+ * flag, fuse_qk_norm_rope_kvcache).
+ *
+ *   q_h <- rope(q_h / sqrt(mean(q_h^2) + eps) * q_weight)   for every q head
+ *   k_h  = rope(k_h / sqrt(mean(k_h^2) + eps) * k_weight)   for every k head
+ * computed in fp32 and rounded once to bf16.  q is overwritten in place in
+ * qkv.  With slot_mapping != NULL, token t with s = slot_mapping[t] >= 0
+ * writes k_h and the unchanged v_h to key_cache / value_cache[s / block_size,
+ * s % block_size, h, :] (layout and slot rules as rope_kv_write).  write_k = 1
+ * also writes k_h back into qkv (always for tokens without a slot).
+ *
+ * qkv          [T, (Hq + 2 Hkv) D] bf16: q heads, then k heads, then v heads;
+ *              row stride qkv_stride; read and written.
+ * q_weight, k_weight  [D] bf16 each.
+ * cos_sin      [max_pos, D] fp32 (see rope_cos_sin_cache).
+ * slot_mapping [T] int64 or NULL (no cache write; caches may then be NULL).
+ * Limits: D in {64, 128, 256}; rot_dim == D; is_neox 1 (pairs (i, i + D/2))
+ * or 0 (pairs (2i, 2i + 1)).
+ */
+int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, int64_t qkv_stride,
+                          const uint16_t* q_weight, const uint16_t* k_weight, float eps,
+                          const float* cos_sin, int64_t max_pos, const int64_t* slot_mapping,
+                          uint16_t* key_cache, uint16_t* value_cache, int write_k, int64_t T,
+                          int Hq, int Hkv, int D, int rot_dim, int block_size,
+                          int64_t num_blocks, int is_neox, void* stream);
+
+/*
+ * Residual add + RMSNorm + padding.
+ * Section "RMSNorm + Padding (fuse_act_padding)": residual add and RMSNorm,
+ * then the hidden dimension padded to the width the next GEMM expects
+ * (GPT-OSS: 2880), as one op.
+ *
+ *   z = bf16(x + residual); residual <- z (in place; z = x if residual NULL)
+ *   out[t, 0:H]     = bf16(z / sqrt(mean(z^2) + eps) * weight)
+ *   out[t, H:H_pad] = +0
+ *
+ * x [T, H], residual [T, H] (or NULL), out [T, H_pad] bf16 with row strides;
+ * weight [H] bf16.  H_pad is the caller's padded width.
+ * Limits: H % 8 == 0, H <= 8192; H_pad % 8 == 0, H_pad >= H.
+ */
+int fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residual,
+                          int64_t residual_stride, const uint16_t* weight, float eps,
+                          uint16_t* out, int64_t out_stride, int64_t T, int64_t H, int64_t H_pad,
+                          void* stream);
+
+/*
+ * MLA RoPE + cache concat.
+ * The MLA split of section "MLA Dual RMSNorm" (kv_lora -> kv_c, k_pe) joined
+ * with the cache write of section "RoPE + KV-Cache Update" (the pages only
+ * name this flag, fuse_rope_kvcache_cat_mla): the rope parts of q and k are
+ * rotated, and each token's cache row receives [kv_c | rotated k_pe].
+ *
+ *   q_pe[t, h, :] <- rope(q_pe[t, h, :])   for the Hq heads (in place)
+ *   kv_cache[s / block_size, s % block_size, 0:kv_lora]       = kv_c[t]
+ *   kv_cache[s / block_size, s % block_size, kv_lora:+rope_dim] = rope(k_pe[t])
+ * for s = slot_mapping[t] >= 0 (tokens with s < 0 write no cache).
+ *
+ * q_pe      rope part of head 0 of token 0; head h of token t starts at
+ *           q_pe + t * q_stride + h * q_head_stride (e.g. q + nope_dim in a
+ *           [T, Hq, nope_dim + rope_dim] q); read and written.
+ * k_pe      [T, rope_dim] bf16, row stride k_pe_stride (one head shared by all q heads).
+ * kv_c      [T, kv_lora] bf16 (already normalized), row stride kv_c_stride.
+ * cos_sin   [max_pos, rope_dim] fp32 (see rope_cos_sin_cache).
+ * kv_cache  [num_blocks, block_size, kv_lora + rope_dim] bf16, contiguous.
+ * Limits: rope_dim in {64, 128}; kv_lora % 8 == 0; q_head_stride % 8 == 0;
+ * is_neox 0 (GPT-J pairs, as DeepSeek) or 1.
+ */
+int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64_t q_stride,
+                      int64_t q_head_stride, const uint16_t* k_pe, int64_t k_pe_stride,
+                      const uint16_t* kv_c, int64_t kv_c_stride, const float* cos_sin,
+                      int64_t max_pos, const int64_t* slot_mapping, uint16_t* kv_cache,
+                      int64_t T, int Hq, int kv_lora, int rope_dim, int block_size,
+                      int64_t num_blocks, int is_neox, void* stream);
 
 /*
  * Diagnostic: out[i] = e4m3fn(in[i]) for n fp32 values, using the same device

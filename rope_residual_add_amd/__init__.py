@@ -23,7 +23,8 @@ _QUANT_NAMES = {"none": Q_NONE, "static": Q_STATIC, "per_token": Q_PER_TOKEN,
                 "per_group": Q_PER_GROUP}
 
 EXPORTS = ("rra_abi_version", "rra_status_string", "fused_add_rmsnorm_quant", "silu_mul_quant",
-           "rope_cos_sin_cache", "rope_kv_write", "dual_rmsnorm_quant", "rra_e4m3fn_encode")
+           "rope_cos_sin_cache", "rope_kv_write", "dual_rmsnorm_quant", "qk_norm_rope_kv_write",
+           "fused_add_rmsnorm_pad", "mla_rope_kv_write", "rra_e4m3fn_encode")
 
 
 class RRAError(RuntimeError):
@@ -56,6 +57,13 @@ def lib() -> ctypes.CDLL:
                                     _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _p]
         L.dual_rmsnorm_quant.argtypes = [_p, _i64, _p, _f32, _p, _i64, _p, _f32, _i32, _i32, _p,
                                          _i64, _p, _p, _i64, _i64, _i64, _i64, _p]
+        L.qk_norm_rope_kv_write.argtypes = [_p, _p, _i64, _p, _p, _f32, _p, _i64, _p, _p, _p,
+                                            _i32, _i64, _i32, _i32, _i32, _i32, _i32, _i64,
+                                            _i32, _p]
+        L.fused_add_rmsnorm_pad.argtypes = [_p, _i64, _p, _i64, _p, _f32, _p, _i64, _i64, _i64,
+                                            _i64, _p]
+        L.mla_rope_kv_write.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p,
+                                        _i64, _i32, _i32, _i32, _i32, _i64, _i32, _p]
         L.rra_e4m3fn_encode.argtypes = [_p, _p, _i64, _p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = _i32
@@ -257,6 +265,92 @@ def dual_rmsnorm_quant(q, q_weight, eps_q, kv, kv_weight, eps_kv, q_quant_mode="
             _ptr(q_scales), _ptr(kv_out), kvos, T, Hq, Hkv, _stream(q))
     _check("dual_rmsnorm_quant", st)
     return q_out, q_scales, kv_out
+
+
+def qk_norm_rope_kv_write(positions, qkv, q_weight, k_weight, eps, cos_sin, Hq, Hkv, D,
+                          slot_mapping=None, key_cache=None, value_cache=None, write_k=False,
+                          is_neox=True):
+    """Per-head RMSNorm of q and k inside the packed qkv rows, then RoPE; q is
+    updated in place in qkv (and k with write_k).  With slot_mapping, rotated
+    k and v go to the paged caches [num_blocks, block_size, Hkv, D].
+    qkv: [T, (Hq + 2 Hkv) D] bf16 with contiguous rows.  Returns qkv."""
+    T = positions.shape[0]
+    qs = _rows("qkv", qkv, _BF16, (Hq + 2 * Hkv) * D)
+    _need_cuda("positions", positions, (torch.int64,))
+    _need_cuda("cos_sin", cos_sin, (torch.float32,))
+    _vector("q_weight", q_weight, D)
+    _vector("k_weight", k_weight, D)
+    num_blocks = block_size = 0
+    if slot_mapping is not None:
+        _need_cuda("slot_mapping", slot_mapping, (torch.int64,))
+        for name, c in (("key_cache", key_cache), ("value_cache", value_cache)):
+            _need_cuda(name, c, _BF16)
+            if not c.is_contiguous() or tuple(c.shape[2:]) != (Hkv, D):
+                raise ValueError(f"{name} must be a contiguous [num_blocks, block_size, Hkv, D] "
+                                 f"tensor")
+        num_blocks, block_size = key_cache.shape[:2]
+        if tuple(value_cache.shape) != tuple(key_cache.shape):
+            raise ValueError("key_cache and value_cache must have the same shape")
+    max_pos, rot_dim = cos_sin.shape
+    with torch.cuda.device(qkv.device):
+        st = lib().qk_norm_rope_kv_write(
+            _ptr(positions), _ptr(qkv), qs, _ptr(q_weight), _ptr(k_weight), float(eps),
+            _ptr(cos_sin), max_pos, _ptr(slot_mapping), _ptr(key_cache), _ptr(value_cache),
+            int(bool(write_k)), T, Hq, Hkv, D, rot_dim, block_size, num_blocks,
+            int(bool(is_neox)), _stream(qkv))
+    _check("qk_norm_rope_kv_write", st)
+    return qkv
+
+
+def fused_add_rmsnorm_pad(x, residual, weight, eps, H_pad, out=None):
+    """Residual add + RMSNorm, written as bf16 into out[:, :H] with out[:, H:H_pad]
+    = 0 (residual updated in place).  Returns out [T, H_pad] bf16."""
+    T, H = x.shape
+    xs = _rows("x", x, _BF16)
+    rs = _rows("residual", residual, _BF16, H) if residual is not None else 0
+    _vector("weight", weight, H)
+    if out is None:
+        out = torch.empty((T, H_pad), dtype=torch.bfloat16, device=x.device)
+    os_ = _rows("out", out, _BF16, H_pad)
+    with torch.cuda.device(x.device):
+        st = lib().fused_add_rmsnorm_pad(_ptr(x), xs, _ptr(residual), rs, _ptr(weight),
+                                         float(eps), _ptr(out), os_, T, H, H_pad, _stream(x))
+    _check("fused_add_rmsnorm_pad", st)
+    return out
+
+
+def mla_rope_kv_write(positions, q, k_pe, kv_c, cos_sin, slot_mapping, kv_cache, Hq, rope_dim,
+                      q_head_stride, q_pe_offset, is_neox=False):
+    """RoPE of the rope part of each q head (in place in q: head h of a row
+    starts at h * q_head_stride, its rope part at q_pe_offset) and of k_pe, and
+    the MLA cache write of [kv_c | rotated k_pe] at each token's slot.
+    q: [T, Hq * q_head_stride] bf16; k_pe: [T, rope_dim]; kv_c: [T, kv_lora];
+    kv_cache: [num_blocks, block_size, kv_lora + rope_dim].  Returns q."""
+    T = positions.shape[0]
+    qs = _rows("q", q, _BF16)
+    ks = _rows("k_pe", k_pe, _BF16, rope_dim)
+    cs = _rows("kv_c", kv_c, _BF16)
+    kv_lora = kv_c.shape[1]
+    _need_cuda("positions", positions, (torch.int64,))
+    _need_cuda("slot_mapping", slot_mapping, (torch.int64,))
+    _need_cuda("cos_sin", cos_sin, (torch.float32,))
+    _need_cuda("kv_cache", kv_cache, _BF16)
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != kv_lora + rope_dim or \
+            not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous [num_blocks, block_size, "
+                         "kv_lora + rope_dim] tensor")
+    if q.shape[1] < (Hq - 1) * q_head_stride + q_pe_offset + rope_dim:
+        raise ValueError("q is too narrow for Hq heads of q_head_stride")
+    num_blocks, block_size = kv_cache.shape[:2]
+    max_pos = cos_sin.shape[0]
+    with torch.cuda.device(q.device):
+        st = lib().mla_rope_kv_write(
+            _ptr(positions), q.data_ptr() + 2 * q_pe_offset if q.numel() else None, qs,
+            q_head_stride, _ptr(k_pe), ks, _ptr(kv_c), cs, _ptr(cos_sin), max_pos,
+            _ptr(slot_mapping), _ptr(kv_cache), T, Hq, kv_lora, rope_dim, block_size,
+            num_blocks, int(bool(is_neox)), _stream(q))
+    _check("mla_rope_kv_write", st)
+    return q
 
 
 def e4m3fn_encode(x, out=None):

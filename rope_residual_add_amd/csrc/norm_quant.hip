@@ -174,14 +174,17 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
 
 // Residual add + RMSNorm + quant.  Workgroup = kBlock lanes = kWavesPerBlock /
 // kW rows; each row lane holds NV vectors of x, residual and weight.
+// mode NONE writes the bf16 norm to out (uint16_t) and +0 to its columns
+// [H, H_pad) (the padding variant); the quantizing modes write FP8 codes
+// (uint8_t) and take H_pad = H.
 template <int NV, int kW, bool kResidual>
 __global__ void __launch_bounds__(kBlock)
     add_rmsnorm_quant_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                              uint16_t* __restrict__ residual, int64_t res_stride,
                              const uint16_t* __restrict__ weight, float eps, int mode,
                              int group, const float* __restrict__ static_scale,
-                             uint8_t* __restrict__ out, int64_t out_stride,
-                             float* __restrict__ scales, int64_t T, int H) {
+                             void* __restrict__ out, int64_t out_stride,
+                             float* __restrict__ scales, int64_t T, int H, int H_pad) {
   constexpr int kRowsPerBlock = kWavesPerBlock / kW;
   constexpr int kStride = kW * kWave;
   __shared__ double lds_ss[kWavesPerBlock];
@@ -222,8 +225,15 @@ __global__ void __launch_bounds__(kBlock)
   float* scale_row = nullptr;
   if (mode == RRA_Q_PER_TOKEN) scale_row = scales + row;
   if (mode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / group);
+  if (mode == RRA_Q_NONE) {
+    uint16_t* o = static_cast<uint16_t*>(out) + row * out_stride;
+    rmsnorm_emit<NV>(t, ss, m, eps, H, nvec, rl, kStride, mode, group, sscale, o, nullptr);
+    for (int idx = nvec + rl; idx < (H_pad >> 3); idx += kStride)
+      st_stream(o + idx * 8, u32x4{0u, 0u, 0u, 0u});
+    return;
+  }
   rmsnorm_emit<NV>(t, ss, m, eps, H, nvec, rl, kStride, mode, group, sscale,
-                   out + row * out_stride, scale_row);
+                   static_cast<uint8_t*>(out) + row * out_stride, scale_row);
 }
 
 // MLA dual RMSNorm: the q and kv latents of a token are two rows handled by
@@ -309,9 +319,9 @@ __global__ void __launch_bounds__(kBlock)
 inline int norm_waves_per_row(int64_t H) { return H <= 1024 ? 1 : (H <= 2048 ? 2 : 4); }
 
 template <bool kResidual>
-static int launch_add_rmsnorm(int64_t T, int H, hipStream_t st, const uint16_t* x, int64_t xs,
-                              uint16_t* res, int64_t rs, const uint16_t* w, float eps, int mode,
-                              int group, const float* sscale, uint8_t* out, int64_t os,
+static int launch_add_rmsnorm(int64_t T, int H, int H_pad, hipStream_t st, const uint16_t* x,
+                              int64_t xs, uint16_t* res, int64_t rs, const uint16_t* w, float eps,
+                              int mode, int group, const float* sscale, void* out, int64_t os,
                               float* scales) {
   const int kw = norm_waves_per_row(H);
   const int nv = static_cast<int>(ceil_div(H, 8 * kWave * kw));
@@ -319,7 +329,8 @@ static int launch_add_rmsnorm(int64_t T, int H, hipStream_t st, const uint16_t* 
 #define RRA_NORM_CASE(N, W)                                                                 \
   if (nv == N && kw == W) {                                                                 \
     hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual>), grid, dim3(kBlock), 0, st, \
-                       x, xs, res, rs, w, eps, mode, group, sscale, out, os, scales, T, H);  \
+                       x, xs, res, rs, w, eps, mode, group, sscale, out, os, scales, T, H,  \
+                       H_pad);                                                               \
     return launch_status();                                                                 \
   }
   RRA_NORM_CASE(1, 1)
@@ -372,13 +383,37 @@ extern "C" int fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint
   if (T == 0) return RRA_OK;
 
   const int g = quant_mode == RRA_Q_PER_GROUP ? group_size : 0;
+  const int h = static_cast<int>(H);
   if (residual)
-    return launch_add_rmsnorm<true>(T, static_cast<int>(H), as_stream(stream), x, x_stride,
-                                    residual, residual_stride, weight, eps, quant_mode, g,
-                                    static_scale, out, out_stride, scales);
-  return launch_add_rmsnorm<false>(T, static_cast<int>(H), as_stream(stream), x, x_stride,
-                                   nullptr, 0, weight, eps, quant_mode, g, static_scale, out,
-                                   out_stride, scales);
+    return launch_add_rmsnorm<true>(T, h, h, as_stream(stream), x, x_stride, residual,
+                                    residual_stride, weight, eps, quant_mode, g, static_scale,
+                                    out, out_stride, scales);
+  return launch_add_rmsnorm<false>(T, h, h, as_stream(stream), x, x_stride, nullptr, 0, weight,
+                                   eps, quant_mode, g, static_scale, out, out_stride, scales);
+}
+
+extern "C" int fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residual,
+                                     int64_t residual_stride, const uint16_t* weight, float eps,
+                                     uint16_t* out, int64_t out_stride, int64_t T, int64_t H,
+                                     int64_t H_pad, void* stream) {
+  RRA_REQUIRE(T >= 0 && H > 0 && H_pad >= H, RRA_ERR_SHAPE);
+  const bool rows_ok = T == 0 || (x && out);
+  RRA_REQUIRE(rows_ok && weight, RRA_ERR_NULL);
+  RRA_REQUIRE(x_stride >= H && out_stride >= H_pad, RRA_ERR_SHAPE);
+  RRA_REQUIRE(!residual || residual_stride >= H, RRA_ERR_SHAPE);
+  RRA_REQUIRE(H % 8 == 0 && H_pad % 8 == 0 && H <= 8192 && H_pad <= (int64_t(1) << 30),
+              RRA_ERR_UNSUPPORTED);
+  RRA_REQUIRE(vec_ok(x, x_stride) && aligned(weight, 16) && vec_ok(out, out_stride),
+              RRA_ERR_ALIGN);
+  RRA_REQUIRE(!residual || vec_ok(residual, residual_stride), RRA_ERR_ALIGN);
+  if (T == 0) return RRA_OK;
+  const int h = static_cast<int>(H), hp = static_cast<int>(H_pad);
+  if (residual)
+    return launch_add_rmsnorm<true>(T, h, hp, as_stream(stream), x, x_stride, residual,
+                                    residual_stride, weight, eps, RRA_Q_NONE, 0, nullptr, out,
+                                    out_stride, nullptr);
+  return launch_add_rmsnorm<false>(T, h, hp, as_stream(stream), x, x_stride, nullptr, 0, weight,
+                                   eps, RRA_Q_NONE, 0, nullptr, out, out_stride, nullptr);
 }
 
 extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_weight,

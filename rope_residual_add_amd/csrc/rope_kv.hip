@@ -1,46 +1,128 @@
-// Rotary embedding + paged KV-cache write for gfx950, and the fp32 cos/sin
-// table it reads.
+// Rotary embedding + paged KV-cache write for gfx950, its QK-norm and MLA
+// variants, and the fp32 cos/sin table they read.
 //
-// Operation: vLLM design page "Fusion torch.compile passes", section
-// "RoPE + KV-Cache Update (fuse_rope_kvcache)": rotary embedding and the
-// KV-cache scatter as one kernel, so k and v are read once and the rotated k
-// goes straight into the cache.  The cache is paged as in the PagedAttention
-// section of "Making vLLM fast: configuration, internals, and the places worth
-// touching code": fixed-size blocks, and every token carries the slot
-// (block * block_size + offset) it writes.
+// Operations (vLLM design page "Fusion torch.compile passes"):
+// - "RoPE + KV-Cache Update (fuse_rope_kvcache)": rotary embedding and the
+//   KV-cache scatter as one kernel, so k and v are read once and the rotated k
+//   goes straight into the cache.
+// - "QK Norm + RoPE": per-head RMSNorm of q and k, then the rotary embedding,
+//   on the packed qkv row; here optionally followed by the same cache write.
+// - The MLA cache layout of section "MLA Dual RMSNorm" (kv_lora split into the
+//   normalized kv_c and the rope part k_pe): rotate q_pe and k_pe and write
+//   [kv_c | rotated k_pe] into the token's cache row.
+// The cache is paged as in the PagedAttention section of "Making vLLM fast:
+// configuration, internals, and the places worth touching code": fixed-size
+// blocks, and every token carries the slot (block * block_size + offset) it
+// writes.
 //
-// Mapping: four waves per token.  The token's work is cut into 16-byte units
-// (rotation pairs of q and k heads, plain vectors of v) spread over the 256
-// lanes so that each lane issues at most a few loads before its stores; see
-// rope_kv_write_kernel.
+// Mapping: four waves (256 lanes) per token.  A token's work is cut into
+// 16-byte units spread over the lanes so that each lane issues only a few
+// loads before its stores.  A rotation unit is 8 rotation pairs of one head:
+//   GPT-NeoX pairing (i, i + D/2): the vectors at columns 8c and D/2 + 8c;
+//   GPT-J pairing (2i, 2i + 1):    the vectors at columns 16c and 16c + 8.
+// Either way unit c rotates pairs 8c .. 8c + 7, i.e. reads entries 8c .. 8c + 7
+// of the cos and of the sin half of a table row.  A head has D/16 units and
+// the 256 lanes are a multiple of that, so all rotation units of a lane share
+// one c: the lane reads its 8 cos and 8 sin values once per token.
 #include "rra_device.hpp"
 #include "rra_host.hpp"
 
 namespace rra {
 
-// Rotate 8 pairs: (a, b) -> (a c - b s, b c + a s), rounded to bf16.
-__device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, const float c[8],
-                                        const float s[8]) {
+constexpr int kRopeWaves = 4;                     // waves per token
+constexpr int kRopeLanes = kRopeWaves * kWave;    // lanes per token
+constexpr int kRopeTokensPerBlock = kWavesPerBlock / kRopeWaves;
+constexpr int kRopeUnitsPerPass = 2;              // units a lane loads before storing
+
+// Where the two vectors of rotation unit c sit inside a head of D values.
+template <int D, bool kNeox>
+__device__ __forceinline__ int unit_lo(int c) {
+  return kNeox ? c * 8 : c * 16;
+}
+template <int D, bool kNeox>
+__device__ __forceinline__ int unit_hi(int c) {
+  return kNeox ? c * 8 + D / 2 : c * 16 + 8;
+}
+
+// The 8 cos and 8 sin values of rotation unit c at one position.
+template <int D>
+__device__ __forceinline__ void unit_cos_sin(const float* row, int c, float cs[8], float sn[8]) {
+  const float* p = row + c * 8;
+  const f32x4 c0 = ld_f32x4(p), c1 = ld_f32x4(p + 4);
+  const f32x4 s0 = ld_f32x4(p + D / 2), s1 = ld_f32x4(p + D / 2 + 4);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float a0 = bf16_lo(lo[k]), a1 = bf16_hi(lo[k]);
-    const float b0 = bf16_lo(hi[k]), b1 = bf16_hi(hi[k]);
-    lo[k] = pack_bf16x2(a0 * c[2 * k] - b0 * s[2 * k], a1 * c[2 * k + 1] - b1 * s[2 * k + 1]);
-    hi[k] = pack_bf16x2(b0 * c[2 * k] + a0 * s[2 * k], b1 * c[2 * k + 1] + a1 * s[2 * k + 1]);
+  for (int j = 0; j < 4; ++j) {
+    cs[j] = c0[j];
+    cs[4 + j] = c1[j];
+    sn[j] = s0[j];
+    sn[4 + j] = s1[j];
   }
 }
 
-// Work of one token, in units: a q unit or a k unit is 8 rotation pairs of one
-// head (a 16-byte vector from each half of the head), a v unit is one 16-byte
-// vector of v copied into the cache.  Units are numbered q first, then k,
-// then v; row lane rl of the token's kW waves takes units rl, rl + 64 kW, ...
-// A head has D/16 units and 64 kW is a multiple of D/16, so every q or k unit
-// of a lane starts at the same column of its head: the lane reads its 8 cos
-// and 8 sin values once.  Each lane reads a q unit before writing it back, so
-// q_out may alias q.  kU units per lane are loaded before any is stored.
-constexpr int kRopeUnitsPerPass = 2;
+// Rotate the 8 pairs of a unit held as 16 fp32 values x[0..8) (lo vector) and
+// x[8..16) (hi vector): (a, b) -> (a cos - b sin, b cos + a sin).
+template <bool kNeox>
+__device__ __forceinline__ void rotate_unit(float x[16], const float cs[8], const float sn[8]) {
+  if (kNeox) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // pair k = (lo[k], hi[k])
+      const float a = x[k], b = x[8 + k];
+      x[k] = a * cs[k] - b * sn[k];
+      x[8 + k] = b * cs[k] + a * sn[k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // pair k = (x[2k], x[2k + 1])
+      const float a = x[2 * k], b = x[2 * k + 1];
+      x[2 * k] = a * cs[k] - b * sn[k];
+      x[2 * k + 1] = b * cs[k] + a * sn[k];
+    }
+  }
+}
 
-template <int D, int kW>
+__device__ __forceinline__ void unpack16(u32x4 lo, u32x4 hi, float x[16]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = bf16_lo(lo[k]);
+    x[2 * k + 1] = bf16_hi(lo[k]);
+    x[8 + 2 * k] = bf16_lo(hi[k]);
+    x[8 + 2 * k + 1] = bf16_hi(hi[k]);
+  }
+}
+
+__device__ __forceinline__ void pack16(const float x[16], u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    lo[k] = pack_bf16x2(x[2 * k], x[2 * k + 1]);
+    hi[k] = pack_bf16x2(x[8 + 2 * k], x[8 + 2 * k + 1]);
+  }
+}
+
+template <bool kNeox>
+__device__ __forceinline__ void rotate_packed(u32x4& lo, u32x4& hi, const float cs[8],
+                                              const float sn[8]) {
+  float x[16];
+  unpack16(lo, hi, x);
+  rotate_unit<kNeox>(x, cs, sn);
+  pack16(x, lo, hi);
+}
+
+// Sum over aligned groups of n lanes (n = 4, 8 or 16), result in every lane
+// of the group.  Executed by all lanes of the wave.
+template <int n>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  v += dpp<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  if (n >= 8) v += dpp<0x141>(v);  // row_half_mirror
+  if (n >= 16) v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
+// ---- RoPE + paged KV write ------------------------------------------------------
+// Units of one token: q units first, then k units, then v units (one 16-byte
+// vector of v copied into the cache); row lane rl takes units rl, rl + 256, ...
+// Each lane reads a q unit before writing it back, so q_out may alias q.
+template <int D, bool kNeox>
 __global__ void __launch_bounds__(kBlock)
     rope_kv_write_kernel(const int64_t* __restrict__ positions, const uint16_t* q,
                          int64_t q_stride, uint16_t* q_out, int64_t q_out_stride,
@@ -50,38 +132,25 @@ __global__ void __launch_bounds__(kBlock)
                          const int64_t* __restrict__ slot_mapping,
                          uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
                          int64_t T, int Hq, int Hkv) {
-  constexpr int kHalf = D / 2;
-  constexpr int kUnitsPerHead = kHalf / 8;
-  constexpr int kLanes = kW * kWave;
-  constexpr int kTokensPerBlock = kWavesPerBlock / kW;
+  constexpr int kUnitsPerHead = D / 16;
   constexpr int kU = kRopeUnitsPerPass;
-  static_assert(kLanes % kUnitsPerHead == 0, "a lane must keep one column");
+  static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
   const int wave = wave_id();
-  const int rl = (wave % kW) * kWave + lane_id();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + wave / kW;
+  const int rl = (wave % kRopeWaves) * kWave + lane_id();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRopeTokensPerBlock + wave / kRopeWaves;
   if (t >= T) return;  // no barrier in this kernel
 
   const int64_t pos = positions[t];
   const int64_t slot = slot_mapping[t];
-  const int col = (rl % kUnitsPerHead) * 8;
+  const int c = rl % kUnitsPerHead;
+  const int lo_off = unit_lo<D, kNeox>(c), hi_off = unit_hi<D, kNeox>(c);
   const int uq = Hq * kUnitsPerHead;
   const int uk = slot >= 0 ? Hkv * kUnitsPerHead : 0;  // padding tokens: q only
   const int uv = slot >= 0 ? Hkv * (D / 8) : 0;
   const int total = uq + uk + uv;
 
-  float c[8], s[8];
-  {
-    const float* cs = cos_sin + pos * D + col;
-    const f32x4 c0 = ld_f32x4(cs), c1 = ld_f32x4(cs + 4);
-    const f32x4 s0 = ld_f32x4(cs + kHalf), s1 = ld_f32x4(cs + kHalf + 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c[j] = c0[j];
-      c[4 + j] = c1[j];
-      s[j] = s0[j];
-      s[4 + j] = s1[j];
-    }
-  }
+  float cs[8], sn[8];
+  unit_cos_sin<D>(cos_sin + pos * D, c, cs, sn);
   const uint16_t* qt = q + t * q_stride;
   uint16_t* qo = q_out + t * q_out_stride;
   const uint16_t* kt = k + t * k_stride;
@@ -91,38 +160,216 @@ __global__ void __launch_bounds__(kBlock)
   uint16_t* kc = key_cache + (slot >= 0 ? slot : 0) * Hkv * D;
   uint16_t* vc = value_cache + (slot >= 0 ? slot : 0) * Hkv * D;
 
-  for (int u0 = 0; u0 < total; u0 += kU * kLanes) {
+  for (int u0 = 0; u0 < total; u0 += kU * kRopeLanes) {
     u32x4 lo[kU], hi[kU];
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      const int u = u0 + j * kLanes + rl;
+      const int u = u0 + j * kRopeLanes + rl;
       if (u < uq) {
-        const uint16_t* p = qt + (u / kUnitsPerHead) * D + col;
-        lo[j] = ld_stream(p);
-        hi[j] = ld_stream(p + kHalf);
+        const uint16_t* p = qt + (u / kUnitsPerHead) * D;
+        lo[j] = ld_stream(p + lo_off);
+        hi[j] = ld_stream(p + hi_off);
       } else if (u < uq + uk) {
-        const uint16_t* p = kt + ((u - uq) / kUnitsPerHead) * D + col;
-        lo[j] = ld_stream(p);
-        hi[j] = ld_stream(p + kHalf);
+        const uint16_t* p = kt + ((u - uq) / kUnitsPerHead) * D;
+        lo[j] = ld_stream(p + lo_off);
+        hi[j] = ld_stream(p + hi_off);
       } else if (u < total) {
         lo[j] = ld_stream(vt + (u - uq - uk) * 8);
       }
     }
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      const int u = u0 + j * kLanes + rl;
+      const int u = u0 + j * kRopeLanes + rl;
       if (u < uq) {
-        rotate8(lo[j], hi[j], c, s);
-        uint16_t* p = qo + (u / kUnitsPerHead) * D + col;
-        st_stream(p, lo[j]);
-        st_stream(p + kHalf, hi[j]);
+        rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
+        uint16_t* p = qo + (u / kUnitsPerHead) * D;
+        st_stream(p + lo_off, lo[j]);
+        st_stream(p + hi_off, hi[j]);
       } else if (u < uq + uk) {
-        rotate8(lo[j], hi[j], c, s);
-        uint16_t* p = kc + ((u - uq) / kUnitsPerHead) * D + col;
-        st_stream(p, lo[j]);
-        st_stream(p + kHalf, hi[j]);
+        rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
+        uint16_t* p = kc + ((u - uq) / kUnitsPerHead) * D;
+        st_stream(p + lo_off, lo[j]);
+        st_stream(p + hi_off, hi[j]);
       } else if (u < total) {
         st_stream(vc + (u - uq - uk) * 8, lo[j]);
+      }
+    }
+  }
+}
+
+// ---- QK norm + RoPE (+ paged KV write) ------------------------------------------
+// qkv row = [q: Hq heads | k: Hkv heads | v: Hkv heads] of D values.  Units as
+// in rope_kv_write_kernel (q, then k, then v).  A head's D/16 rotation units
+// sit on D/16 consecutive lanes, so its sum of squares is a DPP group sum;
+// every lane runs the group sums (lanes without a q or k unit add zeros).
+// The norm and the rotation are applied in fp32 and rounded once to bf16.
+template <int D, bool kNeox>
+__global__ void __launch_bounds__(kBlock)
+    qk_norm_rope_kv_kernel(const int64_t* __restrict__ positions, uint16_t* qkv,
+                           int64_t qkv_stride, const uint16_t* __restrict__ q_weight,
+                           const uint16_t* __restrict__ k_weight, float eps,
+                           const float* __restrict__ cos_sin,
+                           const int64_t* __restrict__ slot_mapping,
+                           uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
+                           int write_k, int64_t T, int Hq, int Hkv) {
+  constexpr int kUnitsPerHead = D / 16;
+  constexpr int kU = kRopeUnitsPerPass;
+  static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
+  const int wave = wave_id();
+  const int rl = (wave % kRopeWaves) * kWave + lane_id();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRopeTokensPerBlock + wave / kRopeWaves;
+  if (t >= T) return;  // wave-uniform: whole waves leave together; no barrier
+
+  const int64_t pos = positions[t];
+  const int64_t slot = slot_mapping ? slot_mapping[t] : -1;
+  const int c = rl % kUnitsPerHead;
+  const int lo_off = unit_lo<D, kNeox>(c), hi_off = unit_hi<D, kNeox>(c);
+  const int uq = Hq * kUnitsPerHead;
+  const int uk = (slot >= 0 || write_k) ? Hkv * kUnitsPerHead : 0;
+  const int uv = slot >= 0 ? Hkv * (D / 8) : 0;
+  const int total = uq + uk + uv;
+
+  float cs[8], sn[8];
+  unit_cos_sin<D>(cos_sin + pos * D, c, cs, sn);
+  // This lane's 16 weight values for q and for k (the same columns in every head).
+  float wq[16], wk[16];
+  unpack16(ld_cached(q_weight + lo_off), ld_cached(q_weight + hi_off), wq);
+  unpack16(ld_cached(k_weight + lo_off), ld_cached(k_weight + hi_off), wk);
+
+  uint16_t* row = qkv + t * qkv_stride;
+  uint16_t* kt = row + Hq * D;
+  const uint16_t* vt = kt + Hkv * D;
+  uint16_t* kc = key_cache ? key_cache + (slot >= 0 ? slot : 0) * Hkv * D : nullptr;
+  uint16_t* vc = value_cache ? value_cache + (slot >= 0 ? slot : 0) * Hkv * D : nullptr;
+  const float inv_d = 1.0f / static_cast<float>(D);
+
+  for (int u0 = 0; u0 < total; u0 += kU * kRopeLanes) {
+    u32x4 lo[kU], hi[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int u = u0 + j * kRopeLanes + rl;
+      lo[j] = u32x4{0u, 0u, 0u, 0u};
+      hi[j] = u32x4{0u, 0u, 0u, 0u};
+      if (u < uq) {
+        const uint16_t* p = row + (u / kUnitsPerHead) * D;
+        lo[j] = ld_stream(p + lo_off);
+        hi[j] = ld_stream(p + hi_off);
+      } else if (u < uq + uk) {
+        const uint16_t* p = kt + ((u - uq) / kUnitsPerHead) * D;
+        lo[j] = ld_stream(p + lo_off);
+        hi[j] = ld_stream(p + hi_off);
+      } else if (u < total) {
+        lo[j] = ld_stream(vt + (u - uq - uk) * 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int u = u0 + j * kRopeLanes + rl;
+      const bool is_q = u < uq, is_k = !is_q && u < uq + uk;
+      float x[16];
+      unpack16(lo[j], hi[j], x);
+      float ss = 0.0f;
+      if (is_q || is_k) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss = fmaf(x[e], x[e], ss);
+      }
+      ss = group_sum<kUnitsPerHead>(ss);  // all lanes: groups are q-only, k-only or idle
+      if (is_q || is_k) {
+        const float rho = __builtin_amdgcn_rsqf(ss * inv_d + eps);
+        const float* w = is_q ? wq : wk;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = x[e] * rho * w[e];
+        rotate_unit<kNeox>(x, cs, sn);
+        u32x4 a, b;
+        pack16(x, a, b);
+        if (is_q) {
+          uint16_t* p = row + (u / kUnitsPerHead) * D;
+          st_stream(p + lo_off, a);
+          st_stream(p + hi_off, b);
+        } else {
+          const int h = (u - uq) / kUnitsPerHead;
+          if (slot >= 0) {
+            st_stream(kc + h * D + lo_off, a);
+            st_stream(kc + h * D + hi_off, b);
+          }
+          if (write_k) {
+            st_stream(kt + h * D + lo_off, a);
+            st_stream(kt + h * D + hi_off, b);
+          }
+        }
+      } else if (u < total) {
+        st_stream(vc + (u - uq - uk) * 8, lo[j]);
+      }
+    }
+  }
+}
+
+// ---- MLA: q_pe / k_pe RoPE + [kv_c | k_pe] cache write ----------------------------
+// Units of one token: the q_pe rotation units of Hq heads (head stride
+// q_head_stride), then the k_pe rotation units, then kv_c vectors copied into
+// the cache row.  The cache is [num_blocks, block_size, kv_lora + R].
+template <int R, bool kNeox>
+__global__ void __launch_bounds__(kBlock)
+    mla_rope_kv_kernel(const int64_t* __restrict__ positions, uint16_t* q_pe, int64_t q_stride,
+                       int64_t q_head_stride, const uint16_t* __restrict__ k_pe,
+                       int64_t k_pe_stride, const uint16_t* __restrict__ kv_c,
+                       int64_t kv_c_stride, const float* __restrict__ cos_sin,
+                       const int64_t* __restrict__ slot_mapping, uint16_t* __restrict__ kv_cache,
+                       int64_t T, int Hq, int kv_lora) {
+  constexpr int kUnitsPerHead = R / 16;
+  constexpr int kU = kRopeUnitsPerPass;
+  static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
+  const int wave = wave_id();
+  const int rl = (wave % kRopeWaves) * kWave + lane_id();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRopeTokensPerBlock + wave / kRopeWaves;
+  if (t >= T) return;  // no barrier in this kernel
+
+  const int64_t pos = positions[t];
+  const int64_t slot = slot_mapping[t];
+  const int c = rl % kUnitsPerHead;
+  const int lo_off = unit_lo<R, kNeox>(c), hi_off = unit_hi<R, kNeox>(c);
+  const int uq = Hq * kUnitsPerHead;
+  const int uk = slot >= 0 ? kUnitsPerHead : 0;
+  const int uc = slot >= 0 ? kv_lora / 8 : 0;
+  const int total = uq + uk + uc;
+
+  float cs[8], sn[8];
+  unit_cos_sin<R>(cos_sin + pos * R, c, cs, sn);
+  uint16_t* qt = q_pe + t * q_stride;
+  const uint16_t* kt = k_pe + t * k_pe_stride;
+  const uint16_t* ct = kv_c + t * kv_c_stride;
+  uint16_t* dst = kv_cache + (slot >= 0 ? slot : 0) * static_cast<int64_t>(kv_lora + R);
+
+  for (int u0 = 0; u0 < total; u0 += kU * kRopeLanes) {
+    u32x4 lo[kU], hi[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int u = u0 + j * kRopeLanes + rl;
+      if (u < uq) {
+        const uint16_t* p = qt + (u / kUnitsPerHead) * q_head_stride;
+        lo[j] = ld_stream(p + lo_off);
+        hi[j] = ld_stream(p + hi_off);
+      } else if (u < uq + uk) {
+        lo[j] = ld_stream(kt + lo_off);
+        hi[j] = ld_stream(kt + hi_off);
+      } else if (u < total) {
+        lo[j] = ld_stream(ct + (u - uq - uk) * 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int u = u0 + j * kRopeLanes + rl;
+      if (u < uq) {
+        rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
+        uint16_t* p = qt + (u / kUnitsPerHead) * q_head_stride;
+        st_stream(p + lo_off, lo[j]);
+        st_stream(p + hi_off, hi[j]);
+      } else if (u < uq + uk) {
+        rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
+        st_stream(dst + kv_lora + lo_off, lo[j]);
+        st_stream(dst + kv_lora + hi_off, hi[j]);
+      } else if (u < total) {
+        st_stream(dst + (u - uq - uk) * 8, lo[j]);
       }
     }
   }
@@ -156,6 +403,10 @@ __global__ void __launch_bounds__(kBlock)
   }
 }
 
+inline dim3 rope_grid(int64_t T) {
+  return dim3(static_cast<unsigned>(ceil_div(T, kRopeTokensPerBlock)));
+}
+
 }  // namespace rra
 
 using namespace rra;
@@ -178,7 +429,7 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
                   k_stride >= int64_t(Hkv) * D && v_stride >= int64_t(Hkv) * D,
               RRA_ERR_SHAPE);
   RRA_REQUIRE(D == 64 || D == 128 || D == 256, RRA_ERR_UNSUPPORTED);
-  RRA_REQUIRE(rot_dim == D && is_neox == 1, RRA_ERR_UNSUPPORTED);
+  RRA_REQUIRE(rot_dim == D && (is_neox == 0 || is_neox == 1), RRA_ERR_UNSUPPORTED);
   RRA_REQUIRE(vec_ok(q, q_stride) && vec_ok(q_out, q_out_stride) && vec_ok(k, k_stride) &&
                   vec_ok(v, v_stride),
               RRA_ERR_ALIGN);
@@ -186,27 +437,111 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
               RRA_ERR_ALIGN);
   RRA_REQUIRE(aligned(positions, 8) && aligned(slot_mapping, 8), RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
+  RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
 
-  // Four waves (256 lanes) per token: each lane carries at most a few units.
-  constexpr int kW = 4;
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock / kW)));
-  RRA_REQUIRE(ceil_div(T, kWavesPerBlock / kW) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
   const hipStream_t st = as_stream(stream);
-#define RRA_ROPE_CASE(DD)                                                                     \
-  case DD:                                                                                    \
-    hipLaunchKernelGGL((rope_kv_write_kernel<DD, kW>), grid, dim3(kBlock), 0, st, positions,  \
-                       q, q_stride, q_out, q_out_stride, k, k_stride, v, v_stride, cos_sin,   \
-                       slot_mapping, key_cache, value_cache, T, Hq, Hkv);                     \
-    break;
-  switch (D) {
-    RRA_ROPE_CASE(64)
-    RRA_ROPE_CASE(128)
-    RRA_ROPE_CASE(256)
-    default:
-      return RRA_ERR_UNSUPPORTED;
+#define RRA_ROPE_CASE(DD, NEOX)                                                                 \
+  if (D == DD && is_neox == NEOX) {                                                             \
+    hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX>), rope_grid(T), dim3(kBlock), 0, st,     \
+                       positions, q, q_stride, q_out, q_out_stride, k, k_stride, v, v_stride,   \
+                       cos_sin, slot_mapping, key_cache, value_cache, T, Hq, Hkv);              \
+    return launch_status();                                                                     \
   }
+  RRA_ROPE_CASE(64, 1)
+  RRA_ROPE_CASE(128, 1)
+  RRA_ROPE_CASE(256, 1)
+  RRA_ROPE_CASE(64, 0)
+  RRA_ROPE_CASE(128, 0)
+  RRA_ROPE_CASE(256, 0)
 #undef RRA_ROPE_CASE
-  return launch_status();
+  return RRA_ERR_UNSUPPORTED;
+}
+
+extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, int64_t qkv_stride,
+                                     const uint16_t* q_weight, const uint16_t* k_weight,
+                                     float eps, const float* cos_sin, int64_t max_pos,
+                                     const int64_t* slot_mapping, uint16_t* key_cache,
+                                     uint16_t* value_cache, int write_k, int64_t T, int Hq,
+                                     int Hkv, int D, int rot_dim, int block_size,
+                                     int64_t num_blocks, int is_neox, void* stream) {
+  RRA_REQUIRE(T >= 0 && Hq > 0 && Hkv > 0 && D > 0 && rot_dim > 0 && max_pos > 0,
+              RRA_ERR_SHAPE);
+  RRA_REQUIRE(qkv_stride >= int64_t(Hq + 2 * Hkv) * D, RRA_ERR_SHAPE);
+  const bool tokens_ok = T == 0 || (positions && qkv);
+  RRA_REQUIRE(tokens_ok && q_weight && k_weight && cos_sin, RRA_ERR_NULL);
+  const bool with_cache = slot_mapping != nullptr;
+  if (with_cache) {
+    RRA_REQUIRE(key_cache && value_cache, RRA_ERR_NULL);
+    RRA_REQUIRE(block_size > 0 && num_blocks > 0, RRA_ERR_SHAPE);
+    RRA_REQUIRE(aligned(key_cache, 16) && aligned(value_cache, 16), RRA_ERR_ALIGN);
+    RRA_REQUIRE(aligned(slot_mapping, 8), RRA_ERR_ALIGN);
+  }
+  RRA_REQUIRE(D == 64 || D == 128 || D == 256, RRA_ERR_UNSUPPORTED);
+  RRA_REQUIRE(rot_dim == D && (is_neox == 0 || is_neox == 1), RRA_ERR_UNSUPPORTED);
+  RRA_REQUIRE(vec_ok(qkv, qkv_stride) && aligned(q_weight, 16) && aligned(k_weight, 16) &&
+                  aligned(cos_sin, 16) && aligned(positions, 8),
+              RRA_ERR_ALIGN);
+  if (T == 0) return RRA_OK;
+  RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
+
+  const hipStream_t st = as_stream(stream);
+#define RRA_QKN_CASE(DD, NEOX)                                                                 \
+  if (D == DD && is_neox == NEOX) {                                                            \
+    hipLaunchKernelGGL((qk_norm_rope_kv_kernel<DD, NEOX>), rope_grid(T), dim3(kBlock), 0, st,  \
+                       positions, qkv, qkv_stride, q_weight, k_weight, eps, cos_sin,           \
+                       slot_mapping, key_cache, value_cache, write_k, T, Hq, Hkv);             \
+    return launch_status();                                                                    \
+  }
+  RRA_QKN_CASE(64, 1)
+  RRA_QKN_CASE(128, 1)
+  RRA_QKN_CASE(256, 1)
+  RRA_QKN_CASE(64, 0)
+  RRA_QKN_CASE(128, 0)
+  RRA_QKN_CASE(256, 0)
+#undef RRA_QKN_CASE
+  return RRA_ERR_UNSUPPORTED;
+}
+
+extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64_t q_stride,
+                                 int64_t q_head_stride, const uint16_t* k_pe,
+                                 int64_t k_pe_stride, const uint16_t* kv_c, int64_t kv_c_stride,
+                                 const float* cos_sin, int64_t max_pos,
+                                 const int64_t* slot_mapping, uint16_t* kv_cache, int64_t T,
+                                 int Hq, int kv_lora, int rope_dim, int block_size,
+                                 int64_t num_blocks, int is_neox, void* stream) {
+  RRA_REQUIRE(T >= 0 && Hq > 0 && kv_lora > 0 && rope_dim > 0 && block_size > 0 &&
+                  num_blocks > 0 && max_pos > 0,
+              RRA_ERR_SHAPE);
+  RRA_REQUIRE(q_head_stride >= rope_dim && q_stride >= int64_t(Hq - 1) * q_head_stride + rope_dim &&
+                  k_pe_stride >= rope_dim && kv_c_stride >= kv_lora,
+              RRA_ERR_SHAPE);
+  const bool tokens_ok = T == 0 || (positions && q_pe && k_pe && kv_c && slot_mapping);
+  RRA_REQUIRE(tokens_ok && cos_sin && kv_cache, RRA_ERR_NULL);
+  RRA_REQUIRE(rope_dim == 64 || rope_dim == 128, RRA_ERR_UNSUPPORTED);
+  RRA_REQUIRE(kv_lora % 8 == 0 && (is_neox == 0 || is_neox == 1), RRA_ERR_UNSUPPORTED);
+  RRA_REQUIRE(vec_ok(q_pe, q_stride) && q_head_stride % 8 == 0 && vec_ok(k_pe, k_pe_stride) &&
+                  vec_ok(kv_c, kv_c_stride),
+              RRA_ERR_ALIGN);
+  RRA_REQUIRE(aligned(kv_cache, 16) && aligned(cos_sin, 16) && aligned(positions, 8) &&
+                  aligned(slot_mapping, 8),
+              RRA_ERR_ALIGN);
+  if (T == 0) return RRA_OK;
+  RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
+
+  const hipStream_t st = as_stream(stream);
+#define RRA_MLA_CASE(RR, NEOX)                                                                \
+  if (rope_dim == RR && is_neox == NEOX) {                                                    \
+    hipLaunchKernelGGL((mla_rope_kv_kernel<RR, NEOX>), rope_grid(T), dim3(kBlock), 0, st,     \
+                       positions, q_pe, q_stride, q_head_stride, k_pe, k_pe_stride, kv_c,     \
+                       kv_c_stride, cos_sin, slot_mapping, kv_cache, T, Hq, kv_lora);         \
+    return launch_status();                                                                   \
+  }
+  RRA_MLA_CASE(64, 0)
+  RRA_MLA_CASE(64, 1)
+  RRA_MLA_CASE(128, 0)
+  RRA_MLA_CASE(128, 1)
+#undef RRA_MLA_CASE
+  return RRA_ERR_UNSUPPORTED;
 }
 
 extern "C" int rope_cos_sin_cache(float* cos_sin, int64_t max_pos, int rot_dim, double theta,

@@ -38,6 +38,7 @@ def declared_functions() -> list:
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fused_add_rmsnorm_quant", "silu_mul_quant", "rope_kv_write", "dual_rmsnorm_quant",
+              "qk_norm_rope_kv_write", "fused_add_rmsnorm_pad", "mla_rope_kv_write",
               "rope_cos_sin_cache", "rra_e4m3fn_encode", "rra_abi_version", "rra_status_string"):
         assert n in names
 
@@ -125,7 +126,7 @@ def test_rope_validation(rra):
     assert f(qs=2048) == ESHAPE
     assert f(D=96, qs=3072, qos=3072, ks=768, vs=768, rd=96) == EUNSUP
     assert f(rd=64) == EUNSUP
-    assert f(neox=0) == EUNSUP
+    assert f(neox=2) == EUNSUP
     assert f(pos=None, q=None, qo=None, k=None, v=None, sm=None, T=0) == OK
     assert f(kc=None, T=0) == ENULL
     assert f(cs=None, T=0) == ENULL
@@ -158,6 +159,74 @@ def test_dual_validation(rra):
     assert f(Hq=4096, qs=4096, qos=4096) == EUNSUP
     assert f(kv=A + 8, T=0) == EALIGN  # alignment is checked before the T == 0 early return
     assert f(g=64, Hq=1000, qs=1000, qos=1000) == ESHAPE  # 64 does not divide 1000
+
+
+def test_qk_norm_rope_validation(rra):
+    L = rra.lib()
+
+    def f(**k):
+        a = dict(pos=A, qkv=A, s=6144, qw=A, kw=A, eps=1e-6, cs=A, mp=8192, sm=A, kc=A, vc=A,
+                 wk=0, T=4, Hq=32, Hkv=8, D=128, rd=128, bs=16, nb=4096, neox=1)
+        a.update(k)
+        return L.qk_norm_rope_kv_write(a["pos"], a["qkv"], a["s"], a["qw"], a["kw"], a["eps"],
+                                       a["cs"], a["mp"], a["sm"], a["kc"], a["vc"], a["wk"],
+                                       a["T"], a["Hq"], a["Hkv"], a["D"], a["rd"], a["bs"],
+                                       a["nb"], a["neox"], None)
+
+    assert f(T=0) == OK
+    assert f(pos=None, qkv=None, sm=None, kc=None, vc=None, T=0) == OK
+    assert f(qw=None, T=0) == ENULL
+    assert f(kc=None) == ENULL  # a slot mapping needs both caches
+    assert f(s=4096) == ESHAPE  # narrower than (Hq + 2 Hkv) D
+    assert f(D=96, s=4608, rd=96) == EUNSUP
+    assert f(rd=64) == EUNSUP
+    assert f(neox=2) == EUNSUP
+    assert f(qkv=A + 2) == EALIGN
+    assert f(kw=A + 8) == EALIGN
+    assert f(bs=0) == ESHAPE
+
+
+def test_rmsnorm_pad_validation(rra):
+    L = rra.lib()
+
+    def f(**k):
+        a = dict(x=A, xs=2880, r=A, rs=2880, w=A, eps=1e-5, o=A, os=3072, T=4, H=2880, Hp=3072)
+        a.update(k)
+        return L.fused_add_rmsnorm_pad(a["x"], a["xs"], a["r"], a["rs"], a["w"], a["eps"],
+                                       a["o"], a["os"], a["T"], a["H"], a["Hp"], None)
+
+    assert f(T=0) == OK
+    assert f(x=None, r=None, o=None, T=0) == OK
+    assert f(w=None, T=0) == ENULL
+    assert f(Hp=2872) == ESHAPE  # pad narrower than H
+    assert f(os=3000) == ESHAPE  # out row narrower than H_pad
+    assert f(Hp=3076, os=3076) == EUNSUP  # H_pad % 8
+    assert f(o=A + 8) == EALIGN
+    assert f(x=A + 2) == EALIGN
+
+
+def test_mla_rope_validation(rra):
+    L = rra.lib()
+
+    def f(**k):
+        a = dict(pos=A, q=A, qs=24576, hs=192, kpe=A, ks=64, c=A, cs_=512, cs=A, mp=8192, sm=A,
+                 kv=A, T=4, Hq=128, lora=512, rd=64, bs=64, nb=1024, neox=0)
+        a.update(k)
+        return L.mla_rope_kv_write(a["pos"], a["q"], a["qs"], a["hs"], a["kpe"], a["ks"],
+                                   a["c"], a["cs_"], a["cs"], a["mp"], a["sm"], a["kv"], a["T"],
+                                   a["Hq"], a["lora"], a["rd"], a["bs"], a["nb"], a["neox"],
+                                   None)
+
+    assert f(T=0) == OK
+    assert f(pos=None, q=None, kpe=None, c=None, sm=None, T=0) == OK
+    assert f(kv=None, T=0) == ENULL
+    assert f(qs=1000) == ESHAPE  # rows too narrow for 128 heads at stride 192
+    assert f(hs=32) == ESHAPE  # head stride below rope_dim
+    assert f(rd=32, ks=32) == EUNSUP
+    assert f(lora=500, cs_=500) == EUNSUP
+    assert f(neox=2) == EUNSUP
+    assert f(hs=196, qs=25088) == EALIGN  # head stride not a multiple of 8
+    assert f(kv=A + 4) == EALIGN
 
 
 def test_e4m3_diag_validation(rra):

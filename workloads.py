@@ -316,3 +316,48 @@ def device_mla_inputs(T: int, cfg: MlaCfg = MLA, device="cuda", salt: int = 0):
     return dict(q=_randn(g, (T, cfg.Hq), device), kv=_randn(g, (T, cfg.Hkv), device),
                 q_w=_randn(g, (cfg.Hq,), device, mean=1.0, std=0.1),
                 kv_w=_randn(g, (cfg.Hkv,), device, mean=1.0, std=0.1))
+
+
+def device_qknorm_inputs(T: int, cfg: QkNormCfg = QKNORM, device="cuda", salt: int = 0,
+                         with_cache: bool = True):
+    import torch
+
+    g = _gen(device, "qknorm", T, salt)
+    n_slots = cfg.num_blocks * cfg.block_size
+    d = dict(
+        qkv=_randn(g, (T, (cfg.Hq + 2 * cfg.Hkv) * cfg.D), device),
+        q_w=_randn(g, (cfg.D,), device, mean=1.0, std=0.1),
+        k_w=_randn(g, (cfg.D,), device, mean=1.0, std=0.1),
+        positions=torch.randint(0, cfg.max_pos, (T,), generator=g, device=device,
+                                dtype=torch.int64),
+        slot_mapping=torch.randperm(n_slots, generator=g, device=device)[:T].contiguous(),
+    )
+    if with_cache:
+        shape = (cfg.num_blocks, cfg.block_size, cfg.Hkv, cfg.D)
+        d["key_cache"] = _randn(g, shape, device)
+        d["value_cache"] = _randn(g, shape, device)
+    return d
+
+
+def device_pad_inputs(T: int, cfg: PadCfg = PAD, device="cuda", salt: int = 0):
+    return device_norm_inputs(T, cfg.H, device, salt, tag="pad")
+
+
+def device_mla_rope_inputs(T: int, cfg: MlaRopeCfg = MLA_ROPE, device="cuda", salt: int = 0,
+                           with_cache: bool = True):
+    import torch
+
+    g = _gen(device, "mla_rope", T, salt)
+    n_slots = cfg.num_blocks * cfg.block_size
+    d = dict(
+        q=_randn(g, (T, cfg.Hq * (cfg.nope + cfg.rope_dim)), device),
+        k_pe=_randn(g, (T, cfg.rope_dim), device),
+        kv_c=_randn(g, (T, cfg.kv_lora), device),
+        positions=torch.randint(0, cfg.max_pos, (T,), generator=g, device=device,
+                                dtype=torch.int64),
+        slot_mapping=torch.randperm(n_slots, generator=g, device=device)[:T].contiguous(),
+    )
+    if with_cache:
+        d["kv_cache"] = _randn(g, (cfg.num_blocks, cfg.block_size, cfg.kv_lora + cfg.rope_dim),
+                               device)
+    return d
