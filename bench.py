@@ -98,6 +98,7 @@ KERNEL_SYMBOL = {
     "rope_kv_write": "rope_kv_write_kernel",
     "dual_rmsnorm_quant": "dual_rmsnorm_quant_kernel",
     "qk_norm_rope_kv_write": "qk_norm_rope_kv_kernel",
+    "fused_add_rmsnorm_pad": "add_rmsnorm_pad_kernel",
     "mla_rope_kv_write": "mla_rope_kv_kernel",
 }
 KERNEL_SOURCES = {
@@ -461,7 +462,7 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int) -> None:
              "GB/s (avg) | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
     for r in csv.DictReader(open(stats_csv)):
         k = _kernel_of(r["Name"])
-        if k is None:
+        if k is None or k not in KERNELS:
             continue
         avg, mn, mx = (float(r[c]) for c in ("AverageNs", "MinNs", "MaxNs"))
         b = algo_bytes(k, T)
@@ -505,7 +506,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out: str, commands: str, T
              "(bench.py reports `traffic` only while it matches).", "",
              "| kernel | source | FETCH_SIZE KiB | WRITE_SIZE KiB | launches | traffic bytes | "
              "algorithmic bytes | traffic / algorithmic |", "|---|---|---|---|---|---|---|---|"]
-    for k in KERNELS:
+    for k in KERNELS + NEXT_KERNELS:
         names = [n for n in fetch if _kernel_of(n) == k]
         if not names:
             continue

@@ -16,8 +16,9 @@
 // writes.
 //
 // Mapping: four waves (256 lanes) per token.  A token's work is cut into
-// 16-byte units spread over the lanes so that each lane issues only a few
-// loads before its stores.  A rotation unit is 8 rotation pairs of one head:
+// 16-byte units spread over the lanes; each lane takes kU of them per pass
+// (chosen per launch so one pass covers a token up to 1024 units) and issues
+// all their loads before its stores.  A rotation unit is 8 rotation pairs of one head:
 //   GPT-NeoX pairing (i, i + D/2): the vectors at columns 8c and D/2 + 8c;
 //   GPT-J pairing (2i, 2i + 1):    the vectors at columns 16c and 16c + 8.
 // Either way unit c rotates pairs 8c .. 8c + 7, i.e. reads entries 8c .. 8c + 7
@@ -32,7 +33,7 @@ namespace rra {
 constexpr int kRopeWaves = 4;                     // waves per token
 constexpr int kRopeLanes = kRopeWaves * kWave;    // lanes per token
 constexpr int kRopeTokensPerBlock = kWavesPerBlock / kRopeWaves;
-constexpr int kRopeUnitsPerPass = 2;              // units a lane loads before storing
+constexpr int kRopeMaxUnitsPerPass = 4;           // units a lane loads before storing
 
 // Where the two vectors of rotation unit c sit inside a head of D values.
 template <int D, bool kNeox>
@@ -122,7 +123,7 @@ __device__ __forceinline__ float group_sum(float v) {
 // Units of one token: q units first, then k units, then v units (one 16-byte
 // vector of v copied into the cache); row lane rl takes units rl, rl + 256, ...
 // Each lane reads a q unit before writing it back, so q_out may alias q.
-template <int D, bool kNeox>
+template <int D, bool kNeox, int kU>
 __global__ void __launch_bounds__(kBlock)
     rope_kv_write_kernel(const int64_t* __restrict__ positions, const uint16_t* q,
                          int64_t q_stride, uint16_t* q_out, int64_t q_out_stride,
@@ -133,7 +134,6 @@ __global__ void __launch_bounds__(kBlock)
                          uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
                          int64_t T, int Hq, int Hkv) {
   constexpr int kUnitsPerHead = D / 16;
-  constexpr int kU = kRopeUnitsPerPass;
   static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
   const int wave = wave_id();
   const int rl = (wave % kRopeWaves) * kWave + lane_id();
@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(kBlock)
 // sit on D/16 consecutive lanes, so its sum of squares is a DPP group sum;
 // every lane runs the group sums (lanes without a q or k unit add zeros).
 // The norm and the rotation are applied in fp32 and rounded once to bf16.
-template <int D, bool kNeox>
+template <int D, bool kNeox, int kU>
 __global__ void __launch_bounds__(kBlock)
     qk_norm_rope_kv_kernel(const int64_t* __restrict__ positions, uint16_t* qkv,
                            int64_t qkv_stride, const uint16_t* __restrict__ q_weight,
@@ -213,7 +213,6 @@ __global__ void __launch_bounds__(kBlock)
                            uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
                            int write_k, int64_t T, int Hq, int Hkv) {
   constexpr int kUnitsPerHead = D / 16;
-  constexpr int kU = kRopeUnitsPerPass;
   static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
   const int wave = wave_id();
   const int rl = (wave % kRopeWaves) * kWave + lane_id();
@@ -308,7 +307,7 @@ __global__ void __launch_bounds__(kBlock)
 // Units of one token: the q_pe rotation units of Hq heads (head stride
 // q_head_stride), then the k_pe rotation units, then kv_c vectors copied into
 // the cache row.  The cache is [num_blocks, block_size, kv_lora + R].
-template <int R, bool kNeox>
+template <int R, bool kNeox, int kU>
 __global__ void __launch_bounds__(kBlock)
     mla_rope_kv_kernel(const int64_t* __restrict__ positions, uint16_t* q_pe, int64_t q_stride,
                        int64_t q_head_stride, const uint16_t* __restrict__ k_pe,
@@ -317,7 +316,6 @@ __global__ void __launch_bounds__(kBlock)
                        const int64_t* __restrict__ slot_mapping, uint16_t* __restrict__ kv_cache,
                        int64_t T, int Hq, int kv_lora) {
   constexpr int kUnitsPerHead = R / 16;
-  constexpr int kU = kRopeUnitsPerPass;
   static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
   const int wave = wave_id();
   const int rl = (wave % kRopeWaves) * kWave + lane_id();
@@ -407,6 +405,13 @@ inline dim3 rope_grid(int64_t T) {
   return dim3(static_cast<unsigned>(ceil_div(T, kRopeTokensPerBlock)));
 }
 
+// Units each lane takes per pass: enough for one pass over a token's largest
+// unit count (all loads of a lane issued before its stores), at most 4.
+inline int rope_units_per_pass(int64_t units) {
+  const int64_t u = ceil_div(units, kRopeLanes);
+  return static_cast<int>(u < 1 ? 1 : (u > kRopeMaxUnitsPerPass ? kRopeMaxUnitsPerPass : u));
+}
+
 }  // namespace rra
 
 using namespace rra;
@@ -440,11 +445,19 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
 
   const hipStream_t st = as_stream(stream);
+  const int ku = rope_units_per_pass(int64_t(Hq + Hkv) * (D / 16) + int64_t(Hkv) * (D / 8));
+#define RRA_ROPE_LAUNCH(DD, NEOX, KU)                                                          \
+  hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX, KU>), rope_grid(T), dim3(kBlock), 0, st,  \
+                     positions, q, q_stride, q_out, q_out_stride, k, k_stride, v, v_stride,    \
+                     cos_sin, slot_mapping, key_cache, value_cache, T, Hq, Hkv)
 #define RRA_ROPE_CASE(DD, NEOX)                                                                 \
   if (D == DD && is_neox == NEOX) {                                                             \
-    hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX>), rope_grid(T), dim3(kBlock), 0, st,     \
-                       positions, q, q_stride, q_out, q_out_stride, k, k_stride, v, v_stride,   \
-                       cos_sin, slot_mapping, key_cache, value_cache, T, Hq, Hkv);              \
+    switch (ku) {                                                                               \
+      case 1: RRA_ROPE_LAUNCH(DD, NEOX, 1); break;                                              \
+      case 2: RRA_ROPE_LAUNCH(DD, NEOX, 2); break;                                              \
+      case 3: RRA_ROPE_LAUNCH(DD, NEOX, 3); break;                                              \
+      default: RRA_ROPE_LAUNCH(DD, NEOX, 4); break;                                             \
+    }                                                                                           \
     return launch_status();                                                                     \
   }
   RRA_ROPE_CASE(64, 1)
@@ -454,6 +467,7 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   RRA_ROPE_CASE(128, 0)
   RRA_ROPE_CASE(256, 0)
 #undef RRA_ROPE_CASE
+#undef RRA_ROPE_LAUNCH
   return RRA_ERR_UNSUPPORTED;
 }
 
@@ -485,11 +499,20 @@ extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, in
   RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
 
   const hipStream_t st = as_stream(stream);
+  const int ku = rope_units_per_pass(int64_t(Hq + Hkv) * (D / 16) +
+                                     (slot_mapping ? int64_t(Hkv) * (D / 8) : 0));
+#define RRA_QKN_LAUNCH(DD, NEOX, KU)                                                            \
+  hipLaunchKernelGGL((qk_norm_rope_kv_kernel<DD, NEOX, KU>), rope_grid(T), dim3(kBlock), 0, st, \
+                     positions, qkv, qkv_stride, q_weight, k_weight, eps, cos_sin,              \
+                     slot_mapping, key_cache, value_cache, write_k, T, Hq, Hkv)
 #define RRA_QKN_CASE(DD, NEOX)                                                                 \
   if (D == DD && is_neox == NEOX) {                                                            \
-    hipLaunchKernelGGL((qk_norm_rope_kv_kernel<DD, NEOX>), rope_grid(T), dim3(kBlock), 0, st,  \
-                       positions, qkv, qkv_stride, q_weight, k_weight, eps, cos_sin,           \
-                       slot_mapping, key_cache, value_cache, write_k, T, Hq, Hkv);             \
+    switch (ku) {                                                                              \
+      case 1: RRA_QKN_LAUNCH(DD, NEOX, 1); break;                                              \
+      case 2: RRA_QKN_LAUNCH(DD, NEOX, 2); break;                                              \
+      case 3: RRA_QKN_LAUNCH(DD, NEOX, 3); break;                                              \
+      default: RRA_QKN_LAUNCH(DD, NEOX, 4); break;                                             \
+    }                                                                                          \
     return launch_status();                                                                    \
   }
   RRA_QKN_CASE(64, 1)
@@ -499,6 +522,7 @@ extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, in
   RRA_QKN_CASE(128, 0)
   RRA_QKN_CASE(256, 0)
 #undef RRA_QKN_CASE
+#undef RRA_QKN_LAUNCH
   return RRA_ERR_UNSUPPORTED;
 }
 
@@ -529,11 +553,19 @@ extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64
   RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
 
   const hipStream_t st = as_stream(stream);
+  const int ku = rope_units_per_pass(int64_t(Hq + 1) * (rope_dim / 16) + kv_lora / 8);
+#define RRA_MLA_LAUNCH(RR, NEOX, KU)                                                          \
+  hipLaunchKernelGGL((mla_rope_kv_kernel<RR, NEOX, KU>), rope_grid(T), dim3(kBlock), 0, st,   \
+                     positions, q_pe, q_stride, q_head_stride, k_pe, k_pe_stride, kv_c,       \
+                     kv_c_stride, cos_sin, slot_mapping, kv_cache, T, Hq, kv_lora)
 #define RRA_MLA_CASE(RR, NEOX)                                                                \
   if (rope_dim == RR && is_neox == NEOX) {                                                    \
-    hipLaunchKernelGGL((mla_rope_kv_kernel<RR, NEOX>), rope_grid(T), dim3(kBlock), 0, st,     \
-                       positions, q_pe, q_stride, q_head_stride, k_pe, k_pe_stride, kv_c,     \
-                       kv_c_stride, cos_sin, slot_mapping, kv_cache, T, Hq, kv_lora);         \
+    switch (ku) {                                                                             \
+      case 1: RRA_MLA_LAUNCH(RR, NEOX, 1); break;                                             \
+      case 2: RRA_MLA_LAUNCH(RR, NEOX, 2); break;                                             \
+      case 3: RRA_MLA_LAUNCH(RR, NEOX, 3); break;                                             \
+      default: RRA_MLA_LAUNCH(RR, NEOX, 4); break;                                            \
+    }                                                                                         \
     return launch_status();                                                                   \
   }
   RRA_MLA_CASE(64, 0)
@@ -541,6 +573,7 @@ extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64
   RRA_MLA_CASE(128, 0)
   RRA_MLA_CASE(128, 1)
 #undef RRA_MLA_CASE
+#undef RRA_MLA_LAUNCH
   return RRA_ERR_UNSUPPORTED;
 }
 
