@@ -156,19 +156,29 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
       const QuantStep qs = quant_step(rho, dynamic_scale(m, rho));
       if (idx < nvec) {
         if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = qs.s;
-        st_stream(o + idx * 8, quant8(t.t[i], qs));
+        st_stream(o + idx * 8, quant8<false>(t.t[i], qs));
       }
     }
     return;
   }
 
-  const float s = mode == RRA_Q_PER_TOKEN ? dynamic_scale(m_row, rho) : static_scale;
-  if (mode == RRA_Q_PER_TOKEN && rl == 0) scale_row[0] = s;
-  const QuantStep qs = quant_step(rho, s);
+  if (mode == RRA_Q_PER_TOKEN) {
+    const float s = dynamic_scale(m_row, rho);
+    if (rl == 0) scale_row[0] = s;
+    const QuantStep qs = quant_step(rho, s);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = i * stride + rl;
+      if (idx < nvec) st_stream(o + idx * 8, quant8<false>(t.t[i], qs));
+    }
+    return;
+  }
+  // RRA_Q_STATIC: |y / s| is unbounded, so codes saturate.
+  const QuantStep qs = quant_step(rho, static_scale);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = i * stride + rl;
-    if (idx < nvec) st_stream(o + idx * 8, quant8(t.t[i], qs));
+    if (idx < nvec) st_stream(o + idx * 8, quant8<true>(t.t[i], qs));
   }
 }
 

@@ -50,18 +50,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---- OCP e4m3fn -----------------------------------------------------------
-// gfx950's v_cvt_pk_fp8_f32 converts to OCP e4m3fn with round-to-nearest-even.
-// Inputs are clamped to the largest finite magnitude first (v_med3_f32), which
-// gives the saturating behaviour for values that land just above 448.
+// gfx950's v_cvt_pk_fp8_f32 converts to OCP e4m3fn with round-to-nearest-even:
+// magnitudes up to 464 (the midpoint above 448, a tie that goes to the even
+// code 448) give finite codes, larger ones give NaN (0x7F).  Saturating
+// conversion clamps to +-448 first (v_med3_f32); a caller whose values are
+// known to stay below 464 in magnitude (dynamic scales, where the largest
+// |y / s| is 448 within a few ulps) skips the clamp.
 
 __device__ __forceinline__ float clamp_e4m3(float v) {
   return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
 }
 
-// Four fp32 -> four e4m3fn bytes, element 0 in the lowest byte.
+// Four fp32 -> four e4m3fn bytes, element 0 in the lowest byte; kClamp
+// saturates to +-448 first.
+template <bool kClamp = true>
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a), clamp_e4m3(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(c), clamp_e4m3(d), w, true);
+  if (kClamp) {
+    a = clamp_e4m3(a);
+    b = clamp_e4m3(b);
+    c = clamp_e4m3(c);
+    d = clamp_e4m3(d);
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return static_cast<uint32_t>(w);
 }
 
@@ -111,7 +122,9 @@ __device__ __forceinline__ QuantStep quant_step(double rho, float s) {
   return QuantStep{f, s, rho};
 }
 
-// Eight codes e4m3fn(t[j] * rho / s).
+// Eight codes e4m3fn(t[j] * rho / s).  kClamp = false when s is a dynamic
+// scale (|t * rho / s| <= 448 within rounding).
+template <bool kClamp>
 __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
   float v[8];
   bool near[8];
@@ -128,7 +141,8 @@ __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
     for (int j = 0; j < 8; ++j)
       if (near[j]) v[j] = f32_round_odd(static_cast<double>(t[j]) * g);
   }
-  return u32x2{pack_e4m3x4(v[0], v[1], v[2], v[3]), pack_e4m3x4(v[4], v[5], v[6], v[7])};
+  return u32x2{pack_e4m3x4<kClamp>(v[0], v[1], v[2], v[3]),
+               pack_e4m3x4<kClamp>(v[4], v[5], v[6], v[7])};
 }
 
 // ---- wavefront reductions ---------------------------------------------------
