@@ -194,10 +194,11 @@ class HipEvents:
 
 # ---- GPU side ------------------------------------------------------------------
 
-def make_launchers(T: int, salt: int = 0, rope_state=None, only=KERNELS):
+def make_launchers(T: int, salt: int = 0, shared=None, only=KERNELS):
     """Allocate one input/output set at T tokens for each kernel in `only` and
-    return {name: zero-argument launch function}.  `rope_state` = (key_cache,
-    value_cache, cos_sin) shares one cache pair and table across sets."""
+    return {name: zero-argument launch function}.  L["_shared"] holds, per
+    cache-writing kernel, its cache(s) and cos/sin table; passing that dict as
+    `shared` makes further buffer sets reuse them."""
     import torch
 
     import rope_residual_add_amd as rra
@@ -205,6 +206,10 @@ def make_launchers(T: int, salt: int = 0, rope_state=None, only=KERNELS):
 
     dev = "cuda"
     L = {}
+    io = {}  # every kernel's tensors, for checking the timed launch path
+    L["_io"] = io
+    shared = dict(shared or {})
+    L["_shared"] = shared
 
     if "fused_add_rmsnorm_quant" in only:
         d = workloads.device_norm_inputs(T, H_NORM, dev, salt)
@@ -212,6 +217,7 @@ def make_launchers(T: int, salt: int = 0, rope_state=None, only=KERNELS):
         sc = torch.empty((T,), dtype=torch.float32, device=dev)
         L["fused_add_rmsnorm_quant"] = lambda d=d, out=out, sc=sc: rra.fused_add_rmsnorm_quant(
             d["x"], d["residual"], d["weight"], 1e-5, rra.Q_PER_TOKEN, 0, None, out, sc)
+        io["fused_add_rmsnorm_quant"] = dict(d, out=out, scales=sc)
 
     if "silu_mul_quant" in only:
         d = workloads.device_silu_inputs(T, I_SILU, dev, salt)
@@ -219,50 +225,55 @@ def make_launchers(T: int, salt: int = 0, rope_state=None, only=KERNELS):
         sc = torch.empty((T, I_SILU // G), dtype=torch.float32, device=dev)
         L["silu_mul_quant"] = lambda d=d, out=out, sc=sc: rra.silu_mul_quant(
             d["inp"], rra.Q_PER_GROUP, G, None, out, sc)
+        io["silu_mul_quant"] = dict(d, out=out, scales=sc)
 
     if "rope_kv_write" in only:
         cfg = workloads.ROPE
-        d = workloads.device_rope_inputs(T, cfg, dev, salt, with_cache=rope_state is None)
-        if rope_state is None:
+        state = shared.get("rope_kv_write")
+        d = workloads.device_rope_inputs(T, cfg, dev, salt, with_cache=state is None)
+        if state is None:
             cs = rra.rope_cos_sin_cache(cfg.max_pos, cfg.rot_dim, cfg.theta, device=dev)
-            rope_state = (d["key_cache"], d["value_cache"], cs)
-        kc, vc, cs = rope_state
+            state = shared["rope_kv_write"] = (d["key_cache"], d["value_cache"], cs)
+        kc, vc, cs = state
         L["rope_kv_write"] = lambda d=d, kc=kc, vc=vc, cs=cs: rra.rope_kv_write(
             d["positions"], d["q"], d["k"], d["v"], cs, d["slot_mapping"], kc, vc)
-        L["_rope_state"] = rope_state
+        io["rope_kv_write"] = dict(d, key_cache=kc, value_cache=vc)
 
     if "qk_norm_rope_kv_write" in only:
         cfg = workloads.QKNORM
-        d = workloads.device_qknorm_inputs(T, cfg, dev, salt, with_cache=rope_state is None)
-        if rope_state is None:
-            kc, vc = d["key_cache"], d["value_cache"]
+        state = shared.get("qk_norm_rope_kv_write")
+        d = workloads.device_qknorm_inputs(T, cfg, dev, salt, with_cache=state is None)
+        if state is None:
             cs_q = rra.rope_cos_sin_cache(cfg.max_pos, cfg.D, cfg.theta, device=dev)
-        else:
-            kc, vc, cs_q = rope_state
-        L["qk_norm_rope_kv_write"] = lambda d=d, kc=kc, vc=vc, cs=cs_q: rra.qk_norm_rope_kv_write(
-            d["positions"], d["qkv"], d["q_w"], d["k_w"], cfg.eps, cs, cfg.Hq, cfg.Hkv, cfg.D,
-            slot_mapping=d["slot_mapping"], key_cache=kc, value_cache=vc)
-        L["_rope_state"] = (kc, vc, cs_q)
+            state = shared["qk_norm_rope_kv_write"] = (d["key_cache"], d["value_cache"], cs_q)
+        kc, vc, cs_q = state
+        def qkn(d=d, kc=kc, vc=vc, cs=cs_q, cfg=cfg):
+            return rra.qk_norm_rope_kv_write(
+                d["positions"], d["qkv"], d["q_w"], d["k_w"], cfg.eps, cs, cfg.Hq, cfg.Hkv,
+                cfg.D, slot_mapping=d["slot_mapping"], key_cache=kc, value_cache=vc)
+        L["qk_norm_rope_kv_write"] = qkn
+        io["qk_norm_rope_kv_write"] = dict(d, key_cache=kc, value_cache=vc)
 
     if "fused_add_rmsnorm_pad" in only:
         cfg = workloads.PAD
         d = workloads.device_pad_inputs(T, cfg, dev, salt)
         out = torch.empty((T, cfg.H_pad), dtype=torch.bfloat16, device=dev)
-        L["fused_add_rmsnorm_pad"] = lambda d=d, out=out: rra.fused_add_rmsnorm_pad(
+        L["fused_add_rmsnorm_pad"] = lambda d=d, out=out, cfg=cfg: rra.fused_add_rmsnorm_pad(
             d["x"], d["residual"], d["weight"], cfg.eps, cfg.H_pad, out)
+        io["fused_add_rmsnorm_pad"] = dict(d, out=out)
 
     if "mla_rope_kv_write" in only:
         cfg = workloads.MLA_ROPE
-        d = workloads.device_mla_rope_inputs(T, cfg, dev, salt, with_cache=rope_state is None)
-        if rope_state is None:
-            cache = d["kv_cache"]
+        state = shared.get("mla_rope_kv_write")
+        d = workloads.device_mla_rope_inputs(T, cfg, dev, salt, with_cache=state is None)
+        if state is None:
             cs_m = rra.rope_cos_sin_cache(cfg.max_pos, cfg.rope_dim, cfg.theta, device=dev)
-        else:
-            cache, cs_m = rope_state
-        L["mla_rope_kv_write"] = lambda d=d, cache=cache, cs=cs_m: rra.mla_rope_kv_write(
+            state = shared["mla_rope_kv_write"] = (d["kv_cache"], cs_m)
+        cache, cs_m = state
+        L["mla_rope_kv_write"] = lambda d=d, cache=cache, cs=cs_m, cfg=cfg: rra.mla_rope_kv_write(
             d["positions"], d["q"], d["k_pe"], d["kv_c"], cs, d["slot_mapping"], cache, cfg.Hq,
             cfg.rope_dim, cfg.nope + cfg.rope_dim, cfg.nope, is_neox=cfg.is_neox)
-        L["_rope_state"] = (cache, cs_m)
+        io["mla_rope_kv_write"] = dict(d, kv_cache=cache)
 
     if "dual_rmsnorm_quant" in only:
         d = workloads.device_mla_inputs(T, workloads.MLA, dev, salt)
@@ -271,12 +282,14 @@ def make_launchers(T: int, salt: int = 0, rope_state=None, only=KERNELS):
         kvo = torch.empty((T, MLA_HKV), dtype=torch.bfloat16, device=dev)
         L["dual_rmsnorm_quant"] = lambda d=d, qo=qo, qs=qs, kvo=kvo: rra.dual_rmsnorm_quant(
             d["q"], d["q_w"], 1e-6, d["kv"], d["kv_w"], 1e-6, rra.Q_PER_GROUP, G, qo, qs, kvo)
+        io["dual_rmsnorm_quant"] = dict(d, q_out=qo, q_scales=qs, kv_out=kvo)
     torch.cuda.synchronize()
     return L
 
 
 def run_steps(launch, steps: int, warmup: int):
-    """Warm up, then time `steps` passes over the four kernels.  Returns
+    """Warm up, then time `steps` passes over the four kernels (launch: the
+    dict of make_launchers).  Returns
     (wall seconds for the timed steps, {kernel: [per-launch ms]})."""
     import torch
 
@@ -363,10 +376,10 @@ def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS):
         for n in kernels:
             n_sets = max(2, min(256, -(-(1 << 30) // algo_bytes(n, T))))
             sets = []
-            state = None  # one cache (and table) shared by the kernel's buffer sets
+            shared = None  # one cache (and table) shared by the kernel's buffer sets
             for salt in range(n_sets):
-                L = make_launchers(T, salt, state, only=(n,))
-                state = L.get("_rope_state", state)
+                L = make_launchers(T, salt, shared, only=(n,))
+                shared = L["_shared"]
                 sets.append(L)
             for s in sets:  # warm-up: one launch per set
                 s[n]()
