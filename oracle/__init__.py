@@ -92,12 +92,16 @@ def _declare(L: ctypes.CDLL) -> None:
     silu = [_p, _i64, _i32, _i32, _f32, _p, _i64, _p, _i64, _i64]
     L.orc_silu_mul_quant.argtypes = silu
     L.orc_unfused_silu_mul_quant.argtypes = silu
+    L.orc_f16_encode.restype = ctypes.c_uint16
+    L.orc_f16_encode.argtypes = [_f64]
+    L.orc_f16_decode.restype = _f64
+    L.orc_f16_decode.argtypes = [ctypes.c_uint16]
     L.orc_rope_kv_write.argtypes = [
         _p, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _f64, _i64, _p, _p, _p,
-        _i64, _i32, _i32, _i32, _i32, _i32, _i64, _i32]
+        _i64, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32]
     L.orc_unfused_rope_kv_write.argtypes = [
         _p, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _f64, _i64, _p, _p, _p,
-        _i64, _i32, _i32, _i32, _i32, _i32, _i64, _i32]
+        _i64, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32]
     dual = [_p, _i64, _p, _f32, _p, _i64, _p, _f32, _i32, _i32, _p, _i64, _p, _p, _i64,
             _i64, _i64, _i64]
     L.orc_dual_rmsnorm_quant.argtypes = dual
@@ -156,6 +160,14 @@ def bf16_decode(h: int) -> float:
     return float(lib().orc_bf16_decode(int(h)))
 
 
+def f16_encode(v: float) -> int:
+    return int(lib().orc_f16_encode(float(v)))
+
+
+def f16_decode(h: int) -> float:
+    return float(lib().orc_f16_decode(int(h)))
+
+
 def e4m3fn_encode(v: float) -> int:
     return int(lib().orc_e4m3fn_encode(float(v)))
 
@@ -204,6 +216,16 @@ def e4m3fn_cross_check(begin: int, end: int) -> int:
 
 
 # ---- fused ops and their unfused compositions --------------------------------
+
+DT_BF16, DT_F16 = 0, 1
+
+
+def _dtype(name: str) -> int:
+    codes = {"bf16": DT_BF16, "f16": DT_F16}
+    if name not in codes:
+        raise ValueError(f"element type must be 'bf16' or 'f16', not {name!r}")
+    return codes[name]
+
 
 def _scales_shape(mode: int, T: int, H: int, g: int):
     if mode == Q_PER_TOKEN:
@@ -278,8 +300,9 @@ def _head_rows(a, H, D):
 
 
 def rope_kv_write(positions, q, k, v, theta, max_pos, slot_mapping, key_cache, value_cache,
-                  Hq, Hkv, D, rot_dim=None, is_neox=True):
-    """Returns (q_out, key_cache', value_cache'); the input caches are not modified."""
+                  Hq, Hkv, D, rot_dim=None, is_neox=True, dtype="bf16"):
+    """Returns (q_out, key_cache', value_cache'); the input caches are not modified.
+    q, k, v and the caches are uint16 bit patterns of dtype ("bf16" or "f16")."""
     rot_dim = D if rot_dim is None else rot_dim
     positions = np.ascontiguousarray(positions, dtype=np.int64)
     slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
@@ -294,13 +317,13 @@ def rope_kv_write(positions, q, k, v, theta, max_pos, slot_mapping, key_cache, v
     rc = lib().orc_rope_kv_write(_ptr(positions), _ptr(q), qs, _ptr(q_out), Hq * D, _ptr(k), ks,
                                  _ptr(v), vs, float(theta), int(max_pos), _ptr(slots), _ptr(kc),
                                  _ptr(vc), T, Hq, Hkv, D, rot_dim, block_size, num_blocks,
-                                 int(bool(is_neox)))
+                                 int(bool(is_neox)), _dtype(dtype))
     _check("orc_rope_kv_write", rc)
     return q_out, kc, vc
 
 
 def unfused_rope_kv_write(positions, q, k, v, theta, max_pos, slot_mapping, key_cache,
-                          value_cache, Hq, Hkv, D, rot_dim=None, is_neox=True):
+                          value_cache, Hq, Hkv, D, rot_dim=None, is_neox=True, dtype="bf16"):
     """Returns (q_out, k_out, key_cache', value_cache')."""
     rot_dim = D if rot_dim is None else rot_dim
     positions = np.ascontiguousarray(positions, dtype=np.int64)
@@ -317,7 +340,7 @@ def unfused_rope_kv_write(positions, q, k, v, theta, max_pos, slot_mapping, key_
     rc = lib().orc_unfused_rope_kv_write(
         _ptr(positions), _ptr(q), qs, _ptr(q_out), Hq * D, _ptr(k), ks, _ptr(k_out), _ptr(v),
         vs, float(theta), int(max_pos), _ptr(slots), _ptr(kc), _ptr(vc), T, Hq, Hkv, D,
-        rot_dim, block_size, num_blocks, int(bool(is_neox)))
+        rot_dim, block_size, num_blocks, int(bool(is_neox)), _dtype(dtype))
     _check("orc_unfused_rope_kv_write", rc)
     return q_out, k_out, kc, vc
 

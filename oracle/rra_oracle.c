@@ -67,6 +67,57 @@ double orc_bf16_decode(uint16_t h) {
 
 float orc_fp32_round(double v) { return (float)v; /* RNE in FE_TONEAREST */ }
 
+/* IEEE 754 binary16 (fp16): 1 sign, 5 exponent (bias 15), 10 fraction bits.
+ * Normal values (1 + f/1024) * 2^(e-15) for exponent fields 1..30, subnormals
+ * f * 2^-24 for field 0, infinities and NaNs for field 31; largest finite
+ * value (2 - 2^-10) * 2^15 = 65504. */
+static const double kF16Max = 65504.0;
+
+/* Round a double to the nearest fp16, ties to even, overflow to infinity,
+ * NaN to a quiet NaN of the same sign.  Same method as orc_bf16_encode: the
+ * neighbours of |v| are integer multiples of the quantum 2^(E-10) of its
+ * binade E, clamped to the smallest normal binade -14 (the subnormals' quantum
+ * 2^-24). */
+uint16_t orc_f16_encode(double v) {
+  const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+  const double a = fabs(v);
+  if (isinf(a)) return (uint16_t)(sign | 0x7C00u);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e); /* a in [2^(e-1), 2^e) */
+  int E = e - 1;
+  if (E < -14) E = -14;
+  const double r = nearbyint(a / ldexp(1.0, E - 10)) * ldexp(1.0, E - 10);
+  if (r > kF16Max) return (uint16_t)(sign | 0x7C00u);
+  /* Encode the fp16 value r exactly. */
+  if (r < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+  frexp(r, &e);
+  const int Er = e - 1; /* r in [2^Er, 2^(Er+1)), -14 <= Er <= 15 */
+  const uint16_t frac = (uint16_t)((r / ldexp(1.0, Er) - 1.0) * 1024.0);
+  return (uint16_t)(sign | (uint16_t)((Er + 15) << 10) | frac);
+}
+
+double orc_f16_decode(uint16_t h) {
+  const int s = h >> 15, e = (h >> 10) & 0x1F, f = h & 0x3FF;
+  double mag;
+  if (e == 0x1F)
+    mag = f ? NAN : INFINITY;
+  else if (e == 0)
+    mag = ldexp((double)f, -24);
+  else
+    mag = ldexp(1.0 + (double)f / 1024.0, e - 15);
+  return s ? -mag : mag;
+}
+
+/* The 16-bit element types the RoPE path reads and writes. */
+static double elem_decode(uint16_t h, int dtype) {
+  return dtype == ORC_DT_F16 ? orc_f16_decode(h) : orc_bf16_decode(h);
+}
+static uint16_t elem_encode(double v, int dtype) {
+  return dtype == ORC_DT_F16 ? orc_f16_encode(v) : orc_bf16_encode(v);
+}
+
 /* [OFP8] E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits.
  * Exponent field 0 encodes subnormals m * 2^-9; S.1111.111 is NaN; there is
  * no infinity, so S.1111.110 = 448 is the largest finite magnitude. */
@@ -404,9 +455,10 @@ int orc_unfused_silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_
 /* ======================================================================= */
 
 static int rope_args_ok(int64_t T, int Hq, int Hkv, int D, int rot_dim, int block_size,
-                        int64_t num_blocks, int is_neox) {
+                        int64_t num_blocks, int is_neox, int dtype) {
   return T >= 0 && Hq > 0 && Hkv > 0 && D > 0 && rot_dim > 0 && rot_dim % 2 == 0 &&
-         rot_dim <= D && block_size > 0 && num_blocks > 0 && (is_neox == 0 || is_neox == 1);
+         rot_dim <= D && block_size > 0 && num_blocks > 0 && (is_neox == 0 || is_neox == 1) &&
+         (dtype == ORC_DT_BF16 || dtype == ORC_DT_F16);
 }
 
 static int cmp_i64(const void* a, const void* b) {
@@ -450,25 +502,26 @@ static void rope_angles(int64_t pos, double theta, int rot_dim, double* c, doubl
   }
 }
 
-/* Rotate one head of D values.  Pairs are (i, i + rot_dim/2) in the GPT-NeoX
+/* Rotate one head of D values of element type dtype (each output rounded once
+ * from double).  Pairs are (i, i + rot_dim/2) in the GPT-NeoX
  * layout and (2i, 2i+1) in the GPT-J layout; each pair (a, b) becomes
  * (a cos - b sin, b cos + a sin).  Dimensions at and past rot_dim pass
  * through.  The head is read completely before it is written, so out may
  * alias in. */
 static void rotate_head(const uint16_t* in, uint16_t* out, const double* c, const double* s,
-                        int D, int rot_dim, int is_neox) {
+                        int D, int rot_dim, int is_neox, int dtype) {
   double* x = (double*)malloc((size_t)D * sizeof(double));
   uint16_t* keep = (uint16_t*)malloc((size_t)D * sizeof(uint16_t));
   for (int d = 0; d < D; ++d) {
-    x[d] = orc_bf16_decode(in[d]);
+    x[d] = elem_decode(in[d], dtype);
     keep[d] = in[d];
   }
   const int half = rot_dim / 2;
   for (int i = 0; i < half; ++i) {
     const int a = is_neox ? i : 2 * i;
     const int b = is_neox ? i + half : 2 * i + 1;
-    out[a] = orc_bf16_encode(x[a] * c[i] - x[b] * s[i]);
-    out[b] = orc_bf16_encode(x[b] * c[i] + x[a] * s[i]);
+    out[a] = elem_encode(x[a] * c[i] - x[b] * s[i], dtype);
+    out[b] = elem_encode(x[b] * c[i] + x[a] * s[i], dtype);
   }
   for (int d = rot_dim; d < D; ++d) out[d] = keep[d];
   free(x);
@@ -489,15 +542,18 @@ static uint16_t* cache_head(uint16_t* cache, int64_t slot, int block_size, int H
 /* Rotary embedding fused with the KV-cache scatter: rotated q is written to
  * q_out (which may alias q), rotated k and the unmodified v go straight into
  * the slot of each token; k is not written anywhere else, and tokens with a
- * negative slot (padding, a reading) write no cache.
+ * negative slot (padding, a reading) write no cache.  q, k, v and the caches
+ * hold one 16-bit element type, bf16 or fp16 (dtype): the fusion is listed
+ * for both on ROCm in the [FUSION] support matrix.
  * [FUSION] section "RoPE + KV-Cache Update (fuse_rope_kvcache)". */
 int orc_rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_stride,
                       uint16_t* q_out, int64_t q_out_stride, const uint16_t* k,
                       int64_t k_stride, const uint16_t* v, int64_t v_stride, double theta,
                       int64_t max_pos, const int64_t* slot_mapping, uint16_t* key_cache,
                       uint16_t* value_cache, int64_t T, int Hq, int Hkv, int D, int rot_dim,
-                      int block_size, int64_t num_blocks, int is_neox) {
-  if (!rope_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox)) return ORC_EARG;
+                      int block_size, int64_t num_blocks, int is_neox, int dtype) {
+  if (!rope_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox, dtype))
+    return ORC_EARG;
   if (!rope_contract_ok(positions, max_pos, slot_mapping, T, block_size, num_blocks))
     return ORC_ECONTRACT;
 #pragma omp parallel for schedule(static)
@@ -507,13 +563,13 @@ int orc_rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_str
     rope_angles(positions[t], theta, rot_dim, c, s);
     for (int h = 0; h < Hq; ++h)
       rotate_head(q + t * q_stride + (int64_t)h * D, q_out + t * q_out_stride + (int64_t)h * D,
-                  c, s, D, rot_dim, is_neox);
+                  c, s, D, rot_dim, is_neox, dtype);
     const int64_t slot = slot_mapping[t];
     if (slot >= 0) {
       for (int h = 0; h < Hkv; ++h) {
         rotate_head(k + t * k_stride + (int64_t)h * D,
                     cache_head(key_cache, slot, block_size, Hkv, D, h), c, s, D, rot_dim,
-                    is_neox);
+                    is_neox, dtype);
         memcpy(cache_head(value_cache, slot, block_size, Hkv, D, h),
                v + t * v_stride + (int64_t)h * D, (size_t)D * sizeof(uint16_t));
       }
@@ -533,8 +589,10 @@ int orc_unfused_rope_kv_write(const int64_t* positions, const uint16_t* q, int64
                               int64_t v_stride, double theta, int64_t max_pos,
                               const int64_t* slot_mapping, uint16_t* key_cache,
                               uint16_t* value_cache, int64_t T, int Hq, int Hkv, int D,
-                              int rot_dim, int block_size, int64_t num_blocks, int is_neox) {
-  if (!rope_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox)) return ORC_EARG;
+                              int rot_dim, int block_size, int64_t num_blocks, int is_neox,
+                              int dtype) {
+  if (!rope_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox, dtype))
+    return ORC_EARG;
   if (!rope_contract_ok(positions, max_pos, slot_mapping, T, block_size, num_blocks))
     return ORC_ECONTRACT;
   /* op 1: rotary embedding of q and k */
@@ -545,10 +603,10 @@ int orc_unfused_rope_kv_write(const int64_t* positions, const uint16_t* q, int64
     rope_angles(positions[t], theta, rot_dim, c, s);
     for (int h = 0; h < Hq; ++h)
       rotate_head(q + t * q_stride + (int64_t)h * D, q_out + t * q_out_stride + (int64_t)h * D,
-                  c, s, D, rot_dim, is_neox);
+                  c, s, D, rot_dim, is_neox, dtype);
     for (int h = 0; h < Hkv; ++h)
       rotate_head(k + t * k_stride + (int64_t)h * D, k_out + (t * Hkv + h) * (int64_t)D, c, s,
-                  D, rot_dim, is_neox);
+                  D, rot_dim, is_neox, dtype);
     free(c);
     free(s);
   }
@@ -686,7 +744,7 @@ static void norm_rope_head(const uint16_t* in, const uint16_t* w, float eps, int
 
 static int qknorm_args_ok(int64_t T, int Hq, int Hkv, int D, int rot_dim, int block_size,
                           int64_t num_blocks, int is_neox, int64_t qkv_stride) {
-  return rope_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox) &&
+  return rope_args_ok(T, Hq, Hkv, D, rot_dim, block_size, num_blocks, is_neox, ORC_DT_BF16) &&
          qkv_stride >= (int64_t)(Hq + 2 * Hkv) * D;
 }
 
@@ -838,13 +896,14 @@ int orc_mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64_t q_st
     rope_angles(positions[t], theta, rope_dim, c, s);
     for (int h = 0; h < Hq; ++h) {
       uint16_t* qh = q_pe + t * q_stride + (int64_t)h * q_head_stride;
-      rotate_head(qh, qh, c, s, rope_dim, rope_dim, is_neox);
+      rotate_head(qh, qh, c, s, rope_dim, rope_dim, is_neox, ORC_DT_BF16);
     }
     const int64_t slot = slot_mapping[t];
     if (slot >= 0) {
       uint16_t* dst = kv_cache + slot * row_w;  /* [num_blocks, block_size] flattened */
       memcpy(dst, kv_c + t * kv_c_stride, (size_t)kv_lora * sizeof(uint16_t));
-      rotate_head(k_pe + t * k_pe_stride, dst + kv_lora, c, s, rope_dim, rope_dim, is_neox);
+      rotate_head(k_pe + t * k_pe_stride, dst + kv_lora, c, s, rope_dim, rope_dim, is_neox,
+                  ORC_DT_BF16);
     }
     free(c);
     free(s);

@@ -45,9 +45,15 @@ extern "C" {
 #define ORC_Q_PER_TOKEN 2 /* scale = row amax / 448 */
 #define ORC_Q_PER_GROUP 3 /* scale = amax of each contiguous group / 448 */
 
+/* 16-bit element types of the RoPE + KV-cache path. */
+#define ORC_DT_BF16 0
+#define ORC_DT_F16 1 /* IEEE binary16 */
+
 /* ---- codecs ------------------------------------------------------------ */
 uint16_t orc_bf16_encode(double v);
 double orc_bf16_decode(uint16_t h);
+uint16_t orc_f16_encode(double v); /* round-to-nearest-even, overflow to inf */
+double orc_f16_decode(uint16_t h);
 uint8_t orc_e4m3fn_encode(double v);       /* table + binary search */
 uint8_t orc_e4m3fn_encode_arith(double v); /* independent: frexp + rint */
 double orc_e4m3fn_decode(uint8_t c);
@@ -83,7 +89,7 @@ int orc_rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_str
                       int64_t k_stride, const uint16_t* v, int64_t v_stride, double theta,
                       int64_t max_pos, const int64_t* slot_mapping, uint16_t* key_cache,
                       uint16_t* value_cache, int64_t T, int Hq, int Hkv, int D, int rot_dim,
-                      int block_size, int64_t num_blocks, int is_neox);
+                      int block_size, int64_t num_blocks, int is_neox, int dtype);
 
 /* q_quant_mode NONE writes bf16 into q_out (as uint16_t), otherwise e4m3fn
  * codes (as uint8_t). */
@@ -121,7 +127,8 @@ int orc_unfused_rope_kv_write(const int64_t* positions, const uint16_t* q, int64
                               int64_t v_stride, double theta, int64_t max_pos,
                               const int64_t* slot_mapping, uint16_t* key_cache,
                               uint16_t* value_cache, int64_t T, int Hq, int Hkv, int D,
-                              int rot_dim, int block_size, int64_t num_blocks, int is_neox);
+                              int rot_dim, int block_size, int64_t num_blocks, int is_neox,
+                              int dtype);
 
 /* ---- next rows ---------------------------------------------------------- */
 /* qkv: [T, (Hq + 2 Hkv) D], row stride qkv_stride; the q part (and with

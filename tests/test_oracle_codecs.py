@@ -100,3 +100,52 @@ def test_bf16_double_rounding_cases(oracle):
 def test_fp32_round(oracle):
     for v in (1 / 3, 1 / 448, 2.0 ** -140, 123456.789):
         assert oracle.fp32_round(v) == float(np.float32(v))
+
+
+# ---- IEEE binary16 (fp16) -----------------------------------------------------
+
+def _all_f16_values() -> np.ndarray:
+    return np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def test_f16_decode_matches_numpy_on_every_code(oracle):
+    ref = _all_f16_values()
+    ours = np.array([oracle.f16_decode(c) for c in range(1 << 16)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))  # -0.0
+
+
+def test_f16_encode_matches_numpy_at_rounding_points(oracle):
+    """Every finite positive fp16 value, the exact midpoint to its upper
+    neighbour (a tie) and doubles a hair on either side of that midpoint, in
+    both signs; numpy converts float64 -> float16 directly, with one rounding."""
+    vals = _all_f16_values()[:0x7C00]  # +0 .. 65504
+    mids = (vals[:-1] + vals[1:]) / 2
+    top = np.array([65504.0 + 8, 65504.0 + 16, 65504.0 + 16 - 2 ** -30, 1e6])
+    x = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf), top])
+    x = np.concatenate([x, -x])
+    ours = np.array([oracle.f16_encode(v) for v in x], np.uint16)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    bad = np.flatnonzero(ours != ref)
+    assert bad.size == 0, [(float(x[i]), hex(ours[i]), hex(ref[i])) for i in bad[:8]]
+
+
+def test_f16_rounding_cases(oracle):
+    enc = oracle.f16_encode
+    assert enc(1.0) == 0x3C00 and enc(-2.0) == 0xC000
+    assert enc(1.0 + 2 ** -11) == 0x3C00  # tie -> even (1.0)
+    assert enc(1.0 + 3 * 2 ** -11) == 0x3C02  # tie -> even (1 + 2^-9)
+    assert enc(1.0 + 2 ** -11 + 2 ** -40) == 0x3C01
+    assert enc(65504.0) == 0x7BFF  # largest finite
+    assert enc(65519.99) == 0x7BFF and enc(65520.0) == 0x7C00  # tie at the top -> inf
+    assert enc(-1e300) == 0xFC00 and enc(math.inf) == 0x7C00
+    assert enc(2 ** -24) == 0x0001 and enc(2 ** -25) == 0x0000  # tie -> even (zero)
+    assert enc(3 * 2 ** -25) == 0x0002  # tie between 1 and 2 units -> 2
+    assert enc(2 ** -14 - 2 ** -25) == 0x0400  # largest subnormal rounds up to the smallest normal
+    assert enc(-0.0) == 0x8000 and enc(0.0) == 0x0000
+    assert (enc(math.nan) & 0x7C00) == 0x7C00 and (enc(math.nan) & 0x3FF)
+    for h in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xC2F7, 0x8001):
+        assert enc(oracle.f16_decode(h)) == h

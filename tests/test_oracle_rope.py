@@ -6,7 +6,9 @@ position) and the geometric progression of the others; pair norms are kept;
 q.k after rotation depends only on the position difference.  Cache write:
 the PagedAttention block-table example, brute force over every injective
 slot assignment on a tiny cache, sentinel preservation and the contract
-errors."""
+errors.  The fp16 element type: identity at position 0, one-hot values equal
+to numpy's fp16 rounding of cos and sin, and agreement with the bf16 path on
+inputs that both types hold exactly."""
 import itertools
 import math
 
@@ -24,9 +26,10 @@ def _bf16(a):
 
 
 def _run(oracle, positions, q, k, v, slots, kc, vc, Hq, Hkv, D, theta=THETA, max_pos=1 << 20,
-         rot_dim=None, is_neox=True):
+         rot_dim=None, is_neox=True, dtype="bf16"):
     return oracle.rope_kv_write(np.asarray(positions, np.int64), q, k, v, theta, max_pos,
-                                np.asarray(slots, np.int64), kc, vc, Hq, Hkv, D, rot_dim, is_neox)
+                                np.asarray(slots, np.int64), kc, vc, Hq, Hkv, D, rot_dim, is_neox,
+                                dtype)
 
 
 def _empty_cache(num_blocks, block_size, Hkv, D, fill=0x7E7E):
@@ -191,3 +194,90 @@ def test_contract_errors(oracle):
         _run(oracle, d["positions"], *args, d["slot_mapping"], kc, kc, 32, 8, 128, rot_dim=127)
     assert e.value.rc == oracle.EARG
     _run(oracle, d["positions"], *args, [-1, -1, 3, 4], kc, kc, 32, 8, 128, max_pos=8192)
+
+
+# ---- fp16 elements ---------------------------------------------------------------
+
+def _f16(a):
+    return np.asarray(a, np.float64).astype(np.float16).view(np.uint16)
+
+
+def _f16_to_f64(h):
+    return np.asarray(h, np.uint16).view(np.float16).astype(np.float64)
+
+
+def test_f16_position_zero_is_identity(oracle):
+    rng = np.random.default_rng(5)
+    q, k, v = (_f16(rng.standard_normal((8, H, 64))) for H in (4, 2, 2))
+    kc = _empty_cache(8, 4, 2, 64)
+    slots = rng.permutation(32)[:8]
+    q_out, kc2, vc2 = _run(oracle, np.zeros(8), q, k, v, slots, kc, kc.copy(), 4, 2, 64,
+                           dtype="f16")
+    assert np.array_equal(q_out, q)
+    assert np.array_equal(kc2.reshape(-1, 2, 64)[slots], k)
+    assert np.array_equal(vc2.reshape(-1, 2, 64)[slots], v)
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_f16_one_hot_is_rounded_cos_sin(oracle, is_neox):
+    """A 1.0 at pair i's first element turns into (cos, sin) of pos * theta^(-2i/D),
+    each rounded once to fp16 (numpy's float64 -> float16 rounding)."""
+    D, pos = 64, 1234
+    for i in (0, 7, 31):
+        q = np.zeros((1, 1, D), np.uint16)
+        a, b = (i, i + D // 2) if is_neox else (2 * i, 2 * i + 1)
+        q[0, 0, a] = 0x3C00
+        q_out, _, _ = _run(oracle, [pos], q, q.copy(), q.copy(), [-1], _empty_cache(1, 1, 1, D),
+                           _empty_cache(1, 1, 1, D), 1, 1, D, is_neox=is_neox, dtype="f16")
+        ang = pos * THETA ** (-2.0 * i / D)
+        assert q_out[0, 0, a] == _f16(math.cos(ang)) and q_out[0, 0, b] == _f16(math.sin(ang))
+        rest = np.delete(q_out[0, 0], [a, b])
+        assert np.all(_f16_to_f64(rest) == 0)  # +0 or -0 (0 * cos - 0 * sin)
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_f16_agrees_with_bf16_on_shared_values(oracle, is_neox):
+    """bf16 inputs in [2^-14, 2^15) are exact fp16 values too.  Both element
+    types rotate the same reals in double, so each fp16 output rounded on to
+    bf16 is within one bf16 unit of the bf16 output, and v is copied bit for
+    bit in either type."""
+    T, Hq, Hkv, D, nb, B = 16, 4, 2, 128, 4, 8
+    rng = np.random.default_rng(11)
+
+    def shared(shape):
+        x = rng.standard_normal(shape)
+        x = np.where(np.abs(x) < 2 ** -13, 0.5, x)
+        return _bf16(x)
+
+    qb, kb, vb = shared((T, Hq, D)), shared((T, Hkv, D)), shared((T, Hkv, D))
+    qh, kh, vh = (_f16(bf16_to_f64(a)) for a in (qb, kb, vb))
+    assert np.array_equal(_f16_to_f64(qh), bf16_to_f64(qb))
+    pos = rng.integers(0, 4096, T)
+    slots = rng.permutation(nb * B)[:T]
+    kc = np.zeros((nb, B, Hkv, D), np.uint16)
+    ob = _run(oracle, pos, qb, kb, vb, slots, kc, kc.copy(), Hq, Hkv, D, is_neox=is_neox)
+    oh = _run(oracle, pos, qh, kh, vh, slots, kc, kc.copy(), Hq, Hkv, D, is_neox=is_neox,
+              dtype="f16")
+    for got_h, got_b in ((oh[0], ob[0]), (oh[1], ob[1])):
+        via = _bf16(_f16_to_f64(got_h)).astype(np.int32)
+        sb = got_b.astype(np.int32)
+        assert np.max(np.abs(via - sb)) <= 1
+        assert np.mean(via == sb) > 0.9
+    w = oh[2].reshape(-1, Hkv, D)[slots]
+    assert np.array_equal(w, vh)
+
+
+def test_f16_fused_equals_unfused_and_bad_dtype(oracle):
+    rng = np.random.default_rng(3)
+    T, Hq, Hkv, D = 8, 2, 1, 64
+    q, k, v = _f16(rng.standard_normal((T, Hq, D))), _f16(rng.standard_normal((T, Hkv, D))), \
+        _f16(rng.standard_normal((T, Hkv, D)))
+    pos, slots = rng.integers(0, 100, T), rng.permutation(16)[:T]
+    kc = _empty_cache(2, 8, Hkv, D)
+    a = _run(oracle, pos, q, k, v, slots, kc, kc.copy(), Hq, Hkv, D, dtype="f16")
+    b = oracle.unfused_rope_kv_write(pos, q, k, v, THETA, 1 << 20, slots, kc, kc.copy(), Hq, Hkv,
+                                     D, dtype="f16")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[2])
+    assert np.array_equal(a[2], b[3])
+    with pytest.raises(ValueError):
+        _run(oracle, pos, q, k, v, slots, kc, kc, Hq, Hkv, D, dtype="fp8")
