@@ -66,11 +66,13 @@ KERNELS = tuple(BYTES_PER_TOKEN)
 
 # The next rows, measured beside the step (not part of it): QK norm + RoPE + KV
 # write at the Qwen3-8B attention shape, residual add + RMSNorm + padding at
-# GPT-OSS width, MLA q_pe/k_pe RoPE + [kv_c | k_pe] cache write at DeepSeek-V3.
+# GPT-OSS width, MLA q_pe/k_pe RoPE + [kv_c | k_pe] cache write at DeepSeek-V3,
+# and the RoPE + KV write of the step with fp16 instead of bf16 elements.
 QK_HQ, QK_HKV, QK_D = 32, 8, 128
 PAD_H, PAD_HP = 2880, 3072
 MR_HQ, MR_NOPE, MR_ROPE, MR_LORA = 128, 128, 64, 512
 BYTES_PER_TOKEN.update({
+    "rope_kv_write_f16": BYTES_PER_TOKEN["rope_kv_write"],
     "qk_norm_rope_kv_write": 2 * (QK_HQ + 2 * QK_HKV) * QK_D + 2 * QK_HQ * QK_D
     + 2 * 2 * QK_HKV * QK_D + 16,
     "fused_add_rmsnorm_pad": 2 * 2 * PAD_H + 2 * PAD_H + 2 * PAD_HP,
@@ -78,11 +80,13 @@ BYTES_PER_TOKEN.update({
     + 2 * (MR_LORA + MR_ROPE) + 16,
 })
 BYTES_PER_LAUNCH.update({
+    "rope_kv_write_f16": 0,
     "qk_norm_rope_kv_write": 2 * 2 * QK_D,
     "fused_add_rmsnorm_pad": 2 * PAD_H,
     "mla_rope_kv_write": 0,
 })
-NEXT_KERNELS = ("qk_norm_rope_kv_write", "fused_add_rmsnorm_pad", "mla_rope_kv_write")
+NEXT_KERNELS = ("qk_norm_rope_kv_write", "fused_add_rmsnorm_pad", "mla_rope_kv_write",
+                "rope_kv_write_f16")
 
 
 def algo_bytes(name: str, T: int) -> int:
@@ -100,7 +104,12 @@ KERNEL_SYMBOL = {
     "qk_norm_rope_kv_write": "qk_norm_rope_kv_kernel",
     "fused_add_rmsnorm_pad": "add_rmsnorm_pad_kernel",
     "mla_rope_kv_write": "mla_rope_kv_kernel",
+    "rope_kv_write_f16": "rope_kv_write_kernel",
 }
+# Kernels that share a symbol with another and differ in a template argument:
+# the argument's text in the demangled name.  Names of the plain kernel must not
+# contain it.
+KERNEL_TAG = {"rope_kv_write_f16": "ElemF16"}
 KERNEL_SOURCES = {
     "fused_add_rmsnorm_quant": ("norm_quant.hip",),
     "dual_rmsnorm_quant": ("norm_quant.hip",),
@@ -109,6 +118,7 @@ KERNEL_SOURCES = {
     "qk_norm_rope_kv_write": ("rope_kv.hip",),
     "fused_add_rmsnorm_pad": ("norm_quant.hip",),
     "mla_rope_kv_write": ("rope_kv.hip",),
+    "rope_kv_write_f16": ("rope_kv.hip",),
 }
 COMMON_SOURCES = ("rra_device.hpp", "rra_host.hpp")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_kernels_T8192_hbm_traffic.md")
@@ -238,6 +248,18 @@ def make_launchers(T: int, salt: int = 0, shared=None, only=KERNELS):
         L["rope_kv_write"] = lambda d=d, kc=kc, vc=vc, cs=cs: rra.rope_kv_write(
             d["positions"], d["q"], d["k"], d["v"], cs, d["slot_mapping"], kc, vc)
         io["rope_kv_write"] = dict(d, key_cache=kc, value_cache=vc)
+
+    if "rope_kv_write_f16" in only:
+        cfg = workloads.ROPE_F16
+        state = shared.get("rope_kv_write_f16")
+        d = workloads.device_rope_inputs(T, cfg, dev, salt, with_cache=state is None)
+        if state is None:
+            cs = rra.rope_cos_sin_cache(cfg.max_pos, cfg.rot_dim, cfg.theta, device=dev)
+            state = shared["rope_kv_write_f16"] = (d["key_cache"], d["value_cache"], cs)
+        kc, vc, cs = state
+        L["rope_kv_write_f16"] = lambda d=d, kc=kc, vc=vc, cs=cs: rra.rope_kv_write(
+            d["positions"], d["q"], d["k"], d["v"], cs, d["slot_mapping"], kc, vc)
+        io["rope_kv_write_f16"] = dict(d, key_cache=kc, value_cache=vc)
 
     if "qk_norm_rope_kv_write" in only:
         cfg = workloads.QKNORM
@@ -456,8 +478,14 @@ def cpu_baseline(sample_T: int):
 # ---- profile summaries (rocprofv3 CSV -> profiles/*.md) ----------------------------
 
 def _kernel_of(symbol_name: str):
+    tags = set(KERNEL_TAG.values())
     for k, sym in KERNEL_SYMBOL.items():
-        if f"rra::{sym}<" in symbol_name or f"rra::{sym}(" in symbol_name:
+        if f"rra::{sym}<" not in symbol_name and f"rra::{sym}(" not in symbol_name:
+            continue
+        tag = KERNEL_TAG.get(k)
+        if tag is not None and tag in symbol_name:
+            return k
+        if tag is None and not any(t in symbol_name for t in tags):
             return k
     return None
 

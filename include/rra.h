@@ -11,7 +11,9 @@
  * ----------------------------------------
  * - Types: bf16 tensors are passed as uint16_t bit patterns; FP8 outputs are
  *   OCP e4m3fn bytes (largest finite value 448, round-to-nearest-even,
- *   saturating); scales are fp32; token indices are int64.
+ *   saturating); scales are fp32; token indices are int64.  Entry points with
+ *   a `dtype` argument (enum rra_dtype) take bf16 or IEEE fp16 tensors, also
+ *   as uint16_t bit patterns; the same alignment rules apply to both.
  * - Layout: 2-D tensors are row-major [T, width] with an arbitrary row stride
  *   (in elements) and contiguous rows, so column slices ("split" views of a
  *   wider projection) are valid inputs.
@@ -44,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RRA_ABI_VERSION 1
+#define RRA_ABI_VERSION 2
 
 enum rra_status {
   RRA_OK = 0,
@@ -60,6 +62,12 @@ enum rra_quant_mode {
   RRA_Q_STATIC = 1,    /* one per-tensor scale given by the caller */
   RRA_Q_PER_TOKEN = 2, /* scale[t] = amax over the row / 448 */
   RRA_Q_PER_GROUP = 3  /* scale[t, k] = amax over columns [k*g, (k+1)*g) / 448 */
+};
+
+/* 16-bit element types selectable through a `dtype` argument. */
+enum rra_dtype {
+  RRA_BF16 = 0, /* bfloat16 */
+  RRA_F16 = 1   /* IEEE 754 binary16; results round to nearest even, overflow to inf */
 };
 
 /* Version of this ABI (RRA_ABI_VERSION of the built library). */
@@ -148,22 +156,28 @@ int rope_cos_sin_cache(float* cos_sin, int64_t max_pos, int rot_dim, double thet
  * s % block_size, :, :] and v, unchanged, to value_cache at the same place.
  * Tokens with s < 0 (padding) write no cache.  Nothing else is written.
  *
+ * The rotation runs in fp32 and each rotated value is rounded once to the
+ * element type dtype (RRA_BF16 or RRA_F16; the section's support matrix lists
+ * the fusion for FP16 and BF16 on ROCm), which q, q_out, k, v and both caches
+ * share.
+ *
  * positions    [T] int64.
- * q            [T, Hq, D] bf16, token stride q_stride, heads contiguous.
- * q_out        [T, Hq, D] bf16, token stride q_out_stride (may alias q).
- * k, v         [T, Hkv, D] bf16, token strides k_stride, v_stride.
+ * q            [T, Hq, D] dtype, token stride q_stride, heads contiguous.
+ * q_out        [T, Hq, D] dtype, token stride q_out_stride (may alias q).
+ * k, v         [T, Hkv, D] dtype, token strides k_stride, v_stride.
  * cos_sin      [max_pos, rot_dim] fp32 (see rope_cos_sin_cache).
  * slot_mapping [T] int64.
- * key_cache, value_cache [num_blocks, block_size, Hkv, D] bf16, contiguous.
+ * key_cache, value_cache [num_blocks, block_size, Hkv, D] dtype, contiguous.
  * Limits: D in {64, 128, 256}; rot_dim == D; is_neox 1 (GPT-NeoX pairs
- * (i, i + D/2)) or 0 (GPT-J pairs (2i, 2i + 1)); Hq, Hkv >= 1; block_size >= 1.
+ * (i, i + D/2)) or 0 (GPT-J pairs (2i, 2i + 1)); Hq, Hkv >= 1; block_size >= 1;
+ * dtype RRA_BF16 or RRA_F16 (else RRA_ERR_UNSUPPORTED).
  */
 int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_stride,
                   uint16_t* q_out, int64_t q_out_stride, const uint16_t* k, int64_t k_stride,
                   const uint16_t* v, int64_t v_stride, const float* cos_sin, int64_t max_pos,
                   const int64_t* slot_mapping, uint16_t* key_cache, uint16_t* value_cache,
                   int64_t T, int Hq, int Hkv, int D, int rot_dim, int block_size,
-                  int64_t num_blocks, int is_neox, void* stream);
+                  int64_t num_blocks, int is_neox, int dtype, void* stream);
 
 /*
  * MLA dual RMSNorm (+ FP8 quant of the q latent).

@@ -33,6 +33,10 @@ class RRAError(RuntimeError):
         self.status = status
 
 
+ABI_VERSION = 2  # RRA_ABI_VERSION of include/rra.h
+BF16, F16 = 0, 1  # enum rra_dtype
+_ELEM = {torch.bfloat16: BF16, torch.float16: F16}
+
 _lib = None
 _p, _i64, _i32, _f32, _f64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float,
                               ctypes.c_double)
@@ -47,6 +51,9 @@ def lib() -> ctypes.CDLL:
                               "`python -m rope_residual_add_amd.build`")
         L = ctypes.CDLL(LIBRARY_PATH)
         L.rra_abi_version.restype = _i32
+        if L.rra_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIBRARY_PATH} has ABI {L.rra_abi_version()}, this binding "
+                              f"needs {ABI_VERSION}: rebuild it")
         L.rra_status_string.restype = ctypes.c_char_p
         L.rra_status_string.argtypes = [_i32]
         L.fused_add_rmsnorm_quant.argtypes = [_p, _i64, _p, _i64, _p, _f32, _i32, _i32, _p, _p,
@@ -54,7 +61,7 @@ def lib() -> ctypes.CDLL:
         L.silu_mul_quant.argtypes = [_p, _i64, _i32, _i32, _p, _p, _i64, _p, _i64, _i64, _p]
         L.rope_cos_sin_cache.argtypes = [_p, _i64, _i32, _f64, _p]
         L.rope_kv_write.argtypes = [_p, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p,
-                                    _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _p]
+                                    _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _p]
         L.dual_rmsnorm_quant.argtypes = [_p, _i64, _p, _f32, _p, _i64, _p, _f32, _i32, _i32, _p,
                                          _i64, _p, _p, _i64, _i64, _i64, _i64, _p]
         L.qk_norm_rope_kv_write.argtypes = [_p, _p, _i64, _p, _p, _f32, _p, _i64, _p, _p, _p,
@@ -116,14 +123,14 @@ def _rows(name: str, t: torch.Tensor, dtypes, width: int | None = None) -> int:
     return t.stride(0)
 
 
-def _heads(name: str, t: torch.Tensor, H: int, D: int) -> int:
+def _heads(name: str, t: torch.Tensor, H: int, D: int, dtypes=(torch.bfloat16,)) -> int:
     """Check a [T, H, D] (or [T, H*D]) tensor whose heads are contiguous."""
-    _need_cuda(name, t, (torch.bfloat16,))
+    _need_cuda(name, t, dtypes)
     if t.dim() == 3:
         if tuple(t.shape[1:]) != (H, D) or (t.numel() > 0 and (t.stride(2) != 1 or t.stride(1) != D)):
             raise ValueError(f"{name} must be [T, {H}, {D}] with contiguous heads")
         return t.stride(0)
-    return _rows(name, t, (torch.bfloat16,), H * D)
+    return _rows(name, t, dtypes, H * D)
 
 
 def _check(fn: str, status: int) -> None:
@@ -205,34 +212,39 @@ def rope_cos_sin_cache(max_pos: int, rot_dim: int, theta: float, device="cuda", 
 
 def rope_kv_write(positions, q, k, v, cos_sin, slot_mapping, key_cache, value_cache,
                   q_out=None, is_neox=True):
-    """Neox RoPE of q and k + paged KV-cache write of rotated k and v.
+    """RoPE of q and k + paged KV-cache write of rotated k and v.
 
-    q: [T, Hq, D], k, v: [T, Hkv, D] bf16; cos_sin: [max_pos, rot_dim] fp32;
+    q: [T, Hq, D], k, v: [T, Hkv, D] bf16 or fp16 (one type for q, k, v,
+    q_out and both caches); cos_sin: [max_pos, rot_dim] fp32;
     positions, slot_mapping: [T] int64 (slot < 0 = padding);
-    caches: [num_blocks, block_size, Hkv, D] bf16.  q_out defaults to q
-    (in place).  Returns q_out."""
+    caches: [num_blocks, block_size, Hkv, D].  q_out defaults to q
+    (in place).  is_neox selects GPT-NeoX pairs (i, i + D/2), else GPT-J
+    pairs (2i, 2i + 1).  Returns q_out."""
     T = positions.shape[0]
     num_blocks, block_size, Hkv, D = key_cache.shape
     Hq = q.shape[1] if q.dim() == 3 else q.shape[1] // D
     _need_cuda("positions", positions, (torch.int64,))
     _need_cuda("slot_mapping", slot_mapping, (torch.int64,))
     _need_cuda("cos_sin", cos_sin, (torch.float32,))
+    _need_cuda("q", q, tuple(_ELEM))
+    elem = (q.dtype,)
     for name, c in (("key_cache", key_cache), ("value_cache", value_cache)):
-        _need_cuda(name, c, _BF16)
+        _need_cuda(name, c, elem)
         if not c.is_contiguous() or tuple(c.shape) != (num_blocks, block_size, Hkv, D):
             raise ValueError(f"{name} must be a contiguous [num_blocks, block_size, Hkv, D] tensor")
     if not (positions.is_contiguous() and slot_mapping.is_contiguous() and cos_sin.is_contiguous()):
         raise ValueError("positions, slot_mapping and cos_sin must be contiguous")
     if q_out is None:
         q_out = q
-    qs, qos = _heads("q", q, Hq, D), _heads("q_out", q_out, Hq, D)
-    ks, vs = _heads("k", k, Hkv, D), _heads("v", v, Hkv, D)
+    qs, qos = _heads("q", q, Hq, D, elem), _heads("q_out", q_out, Hq, D, elem)
+    ks, vs = _heads("k", k, Hkv, D, elem), _heads("v", v, Hkv, D, elem)
     max_pos, rot_dim = cos_sin.shape
     with torch.cuda.device(q.device):
         st = lib().rope_kv_write(
             _ptr(positions), _ptr(q), qs, _ptr(q_out), qos, _ptr(k), ks, _ptr(v), vs,
             _ptr(cos_sin), max_pos, _ptr(slot_mapping), _ptr(key_cache), _ptr(value_cache), T,
-            Hq, Hkv, D, rot_dim, block_size, num_blocks, int(bool(is_neox)), _stream(q))
+            Hq, Hkv, D, rot_dim, block_size, num_blocks, int(bool(is_neox)), _ELEM[q.dtype],
+            _stream(q))
     _check("rope_kv_write", st)
     return q_out
 

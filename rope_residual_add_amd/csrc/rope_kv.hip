@@ -81,31 +81,34 @@ __device__ __forceinline__ void rotate_unit(float x[16], const float cs[8], cons
   }
 }
 
+// Two 16-byte vectors of 8 elements each (element type E) <-> 16 fp32 values.
+template <typename E = ElemBf16>
 __device__ __forceinline__ void unpack16(u32x4 lo, u32x4 hi, float x[16]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    x[2 * k] = bf16_lo(lo[k]);
-    x[2 * k + 1] = bf16_hi(lo[k]);
-    x[8 + 2 * k] = bf16_lo(hi[k]);
-    x[8 + 2 * k + 1] = bf16_hi(hi[k]);
+    x[2 * k] = E::lo(lo[k]);
+    x[2 * k + 1] = E::hi(lo[k]);
+    x[8 + 2 * k] = E::lo(hi[k]);
+    x[8 + 2 * k + 1] = E::hi(hi[k]);
   }
 }
 
+template <typename E = ElemBf16>
 __device__ __forceinline__ void pack16(const float x[16], u32x4& lo, u32x4& hi) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    lo[k] = pack_bf16x2(x[2 * k], x[2 * k + 1]);
-    hi[k] = pack_bf16x2(x[8 + 2 * k], x[8 + 2 * k + 1]);
+    lo[k] = E::pack(x[2 * k], x[2 * k + 1]);
+    hi[k] = E::pack(x[8 + 2 * k], x[8 + 2 * k + 1]);
   }
 }
 
-template <bool kNeox>
+template <bool kNeox, typename E = ElemBf16>
 __device__ __forceinline__ void rotate_packed(u32x4& lo, u32x4& hi, const float cs[8],
                                               const float sn[8]) {
   float x[16];
-  unpack16(lo, hi, x);
+  unpack16<E>(lo, hi, x);
   rotate_unit<kNeox>(x, cs, sn);
-  pack16(x, lo, hi);
+  pack16<E>(x, lo, hi);
 }
 
 // Sum over aligned groups of n lanes (n = 4, 8 or 16), result in every lane
@@ -123,7 +126,8 @@ __device__ __forceinline__ float group_sum(float v) {
 // Units of one token: q units first, then k units, then v units (one 16-byte
 // vector of v copied into the cache); row lane rl takes units rl, rl + 256, ...
 // Each lane reads a q unit before writing it back, so q_out may alias q.
-template <int D, bool kNeox, int kU>
+// E is the element type of q, k, v and the caches (bf16 or fp16).
+template <int D, bool kNeox, int kU, typename E>
 __global__ void __launch_bounds__(kBlock)
     rope_kv_write_kernel(const int64_t* __restrict__ positions, const uint16_t* q,
                          int64_t q_stride, uint16_t* q_out, int64_t q_out_stride,
@@ -181,12 +185,12 @@ __global__ void __launch_bounds__(kBlock)
     for (int j = 0; j < kU; ++j) {
       const int u = u0 + j * kRopeLanes + rl;
       if (u < uq) {
-        rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
+        rotate_packed<kNeox, E>(lo[j], hi[j], cs, sn);
         uint16_t* p = qo + (u / kUnitsPerHead) * D;
         st_stream(p + lo_off, lo[j]);
         st_stream(p + hi_off, hi[j]);
       } else if (u < uq + uk) {
-        rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
+        rotate_packed<kNeox, E>(lo[j], hi[j], cs, sn);
         uint16_t* p = kc + ((u - uq) / kUnitsPerHead) * D;
         st_stream(p + lo_off, lo[j]);
         st_stream(p + hi_off, hi[j]);
@@ -423,7 +427,7 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
                              const int64_t* slot_mapping, uint16_t* key_cache,
                              uint16_t* value_cache, int64_t T, int Hq, int Hkv, int D,
                              int rot_dim, int block_size, int64_t num_blocks, int is_neox,
-                             void* stream) {
+                             int dtype, void* stream) {
   RRA_REQUIRE(T >= 0 && Hq > 0 && Hkv > 0 && D > 0 && rot_dim > 0 && block_size > 0 &&
                   num_blocks > 0 && max_pos > 0,
               RRA_ERR_SHAPE);
@@ -435,6 +439,7 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
               RRA_ERR_SHAPE);
   RRA_REQUIRE(D == 64 || D == 128 || D == 256, RRA_ERR_UNSUPPORTED);
   RRA_REQUIRE(rot_dim == D && (is_neox == 0 || is_neox == 1), RRA_ERR_UNSUPPORTED);
+  RRA_REQUIRE(dtype == RRA_BF16 || dtype == RRA_F16, RRA_ERR_UNSUPPORTED);
   RRA_REQUIRE(vec_ok(q, q_stride) && vec_ok(q_out, q_out_stride) && vec_ok(k, k_stride) &&
                   vec_ok(v, v_stride),
               RRA_ERR_ALIGN);
@@ -446,26 +451,32 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
 
   const hipStream_t st = as_stream(stream);
   const int ku = rope_units_per_pass(int64_t(Hq + Hkv) * (D / 16) + int64_t(Hkv) * (D / 8));
-#define RRA_ROPE_LAUNCH(DD, NEOX, KU)                                                          \
-  hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX, KU>), rope_grid(T), dim3(kBlock), 0, st,  \
-                     positions, q, q_stride, q_out, q_out_stride, k, k_stride, v, v_stride,    \
-                     cos_sin, slot_mapping, key_cache, value_cache, T, Hq, Hkv)
-#define RRA_ROPE_CASE(DD, NEOX)                                                                 \
-  if (D == DD && is_neox == NEOX) {                                                             \
+#define RRA_ROPE_LAUNCH(DD, NEOX, KU, EL)                                                      \
+  hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX, KU, EL>), rope_grid(T), dim3(kBlock), 0,  \
+                     st, positions, q, q_stride, q_out, q_out_stride, k, k_stride, v,          \
+                     v_stride, cos_sin, slot_mapping, key_cache, value_cache, T, Hq, Hkv)
+#define RRA_ROPE_CASE(DD, NEOX, DT, EL)                                                         \
+  if (D == DD && is_neox == NEOX && dtype == DT) {                                              \
     switch (ku) {                                                                               \
-      case 1: RRA_ROPE_LAUNCH(DD, NEOX, 1); break;                                              \
-      case 2: RRA_ROPE_LAUNCH(DD, NEOX, 2); break;                                              \
-      case 3: RRA_ROPE_LAUNCH(DD, NEOX, 3); break;                                              \
-      default: RRA_ROPE_LAUNCH(DD, NEOX, 4); break;                                             \
+      case 1: RRA_ROPE_LAUNCH(DD, NEOX, 1, EL); break;                                          \
+      case 2: RRA_ROPE_LAUNCH(DD, NEOX, 2, EL); break;                                          \
+      case 3: RRA_ROPE_LAUNCH(DD, NEOX, 3, EL); break;                                          \
+      default: RRA_ROPE_LAUNCH(DD, NEOX, 4, EL); break;                                         \
     }                                                                                           \
     return launch_status();                                                                     \
   }
-  RRA_ROPE_CASE(64, 1)
-  RRA_ROPE_CASE(128, 1)
-  RRA_ROPE_CASE(256, 1)
-  RRA_ROPE_CASE(64, 0)
-  RRA_ROPE_CASE(128, 0)
-  RRA_ROPE_CASE(256, 0)
+  RRA_ROPE_CASE(64, 1, RRA_BF16, ElemBf16)
+  RRA_ROPE_CASE(128, 1, RRA_BF16, ElemBf16)
+  RRA_ROPE_CASE(256, 1, RRA_BF16, ElemBf16)
+  RRA_ROPE_CASE(64, 0, RRA_BF16, ElemBf16)
+  RRA_ROPE_CASE(128, 0, RRA_BF16, ElemBf16)
+  RRA_ROPE_CASE(256, 0, RRA_BF16, ElemBf16)
+  RRA_ROPE_CASE(64, 1, RRA_F16, ElemF16)
+  RRA_ROPE_CASE(128, 1, RRA_F16, ElemF16)
+  RRA_ROPE_CASE(256, 1, RRA_F16, ElemF16)
+  RRA_ROPE_CASE(64, 0, RRA_F16, ElemF16)
+  RRA_ROPE_CASE(128, 0, RRA_F16, ElemF16)
+  RRA_ROPE_CASE(256, 0, RRA_F16, ElemF16)
 #undef RRA_ROPE_CASE
 #undef RRA_ROPE_LAUNCH
   return RRA_ERR_UNSUPPORTED;

@@ -16,6 +16,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16 or 16 fp8
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // 8 fp8
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ---- memory ---------------------------------------------------------------
 // Streaming data is touched exactly once, so loads and stores of activations
@@ -48,6 +49,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
+
+// IEEE binary16 halves of a packed word (exact widening to fp32).
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(f16x2, w)[0]);
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(f16x2, w)[1]);
+}
+
+// Two fp32 -> two fp16, round-to-nearest-even, overflow to infinity.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// The 16-bit element types a kernel can be instantiated for: unpack the two
+// halves of a 32-bit word to fp32 and pack two fp32 values back (RNE).
+struct ElemBf16 {
+  static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+};
+struct ElemF16 {
+  static __device__ __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
+};
 
 // ---- OCP e4m3fn -----------------------------------------------------------
 // gfx950's v_cvt_pk_fp8_f32 converts to OCP e4m3fn with round-to-nearest-even:

@@ -4,6 +4,7 @@ and the acceptance bars.
 Bars: FP8 codes may differ from the oracle by at most one code (adjacent
 values) on at most 1e-4 of all codes; bf16 outputs and fp32 scales within
 rtol 1e-2 (bf16 outputs also atol 1e-5, for values that cancel to near zero);
+fp16 outputs within one fp16 unit of the oracle (plus 2^-20 absolute);
 integer and index work (which slots are written, bit copies) bit-exact."""
 from __future__ import annotations
 
@@ -42,12 +43,23 @@ def dev_bf16(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def dev_f16(a: np.ndarray):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).cuda()
+
+
+def dev_elem(a: np.ndarray, dtype: str):
+    """uint16 bit patterns -> a device tensor of element type dtype ("bf16"/"f16")."""
+    return dev_f16(a) if dtype == "f16" else dev_bf16(a)
+
+
 def dev(a: np.ndarray):
     torch = torch_mod()
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
 def host_bf16(t) -> np.ndarray:
+    """16-bit device tensor (bf16 or fp16) -> its uint16 bit patterns."""
     torch = torch_mod()
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -88,6 +100,32 @@ def assert_bf16(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
     assert ok.all(), (what, np.argwhere(~ok)[:5], g[~ok][:5], r[~ok][:5])
     exact = float(np.mean(gpu == ref)) if gpu.size else 1.0
     print(dict(what=what, values=gpu.size, bit_exact_fraction=exact), flush=True)
+
+
+# fp16 results: the kernels compute in fp32 and round once, the oracle in
+# double; the two may straddle a rounding point (one fp16 unit apart) and, where
+# a rotation cancels, differ by fp32 rounding of the products (absolute 2^-20
+# covers |inputs| up to 16).
+ATOL_F16 = 2.0 ** -20
+
+
+def _f16_ulp(r: np.ndarray) -> np.ndarray:
+    e = np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -14)))
+    return np.exp2(e - 10)
+
+
+def assert_f16(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
+    assert gpu.shape == ref.shape
+    g = gpu.view(np.float16).astype(np.float64)
+    r = ref.view(np.float16).astype(np.float64)
+    ok = np.abs(g - r) <= _f16_ulp(r) + ATOL_F16
+    assert ok.all(), (what, np.argwhere(~ok)[:5], g[~ok][:5], r[~ok][:5])
+    exact = float(np.mean(gpu == ref)) if gpu.size else 1.0
+    print(dict(what=what, values=gpu.size, bit_exact_fraction=exact), flush=True)
+
+
+def assert_elem(gpu: np.ndarray, ref: np.ndarray, what: str, dtype: str) -> None:
+    (assert_f16 if dtype == "f16" else assert_bf16)(gpu, ref, what)
 
 
 def sample_rows(T: int, n: int = 256, seed: int = 0) -> np.ndarray:

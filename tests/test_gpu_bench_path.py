@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import assert_bf16, assert_codes, assert_scales, require_gpu, say
+from gpu_util import assert_bf16, assert_codes, assert_elem, assert_scales, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -100,21 +100,22 @@ def _compact_cache(shape_tail, n):
     return np.zeros((n, 1) + tuple(shape_tail), np.uint16)
 
 
-def test_rope(launchers, rows, oracle):
-    c = workloads.ROPE
-    io = launchers["_io"]["rope_kv_write"]
+@pytest.mark.parametrize("name,c", [("rope_kv_write", workloads.ROPE),
+                                    ("rope_kv_write_f16", workloads.ROPE_F16)])
+def test_rope(launchers, rows, oracle, name, c):
+    io = launchers["_io"][name]
     q, k, v = h16(io["q"], rows), h16(io["k"], rows), h16(io["v"], rows)
     pos, slots = hi(io["positions"], rows), hi(io["slot_mapping"], rows)
-    launch(launchers, "rope_kv_write")
+    launch(launchers, name)
     n = len(rows)
     kc0 = _compact_cache((c.Hkv, c.D), n)
     ref_q, ref_kc, ref_vc = oracle.rope_kv_write(pos, q, k, v, c.theta, c.max_pos, np.arange(n),
-                                                 kc0, kc0, c.Hq, c.Hkv, c.D)
-    assert_bf16(h16(io["q"], rows), ref_q, "bench-path rope q")
+                                                 kc0, kc0, c.Hq, c.Hkv, c.D, dtype=c.dtype)
+    assert_elem(h16(io["q"], rows), ref_q, f"bench-path {name} q", c.dtype)
     nb = c.num_blocks * c.block_size
     gk = h16(io["key_cache"]).reshape(nb, c.Hkv, c.D)[slots]
     gv = h16(io["value_cache"]).reshape(nb, c.Hkv, c.D)[slots]
-    assert_bf16(gk, ref_kc.reshape(n, c.Hkv, c.D), "bench-path rope key cache")
+    assert_elem(gk, ref_kc.reshape(n, c.Hkv, c.D), f"bench-path {name} key cache", c.dtype)
     assert np.array_equal(gv, ref_vc.reshape(n, c.Hkv, c.D))
 
 

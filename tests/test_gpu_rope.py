@@ -5,7 +5,8 @@ Covers the Llama-3-8B attention workload (32 q / 8 kv heads of 128, theta
 drawn without repetition from a seeded permutation; T in {16, 2048, 8192,
 16384}), padding tokens (slot -1), in-place and separate q_out, q/k/v as
 views of one fused qkv projection, other head sizes and block sizes, ragged
-head counts and T = 0.
+head counts and T = 0, each also with fp16 elements (the same shapes in IEEE
+binary16; bar: one fp16 unit) and in the GPT-J pairing.
 
 Bars: rotated q and k within rtol 1e-2 (atol 1e-5) of the oracle; the set of
 written cache slots, their placement and the copied v bit-exact; every slot
@@ -18,7 +19,8 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import assert_bf16, dev, dev_bf16, host_bf16, host_f32, require_gpu, sample_rows, say
+from gpu_util import (assert_bf16, assert_elem, dev, dev_bf16, dev_elem, host_bf16, host_f32,
+                      require_gpu, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +38,10 @@ def run(rra, oracle, T, cfg=workloads.ROPE, *, pad_every=0, inplace=True, fused_
     import torch
 
     say(f"[rope] T={T} Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} blocks={cfg.num_blocks}x"
-        f"{cfg.block_size} pad_every={pad_every} inplace={inplace} fused_qkv={fused_qkv}")
+        f"{cfg.block_size} pad_every={pad_every} inplace={inplace} fused_qkv={fused_qkv} "
+        f"neox={cfg.is_neox} dtype={cfg.dtype}")
+    dt = cfg.dtype
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
     d = workloads.rope_inputs(T, cfg)
     slots = d["slot_mapping"].copy()
     if pad_every:
@@ -45,17 +50,17 @@ def run(rra, oracle, T, cfg=workloads.ROPE, *, pad_every=0, inplace=True, fused_
     if fused_qkv:
         qkv = np.concatenate([d["q"].reshape(T, -1), d["k"].reshape(T, -1),
                               d["v"].reshape(T, -1)], axis=1)
-        qkv_dev = dev_bf16(qkv)
+        qkv_dev = dev_elem(qkv, dt)
         q = qkv_dev[:, :Hq * D]
         k = qkv_dev[:, Hq * D:(Hq + Hkv) * D]
         v = qkv_dev[:, (Hq + Hkv) * D:]
     else:
-        q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
-    q_out = None if inplace else torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
-    kc, vc = dev_bf16(d["key_cache"]), dev_bf16(d["value_cache"])
+        q, k, v = dev_elem(d["q"], dt), dev_elem(d["k"], dt), dev_elem(d["v"], dt)
+    q_out = None if inplace else torch.empty((T, Hq, D), dtype=tdt, device="cuda")
+    kc, vc = dev_elem(d["key_cache"], dt), dev_elem(d["value_cache"], dt)
     cos_sin = rra.rope_cos_sin_cache(cfg.max_pos, cfg.rot_dim, cfg.theta)
     res = rra.rope_kv_write(dev(d["positions"]), q, k, v, cos_sin, dev(slots), kc, vc,
-                            q_out=q_out)
+                            q_out=q_out, is_neox=cfg.is_neox)
     torch.cuda.synchronize()
     if inplace:
         assert res.data_ptr() == q.data_ptr()
@@ -81,13 +86,14 @@ def run(rra, oracle, T, cfg=workloads.ROPE, *, pad_every=0, inplace=True, fused_
         return
     ref_q, ref_kc, ref_vc = oracle.rope_kv_write(
         d["positions"][rows], d["q"][rows], d["k"][rows], d["v"][rows], cfg.theta, cfg.max_pos,
-        slots[rows], d["key_cache"], d["value_cache"], Hq, Hkv, D)
-    assert_bf16(gq[rows], ref_q, f"q_out T={T}")
+        slots[rows], d["key_cache"], d["value_cache"], Hq, Hkv, D, is_neox=cfg.is_neox,
+        dtype=dt)
+    assert_elem(gq[rows], ref_q, f"q_out T={T}", dt)
     rs = slots[rows]
     rs = rs[rs >= 0]
     ref_kc = ref_kc.reshape(n_slots, Hkv, D)
     ref_vc = ref_vc.reshape(n_slots, Hkv, D)
-    assert_bf16(gk[rs], ref_kc[rs], f"key cache T={T}")
+    assert_elem(gk[rs], ref_kc[rs], f"key cache T={T}", dt)
     assert np.array_equal(gv[rs], ref_vc[rs])
 
 
@@ -163,3 +169,43 @@ def test_empty(rra):
     out = rra.rope_kv_write(i, e(0, c.Hq, c.D), e(0, c.Hkv, c.D), e(0, c.Hkv, c.D), cs, i, kc,
                             kc.clone())
     assert out.shape == (0, c.Hq, c.D)
+
+
+F16 = dataclasses.replace(workloads.ROPE, dtype="f16")
+
+
+@pytest.mark.parametrize("T", workloads.ROPE_F16.Ts)
+def test_f16_attention_workload(rra, oracle, T):
+    run(rra, oracle, T, workloads.ROPE_F16)
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_f16_padding_separate_out_and_gptj(rra, oracle, is_neox):
+    run(rra, oracle, 200, dataclasses.replace(F16, is_neox=is_neox), pad_every=4, inplace=False)
+
+
+def test_f16_fused_qkv_views(rra, oracle):
+    run(rra, oracle, 65, F16, fused_qkv=True)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(8, 1, 64, 16), (16, 4, 256, 8), (33, 3, 64, 32)])
+def test_f16_head_and_block_shapes(rra, oracle, Hq, Hkv, D, bs):
+    cfg = dataclasses.replace(F16, Hq=Hq, Hkv=Hkv, D=D, rot_dim=D, block_size=bs, **SMALL)
+    run(rra, oracle, 45, cfg, pad_every=7)
+
+
+def test_f16_empty_and_mixed_types_rejected(rra):
+    import torch
+
+    say("[rope] fp16 T=0 and mixed element types")
+    c = dataclasses.replace(F16, **SMALL)
+    e = lambda *s, dt=torch.float16: torch.empty(s, dtype=dt, device="cuda")
+    i = torch.empty(0, dtype=torch.int64, device="cuda")
+    kc = e(c.num_blocks, c.block_size, c.Hkv, c.D)
+    cs = rra.rope_cos_sin_cache(c.max_pos, c.rot_dim, c.theta)
+    out = rra.rope_kv_write(i, e(0, c.Hq, c.D), e(0, c.Hkv, c.D), e(0, c.Hkv, c.D), cs, i, kc,
+                            kc.clone())
+    assert out.shape == (0, c.Hq, c.D) and out.dtype == torch.float16
+    with pytest.raises(TypeError):  # bf16 k with fp16 q: refused on the host
+        rra.rope_kv_write(i, e(0, c.Hq, c.D), e(0, c.Hkv, c.D, dt=torch.bfloat16),
+                          e(0, c.Hkv, c.D), cs, i, kc, kc.clone())

@@ -53,7 +53,7 @@ def test_library_exports_every_declared_function(rra):
 
 
 def test_version_and_status_strings(rra):
-    assert rra.abi_version() == 1
+    assert rra.abi_version() == rra.ABI_VERSION == 2
     for s in (OK, ENULL, ESHAPE, EALIGN, EUNSUP, -5):
         assert rra.status_string(s) and rra.status_string(s) != "unknown status"
     assert rra.status_string(-99) == "unknown status"
@@ -114,12 +114,13 @@ def test_rope_validation(rra):
 
     def f(**k):
         a = dict(pos=A, q=A, qs=4096, qo=A, qos=4096, k=A, ks=1024, v=A, vs=1024, cs=A, mp=8192,
-                 sm=A, kc=A, vc=A, T=4, Hq=32, Hkv=8, D=128, rd=128, bs=16, nb=4096, neox=1)
+                 sm=A, kc=A, vc=A, T=4, Hq=32, Hkv=8, D=128, rd=128, bs=16, nb=4096, neox=1,
+                 dt=rra.BF16)
         a.update(k)
         return L.rope_kv_write(a["pos"], a["q"], a["qs"], a["qo"], a["qos"], a["k"], a["ks"],
                                a["v"], a["vs"], a["cs"], a["mp"], a["sm"], a["kc"], a["vc"],
                                a["T"], a["Hq"], a["Hkv"], a["D"], a["rd"], a["bs"], a["nb"],
-                               a["neox"], None)
+                               a["neox"], a["dt"], None)
 
     assert f(T=0) == OK
     assert f(sm=None) == ENULL
@@ -127,6 +128,9 @@ def test_rope_validation(rra):
     assert f(D=96, qs=3072, qos=3072, ks=768, vs=768, rd=96) == EUNSUP
     assert f(rd=64) == EUNSUP
     assert f(neox=2) == EUNSUP
+    assert f(dt=2) == EUNSUP and f(dt=-1) == EUNSUP  # only bf16 and fp16
+    assert f(dt=rra.F16, T=0) == OK
+    assert f(dt=rra.F16, q=A + 2) == EALIGN  # fp16 keeps the 16-byte rules
     assert f(pos=None, q=None, qo=None, k=None, v=None, sm=None, T=0) == OK
     assert f(kc=None, T=0) == ENULL
     assert f(cs=None, T=0) == ENULL

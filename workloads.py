@@ -61,6 +61,7 @@ class RopeCfg:
     block_size: int = 16
     is_neox: bool = True
     Ts: tuple = ()
+    dtype: str = "bf16"  # element type of q, k, v and the caches: "bf16" or "f16"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -83,6 +84,7 @@ NORM_STATIC = NormCfg("norm_static", H=1024, eps=1e-6, quant="static", static_sc
 NORM_TOKEN = NormCfg("norm_token", H=4096, eps=1e-5, quant="per_token", Ts=(1, 32, 512, 8192))
 SILU = SiluCfg("silu", I=14336, quant="per_group", group_size=128, Ts=(1, 64, 1024, 8192))
 ROPE = RopeCfg("rope", Ts=(16, 2048, 8192, 16384))
+ROPE_F16 = RopeCfg("rope_f16", Ts=(16, 2048, 8192), dtype="f16")
 MLA = MlaCfg("mla", Ts=(1, 1024, 8192, 16384))
 
 HEADLINE_T = 8192
@@ -156,6 +158,15 @@ def bf16_normal(rng: np.random.Generator, shape, mean: float = 0.0, std: float =
     return to_bf16_bits(a)
 
 
+def f16_normal(rng: np.random.Generator, shape):
+    """N(0, 1) draws as IEEE fp16 bit patterns (numpy's round-to-nearest-even)."""
+    return rng.standard_normal(shape, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def elem_normal(dtype: str, rng: np.random.Generator, shape):
+    return f16_normal(rng, shape) if dtype == "f16" else bf16_normal(rng, shape)
+
+
 def norm_inputs(T: int, H: int, salt: int = 0, tag: str = "norm_token"):
     """x, residual ~ N(0,1) [T,H]; weight ~ N(1, 0.1) [H]."""
     return dict(
@@ -171,16 +182,17 @@ def silu_inputs(T: int, I: int, salt: int = 0):
 
 
 def rope_inputs(T: int, cfg: RopeCfg = ROPE, salt: int = 0, with_cache: bool = True):
-    """q [T,Hq,D], k, v [T,Hkv,D] ~ N(0,1); positions uniform in [0, max_pos);
-    slot_mapping = the first T entries of a seeded permutation of all cache slots
-    (distinct); caches filled with a seeded random bf16 sentinel pattern."""
+    """q [T,Hq,D], k, v [T,Hkv,D] ~ N(0,1) as cfg.dtype bit patterns; positions
+    uniform in [0, max_pos); slot_mapping = the first T entries of a seeded
+    permutation of all cache slots (distinct); caches filled with a seeded
+    random sentinel pattern (finite in bf16 and in fp16)."""
     n_slots = cfg.num_blocks * cfg.block_size
     if T > n_slots:
         raise ValueError("more tokens than cache slots")
     d = dict(
-        q=bf16_normal(_rng("rope", T, 0, salt), (T, cfg.Hq, cfg.D)),
-        k=bf16_normal(_rng("rope", T, 1, salt), (T, cfg.Hkv, cfg.D)),
-        v=bf16_normal(_rng("rope", T, 2, salt), (T, cfg.Hkv, cfg.D)),
+        q=elem_normal(cfg.dtype, _rng("rope", T, 0, salt), (T, cfg.Hq, cfg.D)),
+        k=elem_normal(cfg.dtype, _rng("rope", T, 1, salt), (T, cfg.Hkv, cfg.D)),
+        v=elem_normal(cfg.dtype, _rng("rope", T, 2, salt), (T, cfg.Hkv, cfg.D)),
         positions=_rng("rope", T, 3, salt).integers(0, cfg.max_pos, T, dtype=np.int64),
         slot_mapping=_rng("rope", T, 4, salt).permutation(n_slots)[:T].astype(np.int64),
     )
@@ -192,7 +204,8 @@ def rope_inputs(T: int, cfg: RopeCfg = ROPE, salt: int = 0, with_cache: bool = T
 
 
 def sentinel_cache(shape, index: int, salt: int = 0) -> np.ndarray:
-    """Random bf16 bit patterns (finite: exponent field below all-ones)."""
+    """Random 16-bit patterns with bit 14 clear, so the exponent field is below
+    all-ones and the value finite whether read as bf16 or as fp16."""
     r = _rng("rope", 0, index, salt).integers(0, 1 << 16, size=shape, dtype=np.uint16)
     return (r & np.uint16(0xBFFF)).astype(np.uint16)  # clear the top exponent bit
 
@@ -266,7 +279,7 @@ def _gen(device, tag: str, T: int, salt: int = 0):
     return g
 
 
-def _randn(g, shape, device, mean=0.0, std=1.0):
+def _randn(g, shape, device, mean=0.0, std=1.0, dtype="bf16"):
     import torch
 
     a = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
@@ -274,7 +287,7 @@ def _randn(g, shape, device, mean=0.0, std=1.0):
         a.mul_(std)
     if mean != 0.0:
         a.add_(mean)
-    return a.to(torch.bfloat16)
+    return a.to(torch.float16 if dtype == "f16" else torch.bfloat16)
 
 
 def device_norm_inputs(T: int, H: int, device="cuda", salt: int = 0, tag: str = "norm_token"):
@@ -297,17 +310,17 @@ def device_rope_inputs(T: int, cfg: RopeCfg = ROPE, device="cuda", salt: int = 0
     if T > n_slots:
         raise ValueError("more tokens than cache slots")
     d = dict(
-        q=_randn(g, (T, cfg.Hq, cfg.D), device),
-        k=_randn(g, (T, cfg.Hkv, cfg.D), device),
-        v=_randn(g, (T, cfg.Hkv, cfg.D), device),
+        q=_randn(g, (T, cfg.Hq, cfg.D), device, dtype=cfg.dtype),
+        k=_randn(g, (T, cfg.Hkv, cfg.D), device, dtype=cfg.dtype),
+        v=_randn(g, (T, cfg.Hkv, cfg.D), device, dtype=cfg.dtype),
         positions=torch.randint(0, cfg.max_pos, (T,), generator=g, device=device,
                                 dtype=torch.int64),
         slot_mapping=torch.randperm(n_slots, generator=g, device=device)[:T].contiguous(),
     )
     if with_cache:
         cache_shape = (cfg.num_blocks, cfg.block_size, cfg.Hkv, cfg.D)
-        d["key_cache"] = _randn(g, cache_shape, device)
-        d["value_cache"] = _randn(g, cache_shape, device)
+        d["key_cache"] = _randn(g, cache_shape, device, dtype=cfg.dtype)
+        d["value_cache"] = _randn(g, cache_shape, device, dtype=cfg.dtype)
     return d
 
 
