@@ -67,12 +67,14 @@ KERNELS = tuple(BYTES_PER_TOKEN)
 # The next rows, measured beside the step (not part of it): QK norm + RoPE + KV
 # write at the Qwen3-8B attention shape, residual add + RMSNorm + padding at
 # GPT-OSS width, MLA q_pe/k_pe RoPE + [kv_c | k_pe] cache write at DeepSeek-V3,
-# and the RoPE + KV write of the step with fp16 instead of bf16 elements.
+# and the RoPE + KV write of the step and the padding op with fp16 instead of
+# bf16 elements.
 QK_HQ, QK_HKV, QK_D = 32, 8, 128
 PAD_H, PAD_HP = 2880, 3072
 MR_HQ, MR_NOPE, MR_ROPE, MR_LORA = 128, 128, 64, 512
 BYTES_PER_TOKEN.update({
     "rope_kv_write_f16": BYTES_PER_TOKEN["rope_kv_write"],
+    "fused_add_rmsnorm_pad_f16": 2 * 2 * PAD_H + 2 * PAD_H + 2 * PAD_HP,
     "qk_norm_rope_kv_write": 2 * (QK_HQ + 2 * QK_HKV) * QK_D + 2 * QK_HQ * QK_D
     + 2 * 2 * QK_HKV * QK_D + 16,
     "fused_add_rmsnorm_pad": 2 * 2 * PAD_H + 2 * PAD_H + 2 * PAD_HP,
@@ -81,12 +83,13 @@ BYTES_PER_TOKEN.update({
 })
 BYTES_PER_LAUNCH.update({
     "rope_kv_write_f16": 0,
+    "fused_add_rmsnorm_pad_f16": 2 * PAD_H,
     "qk_norm_rope_kv_write": 2 * 2 * QK_D,
     "fused_add_rmsnorm_pad": 2 * PAD_H,
     "mla_rope_kv_write": 0,
 })
 NEXT_KERNELS = ("qk_norm_rope_kv_write", "fused_add_rmsnorm_pad", "mla_rope_kv_write",
-                "rope_kv_write_f16")
+                "rope_kv_write_f16", "fused_add_rmsnorm_pad_f16")
 
 
 def algo_bytes(name: str, T: int) -> int:
@@ -105,11 +108,12 @@ KERNEL_SYMBOL = {
     "fused_add_rmsnorm_pad": "add_rmsnorm_pad_kernel",
     "mla_rope_kv_write": "mla_rope_kv_kernel",
     "rope_kv_write_f16": "rope_kv_write_kernel",
+    "fused_add_rmsnorm_pad_f16": "add_rmsnorm_pad_kernel",
 }
 # Kernels that share a symbol with another and differ in a template argument:
 # the argument's text in the demangled name.  Names of the plain kernel must not
 # contain it.
-KERNEL_TAG = {"rope_kv_write_f16": "ElemF16"}
+KERNEL_TAG = {"rope_kv_write_f16": "ElemF16", "fused_add_rmsnorm_pad_f16": "ElemF16"}
 KERNEL_SOURCES = {
     "fused_add_rmsnorm_quant": ("norm_quant.hip",),
     "dual_rmsnorm_quant": ("norm_quant.hip",),
@@ -119,6 +123,7 @@ KERNEL_SOURCES = {
     "fused_add_rmsnorm_pad": ("norm_quant.hip",),
     "mla_rope_kv_write": ("rope_kv.hip",),
     "rope_kv_write_f16": ("rope_kv.hip",),
+    "fused_add_rmsnorm_pad_f16": ("norm_quant.hip",),
 }
 COMMON_SOURCES = ("rra_device.hpp", "rra_host.hpp")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_kernels_T8192_hbm_traffic.md")
@@ -276,13 +281,15 @@ def make_launchers(T: int, salt: int = 0, shared=None, only=KERNELS):
         L["qk_norm_rope_kv_write"] = qkn
         io["qk_norm_rope_kv_write"] = dict(d, key_cache=kc, value_cache=vc)
 
-    if "fused_add_rmsnorm_pad" in only:
-        cfg = workloads.PAD
+    for name, cfg in (("fused_add_rmsnorm_pad", workloads.PAD),
+                      ("fused_add_rmsnorm_pad_f16", workloads.PAD_F16)):
+        if name not in only:
+            continue
         d = workloads.device_pad_inputs(T, cfg, dev, salt)
-        out = torch.empty((T, cfg.H_pad), dtype=torch.bfloat16, device=dev)
-        L["fused_add_rmsnorm_pad"] = lambda d=d, out=out, cfg=cfg: rra.fused_add_rmsnorm_pad(
+        out = torch.empty((T, cfg.H_pad), dtype=d["x"].dtype, device=dev)
+        L[name] = lambda d=d, out=out, cfg=cfg: rra.fused_add_rmsnorm_pad(
             d["x"], d["residual"], d["weight"], cfg.eps, cfg.H_pad, out)
-        io["fused_add_rmsnorm_pad"] = dict(d, out=out)
+        io[name] = dict(d, out=out)
 
     if "mla_rope_kv_write" in only:
         cfg = workloads.MLA_ROPE

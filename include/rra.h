@@ -241,18 +241,21 @@ int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, int64_t qkv_s
  * then the hidden dimension padded to the width the next GEMM expects
  * (GPT-OSS: 2880), as one op.
  *
- *   z = bf16(x + residual); residual <- z (in place; z = x if residual NULL)
- *   out[t, 0:H]     = bf16(z / sqrt(mean(z^2) + eps) * weight)
+ *   z = E(x + residual); residual <- z (in place; z = x if residual NULL)
+ *   out[t, 0:H]     = E(z / sqrt(mean(z^2) + eps) * weight)
  *   out[t, H:H_pad] = +0
+ * where E() rounds to the element type dtype (RRA_BF16 or RRA_F16, which the
+ * section's support matrix lists for this fusion on ROCm), nearest even.
  *
- * x [T, H], residual [T, H] (or NULL), out [T, H_pad] bf16 with row strides;
- * weight [H] bf16.  H_pad is the caller's padded width.
- * Limits: H % 8 == 0, H <= 8192; H_pad % 8 == 0, H_pad >= H.
+ * x [T, H], residual [T, H] (or NULL), out [T, H_pad] dtype with row strides;
+ * weight [H] dtype.  H_pad is the caller's padded width.
+ * Limits: H % 8 == 0, H <= 8192; H_pad % 8 == 0, H_pad >= H; dtype RRA_BF16
+ * or RRA_F16 (else RRA_ERR_UNSUPPORTED).
  */
 int fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residual,
                           int64_t residual_stride, const uint16_t* weight, float eps,
                           uint16_t* out, int64_t out_stride, int64_t T, int64_t H, int64_t H_pad,
-                          void* stream);
+                          int dtype, void* stream);
 
 /*
  * MLA RoPE + cache concat.

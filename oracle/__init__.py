@@ -111,7 +111,7 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_qk_norm_rope_kv_write.argtypes = qkn
     L.orc_unfused_qk_norm_rope_kv_write.argtypes = qkn
     L.orc_fused_add_rmsnorm_pad.argtypes = [_p, _i64, _p, _i64, _p, _f32, _p, _i64, _i64, _i64,
-                                            _i64]
+                                            _i64, _i32]
     L.orc_mla_rope_kv_write.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _i64, _f64, _i64, _p,
                                         _p, _i64, _i32, _i32, _i32, _i32, _i64, _i32]
     for name in ("orc_qk_norm_rope_kv_write", "orc_unfused_qk_norm_rope_kv_write",
@@ -418,8 +418,9 @@ def unfused_qk_norm_rope_kv_write(positions, qkv, q_weight, k_weight, eps, theta
                 theta, max_pos, Hq, Hkv, D, **kw)
 
 
-def fused_add_rmsnorm_pad(x, residual, weight, eps, H_pad):
-    """Returns (out [T, H_pad] bf16 bits, updated residual or None)."""
+def fused_add_rmsnorm_pad(x, residual, weight, eps, H_pad, dtype="bf16"):
+    """Returns (out [T, H_pad] bit patterns of dtype ("bf16" or "f16"), updated
+    residual or None)."""
     x, xs = _rows(x, np.uint16)
     T, H = x.shape
     res, rs = (None, 0)
@@ -428,7 +429,8 @@ def fused_add_rmsnorm_pad(x, residual, weight, eps, H_pad):
     out = np.full((T, H_pad), 0xFFFF, np.uint16)  # every column must be written
     rc = lib().orc_fused_add_rmsnorm_pad(_ptr(x), xs, _ptr(res), rs,
                                          _ptr(np.ascontiguousarray(weight, np.uint16)),
-                                         float(eps), _ptr(out), H_pad, T, H, H_pad)
+                                         float(eps), _ptr(out), H_pad, T, H, H_pad,
+                                         _dtype(dtype))
     _check("orc_fused_add_rmsnorm_pad", rc)
     return out, res
 

@@ -110,7 +110,7 @@ double orc_f16_decode(uint16_t h) {
   return s ? -mag : mag;
 }
 
-/* The 16-bit element types the RoPE path reads and writes. */
+/* The 16-bit element types of the RoPE + KV-cache and padding ops. */
 static double elem_decode(uint16_t h, int dtype) {
   return dtype == ORC_DT_F16 ? orc_f16_decode(h) : orc_bf16_decode(h);
 }
@@ -264,11 +264,12 @@ static int quant_args_ok(int mode, int group_size, int64_t H, int allow_none) {
  * the reading is the usual one: y_j = z_j / sqrt(mean_j(z_j^2) + eps) * w_j,
  * with eps inside the root and a multiplicative weight.
  * [FUSION] sections "RMSNorm + Quantization" and "MLA Dual RMSNorm". */
-static void rms_norm_row(const double* z, const uint16_t* w, float eps, int64_t H, double* y) {
+static void rms_norm_row(const double* z, const uint16_t* w, float eps, int64_t H, double* y,
+                         int dtype) {
   double ss = 0.0;
   for (int64_t j = 0; j < H; ++j) ss += z[j] * z[j];
   const double rho = 1.0 / sqrt(ss / (double)H + (double)eps);
-  for (int64_t j = 0; j < H; ++j) y[j] = z[j] * rho * orc_bf16_decode(w[j]);
+  for (int64_t j = 0; j < H; ++j) y[j] = z[j] * rho * elem_decode(w[j], dtype);
 }
 
 /* One scale from an amax: s = amax / 448 rounded to fp32 (448 is E4M3's
@@ -353,7 +354,7 @@ int orc_fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint16_t* r
         z[j] = xv;
       }
     }
-    rms_norm_row(z, weight, eps, H, y);
+    rms_norm_row(z, weight, eps, H, y, ORC_DT_BF16);
     quant_row(y, H, quant_mode, group_size, static_scale, out + t * out_stride,
               scales_row_ptr(scales, quant_mode, group_size, H, t));
     free(z);
@@ -388,7 +389,7 @@ int orc_unfused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint16_t*
       z[j] = v;
     }
     /* step 2: rms_norm materializes a bf16 tensor */
-    rms_norm_row(z, weight, eps, H, y);
+    rms_norm_row(z, weight, eps, H, y, ORC_DT_BF16);
     for (int64_t j = 0; j < H; ++j) y[j] = orc_bf16_decode(orc_bf16_encode(y[j]));
     /* step 3: quant_fp8 of that tensor */
     quant_row(y, H, quant_mode, group_size, static_scale, out + t * out_stride,
@@ -636,7 +637,7 @@ static void norm_emit_row(const uint16_t* src, const uint16_t* w, float eps, int
   double* z = (double*)calloc((size_t)H, sizeof(double));
   double* y = (double*)calloc((size_t)H, sizeof(double));
   for (int64_t j = 0; j < H; ++j) z[j] = orc_bf16_decode(src[j]);
-  rms_norm_row(z, w, eps, H, y);
+  rms_norm_row(z, w, eps, H, y, ORC_DT_BF16);
   if (mode == ORC_Q_NONE) {
     uint16_t* o = (uint16_t*)dst;
     for (int64_t j = 0; j < H; ++j) o[j] = orc_bf16_encode(y[j]);
@@ -734,7 +735,7 @@ static void norm_rope_head(const uint16_t* in, const uint16_t* w, float eps, int
   double* z = (double*)calloc((size_t)D, sizeof(double));
   double* y = (double*)calloc((size_t)D, sizeof(double));
   for (int d = 0; d < D; ++d) z[d] = orc_bf16_decode(in[d]);
-  rms_norm_row(z, w, eps, D, y);
+  rms_norm_row(z, w, eps, D, y, ORC_DT_BF16);
   if (round_between)
     for (int d = 0; d < D; ++d) y[d] = orc_bf16_decode(orc_bf16_encode(y[d]));
   rotate_head_f64(y, out, c, s, D, rot_dim, is_neox);
@@ -834,31 +835,34 @@ int orc_unfused_qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv,
 /* Residual add + RMSNorm + padding.
  * [FUSION] section "RMSNorm + Padding (fuse_act_padding)": residual add and
  * RMSNorm, then padding of the hidden dimension to the width the next GEMM
- * wants, as one op (GPT-OSS, hidden 2880).  Readings: the normalized row is
- * written in bf16 to out[:, 0:H] and the pad columns out[:, H:H_pad] are +0;
+ * wants, as one op (GPT-OSS, hidden 2880).  x, residual, weight and out share
+ * one element type, bf16 or fp16 (dtype; the section's support matrix lists
+ * FP16/BF16 on ROCm).  Readings: the normalized row is written in that type to
+ * out[:, 0:H] and the pad columns out[:, H:H_pad] are +0;
  * the residual is updated in place as in "RMSNorm + Quantization"; H_pad is
  * the caller's choice (the pages do not give the multiple). */
 int orc_fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residual,
                               int64_t res_stride, const uint16_t* weight, float eps,
                               uint16_t* out, int64_t out_stride, int64_t T, int64_t H,
-                              int64_t H_pad) {
+                              int64_t H_pad, int dtype) {
   if (T < 0 || H <= 0 || H_pad < H || out_stride < H_pad) return ORC_EARG;
+  if (dtype != ORC_DT_BF16 && dtype != ORC_DT_F16) return ORC_EARG;
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
     double* z = (double*)malloc((size_t)H * sizeof(double));
     double* y = (double*)malloc((size_t)H * sizeof(double));
     const uint16_t* xr = x + t * x_stride;
-    for (int64_t j = 0; j < H; ++j) z[j] = orc_bf16_decode(xr[j]);
+    for (int64_t j = 0; j < H; ++j) z[j] = elem_decode(xr[j], dtype);
     if (residual) {
       uint16_t* rr = residual + t * res_stride;
       for (int64_t j = 0; j < H; ++j) {
-        rr[j] = orc_bf16_encode(z[j] + orc_bf16_decode(rr[j]));
-        z[j] = orc_bf16_decode(rr[j]);
+        rr[j] = elem_encode(z[j] + elem_decode(rr[j], dtype), dtype);
+        z[j] = elem_decode(rr[j], dtype);
       }
     }
-    rms_norm_row(z, weight, eps, H, y);
+    rms_norm_row(z, weight, eps, H, y, dtype);
     uint16_t* o = out + t * out_stride;
-    for (int64_t j = 0; j < H; ++j) o[j] = orc_bf16_encode(y[j]);
+    for (int64_t j = 0; j < H; ++j) o[j] = elem_encode(y[j], dtype);
     for (int64_t j = H; j < H_pad; ++j) o[j] = 0;
     free(z);
     free(y);

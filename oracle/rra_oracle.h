@@ -151,7 +151,7 @@ int orc_unfused_qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv,
 int orc_fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residual,
                               int64_t res_stride, const uint16_t* weight, float eps,
                               uint16_t* out, int64_t out_stride, int64_t T, int64_t H,
-                              int64_t H_pad);
+                              int64_t H_pad, int dtype);
 
 /* q_pe: Hq heads of rope_dim at head stride q_head_stride inside rows of
  * q_stride, rotated in place; kv_cache: [num_blocks, block_size,

@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
                                             _i32, _i64, _i32, _i32, _i32, _i32, _i32, _i64,
                                             _i32, _p]
         L.fused_add_rmsnorm_pad.argtypes = [_p, _i64, _p, _i64, _p, _f32, _p, _i64, _i64, _i64,
-                                            _i64, _p]
+                                            _i64, _i32, _p]
         L.mla_rope_kv_write.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p,
                                         _i64, _i32, _i32, _i32, _i32, _i64, _i32, _p]
         L.rra_e4m3fn_encode.argtypes = [_p, _p, _i64, _p]
@@ -107,10 +107,10 @@ def _need_cuda(name: str, t: torch.Tensor, dtypes) -> None:
         raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
 
 
-def _vector(name: str, t: torch.Tensor, n: int) -> None:
-    _need_cuda(name, t, (torch.bfloat16,))
+def _vector(name: str, t: torch.Tensor, n: int, dtypes=(torch.bfloat16,)) -> None:
+    _need_cuda(name, t, dtypes)
     if t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous [{n}] bf16 tensor")
+        raise ValueError(f"{name} must be a contiguous [{n}] tensor")
 
 
 def _rows(name: str, t: torch.Tensor, dtypes, width: int | None = None) -> int:
@@ -315,18 +315,22 @@ def qk_norm_rope_kv_write(positions, qkv, q_weight, k_weight, eps, cos_sin, Hq, 
 
 
 def fused_add_rmsnorm_pad(x, residual, weight, eps, H_pad, out=None):
-    """Residual add + RMSNorm, written as bf16 into out[:, :H] with out[:, H:H_pad]
-    = 0 (residual updated in place).  Returns out [T, H_pad] bf16."""
+    """Residual add + RMSNorm, written into out[:, :H] with out[:, H:H_pad] = 0
+    (residual updated in place).  x, residual, weight and out share one element
+    type, bf16 or fp16.  Returns out [T, H_pad]."""
     T, H = x.shape
-    xs = _rows("x", x, _BF16)
-    rs = _rows("residual", residual, _BF16, H) if residual is not None else 0
-    _vector("weight", weight, H)
+    _need_cuda("x", x, tuple(_ELEM))
+    elem = (x.dtype,)
+    xs = _rows("x", x, elem)
+    rs = _rows("residual", residual, elem, H) if residual is not None else 0
+    _vector("weight", weight, H, elem)
     if out is None:
-        out = torch.empty((T, H_pad), dtype=torch.bfloat16, device=x.device)
-    os_ = _rows("out", out, _BF16, H_pad)
+        out = torch.empty((T, H_pad), dtype=x.dtype, device=x.device)
+    os_ = _rows("out", out, elem, H_pad)
     with torch.cuda.device(x.device):
         st = lib().fused_add_rmsnorm_pad(_ptr(x), xs, _ptr(residual), rs, _ptr(weight),
-                                         float(eps), _ptr(out), os_, T, H, H_pad, _stream(x))
+                                         float(eps), _ptr(out), os_, T, H, H_pad,
+                                         _ELEM[x.dtype], _stream(x))
     _check("fused_add_rmsnorm_pad", st)
     return out
 

@@ -63,8 +63,9 @@ struct RowT {
 // One pass over this lane's vectors: t = z * w, the sum of z^2 in double
 // (each z widened to double and squared by an fma: the sum keeps enough bits
 // that the fp32 rounding of a scale derived from it is the one the plain
-// definition gives) and, when wanted, max |t|.
-template <int NV>
+// definition gives) and, when wanted, max |t|.  E is the element type of z and
+// w; t is exact in fp32 for bf16 (8 x 8 significand bits) and fp16 (11 x 11).
+template <int NV, typename E = ElemBf16>
 __device__ __forceinline__ void row_prepare(const RowVecs<NV>& z, const RowVecs<NV>& w,
                                             bool want_max, RowT<NV>& t, double& ss, float& m) {
   ss = 0.0;
@@ -73,12 +74,12 @@ __device__ __forceinline__ void row_prepare(const RowVecs<NV>& z, const RowVecs<
   for (int i = 0; i < NV; ++i) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float a = bf16_lo(z.v[i][k]), b = bf16_hi(z.v[i][k]);
+      const float a = E::lo(z.v[i][k]), b = E::hi(z.v[i][k]);
       const double ad = static_cast<double>(a), bd = static_cast<double>(b);
       ss = fma(ad, ad, ss);
       ss = fma(bd, bd, ss);
-      t.t[i][2 * k] = a * bf16_lo(w.v[i][k]);
-      t.t[i][2 * k + 1] = b * bf16_hi(w.v[i][k]);
+      t.t[i][2 * k] = a * E::lo(w.v[i][k]);
+      t.t[i][2 * k + 1] = b * E::hi(w.v[i][k]);
     }
     if (want_max) {
 #pragma unroll
@@ -113,13 +114,14 @@ __device__ __forceinline__ void row_reduce(double& ss, float& m, double* lds_ss,
 
 // The row's output from its statistics:
 //   y = t * rho,  rho = 1/sqrt(ss / H + eps)
-// mode NONE writes bf16(y) to out (uint16_t*); the quantizing modes write
+// mode NONE writes y rounded to the element type E to out (uint16_t*); the
+// quantizing modes (E = bf16 inputs only) write
 // e4m3fn(y / s) to out (uint8_t*) and s to scale_row (row lane 0 for a
 // per-token scale, the first lane of each group for per-group scales).
 // Because rho > 0 is one number per row, max|y| = max|t| * rho, so the amax
 // needs no second pass over y, and the codes are e4m3fn(t * rho / s) (quant8
 // rounds them as the exact quotient would).
-template <int NV>
+template <int NV, typename E = ElemBf16>
 __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float m_row,
                                              float eps, int H, int nvec, int rl, int stride,
                                              int mode, int group, float static_scale,
@@ -134,10 +136,10 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
     for (int i = 0; i < NV; ++i) {
       const int idx = i * stride + rl;
       const float* ti = t.t[i];
-      const u32x4 packed{pack_bf16x2(ti[0] * rho_f, ti[1] * rho_f),
-                         pack_bf16x2(ti[2] * rho_f, ti[3] * rho_f),
-                         pack_bf16x2(ti[4] * rho_f, ti[5] * rho_f),
-                         pack_bf16x2(ti[6] * rho_f, ti[7] * rho_f)};
+      const u32x4 packed{E::pack(ti[0] * rho_f, ti[1] * rho_f),
+                         E::pack(ti[2] * rho_f, ti[3] * rho_f),
+                         E::pack(ti[4] * rho_f, ti[5] * rho_f),
+                         E::pack(ti[6] * rho_f, ti[7] * rho_f)};
       if (idx < nvec) st_stream(o + idx * 8, packed);
     }
     return;
@@ -184,10 +186,10 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
 
 // Residual add + RMSNorm + quant.  Workgroup = kBlock lanes = kWavesPerBlock /
 // kW rows; each row lane holds NV vectors of x, residual and weight.
-// mode NONE writes the bf16 norm to out (uint16_t) and +0 to its columns
-// [H, H_pad) (the padding variant); the quantizing modes write FP8 codes
-// (uint8_t) and take H_pad = H.
-template <int NV, int kW, bool kResidual>
+// mode NONE writes the norm to out (uint16_t, element type E) and +0 to its
+// columns [H, H_pad) (the padding variant); the quantizing modes write FP8
+// codes (uint8_t) from bf16 inputs and take H_pad = H.
+template <int NV, int kW, bool kResidual, typename E = ElemBf16>
 __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x, int64_t x_stride,
                                                  uint16_t* __restrict__ residual,
                                                  int64_t res_stride,
@@ -215,14 +217,15 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   const float sscale = mode == RRA_Q_STATIC ? static_scale[0] : 0.0f;
 
   if (kResidual) {
-    // z = bf16(x + residual): the fp32 sum of two bf16 values rounds to the
-    // same bf16 as their exact sum.
+    // z = E(x + residual): fp32 carries at least 2p + 2 significand bits for
+    // p = 8 (bf16) and p = 11 (fp16), so rounding the fp32 sum of two such
+    // values to E gives the same value as rounding their exact sum.
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        a.v[i][k] = pack_bf16x2(bf16_lo(a.v[i][k]) + bf16_lo(r.v[i][k]),
-                                bf16_hi(a.v[i][k]) + bf16_hi(r.v[i][k]));
+        a.v[i][k] = E::pack(E::lo(a.v[i][k]) + E::lo(r.v[i][k]),
+                            E::hi(a.v[i][k]) + E::hi(r.v[i][k]));
     }
     if (active) store_row(residual + row * res_stride, a, nvec, rl, kStride);
   }
@@ -230,7 +233,7 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   RowT<NV> t;
   double ss;
   float m;
-  row_prepare(a, w, mode == RRA_Q_PER_TOKEN, t, ss, m);
+  row_prepare<NV, E>(a, w, mode == RRA_Q_PER_TOKEN, t, ss, m);
   row_reduce<kW>(ss, m, lds_ss, lds_m, (wave / kW) * kW, wave_in_row);
   if (!active) return;
 
@@ -239,7 +242,7 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   if (mode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / group);
   if (mode == RRA_Q_NONE) {
     uint16_t* o = static_cast<uint16_t*>(out) + row * out_stride;
-    rmsnorm_emit<NV>(t, ss, m, eps, H, nvec, rl, kStride, mode, group, sscale, o, nullptr);
+    rmsnorm_emit<NV, E>(t, ss, m, eps, H, nvec, rl, kStride, mode, group, sscale, o, nullptr);
     for (int idx = nvec + rl; idx < (H_pad >> 3); idx += kStride)
       st_stream(o + idx * 8, u32x4{0u, 0u, 0u, 0u});
     return;
@@ -262,15 +265,16 @@ __global__ void __launch_bounds__(kBlock)
                                       static_scale, out, out_stride, scales, T, H, H);
 }
 
-template <int NV, int kW, bool kResidual>
+template <int NV, int kW, bool kResidual, typename E>
 __global__ void __launch_bounds__(kBlock)
     add_rmsnorm_pad_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                            uint16_t* __restrict__ residual, int64_t res_stride,
                            const uint16_t* __restrict__ weight, float eps,
                            uint16_t* __restrict__ out, int64_t out_stride, int64_t T, int H,
                            int H_pad) {
-  add_rmsnorm_body<NV, kW, kResidual>(x, x_stride, residual, res_stride, weight, eps, RRA_Q_NONE,
-                                      0, nullptr, out, out_stride, nullptr, T, H, H_pad);
+  add_rmsnorm_body<NV, kW, kResidual, E>(x, x_stride, residual, res_stride, weight, eps,
+                                         RRA_Q_NONE, 0, nullptr, out, out_stride, nullptr, T, H,
+                                         H_pad);
 }
 
 // MLA dual RMSNorm: the q and kv latents of a token are two rows handled by
@@ -355,21 +359,27 @@ __global__ void __launch_bounds__(kBlock)
 // most two vectors of a row up to H = 4096 (four up to 8192).
 inline int norm_waves_per_row(int64_t H) { return H <= 1024 ? 1 : (H <= 2048 ? 2 : 4); }
 
-// mode NONE launches the padding kernel (bf16 out, columns [H, H_pad) zeroed),
-// the quantizing modes the quant kernel (H_pad unused).
+// mode NONE launches the padding kernel (out in the element type dtype,
+// columns [H, H_pad) zeroed), the quantizing modes the quant kernel (bf16
+// inputs; H_pad unused).
 template <bool kResidual>
 static int launch_add_rmsnorm(int64_t T, int H, int H_pad, hipStream_t st, const uint16_t* x,
                               int64_t xs, uint16_t* res, int64_t rs, const uint16_t* w, float eps,
                               int mode, int group, const float* sscale, void* out, int64_t os,
-                              float* scales) {
+                              float* scales, int dtype) {
   const int kw = norm_waves_per_row(H);
   const int nv = static_cast<int>(ceil_div(H, 8 * kWave * kw));
   const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock / kw)));
 #define RRA_NORM_CASE(N, W)                                                                   \
   if (nv == N && kw == W) {                                                                   \
-    if (mode == RRA_Q_NONE)                                                                   \
-      hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual>), grid, dim3(kBlock), 0, st, \
-                         x, xs, res, rs, w, eps, static_cast<uint16_t*>(out), os, T, H, H_pad); \
+    if (mode == RRA_Q_NONE && dtype == RRA_F16)                                               \
+      hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, ElemF16>), grid,            \
+                         dim3(kBlock), 0, st, x, xs, res, rs, w, eps,                         \
+                         static_cast<uint16_t*>(out), os, T, H, H_pad);                       \
+    else if (mode == RRA_Q_NONE)                                                              \
+      hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, ElemBf16>), grid,           \
+                         dim3(kBlock), 0, st, x, xs, res, rs, w, eps,                         \
+                         static_cast<uint16_t*>(out), os, T, H, H_pad);                       \
     else                                                                                      \
       hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual>), grid, dim3(kBlock), 0,   \
                          st, x, xs, res, rs, w, eps, mode, group, sscale,                     \
@@ -430,15 +440,16 @@ extern "C" int fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint
   if (residual)
     return launch_add_rmsnorm<true>(T, h, h, as_stream(stream), x, x_stride, residual,
                                     residual_stride, weight, eps, quant_mode, g, static_scale,
-                                    out, out_stride, scales);
+                                    out, out_stride, scales, RRA_BF16);
   return launch_add_rmsnorm<false>(T, h, h, as_stream(stream), x, x_stride, nullptr, 0, weight,
-                                   eps, quant_mode, g, static_scale, out, out_stride, scales);
+                                   eps, quant_mode, g, static_scale, out, out_stride, scales,
+                                   RRA_BF16);
 }
 
 extern "C" int fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residual,
                                      int64_t residual_stride, const uint16_t* weight, float eps,
                                      uint16_t* out, int64_t out_stride, int64_t T, int64_t H,
-                                     int64_t H_pad, void* stream) {
+                                     int64_t H_pad, int dtype, void* stream) {
   RRA_REQUIRE(T >= 0 && H > 0 && H_pad >= H, RRA_ERR_SHAPE);
   const bool rows_ok = T == 0 || (x && out);
   RRA_REQUIRE(rows_ok && weight, RRA_ERR_NULL);
@@ -446,6 +457,7 @@ extern "C" int fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16
   RRA_REQUIRE(!residual || residual_stride >= H, RRA_ERR_SHAPE);
   RRA_REQUIRE(H % 8 == 0 && H_pad % 8 == 0 && H <= 8192 && H_pad <= (int64_t(1) << 30),
               RRA_ERR_UNSUPPORTED);
+  RRA_REQUIRE(dtype == RRA_BF16 || dtype == RRA_F16, RRA_ERR_UNSUPPORTED);
   RRA_REQUIRE(vec_ok(x, x_stride) && aligned(weight, 16) && vec_ok(out, out_stride),
               RRA_ERR_ALIGN);
   RRA_REQUIRE(!residual || vec_ok(residual, residual_stride), RRA_ERR_ALIGN);
@@ -454,9 +466,9 @@ extern "C" int fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16
   if (residual)
     return launch_add_rmsnorm<true>(T, h, hp, as_stream(stream), x, x_stride, residual,
                                     residual_stride, weight, eps, RRA_Q_NONE, 0, nullptr, out,
-                                    out_stride, nullptr);
+                                    out_stride, nullptr, dtype);
   return launch_add_rmsnorm<false>(T, h, hp, as_stream(stream), x, x_stride, nullptr, 0, weight,
-                                   eps, RRA_Q_NONE, 0, nullptr, out, out_stride, nullptr);
+                                   eps, RRA_Q_NONE, 0, nullptr, out, out_stride, nullptr, dtype);
 }
 
 extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_weight,

@@ -143,13 +143,14 @@ def test_qknorm(launchers, rows, oracle):
     assert np.array_equal(gv, ref_vc.reshape(n, c.Hkv, c.D))
 
 
-def test_pad(launchers, rows, oracle):
-    c = workloads.PAD
-    io = launchers["_io"]["fused_add_rmsnorm_pad"]
+@pytest.mark.parametrize("name,c", [("fused_add_rmsnorm_pad", workloads.PAD),
+                                    ("fused_add_rmsnorm_pad_f16", workloads.PAD_F16)])
+def test_pad(launchers, rows, oracle, name, c):
+    io = launchers["_io"][name]
     x, r, w = h16(io["x"], rows), h16(io["residual"], rows), h16(io["weight"])
-    launch(launchers, "fused_add_rmsnorm_pad")
-    ref, ref_res = oracle.fused_add_rmsnorm_pad(x, r, w, c.eps, c.H_pad)
-    assert_bf16(h16(io["out"], rows), ref, "bench-path pad")
+    launch(launchers, name)
+    ref, ref_res = oracle.fused_add_rmsnorm_pad(x, r, w, c.eps, c.H_pad, dtype=c.dtype)
+    assert_elem(h16(io["out"], rows), ref, f"bench-path {name}", c.dtype)
     assert np.array_equal(h16(io["residual"], rows), ref_res)
 
 

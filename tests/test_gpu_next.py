@@ -20,7 +20,8 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import assert_bf16, dev, dev_bf16, host_bf16, require_gpu, sample_rows, say
+from gpu_util import (assert_bf16, assert_elem, dev, dev_bf16, dev_elem, host_bf16, require_gpu,
+                      sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,28 +132,30 @@ def test_qknorm_empty(rra):
 
 # ---- residual add + RMSNorm + padding ---------------------------------------------
 
-def run_pad(rra, oracle, T, H, H_pad, residual=True, eps=1e-5):
+def run_pad(rra, oracle, T, H, H_pad, residual=True, eps=1e-5, dtype="bf16"):
     import torch
 
-    say(f"[pad] T={T} H={H} H_pad={H_pad} residual={residual}")
-    d = workloads.norm_inputs(T, H, tag="pad")
-    x = dev_bf16(d["x"])
-    r = dev_bf16(d["residual"]) if residual else None
+    say(f"[pad] T={T} H={H} H_pad={H_pad} residual={residual} dtype={dtype}")
+    d = workloads.norm_inputs(T, H, tag="pad", dtype=dtype)
+    x = dev_elem(d["x"], dtype)
+    r = dev_elem(d["residual"], dtype) if residual else None
     r0 = r.clone() if residual else None
-    out = rra.fused_add_rmsnorm_pad(x, r, dev_bf16(d["weight"]), eps, H_pad)
+    out = rra.fused_add_rmsnorm_pad(x, r, dev_elem(d["weight"], dtype), eps, H_pad)
     torch.cuda.synchronize()
+    assert out.dtype == x.dtype
     g = host_bf16(out)
     assert np.array_equal(g[:, H:], np.zeros((T, H_pad - H), np.uint16)), "pad columns not +0"
     if residual:
-        full = (x.float() + r0.float()).to(torch.bfloat16)
+        # fp32 carries 2p + 2 bits for both types, so this is the exact sum rounded once
+        full = (x.float() + r0.float()).to(x.dtype)
         assert torch.equal(full.view(torch.int16), r.view(torch.int16))
     rows = sample_rows(T)
     if rows.size == 0:
         return
     ref, ref_res = oracle.fused_add_rmsnorm_pad(d["x"][rows],
                                                 d["residual"][rows] if residual else None,
-                                                d["weight"], eps, H_pad)
-    assert_bf16(g[rows], ref, f"normed T={T} H={H}")
+                                                d["weight"], eps, H_pad, dtype=dtype)
+    assert_elem(g[rows], ref, f"normed T={T} H={H}", dtype)
     if residual:
         assert np.array_equal(host_bf16(r)[rows], ref_res)
 
@@ -167,6 +170,18 @@ def test_pad_workload(rra, oracle, T):
                                                 (3, 2048, 2304, True)])
 def test_pad_shapes(rra, oracle, T, H, H_pad, residual):
     run_pad(rra, oracle, T, H, H_pad, residual)
+
+
+@pytest.mark.parametrize("T", workloads.PAD_F16.Ts)
+def test_pad_f16_workload(rra, oracle, T):
+    c = workloads.PAD_F16
+    run_pad(rra, oracle, T, c.H, c.H_pad, eps=c.eps, dtype="f16")
+
+
+@pytest.mark.parametrize("T,H,H_pad,residual", [(9, 2880, 3072, False), (33, 1000, 1024, True),
+                                                (5, 8, 64, True), (3, 8192, 8192, True)])
+def test_pad_f16_shapes(rra, oracle, T, H, H_pad, residual):
+    run_pad(rra, oracle, T, H, H_pad, residual, dtype="f16")
 
 
 def test_pad_empty(rra):

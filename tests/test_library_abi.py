@@ -194,10 +194,11 @@ def test_rmsnorm_pad_validation(rra):
     L = rra.lib()
 
     def f(**k):
-        a = dict(x=A, xs=2880, r=A, rs=2880, w=A, eps=1e-5, o=A, os=3072, T=4, H=2880, Hp=3072)
+        a = dict(x=A, xs=2880, r=A, rs=2880, w=A, eps=1e-5, o=A, os=3072, T=4, H=2880, Hp=3072,
+                 dt=rra.BF16)
         a.update(k)
         return L.fused_add_rmsnorm_pad(a["x"], a["xs"], a["r"], a["rs"], a["w"], a["eps"],
-                                       a["o"], a["os"], a["T"], a["H"], a["Hp"], None)
+                                       a["o"], a["os"], a["T"], a["H"], a["Hp"], a["dt"], None)
 
     assert f(T=0) == OK
     assert f(x=None, r=None, o=None, T=0) == OK
@@ -207,6 +208,8 @@ def test_rmsnorm_pad_validation(rra):
     assert f(Hp=3076, os=3076) == EUNSUP  # H_pad % 8
     assert f(o=A + 8) == EALIGN
     assert f(x=A + 2) == EALIGN
+    assert f(dt=2) == EUNSUP and f(dt=rra.F16, x=A + 2) == EALIGN
+    assert f(dt=rra.F16, T=0) == OK
 
 
 def test_mla_rope_validation(rra):

@@ -7,7 +7,8 @@ mathematics fix (not against the oracle itself):
   frequency at once), norm preservation, the relative-position property, the
   split of qkv into q / k / v, the cache placement, and fused == unfused.
 - Residual add + RMSNorm + padding (section "RMSNorm + Padding"): the
-  hand-worked norm example, exact +0 padding, the residual update.
+  hand-worked norm example, exact +0 padding, the residual update; with fp16
+  elements the same example and a closed form against numpy's fp16 rounding.
 - MLA RoPE + cache concat (the MLA split of section "MLA Dual RMSNorm" with
   the cache write of section "RoPE + KV-Cache Update"): position 0 is a pure
   copy into [kv_c | k_pe], a one-hot pins GPT-J pairing, strided q heads keep
@@ -225,6 +226,49 @@ def test_pad_without_residual_and_no_padding(oracle):
     assert res is None and a.shape == (3, cfg.H)
     b, _ = oracle.fused_add_rmsnorm_pad(d["x"], None, d["weight"], cfg.eps, cfg.H_pad)
     assert np.array_equal(a, b[:, :cfg.H])
+
+
+def _f16(a):
+    return np.asarray(a, np.float64).astype(np.float16).view(np.uint16)
+
+
+def _f16_to_f64(h):
+    return np.asarray(h, np.uint16).view(np.float16).astype(np.float64)
+
+
+def test_pad_f16_worked_example(oracle):
+    """The worked example's values are exact in fp16 too, so the fp16 op gives
+    the same y = z * w and residual."""
+    ex = read_kv("norm_quant_worked_example.txt")
+    vals = lambda k: np.array([float(v) for v in ex[k]])
+    x, r, w = _f16(vals("x")), _f16(vals("residual")), _f16(vals("weight"))
+    assert np.array_equal(_f16_to_f64(x), vals("x"))
+    out, res = oracle.fused_add_rmsnorm_pad(x[None], r[None], w, 0.0, 8, dtype="f16")
+    assert np.array_equal(_f16_to_f64(res[0]), vals("residual_out"))
+    assert list(_f16_to_f64(out[0, :4])) == [1.0, -0.75, 0.5, -0.328125]
+    assert np.array_equal(out[0, 4:], np.zeros(4, np.uint16))
+
+
+def test_pad_f16_closed_form(oracle):
+    """fp16 elements: the residual is numpy's one-rounding fp16 of x + residual,
+    and each output is within half an fp16 unit of z * rho * w computed in
+    double (the op rounds the exact value once); the pad is +0."""
+    cfg = workloads.PAD_F16
+    d = workloads.pad_inputs(9, cfg)
+    out, res = oracle.fused_add_rmsnorm_pad(d["x"], d["residual"], d["weight"], cfg.eps,
+                                            cfg.H_pad, dtype="f16")
+    z = _f16_to_f64(d["x"]) + _f16_to_f64(d["residual"])
+    assert np.array_equal(res, _f16(z))
+    z = _f16_to_f64(res)
+    rho = 1.0 / np.sqrt(np.mean(z ** 2, axis=1, keepdims=True) + np.float32(cfg.eps))
+    want = z * rho * _f16_to_f64(d["weight"])[None]
+    got = _f16_to_f64(out[:, :cfg.H])
+    assert np.all(np.abs(got - want) <= 2.0 ** -11 * np.abs(want) + 2.0 ** -25)
+    assert np.array_equal(out[:, cfg.H:], np.zeros((9, cfg.H_pad - cfg.H), np.uint16))
+    # read as bf16 the same bits would give a different row: the type is honoured
+    other, _ = oracle.fused_add_rmsnorm_pad(d["x"], d["residual"], d["weight"], cfg.eps,
+                                            cfg.H_pad)
+    assert not np.array_equal(other, out)
 
 
 # ---- MLA RoPE + cache concat ------------------------------------------------------

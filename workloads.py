@@ -3,7 +3,9 @@
 Shared by the tests, the benchmark and the smoke check, and by both the HIP
 path and the CPU oracle.  It holds none of the method's arithmetic: it only
 draws random numbers (numpy ``default_rng``) and stores them as bf16 bit
-patterns (torch's float32 -> bfloat16 conversion, round-to-nearest-even).
+patterns (torch's float32 -> bfloat16 conversion, round-to-nearest-even) or,
+for the fp16 variants, IEEE fp16 bit patterns (numpy's float32 -> float16
+conversion, round-to-nearest-even).
 
 Layer shapes are those of Llama-3-8B (hidden 4096, intermediate 14336, 32 query
 / 8 key-value heads of 128, rope theta 500000) and of DeepSeek-V3's MLA
@@ -113,6 +115,7 @@ class PadCfg:
     H_pad: int = 3072
     eps: float = 1e-5
     Ts: tuple = (16, 2048, 8192)
+    dtype: str = "bf16"  # element type of x, residual, weight and out: "bf16" or "f16"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -134,6 +137,7 @@ class MlaRopeCfg:
 
 QKNORM = QkNormCfg()
 PAD = PadCfg()
+PAD_F16 = PadCfg(name="pad_f16", dtype="f16")
 MLA_ROPE = MlaRopeCfg()
 
 
@@ -167,8 +171,13 @@ def elem_normal(dtype: str, rng: np.random.Generator, shape):
     return f16_normal(rng, shape) if dtype == "f16" else bf16_normal(rng, shape)
 
 
-def norm_inputs(T: int, H: int, salt: int = 0, tag: str = "norm_token"):
-    """x, residual ~ N(0,1) [T,H]; weight ~ N(1, 0.1) [H]."""
+def norm_inputs(T: int, H: int, salt: int = 0, tag: str = "norm_token", dtype: str = "bf16"):
+    """x, residual ~ N(0,1) [T,H]; weight ~ N(1, 0.1) [H]; bit patterns of dtype."""
+    if dtype == "f16":
+        w = 1.0 + 0.1 * _rng(tag, 0, 2, salt).standard_normal(H, dtype=np.float32)
+        return dict(x=f16_normal(_rng(tag, T, 0, salt), (T, H)),
+                    residual=f16_normal(_rng(tag, T, 1, salt), (T, H)),
+                    weight=w.astype(np.float16).view(np.uint16))
     return dict(
         x=bf16_normal(_rng(tag, T, 0, salt), (T, H)),
         residual=bf16_normal(_rng(tag, T, 1, salt), (T, H)),
@@ -232,7 +241,7 @@ def qknorm_inputs(T: int, cfg: QkNormCfg = QKNORM, salt: int = 0, with_cache: bo
 
 def pad_inputs(T: int, cfg: PadCfg = PAD, salt: int = 0):
     """x, residual ~ N(0,1) [T, H]; weight ~ N(1, 0.1)."""
-    return norm_inputs(T, cfg.H, salt=salt, tag="pad")
+    return norm_inputs(T, cfg.H, salt=salt, tag="pad", dtype=cfg.dtype)
 
 
 def mla_rope_inputs(T: int, cfg: MlaRopeCfg = MLA_ROPE, salt: int = 0, with_cache: bool = True):
@@ -290,10 +299,12 @@ def _randn(g, shape, device, mean=0.0, std=1.0, dtype="bf16"):
     return a.to(torch.float16 if dtype == "f16" else torch.bfloat16)
 
 
-def device_norm_inputs(T: int, H: int, device="cuda", salt: int = 0, tag: str = "norm_token"):
+def device_norm_inputs(T: int, H: int, device="cuda", salt: int = 0, tag: str = "norm_token",
+                       dtype: str = "bf16"):
     g = _gen(device, tag, T, salt)
-    return dict(x=_randn(g, (T, H), device), residual=_randn(g, (T, H), device),
-                weight=_randn(g, (H,), device, mean=1.0, std=0.1))
+    return dict(x=_randn(g, (T, H), device, dtype=dtype),
+                residual=_randn(g, (T, H), device, dtype=dtype),
+                weight=_randn(g, (H,), device, mean=1.0, std=0.1, dtype=dtype))
 
 
 def device_silu_inputs(T: int, I: int, device="cuda", salt: int = 0):
@@ -353,7 +364,7 @@ def device_qknorm_inputs(T: int, cfg: QkNormCfg = QKNORM, device="cuda", salt: i
 
 
 def device_pad_inputs(T: int, cfg: PadCfg = PAD, device="cuda", salt: int = 0):
-    return device_norm_inputs(T, cfg.H, device, salt, tag="pad")
+    return device_norm_inputs(T, cfg.H, device, salt, tag="pad", dtype=cfg.dtype)
 
 
 def device_mla_rope_inputs(T: int, cfg: MlaRopeCfg = MLA_ROPE, device="cuda", salt: int = 0,
