@@ -120,16 +120,17 @@ __device__ __forceinline__ void row_reduce(double& ss, float& m, double* lds_ss,
 // per-token scale, the first lane of each group for per-group scales).
 // Because rho > 0 is one number per row, max|y| = max|t| * rho, so the amax
 // needs no second pass over y, and the codes are e4m3fn(t * rho / s) (quant8
-// rounds them as the exact quotient would).
-template <int NV, typename E = ElemBf16>
+// rounds them as the exact quotient would).  kMode and kGroup (64 or 128 for
+// per-group scales, else 0) are compile-time, so group indexing is a shift.
+template <int NV, int kMode, int kGroup, typename E = ElemBf16>
 __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float m_row,
                                              float eps, int H, int nvec, int rl, int stride,
-                                             int mode, int group, float static_scale,
-                                             void* out, float* scale_row) {
+                                             float static_scale, void* out, float* scale_row) {
+  static_assert(kMode != RRA_Q_PER_GROUP || kGroup == 64 || kGroup == 128, "group size");
   const double rho = rsqrt_f64(ss / static_cast<double>(H) + static_cast<double>(eps));
   const int lane = lane_id();
 
-  if (mode == RRA_Q_NONE) {
+  if constexpr (kMode == RRA_Q_NONE) {
     const float rho_f = static_cast<float>(rho);
     uint16_t* o = static_cast<uint16_t*>(out);
 #pragma unroll
@@ -146,25 +147,25 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
   }
 
   uint8_t* o = static_cast<uint8_t*>(out);
-  if (mode == RRA_Q_PER_GROUP) {
-    const int lanes_per_group = group / 8;
+  if constexpr (kMode == RRA_Q_PER_GROUP) {
+    constexpr int kLanesPerGroup = kGroup / 8;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = i * stride + rl;
       float m = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t.t[i][j]));
-      m = group == 128 ? max16(m) : max8(m);
+      m = kGroup == 128 ? max16(m) : max8(m);
       const QuantStep qs = quant_step(rho, dynamic_scale(m, rho));
       if (idx < nvec) {
-        if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = qs.s;
+        if ((lane & (kLanesPerGroup - 1)) == 0) scale_row[idx / kLanesPerGroup] = qs.s;
         st_stream(o + idx * 8, quant8<false>(t.t[i], qs));
       }
     }
     return;
   }
 
-  if (mode == RRA_Q_PER_TOKEN) {
+  if constexpr (kMode == RRA_Q_PER_TOKEN) {
     const float s = dynamic_scale(m_row, rho);
     if (rl == 0) scale_row[0] = s;
     const QuantStep qs = quant_step(rho, s);
@@ -186,15 +187,14 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
 
 // Residual add + RMSNorm + quant.  Workgroup = kBlock lanes = kWavesPerBlock /
 // kW rows; each row lane holds NV vectors of x, residual and weight.
-// mode NONE writes the norm to out (uint16_t, element type E) and +0 to its
+// kMode NONE writes the norm to out (uint16_t, element type E) and +0 to its
 // columns [H, H_pad) (the padding variant); the quantizing modes write FP8
 // codes (uint8_t) from bf16 inputs and take H_pad = H.
-template <int NV, int kW, bool kResidual, typename E = ElemBf16>
+template <int NV, int kW, bool kResidual, int kMode, int kGroup, typename E = ElemBf16>
 __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x, int64_t x_stride,
                                                  uint16_t* __restrict__ residual,
                                                  int64_t res_stride,
                                                  const uint16_t* __restrict__ weight, float eps,
-                                                 int mode, int group,
                                                  const float* __restrict__ static_scale,
                                                  void* __restrict__ out, int64_t out_stride,
                                                  float* __restrict__ scales, int64_t T, int H,
@@ -214,7 +214,7 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   load_row<NV, true>(a, x + row * x_stride, nvec, rl, kStride, active);
   if (kResidual) load_row<NV, true>(r, residual + row * res_stride, nvec, rl, kStride, active);
   load_row<NV, false>(w, weight, nvec, rl, kStride, true);
-  const float sscale = mode == RRA_Q_STATIC ? static_scale[0] : 0.0f;
+  const float sscale = kMode == RRA_Q_STATIC ? static_scale[0] : 0.0f;
 
   if (kResidual) {
     // z = E(x + residual): fp32 carries at least 2p + 2 significand bits for
@@ -233,36 +233,37 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   RowT<NV> t;
   double ss;
   float m;
-  row_prepare<NV, E>(a, w, mode == RRA_Q_PER_TOKEN, t, ss, m);
+  row_prepare<NV, E>(a, w, kMode == RRA_Q_PER_TOKEN, t, ss, m);
   row_reduce<kW>(ss, m, lds_ss, lds_m, (wave / kW) * kW, wave_in_row);
   if (!active) return;
 
-  float* scale_row = nullptr;
-  if (mode == RRA_Q_PER_TOKEN) scale_row = scales + row;
-  if (mode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / group);
-  if (mode == RRA_Q_NONE) {
+  if constexpr (kMode == RRA_Q_NONE) {
     uint16_t* o = static_cast<uint16_t*>(out) + row * out_stride;
-    rmsnorm_emit<NV, E>(t, ss, m, eps, H, nvec, rl, kStride, mode, group, sscale, o, nullptr);
+    rmsnorm_emit<NV, RRA_Q_NONE, 0, E>(t, ss, m, eps, H, nvec, rl, kStride, 0.0f, o, nullptr);
     for (int idx = nvec + rl; idx < (H_pad >> 3); idx += kStride)
       st_stream(o + idx * 8, u32x4{0u, 0u, 0u, 0u});
-    return;
+  } else {
+    float* scale_row = nullptr;
+    if (kMode == RRA_Q_PER_TOKEN) scale_row = scales + row;
+    if (kMode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / kGroup);
+    rmsnorm_emit<NV, kMode, kGroup>(t, ss, m, eps, H, nvec, rl, kStride, sscale,
+                                    static_cast<uint8_t*>(out) + row * out_stride, scale_row);
   }
-  rmsnorm_emit<NV>(t, ss, m, eps, H, nvec, rl, kStride, mode, group, sscale,
-                   static_cast<uint8_t*>(out) + row * out_stride, scale_row);
 }
 
 // Two entry kernels over the same body, so that profiles tell the quantizing
 // op from the padding op.
-template <int NV, int kW, bool kResidual>
+template <int NV, int kW, bool kResidual, int kMode, int kGroup>
 __global__ void __launch_bounds__(kBlock)
     add_rmsnorm_quant_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                              uint16_t* __restrict__ residual, int64_t res_stride,
-                             const uint16_t* __restrict__ weight, float eps, int mode,
-                             int group, const float* __restrict__ static_scale,
+                             const uint16_t* __restrict__ weight, float eps,
+                             const float* __restrict__ static_scale,
                              uint8_t* __restrict__ out, int64_t out_stride,
                              float* __restrict__ scales, int64_t T, int H) {
-  add_rmsnorm_body<NV, kW, kResidual>(x, x_stride, residual, res_stride, weight, eps, mode, group,
-                                      static_scale, out, out_stride, scales, T, H, H);
+  add_rmsnorm_body<NV, kW, kResidual, kMode, kGroup>(x, x_stride, residual, res_stride, weight,
+                                                     eps, static_scale, out, out_stride, scales,
+                                                     T, H, H);
 }
 
 template <int NV, int kW, bool kResidual, typename E>
@@ -272,9 +273,9 @@ __global__ void __launch_bounds__(kBlock)
                            const uint16_t* __restrict__ weight, float eps,
                            uint16_t* __restrict__ out, int64_t out_stride, int64_t T, int H,
                            int H_pad) {
-  add_rmsnorm_body<NV, kW, kResidual, E>(x, x_stride, residual, res_stride, weight, eps,
-                                         RRA_Q_NONE, 0, nullptr, out, out_stride, nullptr, T, H,
-                                         H_pad);
+  add_rmsnorm_body<NV, kW, kResidual, RRA_Q_NONE, 0, E>(x, x_stride, residual, res_stride,
+                                                        weight, eps, nullptr, out, out_stride,
+                                                        nullptr, T, H, H_pad);
 }
 
 // MLA dual RMSNorm: the q and kv latents of a token are two rows handled by
@@ -283,13 +284,13 @@ __global__ void __launch_bounds__(kBlock)
 // wave per token (four tokens per workgroup) beats spreading a token over
 // more waves: the rows are short, and a barrier per token costs more than the
 // extra vectors per lane.
-template <int NVQ, int NVKV, int kW>
+template <int NVQ, int NVKV, int kW, int kMode, int kGroup>
 __global__ void __launch_bounds__(kBlock)
     dual_rmsnorm_quant_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
                               const uint16_t* __restrict__ q_w, float eps_q,
                               const uint16_t* __restrict__ kv, int64_t kv_stride,
-                              const uint16_t* __restrict__ kv_w, float eps_kv, int mode,
-                              int group, void* __restrict__ q_out, int64_t q_out_stride,
+                              const uint16_t* __restrict__ kv_w, float eps_kv,
+                              void* __restrict__ q_out, int64_t q_out_stride,
                               float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
                               int64_t kv_out_stride, int64_t T, int Hq, int Hkv) {
   constexpr int kRowsPerBlock = kWavesPerBlock / kW;
@@ -316,7 +317,7 @@ __global__ void __launch_bounds__(kBlock)
   RowT<NVKV> tkv;
   double ss_q, ss_kv;
   float m_q, m_kv;
-  row_prepare(zq, wq, mode == RRA_Q_PER_TOKEN, tq, ss_q, m_q);
+  row_prepare(zq, wq, kMode == RRA_Q_PER_TOKEN, tq, ss_q, m_q);
   row_prepare(zkv, wkv, false, tkv, ss_kv, m_kv);
   ss_q = wave_sum_f64(ss_q);
   ss_kv = wave_sum_f64(ss_kv);
@@ -343,25 +344,76 @@ __global__ void __launch_bounds__(kBlock)
 
   void* qo;
   float* scale_row = nullptr;
-  if (mode == RRA_Q_NONE) {
+  if constexpr (kMode == RRA_Q_NONE) {
     qo = static_cast<uint16_t*>(q_out) + row * q_out_stride;
   } else {
     qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
-    scale_row = mode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / group);
+    scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
   }
-  rmsnorm_emit<NVQ>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, mode, group, 0.0f, qo,
-                    scale_row);
-  rmsnorm_emit<NVKV>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kStride, RRA_Q_NONE, 0, 0.0f,
-                     kv_out + row * kv_out_stride, nullptr);
+  rmsnorm_emit<NVQ, kMode, kGroup>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, 0.0f, qo,
+                                   scale_row);
+  rmsnorm_emit<NVKV, RRA_Q_NONE, 0>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kStride, 0.0f,
+                                    kv_out + row * kv_out_stride, nullptr);
 }
 
 // Waves per row for the residual-add norm: enough that each lane holds at
 // most two vectors of a row up to H = 4096 (four up to 8192).
 inline int norm_waves_per_row(int64_t H) { return H <= 1024 ? 1 : (H <= 2048 ? 2 : 4); }
 
-// mode NONE launches the padding kernel (out in the element type dtype,
-// columns [H, H_pad) zeroed), the quantizing modes the quant kernel (bf16
-// inputs; H_pad unused).
+// Arguments of one residual-add norm launch.
+struct NormLaunch {
+  dim3 grid;
+  hipStream_t st;
+  const uint16_t* x;
+  int64_t xs;
+  uint16_t* res;
+  int64_t rs;
+  const uint16_t* w;
+  float eps;
+  const float* sscale;
+  void* out;
+  int64_t os;
+  float* scales;
+  int64_t T;
+  int H, H_pad;
+};
+
+template <int N, int W, bool kResidual, int kMode, int kGroup>
+static void launch_norm_quant(const NormLaunch& a) {
+  hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual, kMode, kGroup>), a.grid,
+                     dim3(kBlock), 0, a.st, a.x, a.xs, a.res, a.rs, a.w, a.eps, a.sscale,
+                     static_cast<uint8_t*>(a.out), a.os, a.scales, a.T, a.H);
+}
+
+template <int N, int W, bool kResidual, typename E>
+static void launch_norm_pad(const NormLaunch& a) {
+  hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, E>), a.grid, dim3(kBlock), 0, a.st,
+                     a.x, a.xs, a.res, a.rs, a.w, a.eps, static_cast<uint16_t*>(a.out), a.os,
+                     a.T, a.H, a.H_pad);
+}
+
+// One (vectors per lane, waves per row) case: mode NONE launches the padding
+// kernel (out in the element type dtype, columns [H, H_pad) zeroed), the
+// quantizing modes the quant kernel for that mode and group size (bf16 in).
+template <int N, int W, bool kResidual>
+static void launch_norm_case(const NormLaunch& a, int mode, int group, int dtype) {
+  switch (mode) {
+    case RRA_Q_NONE:
+      if (dtype == RRA_F16)
+        launch_norm_pad<N, W, kResidual, ElemF16>(a);
+      else
+        launch_norm_pad<N, W, kResidual, ElemBf16>(a);
+      break;
+    case RRA_Q_STATIC: launch_norm_quant<N, W, kResidual, RRA_Q_STATIC, 0>(a); break;
+    case RRA_Q_PER_TOKEN: launch_norm_quant<N, W, kResidual, RRA_Q_PER_TOKEN, 0>(a); break;
+    default:
+      if (group == 64)
+        launch_norm_quant<N, W, kResidual, RRA_Q_PER_GROUP, 64>(a);
+      else
+        launch_norm_quant<N, W, kResidual, RRA_Q_PER_GROUP, 128>(a);
+  }
+}
+
 template <bool kResidual>
 static int launch_add_rmsnorm(int64_t T, int H, int H_pad, hipStream_t st, const uint16_t* x,
                               int64_t xs, uint16_t* res, int64_t rs, const uint16_t* w, float eps,
@@ -369,22 +421,12 @@ static int launch_add_rmsnorm(int64_t T, int H, int H_pad, hipStream_t st, const
                               float* scales, int dtype) {
   const int kw = norm_waves_per_row(H);
   const int nv = static_cast<int>(ceil_div(H, 8 * kWave * kw));
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock / kw)));
-#define RRA_NORM_CASE(N, W)                                                                   \
-  if (nv == N && kw == W) {                                                                   \
-    if (mode == RRA_Q_NONE && dtype == RRA_F16)                                               \
-      hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, ElemF16>), grid,            \
-                         dim3(kBlock), 0, st, x, xs, res, rs, w, eps,                         \
-                         static_cast<uint16_t*>(out), os, T, H, H_pad);                       \
-    else if (mode == RRA_Q_NONE)                                                              \
-      hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, ElemBf16>), grid,           \
-                         dim3(kBlock), 0, st, x, xs, res, rs, w, eps,                         \
-                         static_cast<uint16_t*>(out), os, T, H, H_pad);                       \
-    else                                                                                      \
-      hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual>), grid, dim3(kBlock), 0,   \
-                         st, x, xs, res, rs, w, eps, mode, group, sscale,                     \
-                         static_cast<uint8_t*>(out), os, scales, T, H);                       \
-    return launch_status();                                                                   \
+  const NormLaunch a{dim3(static_cast<unsigned>(ceil_div(T, kWavesPerBlock / kw))),
+                     st, x, xs, res, rs, w, eps, sscale, out, os, scales, T, H, H_pad};
+#define RRA_NORM_CASE(N, W)                                   \
+  if (nv == N && kw == W) {                                   \
+    launch_norm_case<N, W, kResidual>(a, mode, group, dtype); \
+    return launch_status();                                   \
   }
   RRA_NORM_CASE(1, 1)
   RRA_NORM_CASE(2, 1)
@@ -394,6 +436,47 @@ static int launch_add_rmsnorm(int64_t T, int H, int H_pad, hipStream_t st, const
   RRA_NORM_CASE(4, 4)
 #undef RRA_NORM_CASE
   return RRA_ERR_UNSUPPORTED;
+}
+
+// Arguments of one MLA dual-norm launch.
+struct DualLaunch {
+  dim3 grid;
+  hipStream_t st;
+  const uint16_t* q;
+  int64_t qs;
+  const uint16_t* qw;
+  float eps_q;
+  const uint16_t* kv;
+  int64_t kvs;
+  const uint16_t* kvw;
+  float eps_kv;
+  void* q_out;
+  int64_t qos;
+  float* q_scales;
+  uint16_t* kv_out;
+  int64_t kvos;
+  int64_t T;
+  int Hq, Hkv;
+};
+
+template <int A, int B, int kMode, int kGroup>
+static void launch_dual(const DualLaunch& a) {
+  hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, 1, kMode, kGroup>), a.grid, dim3(kBlock), 0,
+                     a.st, a.q, a.qs, a.qw, a.eps_q, a.kv, a.kvs, a.kvw, a.eps_kv, a.q_out, a.qos,
+                     a.q_scales, a.kv_out, a.kvos, a.T, a.Hq, a.Hkv);
+}
+
+template <int A, int B>
+static void launch_dual_case(const DualLaunch& a, int mode, int group) {
+  switch (mode) {
+    case RRA_Q_NONE: launch_dual<A, B, RRA_Q_NONE, 0>(a); break;
+    case RRA_Q_PER_TOKEN: launch_dual<A, B, RRA_Q_PER_TOKEN, 0>(a); break;
+    default:
+      if (group == 64)
+        launch_dual<A, B, RRA_Q_PER_GROUP, 64>(a);
+      else
+        launch_dual<A, B, RRA_Q_PER_GROUP, 128>(a);
+  }
 }
 
 }  // namespace rra
@@ -509,16 +592,14 @@ extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uin
   // One wave per token: NVQ = ceil(Hq / 512) and NVKV = ceil(Hkv / 512) vectors per lane.
   const int nvq = static_cast<int>(ceil_div(Hq, 8 * kWave));
   const int nvkv = static_cast<int>(ceil_div(Hkv, 8 * kWave));
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWavesPerBlock)));
-  const hipStream_t st = as_stream(stream);
-  const int g = q_quant_mode == RRA_Q_PER_GROUP ? group_size : 0;
-#define RRA_DUAL_CASE(A, B)                                                                    \
-  if (nvq == A && nvkv == B) {                                                                 \
-    hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, 1>), grid, dim3(kBlock), 0, st, q,     \
-                       q_stride, q_weight, eps_q, kv, kv_stride, kv_weight, eps_kv,             \
-                       q_quant_mode, g, q_out, q_out_stride, q_scales, kv_out, kv_out_stride,  \
-                       T, static_cast<int>(Hq), static_cast<int>(Hkv));                        \
-    return launch_status();                                                                    \
+  const DualLaunch a{dim3(static_cast<unsigned>(ceil_div(T, kWavesPerBlock))),
+                     as_stream(stream), q, q_stride, q_weight, eps_q, kv, kv_stride, kv_weight,
+                     eps_kv, q_out, q_out_stride, q_scales, kv_out, kv_out_stride, T,
+                     static_cast<int>(Hq), static_cast<int>(Hkv)};
+#define RRA_DUAL_CASE(A, B)                                \
+  if (nvq == A && nvkv == B) {                             \
+    launch_dual_case<A, B>(a, q_quant_mode, group_size);   \
+    return launch_status();                                \
   }
   RRA_DUAL_CASE(1, 1)
   RRA_DUAL_CASE(2, 1)

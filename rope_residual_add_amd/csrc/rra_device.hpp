@@ -120,9 +120,11 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // True when v (an fp32 estimate of q) may round differently from q: its 20
 // fraction bits below e4m3's three lie within [-8, +7] ulps of 0x80000 (one
 // half of the e4m3 quantum), or |v| is below 2^-6 (e4m3 subnormals, where the
-// quantum is fixed; zero included).
+// quantum is fixed; zero included).  The first test is bits 4..19 of
+// bits + 8 - 0x80000 all zero, i.e. that value shifted left by 12 below 2^16:
+// one add-and-shift and one compare.
 __device__ __forceinline__ bool e4m3_near_tie(float v) {
-  return ((__float_as_uint(v) + 8u) & 0xFFFF0u) == 0x80000u || fabsf(v) < 0x1p-6f;
+  return ((__float_as_uint(v) + (8u - 0x80000u)) << 12) < 0x10000u || fabsf(v) < 0x1p-6f;
 }
 
 // double -> fp32 rounding to odd: truncate toward zero, set the last bit if

@@ -38,12 +38,15 @@ __device__ __forceinline__ void silu8(u32x4 g, u32x4 u, float a[8]) {
   }
 }
 
-template <int NV>
+// kMode RRA_Q_STATIC or RRA_Q_PER_GROUP with kGroup 64 or 128 (compile-time,
+// so group indexing is a shift).
+template <int NV, int kMode, int kGroup>
 __global__ void __launch_bounds__(kBlock)
-    silu_mul_quant_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int mode,
-                          int group, const float* __restrict__ static_scale,
+    silu_mul_quant_kernel(const uint16_t* __restrict__ in, int64_t in_stride,
+                          const float* __restrict__ static_scale,
                           uint8_t* __restrict__ out, int64_t out_stride,
                           float* __restrict__ scales, int64_t T, int I, int chunks) {
+  static_assert(kMode == RRA_Q_STATIC || kGroup == 64 || kGroup == 128, "group size");
   const int lane = lane_id();
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
   const int64_t row = wid / chunks;
@@ -67,7 +70,7 @@ __global__ void __launch_bounds__(kBlock)
   }
 
   uint8_t* o = out + row * out_stride;
-  if (mode == RRA_Q_STATIC) {
+  if constexpr (kMode == RRA_Q_STATIC) {
     const float f = 1.0f / static_scale[0];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -79,31 +82,29 @@ __global__ void __launch_bounds__(kBlock)
                   u32x2{pack_e4m3x4(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
                         pack_e4m3x4(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
     }
-    return;
-  }
-
-  // RRA_Q_PER_GROUP
-  float* scale_row = scales + row * (I / group);
-  const int lanes_per_group = group / 8;
+  } else {  // RRA_Q_PER_GROUP
+    float* scale_row = scales + row * (I / kGroup);
+    constexpr int kLanesPerGroup = kGroup / 8;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = (chunk * NV + i) * kWave + lane;
-    float a[8];
-    silu8(g[i], u[i], a);
-    float m = 0.0f;
+    for (int i = 0; i < NV; ++i) {
+      const int idx = (chunk * NV + i) * kWave + lane;
+      float a[8];
+      silu8(g[i], u[i], a);
+      float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(a[j]));
-    m = group == 128 ? max16(m) : max8(m);
-    // s = amax / 448 and f = 1 / s with a multiply and the hardware
-    // reciprocal: the activation itself carries ~1e-6 relative error, so
-    // correctly rounded divisions would buy nothing here.
-    const float s = m * (1.0f / 448.0f);
-    const float f = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
-    if (idx < nvec) {
-      if ((lane & (lanes_per_group - 1)) == 0) scale_row[(idx * 8) / group] = s;
-      // |a * f| <= 448 within rounding: no saturation needed
-      st_stream(o + idx * 8, u32x2{pack_e4m3x4<false>(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
-                                   pack_e4m3x4<false>(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(a[j]));
+      m = kGroup == 128 ? max16(m) : max8(m);
+      // s = amax / 448 and f = 1 / s with a multiply and the hardware
+      // reciprocal: the activation itself carries ~1e-6 relative error, so
+      // correctly rounded divisions would buy nothing here.
+      const float s = m * (1.0f / 448.0f);
+      const float f = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+      if (idx < nvec) {
+        if ((lane & (kLanesPerGroup - 1)) == 0) scale_row[idx / kLanesPerGroup] = s;
+        // |a * f| <= 448 within rounding: no saturation needed
+        st_stream(o + idx * 8, u32x2{pack_e4m3x4<false>(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
+                                     pack_e4m3x4<false>(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
+      }
     }
   }
 }
@@ -143,9 +144,18 @@ extern "C" int silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_m
   const int64_t chunks = ceil_div(I, 8 * kWave * kSiluNV);
   const int64_t blocks = ceil_div(T * chunks, kWavesPerBlock);
   RRA_REQUIRE(blocks <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
-  hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kBlock), 0, as_stream(stream), in, in_stride, quant_mode,
-                     quant_mode == RRA_Q_PER_GROUP ? group_size : 0, static_scale, out,
-                     out_stride, scales, T, static_cast<int>(I), static_cast<int>(chunks));
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const hipStream_t st = as_stream(stream);
+  const int i32 = static_cast<int>(I), c32 = static_cast<int>(chunks);
+  if (quant_mode == RRA_Q_STATIC)
+    hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV, RRA_Q_STATIC, 0>), grid, dim3(kBlock), 0,
+                       st, in, in_stride, static_scale, out, out_stride, scales, T, i32, c32);
+  else if (group_size == 64)
+    hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV, RRA_Q_PER_GROUP, 64>), grid, dim3(kBlock),
+                       0, st, in, in_stride, static_scale, out, out_stride, scales, T, i32, c32);
+  else
+    hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV, RRA_Q_PER_GROUP, 128>), grid,
+                       dim3(kBlock), 0, st, in, in_stride, static_scale, out, out_stride, scales,
+                       T, i32, c32);
   return launch_status();
 }
