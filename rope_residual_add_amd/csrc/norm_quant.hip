@@ -25,31 +25,34 @@
 namespace rra {
 
 // One row lane's share of a row: vector i covers columns (i * stride + rl) * 8.
+// kFull: the row is exactly NV * stride vectors, so every index is in range
+// and the per-vector bounds tests (which cost measurably in these short,
+// latency-bound kernels) are compiled out.
 template <int NV>
 struct RowVecs {
   u32x4 v[NV];
 };
 
-template <int NV, bool kStream>
+template <int NV, bool kStream, bool kFull>
 __device__ __forceinline__ void load_row(RowVecs<NV>& r, const uint16_t* base, int nvec, int rl,
                                          int stride, bool active) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = i * stride + rl;
-    if (active && idx < nvec)
+    if (active && (kFull || idx < nvec))
       r.v[i] = kStream ? ld_stream(base + idx * 8) : ld_cached(base + idx * 8);
     else
       r.v[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-template <int NV>
+template <int NV, bool kFull>
 __device__ __forceinline__ void store_row(uint16_t* base, const RowVecs<NV>& r, int nvec, int rl,
                                          int stride) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = i * stride + rl;
-    if (idx < nvec) st_stream(base + idx * 8, r.v[i]);
+    if (kFull || idx < nvec) st_stream(base + idx * 8, r.v[i]);
   }
 }
 
@@ -122,7 +125,7 @@ __device__ __forceinline__ void row_reduce(double& ss, float& m, double* lds_ss,
 // needs no second pass over y, and the codes are e4m3fn(t * rho / s) (quant8
 // rounds them as the exact quotient would).  kMode and kGroup (64 or 128 for
 // per-group scales, else 0) are compile-time, so group indexing is a shift.
-template <int NV, int kMode, int kGroup, typename E = ElemBf16>
+template <int NV, int kMode, int kGroup, bool kFull, typename E = ElemBf16>
 __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float m_row,
                                              float eps, int H, int nvec, int rl, int stride,
                                              float static_scale, void* out, float* scale_row) {
@@ -141,7 +144,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
                          E::pack(ti[2] * rho_f, ti[3] * rho_f),
                          E::pack(ti[4] * rho_f, ti[5] * rho_f),
                          E::pack(ti[6] * rho_f, ti[7] * rho_f)};
-      if (idx < nvec) st_stream(o + idx * 8, packed);
+      if (kFull || idx < nvec) st_stream(o + idx * 8, packed);
     }
     return;
   }
@@ -157,7 +160,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
       for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t.t[i][j]));
       m = kGroup == 128 ? max16(m) : max8(m);
       const QuantStep qs = quant_step(rho, dynamic_scale(m, rho));
-      if (idx < nvec) {
+      if (kFull || idx < nvec) {
         if ((lane & (kLanesPerGroup - 1)) == 0) scale_row[idx / kLanesPerGroup] = qs.s;
         st_stream(o + idx * 8, quant8<false>(t.t[i], qs));
       }
@@ -172,7 +175,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = i * stride + rl;
-      if (idx < nvec) st_stream(o + idx * 8, quant8<false>(t.t[i], qs));
+      if (kFull || idx < nvec) st_stream(o + idx * 8, quant8<false>(t.t[i], qs));
     }
     return;
   }
@@ -181,7 +184,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = i * stride + rl;
-    if (idx < nvec) st_stream(o + idx * 8, quant8<true>(t.t[i], qs));
+    if (kFull || idx < nvec) st_stream(o + idx * 8, quant8<true>(t.t[i], qs));
   }
 }
 
@@ -190,7 +193,8 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
 // kMode NONE writes the norm to out (uint16_t, element type E) and +0 to its
 // columns [H, H_pad) (the padding variant); the quantizing modes write FP8
 // codes (uint8_t) from bf16 inputs and take H_pad = H.
-template <int NV, int kW, bool kResidual, int kMode, int kGroup, typename E = ElemBf16>
+template <int NV, int kW, bool kResidual, int kMode, int kGroup, bool kFull,
+          typename E = ElemBf16>
 __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x, int64_t x_stride,
                                                  uint16_t* __restrict__ residual,
                                                  int64_t res_stride,
@@ -207,13 +211,15 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   const int wave_in_row = wave % kW;
   const int rl = wave_in_row * kWave + lane_id();
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave / kW;
-  const bool active = row < T;
+  // With one row per workgroup the grid has exactly T blocks.
+  const bool active = kRowsPerBlock == 1 || row < T;
   const int nvec = H >> 3;
 
   RowVecs<NV> a, r, w;
-  load_row<NV, true>(a, x + row * x_stride, nvec, rl, kStride, active);
-  if (kResidual) load_row<NV, true>(r, residual + row * res_stride, nvec, rl, kStride, active);
-  load_row<NV, false>(w, weight, nvec, rl, kStride, true);
+  load_row<NV, true, kFull>(a, x + row * x_stride, nvec, rl, kStride, active);
+  if (kResidual)
+    load_row<NV, true, kFull>(r, residual + row * res_stride, nvec, rl, kStride, active);
+  load_row<NV, false, kFull>(w, weight, nvec, rl, kStride, true);
   const float sscale = kMode == RRA_Q_STATIC ? static_scale[0] : 0.0f;
 
   if (kResidual) {
@@ -227,7 +233,7 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
         a.v[i][k] = E::pack(E::lo(a.v[i][k]) + E::lo(r.v[i][k]),
                             E::hi(a.v[i][k]) + E::hi(r.v[i][k]));
     }
-    if (active) store_row(residual + row * res_stride, a, nvec, rl, kStride);
+    if (active) store_row<NV, kFull>(residual + row * res_stride, a, nvec, rl, kStride);
   }
 
   RowT<NV> t;
@@ -239,21 +245,23 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
 
   if constexpr (kMode == RRA_Q_NONE) {
     uint16_t* o = static_cast<uint16_t*>(out) + row * out_stride;
-    rmsnorm_emit<NV, RRA_Q_NONE, 0, E>(t, ss, m, eps, H, nvec, rl, kStride, 0.0f, o, nullptr);
+    rmsnorm_emit<NV, RRA_Q_NONE, 0, kFull, E>(t, ss, m, eps, H, nvec, rl, kStride, 0.0f, o,
+                                              nullptr);
     for (int idx = nvec + rl; idx < (H_pad >> 3); idx += kStride)
       st_stream(o + idx * 8, u32x4{0u, 0u, 0u, 0u});
   } else {
     float* scale_row = nullptr;
     if (kMode == RRA_Q_PER_TOKEN) scale_row = scales + row;
     if (kMode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / kGroup);
-    rmsnorm_emit<NV, kMode, kGroup>(t, ss, m, eps, H, nvec, rl, kStride, sscale,
-                                    static_cast<uint8_t*>(out) + row * out_stride, scale_row);
+    rmsnorm_emit<NV, kMode, kGroup, kFull>(t, ss, m, eps, H, nvec, rl, kStride, sscale,
+                                           static_cast<uint8_t*>(out) + row * out_stride,
+                                           scale_row);
   }
 }
 
 // Two entry kernels over the same body, so that profiles tell the quantizing
 // op from the padding op.
-template <int NV, int kW, bool kResidual, int kMode, int kGroup>
+template <int NV, int kW, bool kResidual, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
     add_rmsnorm_quant_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                              uint16_t* __restrict__ residual, int64_t res_stride,
@@ -261,21 +269,22 @@ __global__ void __launch_bounds__(kBlock)
                              const float* __restrict__ static_scale,
                              uint8_t* __restrict__ out, int64_t out_stride,
                              float* __restrict__ scales, int64_t T, int H) {
-  add_rmsnorm_body<NV, kW, kResidual, kMode, kGroup>(x, x_stride, residual, res_stride, weight,
-                                                     eps, static_scale, out, out_stride, scales,
-                                                     T, H, H);
+  add_rmsnorm_body<NV, kW, kResidual, kMode, kGroup, kFull>(x, x_stride, residual, res_stride,
+                                                            weight, eps, static_scale, out,
+                                                            out_stride, scales, T, H, H);
 }
 
-template <int NV, int kW, bool kResidual, typename E>
+template <int NV, int kW, bool kResidual, bool kFull, typename E>
 __global__ void __launch_bounds__(kBlock)
     add_rmsnorm_pad_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                            uint16_t* __restrict__ residual, int64_t res_stride,
                            const uint16_t* __restrict__ weight, float eps,
                            uint16_t* __restrict__ out, int64_t out_stride, int64_t T, int H,
                            int H_pad) {
-  add_rmsnorm_body<NV, kW, kResidual, RRA_Q_NONE, 0, E>(x, x_stride, residual, res_stride,
-                                                        weight, eps, nullptr, out, out_stride,
-                                                        nullptr, T, H, H_pad);
+  add_rmsnorm_body<NV, kW, kResidual, RRA_Q_NONE, 0, kFull, E>(x, x_stride, residual,
+                                                               res_stride, weight, eps, nullptr,
+                                                               out, out_stride, nullptr, T, H,
+                                                               H_pad);
 }
 
 // MLA dual RMSNorm: the q and kv latents of a token are two rows handled by
@@ -284,7 +293,7 @@ __global__ void __launch_bounds__(kBlock)
 // wave per token (four tokens per workgroup) beats spreading a token over
 // more waves: the rows are short, and a barrier per token costs more than the
 // extra vectors per lane.
-template <int NVQ, int NVKV, int kW, int kMode, int kGroup>
+template <int NVQ, int NVKV, int kW, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
     dual_rmsnorm_quant_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
                               const uint16_t* __restrict__ q_w, float eps_q,
@@ -302,16 +311,18 @@ __global__ void __launch_bounds__(kBlock)
   const int wave_in_row = wave % kW;
   const int rl = wave_in_row * kWave + lane_id();
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave / kW;
-  const bool active = row < T;
+  // With one wave per token there is no barrier: waves past T leave at once.
+  if (kW == 1 && row >= T) return;
+  const bool active = kW == 1 || row < T;
   const int nq = Hq >> 3, nkv = Hkv >> 3;
 
   // Issue every load of the token before either reduction.
   RowVecs<NVQ> zq, wq;
   RowVecs<NVKV> zkv, wkv;
-  load_row<NVQ, true>(zq, q + row * q_stride, nq, rl, kStride, active);
-  load_row<NVKV, true>(zkv, kv + row * kv_stride, nkv, rl, kStride, active);
-  load_row<NVQ, false>(wq, q_w, nq, rl, kStride, true);
-  load_row<NVKV, false>(wkv, kv_w, nkv, rl, kStride, true);
+  load_row<NVQ, true, kFull>(zq, q + row * q_stride, nq, rl, kStride, active);
+  load_row<NVKV, true, kFull>(zkv, kv + row * kv_stride, nkv, rl, kStride, active);
+  load_row<NVQ, false, kFull>(wq, q_w, nq, rl, kStride, true);
+  load_row<NVKV, false, kFull>(wkv, kv_w, nkv, rl, kStride, true);
 
   RowT<NVQ> tq;
   RowT<NVKV> tkv;
@@ -350,10 +361,10 @@ __global__ void __launch_bounds__(kBlock)
     qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
     scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
   }
-  rmsnorm_emit<NVQ, kMode, kGroup>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, 0.0f, qo,
-                                   scale_row);
-  rmsnorm_emit<NVKV, RRA_Q_NONE, 0>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kStride, 0.0f,
-                                    kv_out + row * kv_out_stride, nullptr);
+  rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, 0.0f, qo,
+                                          scale_row);
+  rmsnorm_emit<NVKV, RRA_Q_NONE, 0, kFull>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kStride, 0.0f,
+                                           kv_out + row * kv_out_stride, nullptr);
 }
 
 // Waves per row for the residual-add norm: enough that each lane holds at
@@ -378,16 +389,17 @@ struct NormLaunch {
   int H, H_pad;
 };
 
-template <int N, int W, bool kResidual, int kMode, int kGroup>
+template <int N, int W, bool kResidual, bool kFull, int kMode, int kGroup>
 static void launch_norm_quant(const NormLaunch& a) {
-  hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual, kMode, kGroup>), a.grid,
+  hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual, kMode, kGroup, kFull>), a.grid,
                      dim3(kBlock), 0, a.st, a.x, a.xs, a.res, a.rs, a.w, a.eps, a.sscale,
                      static_cast<uint8_t*>(a.out), a.os, a.scales, a.T, a.H);
 }
 
-template <int N, int W, bool kResidual, typename E>
+template <int N, int W, bool kResidual, bool kFull, typename E>
 static void launch_norm_pad(const NormLaunch& a) {
-  hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, E>), a.grid, dim3(kBlock), 0, a.st,
+  hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, kFull, E>), a.grid, dim3(kBlock), 0,
+                     a.st,
                      a.x, a.xs, a.res, a.rs, a.w, a.eps, static_cast<uint16_t*>(a.out), a.os,
                      a.T, a.H, a.H_pad);
 }
@@ -395,23 +407,32 @@ static void launch_norm_pad(const NormLaunch& a) {
 // One (vectors per lane, waves per row) case: mode NONE launches the padding
 // kernel (out in the element type dtype, columns [H, H_pad) zeroed), the
 // quantizing modes the quant kernel for that mode and group size (bf16 in).
-template <int N, int W, bool kResidual>
-static void launch_norm_case(const NormLaunch& a, int mode, int group, int dtype) {
+template <int N, int W, bool kResidual, bool kFull>
+static void launch_norm_mode(const NormLaunch& a, int mode, int group, int dtype) {
   switch (mode) {
     case RRA_Q_NONE:
       if (dtype == RRA_F16)
-        launch_norm_pad<N, W, kResidual, ElemF16>(a);
+        launch_norm_pad<N, W, kResidual, kFull, ElemF16>(a);
       else
-        launch_norm_pad<N, W, kResidual, ElemBf16>(a);
+        launch_norm_pad<N, W, kResidual, kFull, ElemBf16>(a);
       break;
-    case RRA_Q_STATIC: launch_norm_quant<N, W, kResidual, RRA_Q_STATIC, 0>(a); break;
-    case RRA_Q_PER_TOKEN: launch_norm_quant<N, W, kResidual, RRA_Q_PER_TOKEN, 0>(a); break;
+    case RRA_Q_STATIC: launch_norm_quant<N, W, kResidual, kFull, RRA_Q_STATIC, 0>(a); break;
+    case RRA_Q_PER_TOKEN: launch_norm_quant<N, W, kResidual, kFull, RRA_Q_PER_TOKEN, 0>(a); break;
     default:
       if (group == 64)
-        launch_norm_quant<N, W, kResidual, RRA_Q_PER_GROUP, 64>(a);
+        launch_norm_quant<N, W, kResidual, kFull, RRA_Q_PER_GROUP, 64>(a);
       else
-        launch_norm_quant<N, W, kResidual, RRA_Q_PER_GROUP, 128>(a);
+        launch_norm_quant<N, W, kResidual, kFull, RRA_Q_PER_GROUP, 128>(a);
   }
+}
+
+// The row fills the N * 64 * W vectors of a lane's share exactly, or not.
+template <int N, int W, bool kResidual>
+static void launch_norm_case(const NormLaunch& a, int mode, int group, int dtype) {
+  if (a.H == N * 8 * kWave * W)
+    launch_norm_mode<N, W, kResidual, true>(a, mode, group, dtype);
+  else
+    launch_norm_mode<N, W, kResidual, false>(a, mode, group, dtype);
 }
 
 template <bool kResidual>
@@ -459,24 +480,34 @@ struct DualLaunch {
   int Hq, Hkv;
 };
 
-template <int A, int B, int kMode, int kGroup>
+template <int A, int B, bool kFull, int kMode, int kGroup>
 static void launch_dual(const DualLaunch& a) {
-  hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, 1, kMode, kGroup>), a.grid, dim3(kBlock), 0,
+  hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, 1, kMode, kGroup, kFull>), a.grid,
+                     dim3(kBlock), 0,
                      a.st, a.q, a.qs, a.qw, a.eps_q, a.kv, a.kvs, a.kvw, a.eps_kv, a.q_out, a.qos,
                      a.q_scales, a.kv_out, a.kvos, a.T, a.Hq, a.Hkv);
 }
 
-template <int A, int B>
-static void launch_dual_case(const DualLaunch& a, int mode, int group) {
+template <int A, int B, bool kFull>
+static void launch_dual_mode(const DualLaunch& a, int mode, int group) {
   switch (mode) {
-    case RRA_Q_NONE: launch_dual<A, B, RRA_Q_NONE, 0>(a); break;
-    case RRA_Q_PER_TOKEN: launch_dual<A, B, RRA_Q_PER_TOKEN, 0>(a); break;
+    case RRA_Q_NONE: launch_dual<A, B, kFull, RRA_Q_NONE, 0>(a); break;
+    case RRA_Q_PER_TOKEN: launch_dual<A, B, kFull, RRA_Q_PER_TOKEN, 0>(a); break;
     default:
       if (group == 64)
-        launch_dual<A, B, RRA_Q_PER_GROUP, 64>(a);
+        launch_dual<A, B, kFull, RRA_Q_PER_GROUP, 64>(a);
       else
-        launch_dual<A, B, RRA_Q_PER_GROUP, 128>(a);
+        launch_dual<A, B, kFull, RRA_Q_PER_GROUP, 128>(a);
   }
+}
+
+// Both rows fill their A (B) vectors per lane exactly, or not.
+template <int A, int B>
+static void launch_dual_case(const DualLaunch& a, int mode, int group) {
+  if (a.Hq == A * 8 * kWave && a.Hkv == B * 8 * kWave)
+    launch_dual_mode<A, B, true>(a, mode, group);
+  else
+    launch_dual_mode<A, B, false>(a, mode, group);
 }
 
 }  // namespace rra

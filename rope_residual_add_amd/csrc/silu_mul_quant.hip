@@ -39,8 +39,9 @@ __device__ __forceinline__ void silu8(u32x4 g, u32x4 u, float a[8]) {
 }
 
 // kMode RRA_Q_STATIC or RRA_Q_PER_GROUP with kGroup 64 or 128 (compile-time,
-// so group indexing is a shift).
-template <int NV, int kMode, int kGroup>
+// so group indexing is a shift).  kFull: I is a whole number of chunks, so
+// every vector index is in range and the bounds tests are compiled out.
+template <int NV, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
     silu_mul_quant_kernel(const uint16_t* __restrict__ in, int64_t in_stride,
                           const float* __restrict__ static_scale,
@@ -60,7 +61,7 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = (chunk * NV + i) * kWave + lane;
-    if (idx < nvec) {
+    if (kFull || idx < nvec) {
       g[i] = ld_stream(gate + idx * 8);
       u[i] = ld_stream(up + idx * 8);
     } else {
@@ -77,7 +78,7 @@ __global__ void __launch_bounds__(kBlock)
       const int idx = (chunk * NV + i) * kWave + lane;
       float a[8];
       silu8(g[i], u[i], a);
-      if (idx < nvec)
+      if (kFull || idx < nvec)
         st_stream(o + idx * 8,
                   u32x2{pack_e4m3x4(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
                         pack_e4m3x4(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
@@ -99,7 +100,7 @@ __global__ void __launch_bounds__(kBlock)
       // correctly rounded divisions would buy nothing here.
       const float s = m * (1.0f / 448.0f);
       const float f = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
-      if (idx < nvec) {
+      if (kFull || idx < nvec) {
         if ((lane & (kLanesPerGroup - 1)) == 0) scale_row[idx / kLanesPerGroup] = s;
         // |a * f| <= 448 within rounding: no saturation needed
         st_stream(o + idx * 8, u32x2{pack_e4m3x4<false>(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
@@ -110,6 +111,37 @@ __global__ void __launch_bounds__(kBlock)
 }
 
 constexpr int kSiluNV = 4;  // 2048 output columns per wavefront
+
+// Arguments of one launch.
+struct SiluLaunch {
+  dim3 grid;
+  hipStream_t st;
+  const uint16_t* in;
+  int64_t in_stride;
+  const float* static_scale;
+  uint8_t* out;
+  int64_t out_stride;
+  float* scales;
+  int64_t T;
+  int I, chunks;
+};
+
+template <bool kFull, int kMode, int kGroup>
+static void launch_silu(const SiluLaunch& a) {
+  hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV, kMode, kGroup, kFull>), a.grid, dim3(kBlock),
+                     0, a.st, a.in, a.in_stride, a.static_scale, a.out, a.out_stride, a.scales,
+                     a.T, a.I, a.chunks);
+}
+
+template <bool kFull>
+static void launch_silu_mode(const SiluLaunch& a, int mode, int group) {
+  if (mode == RRA_Q_STATIC)
+    launch_silu<kFull, RRA_Q_STATIC, 0>(a);
+  else if (group == 64)
+    launch_silu<kFull, RRA_Q_PER_GROUP, 64>(a);
+  else
+    launch_silu<kFull, RRA_Q_PER_GROUP, 128>(a);
+}
 
 }  // namespace rra
 
@@ -144,18 +176,12 @@ extern "C" int silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_m
   const int64_t chunks = ceil_div(I, 8 * kWave * kSiluNV);
   const int64_t blocks = ceil_div(T * chunks, kWavesPerBlock);
   RRA_REQUIRE(blocks <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
-  const dim3 grid(static_cast<unsigned>(blocks));
-  const hipStream_t st = as_stream(stream);
-  const int i32 = static_cast<int>(I), c32 = static_cast<int>(chunks);
-  if (quant_mode == RRA_Q_STATIC)
-    hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV, RRA_Q_STATIC, 0>), grid, dim3(kBlock), 0,
-                       st, in, in_stride, static_scale, out, out_stride, scales, T, i32, c32);
-  else if (group_size == 64)
-    hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV, RRA_Q_PER_GROUP, 64>), grid, dim3(kBlock),
-                       0, st, in, in_stride, static_scale, out, out_stride, scales, T, i32, c32);
+  const SiluLaunch a{dim3(static_cast<unsigned>(blocks)), as_stream(stream), in, in_stride,
+                     static_scale, out, out_stride, scales, T, static_cast<int>(I),
+                     static_cast<int>(chunks)};
+  if (I == chunks * 8 * kWave * kSiluNV)
+    launch_silu_mode<true>(a, quant_mode, group_size);
   else
-    hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV, RRA_Q_PER_GROUP, 128>), grid,
-                       dim3(kBlock), 0, st, in, in_stride, static_scale, out, out_stride, scales,
-                       T, i32, c32);
+    launch_silu_mode<false>(a, quant_mode, group_size);
   return launch_status();
 }
