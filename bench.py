@@ -96,6 +96,26 @@ def algo_bytes(name: str, T: int) -> int:
     return BYTES_PER_TOKEN[name] * T + BYTES_PER_LAUNCH[name]
 
 
+# Work-items per launch at T tokens, as the library launches these workloads
+# (256-lane workgroups): one row or token per workgroup for the residual-add
+# norms (four waves per row at widths above 2048) and the RoPE family, four
+# tokens per workgroup for the MLA norm, one wave per 2048 SiLU outputs.  Used
+# only to tell the sweep's launches apart in a kernel trace.
+def grid_threads(name: str, T: int) -> int:
+    if name == "silu_mul_quant":
+        blocks = -(-(T * -(-I_SILU // 2048)) // 4)
+    elif name == "dual_rmsnorm_quant":
+        blocks = -(-T // 4)
+    else:
+        blocks = T
+    return 256 * blocks
+
+
+def copy_half_bytes(nbytes_moved: int) -> int:
+    """Bytes read (= bytes written) by the same-size copy yardstick."""
+    return max(16, (nbytes_moved // 2) // 16 * 16)
+
+
 # ---- kernel identity: symbols and sources ----------------------------------------
 
 CSRC = os.path.join(ROOT, "rope_residual_add_amd", "csrc")
@@ -364,37 +384,84 @@ def _blocker_cycles(target_ms: float = 5.0) -> int:
 
 
 def copy_ceiling(nbytes: int = 1 << 30, n_pairs: int = 4, reps: int = 12) -> dict:
-    """Plain device copy (torch copy_) of nbytes, rotating over n_pairs of
-    buffers (8 GiB in all) so it streams from HBM: read + write bytes / time."""
+    """The library's streaming copy (same 16-byte loads and stores, same cache
+    policy as the fused kernels) of nbytes, rotating over n_pairs of buffers
+    (8 GiB in all) so that it streams from HBM: read + write bytes / time."""
     import torch
+
+    import rope_residual_add_amd as rra
 
     src = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device="cuda") for i in range(n_pairs)]
     dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n_pairs)]
     for i in range(n_pairs):
-        dst[i].copy_(src[i])
+        rra.stream_copy(src[i], dst[i])
     cyc = _blocker_cycles()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = hip.create(2)
     torch.cuda._sleep(cyc)
-    a.record()
+    hip.record(ev[0], stream)
     for r in range(reps):
-        dst[r % n_pairs].copy_(src[r % n_pairs])
-    b.record()
+        rra.stream_copy(src[r % n_pairs], dst[r % n_pairs])
+    hip.record(ev[1], stream)
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    ms = hip.ms(ev[0], ev[1]) / reps
+    hip.destroy(ev)
     gbps = 2 * nbytes / (ms * 1e-3) / 1e9
-    log(f"copy ceiling: {nbytes >> 20} MiB copy_ {ms * 1e3:.1f} us -> {gbps:.1f} GB/s "
+    log(f"copy ceiling: {nbytes >> 20} MiB stream copy {ms * 1e3:.1f} us -> {gbps:.1f} GB/s "
         f"({100 * gbps / PEAK_HBM_GBPS:.1f}% of 8 TB/s)")
     del src, dst
     torch.cuda.empty_cache()
     return dict(gbps=round(gbps, 1), frac_of_peak=round(gbps / PEAK_HBM_GBPS, 4),
-                what=f"torch copy_ of {nbytes >> 20} MiB (read + write bytes), {n_pairs} "
-                     f"rotating buffer pairs")
+                what=f"rra_stream_copy of {nbytes >> 20} MiB (read + write bytes), {n_pairs} "
+                     f"rotating buffer pairs, {reps} launches back to back")
 
 
-def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS):
+def _timed_launches(hip, stream, cyc, fns, n: int) -> float:
+    """Median ms of n launches, fns[j % len(fns)] for launch j, each bracketed
+    by events and all queued behind a spin kernel."""
+    import torch
+
+    ev = hip.create(2 * n)
+    torch.cuda._sleep(cyc)  # queue the timed launches behind a spin kernel
+    for j in range(n):
+        hip.record(ev[2 * j], stream)
+        fns[j % len(fns)]()
+        hip.record(ev[2 * j + 1], stream)
+    torch.cuda.synchronize()
+    ms = statistics.median(hip.ms(ev[2 * j], ev[2 * j + 1]) for j in range(n))
+    hip.destroy(ev)
+    return ms
+
+
+def copy_yardstick(nbytes_moved: int, launches: int, hip, stream, cyc) -> float:
+    """Median ms of a streaming copy that moves nbytes_moved bytes in all
+    (half read, half written), cold, timed like the sweep's kernels."""
+    import torch
+
+    import rope_residual_add_amd as rra
+
+    half = copy_half_bytes(nbytes_moved)
+    n_sets = max(2, min(256, -(-(1 << 30) // (2 * half))))
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
+             torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(n_sets)]
+    fns = [lambda a=a, b=b: rra.stream_copy(a, b) for a, b in bufs]
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    ms = _timed_launches(hip, stream, cyc, fns, launches)
+    del bufs, fns
+    torch.cuda.empty_cache()
+    return ms
+
+
+def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS, with_copy: bool = True):
     """Each kernel alone at each T, rotating over buffer sets of that kernel
     that total at least 1 GiB of algorithmic traffic (four times the 256 MB
-    last-level cache), so every launch reads cold data."""
+    last-level cache), so every launch reads cold data.  With with_copy, each
+    point is also compared with the library's streaming copy moving the same
+    number of bytes (half read, half written), timed the same way: the
+    achievable rate at that size, launch and ramp included."""
     import torch
 
     rows = []
@@ -413,24 +480,22 @@ def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS):
             for s in sets:  # warm-up: one launch per set
                 s[n]()
             torch.cuda.synchronize()
-            ev = hip.create(2 * launches_per_point)
-            torch.cuda._sleep(cyc)  # queue the timed launches behind a spin kernel
-            for j in range(launches_per_point):
-                hip.record(ev[2 * j], stream)
-                sets[j % n_sets][n]()
-                hip.record(ev[2 * j + 1], stream)
-            torch.cuda.synchronize()
-            ms = statistics.median(hip.ms(ev[2 * j], ev[2 * j + 1])
-                                   for j in range(launches_per_point))
-            hip.destroy(ev)
-            gbps = algo_bytes(n, T) / (ms * 1e-3) / 1e9
-            rows.append(dict(kernel=n, T=T, us=round(ms * 1e3, 2), gbps=round(gbps, 1),
-                             frac=round(gbps / PEAK_HBM_GBPS, 4),
-                             tokens_per_s=round(T / (ms * 1e-3), 1), buffer_sets=n_sets))
-            log(f"sweep {n:26s} T={T:6d} {ms * 1e3:9.2f} us {gbps:8.1f} GB/s "
-                f"({100 * gbps / PEAK_HBM_GBPS:5.1f}% of peak), {n_sets} buffer sets")
+            ms = _timed_launches(hip, stream, cyc, [s[n] for s in sets], launches_per_point)
             del sets
             torch.cuda.empty_cache()
+            b = algo_bytes(n, T)
+            gbps = b / (ms * 1e-3) / 1e9
+            row = dict(kernel=n, T=T, us=round(ms * 1e3, 2), gbps=round(gbps, 1),
+                       frac=round(gbps / PEAK_HBM_GBPS, 4),
+                       tokens_per_s=round(T / (ms * 1e-3), 1), buffer_sets=n_sets)
+            if with_copy:
+                cms = copy_yardstick(b, launches_per_point, hip, stream, cyc)
+                row.update(copy_us=round(cms * 1e3, 2), frac_of_copy=round(cms / ms, 4))
+            rows.append(row)
+            log(f"sweep {n:26s} T={T:6d} {ms * 1e3:9.2f} us {gbps:8.1f} GB/s "
+                f"({100 * gbps / PEAK_HBM_GBPS:5.1f}% of peak), {n_sets} buffer sets"
+                + (f"; same-size copy {row['copy_us']:8.2f} us ({100 * row['frac_of_copy']:5.1f}%)"
+                   if with_copy else ""))
     return rows
 
 
@@ -524,8 +589,8 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int) -> None:
 
 def summarize_traffic(fetch_csv: str, write_csv: str, out: str, commands: str, T: int) -> None:
     """HBM traffic per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
-    scaled by what the same counters read for the runtime's copy kernel on the
-    bench's 1 GiB copy (read and written bytes known)."""
+    scaled by what the same counters read for the library's streaming copy of
+    1 GiB in the bench's copy ceiling (read and written bytes known)."""
     import collections
     import csv
 
@@ -537,16 +602,16 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out: str, commands: str, T
         return d
 
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
-    copy = [n for n in fetch if "copyBuffer" in n]
+    copy = [n for n in fetch if "rra::stream_copy_kernel" in n]
     if not copy:
-        raise SystemExit("no copy kernel in the counter run")
+        raise SystemExit("no streaming copy in the counter run")
     gib_kib = float(1 << 20)
     f_copy = statistics.median(v for v in fetch[copy[0]] if v > 0.4 * gib_kib)
     w_copy = statistics.median(v for v in write[copy[0]] if v > 0.4 * gib_kib)
     f_scale, w_scale = gib_kib / f_copy, gib_kib / w_copy
     lines = [f"# HBM traffic per launch at T={T} (rocprofv3 counters)", "",
              "Produced by (from the repository root):", "", "```", commands, "```", "",
-             f"Scale factors from the runtime copy kernel (`{copy[0].split('(')[0]}`) moving "
+             f"Scale factors from the library's streaming copy (`{copy[0].split('(')[0]}`) moving "
              f"1 GiB in the same runs: FETCH_SIZE reads {f_copy:.0f} KiB for 1 GiB read "
              f"(x{f_scale:.4f}), WRITE_SIZE reads {w_copy:.0f} KiB for 1 GiB written "
              f"(x{w_scale:.4f}).", "",
@@ -569,6 +634,54 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out: str, commands: str, T
     print("\n".join(lines))
 
 
+def summarize_sweep(trace_csv: str, out: str, command: str, Ts, kernels=KERNELS) -> None:
+    """Sweep summary from a rocprofv3 kernel trace of `bench.py --sweep-only`:
+    per kernel and T, the median profiler duration of its launches (told apart
+    by grid size), against the median of the same-size streaming copy."""
+    import collections
+    import csv
+
+    dur = collections.defaultdict(list)  # (kernel or "copy", grid work-items) -> ns
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"]
+        k = "copy" if "rra::stream_copy_kernel" in name else _kernel_of(name)
+        if k is None:
+            continue
+        dur[(k, int(r["Grid_Size_X"]))].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+
+    def copy_grid(nbytes_moved):
+        return 256 * -(-(copy_half_bytes(nbytes_moved) // 16) // 256)
+
+    lines = ["# Kernel trace: each fused kernel alone, cold, across token counts", "",
+             "Produced by (from the repository root, after `cd /tmp && export TMPDIR=/tmp` for "
+             "the profiler):", "", "```", command, "```", "",
+             "Each point rotates over buffer sets holding at least 1 GiB, so every launch reads "
+             "cold data. Durations are the profiler's (median over the point's launches). "
+             "`copy` is the library's streaming copy (`rra_stream_copy`, the fused kernels' own "
+             "loads and stores) moving the same number of bytes, half read and half written, "
+             "timed the same way; `% of copy` = copy time / kernel time.", "",
+             "| kernel | T | launches | median us | GB/s | % of 8 TB/s | tokens/s | copy us | "
+             "% of copy |", "|---|---|---|---|---|---|---|---|---|"]
+    for T in Ts:
+        for k in kernels:
+            d = dur.get((k, grid_threads(k, T)))
+            if not d:
+                continue
+            med = statistics.median(d)
+            b = algo_bytes(k, T)
+            c = dur.get(("copy", copy_grid(b)))
+            cmed = statistics.median(c) if c else None
+            lines.append(f"| {k} | {T} | {len(d)} | {med / 1e3:.2f} | {b / med:.0f} | "
+                         f"{100 * b / med / PEAK_HBM_GBPS:.1f}% | {T / (med * 1e-9):.3g} | "
+                         + (f"{cmed / 1e3:.2f} | {100 * cmed / med:.1f}% |" if cmed else "- | - |"))
+    floor = dur.get(("copy", copy_grid(8192)))
+    if floor:
+        lines += ["", f"One-workgroup copy (launch floor), profiler median: "
+                      f"{statistics.median(floor) / 1e3:.2f} us over {len(floor)} launches."]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ---- main ------------------------------------------------------------------------
 
 def main() -> int:
@@ -585,6 +698,10 @@ def main() -> int:
                     help="1 = also time the next-row kernels alone at T (cold, rotating sets)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="write a profiles/ summary from a rocprofv3 --stats run and exit")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="run only the --sweep (no step, ceiling or baseline): for profiling")
+    ap.add_argument("--summarize-sweep", metavar="KERNEL_TRACE_CSV",
+                    help="write a profiles/ summary of a traced --sweep-only run and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write a profiles/ summary from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--out", help="output file for --summarize-*")
@@ -596,6 +713,10 @@ def main() -> int:
         return 0
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.out, args.command, args.T)
+        return 0
+    if args.summarize_sweep:
+        summarize_sweep(args.summarize_sweep, args.out, args.command,
+                        [int(t) for t in args.sweep.split(",") if t])
         return 0
 
     if args.gpus != 1:
@@ -613,6 +734,12 @@ def main() -> int:
         return 1
     rra.lib()  # fail loudly if the HIP library is missing
     T = args.T
+    if args.sweep_only:
+        rows = sweep([int(t) for t in args.sweep.split(",") if t])
+        hip = HipEvents()
+        copy_yardstick(8192, 30, hip, torch.cuda.current_stream().cuda_stream, _blocker_cycles())
+        print(json.dumps(dict(sweep=rows)), flush=True)
+        return 0
     log(f"device: {torch.cuda.get_device_name(0)}; T={T}; steps={args.steps}; "
         f"warmup={args.warmup}")
     launch = make_launchers(T)
@@ -658,6 +785,11 @@ def main() -> int:
                                for r in sweep([T], kernels=NEXT_KERNELS)}
     if args.sweep:
         result["sweep"] = sweep([int(t) for t in args.sweep.split(",") if t])
+        hip = HipEvents()
+        floor_ms = copy_yardstick(8192, 30, hip, torch.cuda.current_stream().cuda_stream,
+                                  _blocker_cycles())
+        result["launch_floor_us"] = round(floor_ms * 1e3, 2)
+        log(f"launch floor (one-workgroup copy, timed as the sweep): {floor_ms * 1e3:.2f} us")
     if args.cpu_sample > 0:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample)
     else:

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RRA_ABI_VERSION 2
+#define RRA_ABI_VERSION 3
 
 enum rra_status {
   RRA_OK = 0,
@@ -293,6 +293,17 @@ int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64_t q_stride
  * in: [n] fp32, 16-byte aligned; out: [n] bytes, 4-byte aligned.
  */
 int rra_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+
+/*
+ * Diagnostic: dst[0:nbytes) = src[0:nbytes), one 16-byte vector per lane,
+ * loaded and stored with the same streaming cache policy as the fused kernels'
+ * activations.  It is the bandwidth yardstick the fused kernels are measured
+ * against (a copy of the same number of bytes at the same size).
+ * src, dst: device pointers, 16-byte aligned; nbytes % 16 == 0 (else
+ * RRA_ERR_ALIGN); the two ranges must not overlap (else RRA_ERR_SHAPE).
+ * nbytes == 0 launches nothing.
+ */
+int rra_stream_copy(const void* src, void* dst, int64_t nbytes, void* stream);
 
 #ifdef __cplusplus
 }

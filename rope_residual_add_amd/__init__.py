@@ -24,7 +24,7 @@ _QUANT_NAMES = {"none": Q_NONE, "static": Q_STATIC, "per_token": Q_PER_TOKEN,
 
 EXPORTS = ("rra_abi_version", "rra_status_string", "fused_add_rmsnorm_quant", "silu_mul_quant",
            "rope_cos_sin_cache", "rope_kv_write", "dual_rmsnorm_quant", "qk_norm_rope_kv_write",
-           "fused_add_rmsnorm_pad", "mla_rope_kv_write", "rra_e4m3fn_encode")
+           "fused_add_rmsnorm_pad", "mla_rope_kv_write", "rra_e4m3fn_encode", "rra_stream_copy")
 
 
 class RRAError(RuntimeError):
@@ -33,7 +33,7 @@ class RRAError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 2  # RRA_ABI_VERSION of include/rra.h
+ABI_VERSION = 3  # RRA_ABI_VERSION of include/rra.h
 BF16, F16 = 0, 1  # enum rra_dtype
 _ELEM = {torch.bfloat16: BF16, torch.float16: F16}
 
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.mla_rope_kv_write.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p,
                                         _i64, _i32, _i32, _i32, _i32, _i64, _i32, _p]
         L.rra_e4m3fn_encode.argtypes = [_p, _p, _i64, _p]
+        L.rra_stream_copy.argtypes = [_p, _p, _i64, _p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = _i32
         _lib = L
@@ -379,3 +380,20 @@ def e4m3fn_encode(x, out=None):
         st = lib().rra_e4m3fn_encode(_ptr(x), _ptr(out), x.numel(), _stream(x))
     _check("rra_e4m3fn_encode", st)
     return out
+
+
+def stream_copy(src, dst):
+    """dst <- src (same byte size, contiguous, non-overlapping) with the fused
+    kernels' streaming loads and stores: the bandwidth yardstick (diagnostic)."""
+    for name, t in (("src", src), ("dst", dst)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("stream_copy: src and dst differ in size")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("stream_copy: src and dst must be contiguous")
+    with torch.cuda.device(src.device):
+        st = lib().rra_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(src))
+    _check("rra_stream_copy", st)
+    return dst

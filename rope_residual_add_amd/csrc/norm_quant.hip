@@ -361,10 +361,13 @@ __global__ void __launch_bounds__(kBlock)
     qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
     scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
   }
-  rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, 0.0f, qo,
-                                          scale_row);
+  // kv first: its short row then leaves the registers before q's quantization
+  // needs them (at the DeepSeek-V3 shape this keeps the kernel within 64 VGPRs,
+  // i.e. 8 waves per SIMD, so 8192 one-wave tokens are resident at once).
   rmsnorm_emit<NVKV, RRA_Q_NONE, 0, kFull>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kStride, 0.0f,
                                            kv_out + row * kv_out_stride, nullptr);
+  rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, 0.0f, qo,
+                                          scale_row);
 }
 
 // Waves per row for the residual-add norm: enough that each lane holds at

@@ -393,18 +393,6 @@ __global__ void __launch_bounds__(kBlock)
   out[p * rot_dim + half + i] = static_cast<float>(sn);
 }
 
-// Elementwise fp32 -> e4m3fn with the quantizing kernels' conversion.
-__global__ void __launch_bounds__(kBlock)
-    e4m3fn_encode_kernel(const float* __restrict__ in, uint8_t* __restrict__ out, int64_t n) {
-  const int64_t i4 = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * 4;
-  if (i4 + 4 <= n) {
-    const f32x4 x = ld_f32x4(in + i4);
-    *reinterpret_cast<uint32_t*>(out + i4) = pack_e4m3x4(x[0], x[1], x[2], x[3]);
-  } else {
-    for (int64_t j = i4; j < n; ++j) out[j] = static_cast<uint8_t>(pack_e4m3x4(in[j], 0, 0, 0));
-  }
-}
-
 inline dim3 rope_grid(int64_t T) {
   return dim3(static_cast<unsigned>(ceil_div(T, kRopeTokensPerBlock)));
 }
@@ -600,37 +588,4 @@ extern "C" int rope_cos_sin_cache(float* cos_sin, int64_t max_pos, int rot_dim, 
   hipLaunchKernelGGL(rope_cos_sin_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
                      as_stream(stream), cos_sin, max_pos, rot_dim, theta);
   return launch_status();
-}
-
-extern "C" int rra_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
-  RRA_REQUIRE(n >= 0, RRA_ERR_SHAPE);
-  RRA_REQUIRE(in && out, RRA_ERR_NULL);
-  RRA_REQUIRE(aligned(in, 16) && aligned(out, 4), RRA_ERR_ALIGN);
-  if (n == 0) return RRA_OK;
-  const int64_t blocks = ceil_div(ceil_div(n, 4), kBlock);
-  RRA_REQUIRE(blocks <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
-  hipLaunchKernelGGL(e4m3fn_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                     as_stream(stream), in, out, n);
-  return launch_status();
-}
-
-extern "C" int rra_abi_version(void) { return RRA_ABI_VERSION; }
-
-extern "C" const char* rra_status_string(int status) {
-  switch (status) {
-    case RRA_OK:
-      return "ok";
-    case RRA_ERR_NULL:
-      return "a required pointer is NULL";
-    case RRA_ERR_SHAPE:
-      return "negative or inconsistent sizes or strides";
-    case RRA_ERR_ALIGN:
-      return "pointer or stride breaks the 16-byte vector alignment rules";
-    case RRA_ERR_UNSUPPORTED:
-      return "unsupported mode, size or layout";
-    case RRA_ERR_LAUNCH:
-      return "kernel launch failed";
-    default:
-      return "unknown status";
-  }
 }

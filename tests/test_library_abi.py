@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fused_add_rmsnorm_quant", "silu_mul_quant", "rope_kv_write", "dual_rmsnorm_quant",
               "qk_norm_rope_kv_write", "fused_add_rmsnorm_pad", "mla_rope_kv_write",
-              "rope_cos_sin_cache", "rra_e4m3fn_encode", "rra_abi_version", "rra_status_string"):
+              "rope_cos_sin_cache", "rra_e4m3fn_encode", "rra_stream_copy", "rra_abi_version",
+              "rra_status_string"):
         assert n in names
 
 
@@ -53,7 +54,7 @@ def test_library_exports_every_declared_function(rra):
 
 
 def test_version_and_status_strings(rra):
-    assert rra.abi_version() == rra.ABI_VERSION == 2
+    assert rra.abi_version() == rra.ABI_VERSION == 3
     for s in (OK, ENULL, ESHAPE, EALIGN, EUNSUP, -5):
         assert rra.status_string(s) and rra.status_string(s) != "unknown status"
     assert rra.status_string(-99) == "unknown status"
@@ -241,3 +242,16 @@ def test_e4m3_diag_validation(rra):
     assert L.rra_e4m3fn_encode(None, A, 4, None) == ENULL
     assert L.rra_e4m3fn_encode(A + 4, A, 4, None) == EALIGN
     assert L.rra_e4m3fn_encode(A, A, 0, None) == OK
+
+
+def test_stream_copy_validation(rra):
+    L = rra.lib()
+    assert L.rra_stream_copy(None, A + 4096, 16, None) == ENULL
+    assert L.rra_stream_copy(A, None, 16, None) == ENULL
+    assert L.rra_stream_copy(A, A + 4096, -16, None) == ESHAPE
+    assert L.rra_stream_copy(A, A + 4096, 24, None) == EALIGN  # not a whole number of vectors
+    assert L.rra_stream_copy(A + 8, A + 4096, 16, None) == EALIGN
+    assert L.rra_stream_copy(A, A + 4104, 16, None) == EALIGN
+    assert L.rra_stream_copy(A, A + 16, 32, None) == ESHAPE  # overlapping ranges
+    assert L.rra_stream_copy(A + 16, A, 32, None) == ESHAPE
+    assert L.rra_stream_copy(None, None, 0, None) == OK
