@@ -16,17 +16,23 @@
 // writes.
 //
 // Mapping: four waves (256 lanes) per token.  A token's work is cut into
-// 16-byte units spread over the lanes; each lane takes kU of them per pass
-// (chosen per launch so one pass covers a token up to 1024 units) and issues
-// all their loads before its stores.  A rotation unit is 8 rotation pairs of one head:
-//   GPT-NeoX pairing (i, i + D/2): the vectors at columns 8c and D/2 + 8c;
-//   GPT-J pairing (2i, 2i + 1):    the vectors at columns 16c and 16c + 8.
-// Either way unit c rotates pairs 8c .. 8c + 7, i.e. reads entries 8c .. 8c + 7
-// of the cos and of the sin half of a table row.  A head has D/16 units and
-// the 256 lanes are a multiple of that, so all rotation units of a lane share
-// one c: the lane reads its 8 cos and 8 sin values once per token.
+// units spread over the lanes; each lane takes kU of them per pass (chosen per
+// launch so that one pass covers a typical token) and issues all their loads
+// before its stores.  A rotation unit depends on the pairing:
+//   GPT-NeoX pairs (i, i + D/2): 8 pairs, the 16-byte vectors at columns 8c
+//     and D/2 + 8c of a head;
+//   GPT-J pairs (2i, 2i + 1): 4 pairs, the one 16-byte vector at columns 8c,
+//     so that the 64 lanes of a load or store instruction cover whole, adjacent
+//     cache lines of each head instead of every other 16 bytes of them;
+// a copy unit is one 16-byte vector of v (or of the MLA kv_c).  Unit c of a
+// head reads entries kPairs*c .. kPairs*(c + 1) - 1 of the cos and of the sin
+// half of a table row.  A head has D/16 (NeoX) or D/8 (GPT-J) rotation units
+// and the 256 lanes are a multiple of that, so all rotation units of a lane
+// share one c: the lane reads its cos and sin values once per token.
 #include "rra_device.hpp"
 #include "rra_host.hpp"
+
+#include <type_traits>
 
 namespace rra {
 
@@ -35,45 +41,48 @@ constexpr int kRopeLanes = kRopeWaves * kWave;    // lanes per token
 constexpr int kRopeTokensPerBlock = kWavesPerBlock / kRopeWaves;
 constexpr int kRopeMaxUnitsPerPass = 4;           // units a lane loads before storing
 
-// Where the two vectors of rotation unit c sit inside a head of D values.
+// Geometry of a rotation unit inside a head of D values (see the mapping
+// above): kPerHead units per head, kPairs rotation pairs per unit, and for
+// NeoX a second vector kHi columns after the first.
 template <int D, bool kNeox>
-__device__ __forceinline__ int unit_lo(int c) {
-  return kNeox ? c * 8 : c * 16;
-}
-template <int D, bool kNeox>
-__device__ __forceinline__ int unit_hi(int c) {
-  return kNeox ? c * 8 + D / 2 : c * 16 + 8;
-}
+struct RotUnit {
+  static constexpr int kPerHead = kNeox ? D / 16 : D / 8;
+  static constexpr int kPairs = kNeox ? 8 : 4;
+  static constexpr int kHi = D / 2;  // NeoX only
+  static __device__ __forceinline__ int lo(int c) { return c * 8; }
+};
 
-// The 8 cos and 8 sin values of rotation unit c at one position.
-template <int D>
+// The kPairs cos and sin values of rotation unit c at one position.
+template <int D, bool kNeox>
 __device__ __forceinline__ void unit_cos_sin(const float* row, int c, float cs[8], float sn[8]) {
-  const float* p = row + c * 8;
-  const f32x4 c0 = ld_f32x4(p), c1 = ld_f32x4(p + 4);
-  const f32x4 s0 = ld_f32x4(p + D / 2), s1 = ld_f32x4(p + D / 2 + 4);
+  constexpr int P = RotUnit<D, kNeox>::kPairs;
+  const float* p = row + c * P;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    cs[j] = c0[j];
-    cs[4 + j] = c1[j];
-    sn[j] = s0[j];
-    sn[4 + j] = s1[j];
+  for (int h = 0; h < P / 4; ++h) {
+    const f32x4 c4 = ld_f32x4(p + 4 * h), s4 = ld_f32x4(p + D / 2 + 4 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cs[4 * h + j] = c4[j];
+      sn[4 * h + j] = s4[j];
+    }
   }
 }
 
-// Rotate the 8 pairs of a unit held as 16 fp32 values x[0..8) (lo vector) and
-// x[8..16) (hi vector): (a, b) -> (a cos - b sin, b cos + a sin).
+// Rotate the pairs of a unit, (a, b) -> (a cos - b sin, b cos + a sin).
+// NeoX: 16 fp32 values x[0..8) (first vector) and x[8..16) (second), pair k
+// = (x[k], x[8 + k]).  GPT-J: 8 values x[0..8), pair k = (x[2k], x[2k + 1]).
 template <bool kNeox>
 __device__ __forceinline__ void rotate_unit(float x[16], const float cs[8], const float sn[8]) {
   if (kNeox) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {  // pair k = (lo[k], hi[k])
+    for (int k = 0; k < 8; ++k) {
       const float a = x[k], b = x[8 + k];
       x[k] = a * cs[k] - b * sn[k];
       x[8 + k] = b * cs[k] + a * sn[k];
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {  // pair k = (x[2k], x[2k + 1])
+    for (int k = 0; k < 4; ++k) {
       const float a = x[2 * k], b = x[2 * k + 1];
       x[2 * k] = a * cs[k] - b * sn[k];
       x[2 * k + 1] = b * cs[k] + a * sn[k];
@@ -81,44 +90,57 @@ __device__ __forceinline__ void rotate_unit(float x[16], const float cs[8], cons
   }
 }
 
-// Two 16-byte vectors of 8 elements each (element type E) <-> 16 fp32 values.
+// One or two 16-byte vectors of 8 elements each (element type E) <-> fp32.
 template <typename E = ElemBf16>
-__device__ __forceinline__ void unpack16(u32x4 lo, u32x4 hi, float x[16]) {
+__device__ __forceinline__ void unpack8(u32x4 v, float x[8]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    x[2 * k] = E::lo(lo[k]);
-    x[2 * k + 1] = E::hi(lo[k]);
-    x[8 + 2 * k] = E::lo(hi[k]);
-    x[8 + 2 * k + 1] = E::hi(hi[k]);
+    x[2 * k] = E::lo(v[k]);
+    x[2 * k + 1] = E::hi(v[k]);
   }
+}
+
+template <typename E = ElemBf16>
+__device__ __forceinline__ u32x4 pack8(const float x[8]) {
+  return u32x4{E::pack(x[0], x[1]), E::pack(x[2], x[3]), E::pack(x[4], x[5]),
+               E::pack(x[6], x[7])};
+}
+
+template <typename E = ElemBf16>
+__device__ __forceinline__ void unpack16(u32x4 lo, u32x4 hi, float x[16]) {
+  unpack8<E>(lo, x);
+  unpack8<E>(hi, x + 8);
 }
 
 template <typename E = ElemBf16>
 __device__ __forceinline__ void pack16(const float x[16], u32x4& lo, u32x4& hi) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    lo[k] = E::pack(x[2 * k], x[2 * k + 1]);
-    hi[k] = E::pack(x[8 + 2 * k], x[8 + 2 * k + 1]);
-  }
+  lo = pack8<E>(x);
+  hi = pack8<E>(x + 8);
 }
 
+// Rotate a unit held as its packed vector(s); GPT-J units leave hi untouched.
 template <bool kNeox, typename E = ElemBf16>
 __device__ __forceinline__ void rotate_packed(u32x4& lo, u32x4& hi, const float cs[8],
                                               const float sn[8]) {
   float x[16];
-  unpack16<E>(lo, hi, x);
+  unpack8<E>(lo, x);
+  if (kNeox) unpack8<E>(hi, x + 8);
   rotate_unit<kNeox>(x, cs, sn);
-  pack16<E>(x, lo, hi);
+  lo = pack8<E>(x);
+  if (kNeox) hi = pack8<E>(x + 8);
 }
 
-// Sum over aligned groups of n lanes (n = 4, 8 or 16), result in every lane
-// of the group.  Executed by all lanes of the wave.
+// Sum over aligned groups of n lanes (n = 4, 8, 16 or 32), result in every
+// lane of the group.  Executed by all lanes of the wave.
 template <int n>
 __device__ __forceinline__ float group_sum(float v) {
+  static_assert(n == 4 || n == 8 || n == 16 || n == 32, "group size");
   v += dpp<0xB1>(v);  // quad_perm [1, 0, 3, 2]
   v += dpp<0x4E>(v);  // quad_perm [2, 3, 0, 1]
   if (n >= 8) v += dpp<0x141>(v);  // row_half_mirror
   if (n >= 16) v += dpp<0x140>(v);  // row_mirror
+  if (n >= 32)  // lane ^ 16 within each 32-lane half (ds_swizzle bit mode, xor mask 16)
+    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (0x10 << 10) | 0x1F));
   return v;
 }
 
@@ -137,7 +159,8 @@ __global__ void __launch_bounds__(kBlock)
                          const int64_t* __restrict__ slot_mapping,
                          uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
                          int64_t T, int Hq, int Hkv) {
-  constexpr int kUnitsPerHead = D / 16;
+  using U = RotUnit<D, kNeox>;
+  constexpr int kUnitsPerHead = U::kPerHead;
   static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
   const int wave = wave_id();
   const int rl = (wave % kRopeWaves) * kWave + lane_id();
@@ -147,14 +170,14 @@ __global__ void __launch_bounds__(kBlock)
   const int64_t pos = positions[t];
   const int64_t slot = slot_mapping[t];
   const int c = rl % kUnitsPerHead;
-  const int lo_off = unit_lo<D, kNeox>(c), hi_off = unit_hi<D, kNeox>(c);
+  const int lo_off = U::lo(c), hi_off = lo_off + U::kHi;
   const int uq = Hq * kUnitsPerHead;
   const int uk = slot >= 0 ? Hkv * kUnitsPerHead : 0;  // padding tokens: q only
   const int uv = slot >= 0 ? Hkv * (D / 8) : 0;
   const int total = uq + uk + uv;
 
   float cs[8], sn[8];
-  unit_cos_sin<D>(cos_sin + pos * D, c, cs, sn);
+  unit_cos_sin<D, kNeox>(cos_sin + pos * D, c, cs, sn);
   const uint16_t* qt = q + t * q_stride;
   uint16_t* qo = q_out + t * q_out_stride;
   const uint16_t* kt = k + t * k_stride;
@@ -172,11 +195,11 @@ __global__ void __launch_bounds__(kBlock)
       if (u < uq) {
         const uint16_t* p = qt + (u / kUnitsPerHead) * D;
         lo[j] = ld_stream(p + lo_off);
-        hi[j] = ld_stream(p + hi_off);
+        if (kNeox) hi[j] = ld_stream(p + hi_off);
       } else if (u < uq + uk) {
         const uint16_t* p = kt + ((u - uq) / kUnitsPerHead) * D;
         lo[j] = ld_stream(p + lo_off);
-        hi[j] = ld_stream(p + hi_off);
+        if (kNeox) hi[j] = ld_stream(p + hi_off);
       } else if (u < total) {
         lo[j] = ld_stream(vt + (u - uq - uk) * 8);
       }
@@ -188,12 +211,12 @@ __global__ void __launch_bounds__(kBlock)
         rotate_packed<kNeox, E>(lo[j], hi[j], cs, sn);
         uint16_t* p = qo + (u / kUnitsPerHead) * D;
         st_stream(p + lo_off, lo[j]);
-        st_stream(p + hi_off, hi[j]);
+        if (kNeox) st_stream(p + hi_off, hi[j]);
       } else if (u < uq + uk) {
         rotate_packed<kNeox, E>(lo[j], hi[j], cs, sn);
         uint16_t* p = kc + ((u - uq) / kUnitsPerHead) * D;
         st_stream(p + lo_off, lo[j]);
-        st_stream(p + hi_off, hi[j]);
+        if (kNeox) st_stream(p + hi_off, hi[j]);
       } else if (u < total) {
         st_stream(vc + (u - uq - uk) * 8, lo[j]);
       }
@@ -216,7 +239,9 @@ __global__ void __launch_bounds__(kBlock)
                            const int64_t* __restrict__ slot_mapping,
                            uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
                            int write_k, int64_t T, int Hq, int Hkv) {
-  constexpr int kUnitsPerHead = D / 16;
+  using U = RotUnit<D, kNeox>;
+  constexpr int kUnitsPerHead = U::kPerHead;
+  constexpr int kVals = kNeox ? 16 : 8;  // values of a rotation unit
   static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
   const int wave = wave_id();
   const int rl = (wave % kRopeWaves) * kWave + lane_id();
@@ -226,18 +251,22 @@ __global__ void __launch_bounds__(kBlock)
   const int64_t pos = positions[t];
   const int64_t slot = slot_mapping ? slot_mapping[t] : -1;
   const int c = rl % kUnitsPerHead;
-  const int lo_off = unit_lo<D, kNeox>(c), hi_off = unit_hi<D, kNeox>(c);
+  const int lo_off = U::lo(c), hi_off = lo_off + U::kHi;
   const int uq = Hq * kUnitsPerHead;
   const int uk = (slot >= 0 || write_k) ? Hkv * kUnitsPerHead : 0;
   const int uv = slot >= 0 ? Hkv * (D / 8) : 0;
   const int total = uq + uk + uv;
 
   float cs[8], sn[8];
-  unit_cos_sin<D>(cos_sin + pos * D, c, cs, sn);
-  // This lane's 16 weight values for q and for k (the same columns in every head).
+  unit_cos_sin<D, kNeox>(cos_sin + pos * D, c, cs, sn);
+  // This lane's weight values for q and for k (the same columns in every head).
   float wq[16], wk[16];
-  unpack16(ld_cached(q_weight + lo_off), ld_cached(q_weight + hi_off), wq);
-  unpack16(ld_cached(k_weight + lo_off), ld_cached(k_weight + hi_off), wk);
+  unpack8(ld_cached(q_weight + lo_off), wq);
+  unpack8(ld_cached(k_weight + lo_off), wk);
+  if (kNeox) {
+    unpack8(ld_cached(q_weight + hi_off), wq + 8);
+    unpack8(ld_cached(k_weight + hi_off), wk + 8);
+  }
 
   uint16_t* row = qkv + t * qkv_stride;
   uint16_t* kt = row + Hq * D;
@@ -256,11 +285,11 @@ __global__ void __launch_bounds__(kBlock)
       if (u < uq) {
         const uint16_t* p = row + (u / kUnitsPerHead) * D;
         lo[j] = ld_stream(p + lo_off);
-        hi[j] = ld_stream(p + hi_off);
+        if (kNeox) hi[j] = ld_stream(p + hi_off);
       } else if (u < uq + uk) {
         const uint16_t* p = kt + ((u - uq) / kUnitsPerHead) * D;
         lo[j] = ld_stream(p + lo_off);
-        hi[j] = ld_stream(p + hi_off);
+        if (kNeox) hi[j] = ld_stream(p + hi_off);
       } else if (u < total) {
         lo[j] = ld_stream(vt + (u - uq - uk) * 8);
       }
@@ -270,34 +299,35 @@ __global__ void __launch_bounds__(kBlock)
       const int u = u0 + j * kRopeLanes + rl;
       const bool is_q = u < uq, is_k = !is_q && u < uq + uk;
       float x[16];
-      unpack16(lo[j], hi[j], x);
+      unpack8(lo[j], x);
+      if (kNeox) unpack8(hi[j], x + 8);
       float ss = 0.0f;
       if (is_q || is_k) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ss = fmaf(x[e], x[e], ss);
+        for (int e = 0; e < kVals; ++e) ss = fmaf(x[e], x[e], ss);
       }
       ss = group_sum<kUnitsPerHead>(ss);  // all lanes: groups are q-only, k-only or idle
       if (is_q || is_k) {
         const float rho = __builtin_amdgcn_rsqf(ss * inv_d + eps);
         const float* w = is_q ? wq : wk;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = x[e] * rho * w[e];
+        for (int e = 0; e < kVals; ++e) x[e] = x[e] * rho * w[e];
         rotate_unit<kNeox>(x, cs, sn);
-        u32x4 a, b;
-        pack16(x, a, b);
+        const u32x4 a = pack8(x);
+        const u32x4 b = kNeox ? pack8(x + 8) : a;
         if (is_q) {
           uint16_t* p = row + (u / kUnitsPerHead) * D;
           st_stream(p + lo_off, a);
-          st_stream(p + hi_off, b);
+          if (kNeox) st_stream(p + hi_off, b);
         } else {
           const int h = (u - uq) / kUnitsPerHead;
           if (slot >= 0) {
             st_stream(kc + h * D + lo_off, a);
-            st_stream(kc + h * D + hi_off, b);
+            if (kNeox) st_stream(kc + h * D + hi_off, b);
           }
           if (write_k) {
             st_stream(kt + h * D + lo_off, a);
-            st_stream(kt + h * D + hi_off, b);
+            if (kNeox) st_stream(kt + h * D + hi_off, b);
           }
         }
       } else if (u < total) {
@@ -319,7 +349,8 @@ __global__ void __launch_bounds__(kBlock)
                        int64_t kv_c_stride, const float* __restrict__ cos_sin,
                        const int64_t* __restrict__ slot_mapping, uint16_t* __restrict__ kv_cache,
                        int64_t T, int Hq, int kv_lora) {
-  constexpr int kUnitsPerHead = R / 16;
+  using U = RotUnit<R, kNeox>;
+  constexpr int kUnitsPerHead = U::kPerHead;
   static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
   const int wave = wave_id();
   const int rl = (wave % kRopeWaves) * kWave + lane_id();
@@ -329,14 +360,14 @@ __global__ void __launch_bounds__(kBlock)
   const int64_t pos = positions[t];
   const int64_t slot = slot_mapping[t];
   const int c = rl % kUnitsPerHead;
-  const int lo_off = unit_lo<R, kNeox>(c), hi_off = unit_hi<R, kNeox>(c);
+  const int lo_off = U::lo(c), hi_off = lo_off + U::kHi;
   const int uq = Hq * kUnitsPerHead;
   const int uk = slot >= 0 ? kUnitsPerHead : 0;
   const int uc = slot >= 0 ? kv_lora / 8 : 0;
   const int total = uq + uk + uc;
 
   float cs[8], sn[8];
-  unit_cos_sin<R>(cos_sin + pos * R, c, cs, sn);
+  unit_cos_sin<R, kNeox>(cos_sin + pos * R, c, cs, sn);
   uint16_t* qt = q_pe + t * q_stride;
   const uint16_t* kt = k_pe + t * k_pe_stride;
   const uint16_t* ct = kv_c + t * kv_c_stride;
@@ -350,10 +381,10 @@ __global__ void __launch_bounds__(kBlock)
       if (u < uq) {
         const uint16_t* p = qt + (u / kUnitsPerHead) * q_head_stride;
         lo[j] = ld_stream(p + lo_off);
-        hi[j] = ld_stream(p + hi_off);
+        if (kNeox) hi[j] = ld_stream(p + hi_off);
       } else if (u < uq + uk) {
         lo[j] = ld_stream(kt + lo_off);
-        hi[j] = ld_stream(kt + hi_off);
+        if (kNeox) hi[j] = ld_stream(kt + hi_off);
       } else if (u < total) {
         lo[j] = ld_stream(ct + (u - uq - uk) * 8);
       }
@@ -365,11 +396,11 @@ __global__ void __launch_bounds__(kBlock)
         rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
         uint16_t* p = qt + (u / kUnitsPerHead) * q_head_stride;
         st_stream(p + lo_off, lo[j]);
-        st_stream(p + hi_off, hi[j]);
+        if (kNeox) st_stream(p + hi_off, hi[j]);
       } else if (u < uq + uk) {
         rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
         st_stream(dst + kv_lora + lo_off, lo[j]);
-        st_stream(dst + kv_lora + hi_off, hi[j]);
+        if (kNeox) st_stream(dst + kv_lora + hi_off, hi[j]);
       } else if (u < total) {
         st_stream(dst + (u - uq - uk) * 8, lo[j]);
       }
@@ -397,11 +428,35 @@ inline dim3 rope_grid(int64_t T) {
   return dim3(static_cast<unsigned>(ceil_div(T, kRopeTokensPerBlock)));
 }
 
-// Units each lane takes per pass: enough for one pass over a token's largest
-// unit count (all loads of a lane issued before its stores), at most 4.
-inline int rope_units_per_pass(int64_t units) {
+// Rotation units per head under the two pairings (RotUnit::kPerHead).
+inline int64_t rot_units_per_head(int D, int is_neox) { return is_neox ? D / 16 : D / 8; }
+
+// Units each lane takes per pass: enough for one pass over a token's unit
+// count (all loads of a lane issued before its stores), at most 4 two-vector
+// (NeoX) or 8 one-vector (GPT-J) rotation units' worth.
+inline int rope_units_per_pass(int64_t units, int is_neox) {
+  const int64_t cap = is_neox ? kRopeMaxUnitsPerPass : 2 * kRopeMaxUnitsPerPass;
   const int64_t u = ceil_div(units, kRopeLanes);
-  return static_cast<int>(u < 1 ? 1 : (u > kRopeMaxUnitsPerPass ? kRopeMaxUnitsPerPass : u));
+  return static_cast<int>(u < 1 ? 1 : (u > cap ? cap : u));
+}
+
+// Calls f(std::integral_constant<int, k>()) with k = ku clamped to [1, kMax],
+// instantiating the launches for 1 .. kMax only.
+template <int kMax, typename F>
+static void with_units_per_pass(int ku, F&& f) {
+  if constexpr (kMax > 1) {
+    if (ku >= kMax) {
+      f(std::integral_constant<int, kMax>());
+      return;
+    }
+    with_units_per_pass<kMax - 1>(ku, f);
+  } else {
+    f(std::integral_constant<int, 1>());
+  }
+}
+
+constexpr int rope_max_units(bool neox) {
+  return neox ? kRopeMaxUnitsPerPass : 2 * kRopeMaxUnitsPerPass;
 }
 
 }  // namespace rra
@@ -438,20 +493,17 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
 
   const hipStream_t st = as_stream(stream);
-  const int ku = rope_units_per_pass(int64_t(Hq + Hkv) * (D / 16) + int64_t(Hkv) * (D / 8));
-#define RRA_ROPE_LAUNCH(DD, NEOX, KU, EL)                                                      \
-  hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX, KU, EL>), rope_grid(T), dim3(kBlock), 0,  \
-                     st, positions, q, q_stride, q_out, q_out_stride, k, k_stride, v,          \
-                     v_stride, cos_sin, slot_mapping, key_cache, value_cache, T, Hq, Hkv)
-#define RRA_ROPE_CASE(DD, NEOX, DT, EL)                                                         \
-  if (D == DD && is_neox == NEOX && dtype == DT) {                                              \
-    switch (ku) {                                                                               \
-      case 1: RRA_ROPE_LAUNCH(DD, NEOX, 1, EL); break;                                          \
-      case 2: RRA_ROPE_LAUNCH(DD, NEOX, 2, EL); break;                                          \
-      case 3: RRA_ROPE_LAUNCH(DD, NEOX, 3, EL); break;                                          \
-      default: RRA_ROPE_LAUNCH(DD, NEOX, 4, EL); break;                                         \
-    }                                                                                           \
-    return launch_status();                                                                     \
+  const int ku = rope_units_per_pass(
+      int64_t(Hq + Hkv) * rot_units_per_head(D, is_neox) + int64_t(Hkv) * (D / 8), is_neox);
+#define RRA_ROPE_CASE(DD, NEOX, DT, EL)                                                        \
+  if (D == DD && is_neox == NEOX && dtype == DT) {                                             \
+    with_units_per_pass<rope_max_units(NEOX)>(ku, [&](auto units) {                                \
+      hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX, decltype(units)::value, EL>),             \
+                         rope_grid(T), dim3(kBlock), 0, st, positions, q, q_stride, q_out,     \
+                         q_out_stride, k, k_stride, v, v_stride, cos_sin, slot_mapping,        \
+                         key_cache, value_cache, T, Hq, Hkv);                                  \
+    });                                                                                        \
+    return launch_status();                                                                    \
   }
   RRA_ROPE_CASE(64, 1, RRA_BF16, ElemBf16)
   RRA_ROPE_CASE(128, 1, RRA_BF16, ElemBf16)
@@ -466,7 +518,6 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   RRA_ROPE_CASE(128, 0, RRA_F16, ElemF16)
   RRA_ROPE_CASE(256, 0, RRA_F16, ElemF16)
 #undef RRA_ROPE_CASE
-#undef RRA_ROPE_LAUNCH
   return RRA_ERR_UNSUPPORTED;
 }
 
@@ -498,20 +549,17 @@ extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, in
   RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
 
   const hipStream_t st = as_stream(stream);
-  const int ku = rope_units_per_pass(int64_t(Hq + Hkv) * (D / 16) +
-                                     (slot_mapping ? int64_t(Hkv) * (D / 8) : 0));
-#define RRA_QKN_LAUNCH(DD, NEOX, KU)                                                            \
-  hipLaunchKernelGGL((qk_norm_rope_kv_kernel<DD, NEOX, KU>), rope_grid(T), dim3(kBlock), 0, st, \
-                     positions, qkv, qkv_stride, q_weight, k_weight, eps, cos_sin,              \
-                     slot_mapping, key_cache, value_cache, write_k, T, Hq, Hkv)
+  const int ku = rope_units_per_pass(int64_t(Hq + Hkv) * rot_units_per_head(D, is_neox) +
+                                         (slot_mapping ? int64_t(Hkv) * (D / 8) : 0),
+                                     is_neox);
 #define RRA_QKN_CASE(DD, NEOX)                                                                 \
   if (D == DD && is_neox == NEOX) {                                                            \
-    switch (ku) {                                                                              \
-      case 1: RRA_QKN_LAUNCH(DD, NEOX, 1); break;                                              \
-      case 2: RRA_QKN_LAUNCH(DD, NEOX, 2); break;                                              \
-      case 3: RRA_QKN_LAUNCH(DD, NEOX, 3); break;                                              \
-      default: RRA_QKN_LAUNCH(DD, NEOX, 4); break;                                             \
-    }                                                                                          \
+    with_units_per_pass<rope_max_units(NEOX)>(ku, [&](auto units) {                                \
+      hipLaunchKernelGGL((qk_norm_rope_kv_kernel<DD, NEOX, decltype(units)::value>), rope_grid(T), \
+                         dim3(kBlock), 0, st, positions, qkv, qkv_stride, q_weight, k_weight,  \
+                         eps, cos_sin, slot_mapping, key_cache, value_cache, write_k, T, Hq,   \
+                         Hkv);                                                                 \
+    });                                                                                        \
     return launch_status();                                                                    \
   }
   RRA_QKN_CASE(64, 1)
@@ -521,7 +569,6 @@ extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, in
   RRA_QKN_CASE(128, 0)
   RRA_QKN_CASE(256, 0)
 #undef RRA_QKN_CASE
-#undef RRA_QKN_LAUNCH
   return RRA_ERR_UNSUPPORTED;
 }
 
@@ -552,27 +599,23 @@ extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64
   RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
 
   const hipStream_t st = as_stream(stream);
-  const int ku = rope_units_per_pass(int64_t(Hq + 1) * (rope_dim / 16) + kv_lora / 8);
-#define RRA_MLA_LAUNCH(RR, NEOX, KU)                                                          \
-  hipLaunchKernelGGL((mla_rope_kv_kernel<RR, NEOX, KU>), rope_grid(T), dim3(kBlock), 0, st,   \
-                     positions, q_pe, q_stride, q_head_stride, k_pe, k_pe_stride, kv_c,       \
-                     kv_c_stride, cos_sin, slot_mapping, kv_cache, T, Hq, kv_lora)
-#define RRA_MLA_CASE(RR, NEOX)                                                                \
-  if (rope_dim == RR && is_neox == NEOX) {                                                    \
-    switch (ku) {                                                                             \
-      case 1: RRA_MLA_LAUNCH(RR, NEOX, 1); break;                                             \
-      case 2: RRA_MLA_LAUNCH(RR, NEOX, 2); break;                                             \
-      case 3: RRA_MLA_LAUNCH(RR, NEOX, 3); break;                                             \
-      default: RRA_MLA_LAUNCH(RR, NEOX, 4); break;                                            \
-    }                                                                                         \
-    return launch_status();                                                                   \
+  const int ku = rope_units_per_pass(
+      int64_t(Hq + 1) * rot_units_per_head(rope_dim, is_neox) + kv_lora / 8, is_neox);
+#define RRA_MLA_CASE(RR, NEOX)                                                                 \
+  if (rope_dim == RR && is_neox == NEOX) {                                                     \
+    with_units_per_pass<rope_max_units(NEOX)>(ku, [&](auto units) {                                \
+      hipLaunchKernelGGL((mla_rope_kv_kernel<RR, NEOX, decltype(units)::value>), rope_grid(T),     \
+                         dim3(kBlock), 0, st, positions, q_pe, q_stride, q_head_stride, k_pe,  \
+                         k_pe_stride, kv_c, kv_c_stride, cos_sin, slot_mapping, kv_cache, T,   \
+                         Hq, kv_lora);                                                         \
+    });                                                                                        \
+    return launch_status();                                                                    \
   }
   RRA_MLA_CASE(64, 0)
   RRA_MLA_CASE(64, 1)
   RRA_MLA_CASE(128, 0)
   RRA_MLA_CASE(128, 1)
 #undef RRA_MLA_CASE
-#undef RRA_MLA_LAUNCH
   return RRA_ERR_UNSUPPORTED;
 }
 

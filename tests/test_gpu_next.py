@@ -111,7 +111,9 @@ def test_qknorm_cache_and_write_k_padding(rra, oracle):
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,neox", [(32, 8, 128, False), (16, 4, 64, True),
-                                           (8, 2, 256, True), (12, 3, 64, False)])
+                                           (8, 2, 256, True), (12, 3, 64, False),
+                                           (8, 2, 256, False), (64, 8, 128, False),
+                                           (96, 16, 128, False)])
 def test_qknorm_shapes(rra, oracle, Hq, Hkv, D, neox):
     cfg = dataclasses.replace(workloads.QKNORM, Hq=Hq, Hkv=Hkv, D=D, **QK_SMALL)
     run_qknorm(rra, oracle, 41, cfg, is_neox=neox, pad_every=5)
@@ -243,7 +245,8 @@ def test_mla_rope_workload(rra, oracle, T):
     run_mla_rope(rra, oracle, T)
 
 
-@pytest.mark.parametrize("Hq,rope,neox", [(16, 64, True), (7, 128, False), (1, 64, False)])
+@pytest.mark.parametrize("Hq,rope,neox", [(16, 64, True), (7, 128, False), (1, 64, False),
+                                           (256, 64, False), (128, 128, False)])
 def test_mla_rope_shapes(rra, oracle, Hq, rope, neox):
     cfg = dataclasses.replace(workloads.MLA_ROPE, Hq=Hq, rope_dim=rope, is_neox=neox,
                               num_blocks=16, max_pos=2048)

@@ -139,6 +139,17 @@ def test_head_and_block_shapes(rra, oracle, Hq, Hkv, D, bs):
     run(rra, oracle, 45, cfg, pad_every=7)
 
 
+# GPT-J pairing takes one 16-byte vector (4 pairs) per rotation unit, so a lane
+# carries 1 to 8 units per pass: these shapes give 1, 1, 3, 5, 7 and 8 units
+# per lane (the last in three passes over a token).
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 1, 64), (12, 2, 128), (32, 8, 128), (64, 8, 128),
+                                      (40, 8, 256), (128, 16, 256)])
+def test_gptj_units_per_pass(rra, oracle, Hq, Hkv, D):
+    cfg = dataclasses.replace(workloads.ROPE, Hq=Hq, Hkv=Hkv, D=D, rot_dim=D, is_neox=False,
+                              **SMALL)
+    run(rra, oracle, 37, cfg, pad_every=5)
+
+
 def test_position_zero_is_identity(rra):
     """At position 0 the rotation is the identity: q_out == q, cache == k."""
     import torch
