@@ -181,11 +181,14 @@ __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
 // row_bcast:15 (0x142) and row_bcast:31 (0x143).  Every combining step adds
 // the same two partials in both lanes of a pair, so all lanes of a segment end
 // with bit-identical results (fp addition and max are commutative).
+// The moves carry no "old" value: within-row patterns write every lane from a
+// valid source, and the row-masked broadcasts leave the other rows undefined,
+// which only the whole-wave reductions use and only through lane 63, whose sum
+// never reads them.  (A zero "old" costs one extra move per step.)
 
 template <int kCtrl, int kRowMask = 0xF>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, kRowMask, 0xF, true));
 }
 
 // Max over each aligned group of 8 lanes, result in all 8.
@@ -227,10 +230,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int kCtrl, int kRowMask = 0xF>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      0, static_cast<int>(u & 0xFFFFFFFFu), kCtrl, kRowMask, 0xF, false));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      0, static_cast<int>(u >> 32), kCtrl, kRowMask, 0xF, false));
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(u & 0xFFFFFFFFu), kCtrl, kRowMask, 0xF, true));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), kCtrl, kRowMask, 0xF, true));
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
