@@ -562,9 +562,16 @@ def _kernel_of(symbol_name: str):
     return None
 
 
-def summarize_trace(stats_csv: str, out: str, command: str, T: int) -> None:
-    """Kernel-trace summary: per-kernel average duration and GB/s."""
+def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=None) -> None:
+    """Kernel-trace summary: per-kernel average duration and GB/s; with
+    bench_json (the JSON line the traced run printed), the run's own
+    event-timed average per kernel beside the profiler's."""
     import csv
+
+    events = {}
+    if bench_json:
+        line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
+        events = {k: v["us"] for k, v in json.loads(line)["kernels"].items()}
 
     lines = [f"# Kernel trace: the four fused kernels at T={T}", "",
              "Produced by (from the repository root, after `cd /tmp && export TMPDIR=/tmp` for "
@@ -572,7 +579,8 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int) -> None:
              "Durations are the profiler's kernel times (AverageNs etc. of "
              "`--stats` kernel_stats.csv). GB/s = algorithmic bytes per launch / average.", "",
              "| kernel | symbol | calls | avg us | min us | max us | algorithmic bytes | "
-             "GB/s (avg) | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
+             "GB/s (avg) | % of 8 TB/s |" + (" bench.py events avg us |" if events else ""),
+             "|---|---|---|---|---|---|---|---|---|" + ("---|" if events else "")]
     for r in csv.DictReader(open(stats_csv)):
         k = _kernel_of(r["Name"])
         if k is None or k not in KERNELS:
@@ -582,7 +590,8 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int) -> None:
         gbps = b / avg
         sym = r["Name"].split("(")[0].replace("void ", "")
         lines.append(f"| {k} | `{sym}` | {r['Calls']} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
-                     f"{mx / 1e3:.2f} | {b} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f}% |")
+                     f"{mx / 1e3:.2f} | {b} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f}% |"
+                     + (f" {events[k]:.2f} |" if events else ""))
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -705,11 +714,12 @@ def main() -> int:
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write a profiles/ summary from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--out", help="output file for --summarize-*")
+    ap.add_argument("--bench-json", help="with --summarize-trace: the traced run's JSON output")
     ap.add_argument("--command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
 
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.out, args.command, args.T)
+        summarize_trace(args.summarize_trace, args.out, args.command, args.T, args.bench_json)
         return 0
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.out, args.command, args.T)
