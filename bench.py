@@ -499,6 +499,19 @@ def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS, with_copy: bool = T
     return rows
 
 
+def environment() -> dict:
+    """Versions and device facts recorded beside the numbers."""
+    import platform
+
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    return dict(device=torch.cuda.get_device_name(0), arch=getattr(p, "gcnArchName", ""),
+                compute_units=p.multi_processor_count, memory_gib=round(p.total_memory / 2**30, 1),
+                torch=torch.__version__, hip=getattr(torch.version, "hip", None),
+                host_cpus=os.cpu_count(), host=platform.processor() or platform.machine())
+
+
 # ---- CPU baseline: the oracle on a bounded sample --------------------------------
 
 def cpu_baseline(sample_T: int):
@@ -510,7 +523,6 @@ def cpu_baseline(sample_T: int):
     except AttributeError:
         cores = os.cpu_count() or 1
     cores = max(1, min(cores, 16))
-    oracle.set_threads(cores)
     cfg = workloads.ROPE
     n = sample_T
     dn = workloads.norm_inputs(n, H_NORM)
@@ -527,24 +539,36 @@ def cpu_baseline(sample_T: int):
         "dual_rmsnorm_quant": lambda: oracle.dual_rmsnorm_quant(
             dm["q"], dm["q_w"], 1e-6, dm["kv"], dm["kv_w"], 1e-6, oracle.Q_PER_GROUP, G),
     }
-    secs = {}
-    for name, f in calls.items():
-        f()  # warm-up
-        ts = []
-        for _ in range(3):
-            t0 = time.perf_counter()
-            f()
-            ts.append(time.perf_counter() - t0)
-        secs[name] = statistics.median(ts)
-        log(f"oracle {name:26s} T={n} {secs[name] * 1e3:8.1f} ms on {oracle.get_threads()} threads")
+    def timed(threads):
+        oracle.set_threads(threads)
+        secs = {}
+        for name, f in calls.items():
+            f()  # warm-up
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                f()
+                ts.append(time.perf_counter() - t0)
+            secs[name] = statistics.median(ts)
+            log(f"oracle {name:26s} T={n} {secs[name] * 1e3:8.1f} ms on {oracle.get_threads()} "
+                f"threads")
+        return secs
+
     total_bytes = sum(algo_bytes(k, n) for k in KERNELS)
+    one = timed(1)
+    secs = timed(cores)
+    cores = int(oracle.get_threads())  # the threads the timed calls actually used
     total_s = sum(secs.values())
     return dict(value=round(total_bytes / total_s / 1e9, 4), unit="GB/s",
-                cores=int(oracle.get_threads()), kind="oracle",
+                cores=cores, kind="oracle",
                 sample=f"T={n} tokens of each of the four kernels' workloads (the GPU step "
                        f"uses T=8192); fp64 C oracle, OpenMP over rows, median of 3 calls "
-                       f"after one warm-up; bytes counted as for the GPU",
-                per_kernel_ms={k: round(v * 1e3, 2) for k, v in secs.items()})
+                       f"after one warm-up; bytes counted as for the GPU; one_core: the same "
+                       f"on one thread. The RoPE oracle returns fresh copies of both 128 MiB caches on "
+                       f"every call, which dominates its time at this sample size",
+                per_kernel_ms={k: round(v * 1e3, 2) for k, v in secs.items()},
+                one_core=dict(value=round(total_bytes / sum(one.values()) / 1e9, 4), unit="GB/s",
+                              per_kernel_ms={k: round(v * 1e3, 2) for k, v in one.items()}))
 
 
 # ---- profile summaries (rocprofv3 CSV -> profiles/*.md) ----------------------------
@@ -563,11 +587,22 @@ def _kernel_of(symbol_name: str):
 
 
 def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=None) -> None:
-    """Kernel-trace summary: per-kernel average duration and GB/s; with
+    import collections
+
+    """Kernel-trace summary: per-kernel average duration and GB/s (and p10 /
+    median / p90 from the per-dispatch trace next to the stats file); with
     bench_json (the JSON line the traced run printed), the run's own
     event-timed average per kernel beside the profiler's."""
     import csv
 
+    # per-dispatch durations from the kernel trace beside the stats file, if present
+    per = collections.defaultdict(list)
+    trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
+    if trace_csv != stats_csv and os.path.exists(trace_csv):
+        for r in csv.DictReader(open(trace_csv)):
+            k = _kernel_of(r["Kernel_Name"])
+            if k is not None:
+                per[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     events = {}
     if bench_json:
         line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
@@ -578,9 +613,10 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=N
              "the profiler):", "", "```", command, "```", "",
              "Durations are the profiler's kernel times (AverageNs etc. of "
              "`--stats` kernel_stats.csv). GB/s = algorithmic bytes per launch / average.", "",
-             "| kernel | symbol | calls | avg us | min us | max us | algorithmic bytes | "
-             "GB/s (avg) | % of 8 TB/s |" + (" bench.py events avg us |" if events else ""),
-             "|---|---|---|---|---|---|---|---|---|" + ("---|" if events else "")]
+             "| kernel | symbol | calls | avg us | min us | max us | p10 / median / p90 us | "
+             "algorithmic bytes | GB/s (avg) | % of 8 TB/s |"
+             + (" bench.py events avg us |" if events else ""),
+             "|---|---|---|---|---|---|---|---|---|---|" + ("---|" if events else "")]
     for r in csv.DictReader(open(stats_csv)):
         k = _kernel_of(r["Name"])
         if k is None or k not in KERNELS:
@@ -589,8 +625,13 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=N
         b = algo_bytes(k, T)
         gbps = b / avg
         sym = r["Name"].split("(")[0].replace("void ", "")
+        pct = "-"
+        if per.get(k):
+            q = statistics.quantiles(per[k], n=10)
+            pct = f"{q[0] / 1e3:.2f} / {statistics.median(per[k]) / 1e3:.2f} / {q[-1] / 1e3:.2f}"
         lines.append(f"| {k} | `{sym}` | {r['Calls']} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
-                     f"{mx / 1e3:.2f} | {b} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f}% |"
+                     f"{mx / 1e3:.2f} | {pct} | {b} | {gbps:.0f} | "
+                     f"{100 * gbps / PEAK_HBM_GBPS:.1f}% |"
                      + (f" {events[k]:.2f} |" if events else ""))
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -784,7 +825,7 @@ def main() -> int:
                              f"(1536 FP8 group-128 / 512 bf16)",
                     T=T, io="bf16 in; e4m3fn codes + fp32 scales / bf16 out; fp32 arithmetic",
                     step_bytes=step_bytes),
-        kernels=kern, roofline=roofline,
+        kernels=kern, roofline=roofline, env=environment(),
     )
     ceiling = copy_ceiling()
     for n in KERNELS:
