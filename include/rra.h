@@ -24,6 +24,8 @@
  *   allocates nothing, keeps no mutable state, never synchronizes, and only
  *   enqueues work on `stream` (a hipStream_t; NULL = the null stream).  Calls
  *   are therefore reentrant and may be captured into a HIP graph.
+ * - Sizes: a launch covers T with at most 2^31 - 1 workgroups (one row or
+ *   token per workgroup for most ops); a larger T returns RRA_ERR_UNSUPPORTED.
  * - Errors: each function returns RRA_OK (0) or a negative rra_status.  All
  *   argument checks run on the host before anything is launched, so an error
  *   return means nothing was enqueued.  T == 0 returns RRA_OK without a launch;

@@ -445,6 +445,7 @@ static int launch_add_rmsnorm(int64_t T, int H, int H_pad, hipStream_t st, const
                               float* scales, int dtype) {
   const int kw = norm_waves_per_row(H);
   const int nv = static_cast<int>(ceil_div(H, 8 * kWave * kw));
+  RRA_REQUIRE(ceil_div(T, kWavesPerBlock / kw) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);  // grid.x
   const NormLaunch a{dim3(static_cast<unsigned>(ceil_div(T, kWavesPerBlock / kw))),
                      st, x, xs, res, rs, w, eps, sscale, out, os, scales, T, H, H_pad};
 #define RRA_NORM_CASE(N, W)                                   \
@@ -623,6 +624,7 @@ extern "C" int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uin
   RRA_REQUIRE(!q_scales || aligned(q_scales, 4), RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
 
+  RRA_REQUIRE(ceil_div(T, kWavesPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);  // grid.x
   // One wave per token: NVQ = ceil(Hq / 512) and NVKV = ceil(Hkv / 512) vectors per lane.
   const int nvq = static_cast<int>(ceil_div(Hq, 8 * kWave));
   const int nvkv = static_cast<int>(ceil_div(Hkv, 8 * kWave));

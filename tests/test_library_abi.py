@@ -90,6 +90,7 @@ def test_norm_validation(rra):
     # with T == 0 the per-row tensors may be NULL (empty tensors), the weight may not
     assert norm(L, x=None, res=None, out=None, sc=None, T=0) == OK
     assert norm(L, w=None, T=0) == ENULL
+    assert norm(L, T=(1 << 31) + 5) == EUNSUP  # one row per workgroup: grid above 2^31 - 1
 
 
 def test_silu_validation(rra):
@@ -164,6 +165,7 @@ def test_dual_validation(rra):
     assert f(Hq=4096, qs=4096, qos=4096) == EUNSUP
     assert f(kv=A + 8, T=0) == EALIGN  # alignment is checked before the T == 0 early return
     assert f(g=64, Hq=1000, qs=1000, qos=1000) == ESHAPE  # 64 does not divide 1000
+    assert f(T=4 << 31) == EUNSUP  # four tokens per workgroup: grid above 2^31 - 1
 
 
 def test_qk_norm_rope_validation(rra):
