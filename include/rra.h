@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define RRA_ABI_VERSION 3
+#define RRA_ABI_VERSION 4
 
 enum rra_status {
   RRA_OK = 0,
@@ -297,15 +297,19 @@ int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64_t q_stride
 int rra_e4m3fn_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 
 /*
- * Diagnostic: dst[0:nbytes) = src[0:nbytes), one 16-byte vector per lane,
- * loaded and stored with the same streaming cache policy as the fused kernels'
+ * Diagnostic: dst[0:nbytes) = src[0:nbytes), vectors_per_lane 16-byte vectors
+ * per lane (1, 2, 4 or 8: all of a lane's loads, then its stores), loaded and
+ * stored with the same streaming cache policy as the fused kernels'
  * activations.  It is the bandwidth yardstick the fused kernels are measured
- * against (a copy of the same number of bytes at the same size).
+ * against (a copy of the same number of bytes; the fastest vectors_per_lane
+ * differs with the size).
  * src, dst: device pointers, 16-byte aligned; nbytes % 16 == 0 (else
- * RRA_ERR_ALIGN); the two ranges must not overlap (else RRA_ERR_SHAPE).
- * nbytes == 0 launches nothing.
+ * RRA_ERR_ALIGN); the two ranges must not overlap (else RRA_ERR_SHAPE);
+ * another vectors_per_lane gives RRA_ERR_UNSUPPORTED.  nbytes == 0 launches
+ * nothing.
  */
-int rra_stream_copy(const void* src, void* dst, int64_t nbytes, void* stream);
+int rra_stream_copy(const void* src, void* dst, int64_t nbytes, int vectors_per_lane,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ class RRAError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 3  # RRA_ABI_VERSION of include/rra.h
+ABI_VERSION = 4  # RRA_ABI_VERSION of include/rra.h
 BF16, F16 = 0, 1  # enum rra_dtype
 _ELEM = {torch.bfloat16: BF16, torch.float16: F16}
 
@@ -72,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.mla_rope_kv_write.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p,
                                         _i64, _i32, _i32, _i32, _i32, _i64, _i32, _p]
         L.rra_e4m3fn_encode.argtypes = [_p, _p, _i64, _p]
-        L.rra_stream_copy.argtypes = [_p, _p, _i64, _p]
+        L.rra_stream_copy.argtypes = [_p, _p, _i64, _i32, _p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = _i32
         _lib = L
@@ -382,9 +382,10 @@ def e4m3fn_encode(x, out=None):
     return out
 
 
-def stream_copy(src, dst):
+def stream_copy(src, dst, vectors_per_lane=1):
     """dst <- src (same byte size, contiguous, non-overlapping) with the fused
-    kernels' streaming loads and stores: the bandwidth yardstick (diagnostic)."""
+    kernels' streaming loads and stores, vectors_per_lane (1, 2, 4 or 8)
+    16-byte vectors per lane: the bandwidth yardstick (diagnostic)."""
     for name, t in (("src", src), ("dst", dst)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError(f"{name} must be a GPU tensor")
@@ -394,6 +395,7 @@ def stream_copy(src, dst):
     if not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("stream_copy: src and dst must be contiguous")
     with torch.cuda.device(src.device):
-        st = lib().rra_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(src))
+        st = lib().rra_stream_copy(_ptr(src), _ptr(dst), nbytes, int(vectors_per_lane),
+                                   _stream(src))
     _check("rra_stream_copy", st)
     return dst

@@ -112,10 +112,11 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // left by rounding s to fp32 decides the side.  An fp32 quotient cannot see d.
 // So each value is first rounded as v = fp32(t * f) with f ~ fp32(rho / s)
 // (within 3 fp32 ulps of q); where v lies within 8 ulps of a midpoint, or in
-// the e4m3 subnormal range, q = t * rho / s is recomputed in double and
-// narrowed to fp32 with round-to-odd, after which the single hardware rounding
-// to e4m3 is the correct rounding of q (fp32 keeps 20 more fraction bits than
-// e4m3; round-to-odd makes the double rounding innocuous).
+// the e4m3 subnormal range, q = (t * rho) / s is recomputed in double (the
+// quotient correctly rounded) and narrowed to fp32 with round-to-odd, after
+// which the single hardware rounding to e4m3 is the correct rounding of q
+// (fp32 keeps 20 more fraction bits than e4m3; round-to-odd makes the double
+// rounding innocuous).
 
 // True when v (an fp32 estimate of q) may round differently from q: its 20
 // fraction bits below e4m3's three lie within [-8, +7] ulps of 0x80000 (one
@@ -166,10 +167,22 @@ __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
     exact |= near[j];
   }
   if (exact && qs.s > 0.0f) {
-    const double g = qs.rho / static_cast<double>(qs.s);
+    // q = p / s for p = t * rho, correctly rounded: q0 = p * y with y the
+    // rounded reciprocal of s, then one correction with the residual
+    // p - q0 * s, which an fma gives exactly (Markstein's final division
+    // step).  Taking p * (rho / s) instead can miss an exact midpoint by an
+    // ulp of the double, and the round-to-odd narrowing would then move a
+    // true tie off it.
+    const double sd = static_cast<double>(qs.s);
+    const double y = 1.0 / sd;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (near[j]) v[j] = f32_round_odd(static_cast<double>(t[j]) * g);
+    for (int j = 0; j < 8; ++j) {
+      if (near[j]) {
+        const double p = static_cast<double>(t[j]) * qs.rho;
+        const double q0 = p * y;
+        v[j] = f32_round_odd(fma(fma(-q0, sd, p), y, q0));
+      }
+    }
   }
   return u32x2{pack_e4m3x4<kClamp>(v[0], v[1], v[2], v[3]),
                pack_e4m3x4<kClamp>(v[4], v[5], v[6], v[7])};

@@ -67,3 +67,31 @@ def read_rows(name: str) -> list:
             if line:
                 rows.append(line.split())
     return rows
+
+
+# Exact ties through the whole op.  A row whose only nonzero is z0, with
+# eps = 1 - z0^2 / H, has mean(z^2) + eps = 1 and so rho = 1 exactly; with
+# weight w0 its output is y0 = z0 * w0 exactly, and the static scale s is
+# chosen so that y0 / s is exactly the midpoint m between two adjacent e4m3fn
+# values.  The code must then be the one with the even mantissa (round to
+# nearest, ties to even, of the exact quotient).  For every s below the double
+# reciprocal of s is inexact enough that y0 * (1/s) misses m (the last column
+# says to which side), so a quotient taken by a reciprocal fails this pin.
+# Columns: s, m, z0, w0, eps, the expected code, side of y0 * (1/s).
+TIE_CASES = [
+    (1.095703125, 0.0009765625, 0.0029296875, 0.365234375, 0.999998927116394, 0, "down"),
+    (1.171875, 0.0068359375, 0.0029296875, 2.734375, 0.999998927116394, 4, "up"),
+    (1.736328125, 0.0185546875, 0.1240234375, 0.259765625, 0.9980772733688354, 10, "up"),
+    (1.416015625, 0.048828125, 0.1220703125, 0.56640625, 0.998137354850769, 20, "down"),
+    (1.921875, 0.265625, 0.0166015625, 30.75, 0.9999655485153198, 40, "up"),
+    (1.416015625, 1.5625, 0.1220703125, 18.125, 0.998137354850769, 60, "down"),
+    (1.921875, 8.5, 0.0166015625, 984.0, 0.9999655485153198, 80, "up"),
+    (1.416015625, 50.0, 0.1220703125, 580.0, 0.998137354850769, 100, "down"),
+    (1.421875, 184.0, 0.0126953125, 20608.0, 0.9999798536300659, 116, "up"),
+]
+
+
+def e4m3_value(code: int) -> float:
+    """Value of a non-negative e4m3fn code from the format definition."""
+    e, m = code >> 3, code & 7
+    return m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)

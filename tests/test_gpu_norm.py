@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import workloads
+from helpers import TIE_CASES
 from gpu_util import (assert_codes, assert_scales, dev_bf16, host_bf16, host_f32, host_u8,
                       require_gpu, sample_rows, say)
 
@@ -153,3 +154,25 @@ def test_error_is_raised(rra):
     w = torch.ones(1000, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(rra.RRAError):
         rra.fused_add_rmsnorm_quant(x, None, w, 1e-6, 3, 128)
+
+
+@pytest.mark.parametrize("s,m,z0,w0,eps,code,side", TIE_CASES)
+def test_exact_tie_rounds_to_even(rra, s, m, z0, w0, eps, code, side):
+    """Rows built so that y / s is exactly an e4m3 midpoint (rho = 1, y = z0 *
+    w0, static scale s): the code must be the even one, bit for bit, here as
+    in the oracle's pin.  Nine rows of 1024, one launch (several workgroups,
+    and the same row at every T position)."""
+    import torch
+
+    say(f"[norm] exact tie m={m} s={s}")
+    H, T = 8, 1024
+    x = torch.zeros((T, H), dtype=torch.float32)
+    x[:, 0] = z0
+    w = torch.ones(H, dtype=torch.float32)
+    w[0] = w0
+    x, w = x.to(torch.bfloat16).cuda(), w.to(torch.bfloat16).cuda()
+    ss = torch.tensor([s], dtype=torch.float32, device="cuda")
+    out, _ = rra.fused_add_rmsnorm_quant(x, None, w, eps, 1, 0, ss)
+    torch.cuda.synchronize()
+    got = out.view(torch.uint8).cpu().numpy()
+    assert (got[:, 0] == code).all() and not got[:, 1:].any(), (got[:, 0][:4], code)

@@ -54,7 +54,7 @@ def test_library_exports_every_declared_function(rra):
 
 
 def test_version_and_status_strings(rra):
-    assert rra.abi_version() == rra.ABI_VERSION == 3
+    assert rra.abi_version() == rra.ABI_VERSION == 4
     for s in (OK, ENULL, ESHAPE, EALIGN, EUNSUP, -5):
         assert rra.status_string(s) and rra.status_string(s) != "unknown status"
     assert rra.status_string(-99) == "unknown status"
@@ -248,12 +248,14 @@ def test_e4m3_diag_validation(rra):
 
 def test_stream_copy_validation(rra):
     L = rra.lib()
-    assert L.rra_stream_copy(None, A + 4096, 16, None) == ENULL
-    assert L.rra_stream_copy(A, None, 16, None) == ENULL
-    assert L.rra_stream_copy(A, A + 4096, -16, None) == ESHAPE
-    assert L.rra_stream_copy(A, A + 4096, 24, None) == EALIGN  # not a whole number of vectors
-    assert L.rra_stream_copy(A + 8, A + 4096, 16, None) == EALIGN
-    assert L.rra_stream_copy(A, A + 4104, 16, None) == EALIGN
-    assert L.rra_stream_copy(A, A + 16, 32, None) == ESHAPE  # overlapping ranges
-    assert L.rra_stream_copy(A + 16, A, 32, None) == ESHAPE
-    assert L.rra_stream_copy(None, None, 0, None) == OK
+    assert L.rra_stream_copy(None, A + 4096, 16, 1, None) == ENULL
+    assert L.rra_stream_copy(A, None, 16, 1, None) == ENULL
+    assert L.rra_stream_copy(A, A + 4096, -16, 1, None) == ESHAPE
+    assert L.rra_stream_copy(A, A + 4096, 24, 1, None) == EALIGN  # not a whole number of vectors
+    assert L.rra_stream_copy(A + 8, A + 4096, 16, 1, None) == EALIGN
+    assert L.rra_stream_copy(A, A + 4104, 16, 1, None) == EALIGN
+    assert L.rra_stream_copy(A, A + 16, 32, 1, None) == ESHAPE  # overlapping ranges
+    assert L.rra_stream_copy(A + 16, A, 32, 1, None) == ESHAPE
+    assert L.rra_stream_copy(A, A + 4096, 16, 3, None) == EUNSUP  # vectors per lane
+    assert L.rra_stream_copy(A, A + 4096, 16, 16, None) == EUNSUP
+    assert L.rra_stream_copy(None, None, 0, 1, None) == OK

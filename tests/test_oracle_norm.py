@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads
-from helpers import bf16_to_f64, code_ulp_diff, read_kv, torch_e4m3fn
+from helpers import TIE_CASES, bf16_to_f64, code_ulp_diff, e4m3_value, read_kv, torch_e4m3fn
 
 
 def _bf16(vals):
@@ -189,3 +189,28 @@ def test_argument_errors(oracle):
         oracle.fused_add_rmsnorm_quant(d["x"], None, d["weight"], 1e-6, 7)
     out = oracle.fused_add_rmsnorm_quant(d["x"][:0], None, d["weight"], 1e-6, 2)
     assert out[0].shape == (0, 1000)
+
+
+def tie_row(z0, w0, H=8):
+    x = _bf16([z0] + [0.0] * (H - 1))[None, :]
+    w = _bf16([w0] + [1.0] * (H - 1))
+    return x, w
+
+
+@pytest.mark.parametrize("s,m,z0,w0,eps,code,side", TIE_CASES)
+def test_exact_tie_rounds_to_even(oracle, s, m, z0, w0, eps, code, side):
+    from fractions import Fraction as F
+
+    H = 8
+    # the construction is exact in every step
+    assert all(float(np.float32(v)) == v for v in (s, eps, z0, w0))
+    assert F(z0) ** 2 / H + F(eps) == 1 and F(z0) * F(w0) / F(s) == F(m)
+    # m is half-way between the expected code and a neighbour, and that code is even
+    lo, hi = (code - 1, code) if e4m3_value(code) > m else (code, code + 1)
+    assert F(e4m3_value(lo)) + F(e4m3_value(hi)) == 2 * F(m) and code % 2 == 0
+    # the reciprocal form misses the midpoint on the recorded side
+    assert (z0 * w0 * (1.0 / s) > m) == (side == "up") and z0 * w0 * (1.0 / s) != m
+    x, w = tie_row(z0, w0, H)
+    codes, _, _ = oracle.fused_add_rmsnorm_quant(x, None, w, eps, oracle.Q_STATIC,
+                                                  static_scale=s)
+    assert codes[0, 0] == code and not codes[0, 1:].any()
