@@ -434,9 +434,14 @@ def _timed_launches(hip, stream, cyc, fns, n: int) -> float:
     return ms
 
 
-def copy_yardstick(nbytes_moved: int, launches: int, hip, stream, cyc) -> float:
-    """Median ms of a streaming copy that moves nbytes_moved bytes in all
-    (half read, half written), cold, timed like the sweep's kernels."""
+COPY_VECTORS_PER_LANE = (1, 2, 4, 8)
+
+
+def copy_yardstick(nbytes_moved: int, launches: int, hip, stream, cyc):
+    """(median ms, vectors per lane) of the fastest streaming copy that moves
+    nbytes_moved bytes in all (half read, half written), cold, timed like the
+    sweep's kernels; the copy is tried with 1, 2, 4 and 8 vectors per lane,
+    whose best choice changes with the size."""
     import torch
 
     import rope_residual_add_amd as rra
@@ -445,14 +450,18 @@ def copy_yardstick(nbytes_moved: int, launches: int, hip, stream, cyc) -> float:
     n_sets = max(2, min(256, -(-(1 << 30) // (2 * half))))
     bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
              torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(n_sets)]
-    fns = [lambda a=a, b=b: rra.stream_copy(a, b) for a, b in bufs]
-    for f in fns:
-        f()
-    torch.cuda.synchronize()
-    ms = _timed_launches(hip, stream, cyc, fns, launches)
-    del bufs, fns
+    best = None
+    for v in COPY_VECTORS_PER_LANE:
+        fns = [lambda a=a, b=b, v=v: rra.stream_copy(a, b, v) for a, b in bufs]
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        ms = _timed_launches(hip, stream, cyc, fns, launches)
+        if best is None or ms < best[0]:
+            best = (ms, v)
+    del bufs
     torch.cuda.empty_cache()
-    return ms
+    return best
 
 
 def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS, with_copy: bool = True):
@@ -489,8 +498,9 @@ def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS, with_copy: bool = T
                        frac=round(gbps / PEAK_HBM_GBPS, 4),
                        tokens_per_s=round(T / (ms * 1e-3), 1), buffer_sets=n_sets)
             if with_copy:
-                cms = copy_yardstick(b, launches_per_point, hip, stream, cyc)
-                row.update(copy_us=round(cms * 1e3, 2), frac_of_copy=round(cms / ms, 4))
+                cms, cv = copy_yardstick(b, launches_per_point, hip, stream, cyc)
+                row.update(copy_us=round(cms * 1e3, 2), copy_vectors_per_lane=cv,
+                           frac_of_copy=round(cms / ms, 4))
             rows.append(row)
             log(f"sweep {n:26s} T={T:6d} {ms * 1e3:9.2f} us {gbps:8.1f} GB/s "
                 f"({100 * gbps / PEAK_HBM_GBPS:5.1f}% of peak), {n_sets} buffer sets"
@@ -691,26 +701,37 @@ def summarize_sweep(trace_csv: str, out: str, command: str, Ts, kernels=KERNELS)
     import collections
     import csv
 
-    dur = collections.defaultdict(list)  # (kernel or "copy", grid work-items) -> ns
+    import re
+
+    dur = collections.defaultdict(list)  # (kernel or ("copy", V), grid work-items) -> ns
     for r in csv.DictReader(open(trace_csv)):
         name = r["Kernel_Name"]
-        k = "copy" if "rra::stream_copy_kernel" in name else _kernel_of(name)
+        m = re.search(r"rra::stream_copy_kernel<(\d+)>", name)
+        k = ("copy", int(m.group(1))) if m else _kernel_of(name)
         if k is None:
             continue
         dur[(k, int(r["Grid_Size_X"]))].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
 
-    def copy_grid(nbytes_moved):
-        return 256 * -(-(copy_half_bytes(nbytes_moved) // 16) // 256)
+    def copy_best(nbytes_moved):
+        """(median ns, vectors per lane) of the fastest copy of that size."""
+        n16 = copy_half_bytes(nbytes_moved) // 16
+        best = None
+        for v in COPY_VECTORS_PER_LANE:
+            d = dur.get((("copy", v), 256 * -(-n16 // (256 * v))))
+            if d and (best is None or statistics.median(d) < best[0]):
+                best = (statistics.median(d), v)
+        return best
 
     lines = ["# Kernel trace: each fused kernel alone, cold, across token counts", "",
              "Produced by (from the repository root, after `cd /tmp && export TMPDIR=/tmp` for "
              "the profiler):", "", "```", command, "```", "",
              "Each point rotates over buffer sets holding at least 1 GiB, so every launch reads "
              "cold data. Durations are the profiler's (median over the point's launches). "
-             "`copy` is the library's streaming copy (`rra_stream_copy`, the fused kernels' own "
-             "loads and stores) moving the same number of bytes, half read and half written, "
-             "timed the same way; `% of copy` = copy time / kernel time.", "",
-             "| kernel | T | launches | median us | GB/s | % of 8 TB/s | tokens/s | copy us | "
+             "`copy` is the fastest of the library's streaming copies (`rra_stream_copy`, the "
+             "fused kernels' own loads and stores, with 1, 2, 4 or 8 vectors per lane: `vpl`) "
+             "moving the same number of bytes, half read and half written, timed the same way; "
+             "`% of copy` = copy time / kernel time.", "",
+             "| kernel | T | launches | median us | GB/s | % of 8 TB/s | tokens/s | copy us (vpl) | "
              "% of copy |", "|---|---|---|---|---|---|---|---|---|"]
     for T in Ts:
         for k in kernels:
@@ -719,12 +740,12 @@ def summarize_sweep(trace_csv: str, out: str, command: str, Ts, kernels=KERNELS)
                 continue
             med = statistics.median(d)
             b = algo_bytes(k, T)
-            c = dur.get(("copy", copy_grid(b)))
-            cmed = statistics.median(c) if c else None
+            c = copy_best(b)
             lines.append(f"| {k} | {T} | {len(d)} | {med / 1e3:.2f} | {b / med:.0f} | "
                          f"{100 * b / med / PEAK_HBM_GBPS:.1f}% | {T / (med * 1e-9):.3g} | "
-                         + (f"{cmed / 1e3:.2f} | {100 * cmed / med:.1f}% |" if cmed else "- | - |"))
-    floor = dur.get(("copy", copy_grid(8192)))
+                         + (f"{c[0] / 1e3:.2f} ({c[1]}) | {100 * c[0] / med:.1f}% |" if c
+                            else "- | - |"))
+    floor = dur.get((("copy", 1), 256))
     if floor:
         lines += ["", f"One-workgroup copy (launch floor), profiler median: "
                       f"{statistics.median(floor) / 1e3:.2f} us over {len(floor)} launches."]
@@ -837,8 +858,8 @@ def main() -> int:
     if args.sweep:
         result["sweep"] = sweep([int(t) for t in args.sweep.split(",") if t])
         hip = HipEvents()
-        floor_ms = copy_yardstick(8192, 30, hip, torch.cuda.current_stream().cuda_stream,
-                                  _blocker_cycles())
+        floor_ms, _ = copy_yardstick(8192, 30, hip, torch.cuda.current_stream().cuda_stream,
+                                     _blocker_cycles())
         result["launch_floor_us"] = round(floor_ms * 1e3, 2)
         log(f"launch floor (one-workgroup copy, timed as the sweep): {floor_ms * 1e3:.2f} us")
     if args.cpu_sample > 0:

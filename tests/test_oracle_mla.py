@@ -56,6 +56,26 @@ def test_constant_row_closed_form(oracle, c, eps):
     assert np.array_equal(kv_out[0], expect)
 
 
+@pytest.mark.parametrize("cq,eps_q,ckv,eps_kv", [(0.1, 1e-2, 0.25, 1e-6), (0.3, 1e-6, 0.1, 3e-2)])
+def test_each_side_uses_its_own_weight_and_eps(oracle, cq, eps_q, ckv, eps_kv):
+    """Constant rows whose epsilons matter (c^2 and eps of the same order), with
+    different weights and epsilons on the two sides: a side that took the
+    other's weight or eps would be off by far more than a bf16 step."""
+    wq = _bf16([1.0, 0.5, -0.75, 2.0] * 384)
+    wkv = _bf16([1.5, -0.25, 0.75, 1.0] * 128)
+    q = _bf16([[cq] * 1536])
+    kv = _bf16([[ckv] * 512])
+    q_out, _, kv_out = oracle.dual_rmsnorm_quant(q, wq, eps_q, kv, wkv, eps_kv, 0)
+    for out, c, eps, w in ((q_out, cq, eps_q, wq), (kv_out, ckv, eps_kv, wkv)):
+        cb = float(bf16_to_f64(_bf16([c]))[0])  # the row value as stored
+        y = cb / math.sqrt(cb * cb + float(np.float32(eps))) * bf16_to_f64(w)
+        got = bf16_to_f64(out[0])
+        assert np.allclose(got, y, rtol=2 ** -8, atol=0)
+        # the other side's eps or weight would not do
+        other = cb / math.sqrt(cb * cb + float(np.float32(eps_kv if eps == eps_q else eps_q)))
+        assert not np.allclose(got[:4], other * bf16_to_f64(w)[:4], rtol=2 ** -6)
+
+
 def test_unit_rms_with_zero_eps(oracle):
     d = workloads.mla_inputs(4)
     w = _bf16([1.0] * 512)
