@@ -204,18 +204,35 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, kRowMask, 0xF, true));
 }
 
-// Max over each aligned group of 8 lanes, result in all 8.
-__device__ __forceinline__ float max8(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  return v;
+// The max reductions take non-negative values only (amaxes of |x|), whose
+// bit patterns order like unsigned integers: the cross-lane steps compare the
+// bits with v_max_u32, which needs no NaN canonicalization (fmaxf adds one
+// instruction per step) and takes the DPP move as an operand modifier.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(v), kCtrl, kRowMask, 0xF, true));
 }
 
-// Max over each 16-lane row, result in all 16.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t max_step(uint32_t u) {
+  const uint32_t o = dpp_u32<kCtrl, kRowMask>(u);
+  return u > o ? u : o;
+}
+
+// Max over each aligned group of 8 lanes (inputs >= 0), result in all 8.
+__device__ __forceinline__ float max8(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = max_step<0xB1>(u);
+  u = max_step<0x4E>(u);
+  u = max_step<0x141>(u);
+  return __uint_as_float(u);
+}
+
+// Max over each 16-lane row (inputs >= 0), result in all 16.
 __device__ __forceinline__ float max16(float v) {
-  v = max8(v);
-  return fmaxf(v, dpp<0x140>(v));
+  uint32_t u = __float_as_uint(max8(v));
+  return __uint_as_float(max_step<0x140>(u));
 }
 
 __device__ __forceinline__ float sum16(float v) {
@@ -266,10 +283,10 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 // Max over the whole wave (inputs >= 0); wave-uniform result.
 __device__ __forceinline__ float wave_max(float v) {
-  v = max16(v);
-  v = fmaxf(v, dpp<0x142, 0xA>(v));
-  v = fmaxf(v, dpp<0x143, 0xC>(v));
-  return readlane63(v);
+  uint32_t u = __float_as_uint(max16(v));
+  u = max_step<0x142, 0xA>(u);
+  u = max_step<0x143, 0xC>(u);
+  return readlane63(__uint_as_float(u));
 }
 
 // Index of this lane's wave inside its workgroup, as a wave-uniform value.
