@@ -338,21 +338,28 @@ def make_launchers(T: int, salt: int = 0, shared=None, only=KERNELS):
 
 def run_steps(launch, steps: int, warmup: int):
     """Warm up, then time `steps` passes over the four kernels (launch: the
-    dict of make_launchers).  Returns
-    (wall seconds for the timed steps, {kernel: [per-launch ms]})."""
+    dict of make_launchers) twice: first with nothing between the launches,
+    for the whole step's wall time, then with HIP events around every launch,
+    for each kernel's duration.  Returns
+    (wall seconds for the first timed steps, {kernel: [per-launch ms]})."""
     import torch
 
     for _ in range(warmup):
         for n in KERNELS:
             launch[n]()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for n in KERNELS:
+            launch[n]()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
 
     hip = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
     nk = len(KERNELS)
     ev = hip.create(steps * (nk + 1))
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(steps):
         base = s * (nk + 1)
         hip.record(ev[base], stream)
@@ -360,7 +367,6 @@ def run_steps(launch, steps: int, warmup: int):
             launch[n]()
             hip.record(ev[base + i + 1], stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = {n: [hip.ms(ev[s * (nk + 1) + i], ev[s * (nk + 1) + i + 1]) for s in range(steps)]
            for i, n in enumerate(KERNELS)}
     hip.destroy(ev)
