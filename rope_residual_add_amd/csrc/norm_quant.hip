@@ -287,13 +287,14 @@ __global__ void __launch_bounds__(kBlock)
                                                                H_pad);
 }
 
-// MLA dual RMSNorm: the q and kv latents of a token are two rows handled by
-// the same kW waves (NVQ and NVKV vectors per row lane); both row reductions
-// share one LDS exchange.  Measured on MI355X at the DeepSeek-V3 shape, one
-// wave per token (four tokens per workgroup) beats spreading a token over
-// more waves: the rows are short, and a barrier per token costs more than the
-// extra vectors per lane.
-template <int NVQ, int NVKV, int kW, int kMode, int kGroup, bool kFull>
+// MLA dual RMSNorm: one wave per token handles both of its rows, the q latent
+// (NVQ vectors per lane) and the kv latent (NVKV), so both row reductions are
+// wave-local DPP reductions with no LDS exchange and no barrier (four tokens
+// per workgroup; waves past T leave at once).  Measured on MI355X at the
+// DeepSeek-V3 shape, this beats spreading a token over 2 or 4 waves at every
+// T from 512 to 16384: the rows are short, and a barrier per token costs more
+// than the extra vectors per lane.
+template <int NVQ, int NVKV, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
     dual_rmsnorm_quant_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
                               const uint16_t* __restrict__ q_w, float eps_q,
@@ -302,27 +303,18 @@ __global__ void __launch_bounds__(kBlock)
                               void* __restrict__ q_out, int64_t q_out_stride,
                               float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
                               int64_t kv_out_stride, int64_t T, int Hq, int Hkv) {
-  constexpr int kRowsPerBlock = kWavesPerBlock / kW;
-  constexpr int kStride = kW * kWave;
-  __shared__ double lds_q[kWavesPerBlock];
-  __shared__ double lds_kv[kWavesPerBlock];
-  __shared__ float lds_m[kWavesPerBlock];
-  const int wave = wave_id();
-  const int wave_in_row = wave % kW;
-  const int rl = wave_in_row * kWave + lane_id();
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave / kW;
-  // With one wave per token there is no barrier: waves past T leave at once.
-  if (kW == 1 && row >= T) return;
-  const bool active = kW == 1 || row < T;
+  const int rl = lane_id();
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
+  if (row >= T) return;
   const int nq = Hq >> 3, nkv = Hkv >> 3;
 
   // Issue every load of the token before either reduction.
   RowVecs<NVQ> zq, wq;
   RowVecs<NVKV> zkv, wkv;
-  load_row<NVQ, true, kFull>(zq, q + row * q_stride, nq, rl, kStride, active);
-  load_row<NVKV, true, kFull>(zkv, kv + row * kv_stride, nkv, rl, kStride, active);
-  load_row<NVQ, false, kFull>(wq, q_w, nq, rl, kStride, true);
-  load_row<NVKV, false, kFull>(wkv, kv_w, nkv, rl, kStride, true);
+  load_row<NVQ, true, kFull>(zq, q + row * q_stride, nq, rl, kWave, true);
+  load_row<NVKV, true, kFull>(zkv, kv + row * kv_stride, nkv, rl, kWave, true);
+  load_row<NVQ, false, kFull>(wq, q_w, nq, rl, kWave, true);
+  load_row<NVKV, false, kFull>(wkv, kv_w, nkv, rl, kWave, true);
 
   RowT<NVQ> tq;
   RowT<NVKV> tkv;
@@ -332,26 +324,7 @@ __global__ void __launch_bounds__(kBlock)
   row_prepare(zkv, wkv, false, tkv, ss_kv, m_kv);
   ss_q = wave_sum_f64(ss_q);
   ss_kv = wave_sum_f64(ss_kv);
-  m_q = wave_max(m_q);
-  if (kW > 1) {
-    if (lane_id() == 0) {
-      lds_q[wave] = ss_q;
-      lds_kv[wave] = ss_kv;
-      lds_m[wave] = m_q;
-    }
-    __syncthreads();
-    const int s0 = (wave / kW) * kW;
-    ss_q = lds_q[s0];
-    ss_kv = lds_kv[s0];
-    m_q = lds_m[s0];
-#pragma unroll
-    for (int j = 1; j < kW; ++j) {
-      ss_q += lds_q[s0 + j];
-      ss_kv += lds_kv[s0 + j];
-      m_q = fmaxf(m_q, lds_m[s0 + j]);
-    }
-  }
-  if (!active) return;
+  if (kMode == RRA_Q_PER_TOKEN) m_q = wave_max(m_q);
 
   void* qo;
   float* scale_row = nullptr;
@@ -364,9 +337,9 @@ __global__ void __launch_bounds__(kBlock)
   // kv first: its short row then leaves the registers before q's quantization
   // needs them (at the DeepSeek-V3 shape this keeps the kernel within 64 VGPRs,
   // i.e. 8 waves per SIMD, so 8192 one-wave tokens are resident at once).
-  rmsnorm_emit<NVKV, RRA_Q_NONE, 0, kFull>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kStride, 0.0f,
+  rmsnorm_emit<NVKV, RRA_Q_NONE, 0, kFull>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kWave, 0.0f,
                                            kv_out + row * kv_out_stride, nullptr);
-  rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kStride, 0.0f, qo,
+  rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kWave, 0.0f, qo,
                                           scale_row);
 }
 
@@ -486,7 +459,7 @@ struct DualLaunch {
 
 template <int A, int B, bool kFull, int kMode, int kGroup>
 static void launch_dual(const DualLaunch& a) {
-  hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, 1, kMode, kGroup, kFull>), a.grid,
+  hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, kMode, kGroup, kFull>), a.grid,
                      dim3(kBlock), 0,
                      a.st, a.q, a.qs, a.qw, a.eps_q, a.kv, a.kvs, a.kvw, a.eps_kv, a.q_out, a.qos,
                      a.q_scales, a.kv_out, a.kvos, a.T, a.Hq, a.Hkv);
