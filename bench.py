@@ -530,22 +530,17 @@ def environment() -> dict:
 
 # ---- CPU baseline: the oracle on a bounded sample --------------------------------
 
-def cpu_baseline(sample_T: int):
+def _oracle_calls(n: int) -> dict:
+    """{kernel: zero-argument oracle call} on n tokens of each kernel's workload."""
     import oracle
     import workloads
 
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
     cfg = workloads.ROPE
-    n = sample_T
     dn = workloads.norm_inputs(n, H_NORM)
     ds = workloads.silu_inputs(n, I_SILU)
     dr = workloads.rope_inputs(n, cfg)
     dm = workloads.mla_inputs(n)
-    calls = {
+    return {
         "fused_add_rmsnorm_quant": lambda: oracle.fused_add_rmsnorm_quant(
             dn["x"], dn["residual"], dn["weight"], 1e-5, oracle.Q_PER_TOKEN),
         "silu_mul_quant": lambda: oracle.silu_mul_quant(ds["inp"], oracle.Q_PER_GROUP, G),
@@ -555,7 +550,23 @@ def cpu_baseline(sample_T: int):
         "dual_rmsnorm_quant": lambda: oracle.dual_rmsnorm_quant(
             dm["q"], dm["q_w"], 1e-6, dm["kv"], dm["kv_w"], 1e-6, oracle.Q_PER_GROUP, G),
     }
-    def timed(threads):
+
+
+def cpu_baseline(T: int, one_core_T: int = 1024) -> dict:
+    """The oracle as it stands, timed on the host's cores: all of them (up to
+    16) on the GPU step's own workload at T tokens, and one core on one_core_T
+    tokens.  Reported in GB/s of the same algorithmic bytes as the GPU, with
+    tokens/s per kernel."""
+    import oracle
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+
+    def timed(n, threads):
+        calls = _oracle_calls(n)
         oracle.set_threads(threads)
         secs = {}
         for name, f in calls.items():
@@ -568,23 +579,25 @@ def cpu_baseline(sample_T: int):
             secs[name] = statistics.median(ts)
             log(f"oracle {name:26s} T={n} {secs[name] * 1e3:8.1f} ms on {oracle.get_threads()} "
                 f"threads")
-        return secs
+        return secs, int(oracle.get_threads())
 
-    total_bytes = sum(algo_bytes(k, n) for k in KERNELS)
-    one = timed(1)
-    secs = timed(cores)
-    cores = int(oracle.get_threads())  # the threads the timed calls actually used
-    total_s = sum(secs.values())
-    return dict(value=round(total_bytes / total_s / 1e9, 4), unit="GB/s",
-                cores=cores, kind="oracle",
-                sample=f"T={n} tokens of each of the four kernels' workloads (the GPU step "
-                       f"uses T=8192); fp64 C oracle, OpenMP over rows, median of 3 calls "
-                       f"after one warm-up; bytes counted as for the GPU; one_core: the same "
-                       f"on one thread. The RoPE oracle returns fresh copies of both 128 MiB caches on "
-                       f"every call, which dominates its time at this sample size",
-                per_kernel_ms={k: round(v * 1e3, 2) for k, v in secs.items()},
-                one_core=dict(value=round(total_bytes / sum(one.values()) / 1e9, 4), unit="GB/s",
-                              per_kernel_ms={k: round(v * 1e3, 2) for k, v in one.items()}))
+    def summary(n, secs):
+        total_bytes = sum(algo_bytes(k, n) for k in KERNELS)
+        return dict(value=round(total_bytes / sum(secs.values()) / 1e9, 4), unit="GB/s",
+                    per_kernel_ms={k: round(v * 1e3, 2) for k, v in secs.items()},
+                    tokens_per_s={k: round(n / v, 1) for k, v in secs.items()})
+
+    one, _ = timed(one_core_T, 1)
+    secs, used = timed(T, cores)
+    out = summary(T, secs)
+    out.update(cores=used, kind="oracle",
+               sample=f"the GPU step's workload, T={T} tokens of each of the four kernels; "
+                      f"fp64 C oracle, OpenMP over rows, median of 3 calls after one warm-up; "
+                      f"bytes counted as for the GPU; one_core: T={one_core_T} on one thread. "
+                      f"The RoPE oracle returns fresh copies of both 128 MiB caches on every "
+                      f"call, which is a large part of its time")
+    out["one_core"] = dict(summary(one_core_T, one), T=one_core_T)
+    return out
 
 
 # ---- profile summaries (rocprofv3 CSV -> profiles/*.md) ----------------------------
@@ -603,12 +616,11 @@ def _kernel_of(symbol_name: str):
 
 
 def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=None) -> None:
-    import collections
-
     """Kernel-trace summary: per-kernel average duration and GB/s (and p10 /
     median / p90 from the per-dispatch trace next to the stats file); with
     bench_json (the JSON line the traced run printed), the run's own
     event-timed average per kernel beside the profiler's."""
+    import collections
     import csv
 
     # per-dispatch durations from the kernel trace beside the stats file, if present
@@ -767,7 +779,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--T", type=int, default=8192, help="tokens per step")
-    ap.add_argument("--cpu-sample", type=int, default=1024,
+    ap.add_argument("--cpu-sample", type=int, default=8192,
                     help="tokens per kernel for the oracle baseline (0 = skip)")
     ap.add_argument("--sweep", default="", help="comma-separated token counts for the "
                                                 "per-kernel cold-cache sweep")
@@ -869,7 +881,7 @@ def main() -> int:
         result["launch_floor_us"] = round(floor_ms * 1e3, 2)
         log(f"launch floor (one-workgroup copy, timed as the sweep): {floor_ms * 1e3:.2f} us")
     if args.cpu_sample > 0:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_sample, min(1024, args.cpu_sample))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
