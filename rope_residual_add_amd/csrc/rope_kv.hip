@@ -15,20 +15,25 @@
 // blocks, and every token carries the slot (block * block_size + offset) it
 // writes.
 //
-// Mapping: four waves (256 lanes) per token.  A token's work is cut into
-// units spread over the lanes; each lane takes kU of them per pass (chosen per
-// launch so that one pass covers a typical token) and issues all their loads
-// before its stores.  A rotation unit depends on the pairing:
+// Mapping: W waves per token, as many as the token's units need at one unit
+// per lane (at most 32; beyond that each lane takes kU > 1 units per pass),
+// in ordinary four-wave workgroups: wave g of the launch is wave g % W of
+// token g / W, so a token may straddle two workgroups (the kernels have no
+// barriers).  Each lane issues all its loads before its stores.  Measured at
+// the Llama-3-8B attention shape (384 units): one unit per lane on six waves
+// beats two units per lane on four waves by 3%, while workgroups of six waves
+// (one token each) lose that gain, and fewer, fuller waves are slower still.
+// A rotation unit depends on the pairing:
 //   GPT-NeoX pairs (i, i + D/2): 8 pairs, the 16-byte vectors at columns 8c
 //     and D/2 + 8c of a head;
 //   GPT-J pairs (2i, 2i + 1): 4 pairs, the one 16-byte vector at columns 8c,
 //     so that the 64 lanes of a load or store instruction cover whole, adjacent
 //     cache lines of each head instead of every other 16 bytes of them;
-// a copy unit is one 16-byte vector of v (or of the MLA kv_c).  Unit c of a
+// a copy unit moves v (or the MLA kv_c) without rotating it.  Unit c of a
 // head reads entries kPairs*c .. kPairs*(c + 1) - 1 of the cos and of the sin
-// half of a table row.  A head has D/16 (NeoX) or D/8 (GPT-J) rotation units
-// and the 256 lanes are a multiple of that, so all rotation units of a lane
-// share one c: the lane reads its cos and sin values once per token.
+// half of a table row.  A head has D/16 (NeoX) or D/8 (GPT-J) rotation units,
+// which divides the 64 lanes of a wave, so all rotation units of a lane share
+// one c: the lane reads its cos and sin values once per token.
 #include "rra_device.hpp"
 #include "rra_host.hpp"
 
@@ -36,10 +41,33 @@
 
 namespace rra {
 
-constexpr int kRopeWaves = 4;                     // waves per token
-constexpr int kRopeLanes = kRopeWaves * kWave;    // lanes per token
-constexpr int kRopeTokensPerBlock = kWavesPerBlock / kRopeWaves;
+constexpr int kRopeMaxWaves = 32;                 // waves per token at most
 constexpr int kRopeMaxUnitsPerPass = 4;           // units a lane loads before storing
+
+// Most units per lane and pass: 4 two-vector (NeoX) or 8 one-vector (GPT-J)
+// rotation units.  A launch uses fewer only when one pass covers a token.
+constexpr int rope_max_units(bool neox) {
+  return neox ? kRopeMaxUnitsPerPass : 2 * kRopeMaxUnitsPerPass;
+}
+
+// Waves per token W and the constants of gw / W as a multiply-high
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994, for dividends below 2^31): with l = ceil(log2 W),
+// magic = ceil(2^(31 + l) / W) and shift = 31 + l, (gw * magic) >> shift equals
+// gw / W exactly, because magic * W exceeds 2^(31 + l) by less than W <= 2^l.
+struct TokenWaves {
+  uint32_t waves;
+  uint32_t magic;
+  uint32_t shift;
+};
+
+// Token t and row lane rl (0 .. W*64 - 1) of this lane.
+__device__ __forceinline__ void token_lane(const TokenWaves& tw, int64_t& t, int& rl) {
+  const uint32_t gw = blockIdx.x * kWavesPerBlock + static_cast<uint32_t>(wave_id());
+  const uint32_t tt = static_cast<uint32_t>((static_cast<uint64_t>(gw) * tw.magic) >> tw.shift);
+  t = tt;
+  rl = static_cast<int>(gw - tt * tw.waves) * kWave + lane_id();
+}
 
 // Geometry of a rotation unit inside a head of D values (see the mapping
 // above): kPerHead units per head, kPairs rotation pairs per unit, and for
@@ -145,10 +173,15 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // ---- RoPE + paged KV write ------------------------------------------------------
-// Units of one token: q units first, then k units, then v units (one 16-byte
-// vector of v copied into the cache); row lane rl takes units rl, rl + 256, ...
-// Each lane reads a q unit before writing it back, so q_out may alias q.
-// E is the element type of q, k, v and the caches (bf16 or fp16).
+// Units of one token: q units, then k units, then v units, all of the rotation
+// unit's geometry (kUnitsPerHead per head); q and k units are rotated, v units
+// copied.  Row lane rl takes units rl, rl + 256, ...  A lane issues its loads
+// before it needs the token's position or slot: the loads depend on t alone
+// (a lane past the last unit re-reads the token's first q vector and discards
+// it, and a padding token's k and v are read but not stored), so they leave
+// before the table row and the slot arrive.  Each lane reads a q unit before
+// writing it back, so q_out may alias q.  E is the element type of q, k, v and
+// the caches (bf16 or fp16).
 template <int D, bool kNeox, int kU, typename E>
 __global__ void __launch_bounds__(kBlock)
     rope_kv_write_kernel(const int64_t* __restrict__ positions, const uint16_t* q,
@@ -158,78 +191,75 @@ __global__ void __launch_bounds__(kBlock)
                          const float* __restrict__ cos_sin,
                          const int64_t* __restrict__ slot_mapping,
                          uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
-                         int64_t T, int Hq, int Hkv) {
+                         int64_t T, int Hq, int Hkv, TokenWaves tw) {
   using U = RotUnit<D, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
-  static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
-  const int wave = wave_id();
-  const int rl = (wave % kRopeWaves) * kWave + lane_id();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRopeTokensPerBlock + wave / kRopeWaves;
-  if (t >= T) return;  // no barrier in this kernel
+  static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
+  int64_t t;
+  int rl;
+  token_lane(tw, t, rl);
+  if (t >= T) return;  // whole waves; no barrier in this kernel
+  const int lanes = static_cast<int>(tw.waves) * kWave;
 
-  const int64_t pos = positions[t];
-  const int64_t slot = slot_mapping[t];
   const int c = rl % kUnitsPerHead;
   const int lo_off = U::lo(c), hi_off = lo_off + U::kHi;
   const int uq = Hq * kUnitsPerHead;
-  const int uk = slot >= 0 ? Hkv * kUnitsPerHead : 0;  // padding tokens: q only
-  const int uv = slot >= 0 ? Hkv * (D / 8) : 0;
-  const int total = uq + uk + uv;
-
-  float cs[8], sn[8];
-  unit_cos_sin<D, kNeox>(cos_sin + pos * D, c, cs, sn);
+  const int ukv = Hkv * kUnitsPerHead;
+  const int total = uq + 2 * ukv;
   const uint16_t* qt = q + t * q_stride;
   uint16_t* qo = q_out + t * q_out_stride;
   const uint16_t* kt = k + t * k_stride;
   const uint16_t* vt = v + t * v_stride;
-  // The cache is [num_blocks, block_size, Hkv, D] and contiguous, so slot
-  // block * block_size + offset starts at element slot * Hkv * D.
-  uint16_t* kc = key_cache + (slot >= 0 ? slot : 0) * Hkv * D;
-  uint16_t* vc = value_cache + (slot >= 0 ? slot : 0) * Hkv * D;
 
-  for (int u0 = 0; u0 < total; u0 += kU * kRopeLanes) {
+  float cs[8], sn[8];
+  for (int u0 = 0; u0 < total; u0 += kU * lanes) {
     u32x4 lo[kU], hi[kU];
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      const int u = u0 + j * kRopeLanes + rl;
-      if (u < uq) {
-        const uint16_t* p = qt + (u / kUnitsPerHead) * D;
-        lo[j] = ld_stream(p + lo_off);
-        if (kNeox) hi[j] = ld_stream(p + hi_off);
-      } else if (u < uq + uk) {
-        const uint16_t* p = kt + ((u - uq) / kUnitsPerHead) * D;
-        lo[j] = ld_stream(p + lo_off);
-        if (kNeox) hi[j] = ld_stream(p + hi_off);
-      } else if (u < total) {
-        lo[j] = ld_stream(vt + (u - uq - uk) * 8);
-      }
+      const int u = u0 + j * lanes + rl;
+      const uint16_t* p = u < uq          ? qt + (u / kUnitsPerHead) * D
+                          : u < uq + ukv  ? kt + ((u - uq) / kUnitsPerHead) * D
+                          : u < total     ? vt + ((u - uq - ukv) / kUnitsPerHead) * D
+                                          : qt;
+      lo[j] = ld_stream(p + lo_off);
+      if (kNeox) hi[j] = ld_stream(p + hi_off);
     }
+    if (u0 == 0) unit_cos_sin<D, kNeox>(cos_sin + positions[t] * D, c, cs, sn);
+    const int64_t slot = slot_mapping[t];
+    // The cache is [num_blocks, block_size, Hkv, D] and contiguous, so slot
+    // block * block_size + offset starts at element slot * Hkv * D.
+    const int64_t cache_row = (slot >= 0 ? slot : 0) * Hkv * D;
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      const int u = u0 + j * kRopeLanes + rl;
+      const int u = u0 + j * lanes + rl;
+      uint16_t* p;
       if (u < uq) {
         rotate_packed<kNeox, E>(lo[j], hi[j], cs, sn);
-        uint16_t* p = qo + (u / kUnitsPerHead) * D;
-        st_stream(p + lo_off, lo[j]);
-        if (kNeox) st_stream(p + hi_off, hi[j]);
-      } else if (u < uq + uk) {
-        rotate_packed<kNeox, E>(lo[j], hi[j], cs, sn);
-        uint16_t* p = kc + ((u - uq) / kUnitsPerHead) * D;
-        st_stream(p + lo_off, lo[j]);
-        if (kNeox) st_stream(p + hi_off, hi[j]);
-      } else if (u < total) {
-        st_stream(vc + (u - uq - uk) * 8, lo[j]);
+        p = qo + (u / kUnitsPerHead) * D;
+      } else if (u < total && slot >= 0) {  // padding tokens: q only
+        const bool is_k = u < uq + ukv;
+        if (is_k) rotate_packed<kNeox, E>(lo[j], hi[j], cs, sn);
+        p = (is_k ? key_cache : value_cache) + cache_row +
+            ((u - (is_k ? uq : uq + ukv)) / kUnitsPerHead) * D;
+      } else {
+        continue;
       }
+      st_stream(p + lo_off, lo[j]);
+      if (kNeox) st_stream(p + hi_off, hi[j]);
     }
+    if (kU < rope_max_units(kNeox)) break;  // fewer than the most units per lane: one pass
   }
 }
 
 // ---- QK norm + RoPE (+ paged KV write) ------------------------------------------
 // qkv row = [q: Hq heads | k: Hkv heads | v: Hkv heads] of D values.  Units as
-// in rope_kv_write_kernel (q, then k, then v).  A head's D/16 rotation units
-// sit on D/16 consecutive lanes, so its sum of squares is a DPP group sum;
-// every lane runs the group sums (lanes without a q or k unit add zeros).
-// The norm and the rotation are applied in fp32 and rounded once to bf16.
+// in rope_kv_write_kernel (q, then k, then v, all of the rotation unit's
+// geometry); k units are present when k is written back or cached, v units
+// when there is a cache.  A head's units sit on consecutive lanes of one wave,
+// so its sum of squares is a DPP group sum; every lane runs the group sums
+// (lanes without a q or k unit add zeros).  As in rope_kv_write_kernel the
+// loads leave before the position, slot and weights are needed.  The norm and
+// the rotation are applied in fp32 and rounded once to bf16.
 template <int D, bool kNeox, int kU>
 __global__ void __launch_bounds__(kBlock)
     qk_norm_rope_kv_kernel(const int64_t* __restrict__ positions, uint16_t* qkv,
@@ -238,65 +268,57 @@ __global__ void __launch_bounds__(kBlock)
                            const float* __restrict__ cos_sin,
                            const int64_t* __restrict__ slot_mapping,
                            uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
-                           int write_k, int64_t T, int Hq, int Hkv) {
+                           int write_k, int64_t T, int Hq, int Hkv, TokenWaves tw) {
   using U = RotUnit<D, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   constexpr int kVals = kNeox ? 16 : 8;  // values of a rotation unit
-  static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
-  const int wave = wave_id();
-  const int rl = (wave % kRopeWaves) * kWave + lane_id();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRopeTokensPerBlock + wave / kRopeWaves;
-  if (t >= T) return;  // wave-uniform: whole waves leave together; no barrier
+  static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
+  int64_t t;
+  int rl;
+  token_lane(tw, t, rl);
+  if (t >= T) return;  // whole waves; no barrier in this kernel
+  const int lanes = static_cast<int>(tw.waves) * kWave;
 
-  const int64_t pos = positions[t];
-  const int64_t slot = slot_mapping ? slot_mapping[t] : -1;
+  const bool cached = slot_mapping != nullptr;
   const int c = rl % kUnitsPerHead;
   const int lo_off = U::lo(c), hi_off = lo_off + U::kHi;
   const int uq = Hq * kUnitsPerHead;
-  const int uk = (slot >= 0 || write_k) ? Hkv * kUnitsPerHead : 0;
-  const int uv = slot >= 0 ? Hkv * (D / 8) : 0;
+  const int uk = (cached || write_k) ? Hkv * kUnitsPerHead : 0;
+  const int uv = cached ? Hkv * kUnitsPerHead : 0;
   const int total = uq + uk + uv;
-
-  float cs[8], sn[8];
-  unit_cos_sin<D, kNeox>(cos_sin + pos * D, c, cs, sn);
-  // This lane's weight values for q and for k (the same columns in every head).
-  float wq[16], wk[16];
-  unpack8(ld_cached(q_weight + lo_off), wq);
-  unpack8(ld_cached(k_weight + lo_off), wk);
-  if (kNeox) {
-    unpack8(ld_cached(q_weight + hi_off), wq + 8);
-    unpack8(ld_cached(k_weight + hi_off), wk + 8);
-  }
-
   uint16_t* row = qkv + t * qkv_stride;
   uint16_t* kt = row + Hq * D;
   const uint16_t* vt = kt + Hkv * D;
-  uint16_t* kc = key_cache ? key_cache + (slot >= 0 ? slot : 0) * Hkv * D : nullptr;
-  uint16_t* vc = value_cache ? value_cache + (slot >= 0 ? slot : 0) * Hkv * D : nullptr;
   const float inv_d = 1.0f / static_cast<float>(D);
 
-  for (int u0 = 0; u0 < total; u0 += kU * kRopeLanes) {
+  float cs[8], sn[8], wq[16], wk[16];
+  for (int u0 = 0; u0 < total; u0 += kU * lanes) {
     u32x4 lo[kU], hi[kU];
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      const int u = u0 + j * kRopeLanes + rl;
-      lo[j] = u32x4{0u, 0u, 0u, 0u};
-      hi[j] = u32x4{0u, 0u, 0u, 0u};
-      if (u < uq) {
-        const uint16_t* p = row + (u / kUnitsPerHead) * D;
-        lo[j] = ld_stream(p + lo_off);
-        if (kNeox) hi[j] = ld_stream(p + hi_off);
-      } else if (u < uq + uk) {
-        const uint16_t* p = kt + ((u - uq) / kUnitsPerHead) * D;
-        lo[j] = ld_stream(p + lo_off);
-        if (kNeox) hi[j] = ld_stream(p + hi_off);
-      } else if (u < total) {
-        lo[j] = ld_stream(vt + (u - uq - uk) * 8);
+      const int u = u0 + j * lanes + rl;
+      const uint16_t* p = u < uq          ? row + (u / kUnitsPerHead) * D
+                          : u < uq + uk   ? kt + ((u - uq) / kUnitsPerHead) * D
+                          : u < total     ? vt + ((u - uq - uk) / kUnitsPerHead) * D
+                                          : row;
+      lo[j] = ld_stream(p + lo_off);
+      if (kNeox) hi[j] = ld_stream(p + hi_off);
+    }
+    if (u0 == 0) {
+      unit_cos_sin<D, kNeox>(cos_sin + positions[t] * D, c, cs, sn);
+      // This lane's weight values for q and for k (the same columns in every head).
+      unpack8(ld_cached(q_weight + lo_off), wq);
+      unpack8(ld_cached(k_weight + lo_off), wk);
+      if (kNeox) {
+        unpack8(ld_cached(q_weight + hi_off), wq + 8);
+        unpack8(ld_cached(k_weight + hi_off), wk + 8);
       }
     }
+    const int64_t slot = cached ? slot_mapping[t] : -1;
+    const int64_t cache_row = (slot >= 0 ? slot : 0) * Hkv * D;
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      const int u = u0 + j * kRopeLanes + rl;
+      const int u = u0 + j * lanes + rl;
       const bool is_q = u < uq, is_k = !is_q && u < uq + uk;
       float x[16];
       unpack8(lo[j], x);
@@ -306,7 +328,7 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
         for (int e = 0; e < kVals; ++e) ss = fmaf(x[e], x[e], ss);
       }
-      ss = group_sum<kUnitsPerHead>(ss);  // all lanes: groups are q-only, k-only or idle
+      ss = group_sum<kUnitsPerHead>(ss);  // all lanes: groups are q-, k-, v-only or idle
       if (is_q || is_k) {
         const float rho = __builtin_amdgcn_rsqf(ss * inv_d + eps);
         const float* w = is_q ? wq : wk;
@@ -322,25 +344,33 @@ __global__ void __launch_bounds__(kBlock)
         } else {
           const int h = (u - uq) / kUnitsPerHead;
           if (slot >= 0) {
-            st_stream(kc + h * D + lo_off, a);
-            if (kNeox) st_stream(kc + h * D + hi_off, b);
+            uint16_t* p = key_cache + cache_row + h * D;
+            st_stream(p + lo_off, a);
+            if (kNeox) st_stream(p + hi_off, b);
           }
           if (write_k) {
             st_stream(kt + h * D + lo_off, a);
             if (kNeox) st_stream(kt + h * D + hi_off, b);
           }
         }
-      } else if (u < total) {
-        st_stream(vc + (u - uq - uk) * 8, lo[j]);
+      } else if (u < total && slot >= 0) {  // v: a bit copy into the cache
+        uint16_t* p = value_cache + cache_row + ((u - uq - uk) / kUnitsPerHead) * D;
+        st_stream(p + lo_off, lo[j]);
+        if (kNeox) st_stream(p + hi_off, hi[j]);
       }
     }
+    if (kU < rope_max_units(kNeox)) break;  // fewer than the most units per lane: one pass
   }
 }
 
 // ---- MLA: q_pe / k_pe RoPE + [kv_c | k_pe] cache write ----------------------------
 // Units of one token: the q_pe rotation units of Hq heads (head stride
 // q_head_stride), then the k_pe rotation units, then kv_c vectors copied into
-// the cache row.  The cache is [num_blocks, block_size, kv_lora + R].
+// the cache row (one vector each).  The cache is [num_blocks, block_size,
+// kv_lora + R].  As in rope_kv_write_kernel the loads depend on t alone: they
+// leave before the position and slot are needed (a padding token's k_pe and
+// kv_c are read but not stored; a lane past the last unit re-reads the
+// token's first kv_c vector).
 template <int R, bool kNeox, int kU>
 __global__ void __launch_bounds__(kBlock)
     mla_rope_kv_kernel(const int64_t* __restrict__ positions, uint16_t* q_pe, int64_t q_stride,
@@ -348,63 +378,66 @@ __global__ void __launch_bounds__(kBlock)
                        int64_t k_pe_stride, const uint16_t* __restrict__ kv_c,
                        int64_t kv_c_stride, const float* __restrict__ cos_sin,
                        const int64_t* __restrict__ slot_mapping, uint16_t* __restrict__ kv_cache,
-                       int64_t T, int Hq, int kv_lora) {
+                       int64_t T, int Hq, int kv_lora, TokenWaves tw) {
   using U = RotUnit<R, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
-  static_assert(kRopeLanes % kUnitsPerHead == 0, "a lane must keep one column");
-  const int wave = wave_id();
-  const int rl = (wave % kRopeWaves) * kWave + lane_id();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRopeTokensPerBlock + wave / kRopeWaves;
-  if (t >= T) return;  // no barrier in this kernel
+  static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
+  int64_t t;
+  int rl;
+  token_lane(tw, t, rl);
+  if (t >= T) return;  // whole waves; no barrier in this kernel
+  const int lanes = static_cast<int>(tw.waves) * kWave;
 
-  const int64_t pos = positions[t];
-  const int64_t slot = slot_mapping[t];
   const int c = rl % kUnitsPerHead;
   const int lo_off = U::lo(c), hi_off = lo_off + U::kHi;
   const int uq = Hq * kUnitsPerHead;
-  const int uk = slot >= 0 ? kUnitsPerHead : 0;
-  const int uc = slot >= 0 ? kv_lora / 8 : 0;
-  const int total = uq + uk + uc;
-
-  float cs[8], sn[8];
-  unit_cos_sin<R, kNeox>(cos_sin + pos * R, c, cs, sn);
+  const int ur = uq + kUnitsPerHead;  // rotation units (q_pe and k_pe)
+  const int total = ur + kv_lora / 8;
   uint16_t* qt = q_pe + t * q_stride;
   const uint16_t* kt = k_pe + t * k_pe_stride;
   const uint16_t* ct = kv_c + t * kv_c_stride;
-  uint16_t* dst = kv_cache + (slot >= 0 ? slot : 0) * static_cast<int64_t>(kv_lora + R);
 
-  for (int u0 = 0; u0 < total; u0 += kU * kRopeLanes) {
+  float cs[8], sn[8];
+  for (int u0 = 0; u0 < total; u0 += kU * lanes) {
     u32x4 lo[kU], hi[kU];
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      const int u = u0 + j * kRopeLanes + rl;
-      if (u < uq) {
-        const uint16_t* p = qt + (u / kUnitsPerHead) * q_head_stride;
-        lo[j] = ld_stream(p + lo_off);
-        if (kNeox) hi[j] = ld_stream(p + hi_off);
-      } else if (u < uq + uk) {
-        lo[j] = ld_stream(kt + lo_off);
-        if (kNeox) hi[j] = ld_stream(kt + hi_off);
-      } else if (u < total) {
-        lo[j] = ld_stream(ct + (u - uq - uk) * 8);
+      const int u = u0 + j * lanes + rl;
+      const uint16_t* pl;
+      const uint16_t* ph;
+      if (u < ur) {
+        const uint16_t* p = u < uq ? qt + (u / kUnitsPerHead) * q_head_stride : kt;
+        pl = p + lo_off;
+        ph = p + hi_off;
+      } else {
+        pl = ct + (u < total ? (u - ur) * 8 : 0);
+        ph = pl;  // a copy unit has one vector
       }
+      lo[j] = ld_stream(pl);
+      if (kNeox) hi[j] = ld_stream(ph);
     }
+    if (u0 == 0) unit_cos_sin<R, kNeox>(cos_sin + positions[t] * R, c, cs, sn);
+    const int64_t slot = slot_mapping[t];
+    uint16_t* dst = kv_cache + (slot >= 0 ? slot : 0) * static_cast<int64_t>(kv_lora + R);
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      const int u = u0 + j * kRopeLanes + rl;
+      const int u = u0 + j * lanes + rl;
       if (u < uq) {
         rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
         uint16_t* p = qt + (u / kUnitsPerHead) * q_head_stride;
         st_stream(p + lo_off, lo[j]);
         if (kNeox) st_stream(p + hi_off, hi[j]);
-      } else if (u < uq + uk) {
-        rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
-        st_stream(dst + kv_lora + lo_off, lo[j]);
-        if (kNeox) st_stream(dst + kv_lora + hi_off, hi[j]);
-      } else if (u < total) {
-        st_stream(dst + (u - uq - uk) * 8, lo[j]);
+      } else if (u < total && slot >= 0) {  // padding tokens: q_pe only
+        if (u < ur) {
+          rotate_packed<kNeox>(lo[j], hi[j], cs, sn);
+          st_stream(dst + kv_lora + lo_off, lo[j]);
+          if (kNeox) st_stream(dst + kv_lora + hi_off, hi[j]);
+        } else {
+          st_stream(dst + (u - ur) * 8, lo[j]);
+        }
       }
     }
+    if (kU < rope_max_units(kNeox)) break;  // fewer than the most units per lane: one pass
   }
 }
 
@@ -424,20 +457,37 @@ __global__ void __launch_bounds__(kBlock)
   out[p * rot_dim + half + i] = static_cast<float>(sn);
 }
 
-inline dim3 rope_grid(int64_t T) {
-  return dim3(static_cast<unsigned>(ceil_div(T, kRopeTokensPerBlock)));
-}
-
 // Rotation units per head under the two pairings (RotUnit::kPerHead).
 inline int64_t rot_units_per_head(int D, int is_neox) { return is_neox ? D / 16 : D / 8; }
 
-// Units each lane takes per pass: enough for one pass over a token's unit
-// count (all loads of a lane issued before its stores), at most 4 two-vector
-// (NeoX) or 8 one-vector (GPT-J) rotation units' worth.
-inline int rope_units_per_pass(int64_t units, int is_neox) {
-  const int64_t cap = is_neox ? kRopeMaxUnitsPerPass : 2 * kRopeMaxUnitsPerPass;
-  const int64_t u = ceil_div(units, kRopeLanes);
-  return static_cast<int>(u < 1 ? 1 : (u > cap ? cap : u));
+// Launch shape for tokens of `units` units each: ku units per lane per pass,
+// the fewest that fit the units on kRopeMaxWaves waves (at most 4 two-vector
+// NeoX or 8 one-vector GPT-J units; beyond that the lanes loop over passes),
+// and the fewest waves per token that hold the units at ku per lane.
+struct RopeLaunch {
+  int ku;
+  TokenWaves tw;
+};
+
+inline RopeLaunch rope_launch(int64_t units, int is_neox) {
+  const int64_t cap = rope_max_units(is_neox);
+  int64_t ku = ceil_div(units, int64_t(kRopeMaxWaves) * kWave);
+  ku = ku < 1 ? 1 : (ku > cap ? cap : ku);
+  int64_t w = ceil_div(ceil_div(units, ku), kWave);
+  w = w < 1 ? 1 : (w > kRopeMaxWaves ? kRopeMaxWaves : w);
+  uint32_t l = 0;
+  while ((int64_t(1) << l) < w) ++l;
+  const uint64_t magic = ((uint64_t(1) << (31 + l)) + uint64_t(w) - 1) / uint64_t(w);
+  return RopeLaunch{static_cast<int>(ku),
+                    TokenWaves{static_cast<uint32_t>(w), static_cast<uint32_t>(magic), 31 + l}};
+}
+
+// Workgroups for T tokens of shape.tw.waves waves; 0 when the launch's wave
+// count would reach 2^31 (the multiply-high division covers smaller ones).
+inline int64_t rope_blocks(int64_t T, const RopeLaunch& shape) {
+  const int64_t waves = T * shape.tw.waves;
+  if (T > (int64_t(1) << 31) || waves > 0x7FFFFFFF - kWavesPerBlock) return 0;
+  return ceil_div(waves, kWavesPerBlock);
 }
 
 // Calls f(std::integral_constant<int, k>()) with k = ku clamped to [1, kMax],
@@ -453,10 +503,6 @@ static void with_units_per_pass(int ku, F&& f) {
   } else {
     f(std::integral_constant<int, 1>());
   }
-}
-
-constexpr int rope_max_units(bool neox) {
-  return neox ? kRopeMaxUnitsPerPass : 2 * kRopeMaxUnitsPerPass;
 }
 
 }  // namespace rra
@@ -490,18 +536,19 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
               RRA_ERR_ALIGN);
   RRA_REQUIRE(aligned(positions, 8) && aligned(slot_mapping, 8), RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
-  RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
-
   const hipStream_t st = as_stream(stream);
-  const int ku = rope_units_per_pass(
-      int64_t(Hq + Hkv) * rot_units_per_head(D, is_neox) + int64_t(Hkv) * (D / 8), is_neox);
+  const RopeLaunch shape =
+      rope_launch(int64_t(Hq + 2 * Hkv) * rot_units_per_head(D, is_neox), is_neox);
+  const int64_t blocks = rope_blocks(T, shape);
+  RRA_REQUIRE(blocks > 0, RRA_ERR_UNSUPPORTED);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
 #define RRA_ROPE_CASE(DD, NEOX, DT, EL)                                                        \
   if (D == DD && is_neox == NEOX && dtype == DT) {                                             \
-    with_units_per_pass<rope_max_units(NEOX)>(ku, [&](auto units) {                                \
-      hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX, decltype(units)::value, EL>),             \
-                         rope_grid(T), dim3(kBlock), 0, st, positions, q, q_stride, q_out,     \
+    with_units_per_pass<rope_max_units(NEOX)>(shape.ku, [&](auto units) {                      \
+      hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX, decltype(units)::value, EL>), grid,   \
+                         block, 0, st, positions, q, q_stride, q_out,                          \
                          q_out_stride, k, k_stride, v, v_stride, cos_sin, slot_mapping,        \
-                         key_cache, value_cache, T, Hq, Hkv);                                  \
+                         key_cache, value_cache, T, Hq, Hkv, shape.tw);                        \
     });                                                                                        \
     return launch_status();                                                                    \
   }
@@ -546,19 +593,19 @@ extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, in
                   aligned(cos_sin, 16) && aligned(positions, 8),
               RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
-  RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
-
   const hipStream_t st = as_stream(stream);
-  const int ku = rope_units_per_pass(int64_t(Hq + Hkv) * rot_units_per_head(D, is_neox) +
-                                         (slot_mapping ? int64_t(Hkv) * (D / 8) : 0),
-                                     is_neox);
+  const RopeLaunch shape = rope_launch(
+      int64_t(Hq + Hkv + (slot_mapping ? Hkv : 0)) * rot_units_per_head(D, is_neox), is_neox);
+  const int64_t blocks = rope_blocks(T, shape);
+  RRA_REQUIRE(blocks > 0, RRA_ERR_UNSUPPORTED);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
 #define RRA_QKN_CASE(DD, NEOX)                                                                 \
   if (D == DD && is_neox == NEOX) {                                                            \
-    with_units_per_pass<rope_max_units(NEOX)>(ku, [&](auto units) {                                \
-      hipLaunchKernelGGL((qk_norm_rope_kv_kernel<DD, NEOX, decltype(units)::value>), rope_grid(T), \
-                         dim3(kBlock), 0, st, positions, qkv, qkv_stride, q_weight, k_weight,  \
+    with_units_per_pass<rope_max_units(NEOX)>(shape.ku, [&](auto units) {                      \
+      hipLaunchKernelGGL((qk_norm_rope_kv_kernel<DD, NEOX, decltype(units)::value>), grid,     \
+                         block, 0, st, positions, qkv, qkv_stride, q_weight, k_weight,         \
                          eps, cos_sin, slot_mapping, key_cache, value_cache, write_k, T, Hq,   \
-                         Hkv);                                                                 \
+                         Hkv, shape.tw);                                                       \
     });                                                                                        \
     return launch_status();                                                                    \
   }
@@ -596,18 +643,19 @@ extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64
                   aligned(slot_mapping, 8),
               RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
-  RRA_REQUIRE(ceil_div(T, kRopeTokensPerBlock) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
-
   const hipStream_t st = as_stream(stream);
-  const int ku = rope_units_per_pass(
+  const RopeLaunch shape = rope_launch(
       int64_t(Hq + 1) * rot_units_per_head(rope_dim, is_neox) + kv_lora / 8, is_neox);
+  const int64_t blocks = rope_blocks(T, shape);
+  RRA_REQUIRE(blocks > 0, RRA_ERR_UNSUPPORTED);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
 #define RRA_MLA_CASE(RR, NEOX)                                                                 \
   if (rope_dim == RR && is_neox == NEOX) {                                                     \
-    with_units_per_pass<rope_max_units(NEOX)>(ku, [&](auto units) {                                \
-      hipLaunchKernelGGL((mla_rope_kv_kernel<RR, NEOX, decltype(units)::value>), rope_grid(T),     \
-                         dim3(kBlock), 0, st, positions, q_pe, q_stride, q_head_stride, k_pe,  \
+    with_units_per_pass<rope_max_units(NEOX)>(shape.ku, [&](auto units) {                      \
+      hipLaunchKernelGGL((mla_rope_kv_kernel<RR, NEOX, decltype(units)::value>), grid, block,  \
+                         0, st, positions, q_pe, q_stride, q_head_stride, k_pe,                \
                          k_pe_stride, kv_c, kv_c_stride, cos_sin, slot_mapping, kv_cache, T,   \
-                         Hq, kv_lora);                                                         \
+                         Hq, kv_lora, shape.tw);                                               \
     });                                                                                        \
     return launch_status();                                                                    \
   }

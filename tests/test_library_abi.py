@@ -139,6 +139,10 @@ def test_rope_validation(rra):
     assert f(kc=A + 2) == EALIGN
     assert f(pos=A + 4) == EALIGN
     assert f(bs=0) == ESHAPE
+    # six waves per token at this shape (384 units, one per lane): a launch of
+    # 2^31 waves or more is refused before anything is enqueued
+    assert f(T=(1 << 31) // 6 + 1) == EUNSUP
+    assert f(T=(1 << 31) + 1, Hq=1, Hkv=1, qs=128, qos=128, ks=128, vs=128) == EUNSUP
     assert L.rope_cos_sin_cache(None, 8192, 128, 5e5, None) == ENULL
     assert L.rope_cos_sin_cache(A, 8192, 127, 5e5, None) == ESHAPE
     assert L.rope_cos_sin_cache(A, 8192, 128, -1.0, None) == EUNSUP
@@ -191,6 +195,7 @@ def test_qk_norm_rope_validation(rra):
     assert f(qkv=A + 2) == EALIGN
     assert f(kw=A + 8) == EALIGN
     assert f(bs=0) == ESHAPE
+    assert f(T=(1 << 31) // 6 + 1) == EUNSUP  # 384 units: six waves per token
 
 
 def test_rmsnorm_pad_validation(rra):
@@ -235,6 +240,7 @@ def test_mla_rope_validation(rra):
     assert f(rd=32, ks=32) == EUNSUP
     assert f(lora=500, cs_=500) == EUNSUP
     assert f(neox=2) == EUNSUP
+    assert f(T=(1 << 31) // 18 + 1) == EUNSUP  # 1096 one-vector units: eighteen waves per token
     assert f(hs=196, qs=25088) == EALIGN  # head stride not a multiple of 8
     assert f(kv=A + 4) == EALIGN
 
