@@ -50,23 +50,13 @@ constexpr int rope_max_units(bool neox) {
   return neox ? kRopeMaxUnitsPerPass : 2 * kRopeMaxUnitsPerPass;
 }
 
-// Waves per token W and the constants of gw / W as a multiply-high
-// (Granlund and Montgomery, "Division by invariant integers using
-// multiplication", 1994, for dividends below 2^31): with l = ceil(log2 W),
-// magic = ceil(2^(31 + l) / W) and shift = 31 + l, (gw * magic) >> shift equals
-// gw / W exactly, because magic * W exceeds 2^(31 + l) by less than W <= 2^l.
-struct TokenWaves {
-  uint32_t waves;
-  uint32_t magic;
-  uint32_t shift;
-};
-
-// Token t and row lane rl (0 .. W*64 - 1) of this lane.
-__device__ __forceinline__ void token_lane(const TokenWaves& tw, int64_t& t, int& rl) {
+// Token t and row lane rl (0 .. W*64 - 1) of this lane, for W = tw.d waves per
+// token (launches stay below 2^31 waves).
+__device__ __forceinline__ void token_lane(const FastDiv& tw, int64_t& t, int& rl) {
   const uint32_t gw = blockIdx.x * kWavesPerBlock + static_cast<uint32_t>(wave_id());
-  const uint32_t tt = static_cast<uint32_t>((static_cast<uint64_t>(gw) * tw.magic) >> tw.shift);
+  const uint32_t tt = fast_div(gw, tw);
   t = tt;
-  rl = static_cast<int>(gw - tt * tw.waves) * kWave + lane_id();
+  rl = static_cast<int>(gw - tt * tw.d) * kWave + lane_id();
 }
 
 // Geometry of a rotation unit inside a head of D values (see the mapping
@@ -191,7 +181,7 @@ __global__ void __launch_bounds__(kBlock)
                          const float* __restrict__ cos_sin,
                          const int64_t* __restrict__ slot_mapping,
                          uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
-                         int64_t T, int Hq, int Hkv, TokenWaves tw) {
+                         int64_t T, int Hq, int Hkv, FastDiv tw) {
   using U = RotUnit<D, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
@@ -199,7 +189,7 @@ __global__ void __launch_bounds__(kBlock)
   int rl;
   token_lane(tw, t, rl);
   if (t >= T) return;  // whole waves; no barrier in this kernel
-  const int lanes = static_cast<int>(tw.waves) * kWave;
+  const int lanes = static_cast<int>(tw.d) * kWave;
 
   const int c = rl % kUnitsPerHead;
   const int lo_off = U::lo(c), hi_off = lo_off + U::kHi;
@@ -268,7 +258,7 @@ __global__ void __launch_bounds__(kBlock)
                            const float* __restrict__ cos_sin,
                            const int64_t* __restrict__ slot_mapping,
                            uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
-                           int write_k, int64_t T, int Hq, int Hkv, TokenWaves tw) {
+                           int write_k, int64_t T, int Hq, int Hkv, FastDiv tw) {
   using U = RotUnit<D, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   constexpr int kVals = kNeox ? 16 : 8;  // values of a rotation unit
@@ -277,7 +267,7 @@ __global__ void __launch_bounds__(kBlock)
   int rl;
   token_lane(tw, t, rl);
   if (t >= T) return;  // whole waves; no barrier in this kernel
-  const int lanes = static_cast<int>(tw.waves) * kWave;
+  const int lanes = static_cast<int>(tw.d) * kWave;
 
   const bool cached = slot_mapping != nullptr;
   const int c = rl % kUnitsPerHead;
@@ -378,7 +368,7 @@ __global__ void __launch_bounds__(kBlock)
                        int64_t k_pe_stride, const uint16_t* __restrict__ kv_c,
                        int64_t kv_c_stride, const float* __restrict__ cos_sin,
                        const int64_t* __restrict__ slot_mapping, uint16_t* __restrict__ kv_cache,
-                       int64_t T, int Hq, int kv_lora, TokenWaves tw) {
+                       int64_t T, int Hq, int kv_lora, FastDiv tw) {
   using U = RotUnit<R, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
@@ -386,7 +376,7 @@ __global__ void __launch_bounds__(kBlock)
   int rl;
   token_lane(tw, t, rl);
   if (t >= T) return;  // whole waves; no barrier in this kernel
-  const int lanes = static_cast<int>(tw.waves) * kWave;
+  const int lanes = static_cast<int>(tw.d) * kWave;
 
   const int c = rl % kUnitsPerHead;
   const int lo_off = U::lo(c), hi_off = lo_off + U::kHi;
@@ -466,7 +456,7 @@ inline int64_t rot_units_per_head(int D, int is_neox) { return is_neox ? D / 16 
 // and the fewest waves per token that hold the units at ku per lane.
 struct RopeLaunch {
   int ku;
-  TokenWaves tw;
+  FastDiv tw;  // waves per token
 };
 
 inline RopeLaunch rope_launch(int64_t units, int is_neox) {
@@ -475,17 +465,13 @@ inline RopeLaunch rope_launch(int64_t units, int is_neox) {
   ku = ku < 1 ? 1 : (ku > cap ? cap : ku);
   int64_t w = ceil_div(ceil_div(units, ku), kWave);
   w = w < 1 ? 1 : (w > kRopeMaxWaves ? kRopeMaxWaves : w);
-  uint32_t l = 0;
-  while ((int64_t(1) << l) < w) ++l;
-  const uint64_t magic = ((uint64_t(1) << (31 + l)) + uint64_t(w) - 1) / uint64_t(w);
-  return RopeLaunch{static_cast<int>(ku),
-                    TokenWaves{static_cast<uint32_t>(w), static_cast<uint32_t>(magic), 31 + l}};
+  return RopeLaunch{static_cast<int>(ku), make_fast_div(static_cast<uint32_t>(w))};
 }
 
-// Workgroups for T tokens of shape.tw.waves waves; 0 when the launch's wave
-// count would reach 2^31 (the multiply-high division covers smaller ones).
+// Workgroups for T tokens of shape.tw.d waves; 0 when the launch's wave count
+// would reach 2^31 (the multiply-high division covers smaller ones).
 inline int64_t rope_blocks(int64_t T, const RopeLaunch& shape) {
-  const int64_t waves = T * shape.tw.waves;
+  const int64_t waves = T * shape.tw.d;
   if (T > (int64_t(1) << 31) || waves > 0x7FFFFFFF - kWavesPerBlock) return 0;
   return ceil_div(waves, kWavesPerBlock);
 }

@@ -18,6 +18,24 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// ---- wave -> work-item mapping ---------------------------------------------
+// n / d for 0 <= n < 2^31 as a multiply-high (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994): with
+// l = ceil(log2 d), magic = ceil(2^(31 + l) / d) and shift = 31 + l,
+// (n * magic) >> shift equals n / d exactly, because magic * d exceeds
+// 2^(31 + l) by less than d <= 2^l.  The host builds it (make_fast_div); in a
+// kernel the operands are wave-uniform, so the division costs a few scalar
+// instructions.
+struct FastDiv {
+  uint32_t d;
+  uint32_t magic;
+  uint32_t shift;
+};
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(n) * f.magic) >> f.shift);
+}
+
 // ---- memory ---------------------------------------------------------------
 // Streaming data is touched exactly once, so loads and stores of activations
 // use the non-temporal hint; weights and tables use ordinary loads.

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "rra.h"
+#include "rra_device.hpp"
 
 namespace rra {
 
@@ -27,6 +28,15 @@ inline int launch_status() {
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The multiply-high constants of n / d for 0 <= n < 2^31, 1 <= d < 2^31
+// (FastDiv in the device header).
+inline FastDiv make_fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t magic = ((uint64_t(1) << (31 + l)) + d - 1) / d;
+  return FastDiv{d, static_cast<uint32_t>(magic), 31 + l};
+}
 
 // Per-group scales are reduced inside one 16-lane row (group 128 = 16 lanes x
 // 8 values) or one 8-lane half row (group 64).

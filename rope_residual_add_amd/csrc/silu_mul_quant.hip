@@ -5,12 +5,15 @@
 // silu(gate) * up followed by static or per-group FP8 quantization, without
 // writing the activation to memory.
 //
-// Mapping: each wavefront owns one chunk of NV*512 output columns of one row.
-// Lane l handles vectors l, l + 64, ... of the chunk (8 columns each) and loads
+// Mapping: each wavefront owns one chunk of 512 output columns of one row
+// (wave g of the launch: row g / chunks, chunk g % chunks, the division a
+// multiply-high).  Lane l handles the chunk's vector l (8 columns) and loads
 // the matching 16-byte vectors of the gate half and of the up half, so every
 // load instruction of the wave reads 1 KiB of contiguous memory.  A group of
-// 128 (64) outputs is 16 (8) consecutive lanes of one vector: the group amax is
-// a DPP row reduction.
+// 128 (64) outputs is 16 (8) consecutive lanes: the group amax is a DPP row
+// reduction.  Measured at T = 8192, I = 14336: one vector per lane and 32-bit
+// index arithmetic beat 2 or 4 vectors per lane (fewer, longer waves) by 3%;
+// with the earlier 64-bit row division one vector per lane was 8% slower.
 //
 // Arithmetic budget: at the HBM roofline this kernel has about 25 VALU lane
 // slots per output element on MI355X (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
@@ -40,77 +43,55 @@ __device__ __forceinline__ void silu8(u32x4 g, u32x4 u, float a[8]) {
 
 // kMode RRA_Q_STATIC or RRA_Q_PER_GROUP with kGroup 64 or 128 (compile-time,
 // so group indexing is a shift).  kFull: I is a whole number of chunks, so
-// every vector index is in range and the bounds tests are compiled out.
-template <int NV, int kMode, int kGroup, bool kFull>
+// every vector index is in range and the bounds test is compiled out.
+template <int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
     silu_mul_quant_kernel(const uint16_t* __restrict__ in, int64_t in_stride,
                           const float* __restrict__ static_scale,
                           uint8_t* __restrict__ out, int64_t out_stride,
-                          float* __restrict__ scales, int64_t T, int I, int chunks) {
+                          float* __restrict__ scales, uint32_t T, int I, FastDiv chunks) {
   static_assert(kMode == RRA_Q_STATIC || kGroup == 64 || kGroup == 128, "group size");
+  const uint32_t g = blockIdx.x * kWavesPerBlock + static_cast<uint32_t>(wave_id());
+  const uint32_t row = fast_div(g, chunks);
+  if (row >= T) return;  // whole waves; no barrier in this kernel
   const int lane = lane_id();
-  const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
-  const int64_t row = wid / chunks;
-  if (row >= T) return;
-  const int chunk = static_cast<int>(wid - row * chunks);
-  const int nvec = I >> 3;
-  const uint16_t* gate = in + row * in_stride;
-  const uint16_t* up = gate + I;
+  const int idx = static_cast<int>(g - row * chunks.d) * kWave + lane;  // vector in the row
+  const bool in_row = kFull || idx < (I >> 3);
+  const uint16_t* gate = in + row * in_stride + idx * 8;
 
-  u32x4 g[NV], u[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = (chunk * NV + i) * kWave + lane;
-    if (kFull || idx < nvec) {
-      g[i] = ld_stream(gate + idx * 8);
-      u[i] = ld_stream(up + idx * 8);
-    } else {
-      g[i] = u32x4{0u, 0u, 0u, 0u};
-      u[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+  u32x4 gv = u32x4{0u, 0u, 0u, 0u}, uv = u32x4{0u, 0u, 0u, 0u};
+  if (in_row) {
+    gv = ld_stream(gate);
+    uv = ld_stream(gate + I);
   }
-
-  uint8_t* o = out + row * out_stride;
+  float a[8];
+  silu8(gv, uv, a);
+  uint8_t* o = out + row * out_stride + idx * 8;
   if constexpr (kMode == RRA_Q_STATIC) {
     const float f = 1.0f / static_scale[0];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int idx = (chunk * NV + i) * kWave + lane;
-      float a[8];
-      silu8(g[i], u[i], a);
-      if (kFull || idx < nvec)
-        st_stream(o + idx * 8,
-                  u32x2{pack_e4m3x4(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
-                        pack_e4m3x4(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
-    }
+    if (in_row)
+      st_stream(o, u32x2{pack_e4m3x4(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
+                         pack_e4m3x4(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
   } else {  // RRA_Q_PER_GROUP
-    float* scale_row = scales + row * (I / kGroup);
     constexpr int kLanesPerGroup = kGroup / 8;
+    float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int idx = (chunk * NV + i) * kWave + lane;
-      float a[8];
-      silu8(g[i], u[i], a);
-      float m = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(a[j]));
-      m = kGroup == 128 ? max16(m) : max8(m);
-      // s = amax / 448 and f = 1 / s with a multiply and the hardware
-      // reciprocal: the activation itself carries ~1e-6 relative error, so
-      // correctly rounded divisions would buy nothing here.
-      const float s = m * (1.0f / 448.0f);
-      const float f = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
-      if (kFull || idx < nvec) {
-        if ((lane & (kLanesPerGroup - 1)) == 0) scale_row[idx / kLanesPerGroup] = s;
-        // |a * f| <= 448 within rounding: no saturation needed
-        st_stream(o + idx * 8, u32x2{pack_e4m3x4<false>(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
-                                     pack_e4m3x4<false>(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
-      }
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(a[j]));
+    m = kGroup == 128 ? max16(m) : max8(m);
+    // s = amax / 448 and f = 1 / s with a multiply and the hardware
+    // reciprocal: the activation itself carries ~1e-6 relative error, so
+    // correctly rounded divisions would buy nothing here.
+    const float s = m * (1.0f / 448.0f);
+    const float f = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+    if (in_row) {
+      if ((lane & (kLanesPerGroup - 1)) == 0)
+        scales[static_cast<int64_t>(row) * (I / kGroup) + idx / kLanesPerGroup] = s;
+      // |a * f| <= 448 within rounding: no saturation needed
+      st_stream(o, u32x2{pack_e4m3x4<false>(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
+                         pack_e4m3x4<false>(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
     }
   }
 }
-
-constexpr int kSiluNV = 4;  // 2048 output columns per wavefront
 
 // Arguments of one launch.
 struct SiluLaunch {
@@ -122,15 +103,16 @@ struct SiluLaunch {
   uint8_t* out;
   int64_t out_stride;
   float* scales;
-  int64_t T;
-  int I, chunks;
+  uint32_t T;
+  int I;
+  FastDiv chunks;
 };
 
 template <bool kFull, int kMode, int kGroup>
 static void launch_silu(const SiluLaunch& a) {
-  hipLaunchKernelGGL((silu_mul_quant_kernel<kSiluNV, kMode, kGroup, kFull>), a.grid, dim3(kBlock),
-                     0, a.st, a.in, a.in_stride, a.static_scale, a.out, a.out_stride, a.scales,
-                     a.T, a.I, a.chunks);
+  hipLaunchKernelGGL((silu_mul_quant_kernel<kMode, kGroup, kFull>), a.grid, dim3(kBlock), 0,
+                     a.st, a.in, a.in_stride, a.static_scale, a.out, a.out_stride, a.scales, a.T,
+                     a.I, a.chunks);
 }
 
 template <bool kFull>
@@ -173,13 +155,16 @@ extern "C" int silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_m
   RRA_REQUIRE(aligned(out, 8) && out_stride % 8 == 0, RRA_ERR_ALIGN);
   if (T == 0) return RRA_OK;
 
-  const int64_t chunks = ceil_div(I, 8 * kWave * kSiluNV);
+  // One wave per 512-column chunk of a row; the launch's wave index stays
+  // below 2^31 (the multiply-high division's range).
+  const int64_t chunks = ceil_div(I, 8 * kWave);
+  RRA_REQUIRE(T <= 0x7FFFFFFF && T * chunks <= 0x7FFFFFFF - kWavesPerBlock,
+              RRA_ERR_UNSUPPORTED);
   const int64_t blocks = ceil_div(T * chunks, kWavesPerBlock);
-  RRA_REQUIRE(blocks <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);
   const SiluLaunch a{dim3(static_cast<unsigned>(blocks)), as_stream(stream), in, in_stride,
-                     static_scale, out, out_stride, scales, T, static_cast<int>(I),
-                     static_cast<int>(chunks)};
-  if (I == chunks * 8 * kWave * kSiluNV)
+                     static_scale, out, out_stride, scales, static_cast<uint32_t>(T),
+                     static_cast<int>(I), make_fast_div(static_cast<uint32_t>(chunks))};
+  if (I % (8 * kWave) == 0)
     launch_silu_mode<true>(a, quant_mode, group_size);
   else
     launch_silu_mode<false>(a, quant_mode, group_size);

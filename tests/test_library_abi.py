@@ -109,6 +109,9 @@ def test_silu_validation(rra):
     assert f(inp=A + 2) == EALIGN
     assert f(mode=1, ss=None) == ENULL
     assert f(inp=None, out=None, sc=None, T=0) == OK
+    # one wave per 512-column chunk (28 per row here): 2^31 waves or more are refused
+    assert f(T=(1 << 31) // 28 + 1) == EUNSUP
+    assert f(T=(1 << 31) + 1, I=512, s=1024, os=512) == EUNSUP
 
 
 def test_rope_validation(rra):
