@@ -281,7 +281,10 @@ __global__ void __launch_bounds__(kBlock)
   const uint16_t* vt = kt + Hkv * D;
   const float inv_d = 1.0f / static_cast<float>(D);
 
-  float cs[8], sn[8], wq[16], wk[16];
+  float cs[8], sn[8];
+  // This lane's q and k weight columns (the same in every head), packed.  With
+  // one unit per lane only the weight of that unit's kind is loaded (kept in wq).
+  u32x4 wq[2], wk[2];
   for (int u0 = 0; u0 < total; u0 += kU * lanes) {
     u32x4 lo[kU], hi[kU];
 #pragma unroll
@@ -296,12 +299,12 @@ __global__ void __launch_bounds__(kBlock)
     }
     if (u0 == 0) {
       unit_cos_sin<D, kNeox>(cos_sin + positions[t] * D, c, cs, sn);
-      // This lane's weight values for q and for k (the same columns in every head).
-      unpack8(ld_cached(q_weight + lo_off), wq);
-      unpack8(ld_cached(k_weight + lo_off), wk);
-      if (kNeox) {
-        unpack8(ld_cached(q_weight + hi_off), wq + 8);
-        unpack8(ld_cached(k_weight + hi_off), wk + 8);
+      const uint16_t* w0 = (kU == 1 && rl >= uq) ? k_weight : q_weight;
+      wq[0] = ld_cached(w0 + lo_off);
+      if (kNeox) wq[1] = ld_cached(w0 + hi_off);
+      if (kU > 1) {
+        wk[0] = ld_cached(k_weight + lo_off);
+        if (kNeox) wk[1] = ld_cached(k_weight + hi_off);
       }
     }
     const int64_t slot = cached ? slot_mapping[t] : -1;
@@ -321,7 +324,10 @@ __global__ void __launch_bounds__(kBlock)
       ss = group_sum<kUnitsPerHead>(ss);  // all lanes: groups are q-, k-, v-only or idle
       if (is_q || is_k) {
         const float rho = __builtin_amdgcn_rsqf(ss * inv_d + eps);
-        const float* w = is_q ? wq : wk;
+        float w[16];
+        const bool use_q = kU == 1 || is_q;
+        unpack8(use_q ? wq[0] : wk[0], w);
+        if (kNeox) unpack8(use_q ? wq[1] : wk[1], w + 8);
 #pragma unroll
         for (int e = 0; e < kVals; ++e) x[e] = x[e] * rho * w[e];
         rotate_unit<kNeox>(x, cs, sn);
