@@ -97,18 +97,26 @@ def algo_bytes(name: str, T: int) -> int:
 
 
 # Work-items per launch at T tokens, as the library launches these workloads
-# (256-lane workgroups): one row or token per workgroup for the residual-add
-# norms (four waves per row at widths above 2048) and the RoPE family, four
-# tokens per workgroup for the MLA norm, one wave per 2048 SiLU outputs.  Used
-# only to tell the sweep's launches apart in a kernel trace.
+# (256-lane workgroups): one row per workgroup for the residual-add norm (four
+# waves per row at width 4096), one wave per 512 SiLU outputs, as many waves per
+# token as the RoPE units need at one unit per lane (48 heads x 8 two-vector
+# units: six), and one wave per token for the MLA norm.  Used only to tell the
+# sweep's launches apart in a kernel trace.
 def grid_threads(name: str, T: int) -> int:
     if name == "silu_mul_quant":
-        blocks = -(-(T * -(-I_SILU // 2048)) // 4)
+        waves = T * -(-I_SILU // 512)
+    elif name == "rope_kv_write":
+        import workloads
+
+        cfg = workloads.ROPE
+        units = (cfg.Hq + 2 * cfg.Hkv) * (cfg.D // 16 if cfg.is_neox else cfg.D // 8)
+        ku = max(1, -(-units // 2048))
+        waves = T * -(-(-(-units // ku)) // 64)
     elif name == "dual_rmsnorm_quant":
-        blocks = -(-T // 4)
+        waves = T
     else:
-        blocks = T
-    return 256 * blocks
+        waves = 4 * T
+    return 64 * 4 * -(-waves // 4)
 
 
 def copy_half_bytes(nbytes_moved: int) -> int:

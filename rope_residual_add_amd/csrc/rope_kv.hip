@@ -51,9 +51,11 @@ constexpr int rope_max_units(bool neox) {
 }
 
 // Token t and row lane rl (0 .. W*64 - 1) of this lane, for W = tw.d waves per
-// token (launches stay below 2^31 waves).
+// token (launches stay below 2^31 waves).  The waves of one token span up to
+// two neighbouring workgroups; xcd_block keeps neighbours on one XCD, so the
+// token's table row, position and slot are fetched into one L2.
 __device__ __forceinline__ void token_lane(const FastDiv& tw, int64_t& t, int& rl) {
-  const uint32_t gw = blockIdx.x * kWavesPerBlock + static_cast<uint32_t>(wave_id());
+  const uint32_t gw = xcd_block() * kWavesPerBlock + static_cast<uint32_t>(wave_id());
   const uint32_t tt = fast_div(gw, tw);
   t = tt;
   rl = static_cast<int>(gw - tt * tw.d) * kWave + lane_id();

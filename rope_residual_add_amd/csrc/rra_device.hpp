@@ -36,6 +36,23 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
   return static_cast<uint32_t>((static_cast<uint64_t>(n) * f.magic) >> f.shift);
 }
 
+// Workgroups are dispatched to the 8 XCDs (each with its own L2) in turn:
+// workgroup x runs on XCD x % 8.  xcd_block() renumbers them so that runs of
+// kXcdRun consecutive numbers share an XCD while the runs still go round the
+// XCDs in order: x = 8 kXcdRun c + 8 s + k (XCD k, slot s < kXcdRun) becomes
+// kXcdRun (8 c + k) + s.  The last, partial group of 8 kXcdRun workgroups
+// keeps its numbers; the map is a bijection on [0, n).
+constexpr uint32_t kXcds = 8;
+constexpr uint32_t kXcdRun = 16;
+
+__device__ __forceinline__ uint32_t xcd_block() {
+  const uint32_t x = blockIdx.x;
+  const uint32_t full = gridDim.x / (kXcds * kXcdRun) * (kXcds * kXcdRun);
+  if (x >= full) return x;
+  const uint32_t k = x % kXcds, s = x / kXcds;
+  return (s / kXcdRun * kXcds + k) * kXcdRun + s % kXcdRun;
+}
+
 // ---- memory ---------------------------------------------------------------
 // Streaming data is touched exactly once, so loads and stores of activations
 // use the non-temporal hint; weights and tables use ordinary loads.
