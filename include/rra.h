@@ -24,8 +24,12 @@
  *   allocates nothing, keeps no mutable state, never synchronizes, and only
  *   enqueues work on `stream` (a hipStream_t; NULL = the null stream).  Calls
  *   are therefore reentrant and may be captured into a HIP graph.
- * - Sizes: a launch covers T with at most 2^31 - 1 workgroups (one row or
- *   token per workgroup for most ops); a larger T returns RRA_ERR_UNSUPPORTED.
+ * - Sizes: a launch covers T with at most 2^31 - 1 workgroups (one row per
+ *   workgroup for the residual-add norms, four tokens per workgroup for the
+ *   MLA norm) and, where waves are numbered across the launch, fewer than 2^31
+ *   waves (SiLU: one wave per 512 outputs of a row; the RoPE family: one wave
+ *   per 64 rotation or copy units of a token); a larger T returns
+ *   RRA_ERR_UNSUPPORTED.
  * - Errors: each function returns RRA_OK (0) or a negative rra_status.  All
  *   argument checks run on the host before anything is launched, so an error
  *   return means nothing was enqueued.  T == 0 returns RRA_OK without a launch;
