@@ -119,6 +119,14 @@ def test_qknorm_shapes(rra, oracle, Hq, Hkv, D, neox):
     run_qknorm(rra, oracle, 41, cfg, is_neox=neox, pad_every=5)
 
 
+@pytest.mark.parametrize("neox", [True, False])
+def test_qknorm_multi_pass_tokens(rra, oracle, neox):
+    """480 q and 32 kv heads of 256 with a cache: 8704 NeoX or 17408 GPT-J
+    units per token, two passes per lane at the most units per lane."""
+    cfg = dataclasses.replace(workloads.QKNORM, Hq=480, Hkv=32, D=256, **QK_SMALL)
+    run_qknorm(rra, oracle, 5, cfg, is_neox=neox, write_k=True, pad_every=3)
+
+
 def test_qknorm_empty(rra):
     import torch
 
@@ -251,6 +259,15 @@ def test_mla_rope_shapes(rra, oracle, Hq, rope, neox):
     cfg = dataclasses.replace(workloads.MLA_ROPE, Hq=Hq, rope_dim=rope, is_neox=neox,
                               num_blocks=16, max_pos=2048)
     run_mla_rope(rra, oracle, 57, cfg, pad_every=6)
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_mla_rope_multi_pass_tokens(rra, oracle, neox):
+    """2100 heads: 8468 NeoX or 16872 GPT-J units per token (with kv_c's 64
+    copy units), two passes per lane at the most units per lane."""
+    cfg = dataclasses.replace(workloads.MLA_ROPE, Hq=2100, is_neox=neox, num_blocks=16,
+                              max_pos=2048)
+    run_mla_rope(rra, oracle, 5, cfg, pad_every=3)
 
 
 def test_mla_rope_empty(rra):

@@ -139,15 +139,26 @@ def test_head_and_block_shapes(rra, oracle, Hq, Hkv, D, bs):
     run(rra, oracle, 45, cfg, pad_every=7)
 
 
-# GPT-J pairing takes one 16-byte vector (4 pairs) per rotation unit, so a lane
-# carries 1 to 8 units per pass: these shapes give 1, 1, 3, 5, 7 and 8 units
-# per lane (the last in three passes over a token).
+# GPT-J pairing takes one 16-byte vector (4 pairs) per rotation unit.  A token
+# gets one wave per 64 units at one unit per lane, up to 32 waves: these shapes
+# give 2, 4, 12, 20 and 28 waves of one unit per lane and, for the last (5120
+# units), 27 waves of three units per lane.
 @pytest.mark.parametrize("Hq,Hkv,D", [(8, 1, 64), (12, 2, 128), (32, 8, 128), (64, 8, 128),
                                       (40, 8, 256), (128, 16, 256)])
 def test_gptj_units_per_pass(rra, oracle, Hq, Hkv, D):
     cfg = dataclasses.replace(workloads.ROPE, Hq=Hq, Hkv=Hkv, D=D, rot_dim=D, is_neox=False,
                               **SMALL)
     run(rra, oracle, 37, cfg, pad_every=5)
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_multi_pass_tokens(rra, oracle, neox):
+    """544 heads of 256: 8704 NeoX or 17408 GPT-J units per token, more than
+    32 waves carry at the most units per lane (4 or 8), so each lane loops over
+    two passes."""
+    cfg = dataclasses.replace(workloads.ROPE, Hq=480, Hkv=32, D=256, rot_dim=256, is_neox=neox,
+                              **SMALL)
+    run(rra, oracle, 6, cfg, pad_every=4)
 
 
 def test_position_zero_is_identity(rra):
