@@ -20,10 +20,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops keeps the compiler from forming v_pk_{add,mul,fma}_f32.
 # Code object v5 loads under both the ROCm 7.2 toolchain's runtime and the
-# ROCm 7.0 HIP runtime bundled with PyTorch.
+# ROCm 7.0 HIP runtime bundled with PyTorch.  Kernel-argument preloading puts
+# the first 14 dwords of each kernel's arguments in scalar registers at wave
+# start (with a fallback prologue that loads them where the firmware does
+# not), so a short wave's first loads need not wait for its arguments; the
+# kernels lead with the arguments those loads need.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -176,14 +176,15 @@ __device__ __forceinline__ float group_sum(float v) {
 // the caches (bf16 or fp16).
 template <int D, bool kNeox, int kU, typename E>
 __global__ void __launch_bounds__(kBlock)
-    rope_kv_write_kernel(const int64_t* __restrict__ positions, const uint16_t* q,
-                         int64_t q_stride, uint16_t* q_out, int64_t q_out_stride,
+    rope_kv_write_kernel(uint32_t tw_d, uint32_t tw_magic, uint32_t tw_shift, uint32_t T, int Hq,
+                         int Hkv, const uint16_t* q, int64_t q_stride,
                          const uint16_t* __restrict__ k, int64_t k_stride,
-                         const uint16_t* __restrict__ v, int64_t v_stride,
+                         const uint16_t* __restrict__ v, int64_t v_stride, uint16_t* q_out,
+                         int64_t q_out_stride, const int64_t* __restrict__ positions,
                          const float* __restrict__ cos_sin,
                          const int64_t* __restrict__ slot_mapping,
-                         uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
-                         int64_t T, int Hq, int Hkv, FastDiv tw) {
+                         uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache) {
+  const FastDiv tw{tw_d, tw_magic, tw_shift};
   using U = RotUnit<D, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
@@ -254,13 +255,15 @@ __global__ void __launch_bounds__(kBlock)
 // the rotation are applied in fp32 and rounded once to bf16.
 template <int D, bool kNeox, int kU>
 __global__ void __launch_bounds__(kBlock)
-    qk_norm_rope_kv_kernel(const int64_t* __restrict__ positions, uint16_t* qkv,
-                           int64_t qkv_stride, const uint16_t* __restrict__ q_weight,
-                           const uint16_t* __restrict__ k_weight, float eps,
+    qk_norm_rope_kv_kernel(uint32_t tw_d, uint32_t tw_magic, uint32_t tw_shift, uint32_t T,
+                           int Hq, int Hkv, uint16_t* qkv, int64_t qkv_stride, int write_k,
+                           float eps, const uint16_t* __restrict__ q_weight,
+                           const uint16_t* __restrict__ k_weight,
+                           const int64_t* __restrict__ positions,
                            const float* __restrict__ cos_sin,
                            const int64_t* __restrict__ slot_mapping,
-                           uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
-                           int write_k, int64_t T, int Hq, int Hkv, FastDiv tw) {
+                           uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache) {
+  const FastDiv tw{tw_d, tw_magic, tw_shift};
   using U = RotUnit<D, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   constexpr int kVals = kNeox ? 16 : 8;  // values of a rotation unit
@@ -371,12 +374,13 @@ __global__ void __launch_bounds__(kBlock)
 // token's first kv_c vector).
 template <int R, bool kNeox, int kU>
 __global__ void __launch_bounds__(kBlock)
-    mla_rope_kv_kernel(const int64_t* __restrict__ positions, uint16_t* q_pe, int64_t q_stride,
-                       int64_t q_head_stride, const uint16_t* __restrict__ k_pe,
-                       int64_t k_pe_stride, const uint16_t* __restrict__ kv_c,
-                       int64_t kv_c_stride, const float* __restrict__ cos_sin,
-                       const int64_t* __restrict__ slot_mapping, uint16_t* __restrict__ kv_cache,
-                       int64_t T, int Hq, int kv_lora, FastDiv tw) {
+    mla_rope_kv_kernel(uint32_t tw_d, uint32_t tw_magic, uint32_t tw_shift, uint32_t T, int Hq,
+                       int kv_lora, uint16_t* q_pe, int64_t q_stride, int64_t q_head_stride,
+                       const uint16_t* __restrict__ k_pe, int64_t k_pe_stride,
+                       const uint16_t* __restrict__ kv_c, int64_t kv_c_stride,
+                       const int64_t* __restrict__ positions, const float* __restrict__ cos_sin,
+                       const int64_t* __restrict__ slot_mapping, uint16_t* __restrict__ kv_cache) {
+  const FastDiv tw{tw_d, tw_magic, tw_shift};
   using U = RotUnit<R, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
@@ -536,13 +540,14 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   const int64_t blocks = rope_blocks(T, shape);
   RRA_REQUIRE(blocks > 0, RRA_ERR_UNSUPPORTED);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
+  const uint32_t T32 = static_cast<uint32_t>(T);  // below 2^31: rope_blocks refuses larger T
 #define RRA_ROPE_CASE(DD, NEOX, DT, EL)                                                        \
   if (D == DD && is_neox == NEOX && dtype == DT) {                                             \
     with_units_per_pass<rope_max_units(NEOX)>(shape.ku, [&](auto units) {                      \
       hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX, decltype(units)::value, EL>), grid,   \
-                         block, 0, st, positions, q, q_stride, q_out,                          \
-                         q_out_stride, k, k_stride, v, v_stride, cos_sin, slot_mapping,        \
-                         key_cache, value_cache, T, Hq, Hkv, shape.tw);                        \
+                         block, 0, st, shape.tw.d, shape.tw.magic, shape.tw.shift, T32, Hq,    \
+                         Hkv, q, q_stride, k, k_stride, v, v_stride, q_out, q_out_stride,      \
+                         positions, cos_sin, slot_mapping, key_cache, value_cache);            \
     });                                                                                        \
     return launch_status();                                                                    \
   }
@@ -593,13 +598,14 @@ extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, in
   const int64_t blocks = rope_blocks(T, shape);
   RRA_REQUIRE(blocks > 0, RRA_ERR_UNSUPPORTED);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
+  const uint32_t T32 = static_cast<uint32_t>(T);  // below 2^31: rope_blocks refuses larger T
 #define RRA_QKN_CASE(DD, NEOX)                                                                 \
   if (D == DD && is_neox == NEOX) {                                                            \
     with_units_per_pass<rope_max_units(NEOX)>(shape.ku, [&](auto units) {                      \
       hipLaunchKernelGGL((qk_norm_rope_kv_kernel<DD, NEOX, decltype(units)::value>), grid,     \
-                         block, 0, st, positions, qkv, qkv_stride, q_weight, k_weight,         \
-                         eps, cos_sin, slot_mapping, key_cache, value_cache, write_k, T, Hq,   \
-                         Hkv, shape.tw);                                                       \
+                         block, 0, st, shape.tw.d, shape.tw.magic, shape.tw.shift, T32, Hq,    \
+                         Hkv, qkv, qkv_stride, write_k, eps, q_weight, k_weight, positions,    \
+                         cos_sin, slot_mapping, key_cache, value_cache);                       \
     });                                                                                        \
     return launch_status();                                                                    \
   }
@@ -643,13 +649,14 @@ extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64
   const int64_t blocks = rope_blocks(T, shape);
   RRA_REQUIRE(blocks > 0, RRA_ERR_UNSUPPORTED);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
+  const uint32_t T32 = static_cast<uint32_t>(T);  // below 2^31: rope_blocks refuses larger T
 #define RRA_MLA_CASE(RR, NEOX)                                                                 \
   if (rope_dim == RR && is_neox == NEOX) {                                                     \
     with_units_per_pass<rope_max_units(NEOX)>(shape.ku, [&](auto units) {                      \
       hipLaunchKernelGGL((mla_rope_kv_kernel<RR, NEOX, decltype(units)::value>), grid, block,  \
-                         0, st, positions, q_pe, q_stride, q_head_stride, k_pe,                \
-                         k_pe_stride, kv_c, kv_c_stride, cos_sin, slot_mapping, kv_cache, T,   \
-                         Hq, kv_lora, shape.tw);                                               \
+                         0, st, shape.tw.d, shape.tw.magic, shape.tw.shift, T32, Hq, kv_lora,  \
+                         q_pe, q_stride, q_head_stride, k_pe, k_pe_stride, kv_c, kv_c_stride,  \
+                         positions, cos_sin, slot_mapping, kv_cache);                          \
     });                                                                                        \
     return launch_status();                                                                    \
   }

@@ -46,11 +46,14 @@ __device__ __forceinline__ void silu8(u32x4 g, u32x4 u, float a[8]) {
 // every vector index is in range and the bounds test is compiled out.
 template <int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
-    silu_mul_quant_kernel(const uint16_t* __restrict__ in, int64_t in_stride,
-                          const float* __restrict__ static_scale,
+    silu_mul_quant_kernel(uint32_t chunks_d, uint32_t chunks_magic, uint32_t chunks_shift,
+                          uint32_t T, int I, const uint16_t* __restrict__ in, int64_t in_stride,
                           uint8_t* __restrict__ out, int64_t out_stride,
-                          float* __restrict__ scales, uint32_t T, int I, FastDiv chunks) {
+                          float* __restrict__ scales, const float* __restrict__ static_scale) {
   static_assert(kMode == RRA_Q_STATIC || kGroup == 64 || kGroup == 128, "group size");
+  // The launch shape leads the argument list as plain scalars, so that it is
+  // preloaded into scalar registers with the first pointers.
+  const FastDiv chunks{chunks_d, chunks_magic, chunks_shift};
   const uint32_t g = blockIdx.x * kWavesPerBlock + static_cast<uint32_t>(wave_id());
   const uint32_t row = fast_div(g, chunks);
   if (row >= T) return;  // whole waves; no barrier in this kernel
@@ -111,8 +114,8 @@ struct SiluLaunch {
 template <bool kFull, int kMode, int kGroup>
 static void launch_silu(const SiluLaunch& a) {
   hipLaunchKernelGGL((silu_mul_quant_kernel<kMode, kGroup, kFull>), a.grid, dim3(kBlock), 0,
-                     a.st, a.in, a.in_stride, a.static_scale, a.out, a.out_stride, a.scales, a.T,
-                     a.I, a.chunks);
+                     a.st, a.chunks.d, a.chunks.magic, a.chunks.shift, a.T, a.I, a.in, a.in_stride,
+                     a.out, a.out_stride, a.scales, a.static_scale);
 }
 
 template <bool kFull>
