@@ -287,7 +287,9 @@ __global__ void __launch_bounds__(kBlock)
                                                                H_pad);
 }
 
-// MLA dual RMSNorm: one wave per token handles both of its rows, the q latent
+// MLA dual RMSNorm (arguments ordered so that the row count and everything
+// the first loads need are among the preloaded ones): one wave per token
+// handles both of its rows, the q latent
 // (NVQ vectors per lane) and the kv latent (NVKV), so both row reductions are
 // wave-local DPP reductions with no LDS exchange and no barrier (four tokens
 // per workgroup; waves past T leave at once).  Measured on MI355X at the
@@ -296,13 +298,13 @@ __global__ void __launch_bounds__(kBlock)
 // than the extra vectors per lane.
 template <int NVQ, int NVKV, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
-    dual_rmsnorm_quant_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
-                              const uint16_t* __restrict__ q_w, float eps_q,
-                              const uint16_t* __restrict__ kv, int64_t kv_stride,
-                              const uint16_t* __restrict__ kv_w, float eps_kv,
+    dual_rmsnorm_quant_kernel(int64_t T, int Hq, int Hkv, const uint16_t* __restrict__ q,
+                              int64_t q_stride, const uint16_t* __restrict__ kv,
+                              int64_t kv_stride, const uint16_t* __restrict__ q_w,
+                              const uint16_t* __restrict__ kv_w, float eps_q, float eps_kv,
                               void* __restrict__ q_out, int64_t q_out_stride,
                               float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
-                              int64_t kv_out_stride, int64_t T, int Hq, int Hkv) {
+                              int64_t kv_out_stride) {
   const int rl = lane_id();
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
   if (row >= T) return;
@@ -461,8 +463,8 @@ template <int A, int B, bool kFull, int kMode, int kGroup>
 static void launch_dual(const DualLaunch& a) {
   hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, kMode, kGroup, kFull>), a.grid,
                      dim3(kBlock), 0,
-                     a.st, a.q, a.qs, a.qw, a.eps_q, a.kv, a.kvs, a.kvw, a.eps_kv, a.q_out, a.qos,
-                     a.q_scales, a.kv_out, a.kvos, a.T, a.Hq, a.Hkv);
+                     a.st, a.T, a.Hq, a.Hkv, a.q, a.qs, a.kv, a.kvs, a.qw, a.kvw, a.eps_q,
+                     a.eps_kv, a.q_out, a.qos, a.q_scales, a.kv_out, a.kvos);
 }
 
 template <int A, int B, bool kFull>
