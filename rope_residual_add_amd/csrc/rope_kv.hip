@@ -51,11 +51,13 @@ constexpr int rope_max_units(bool neox) {
 }
 
 // Token t and row lane rl (0 .. W*64 - 1) of this lane, for W = tw.d waves per
-// token (launches stay below 2^31 waves).  The waves of one token span up to
-// two neighbouring workgroups; xcd_block keeps neighbours on one XCD, so the
-// token's table row, position and slot are fetched into one L2.
-__device__ __forceinline__ void token_lane(const FastDiv& tw, int64_t& t, int& rl) {
-  const uint32_t gw = xcd_block() * kWavesPerBlock + static_cast<uint32_t>(wave_id());
+// token and T tokens (launches stay below 2^31 waves, in ceil(T W / 4)
+// workgroups).  The waves of one token span up to two neighbouring
+// workgroups; xcd_block keeps neighbours on one XCD, so the token's table row,
+// position and slot are fetched into one L2.
+__device__ __forceinline__ void token_lane(const FastDiv& tw, uint32_t T, int64_t& t, int& rl) {
+  const uint32_t blocks = (T * tw.d + kWavesPerBlock - 1) / kWavesPerBlock;
+  const uint32_t gw = xcd_block(blocks) * kWavesPerBlock + static_cast<uint32_t>(wave_id());
   const uint32_t tt = fast_div(gw, tw);
   t = tt;
   rl = static_cast<int>(gw - tt * tw.d) * kWave + lane_id();
@@ -190,7 +192,7 @@ __global__ void __launch_bounds__(kBlock)
   static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
   int64_t t;
   int rl;
-  token_lane(tw, t, rl);
+  token_lane(tw, T, t, rl);
   if (t >= T) return;  // whole waves; no barrier in this kernel
   const int lanes = static_cast<int>(tw.d) * kWave;
 
@@ -207,15 +209,25 @@ __global__ void __launch_bounds__(kBlock)
   float cs[8], sn[8];
   for (int u0 = 0; u0 < total; u0 += kU * lanes) {
     u32x4 lo[kU], hi[kU];
+    // q and k first: their addresses use only preloaded arguments.
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
       const int u = u0 + j * lanes + rl;
-      const uint16_t* p = u < uq          ? qt + (u / kUnitsPerHead) * D
-                          : u < uq + ukv  ? kt + ((u - uq) / kUnitsPerHead) * D
-                          : u < total     ? vt + ((u - uq - ukv) / kUnitsPerHead) * D
-                                          : qt;
-      lo[j] = ld_stream(p + lo_off);
-      if (kNeox) hi[j] = ld_stream(p + hi_off);
+      if (u < uq + ukv) {
+        const uint16_t* p = u < uq ? qt + (u / kUnitsPerHead) * D
+                                   : kt + ((u - uq) / kUnitsPerHead) * D;
+        lo[j] = ld_stream(p + lo_off);
+        if (kNeox) hi[j] = ld_stream(p + hi_off);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int u = u0 + j * lanes + rl;
+      if (u >= uq + ukv) {
+        const uint16_t* p = u < total ? vt + ((u - uq - ukv) / kUnitsPerHead) * D : qt;
+        lo[j] = ld_stream(p + lo_off);
+        if (kNeox) hi[j] = ld_stream(p + hi_off);
+      }
     }
     if (u0 == 0) unit_cos_sin<D, kNeox>(cos_sin + positions[t] * D, c, cs, sn);
     const int64_t slot = slot_mapping[t];
@@ -270,7 +282,7 @@ __global__ void __launch_bounds__(kBlock)
   static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
   int64_t t;
   int rl;
-  token_lane(tw, t, rl);
+  token_lane(tw, T, t, rl);
   if (t >= T) return;  // whole waves; no barrier in this kernel
   const int lanes = static_cast<int>(tw.d) * kWave;
 
@@ -386,7 +398,7 @@ __global__ void __launch_bounds__(kBlock)
   static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
   int64_t t;
   int rl;
-  token_lane(tw, t, rl);
+  token_lane(tw, T, t, rl);
   if (t >= T) return;  // whole waves; no barrier in this kernel
   const int lanes = static_cast<int>(tw.d) * kWave;
 
@@ -402,21 +414,32 @@ __global__ void __launch_bounds__(kBlock)
   float cs[8], sn[8];
   for (int u0 = 0; u0 < total; u0 += kU * lanes) {
     u32x4 lo[kU], hi[kU];
+    // q_pe first: its addresses use only preloaded arguments.
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
       const int u = u0 + j * lanes + rl;
-      const uint16_t* pl;
-      const uint16_t* ph;
-      if (u < ur) {
-        const uint16_t* p = u < uq ? qt + (u / kUnitsPerHead) * q_head_stride : kt;
-        pl = p + lo_off;
-        ph = p + hi_off;
-      } else {
-        pl = ct + (u < total ? (u - ur) * 8 : 0);
-        ph = pl;  // a copy unit has one vector
+      if (u < uq) {
+        const uint16_t* p = qt + (u / kUnitsPerHead) * q_head_stride;
+        lo[j] = ld_stream(p + lo_off);
+        if (kNeox) hi[j] = ld_stream(p + hi_off);
       }
-      lo[j] = ld_stream(pl);
-      if (kNeox) hi[j] = ld_stream(ph);
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int u = u0 + j * lanes + rl;
+      if (u >= uq) {
+        const uint16_t* pl;
+        const uint16_t* ph;
+        if (u < ur) {
+          pl = kt + lo_off;
+          ph = kt + hi_off;
+        } else {
+          pl = ct + (u < total ? (u - ur) * 8 : 0);
+          ph = pl;  // a copy unit has one vector
+        }
+        lo[j] = ld_stream(pl);
+        if (kNeox) hi[j] = ld_stream(ph);
+      }
     }
     if (u0 == 0) unit_cos_sin<R, kNeox>(cos_sin + positions[t] * R, c, cs, sn);
     const int64_t slot = slot_mapping[t];

@@ -45,9 +45,11 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
 constexpr uint32_t kXcds = 8;
 constexpr uint32_t kXcdRun = 16;
 
-__device__ __forceinline__ uint32_t xcd_block() {
+// n is the grid size (gridDim.x, which a kernel may instead derive from its
+// own arguments: the implicit argument that holds it is not preloaded).
+__device__ __forceinline__ uint32_t xcd_block(uint32_t n) {
   const uint32_t x = blockIdx.x;
-  const uint32_t full = gridDim.x / (kXcds * kXcdRun) * (kXcds * kXcdRun);
+  const uint32_t full = n / (kXcds * kXcdRun) * (kXcds * kXcdRun);
   if (x >= full) return x;
   const uint32_t k = x % kXcds, s = x / kXcds;
   return (s / kXcdRun * kXcds + k) * kXcdRun + s % kXcdRun;
