@@ -151,6 +151,16 @@ def test_gptj_units_per_pass(rra, oracle, Hq, Hkv, D):
     run(rra, oracle, 37, cfg, pad_every=5)
 
 
+@pytest.mark.parametrize("T", [1000, 1365, 171])
+def test_partial_xcd_groups(rra, oracle, T):
+    """Six waves per token in four-wave workgroups, numbered in groups of 128
+    workgroups (16 per XCD): T = 1000 gives 1500 workgroups (92 past the last
+    whole group), 1365 gives 2048 (whole groups; the last token ends
+    mid-workgroup) and 171 gives 257 (one past)."""
+    cfg = dataclasses.replace(workloads.ROPE, num_blocks=128, max_pos=4096)
+    run(rra, oracle, T, cfg, pad_every=9)
+
+
 @pytest.mark.parametrize("neox", [True, False])
 def test_multi_pass_tokens(rra, oracle, neox):
     """544 heads of 256: 8704 NeoX or 17408 GPT-J units per token, more than
