@@ -18,7 +18,7 @@
 // Mapping: W waves per token, as many as the token's units need at one unit
 // per lane (at most 32; beyond that each lane takes kU > 1 units per pass),
 // in ordinary four-wave workgroups: wave g of the launch is wave g % W of
-// token g / W, so a token may straddle two workgroups (the kernels have no
+// token g / W, so a token may straddle workgroups (the kernels have no
 // barriers).  Each lane issues all its loads before its stores.  Measured at
 // the Llama-3-8B attention shape (384 units): one unit per lane on six waves
 // beats two units per lane on four waves by 3%, while workgroups of six waves
@@ -52,9 +52,10 @@ constexpr int rope_max_units(bool neox) {
 
 // Token t and row lane rl (0 .. W*64 - 1) of this lane, for W = tw.d waves per
 // token and T tokens (launches stay below 2^31 waves, in ceil(T W / 4)
-// workgroups).  The waves of one token span up to two neighbouring
-// workgroups; xcd_block keeps neighbours on one XCD, so the token's table row,
-// position and slot are fetched into one L2.
+// workgroups).  The waves of one token span neighbouring workgroups (up to
+// W/4 + 1 of them); xcd_block keeps neighbours on one XCD except across its
+// 16-workgroup runs, so a token's table row, position and slot are fetched
+// into one L2.
 __device__ __forceinline__ void token_lane(const FastDiv& tw, uint32_t T, int64_t& t, int& rl) {
   const uint32_t blocks = (T * tw.d + kWavesPerBlock - 1) / kWavesPerBlock;
   const uint32_t gw = xcd_block(blocks) * kWavesPerBlock + static_cast<uint32_t>(wave_id());
