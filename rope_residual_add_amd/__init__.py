@@ -101,37 +101,70 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _need_cuda(name: str, t: torch.Tensor, dtypes) -> None:
+# Every tensor an entry point touches is checked here before the call: device,
+# dtype, shape (rows included) and layout.  The kernels trust the sizes they
+# are given, so a tensor smaller than its stated shape would be read or
+# written out of bounds.
+
+def _need_cuda(name: str, t: torch.Tensor, dtypes, device=None) -> None:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a GPU tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
 
 
-def _vector(name: str, t: torch.Tensor, n: int, dtypes=(torch.bfloat16,)) -> None:
-    _need_cuda(name, t, dtypes)
+def _vector(name: str, t: torch.Tensor, n: int, dtypes=(torch.bfloat16,), device=None) -> None:
+    _need_cuda(name, t, dtypes, device)
     if t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous [{n}] tensor")
 
 
-def _rows(name: str, t: torch.Tensor, dtypes, width: int | None = None) -> int:
-    """Check a [T, width] tensor with contiguous rows; return its row stride."""
-    _need_cuda(name, t, dtypes)
+def _rows(name: str, t: torch.Tensor, dtypes, width: int | None = None, rows: int | None = None,
+          device=None) -> int:
+    """Check a [rows, width] tensor with contiguous rows; return its row stride."""
+    _need_cuda(name, t, dtypes, device)
     if t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with contiguous rows")
     if width is not None and t.shape[1] != width:
         raise ValueError(f"{name} must have {width} columns, got {t.shape[1]}")
+    if rows is not None and t.shape[0] != rows:
+        raise ValueError(f"{name} must have {rows} rows, got {t.shape[0]}")
     return t.stride(0)
 
 
-def _heads(name: str, t: torch.Tensor, H: int, D: int, dtypes=(torch.bfloat16,)) -> int:
+def _heads(name: str, t: torch.Tensor, H: int, D: int, dtypes=(torch.bfloat16,),
+           rows: int | None = None, device=None) -> int:
     """Check a [T, H, D] (or [T, H*D]) tensor whose heads are contiguous."""
-    _need_cuda(name, t, dtypes)
+    _need_cuda(name, t, dtypes, device)
     if t.dim() == 3:
         if tuple(t.shape[1:]) != (H, D) or (t.numel() > 0 and (t.stride(2) != 1 or t.stride(1) != D)):
             raise ValueError(f"{name} must be [T, {H}, {D}] with contiguous heads")
+        if rows is not None and t.shape[0] != rows:
+            raise ValueError(f"{name} must have {rows} tokens, got {t.shape[0]}")
         return t.stride(0)
-    return _rows(name, t, dtypes, H * D)
+    return _rows(name, t, dtypes, H * D, rows, device)
+
+
+def _tokens(name: str, t: torch.Tensor, T: int, device) -> None:
+    """A contiguous [T] int64 tensor (positions, slot mapping)."""
+    _vector(name, t, T, (torch.int64,), device)
+
+
+def _exact(name: str, t: torch.Tensor, shape, dtypes, device) -> None:
+    """A contiguous tensor of exactly this shape (scales, tables, codes)."""
+    _need_cuda(name, t, dtypes, device)
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {list(shape)} tensor, got "
+                         f"{list(t.shape)}")
+
+
+def _static(t, device) -> None:
+    """The static scale: a device fp32 tensor holding at least one value."""
+    _need_cuda("static_scale", t, (torch.float32,), device)
+    if t.numel() < 1:
+        raise ValueError("static_scale must hold one value")
 
 
 def _check(fn: str, status: int) -> None:
@@ -161,16 +194,21 @@ def fused_add_rmsnorm_quant(x, residual, weight, eps, quant_mode, group_size=0,
     static_scale: [1] fp32 device tensor (static mode).  Returns (out, scales):
     out [T, H] float8_e4m3fn, scales [T] / [T, H/g] fp32 or None."""
     mode = _mode(quant_mode)
-    T, H = x.shape
     xs = _rows("x", x, _BF16)
-    rs = _rows("residual", residual, _BF16, H) if residual is not None else 0
-    _vector("weight", weight, H)
+    T, H = x.shape
+    dev = x.device
+    rs = _rows("residual", residual, _BF16, H, T, dev) if residual is not None else 0
+    _vector("weight", weight, H, device=dev)
+    if static_scale is not None:
+        _static(static_scale, dev)
     if out is None:
-        out = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=x.device)
-    os_ = _rows("out", out, _FP8, H)
+        out = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=dev)
+    os_ = _rows("out", out, _FP8, H, T, dev)
     shape = _scales_shape(mode, T, H, group_size or 1)
     if scales is None and shape is not None:
-        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+        scales = torch.empty(shape, dtype=torch.float32, device=dev)
+    if scales is not None and shape is not None:
+        _exact("scales", scales, shape, (torch.float32,), dev)
     with torch.cuda.device(x.device):
         st = lib().fused_add_rmsnorm_quant(
             _ptr(x), xs, _ptr(residual), rs, _ptr(weight), float(eps), mode,
@@ -183,15 +221,22 @@ def silu_mul_quant(inp, quant_mode, group_size=0, static_scale=None, out=None, s
     """SiLU-and-Mul + FP8 quant.  inp: [T, 2I] bf16 (gate | up).
     Returns (out [T, I] float8_e4m3fn, scales [T, I/g] fp32 or None)."""
     mode = _mode(quant_mode)
-    T, two_i = inp.shape
-    I = two_i // 2
     s = _rows("inp", inp, _BF16)
+    T, two_i = inp.shape
+    if two_i % 2:
+        raise ValueError("inp must hold gate and up halves of equal width")
+    I = two_i // 2
+    dev = inp.device
+    if static_scale is not None:
+        _static(static_scale, dev)
     if out is None:
-        out = torch.empty((T, I), dtype=torch.float8_e4m3fn, device=inp.device)
-    os_ = _rows("out", out, _FP8, I)
+        out = torch.empty((T, I), dtype=torch.float8_e4m3fn, device=dev)
+    os_ = _rows("out", out, _FP8, I, T, dev)
     shape = _scales_shape(mode, T, I, group_size or 1)
     if scales is None and shape is not None:
-        scales = torch.empty(shape, dtype=torch.float32, device=inp.device)
+        scales = torch.empty(shape, dtype=torch.float32, device=dev)
+    if scales is not None and shape is not None:
+        _exact("scales", scales, shape, (torch.float32,), dev)
     with torch.cuda.device(inp.device):
         st = lib().silu_mul_quant(_ptr(inp), s, mode, int(group_size), _ptr(static_scale),
                                   _ptr(out), os_, _ptr(scales), T, I, _stream(inp))
@@ -203,7 +248,7 @@ def rope_cos_sin_cache(max_pos: int, rot_dim: int, theta: float, device="cuda", 
     """[max_pos, rot_dim] fp32 table: cos of the rot_dim/2 angles, then sin."""
     if out is None:
         out = torch.empty((max_pos, rot_dim), dtype=torch.float32, device=device)
-    _need_cuda("out", out, (torch.float32,))
+    _exact("out", out, (max_pos, rot_dim), (torch.float32,), out.device)
     with torch.cuda.device(out.device):
         st = lib().rope_cos_sin_cache(_ptr(out), int(max_pos), int(rot_dim), float(theta),
                                       _stream(out))
@@ -221,24 +266,28 @@ def rope_kv_write(positions, q, k, v, cos_sin, slot_mapping, key_cache, value_ca
     caches: [num_blocks, block_size, Hkv, D].  q_out defaults to q
     (in place).  is_neox selects GPT-NeoX pairs (i, i + D/2), else GPT-J
     pairs (2i, 2i + 1).  Returns q_out."""
-    T = positions.shape[0]
-    num_blocks, block_size, Hkv, D = key_cache.shape
-    Hq = q.shape[1] if q.dim() == 3 else q.shape[1] // D
-    _need_cuda("positions", positions, (torch.int64,))
-    _need_cuda("slot_mapping", slot_mapping, (torch.int64,))
-    _need_cuda("cos_sin", cos_sin, (torch.float32,))
     _need_cuda("q", q, tuple(_ELEM))
-    elem = (q.dtype,)
+    dev, elem = q.device, (q.dtype,)
+    _need_cuda("key_cache", key_cache, elem, dev)
+    if key_cache.dim() != 4:
+        raise ValueError("key_cache must be [num_blocks, block_size, Hkv, D]")
+    num_blocks, block_size, Hkv, D = key_cache.shape
     for name, c in (("key_cache", key_cache), ("value_cache", value_cache)):
-        _need_cuda(name, c, elem)
-        if not c.is_contiguous() or tuple(c.shape) != (num_blocks, block_size, Hkv, D):
-            raise ValueError(f"{name} must be a contiguous [num_blocks, block_size, Hkv, D] tensor")
-    if not (positions.is_contiguous() and slot_mapping.is_contiguous() and cos_sin.is_contiguous()):
-        raise ValueError("positions, slot_mapping and cos_sin must be contiguous")
+        _exact(name, c, (num_blocks, block_size, Hkv, D), elem, dev)
+    if q.dim() not in (2, 3) or D == 0:
+        raise ValueError("q must be [T, Hq, D] or [T, Hq * D]")
+    T = q.shape[0]
+    Hq = q.shape[1] if q.dim() == 3 else q.shape[1] // D
+    _tokens("positions", positions, T, dev)
+    _tokens("slot_mapping", slot_mapping, T, dev)
+    if cos_sin.dim() != 2:
+        raise ValueError("cos_sin must be [max_pos, rot_dim]")
+    _exact("cos_sin", cos_sin, cos_sin.shape, (torch.float32,), dev)
     if q_out is None:
         q_out = q
-    qs, qos = _heads("q", q, Hq, D, elem), _heads("q_out", q_out, Hq, D, elem)
-    ks, vs = _heads("k", k, Hkv, D, elem), _heads("v", v, Hkv, D, elem)
+    qs = _heads("q", q, Hq, D, elem, T, dev)
+    qos = _heads("q_out", q_out, Hq, D, elem, T, dev)
+    ks, vs = _heads("k", k, Hkv, D, elem, T, dev), _heads("v", v, Hkv, D, elem, T, dev)
     max_pos, rot_dim = cos_sin.shape
     with torch.cuda.device(q.device):
         st = lib().rope_kv_write(
@@ -255,22 +304,25 @@ def dual_rmsnorm_quant(q, q_weight, eps_q, kv, kv_weight, eps_kv, q_quant_mode="
     """MLA dual RMSNorm of the q and kv latents in one launch; the q side is
     optionally FP8-quantized.  Returns (q_out, q_scales or None, kv_out)."""
     mode = _mode(q_quant_mode)
-    T, Hq = q.shape
-    Hkv = kv.shape[1]
     qs = _rows("q", q, _BF16)
-    kvs = _rows("kv", kv, _BF16)
-    _vector("q_weight", q_weight, Hq)
-    _vector("kv_weight", kv_weight, Hkv)
+    T, Hq = q.shape
+    dev = q.device
+    kvs = _rows("kv", kv, _BF16, rows=T, device=dev)
+    Hkv = kv.shape[1]
+    _vector("q_weight", q_weight, Hq, device=dev)
+    _vector("kv_weight", kv_weight, Hkv, device=dev)
     if q_out is None:
         dt = torch.bfloat16 if mode == Q_NONE else torch.float8_e4m3fn
-        q_out = torch.empty((T, Hq), dtype=dt, device=q.device)
-    qos = _rows("q_out", q_out, _BF16 if mode == Q_NONE else _FP8, Hq)
+        q_out = torch.empty((T, Hq), dtype=dt, device=dev)
+    qos = _rows("q_out", q_out, _BF16 if mode == Q_NONE else _FP8, Hq, T, dev)
     shape = _scales_shape(mode, T, Hq, group_size or 1)
     if q_scales is None and shape is not None:
-        q_scales = torch.empty(shape, dtype=torch.float32, device=q.device)
+        q_scales = torch.empty(shape, dtype=torch.float32, device=dev)
+    if q_scales is not None and shape is not None:
+        _exact("q_scales", q_scales, shape, (torch.float32,), dev)
     if kv_out is None:
-        kv_out = torch.empty((T, Hkv), dtype=torch.bfloat16, device=q.device)
-    kvos = _rows("kv_out", kv_out, _BF16, Hkv)
+        kv_out = torch.empty((T, Hkv), dtype=torch.bfloat16, device=dev)
+    kvos = _rows("kv_out", kv_out, _BF16, Hkv, T, dev)
     with torch.cuda.device(q.device):
         st = lib().dual_rmsnorm_quant(
             _ptr(q), qs, _ptr(q_weight), float(eps_q), _ptr(kv), kvs,
@@ -287,23 +339,24 @@ def qk_norm_rope_kv_write(positions, qkv, q_weight, k_weight, eps, cos_sin, Hq, 
     updated in place in qkv (and k with write_k).  With slot_mapping, rotated
     k and v go to the paged caches [num_blocks, block_size, Hkv, D].
     qkv: [T, (Hq + 2 Hkv) D] bf16 with contiguous rows.  Returns qkv."""
-    T = positions.shape[0]
     qs = _rows("qkv", qkv, _BF16, (Hq + 2 * Hkv) * D)
-    _need_cuda("positions", positions, (torch.int64,))
-    _need_cuda("cos_sin", cos_sin, (torch.float32,))
-    _vector("q_weight", q_weight, D)
-    _vector("k_weight", k_weight, D)
+    T, dev = qkv.shape[0], qkv.device
+    _tokens("positions", positions, T, dev)
+    if cos_sin.dim() != 2:
+        raise ValueError("cos_sin must be [max_pos, rot_dim]")
+    _exact("cos_sin", cos_sin, cos_sin.shape, (torch.float32,), dev)
+    _vector("q_weight", q_weight, D, device=dev)
+    _vector("k_weight", k_weight, D, device=dev)
     num_blocks = block_size = 0
     if slot_mapping is not None:
-        _need_cuda("slot_mapping", slot_mapping, (torch.int64,))
-        for name, c in (("key_cache", key_cache), ("value_cache", value_cache)):
-            _need_cuda(name, c, _BF16)
-            if not c.is_contiguous() or tuple(c.shape[2:]) != (Hkv, D):
-                raise ValueError(f"{name} must be a contiguous [num_blocks, block_size, Hkv, D] "
-                                 f"tensor")
+        _tokens("slot_mapping", slot_mapping, T, dev)
+        _need_cuda("key_cache", key_cache, _BF16, dev)
+        if key_cache.dim() != 4 or tuple(key_cache.shape[2:]) != (Hkv, D):
+            raise ValueError("key_cache must be a contiguous [num_blocks, block_size, Hkv, D] "
+                             "tensor")
         num_blocks, block_size = key_cache.shape[:2]
-        if tuple(value_cache.shape) != tuple(key_cache.shape):
-            raise ValueError("key_cache and value_cache must have the same shape")
+        for name, c in (("key_cache", key_cache), ("value_cache", value_cache)):
+            _exact(name, c, (num_blocks, block_size, Hkv, D), _BF16, dev)
     max_pos, rot_dim = cos_sin.shape
     with torch.cuda.device(qkv.device):
         st = lib().qk_norm_rope_kv_write(
@@ -319,15 +372,15 @@ def fused_add_rmsnorm_pad(x, residual, weight, eps, H_pad, out=None):
     """Residual add + RMSNorm, written into out[:, :H] with out[:, H:H_pad] = 0
     (residual updated in place).  x, residual, weight and out share one element
     type, bf16 or fp16.  Returns out [T, H_pad]."""
-    T, H = x.shape
     _need_cuda("x", x, tuple(_ELEM))
-    elem = (x.dtype,)
+    elem, dev = (x.dtype,), x.device
     xs = _rows("x", x, elem)
-    rs = _rows("residual", residual, elem, H) if residual is not None else 0
-    _vector("weight", weight, H, elem)
+    T, H = x.shape
+    rs = _rows("residual", residual, elem, H, T, dev) if residual is not None else 0
+    _vector("weight", weight, H, elem, dev)
     if out is None:
-        out = torch.empty((T, H_pad), dtype=x.dtype, device=x.device)
-    os_ = _rows("out", out, elem, H_pad)
+        out = torch.empty((T, H_pad), dtype=x.dtype, device=dev)
+    os_ = _rows("out", out, elem, H_pad, T, dev)
     with torch.cuda.device(x.device):
         st = lib().fused_add_rmsnorm_pad(_ptr(x), xs, _ptr(residual), rs, _ptr(weight),
                                          float(eps), _ptr(out), os_, T, H, H_pad,
@@ -343,15 +396,17 @@ def mla_rope_kv_write(positions, q, k_pe, kv_c, cos_sin, slot_mapping, kv_cache,
     the MLA cache write of [kv_c | rotated k_pe] at each token's slot.
     q: [T, Hq * q_head_stride] bf16; k_pe: [T, rope_dim]; kv_c: [T, kv_lora];
     kv_cache: [num_blocks, block_size, kv_lora + rope_dim].  Returns q."""
-    T = positions.shape[0]
     qs = _rows("q", q, _BF16)
-    ks = _rows("k_pe", k_pe, _BF16, rope_dim)
-    cs = _rows("kv_c", kv_c, _BF16)
+    T, dev = q.shape[0], q.device
+    ks = _rows("k_pe", k_pe, _BF16, rope_dim, T, dev)
+    cs = _rows("kv_c", kv_c, _BF16, rows=T, device=dev)
     kv_lora = kv_c.shape[1]
-    _need_cuda("positions", positions, (torch.int64,))
-    _need_cuda("slot_mapping", slot_mapping, (torch.int64,))
-    _need_cuda("cos_sin", cos_sin, (torch.float32,))
-    _need_cuda("kv_cache", kv_cache, _BF16)
+    _tokens("positions", positions, T, dev)
+    _tokens("slot_mapping", slot_mapping, T, dev)
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != rope_dim:
+        raise ValueError(f"cos_sin must be [max_pos, {rope_dim}]")
+    _exact("cos_sin", cos_sin, cos_sin.shape, (torch.float32,), dev)
+    _need_cuda("kv_cache", kv_cache, _BF16, dev)
     if kv_cache.dim() != 3 or kv_cache.shape[2] != kv_lora + rope_dim or \
             not kv_cache.is_contiguous():
         raise ValueError("kv_cache must be a contiguous [num_blocks, block_size, "
@@ -376,6 +431,7 @@ def e4m3fn_encode(x, out=None):
     x = x.contiguous()
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _exact("out", out, x.shape, (torch.uint8,), x.device)
     with torch.cuda.device(x.device):
         st = lib().rra_e4m3fn_encode(_ptr(x), _ptr(out), x.numel(), _stream(x))
     _check("rra_e4m3fn_encode", st)
