@@ -287,15 +287,14 @@ __global__ void __launch_bounds__(kBlock)
                                                                H_pad);
 }
 
-// MLA dual RMSNorm (arguments ordered so that the row count and everything
-// the first loads need are among the preloaded ones): one wave per token
-// handles both of its rows, the q latent
+// MLA dual RMSNorm: one wave per token handles both of its rows, the q latent
 // (NVQ vectors per lane) and the kv latent (NVKV), so both row reductions are
 // wave-local DPP reductions with no LDS exchange and no barrier (four tokens
 // per workgroup; waves past T leave at once).  Measured on MI355X at the
 // DeepSeek-V3 shape, this beats spreading a token over 2 or 4 waves at every
 // T from 512 to 16384: the rows are short, and a barrier per token costs more
-// than the extra vectors per lane.
+// than the extra vectors per lane.  The row count, both rows and the q weight
+// lead the argument list, so they are among the preloaded arguments.
 template <int NVQ, int NVKV, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
     dual_rmsnorm_quant_kernel(int64_t T, int Hq, int Hkv, const uint16_t* __restrict__ q,
