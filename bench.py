@@ -157,15 +157,26 @@ COMMON_SOURCES = ("rra_device.hpp", "rra_host.hpp")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_kernels_T8192_hbm_traffic.md")
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed (string
+    literals in these sources hold no comment markers)."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(kernel: str) -> str:
-    """sha256 (first 16 hex digits) of the sources a kernel is built from, so
-    that stored counter readings can be matched to the code they measured."""
+    """sha256 (first 16 hex digits) of the code of the sources a kernel is
+    built from (comments and layout excluded), so that stored counter readings
+    can be matched to the code they measured."""
     import hashlib
 
     h = hashlib.sha256()
     for name in sorted(KERNEL_SOURCES[kernel] + COMMON_SOURCES):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -701,8 +712,9 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out: str, commands: str, T
              f"1 GiB in the same runs: FETCH_SIZE reads {f_copy:.0f} KiB for 1 GiB read "
              f"(x{f_scale:.4f}), WRITE_SIZE reads {w_copy:.0f} KiB for 1 GiB written "
              f"(x{w_scale:.4f}).", "",
-             "`source` is the hash of the kernel's sources when the counters were taken "
-             "(bench.py reports `traffic` only while it matches).", "",
+             "`source` is the hash of the kernel's source code (comments and layout "
+             "excluded) when the counters were taken (bench.py reports `traffic` only while "
+             "it matches).", "",
              "| kernel | source | FETCH_SIZE KiB | WRITE_SIZE KiB | launches | traffic bytes | "
              "algorithmic bytes | traffic / algorithmic |", "|---|---|---|---|---|---|---|---|"]
     for k in KERNELS + NEXT_KERNELS:
