@@ -8,6 +8,7 @@ of the op's own GPU test (codes within 1 ULP on at most 1e-4 of them, scales
 and bf16/fp16 outputs within rtol 1e-2, caches exact outside the written
 slots)."""
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -31,7 +32,8 @@ def rra():
     r.lib()
     return r
 
-N_CASES = 20
+# Cases per entry point; RRA_RANDOM_CASES widens a run (the first cases stay the same).
+N_CASES = int(os.environ.get("RRA_RANDOM_CASES", "20"))
 
 
 def _cases(tag, draw):
