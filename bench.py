@@ -541,10 +541,21 @@ def environment() -> dict:
     import torch
 
     p = torch.cuda.get_device_properties(0)
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            names = [ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")]
+        cpu_model = names[0] if names else cpu_model
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
     return dict(device=torch.cuda.get_device_name(0), arch=getattr(p, "gcnArchName", ""),
                 compute_units=p.multi_processor_count, memory_gib=round(p.total_memory / 2**30, 1),
                 torch=torch.__version__, hip=getattr(torch.version, "hip", None),
-                host_cpus=os.cpu_count(), host=platform.processor() or platform.machine())
+                host_cpus=os.cpu_count(), host_cpus_usable=usable, host_cpu=cpu_model)
 
 
 # ---- CPU baseline: the oracle on a bounded sample --------------------------------
