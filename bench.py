@@ -97,21 +97,34 @@ def algo_bytes(name: str, T: int) -> int:
 
 
 # Work-items per launch at T tokens, as the library launches these workloads
-# (256-lane workgroups): one row per workgroup for the residual-add norm (four
-# waves per row at width 4096), one wave per 512 SiLU outputs, as many waves per
-# token as the RoPE units need at one unit per lane (48 heads x 8 two-vector
-# units: six), and one wave per token for the MLA norm.  Used only to tell the
-# sweep's launches apart in a kernel trace.
+# (256-lane workgroups): one row per workgroup for the residual-add norms (four
+# waves per row at widths above 2048), one wave per 512 SiLU outputs, one wave
+# per token for the MLA norm, and for the RoPE family as many waves per token
+# as its units need at one unit per lane (Llama-3-8B / Qwen3-8B attention: 48
+# heads x 8 two-vector units, six waves; DeepSeek-V3 MLA: 129 heads x 8
+# one-vector units + 64 kv_c vectors, eighteen).  Used only to tell the sweep's
+# launches apart in a kernel trace.
+def _rope_waves_per_token(units: int) -> int:
+    ku = max(1, -(-units // 2048))
+    return -(-(-(-units // ku)) // 64)
+
+
 def grid_threads(name: str, T: int) -> int:
+    import workloads
+
     if name == "silu_mul_quant":
         waves = T * -(-I_SILU // 512)
-    elif name == "rope_kv_write":
-        import workloads
-
+    elif name in ("rope_kv_write", "rope_kv_write_f16"):
         cfg = workloads.ROPE
         units = (cfg.Hq + 2 * cfg.Hkv) * (cfg.D // 16 if cfg.is_neox else cfg.D // 8)
-        ku = max(1, -(-units // 2048))
-        waves = T * -(-(-(-units // ku)) // 64)
+        waves = T * _rope_waves_per_token(units)
+    elif name == "qk_norm_rope_kv_write":
+        cfg = workloads.QKNORM
+        waves = T * _rope_waves_per_token((cfg.Hq + 2 * cfg.Hkv) * (cfg.D // 16))
+    elif name == "mla_rope_kv_write":
+        cfg = workloads.MLA_ROPE
+        per_head = cfg.rope_dim // 16 if cfg.is_neox else cfg.rope_dim // 8
+        waves = T * _rope_waves_per_token((cfg.Hq + 1) * per_head + cfg.kv_lora // 8)
     elif name == "dual_rmsnorm_quant":
         waves = T
     else:
@@ -804,6 +817,14 @@ def summarize_sweep(trace_csv: str, out: str, command: str, Ts, kernels=KERNELS)
 
 # ---- main ------------------------------------------------------------------------
 
+def _sweep_kernels(args) -> tuple:
+    names = tuple(k for k in args.sweep_kernels.split(",") if k)
+    unknown = [k for k in names if k not in BYTES_PER_TOKEN]
+    if unknown:
+        raise SystemExit(f"unknown kernels for --sweep-kernels: {unknown}")
+    return names
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -818,6 +839,9 @@ def main() -> int:
                     help="1 = also time the next-row kernels alone at T (cold, rotating sets)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="write a profiles/ summary from a rocprofv3 --stats run and exit")
+    ap.add_argument("--sweep-kernels", default=",".join(KERNELS),
+                    help="comma-separated kernels for --sweep / --summarize-sweep "
+                         "(default: the four step kernels)")
     ap.add_argument("--sweep-only", action="store_true",
                     help="run only the --sweep (no step, ceiling or baseline): for profiling")
     ap.add_argument("--summarize-sweep", metavar="KERNEL_TRACE_CSV",
@@ -837,7 +861,7 @@ def main() -> int:
         return 0
     if args.summarize_sweep:
         summarize_sweep(args.summarize_sweep, args.out, args.command,
-                        [int(t) for t in args.sweep.split(",") if t])
+                        [int(t) for t in args.sweep.split(",") if t], _sweep_kernels(args))
         return 0
 
     if args.gpus != 1:
@@ -856,7 +880,7 @@ def main() -> int:
     rra.lib()  # fail loudly if the HIP library is missing
     T = args.T
     if args.sweep_only:
-        rows = sweep([int(t) for t in args.sweep.split(",") if t])
+        rows = sweep([int(t) for t in args.sweep.split(",") if t], kernels=_sweep_kernels(args))
         hip = HipEvents()
         copy_yardstick(8192, 30, hip, torch.cuda.current_stream().cuda_stream, _blocker_cycles())
         print(json.dumps(dict(sweep=rows)), flush=True)
@@ -905,7 +929,8 @@ def main() -> int:
         result["next_rows"] = {r["kernel"]: {k: v for k, v in r.items() if k != "kernel"}
                                for r in sweep([T], kernels=NEXT_KERNELS)}
     if args.sweep:
-        result["sweep"] = sweep([int(t) for t in args.sweep.split(",") if t])
+        result["sweep"] = sweep([int(t) for t in args.sweep.split(",") if t],
+                                kernels=_sweep_kernels(args))
         hip = HipEvents()
         floor_ms, _ = copy_yardstick(8192, 30, hip, torch.cuda.current_stream().cuda_stream,
                                      _blocker_cycles())
