@@ -175,8 +175,8 @@ int rope_cos_sin_cache(float* cos_sin, int64_t max_pos, int rot_dim, double thet
  * slot_mapping [T] int64.
  * key_cache, value_cache [num_blocks, block_size, Hkv, D] dtype, contiguous.
  * Limits: D in {64, 128, 256}; rot_dim == D; is_neox 1 (GPT-NeoX pairs
- * (i, i + D/2)) or 0 (GPT-J pairs (2i, 2i + 1)); Hq, Hkv >= 1; block_size >= 1;
- * dtype RRA_BF16 or RRA_F16 (else RRA_ERR_UNSUPPORTED).
+ * (i, i + D/2)) or 0 (GPT-J pairs (2i, 2i + 1)); 1 <= Hq, Hkv <= 65536;
+ * block_size >= 1; dtype RRA_BF16 or RRA_F16 (else RRA_ERR_UNSUPPORTED).
  */
 int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_stride,
                   uint16_t* q_out, int64_t q_out_stride, const uint16_t* k, int64_t k_stride,
@@ -232,7 +232,7 @@ int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_we
  * cos_sin      [max_pos, D] fp32 (see rope_cos_sin_cache).
  * slot_mapping [T] int64 or NULL (no cache write; caches may then be NULL).
  * Limits: D in {64, 128, 256}; rot_dim == D; is_neox 1 (pairs (i, i + D/2))
- * or 0 (pairs (2i, 2i + 1)).
+ * or 0 (pairs (2i, 2i + 1)); 1 <= Hq, Hkv <= 65536.
  */
 int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, int64_t qkv_stride,
                           const uint16_t* q_weight, const uint16_t* k_weight, float eps,
@@ -282,8 +282,9 @@ int fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residua
  * kv_c      [T, kv_lora] bf16 (already normalized), row stride kv_c_stride.
  * cos_sin   [max_pos, rope_dim] fp32 (see rope_cos_sin_cache).
  * kv_cache  [num_blocks, block_size, kv_lora + rope_dim] bf16, contiguous.
- * Limits: rope_dim in {64, 128}; kv_lora % 8 == 0; q_head_stride % 8 == 0;
- * is_neox 0 (GPT-J pairs, as DeepSeek) or 1.
+ * Limits: rope_dim in {64, 128}; kv_lora % 8 == 0, kv_lora <= 2^24;
+ * q_head_stride % 8 == 0; 1 <= Hq <= 65536; is_neox 0 (GPT-J pairs, as
+ * DeepSeek) or 1.
  */
 int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64_t q_stride,
                       int64_t q_head_stride, const uint16_t* k_pe, int64_t k_pe_stride,

@@ -42,6 +42,7 @@
 namespace rra {
 
 constexpr int kRopeMaxWaves = 32;                 // waves per token at most
+constexpr int kRopeMaxHeads = 1 << 16;            // head counts accepted (unit indices fit int)
 constexpr int kRopeMaxUnitsPerPass = 4;           // units a lane loads before storing
 
 // Most units per lane and pass: 4 two-vector (NeoX) or 8 one-vector (GPT-J)
@@ -507,8 +508,9 @@ inline RopeLaunch rope_launch(int64_t units, int is_neox) {
 // Workgroups for T tokens of shape.tw.d waves; 0 when the launch's wave count
 // would reach 2^31 (the multiply-high division covers smaller ones).
 inline int64_t rope_blocks(int64_t T, const RopeLaunch& shape) {
+  if (T > (int64_t(1) << 31)) return 0;
   const int64_t waves = T * shape.tw.d;
-  if (T > (int64_t(1) << 31) || waves > 0x7FFFFFFF - kWavesPerBlock) return 0;
+  if (waves > 0x7FFFFFFF - kWavesPerBlock) return 0;
   return ceil_div(waves, kWavesPerBlock);
 }
 
@@ -542,6 +544,7 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   RRA_REQUIRE(T >= 0 && Hq > 0 && Hkv > 0 && D > 0 && rot_dim > 0 && block_size > 0 &&
                   num_blocks > 0 && max_pos > 0,
               RRA_ERR_SHAPE);
+  RRA_REQUIRE(Hq <= kRopeMaxHeads && Hkv <= kRopeMaxHeads, RRA_ERR_UNSUPPORTED);
   // Tensors of T tokens may be NULL when T == 0 (an empty torch tensor has no storage).
   const bool tokens_ok = T == 0 || (positions && q && q_out && k && v && slot_mapping);
   RRA_REQUIRE(tokens_ok && cos_sin && key_cache && value_cache, RRA_ERR_NULL);
@@ -600,6 +603,7 @@ extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, in
                                      int64_t num_blocks, int is_neox, void* stream) {
   RRA_REQUIRE(T >= 0 && Hq > 0 && Hkv > 0 && D > 0 && rot_dim > 0 && max_pos > 0,
               RRA_ERR_SHAPE);
+  RRA_REQUIRE(Hq <= kRopeMaxHeads && Hkv <= kRopeMaxHeads, RRA_ERR_UNSUPPORTED);
   RRA_REQUIRE(qkv_stride >= int64_t(Hq + 2 * Hkv) * D, RRA_ERR_SHAPE);
   const bool tokens_ok = T == 0 || (positions && qkv);
   RRA_REQUIRE(tokens_ok && q_weight && k_weight && cos_sin, RRA_ERR_NULL);
@@ -653,7 +657,10 @@ extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64
   RRA_REQUIRE(T >= 0 && Hq > 0 && kv_lora > 0 && rope_dim > 0 && block_size > 0 &&
                   num_blocks > 0 && max_pos > 0,
               RRA_ERR_SHAPE);
-  RRA_REQUIRE(q_head_stride >= rope_dim && q_stride >= int64_t(Hq - 1) * q_head_stride + rope_dim &&
+  RRA_REQUIRE(Hq <= kRopeMaxHeads && kv_lora <= (1 << 24), RRA_ERR_UNSUPPORTED);
+  // q_stride >= (Hq - 1) * q_head_stride + rope_dim, written so nothing overflows
+  RRA_REQUIRE(q_head_stride >= rope_dim && q_stride >= rope_dim &&
+                  (Hq == 1 || q_head_stride <= (q_stride - rope_dim) / (Hq - 1)) &&
                   k_pe_stride >= rope_dim && kv_c_stride >= kv_lora,
               RRA_ERR_SHAPE);
   const bool tokens_ok = T == 0 || (positions && q_pe && k_pe && kv_c && slot_mapping);

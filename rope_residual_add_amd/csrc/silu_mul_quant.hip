@@ -137,9 +137,9 @@ extern "C" int silu_mul_quant(const uint16_t* in, int64_t in_stride, int quant_m
                               int64_t out_stride, float* scales, int64_t T, int64_t I,
                               void* stream) {
   RRA_REQUIRE(T >= 0 && I > 0, RRA_ERR_SHAPE);
+  RRA_REQUIRE(I % 8 == 0 && I <= (int64_t(1) << 30), RRA_ERR_UNSUPPORTED);
   RRA_REQUIRE(T == 0 || (in && out), RRA_ERR_NULL);  // empty tensors have no storage
   RRA_REQUIRE(in_stride >= 2 * I && out_stride >= I, RRA_ERR_SHAPE);
-  RRA_REQUIRE(I % 8 == 0 && I <= (int64_t(1) << 30), RRA_ERR_UNSUPPORTED);
   switch (quant_mode) {
     case RRA_Q_STATIC:
       RRA_REQUIRE(static_scale, RRA_ERR_NULL);

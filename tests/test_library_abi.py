@@ -112,6 +112,7 @@ def test_silu_validation(rra):
     # one wave per 512-column chunk (28 per row here): 2^31 waves or more are refused
     assert f(T=(1 << 31) // 28 + 1) == EUNSUP
     assert f(T=(1 << 31) + 1, I=512, s=1024, os=512) == EUNSUP
+    assert f(I=1 << 62, s=1 << 62, os=1 << 62) == EUNSUP  # no overflow in the stride checks
 
 
 def test_rope_validation(rra):
@@ -146,6 +147,8 @@ def test_rope_validation(rra):
     # 2^31 waves or more is refused before anything is enqueued
     assert f(T=(1 << 31) // 6 + 1) == EUNSUP
     assert f(T=(1 << 31) + 1, Hq=1, Hkv=1, qs=128, qos=128, ks=128, vs=128) == EUNSUP
+    assert f(T=1 << 62) == EUNSUP  # refused before any product of T
+    assert f(Hq=(1 << 16) + 1) == EUNSUP  # head counts up to 65536
     assert L.rope_cos_sin_cache(None, 8192, 128, 5e5, None) == ENULL
     assert L.rope_cos_sin_cache(A, 8192, 127, 5e5, None) == ESHAPE
     assert L.rope_cos_sin_cache(A, 8192, 128, -1.0, None) == EUNSUP
@@ -199,6 +202,7 @@ def test_qk_norm_rope_validation(rra):
     assert f(kw=A + 8) == EALIGN
     assert f(bs=0) == ESHAPE
     assert f(T=(1 << 31) // 6 + 1) == EUNSUP  # 384 units: six waves per token
+    assert f(Hkv=70000) == EUNSUP
 
 
 def test_rmsnorm_pad_validation(rra):
@@ -244,6 +248,8 @@ def test_mla_rope_validation(rra):
     assert f(lora=500, cs_=500) == EUNSUP
     assert f(neox=2) == EUNSUP
     assert f(T=(1 << 31) // 18 + 1) == EUNSUP  # 1096 one-vector units: eighteen waves per token
+    assert f(Hq=70000) == EUNSUP
+    assert f(hs=1 << 62) == ESHAPE  # (Hq - 1) * head stride past the row, without overflow
     assert f(hs=196, qs=25088) == EALIGN  # head stride not a multiple of 8
     assert f(kv=A + 4) == EALIGN
 
