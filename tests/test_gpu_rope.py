@@ -116,6 +116,12 @@ def test_attention_workload(rra, oracle, T):
     run(rra, oracle, T)
 
 
+def test_gptj_at_full_size(rra, oracle):
+    """The attention workload at T = 8192 with GPT-J pairs (768 one-vector
+    units per token: twelve waves) and padding tokens mixed in."""
+    run(rra, oracle, 8192, dataclasses.replace(workloads.ROPE, is_neox=False), pad_every=97)
+
+
 def test_padding_tokens(rra, oracle):
     run(rra, oracle, 300, pad_every=3)
 
