@@ -136,14 +136,22 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
   if constexpr (kMode == RRA_Q_NONE) {
     const float rho_f = static_cast<float>(rho);
     uint16_t* o = static_cast<uint16_t*>(out);
+    // A row of values near the fp32 subnormal range (with eps = 0) can have a
+    // rho beyond fp32: then y = t * rho is formed in double.
+    const bool wide = !(rho_f < 0x1p127f);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = i * stride + rl;
-      const float* ti = t.t[i];
-      const u32x4 packed{E::pack(ti[0] * rho_f, ti[1] * rho_f),
-                         E::pack(ti[2] * rho_f, ti[3] * rho_f),
-                         E::pack(ti[4] * rho_f, ti[5] * rho_f),
-                         E::pack(ti[6] * rho_f, ti[7] * rho_f)};
+      float y[8];
+      if (!wide) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = t.t[i][k] * rho_f;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = static_cast<float>(static_cast<double>(t.t[i][k]) * rho);
+      }
+      const u32x4 packed{E::pack(y[0], y[1]), E::pack(y[2], y[3]), E::pack(y[4], y[5]),
+                         E::pack(y[6], y[7])};
       if (kFull || idx < nvec) st_stream(o + idx * 8, packed);
     }
     return;

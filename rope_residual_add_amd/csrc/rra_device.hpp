@@ -178,7 +178,11 @@ __device__ __forceinline__ float f32_round_odd(double q) {
 
 // A quantization step: codes e4m3fn(t * rho / s).  f = fp32(rho) * rcp(s)
 // drives the fast path; rho (double) and s the exact one.  s = 0 (an all-zero
-// slice) gives f = 0 and all-zero codes.
+// slice) gives f = 0 and all-zero codes.  Where rho / s leaves the fp32 range
+// (a row of values near the fp32 subnormal range, where rho or 448 / amax is
+// huge) or s is itself subnormal (whose hardware reciprocal is not accurate),
+// f is set to 0: every v is then 0, which e4m3_near_tie flags, so every value
+// takes the exact path.
 struct QuantStep {
   float f;
   float s;
@@ -186,8 +190,10 @@ struct QuantStep {
 };
 
 __device__ __forceinline__ QuantStep quant_step(double rho, float s) {
-  const float f = s > 0.0f ? static_cast<float>(rho) * __builtin_amdgcn_rcpf(s) : 0.0f;
-  return QuantStep{f, s, rho};
+  if (!(s > 0.0f)) return QuantStep{0.0f, s, rho};
+  const float f = static_cast<float>(rho) * __builtin_amdgcn_rcpf(s);
+  const bool in_range = f < 0x1p127f && s >= 0x1p-126f;  // false for inf / NaN f too
+  return QuantStep{in_range ? f : 0.0f, s, rho};
 }
 
 // Eight codes e4m3fn(t[j] * rho / s).  kClamp = false when s is a dynamic
@@ -209,7 +215,8 @@ __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
     // p - q0 * s, which an fma gives exactly (Markstein's final division
     // step).  Taking p * (rho / s) instead can miss an exact midpoint by an
     // ulp of the double, and the round-to-odd narrowing would then move a
-    // true tie off it.
+    // true tie off it.  The quotient takes t's sign: the correction cannot
+    // flip a nonzero q0, but for t = -0 the residual sum +0 + -0 is +0.
     const double sd = static_cast<double>(qs.s);
     const double y = 1.0 / sd;
 #pragma unroll
@@ -217,7 +224,7 @@ __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
       if (near[j]) {
         const double p = static_cast<double>(t[j]) * qs.rho;
         const double q0 = p * y;
-        v[j] = f32_round_odd(fma(fma(-q0, sd, p), y, q0));
+        v[j] = copysignf(f32_round_odd(fma(fma(-q0, sd, p), y, q0)), t[j]);
       }
     }
   }
@@ -302,6 +309,18 @@ __device__ __forceinline__ double dpp_f64(double v) {
   const uint32_t hi = static_cast<uint32_t>(
       __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), kCtrl, kRowMask, 0xF, true));
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Max over aligned groups of n lanes (n = 8 or 16) of doubles >= 0; result in
+// every lane of the group.
+template <int n>
+__device__ __forceinline__ double group_max_f64(double v) {
+  static_assert(n == 8 || n == 16, "group size");
+  v = fmax(v, dpp_f64<0xB1>(v));
+  v = fmax(v, dpp_f64<0x4E>(v));
+  v = fmax(v, dpp_f64<0x141>(v));
+  if (n == 16) v = fmax(v, dpp_f64<0x140>(v));
+  return v;
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {

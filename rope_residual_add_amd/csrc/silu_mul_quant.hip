@@ -41,6 +41,36 @@ __device__ __forceinline__ void silu8(u32x4 g, u32x4 u, float a[8]) {
   }
 }
 
+// The per-group path for a group of tiny activations, in double: a = g / (1 +
+// exp(-g)) * u from the bf16 inputs, s = fp32(max |a| / 448), and each code's
+// quotient a / s narrowed to fp32 with round-to-odd before the one rounding to
+// e4m3 (as the exact path of the norms).  Called by every lane of a group when
+// its fp32 amax is below 2^-100; lanes whose group has no nonzero product
+// g * u keep the fast path's results (s = 0 or exact zeros).
+template <int kGroup>
+__device__ __forceinline__ void tiny_group(u32x4 gv, u32x4 uv, float& s, float v[8]) {
+  double a[8];
+  bool nonzero = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double g0 = bf16_lo(gv[k]), g1 = bf16_hi(gv[k]);
+    const double u0 = bf16_lo(uv[k]), u1 = bf16_hi(uv[k]);
+    a[2 * k] = g0 / (1.0 + exp(-g0)) * u0;
+    a[2 * k + 1] = g1 / (1.0 + exp(-g1)) * u1;
+    nonzero |= (g0 != 0.0 && u0 != 0.0) || (g1 != 0.0 && u1 != 0.0);
+  }
+  double m = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmax(m, fabs(a[j]));
+  m = group_max_f64<kGroup / 8>(m);
+  const float nz = group_max_f64<kGroup / 8>(nonzero ? 1.0 : 0.0);
+  if (nz == 0.0f) return;
+  s = static_cast<float>(m / 448.0);
+  const double sd = static_cast<double>(s);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = s > 0.0f ? f32_round_odd(a[j] / sd) : 0.0f;
+}
+
 // kMode RRA_Q_STATIC or RRA_Q_PER_GROUP with kGroup 64 or 128 (compile-time,
 // so group indexing is a shift).  kFull: I is a whole number of chunks, so
 // every vector index is in range and the bounds test is compiled out.
@@ -84,14 +114,22 @@ __global__ void __launch_bounds__(kBlock)
     // s = amax / 448 and f = 1 / s with a multiply and the hardware
     // reciprocal: the activation itself carries ~1e-6 relative error, so
     // correctly rounded divisions would buy nothing here.
-    const float s = m * (1.0f / 448.0f);
-    const float f = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+    float s = m * (1.0f / 448.0f);
+    float f = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = a[j] * f;
+    // A group whose activations are all below 2^-100 (gates below about -88,
+    // where exp overflows and the fp32 silu flushes to 0, or values near the
+    // fp32 subnormal range) is redone in double from the bf16 inputs, unless
+    // every product g * u is exactly 0 (an all-zero group needs nothing).
+    if (__builtin_expect(!(m >= 0x1p-100f), 0)) tiny_group<kGroup>(gv, uv, s, v);
     if (in_row) {
       if ((lane & (kLanesPerGroup - 1)) == 0)
         scales[static_cast<int64_t>(row) * (I / kGroup) + idx / kLanesPerGroup] = s;
       // |a * f| <= 448 within rounding: no saturation needed
-      st_stream(o, u32x2{pack_e4m3x4<false>(a[0] * f, a[1] * f, a[2] * f, a[3] * f),
-                         pack_e4m3x4<false>(a[4] * f, a[5] * f, a[6] * f, a[7] * f)});
+      st_stream(o, u32x2{pack_e4m3x4<false>(v[0], v[1], v[2], v[3]),
+                         pack_e4m3x4<false>(v[4], v[5], v[6], v[7])});
     }
   }
 }

@@ -1,0 +1,130 @@
+"""GPU parity on inputs of extreme magnitude and signed zeros.
+
+The fast paths work in fp32; these cases push them out of its range, where
+the kernels take their double-precision paths:
+  * RMSNorm rows near the fp32 subnormal range (rho or 448 / amax beyond fp32,
+    scales that are themselves subnormal), and rows near the bf16 maximum;
+  * SiLU groups whose gates lie below about -88 (exp(-g) overflows fp32 and
+    the fp32 activation flushes to zero), whose products g * u fall in the
+    fp32 subnormal range, or that are all zero;
+  * -0.0 inputs, whose code is 0x80 (e4m3fn keeps the sign of zero).
+Bars as in the other parity tests (codes within one code on at most 1e-4 of
+them, scales rtol 1e-2, bf16 within rtol 1e-2)."""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import (assert_bf16, assert_codes, assert_scales, dev_bf16, host_bf16, host_f32,
+                      host_u8, require_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rra():
+    require_gpu()
+    import rope_residual_add_amd as r
+
+    r.lib()
+    return r
+
+
+def _bf16(a) -> np.ndarray:
+    return workloads.to_bf16_bits(np.asarray(a, np.float32))
+
+
+NORM_ROWS = [  # (magnitude of x, eps)
+    (1e-20, 0.0), (1e-30, 1e-6), (1e-38, 1e-5), (1e-39, 0.0), (1e36, 1e-6)]
+
+
+@pytest.mark.parametrize("mode,g", [(1, 0), (2, 0), (3, 64), (3, 128)])
+@pytest.mark.parametrize("mag,eps", NORM_ROWS)
+def test_norm_extreme_rows(rra, oracle, mag, eps, mode, g):
+    import torch
+
+    say(f"[extreme] norm |x|~{mag:g} eps={eps:g} mode={mode} g={g}")
+    rng = np.random.default_rng(11)
+    T, H = 64, 1024
+    x = _bf16(rng.standard_normal((T, H)) * mag)
+    w = _bf16(1 + 0.1 * rng.standard_normal(H))
+    static = 0.05
+    ss = torch.tensor([static], dtype=torch.float32, device="cuda") if mode == 1 else None
+    out, scales = rra.fused_add_rmsnorm_quant(dev_bf16(x), None, dev_bf16(w), eps, mode, g, ss)
+    torch.cuda.synchronize()
+    ref, ref_scales, _ = oracle.fused_add_rmsnorm_quant(x, None, w, eps, mode, g, static)
+    assert_codes(host_u8(out), ref, f"codes |x|~{mag:g}")
+    if mode >= 2:
+        assert_scales(host_f32(scales).reshape(ref_scales.shape), ref_scales, "scales")
+
+
+def test_norm_negative_zero(rra, oracle):
+    """Rows of ordinary values with -0.0 entries: their codes are 0x80 in every
+    mode (zeros take the exact-quotient path)."""
+    import torch
+
+    say("[extreme] norm -0.0 entries")
+    rng = np.random.default_rng(12)
+    T, H = 32, 512
+    x = _bf16(rng.standard_normal((T, H)))
+    neg = rng.random((T, H)) < 0.1
+    x[neg] = 0x8000
+    w = _bf16(1 + 0.1 * rng.standard_normal(H))
+    for mode, g in ((1, 0), (2, 0), (3, 64), (3, 128)):
+        ss = torch.tensor([0.05], dtype=torch.float32, device="cuda") if mode == 1 else None
+        out, _ = rra.fused_add_rmsnorm_quant(dev_bf16(x), None, dev_bf16(w), 1e-6, mode, g, ss)
+        torch.cuda.synchronize()
+        ref, _, _ = oracle.fused_add_rmsnorm_quant(x, None, w, 1e-6, mode, g, 0.05)
+        codes = host_u8(out)
+        assert (ref[neg] == 0x80).all()
+        assert (codes[neg] == 0x80).all(), (mode, g, np.unique(codes[neg]))
+        assert_codes(codes, ref, f"-0 codes mode={mode}")
+
+
+@pytest.mark.parametrize("mag,eps", [(1e-20, 0.0), (1e-39, 0.0), (1e36, 1e-6)])
+def test_dual_extreme_rows(rra, oracle, mag, eps):
+    """MLA dual norm: bf16 kv output (rho beyond fp32 for the 1e-39 rows) and
+    per-group FP8 q."""
+    import torch
+
+    say(f"[extreme] dual |x|~{mag:g} eps={eps:g}")
+    rng = np.random.default_rng(13)
+    T, Hq, Hkv = 32, 1536, 512
+    q = _bf16(rng.standard_normal((T, Hq)) * mag)
+    kv = _bf16(rng.standard_normal((T, Hkv)) * mag)
+    qw = _bf16(1 + 0.1 * rng.standard_normal(Hq))
+    kw = _bf16(1 + 0.1 * rng.standard_normal(Hkv))
+    q_out, q_sc, kv_out = rra.dual_rmsnorm_quant(dev_bf16(q), dev_bf16(qw), eps, dev_bf16(kv),
+                                                 dev_bf16(kw), eps, 3, 128)
+    torch.cuda.synchronize()
+    rq, rs, rkv = oracle.dual_rmsnorm_quant(q, qw, eps, kv, kw, eps, 3, 128)
+    assert_codes(host_u8(q_out), rq, "dual q codes")
+    assert_scales(host_f32(q_sc).reshape(rs.shape), rs, "dual q scales")
+    assert_bf16(host_bf16(kv_out), rkv, "dual kv")
+
+
+def test_silu_extreme_groups(rra, oracle):
+    """Per-group SiLU with groups of gates in [-120, -90] and [-87, -80]
+    (activations near or below the fp32 subnormal range), products of
+    subnormal size, -0.0 gates, and an all-zero group."""
+    import torch
+
+    rng = np.random.default_rng(14)
+    for G in (64, 128):
+        say(f"[extreme] silu g={G}")
+        T, I = 16, 6 * G
+        g = rng.standard_normal((T, I)).astype(np.float32)
+        u = rng.standard_normal((T, I)).astype(np.float32)
+        g[:, 0:G] = rng.uniform(-120, -90, (T, G))
+        g[:, G:2 * G] = rng.uniform(-87, -80, (T, G))
+        u[:, 2 * G:3 * G] *= 1e-39
+        g[:, 3 * G:4 * G] = 0.0
+        u[:, 3 * G:4 * G] = 0.0
+        g[:, 4 * G:5 * G][rng.random((T, G)) < 0.25] = -0.0
+        inp = np.concatenate([_bf16(g), _bf16(u)], axis=1)
+        out, sc = rra.silu_mul_quant(dev_bf16(inp), 3, G)
+        torch.cuda.synchronize()
+        ref, ref_scales = oracle.silu_mul_quant(inp, 3, G)
+        codes, scales = host_u8(out), host_f32(sc)
+        assert_codes(codes, ref, f"silu extreme codes g={G}")
+        assert_scales(scales, ref_scales, f"silu extreme scales g={G}")
+        assert (scales[:, 0:3] > 0).all() and (scales[:, 3] == 0).all()
