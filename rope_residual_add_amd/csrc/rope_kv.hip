@@ -341,8 +341,27 @@ __global__ void __launch_bounds__(kBlock)
         for (int e = 0; e < kVals; ++e) ss = fmaf(x[e], x[e], ss);
       }
       ss = group_sum<kUnitsPerHead>(ss);  // all lanes: groups are q-, k-, v-only or idle
+      const float ms = ss * inv_d + eps;
+      float rho = __builtin_amdgcn_rsqf(ms);
+      // A head whose mean square (plus eps) is below 2^-100 (eps ~ 0 and
+      // values below about 1e-15, whose squares lose bits or flush in fp32)
+      // is normalized from x * 2^100 instead, with rho * 2^-100 folded into
+      // x * rho.  The branch is wave-uniform, so every lane of each group
+      // takes part in the second reduction.
+      const bool tiny = (is_q || is_k) && !(ms >= 0x1p-100f);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(tiny) != 0, 0)) {
+        float ss2 = 0.0f;
+        if (tiny) {
+#pragma unroll
+          for (int e = 0; e < kVals; ++e) {
+            x[e] *= 0x1p100f;
+            ss2 = fmaf(x[e], x[e], ss2);
+          }
+        }
+        ss2 = group_sum<kUnitsPerHead>(ss2);
+        if (tiny) rho = __builtin_amdgcn_rsqf(ss2 * inv_d + (eps * 0x1p100f) * 0x1p100f);
+      }
       if (is_q || is_k) {
-        const float rho = __builtin_amdgcn_rsqf(ss * inv_d + eps);
         float w[16];
         const bool use_q = kU == 1 || is_q;
         unpack8(use_q ? wq[0] : wk[0], w);

@@ -7,15 +7,17 @@ the kernels take their double-precision paths:
   * SiLU groups whose gates lie below about -88 (exp(-g) overflows fp32 and
     the fp32 activation flushes to zero), whose products g * u fall in the
     fp32 subnormal range, or that are all zero;
-  * -0.0 inputs, whose code is 0x80 (e4m3fn keeps the sign of zero).
+  * -0.0 inputs, whose code is 0x80 (e4m3fn keeps the sign of zero);
+  * QK-norm heads whose mean square is below 2^-100 with eps = 0.
 Bars as in the other parity tests (codes within one code on at most 1e-4 of
 them, scales rtol 1e-2, bf16 within rtol 1e-2)."""
 import numpy as np
 import pytest
 
 import workloads
-from gpu_util import (assert_bf16, assert_codes, assert_scales, dev_bf16, host_bf16, host_f32,
-                      host_u8, require_gpu, say)
+from gpu_util import (assert_bf16, assert_codes, assert_scales, dev, dev_bf16, host_bf16,
+                      host_f32, host_u8, require_gpu, say)
+from helpers import bf16_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -128,3 +130,35 @@ def test_silu_extreme_groups(rra, oracle):
         assert_codes(codes, ref, f"silu extreme codes g={G}")
         assert_scales(scales, ref_scales, f"silu extreme scales g={G}")
         assert (scales[:, 0:3] > 0).all() and (scales[:, 3] == 0).all()
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_qknorm_tiny_heads(rra, oracle, is_neox):
+    """QK norm with eps = 0 on heads of magnitude 1e-39 (bf16 subnormals) to
+    1e-15, mixed with ordinary heads in the same token: the tiny heads are
+    normalized from rescaled values, the others as usual (k written back)."""
+    import dataclasses
+
+    import torch
+
+    say(f"[extreme] qknorm tiny heads neox={is_neox}")
+    cfg = dataclasses.replace(workloads.QKNORM, eps=0.0)
+    T, Hq, Hkv, D = 64, cfg.Hq, cfg.Hkv, cfg.D
+    d = workloads.qknorm_inputs(T, cfg, with_cache=False)
+    rng = np.random.default_rng(15)
+    mags = np.array([1e-39, 1e-30, 1e-20, 1e-15, 1.0, 1e3])
+    heads = Hq + Hkv
+    x = rng.standard_normal((T, heads, D)) * mags[rng.integers(0, mags.size, (T, heads))][..., None]
+    qkv = d["qkv"].copy()
+    qkv[:, :heads * D] = _bf16(x.reshape(T, heads * D))
+    g = dev_bf16(qkv)
+    cs = rra.rope_cos_sin_cache(cfg.max_pos, D, cfg.theta)
+    rra.qk_norm_rope_kv_write(dev(d["positions"]), g, dev_bf16(d["q_w"]), dev_bf16(d["k_w"]),
+                              0.0, cs, Hq, Hkv, D, write_k=True, is_neox=is_neox)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.qk_norm_rope_kv_write(d["positions"], qkv, d["q_w"], d["k_w"], 0.0,
+                                             cfg.theta, cfg.max_pos, Hq, Hkv, D, write_k=True,
+                                             is_neox=is_neox)
+    got = host_bf16(g)
+    assert np.isfinite(bf16_to_f64(got[:, :heads * D])).all()
+    assert_bf16(got[:, :heads * D], ref[:, :heads * D], "q and k, tiny heads")
