@@ -37,11 +37,19 @@
  *   while weights, static scales, tables and caches must still be given.
  *   RRA_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).
  * - Device-data contract (not checked: checking would need a host sync):
- *   inputs are finite; a static scale is finite and > 0; positions lie in
- *   [0, max_pos); non-negative slots lie below num_blocks * block_size and are
- *   pairwise distinct.  Breaking it gives unspecified outputs (no memory is
- *   written outside the documented output ranges except through an
- *   out-of-range slot or position, which is undefined behaviour).
+ *   a static scale is finite and > 0; positions lie in [0, max_pos);
+ *   non-negative slots lie below num_blocks * block_size and are pairwise
+ *   distinct; in the quantizing norms each product z * weight stays below the
+ *   fp32 maximum (~3.4e38) in magnitude.  Breaking it gives unspecified
+ *   outputs (no memory is written outside the documented output ranges except
+ *   through an out-of-range slot or position, which is undefined behaviour).
+ * - Non-finite inputs propagate as IEEE arithmetic does, with these readings
+ *   of the dynamic scales: a NaN (or an infinity) in a normalized row makes
+ *   rho NaN (or 0) and every value of the row NaN or +-0, so each dynamic
+ *   scale of that row is 0 and its codes are +0; any slice whose scale comes
+ *   out 0 gets +0 codes; NaN activations (SiLU) are left out of their group's
+ *   amax and code as NaN; a static scale saturates infinities to +-448 and
+ *   keeps NaN.  The sign bit of a NaN result is unspecified.
  */
 #ifndef RRA_H
 #define RRA_H

@@ -177,9 +177,8 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
   }
 
   if constexpr (kMode == RRA_Q_PER_TOKEN) {
-    const float s = dynamic_scale(m_row, rho);
-    if (rl == 0) scale_row[0] = s;
-    const QuantStep qs = quant_step(rho, s);
+    const QuantStep qs = quant_step(rho, dynamic_scale(m_row, rho));
+    if (rl == 0) scale_row[0] = qs.s;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = i * stride + rl;

@@ -118,12 +118,13 @@ struct ElemF16 {
 // gfx950's v_cvt_pk_fp8_f32 converts to OCP e4m3fn with round-to-nearest-even:
 // magnitudes up to 464 (the midpoint above 448, a tie that goes to the even
 // code 448) give finite codes, larger ones give NaN (0x7F).  Saturating
-// conversion clamps to +-448 first (v_med3_f32); a caller whose values are
-// known to stay below 464 in magnitude (dynamic scales, where the largest
-// |y / s| is 448 within a few ulps) skips the clamp.
+// conversion clamps to +-448 first (v_med3_f32, which would turn a NaN into
+// -448, so a NaN is passed through to the conversion as it is); a caller whose
+// values are known to stay below 464 in magnitude (dynamic scales, where the
+// largest |y / s| is 448 within a few ulps) skips the clamp.
 
 __device__ __forceinline__ float clamp_e4m3(float v) {
-  return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+  return __builtin_isnan(v) ? v : __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
 }
 
 // Four fp32 -> four e4m3fn bytes, element 0 in the lowest byte; kClamp
@@ -177,8 +178,10 @@ __device__ __forceinline__ float f32_round_odd(double q) {
 }
 
 // A quantization step: codes e4m3fn(t * rho / s).  f = fp32(rho) * rcp(s)
-// drives the fast path; rho (double) and s the exact one.  s = 0 (an all-zero
-// slice) gives f = 0 and all-zero codes.  Where rho / s leaves the fp32 range
+// drives the fast path; rho (double) and s the exact one.  A scale that is not
+// positive (s = 0 for an all-zero slice; NaN where rho is NaN, from a NaN or
+// infinite value in the row) becomes s = 0, and such a slice gets +0 codes.
+// Where rho / s leaves the fp32 range
 // (a row of values near the fp32 subnormal range, where rho or 448 / amax is
 // huge) or s is itself subnormal (whose hardware reciprocal is not accurate),
 // f is set to 0: every v is then 0, which e4m3_near_tie flags, so every value
@@ -190,7 +193,7 @@ struct QuantStep {
 };
 
 __device__ __forceinline__ QuantStep quant_step(double rho, float s) {
-  if (!(s > 0.0f)) return QuantStep{0.0f, s, rho};
+  if (!(s > 0.0f)) return QuantStep{0.0f, 0.0f, rho};
   const float f = static_cast<float>(rho) * __builtin_amdgcn_rcpf(s);
   const bool in_range = f < 0x1p127f && s >= 0x1p-126f;  // false for inf / NaN f too
   return QuantStep{in_range ? f : 0.0f, s, rho};
@@ -200,6 +203,7 @@ __device__ __forceinline__ QuantStep quant_step(double rho, float s) {
 // scale (|t * rho / s| <= 448 within rounding).
 template <bool kClamp>
 __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
+  if (!(qs.s > 0.0f)) return u32x2{0u, 0u};
   float v[8];
   bool near[8];
   bool exact = false;
@@ -209,7 +213,7 @@ __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
     near[j] = e4m3_near_tie(v[j]);
     exact |= near[j];
   }
-  if (exact && qs.s > 0.0f) {
+  if (exact) {
     // q = p / s for p = t * rho, correctly rounded: q0 = p * y with y the
     // rounded reciprocal of s, then one correction with the residual
     // p - q0 * s, which an fma gives exactly (Markstein's final division
@@ -363,6 +367,7 @@ __device__ __forceinline__ float dynamic_scale(float m, double rho) {
 
 // 1/sqrt(x) in double for x > 0: the hardware estimate refined by two Newton
 // steps y <- y + y/2 * (1 - x y^2), each roughly doubling the correct bits.
+// x = +inf gives 0 (the steps alone would give inf * 0 = NaN).
 __device__ __forceinline__ double rsqrt_f64(double x) {
   double y = __builtin_amdgcn_rsq(x);
 #pragma unroll
@@ -370,7 +375,7 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
     const double e = fma(-x * y, y, 1.0);
     y = fma(0.5 * y, e, y);
   }
-  return y;
+  return __builtin_isinf(x) ? 0.0 : y;
 }
 
 }  // namespace rra

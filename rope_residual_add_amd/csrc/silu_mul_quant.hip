@@ -45,8 +45,9 @@ __device__ __forceinline__ void silu8(u32x4 g, u32x4 u, float a[8]) {
 // exp(-g)) * u from the bf16 inputs, s = fp32(max |a| / 448), and each code's
 // quotient a / s narrowed to fp32 with round-to-odd before the one rounding to
 // e4m3 (as the exact path of the norms).  Called by every lane of a group when
-// its fp32 amax is below 2^-100; lanes whose group has no nonzero product
-// g * u keep the fast path's results (s = 0 or exact zeros).
+// its fp32 amax is below 2^-100 (NaN activations do not count towards it); a
+// group with no nonzero product g * u keeps s = 0 and gets +0 codes, as any
+// slice whose scale is 0.
 template <int kGroup>
 __device__ __forceinline__ void tiny_group(u32x4 gv, u32x4 uv, float& s, float v[8]) {
   double a[8];
@@ -64,7 +65,11 @@ __device__ __forceinline__ void tiny_group(u32x4 gv, u32x4 uv, float& s, float v
   for (int j = 0; j < 8; ++j) m = fmax(m, fabs(a[j]));
   m = group_max_f64<kGroup / 8>(m);
   const float nz = group_max_f64<kGroup / 8>(nonzero ? 1.0 : 0.0);
-  if (nz == 0.0f) return;
+  if (nz == 0.0f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    return;
+  }
   s = static_cast<float>(m / 448.0);
   const double sd = static_cast<double>(s);
 #pragma unroll

@@ -162,3 +162,120 @@ def test_qknorm_tiny_heads(rra, oracle, is_neox):
     got = host_bf16(g)
     assert np.isfinite(bf16_to_f64(got[:, :heads * D])).all()
     assert_bf16(got[:, :heads * D], ref[:, :heads * D], "q and k, tiny heads")
+
+
+# ---- non-finite inputs -------------------------------------------------------
+# NaN codes are compared as one class (0x7F and 0xFF, and for bf16 every NaN
+# pattern): the sign of a NaN that arithmetic creates is not fixed by IEEE 754
+# and differs between the host's and the GPU's arithmetic.
+
+def _e4m3_nan_merged(c: np.ndarray) -> np.ndarray:
+    c = c.copy()
+    c[(c & 0x7F) == 0x7F] = 0x7F
+    return c
+
+
+def _bf16_nan_merged(h: np.ndarray) -> np.ndarray:
+    h = h.copy()
+    h[((h & 0x7F80) == 0x7F80) & ((h & 0x007F) != 0)] = 0x7FC0
+    return h
+
+
+def _special_norm_rows(rng, T, H):
+    """Rows 1-5 hold a NaN, +inf, -inf, an all-zero row with -0.0 entries and
+    an all -0.0 row; the rest are ordinary."""
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[1, 5] = np.nan
+    x[2, 7] = np.inf
+    x[3, 9] = -np.inf
+    x[4] = 0.0
+    x[4, ::3] = -0.0
+    x[5] = -0.0
+    return _bf16(x), [1, 2, 3, 4, 5]
+
+
+@pytest.mark.parametrize("mode,g", [(1, 0), (2, 0), (3, 64), (3, 128)])
+def test_norm_non_finite_rows(rra, oracle, mode, g):
+    """A row holding a NaN or an infinity: rho is NaN or 0, and the oracle's
+    reading gives scale 0 and +0 codes for every dynamic slice of it (the amax
+    of NaN values is 0), NaN codes (static scale) where a value is NaN.  Zero
+    rows with -0.0 entries get scale 0 and +0 codes."""
+    import torch
+
+    say(f"[extreme] norm non-finite rows mode={mode} g={g}")
+    rng = np.random.default_rng(16)
+    T, H = 16, 1024
+    x, special = _special_norm_rows(rng, T, H)
+    w = _bf16(1 + 0.1 * rng.standard_normal(H))
+    ss = torch.tensor([0.05], dtype=torch.float32, device="cuda") if mode == 1 else None
+    out, scales = rra.fused_add_rmsnorm_quant(dev_bf16(x), None, dev_bf16(w), 1e-6, mode, g, ss)
+    torch.cuda.synchronize()
+    ref, ref_scales, _ = oracle.fused_add_rmsnorm_quant(x, None, w, 1e-6, mode, g, 0.05)
+    codes = host_u8(out)
+    ordinary = np.setdiff1d(np.arange(T), special)
+    assert np.array_equal(_e4m3_nan_merged(codes[special]), _e4m3_nan_merged(ref[special]))
+    assert_codes(codes[ordinary], ref[ordinary], "ordinary rows")
+    if mode >= 2:
+        got = host_f32(scales).reshape(ref_scales.shape)
+        assert not np.isnan(got).any()
+        assert (got[special] == 0).all() and (ref_scales[special] == 0).all()
+        assert_scales(got[ordinary], ref_scales[ordinary], "ordinary scales")
+
+
+def test_dual_non_finite_rows(rra, oracle):
+    import torch
+
+    say("[extreme] dual non-finite rows")
+    rng = np.random.default_rng(17)
+    T, Hq, Hkv = 16, 1536, 512
+    q, special = _special_norm_rows(rng, T, Hq)
+    kv, _ = _special_norm_rows(rng, T, Hkv)
+    qw = _bf16(1 + 0.1 * rng.standard_normal(Hq))
+    kw = _bf16(1 + 0.1 * rng.standard_normal(Hkv))
+    q_out, q_sc, kv_out = rra.dual_rmsnorm_quant(dev_bf16(q), dev_bf16(qw), 1e-6, dev_bf16(kv),
+                                                 dev_bf16(kw), 1e-6, 3, 128)
+    torch.cuda.synchronize()
+    rq, rs, rkv = oracle.dual_rmsnorm_quant(q, qw, 1e-6, kv, kw, 1e-6, 3, 128)
+    ordinary = np.setdiff1d(np.arange(T), special)
+    codes, kvg, sc = host_u8(q_out), host_bf16(kv_out), host_f32(q_sc).reshape(rs.shape)
+    assert np.array_equal(_e4m3_nan_merged(codes[special]), _e4m3_nan_merged(rq[special]))
+    assert (sc[special] == 0).all() and (rs[special] == 0).all()
+    assert np.array_equal(_bf16_nan_merged(kvg[special]), _bf16_nan_merged(rkv[special]))
+    assert_codes(codes[ordinary], rq[ordinary], "dual ordinary q")
+    assert_bf16(kvg[ordinary], rkv[ordinary], "dual ordinary kv")
+
+
+@pytest.mark.parametrize("mode,G", [(1, 0), (3, 64), (3, 128)])
+def test_silu_non_finite(rra, oracle, mode, G):
+    """NaN and infinite gates and ups: NaN activations code as NaN and do not
+    count towards a group's amax; an infinite activation makes the group's
+    scale infinite (its other codes +-0); a group of -0.0 products gets scale 0
+    and +0 codes; a static scale saturates infinities and keeps NaN."""
+    import torch
+
+    say(f"[extreme] silu non-finite mode={mode} g={G}")
+    rng = np.random.default_rng(18)
+    T, I = 8, 512
+    g = (2 * rng.standard_normal((T, I))).astype(np.float32)
+    u = rng.standard_normal((T, I)).astype(np.float32)
+    g[1, 5] = np.nan
+    g[2, 7] = np.inf
+    g[3, 9] = -np.inf
+    u[4, 10] = np.inf
+    u[5, 11] = np.nan
+    g[6, :128] = -0.0
+    special = (np.isnan(g) | np.isinf(g) | np.isnan(u) | np.isinf(u))
+    special[6, :128] = True
+    inp = np.concatenate([_bf16(g), _bf16(u)], axis=1)
+    ss = torch.tensor([0.05], dtype=torch.float32, device="cuda") if mode == 1 else None
+    out, sc = rra.silu_mul_quant(dev_bf16(inp), mode, G, ss)
+    torch.cuda.synchronize()
+    ref, ref_scales = oracle.silu_mul_quant(inp, mode, G, 0.05)
+    codes = host_u8(out)
+    assert np.array_equal(_e4m3_nan_merged(codes[special]), _e4m3_nan_merged(ref[special]))
+    assert_codes(np.where(special, 0, codes), np.where(special, 0, ref).astype(np.uint8),
+                 "silu other codes")
+    if mode == 3:
+        got = host_f32(sc)
+        assert not np.isnan(got).any()
+        assert_scales(got, ref_scales, "silu scales")
