@@ -316,22 +316,32 @@ __global__ void __launch_bounds__(kBlock)
   if (row >= T) return;
   const int nq = Hq >> 3, nkv = Hkv >> 3;
 
-  // Issue every load of the token before either reduction.
+  // Issue every load of the token before either reduction, kv's first: its
+  // whole norm (reduction, rsqrt and bf16 output) then runs while q's loads
+  // are still in flight, and its short row leaves the registers before q's
+  // quantization needs them (at the DeepSeek-V3 shape this keeps the kernel
+  // within 64 VGPRs, i.e. 8 waves per SIMD, so 8192 one-wave tokens are
+  // resident at once).
   RowVecs<NVQ> zq, wq;
   RowVecs<NVKV> zkv, wkv;
-  load_row<NVQ, true, kFull>(zq, q + row * q_stride, nq, rl, kWave, true);
   load_row<NVKV, true, kFull>(zkv, kv + row * kv_stride, nkv, rl, kWave, true);
-  load_row<NVQ, false, kFull>(wq, q_w, nq, rl, kWave, true);
   load_row<NVKV, false, kFull>(wkv, kv_w, nkv, rl, kWave, true);
+  load_row<NVQ, true, kFull>(zq, q + row * q_stride, nq, rl, kWave, true);
+  load_row<NVQ, false, kFull>(wq, q_w, nq, rl, kWave, true);
+
+  RowT<NVKV> tkv;
+  double ss_kv;
+  float m_kv;
+  row_prepare(zkv, wkv, false, tkv, ss_kv, m_kv);
+  ss_kv = wave_sum_f64(ss_kv);
+  rmsnorm_emit<NVKV, RRA_Q_NONE, 0, kFull>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kWave, 0.0f,
+                                           kv_out + row * kv_out_stride, nullptr);
 
   RowT<NVQ> tq;
-  RowT<NVKV> tkv;
-  double ss_q, ss_kv;
-  float m_q, m_kv;
+  double ss_q;
+  float m_q;
   row_prepare(zq, wq, kMode == RRA_Q_PER_TOKEN, tq, ss_q, m_q);
-  row_prepare(zkv, wkv, false, tkv, ss_kv, m_kv);
   ss_q = wave_sum_f64(ss_q);
-  ss_kv = wave_sum_f64(ss_kv);
   if (kMode == RRA_Q_PER_TOKEN) m_q = wave_max(m_q);
 
   void* qo;
@@ -342,11 +352,6 @@ __global__ void __launch_bounds__(kBlock)
     qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
     scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
   }
-  // kv first: its short row then leaves the registers before q's quantization
-  // needs them (at the DeepSeek-V3 shape this keeps the kernel within 64 VGPRs,
-  // i.e. 8 waves per SIMD, so 8192 one-wave tokens are resident at once).
-  rmsnorm_emit<NVKV, RRA_Q_NONE, 0, kFull>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kWave, 0.0f,
-                                           kv_out + row * kv_out_stride, nullptr);
   rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kWave, 0.0f, qo,
                                           scale_row);
 }
