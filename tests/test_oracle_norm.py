@@ -214,3 +214,29 @@ def test_exact_tie_rounds_to_even(oracle, s, m, z0, w0, eps, code, side):
     codes, _, _ = oracle.fused_add_rmsnorm_quant(x, None, w, eps, oracle.Q_STATIC,
                                                   static_scale=s)
     assert codes[0, 0] == code and not codes[0, 1:].any()
+
+
+def test_non_finite_rows(oracle):
+    """The stated readings for non-finite rows: a NaN makes rho NaN and every
+    value NaN, whose amax is 0, so each dynamic scale of the row is 0 with +0
+    codes, and a static scale codes every value as NaN; an infinity makes
+    rho 0, so the static codes are +-0 (sign of z * w) except NaN at the
+    infinity itself.  Ordinary rows in the same call are unaffected."""
+    H = 16
+    w = workloads.to_bf16_bits(np.linspace(0.5, 1.5, H).astype(np.float32))
+    x = np.ones((3, H), np.float32)
+    x[0, 3] = np.nan
+    x[1, 4] = np.inf
+    x[1, 5] = -2.0
+    xb = workloads.to_bf16_bits(x)
+    for mode, g in ((2, 0), (3, 8)):
+        codes, scales, _ = oracle.fused_add_rmsnorm_quant(xb, None, w, 1e-6, mode, g)
+        assert (scales[:2] == 0).all() and (codes[:2] == 0).all()
+        assert (scales[2] > 0).all() and (codes[2] != 0).all()
+    codes, _, _ = oracle.fused_add_rmsnorm_quant(xb, None, w, 1e-6, 1, 0, 0.05)
+    assert ((codes[0] & 0x7F) == 0x7F).all()
+    assert (codes[1, 4] & 0x7F) == 0x7F
+    assert codes[1, 5] == 0x80
+    assert (codes[1, np.r_[0:4, 6:H]] == 0x00).all()
+    ref, _, _ = oracle.fused_add_rmsnorm_quant(xb[2:], None, w, 1e-6, 1, 0, 0.05)
+    assert np.array_equal(codes[2], ref[0])

@@ -86,3 +86,27 @@ def test_argument_errors(oracle):
         oracle.silu_mul_quant(d["inp"], oracle.Q_PER_GROUP, 128)
     with pytest.raises(oracle.OracleError):
         oracle.silu_mul_quant(d["inp"], oracle.Q_STATIC, static_scale=-1.0)
+
+
+def test_non_finite_activations(oracle):
+    """The stated readings for SiLU: a NaN activation codes as NaN and is left
+    out of its group's amax; an infinite one makes the group's scale infinite
+    (its finite values then code as +-0); a group of zero products gets scale 0
+    and +0 codes, also for -0.0; a static scale saturates an infinity to 448."""
+    G, I = 8, 32
+    g = np.full((1, I), 1.0, np.float32)
+    u = np.full((1, I), 1.0, np.float32)
+    g[0, 2] = np.nan
+    u[0, 9] = np.inf
+    g[0, 16:24] = -0.0
+    inp = np.concatenate([workloads.to_bf16_bits(g), workloads.to_bf16_bits(u)], axis=1)
+    codes, scales = oracle.silu_mul_quant(inp, 3, G)
+    silu1 = 1.0 / (1.0 + np.exp(-1.0))
+    assert (codes[0, 2] & 0x7F) == 0x7F
+    assert scales[0, 0] == np.float32(silu1 / 448.0)
+    assert np.isinf(scales[0, 1]) and (codes[0, 8:16][np.arange(8) != 1] == 0).all()
+    assert (codes[0, 9] & 0x7F) == 0x7F
+    assert scales[0, 2] == 0 and (codes[0, 16:24] == 0).all()
+    assert (codes[0, 24:32] == 0x7E).all()
+    static, _ = oracle.silu_mul_quant(inp, 1, 0, 0.05)
+    assert static[0, 9] == 0x7E and (static[0, 2] & 0x7F) == 0x7F
