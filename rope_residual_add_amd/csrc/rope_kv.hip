@@ -231,14 +231,8 @@ __global__ void __launch_bounds__(kBlock)
         if (kNeox) hi[j] = ld_stream(p + hi_off);
       }
     }
-    // Wave-uniform tests on the wave's first and last unit of this pass (units
-    // grow with the lane and the pass): a wave that holds only v units needs
-    // no cos/sin (and, since later passes only move further into v, never
-    // will), and one that holds only q units needs no slot.
-    const int first = u0 + (rl - lane_id());
-    if (u0 == 0 && first < uq + ukv)
-      unit_cos_sin<D, kNeox>(cos_sin + positions[t] * D, c, cs, sn);
-    const int64_t slot = first + (kU - 1) * lanes + (kWave - 1) >= uq ? slot_mapping[t] : -1;
+    if (u0 == 0) unit_cos_sin<D, kNeox>(cos_sin + positions[t] * D, c, cs, sn);
+    const int64_t slot = slot_mapping[t];
     // The cache is [num_blocks, block_size, Hkv, D] and contiguous, so slot
     // block * block_size + offset starts at element slot * Hkv * D.
     const int64_t cache_row = (slot >= 0 ? slot : 0) * Hkv * D;
