@@ -240,3 +240,22 @@ def test_non_finite_rows(oracle):
     assert (codes[1, np.r_[0:4, 6:H]] == 0x00).all()
     ref, _, _ = oracle.fused_add_rmsnorm_quant(xb[2:], None, w, 1e-6, 1, 0, 0.05)
     assert np.array_equal(codes[2], ref[0])
+
+
+@pytest.mark.parametrize("factor", [2.0 ** -100, 2.0 ** -120, 2.0 ** 100])
+@pytest.mark.parametrize("mode,g", [(2, 0), (3, 64)])
+def test_scale_invariance_at_range_ends(oracle, factor, mode, g):
+    """The same law far from 1: with eps = 0, x scaled by 2^-100, 2^-120 or
+    2^100 (exact in bf16 for these rows, whose values stay normal) gives the
+    codes and scales of x, so rows near the ends of the range have a fixed
+    expected answer."""
+    rng = np.random.default_rng(21)
+    x = workloads.to_bf16_bits((rng.uniform(0.5, 2.0, (8, 256)) *
+                                rng.choice([-1, 1], (8, 256))).astype(np.float32))
+    w = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(256)).astype(np.float32))
+    scaled = bf16_to_f64(x) * factor
+    xs = workloads.to_bf16_bits(scaled.astype(np.float32))
+    assert np.array_equal(bf16_to_f64(xs), scaled)  # the scaling is exact
+    a = oracle.fused_add_rmsnorm_quant(x, None, w, 0.0, mode, g)
+    b = oracle.fused_add_rmsnorm_quant(xs, None, w, 0.0, mode, g)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
