@@ -358,3 +358,26 @@ def test_mla_k_pe_matches_single_head_rope(oracle):
     flat = cache.reshape(n, -1)
     assert np.array_equal(flat[d["slot_mapping"], cfg.kv_lora:],
                           kc.reshape(n, -1)[d["slot_mapping"]])
+
+
+@pytest.mark.parametrize("factor", [2.0 ** -110, 2.0 ** 100])
+def test_qknorm_scale_invariance_at_range_ends(oracle, factor):
+    """With eps = 0 the per-head norm ignores a power-of-two scale of q and k
+    (exact in bf16 for these values), so heads near the ends of the range have
+    the outputs of ordinary ones."""
+    import dataclasses
+
+    cfg = dataclasses.replace(workloads.QKNORM, Hq=4, Hkv=2, eps=0.0)
+    d = workloads.qknorm_inputs(5, cfg, with_cache=False)
+    rng = np.random.default_rng(22)
+    n = (cfg.Hq + cfg.Hkv) * cfg.D
+    vals = rng.uniform(0.5, 2.0, (5, n)) * rng.choice([-1, 1], (5, n))
+    base = d["qkv"].copy()
+    base[:, :n] = workloads.to_bf16_bits(vals.astype(np.float32))
+    scaled = base.copy()
+    scaled[:, :n] = workloads.to_bf16_bits((vals * factor).astype(np.float32))
+    assert np.array_equal(bf16_to_f64(scaled[:, :n]), bf16_to_f64(base[:, :n]) * factor)
+    args = (d["q_w"], d["k_w"], 0.0, cfg.theta, cfg.max_pos, cfg.Hq, cfg.Hkv, cfg.D)
+    a, _, _ = oracle.qk_norm_rope_kv_write(d["positions"], base, *args, write_k=True)
+    b, _, _ = oracle.qk_norm_rope_kv_write(d["positions"], scaled, *args, write_k=True)
+    assert np.array_equal(a[:, :n], b[:, :n])
