@@ -232,7 +232,11 @@ int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_we
  * qkv.  With slot_mapping != NULL, token t with s = slot_mapping[t] >= 0
  * writes k_h and the unchanged v_h to key_cache / value_cache[s / block_size,
  * s % block_size, h, :] (layout and slot rules as rope_kv_write).  write_k = 1
- * also writes k_h back into qkv (always for tokens without a slot).
+ * also writes k_h back into qkv, for every token, with or without a slot.
+ * With write_k = 0, qkv's k heads keep their input values, and the k result of
+ * a padding token (slot < 0) goes nowhere.  Without a cache (slot_mapping ==
+ * NULL) write_k must be 1: write_k = 0 there returns RRA_ERR_UNSUPPORTED,
+ * since k's result would be dropped for every token.
  *
  * qkv          [T, (Hq + 2 Hkv) D] bf16: q heads, then k heads, then v heads;
  *              row stride qkv_stride; read and written.

@@ -333,12 +333,16 @@ def dual_rmsnorm_quant(q, q_weight, eps_q, kv, kv_weight, eps_kv, q_quant_mode="
 
 
 def qk_norm_rope_kv_write(positions, qkv, q_weight, k_weight, eps, cos_sin, Hq, Hkv, D,
-                          slot_mapping=None, key_cache=None, value_cache=None, write_k=False,
+                          slot_mapping=None, key_cache=None, value_cache=None, write_k=None,
                           is_neox=True):
     """Per-head RMSNorm of q and k inside the packed qkv rows, then RoPE; q is
     updated in place in qkv (and k with write_k).  With slot_mapping, rotated
     k and v go to the paged caches [num_blocks, block_size, Hkv, D].
+    write_k defaults to True without a cache (k's only destination is then
+    qkv; False is refused there) and to False with one.
     qkv: [T, (Hq + 2 Hkv) D] bf16 with contiguous rows.  Returns qkv."""
+    if write_k is None:
+        write_k = slot_mapping is None
     qs = _rows("qkv", qkv, _BF16, (Hq + 2 * Hkv) * D)
     T, dev = qkv.shape[0], qkv.device
     _tokens("positions", positions, T, dev)

@@ -68,19 +68,23 @@ struct RowT {
 // that the fp32 rounding of a scale derived from it is the one the plain
 // definition gives) and, when wanted, max |t|.  E is the element type of z and
 // w; t is exact in fp32 for bf16 (8 x 8 significand bits) and fp16 (11 x 11).
+// Each vector has its own accumulator, so the dependent chain of double fmas
+// is 8 long rather than 8 NV (the serial latency of a lone wave at decode
+// sizes).
 template <int NV, typename E = ElemBf16>
 __device__ __forceinline__ void row_prepare(const RowVecs<NV>& z, const RowVecs<NV>& w,
                                             bool want_max, RowT<NV>& t, double& ss, float& m) {
-  ss = 0.0;
+  double acc[NV];
   m = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
+    acc[i] = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float a = E::lo(z.v[i][k]), b = E::hi(z.v[i][k]);
       const double ad = static_cast<double>(a), bd = static_cast<double>(b);
-      ss = fma(ad, ad, ss);
-      ss = fma(bd, bd, ss);
+      acc[i] = fma(ad, ad, acc[i]);
+      acc[i] = fma(bd, bd, acc[i]);
       t.t[i][2 * k] = a * E::lo(w.v[i][k]);
       t.t[i][2 * k + 1] = b * E::hi(w.v[i][k]);
     }
@@ -89,6 +93,14 @@ __device__ __forceinline__ void row_prepare(const RowVecs<NV>& z, const RowVecs<
       for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t.t[i][j]));
     }
   }
+  ss = acc[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) ss += acc[i];
+}
+
+// rho = 1/sqrt(ss / H + eps) of a row, in double.
+__device__ __forceinline__ double row_rho(double ss, int H, float eps) {
+  return rsqrt_f64(ss / static_cast<double>(H) + static_cast<double>(eps));
 }
 
 // Combine the partials of the kW waves of a row: wave-level DPP reductions,
@@ -115,8 +127,8 @@ __device__ __forceinline__ void row_reduce(double& ss, float& m, double* lds_ss,
   }
 }
 
-// The row's output from its statistics:
-//   y = t * rho,  rho = 1/sqrt(ss / H + eps)
+// The row's output from rho = 1/sqrt(ss / H + eps):
+//   y = t * rho
 // mode NONE writes y rounded to the element type E to out (uint16_t*); the
 // quantizing modes (E = bf16 inputs only) write
 // e4m3fn(y / s) to out (uint8_t*) and s to scale_row (row lane 0 for a
@@ -126,11 +138,10 @@ __device__ __forceinline__ void row_reduce(double& ss, float& m, double* lds_ss,
 // rounds them as the exact quotient would).  kMode and kGroup (64 or 128 for
 // per-group scales, else 0) are compile-time, so group indexing is a shift.
 template <int NV, int kMode, int kGroup, bool kFull, typename E = ElemBf16>
-__device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float m_row,
-                                             float eps, int H, int nvec, int rl, int stride,
-                                             float static_scale, void* out, float* scale_row) {
+__device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double rho, float m_row,
+                                             int nvec, int rl, int stride, float static_scale,
+                                             void* out, float* scale_row) {
   static_assert(kMode != RRA_Q_PER_GROUP || kGroup == 64 || kGroup == 128, "group size");
-  const double rho = rsqrt_f64(ss / static_cast<double>(H) + static_cast<double>(eps));
   const int lane = lane_id();
 
   if constexpr (kMode == RRA_Q_NONE) {
@@ -158,6 +169,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
   }
 
   uint8_t* o = static_cast<uint8_t*>(out);
+  const double rho448 = rho_448(rho);
   if constexpr (kMode == RRA_Q_PER_GROUP) {
     constexpr int kLanesPerGroup = kGroup / 8;
 #pragma unroll
@@ -167,7 +179,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t.t[i][j]));
       m = kGroup == 128 ? max16(m) : max8(m);
-      const QuantStep qs = quant_step(rho, dynamic_scale(m, rho));
+      const QuantStep qs = quant_step(rho, dynamic_scale(m, rho448));
       if (kFull || idx < nvec) {
         if ((lane & (kLanesPerGroup - 1)) == 0) scale_row[idx / kLanesPerGroup] = qs.s;
         st_stream(o + idx * 8, quant8<false>(t.t[i], qs));
@@ -177,7 +189,7 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double ss, float
   }
 
   if constexpr (kMode == RRA_Q_PER_TOKEN) {
-    const QuantStep qs = quant_step(rho, dynamic_scale(m_row, rho));
+    const QuantStep qs = quant_step(rho, dynamic_scale(m_row, rho448));
     if (rl == 0) scale_row[0] = qs.s;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -249,18 +261,18 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   row_prepare<NV, E>(a, w, kMode == RRA_Q_PER_TOKEN, t, ss, m);
   row_reduce<kW>(ss, m, lds_ss, lds_m, (wave / kW) * kW, wave_in_row);
   if (!active) return;
+  const double rho = row_rho(ss, H, eps);
 
   if constexpr (kMode == RRA_Q_NONE) {
     uint16_t* o = static_cast<uint16_t*>(out) + row * out_stride;
-    rmsnorm_emit<NV, RRA_Q_NONE, 0, kFull, E>(t, ss, m, eps, H, nvec, rl, kStride, 0.0f, o,
-                                              nullptr);
+    rmsnorm_emit<NV, RRA_Q_NONE, 0, kFull, E>(t, rho, m, nvec, rl, kStride, 0.0f, o, nullptr);
     for (int idx = nvec + rl; idx < (H_pad >> 3); idx += kStride)
       st_stream(o + idx * 8, u32x4{0u, 0u, 0u, 0u});
   } else {
     float* scale_row = nullptr;
     if (kMode == RRA_Q_PER_TOKEN) scale_row = scales + row;
     if (kMode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / kGroup);
-    rmsnorm_emit<NV, kMode, kGroup, kFull>(t, ss, m, eps, H, nvec, rl, kStride, sscale,
+    rmsnorm_emit<NV, kMode, kGroup, kFull>(t, rho, m, nvec, rl, kStride, sscale,
                                            static_cast<uint8_t*>(out) + row * out_stride,
                                            scale_row);
   }
@@ -300,8 +312,13 @@ __global__ void __launch_bounds__(kBlock)
 // per workgroup; waves past T leave at once).  Measured on MI355X at the
 // DeepSeek-V3 shape, this beats spreading a token over 2 or 4 waves at every
 // T from 512 to 16384: the rows are short, and a barrier per token costs more
-// than the extra vectors per lane.  The row count, both rows and the q weight
-// lead the argument list, so they are among the preloaded arguments.
+// than the extra vectors per lane.  The two rows share their statistics work:
+// one paired reduction leaves q's sum of squares in lane 31 and kv's in lane
+// 63, and one vector pass takes both mean squares and both rsqrts (each lane
+// with its half's width and epsilon).  The row count, both rows and the q
+// weight lead the argument list, so they are among the preloaded arguments;
+// 1/Hq and 1/Hkv (double) come last and are used only when the widths are not
+// the compile-time ones of kFull.
 template <int NVQ, int NVKV, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
     dual_rmsnorm_quant_kernel(int64_t T, int Hq, int Hkv, const uint16_t* __restrict__ q,
@@ -310,18 +327,15 @@ __global__ void __launch_bounds__(kBlock)
                               const uint16_t* __restrict__ kv_w, float eps_q, float eps_kv,
                               void* __restrict__ q_out, int64_t q_out_stride,
                               float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
-                              int64_t kv_out_stride) {
+                              int64_t kv_out_stride, double inv_hq, double inv_hkv) {
   const int rl = lane_id();
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
   if (row >= T) return;
   const int nq = Hq >> 3, nkv = Hkv >> 3;
 
-  // Issue every load of the token before either reduction, kv's first: its
-  // whole norm (reduction, rsqrt and bf16 output) then runs while q's loads
-  // are still in flight, and its short row leaves the registers before q's
-  // quantization needs them (at the DeepSeek-V3 shape this keeps the kernel
-  // within 64 VGPRs, i.e. 8 waves per SIMD, so 8192 one-wave tokens are
-  // resident at once).
+  // Every load of the token is issued before either row is touched, kv's
+  // first (in-order returns then let kv's products start while q's vectors
+  // are still in flight).
   RowVecs<NVQ> zq, wq;
   RowVecs<NVKV> zkv, wkv;
   load_row<NVKV, true, kFull>(zkv, kv + row * kv_stride, nkv, rl, kWave, true);
@@ -330,20 +344,35 @@ __global__ void __launch_bounds__(kBlock)
   load_row<NVQ, false, kFull>(wq, q_w, nq, rl, kWave, true);
 
   RowT<NVKV> tkv;
-  double ss_kv;
-  float m_kv;
-  row_prepare(zkv, wkv, false, tkv, ss_kv, m_kv);
-  ss_kv = wave_sum_f64(ss_kv);
-  rmsnorm_emit<NVKV, RRA_Q_NONE, 0, kFull>(tkv, ss_kv, 0.0f, eps_kv, Hkv, nkv, rl, kWave, 0.0f,
-                                           kv_out + row * kv_out_stride, nullptr);
-
   RowT<NVQ> tq;
-  double ss_q;
-  float m_q;
+  double ss_kv, ss_q;
+  float m_kv, m_q;
+  row_prepare(zkv, wkv, false, tkv, ss_kv, m_kv);
   row_prepare(zq, wq, kMode == RRA_Q_PER_TOKEN, tq, ss_q, m_q);
-  ss_q = wave_sum_f64(ss_q);
+
+  // Lanes 0-31 finish with q's row, lanes 32-63 with kv's.  ms = ss / H is
+  // taken correctly rounded: the product with the rounded reciprocal of H,
+  // corrected once by its residual ss - ms0 * H, which an fma gives exactly
+  // (Markstein's final division step).  An infinite ss (an infinite value in
+  // the row) keeps ms = inf, hence rho = 0.
+  const double ss = pair_sum_f64(ss_q, ss_kv);
+  const bool kv_half = rl >= 32;
+  double h, r;
+  if constexpr (kFull) {
+    h = kv_half ? NVKV * 512.0 : NVQ * 512.0;
+    r = kv_half ? 1.0 / (NVKV * 512.0) : 1.0 / (NVQ * 512.0);
+  } else {
+    h = static_cast<double>(kv_half ? Hkv : Hq);
+    r = kv_half ? inv_hkv : inv_hq;
+  }
+  const double ms0 = ss * r;
+  const double ms = __builtin_isfinite(ms0) ? fma(fma(-ms0, h, ss), r, ms0) : ms0;
+  const double rho = rsqrt_f64(ms + static_cast<double>(kv_half ? eps_kv : eps_q));
+  const double rho_q = readlane_f64(rho, 31), rho_kv = readlane_f64(rho, 63);
   if (kMode == RRA_Q_PER_TOKEN) m_q = wave_max(m_q);
 
+  rmsnorm_emit<NVKV, RRA_Q_NONE, 0, kFull>(tkv, rho_kv, 0.0f, nkv, rl, kWave, 0.0f,
+                                           kv_out + row * kv_out_stride, nullptr);
   void* qo;
   float* scale_row = nullptr;
   if constexpr (kMode == RRA_Q_NONE) {
@@ -352,8 +381,7 @@ __global__ void __launch_bounds__(kBlock)
     qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
     scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
   }
-  rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, ss_q, m_q, eps_q, Hq, nq, rl, kWave, 0.0f, qo,
-                                          scale_row);
+  rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, rho_q, m_q, nq, rl, kWave, 0.0f, qo, scale_row);
 }
 
 // Waves per row for the residual-add norm: enough that each lane holds at
@@ -475,7 +503,8 @@ static void launch_dual(const DualLaunch& a) {
   hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, kMode, kGroup, kFull>), a.grid,
                      dim3(kBlock), 0,
                      a.st, a.T, a.Hq, a.Hkv, a.q, a.qs, a.kv, a.kvs, a.qw, a.kvw, a.eps_q,
-                     a.eps_kv, a.q_out, a.qos, a.q_scales, a.kv_out, a.kvos);
+                     a.eps_kv, a.q_out, a.qos, a.q_scales, a.kv_out, a.kvos,
+                     1.0 / static_cast<double>(a.Hq), 1.0 / static_cast<double>(a.Hkv));
 }
 
 template <int A, int B, bool kFull>

@@ -343,23 +343,31 @@ __global__ void __launch_bounds__(kBlock)
       ss = group_sum<kUnitsPerHead>(ss);  // all lanes: groups are q-, k-, v-only or idle
       const float ms = ss * inv_d + eps;
       float rho = __builtin_amdgcn_rsqf(ms);
-      // A head whose mean square (plus eps) is below 2^-100 (eps ~ 0 and
-      // values below about 1e-15, whose squares lose bits or flush in fp32)
-      // is normalized from x * 2^100 instead, with rho * 2^-100 folded into
-      // x * rho.  The branch is wave-uniform, so every lane of each group
-      // takes part in the second reduction.
-      const bool tiny = (is_q || is_k) && !(ms >= 0x1p-100f);
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(tiny) != 0, 0)) {
+      // A head whose mean square (plus eps) lies outside [2^-100, 2^100) is
+      // normalized from rescaled values, with the inverse scale folded into
+      // x * rho:
+      //  - below 2^-100 (eps ~ 0 and values below about 1e-15, whose squares
+      //    lose bits or flush in fp32), from x * 2^100, with eps * 2^200
+      //    (finite: eps is then below 2^-100 itself);
+      //  - from 2^100 up, where the fp32 sum of squares may overflow (values
+      //    above about 1e18 for D = 128, which would give rho = 0 and zero
+      //    outputs), from x * 2^-100, with eps * 2^-200, which flushes to 0
+      //    against a mean square of at least 2^-100 there.
+      // The branch is wave-uniform, so every lane of each group takes part in
+      // the second reduction.
+      const bool rescale = (is_q || is_k) && !(ms >= 0x1p-100f && ms < 0x1p100f);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(rescale) != 0, 0)) {
+        const float sc = ms < 1.0f ? 0x1p100f : 0x1p-100f;
         float ss2 = 0.0f;
-        if (tiny) {
+        if (rescale) {
 #pragma unroll
           for (int e = 0; e < kVals; ++e) {
-            x[e] *= 0x1p100f;
+            x[e] *= sc;
             ss2 = fmaf(x[e], x[e], ss2);
           }
         }
         ss2 = group_sum<kUnitsPerHead>(ss2);
-        if (tiny) rho = __builtin_amdgcn_rsqf(ss2 * inv_d + (eps * 0x1p100f) * 0x1p100f);
+        if (rescale) rho = __builtin_amdgcn_rsqf(ss2 * inv_d + (eps * sc) * sc);
       }
       if (is_q || is_k) {
         float w[16];
@@ -633,6 +641,8 @@ extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, in
     RRA_REQUIRE(aligned(key_cache, 16) && aligned(value_cache, 16), RRA_ERR_ALIGN);
     RRA_REQUIRE(aligned(slot_mapping, 8), RRA_ERR_ALIGN);
   }
+  // Without a cache, k's result has only qkv to go to.
+  RRA_REQUIRE(with_cache || write_k, RRA_ERR_UNSUPPORTED);
   RRA_REQUIRE(D == 64 || D == 128 || D == 256, RRA_ERR_UNSUPPORTED);
   RRA_REQUIRE(rot_dim == D && (is_neox == 0 || is_neox == 1), RRA_ERR_UNSUPPORTED);
   RRA_REQUIRE(vec_ok(qkv, qkv_stride) && aligned(q_weight, 16) && aligned(k_weight, 16) &&

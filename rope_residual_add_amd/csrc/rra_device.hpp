@@ -148,23 +148,19 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // two bf16 values) often stand in a short ratio such as 3/8 that puts
 // 448 * t / m exactly on an e4m3 rounding midpoint, and only the tiny offset d
 // left by rounding s to fp32 decides the side.  An fp32 quotient cannot see d.
-// So each value is first rounded as v = fp32(t * f) with f ~ fp32(rho / s)
-// (within 3 fp32 ulps of q); where v lies within 8 ulps of a midpoint, or in
-// the e4m3 subnormal range, q = (t * rho) / s is recomputed in double (the
-// quotient correctly rounded) and narrowed to fp32 with round-to-odd, after
-// which the single hardware rounding to e4m3 is the correct rounding of q
-// (fp32 keeps 20 more fraction bits than e4m3; round-to-odd makes the double
-// rounding innocuous).
-
-// True when v (an fp32 estimate of q) may round differently from q: its 20
-// fraction bits below e4m3's three lie within [-8, +7] ulps of 0x80000 (one
-// half of the e4m3 quantum), or |v| is below 2^-6 (e4m3 subnormals, where the
-// quantum is fixed; zero included).  The first test is bits 4..19 of
-// bits + 8 - 0x80000 all zero, i.e. that value shifted left by 12 below 2^16:
-// one add-and-shift and one compare.
-__device__ __forceinline__ bool e4m3_near_tie(float v) {
-  return ((__float_as_uint(v) + (8u - 0x80000u)) << 12) < 0x10000u || fabsf(v) < 0x1p-6f;
-}
+// So each value is bracketed: v_dn = fp32(t * f_dn) and v_up = fp32(t * f_up)
+// with f_dn and f_up fp32 multipliers a little below and above rho / s, so
+// that q lies strictly between v_dn and v_up.  Rounding to e4m3 is monotone,
+// so where the two give the same code that code is e4m3fn(q).  Where they
+// differ a rounding midpoint lies within about 2^-20 of q (an exact tie, or a
+// near one, about 2.5e-4 of the codes at dynamic scales): q = (t * rho) / s is
+// then recomputed in double (the quotient correctly rounded) and narrowed to
+// fp32 with round-to-odd, after which the single hardware rounding to e4m3 is
+// the correct rounding of q (fp32 keeps 20 more fraction bits than e4m3;
+// round-to-odd makes the double rounding innocuous).  The bracket needs no
+// special case for e4m3 subnormals, zeros or saturation: it holds wherever
+// t * f is a normal fp32 number, and below that (|q| < 2^-126) every code is
+// a zero of t's sign on both sides.
 
 // double -> fp32 rounding to odd: truncate toward zero, set the last bit if
 // anything was discarded.
@@ -177,43 +173,50 @@ __device__ __forceinline__ float f32_round_odd(double q) {
   return __uint_as_float(b | 1u);
 }
 
-// A quantization step: codes e4m3fn(t * rho / s).  f = fp32(rho) * rcp(s)
-// drives the fast path; rho (double) and s the exact one.  A scale that is not
-// positive (s = 0 for an all-zero slice; NaN where rho is NaN, from a NaN or
-// infinite value in the row) becomes s = 0, and such a slice gets +0 codes.
-// Where rho / s leaves the fp32 range
-// (a row of values near the fp32 subnormal range, where rho or 448 / amax is
-// huge) or s is itself subnormal (whose hardware reciprocal is not accurate),
-// f is set to 0: every v is then 0, which e4m3_near_tie flags, so every value
-// takes the exact path.
+// A quantization step: codes e4m3fn(t * rho / s).  f = fp32(rho) * rcp(s) is
+// within 2.5 fp32 ulps (2^-21.6 relative) of rho / s, so f_dn = f (1 - 2^-20)
+// and f_up = f (1 + 2^-20), each rounded once more, lie below and above it by
+// more than 2^-21; after the final rounding of t * f (2^-24) the bracket still
+// holds.  A scale that is not positive (s = 0 for an all-zero slice; NaN where
+// rho is NaN, from a NaN or infinite value in the row) becomes s = 0, and such
+// a slice gets +0 codes.  Where rho / s leaves the normal fp32 range (a row of
+// values near the fp32 subnormal range, where rho or 448 / amax is huge) or s
+// is itself subnormal (whose hardware reciprocal is not accurate), the bracket
+// is made [0, inf]: the two codes then differ for every value (0 against NaN
+// or 448), so every value takes the exact path.
 struct QuantStep {
-  float f;
+  float f_dn;
+  float f_up;
   float s;
   double rho;
 };
 
 __device__ __forceinline__ QuantStep quant_step(double rho, float s) {
-  if (!(s > 0.0f)) return QuantStep{0.0f, 0.0f, rho};
+  if (!(s > 0.0f)) return QuantStep{0.0f, 0.0f, 0.0f, rho};
   const float f = static_cast<float>(rho) * __builtin_amdgcn_rcpf(s);
-  const bool in_range = f < 0x1p127f && s >= 0x1p-126f;  // false for inf / NaN f too
-  return QuantStep{in_range ? f : 0.0f, s, rho};
+  // false for an infinite or NaN f too
+  const bool in_range = f < 0x1p127f && f >= 0x1p-126f && s >= 0x1p-126f;
+  if (!in_range) return QuantStep{0.0f, __builtin_inff(), s, rho};
+  return QuantStep{f * (1.0f - 0x1p-20f), f * (1.0f + 0x1p-20f), s, rho};
 }
 
 // Eight codes e4m3fn(t[j] * rho / s).  kClamp = false when s is a dynamic
-// scale (|t * rho / s| <= 448 within rounding).
+// scale (|t * rho / s| <= 448 within rounding; the conversion rounds up to
+// 464 to 448 by itself).
 template <bool kClamp>
 __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
   if (!(qs.s > 0.0f)) return u32x2{0u, 0u};
-  float v[8];
-  bool near[8];
-  bool exact = false;
+  float lo[8], hi[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    v[j] = t[j] * qs.f;
-    near[j] = e4m3_near_tie(v[j]);
-    exact |= near[j];
+    lo[j] = t[j] * qs.f_dn;
+    hi[j] = t[j] * qs.f_up;
   }
-  if (exact) {
+  u32x2 c{pack_e4m3x4<kClamp>(lo[0], lo[1], lo[2], lo[3]),
+          pack_e4m3x4<kClamp>(lo[4], lo[5], lo[6], lo[7])};
+  const uint32_t d0 = c[0] ^ pack_e4m3x4<kClamp>(hi[0], hi[1], hi[2], hi[3]);
+  const uint32_t d1 = c[1] ^ pack_e4m3x4<kClamp>(hi[4], hi[5], hi[6], hi[7]);
+  if ((d0 | d1) != 0u) {
     // q = p / s for p = t * rho, correctly rounded: q0 = p * y with y the
     // rounded reciprocal of s, then one correction with the residual
     // p - q0 * s, which an fma gives exactly (Markstein's final division
@@ -225,15 +228,16 @@ __device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
     const double y = 1.0 / sd;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (near[j]) {
+      if ((((j < 4 ? d0 : d1) >> (8 * (j & 3))) & 0xFFu) != 0u) {
         const double p = static_cast<double>(t[j]) * qs.rho;
         const double q0 = p * y;
-        v[j] = copysignf(f32_round_odd(fma(fma(-q0, sd, p), y, q0)), t[j]);
+        lo[j] = copysignf(f32_round_odd(fma(fma(-q0, sd, p), y, q0)), t[j]);
       }
     }
+    c = u32x2{pack_e4m3x4<kClamp>(lo[0], lo[1], lo[2], lo[3]),
+              pack_e4m3x4<kClamp>(lo[4], lo[5], lo[6], lo[7])};
   }
-  return u32x2{pack_e4m3x4<kClamp>(v[0], v[1], v[2], v[3]),
-               pack_e4m3x4<kClamp>(v[4], v[5], v[6], v[7])};
+  return c;
 }
 
 // ---- wavefront reductions ---------------------------------------------------
@@ -341,6 +345,42 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
+// Sums of two rows' doubles at once, one value per lane of each: a (lanes
+// 0-63) and b (lanes 0-63).  v_permlane32_swap exchanges the upper half of a
+// with the lower half of b, so that one add leaves a's half sums in lanes
+// 0-31 and b's in lanes 32-63; five DPP steps then finish each half (the last
+// adds row 0 into row 1 and row 2 into row 3).  Lane 31 ends with the sum of
+// a, lane 63 with the sum of b; other lanes hold partial sums.  Half the DPP
+// work of two whole-wave reductions, in a fixed order.
+__device__ __forceinline__ double pair_sum_f64(double a, double b) {
+  const uint64_t ua = static_cast<uint64_t>(__double_as_longlong(a));
+  const uint64_t ub = static_cast<uint64_t>(__double_as_longlong(b));
+  const auto lo = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(ua),
+                                                   static_cast<uint32_t>(ub), false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(ua >> 32),
+                                                   static_cast<uint32_t>(ub >> 32), false, false);
+  const double x = __longlong_as_double(
+      static_cast<long long>((static_cast<uint64_t>(hi[0]) << 32) | lo[0]));
+  const double y = __longlong_as_double(
+      static_cast<long long>((static_cast<uint64_t>(hi[1]) << 32) | lo[1]));
+  double v = x + y;
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  v += dpp_f64<0x142, 0xA>(v);
+  return v;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(u & 0xFFFFFFFFu), lane));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
 // Max over the whole wave (inputs >= 0); wave-uniform result.
 __device__ __forceinline__ float wave_max(float v) {
   uint32_t u = __float_as_uint(max16(v));
@@ -357,12 +397,15 @@ __device__ __forceinline__ int wave_id() {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 // Dynamic scale from an amax given as m * rho (m >= 0 exact in fp32, rho in
-// double): s = fp32(m * rho / 448), 448 being e4m3fn's largest finite value.
-// Multiplying by the double nearest 1/448 instead of dividing changes the
-// double intermediate by at most an ulp, which moves the fp32 result only if
-// it lies within 2^-52 of an fp32 rounding boundary.
-__device__ __forceinline__ float dynamic_scale(float m, double rho) {
-  return static_cast<float>(static_cast<double>(m) * rho * (1.0 / 448.0));
+// double): s = fp32(m * rho / 448), 448 being e4m3fn's largest finite value,
+// computed as m * rho448 with rho448 = rho * (1/448) formed once per row.  The
+// double product then differs from m * rho / 448 by at most two ulps, which
+// moves the fp32 result only if it lies within 2^-51 of an fp32 rounding
+// boundary.
+__device__ __forceinline__ double rho_448(double rho) { return rho * (1.0 / 448.0); }
+
+__device__ __forceinline__ float dynamic_scale(float m, double rho448) {
+  return static_cast<float>(static_cast<double>(m) * rho448);
 }
 
 // 1/sqrt(x) in double for x > 0: the hardware estimate refined by two Newton

@@ -20,7 +20,7 @@
 // against 5 bytes of traffic per output element at 8 TB/s), and the loop
 // already needs most of them.  A correctly rounded expf and fp32 divide would
 // use more than that, so silu uses the hardware exp2 and reciprocal:
-// silu(g) * u = g * u * rcp(1 + exp2(-g * log2(e))), relative error ~1e-6,
+// silu(g) * u = (g * rcp(1 + exp2(-g * log2(e)))) * u, relative error ~1e-6,
 // which moves an FP8 code only for values within that distance of a rounding
 // midpoint.
 #include "rra_device.hpp"
@@ -28,9 +28,12 @@
 
 namespace rra {
 
+// silu(g) is formed before the product with u, so that a large u cannot
+// meet an overflowed g * u (g = -100, u = 4e36: -inf * 0 = NaN, where
+// silu(g) * u is about -1.5e-5).
 __device__ __forceinline__ float silu_mul(float g, float u) {
   const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
-  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 __device__ __forceinline__ void silu8(u32x4 g, u32x4 u, float a[8]) {
@@ -41,15 +44,16 @@ __device__ __forceinline__ void silu8(u32x4 g, u32x4 u, float a[8]) {
   }
 }
 
-// The per-group path for a group of tiny activations, in double: a = g / (1 +
-// exp(-g)) * u from the bf16 inputs, s = fp32(max |a| / 448), and each code's
-// quotient a / s narrowed to fp32 with round-to-odd before the one rounding to
-// e4m3 (as the exact path of the norms).  Called by every lane of a group when
-// its fp32 amax is below 2^-100 (NaN activations do not count towards it); a
-// group with no nonzero product g * u keeps s = 0 and gets +0 codes, as any
-// slice whose scale is 0.
+// The per-group path for a group whose activations leave the range of the
+// fp32 path, in double: a = g / (1 + exp(-g)) * u from the bf16 inputs,
+// s = fp32(max |a| / 448) (infinite where that exceeds fp32, as it rounds),
+// and each code's quotient a / s narrowed to fp32 with round-to-odd before the
+// one rounding to e4m3 (as the exact path of the norms).  Called by every lane
+// of a group when its fp32 amax is below 2^-100 or infinite (NaN activations
+// do not count towards it); a group with no nonzero product g * u keeps s = 0
+// and gets +0 codes, as any slice whose scale is 0.
 template <int kGroup>
-__device__ __forceinline__ void tiny_group(u32x4 gv, u32x4 uv, float& s, float v[8]) {
+__device__ __forceinline__ void double_group(u32x4 gv, u32x4 uv, float& s, float v[8]) {
   double a[8];
   bool nonzero = false;
 #pragma unroll
@@ -126,9 +130,12 @@ __global__ void __launch_bounds__(kBlock)
     for (int j = 0; j < 8; ++j) v[j] = a[j] * f;
     // A group whose activations are all below 2^-100 (gates below about -88,
     // where exp overflows and the fp32 silu flushes to 0, or values near the
-    // fp32 subnormal range) is redone in double from the bf16 inputs, unless
-    // every product g * u is exactly 0 (an all-zero group needs nothing).
-    if (__builtin_expect(!(m >= 0x1p-100f), 0)) tiny_group<kGroup>(gv, uv, s, v);
+    // fp32 subnormal range), or whose largest one overflows fp32 (|silu(g) u|
+    // above 3.4e38, or an infinite input), is redone in double from the bf16
+    // inputs, unless every product g * u is exactly 0 (an all-zero group needs
+    // nothing).
+    if (__builtin_expect(!(m >= 0x1p-100f && m < __builtin_inff()), 0))
+      double_group<kGroup>(gv, uv, s, v);
     if (in_row) {
       if ((lane & (kLanesPerGroup - 1)) == 0)
         scales[static_cast<int64_t>(row) * (I / kGroup) + idx / kLanesPerGroup] = s;

@@ -18,8 +18,27 @@ def code_index(c) -> np.ndarray:
     return np.where(c & 0x80, -mag, mag)
 
 
+# Distance given to a position where exactly one side is a NaN code: no
+# finite number of ULPs, so it fails every bar.
+NAN_MISMATCH = 1 << 10
+
+
+def is_nan_code(c) -> np.ndarray:
+    """e4m3fn NaN codes (0x7F and 0xFF; the format has no infinities)."""
+    return (np.asarray(c, dtype=np.uint8) & 0x7F) == 0x7F
+
+
 def code_ulp_diff(a, b) -> np.ndarray:
-    return np.abs(code_index(a) - code_index(b))
+    """Distance in ULPs between e4m3fn codes, position by position.
+
+    Two NaN codes are equal (whatever their sign bits); a NaN against any
+    finite code counts as NAN_MISMATCH, so a NaN where the other side has
+    +-448 is never taken for the neighbouring code.  Finite codes are compared
+    by their positions on the value line (+0 and -0 both 0)."""
+    na, nb = is_nan_code(a), is_nan_code(b)
+    d = np.abs(code_index(a) - code_index(b))
+    d = np.where(na & nb, 0, d)
+    return np.where(na ^ nb, NAN_MISMATCH, d)
 
 
 def bf16_to_f64(h) -> np.ndarray:

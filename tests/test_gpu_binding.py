@@ -74,6 +74,8 @@ def test_rope_family_refuses_mismatched_tensors(rra):
     with pytest.raises(ValueError):
         rra.qk_norm_rope_kv_write(pos, qkv, w, w, 1e-6, cs, Hq, Hkv, D,
                                   slot_mapping=_t(2, dtype="i64"), key_cache=kc, value_cache=vc)
+    with pytest.raises(rra.RRAError):  # no cache and k not written back: k would be dropped
+        rra.qk_norm_rope_kv_write(pos, qkv, w, w, 1e-6, cs, Hq, Hkv, D, write_k=False)
     mq = _t(T, 8 * 192)
     with pytest.raises(ValueError):  # k_pe with fewer tokens than q
         rra.mla_rope_kv_write(pos, mq, _t(T - 1, 64), _t(T, 512), cs, slots,

@@ -8,7 +8,9 @@ the kernels take their double-precision paths:
     the fp32 activation flushes to zero), whose products g * u fall in the
     fp32 subnormal range, or that are all zero;
   * -0.0 inputs, whose code is 0x80 (e4m3fn keeps the sign of zero);
-  * QK-norm heads whose mean square is below 2^-100 with eps = 0.
+  * QK-norm heads whose mean square is below 2^-100 with eps = 0, or at or
+    above 2^100 (where an fp32 sum of squares overflows);
+  * SiLU groups whose products g * u exceed the fp32 range.
 Bars as in the other parity tests (codes within one code on at most 1e-4 of
 them, scales rtol 1e-2, bf16 within rtol 1e-2)."""
 import numpy as np
@@ -132,6 +134,38 @@ def test_silu_extreme_groups(rra, oracle):
         assert (scales[:, 0:3] > 0).all() and (scales[:, 3] == 0).all()
 
 
+def test_silu_products_beyond_fp32(rra, oracle):
+    """Per-group SiLU where silu(g) * u exceeds fp32 (gates near 100, up values
+    scaled by 2^120, and gates near -100 with huge up values, whose fp32
+    product g * u would overflow before the sigmoid takes it back), plus one
+    group whose amax / 448 exceeds fp32 (infinite scale, +-0 codes)."""
+    import torch
+
+    rng = np.random.default_rng(17)
+    for G in (64, 128):
+        say(f"[extreme] silu products beyond fp32 g={G}")
+        T, I = 16, 4 * G
+        g = (2.0 * rng.standard_normal((T, I))).astype(np.float32)
+        u = rng.standard_normal((T, I)).astype(np.float32)
+        g[:, :G] += 100.0
+        u[:, :G] *= np.float32(2.0 ** 120)
+        g[:, G:2 * G] -= 100.0
+        u[:, G:2 * G] = rng.uniform(1e36, 3e38, (T, G)).astype(np.float32)
+        g[0, 2 * G:3 * G] = 3e38
+        u[0, 2 * G:3 * G] = 3e38
+        inp = np.concatenate([_bf16(g), _bf16(u)], axis=1)
+        out, sc = rra.silu_mul_quant(dev_bf16(inp), 3, G)
+        torch.cuda.synchronize()
+        ref, ref_scales = oracle.silu_mul_quant(inp, 3, G)
+        codes, scales = host_u8(out), host_f32(sc)
+        assert np.isinf(ref_scales[0, 2]) and np.isinf(scales[0, 2])
+        assert_codes(codes, ref, f"silu beyond-fp32 codes g={G}")
+        fin = np.isfinite(ref_scales)
+        assert (np.isfinite(scales) == fin).all()
+        assert_scales(np.where(fin, scales, 1.0), np.where(fin, ref_scales, 1.0),
+                      f"silu beyond-fp32 scales g={G}")
+
+
 @pytest.mark.parametrize("is_neox", [True, False])
 def test_qknorm_tiny_heads(rra, oracle, is_neox):
     """QK norm with eps = 0 on heads of magnitude 1e-39 (bf16 subnormals) to
@@ -162,6 +196,41 @@ def test_qknorm_tiny_heads(rra, oracle, is_neox):
     got = host_bf16(g)
     assert np.isfinite(bf16_to_f64(got[:, :heads * D])).all()
     assert_bf16(got[:, :heads * D], ref[:, :heads * D], "q and k, tiny heads")
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_qknorm_large_heads(rra, oracle, is_neox):
+    """QK norm (eps 1e-6) on heads of magnitude 1e18 to 1e37, among them 2^100,
+    mixed with ordinary heads in the same token: an fp32 sum of squares of such
+    a head overflows, so it is normalized from values scaled by 2^-100; the
+    others as usual (k written back).  No output may be zero or non-finite."""
+    import dataclasses
+
+    import torch
+
+    say(f"[extreme] qknorm large heads neox={is_neox}")
+    cfg = dataclasses.replace(workloads.QKNORM, eps=1e-6)
+    T, Hq, Hkv, D = 64, cfg.Hq, cfg.Hkv, cfg.D
+    d = workloads.qknorm_inputs(T, cfg, with_cache=False)
+    rng = np.random.default_rng(16)
+    mags = np.array([1e18, 1e20, 2.0 ** 100, 1e36, 1e37, 1.0, 1e-3])
+    heads = Hq + Hkv
+    x = rng.standard_normal((T, heads, D)) * mags[rng.integers(0, mags.size, (T, heads))][..., None]
+    qkv = d["qkv"].copy()
+    qkv[:, :heads * D] = _bf16(x.reshape(T, heads * D))
+    g = dev_bf16(qkv)
+    cs = rra.rope_cos_sin_cache(cfg.max_pos, D, cfg.theta)
+    rra.qk_norm_rope_kv_write(dev(d["positions"]), g, dev_bf16(d["q_w"]), dev_bf16(d["k_w"]),
+                              cfg.eps, cs, Hq, Hkv, D, write_k=True, is_neox=is_neox)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.qk_norm_rope_kv_write(d["positions"], qkv, d["q_w"], d["k_w"], cfg.eps,
+                                             cfg.theta, cfg.max_pos, Hq, Hkv, D, write_k=True,
+                                             is_neox=is_neox)
+    got = host_bf16(g)
+    vals = bf16_to_f64(got[:, :heads * D]).reshape(T, heads, D)
+    assert np.isfinite(vals).all()
+    assert (np.abs(vals).max(axis=-1) > 0.1).all(), "a normalized head came out (near) zero"
+    assert_bf16(got[:, :heads * D], ref[:, :heads * D], "q and k, large heads")
 
 
 # ---- non-finite inputs -------------------------------------------------------

@@ -191,7 +191,10 @@ def test_qk_norm_rope_validation(rra):
                                        a["nb"], a["neox"], None)
 
     assert f(T=0) == OK
-    assert f(pos=None, qkv=None, sm=None, kc=None, vc=None, T=0) == OK
+    assert f(pos=None, qkv=None, sm=None, kc=None, vc=None, wk=1, T=0) == OK
+    # without a cache, k's result has only qkv to go to: write_k = 0 is refused
+    assert f(sm=None, kc=None, vc=None, wk=0) == EUNSUP
+    assert f(sm=None, kc=None, vc=None, wk=0, T=0) == EUNSUP
     assert f(qw=None, T=0) == ENULL
     assert f(kc=None) == ENULL  # a slot mapping needs both caches
     assert f(s=4096) == ESHAPE  # narrower than (Hq + 2 Hkv) D

@@ -110,3 +110,31 @@ def test_non_finite_activations(oracle):
     assert (codes[0, 24:32] == 0x7E).all()
     static, _ = oracle.silu_mul_quant(inp, 1, 0, 0.05)
     assert static[0, 9] == 0x7E and (static[0, 2] & 0x7F) == 0x7F
+
+
+def test_products_beyond_fp32(oracle):
+    """Per-group SiLU where silu(g) * u exceeds the fp32 range: scaling every u
+    by 2^120 (exact in bf16 and in double) leaves every code unchanged and
+    scales every group scale by exactly 2^120, as long as the scale itself
+    stays finite in fp32; a group whose amax / 448 exceeds fp32 gets an
+    infinite scale and codes +-0 (finite / inf)."""
+    rng = np.random.default_rng(21)
+    G, I = 128, 512
+    g = (2.0 * rng.standard_normal((4, I))).astype(np.float32)
+    u = rng.standard_normal((4, I)).astype(np.float32)
+    g[:, :G] += 100.0  # silu(g) = g to double precision: products of a few hundred
+    base = np.concatenate([workloads.to_bf16_bits(g), workloads.to_bf16_bits(u)], axis=1)
+    big = np.concatenate([workloads.to_bf16_bits(g),
+                          workloads.to_bf16_bits(u * np.float32(2.0 ** 120))], axis=1)
+    c0, s0 = oracle.silu_mul_quant(base, 3, G)
+    c1, s1 = oracle.silu_mul_quant(big, 3, G)
+    assert np.abs(bf16_to_f64(big[:, I:]) * bf16_to_f64(big[:, :I])).max() > 3.5e38
+    assert np.array_equal(c0, c1)
+    assert np.array_equal(s1.astype(np.float64), s0.astype(np.float64) * 2.0 ** 120)
+    assert np.isfinite(s1).all()
+    huge = big.copy()
+    huge[0, :G] = workloads.to_bf16_bits(np.full(G, 3e38, np.float32))
+    huge[0, I:I + G] = workloads.to_bf16_bits(np.full(G, 3e38, np.float32))
+    c2, s2 = oracle.silu_mul_quant(huge, 3, G)
+    assert np.isinf(s2[0, 0]) and (c2[0, :G] == 0).all()
+    assert np.array_equal(c2[1:], c1[1:]) and np.array_equal(c2[0, G:], c1[0, G:])
