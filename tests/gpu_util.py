@@ -8,6 +8,8 @@ fp16 outputs within one fp16 unit of the oracle (plus 2^-20 absolute);
 integer and index work (which slots are written, bit copies) bit-exact."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -80,6 +82,7 @@ def assert_codes(gpu: np.ndarray, ref: np.ndarray, what: str) -> dict:
     bad = int(np.count_nonzero(d))
     stats = dict(what=what, codes=n, mismatches=bad, max_ulp=int(d.max()) if n else 0)
     print(stats, flush=True)
+    _record("codes", stats)
     assert stats["max_ulp"] <= 1, stats
     assert bad <= CODE_MISMATCH_BUDGET * n, stats
     return stats
@@ -90,7 +93,9 @@ def assert_scales(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
     ok = np.isclose(gpu.astype(np.float64), ref.astype(np.float64), rtol=RTOL, atol=0)
     assert ok.all(), (what, np.argwhere(~ok)[:5])
     exact = np.mean(gpu.view(np.uint32) == ref.view(np.uint32)) if gpu.size else 1.0
-    print(dict(what=what, scales=gpu.size, bit_exact_fraction=float(exact)), flush=True)
+    stats = dict(what=what, scales=gpu.size, bit_exact_fraction=float(exact))
+    print(stats, flush=True)
+    _record("scales", stats)
 
 
 def assert_bf16(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
@@ -99,7 +104,9 @@ def assert_bf16(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
     ok = np.isclose(g, r, rtol=RTOL, atol=ATOL_BF16)
     assert ok.all(), (what, np.argwhere(~ok)[:5], g[~ok][:5], r[~ok][:5])
     exact = float(np.mean(gpu == ref)) if gpu.size else 1.0
-    print(dict(what=what, values=gpu.size, bit_exact_fraction=exact), flush=True)
+    stats = dict(what=what, values=gpu.size, bit_exact_fraction=exact)
+    print(stats, flush=True)
+    _record("bf16", stats)
 
 
 # fp16 results: the kernels compute in fp32 and round once, the oracle in
@@ -121,17 +128,29 @@ def assert_f16(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
     ok = np.abs(g - r) <= _f16_ulp(r) + ATOL_F16
     assert ok.all(), (what, np.argwhere(~ok)[:5], g[~ok][:5], r[~ok][:5])
     exact = float(np.mean(gpu == ref)) if gpu.size else 1.0
-    print(dict(what=what, values=gpu.size, bit_exact_fraction=exact), flush=True)
+    stats = dict(what=what, values=gpu.size, bit_exact_fraction=exact)
+    print(stats, flush=True)
+    _record("f16", stats)
 
 
 def assert_elem(gpu: np.ndarray, ref: np.ndarray, what: str, dtype: str) -> None:
     (assert_f16 if dtype == "f16" else assert_bf16)(gpu, ref, what)
 
 
-def sample_rows(T: int, n: int = 256, seed: int = 0) -> np.ndarray:
-    """Sorted sample of row indices (always the first and last row)."""
-    if T <= n:
-        return np.arange(T)
-    rng = np.random.default_rng(seed)
-    idx = rng.choice(T, size=n - 2, replace=False)
-    return np.unique(np.concatenate([[0, T - 1], idx]))
+def compare_rows(T: int) -> np.ndarray:
+    """Row (token) indices compared element by element with the oracle: every
+    row, at every size the tests run (the oracle computes T = 16384 rows of any
+    kernel in a few seconds)."""
+    return np.arange(T)
+
+
+def _record(kind: str, stats: dict) -> None:
+    """Append one comparison's measured figures to the JSON-lines file named by
+    RRA_PARITY_LOG (when set), tagged with the running test, for the committed
+    parity summary (tests/parity_summary.py)."""
+    path = os.environ.get("RRA_PARITY_LOG")
+    if not path:
+        return
+    rec = dict(stats, kind=kind, test=os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0])
+    with open(path, "a", encoding="utf-8") as f:
+        f.write(json.dumps(rec) + "\n")

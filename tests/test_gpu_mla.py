@@ -5,14 +5,14 @@ Covers the DeepSeek-V3 shape (q latent 1536 with per-group-128 FP8 quant, kv
 latent 512 kept bf16, eps 1e-6 for both; T in {1, 1024, 8192, 16384}), the
 per-token and unquantized q variants, group 64, the two latents taken as
 views of one [T, 1536 + 576] projection (kv = the first 512 columns of the
-576-wide kv_a slice), distinct epsilons and T = 0.  Large T compares sampled
-rows with the oracle; the amax-448 rule is checked on every group."""
+576-wide kv_a slice), distinct epsilons and T = 0.  Every row is compared
+with the oracle at every T; the amax-448 rule is checked on every group."""
 import numpy as np
 import pytest
 
 import workloads
 from gpu_util import (assert_bf16, assert_codes, assert_scales, dev_bf16, host_bf16, host_f32,
-                      host_u8, require_gpu, sample_rows, say)
+                      host_u8, require_gpu, compare_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def run(rra, oracle, T, mode=3, g=128, eps_q=1e-6, eps_kv=1e-6, split_views=Fals
                                                      g if mode == 3 else 0)
     torch.cuda.synchronize()
 
-    rows = sample_rows(T)
+    rows = compare_rows(T)
     ref_q, ref_s, ref_kv = oracle.dual_rmsnorm_quant(d["q"][rows], d["q_w"], eps_q,
                                                      d["kv"][rows], d["kv_w"], eps_kv, mode,
                                                      g if mode == 3 else 0)

@@ -10,9 +10,9 @@ binary16; bar: one fp16 unit) and in the GPT-J pairing.
 
 Bars: rotated q and k within rtol 1e-2 (atol 1e-5) of the oracle; the set of
 written cache slots, their placement and the copied v bit-exact; every slot
-outside slot_mapping keeps its sentinel bit pattern.  At large T the oracle
-recomputes a sample of tokens; the placement, v copy and sentinel checks run
-on every slot."""
+outside slot_mapping keeps its sentinel bit pattern.  The oracle recomputes
+every token at every T; the placement, v copy and sentinel checks run on
+every slot."""
 import dataclasses
 
 import numpy as np
@@ -20,7 +20,7 @@ import pytest
 
 import workloads
 from gpu_util import (assert_bf16, assert_elem, dev, dev_bf16, dev_elem, host_bf16, host_f32,
-                      require_gpu, sample_rows, say)
+                      require_gpu, compare_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,8 +80,8 @@ def run(rra, oracle, T, cfg=workloads.ROPE, *, pad_every=0, inplace=True, fused_
     assert np.array_equal(gv[~written], v0[~written]), "value cache changed outside slot_mapping"
     assert np.array_equal(gv[slots[live]], d["v"][live]), "value cache != v at the token slots"
 
-    # sampled tokens: rotated q and k against the oracle
-    rows = sample_rows(T)
+    # every token: rotated q and k against the oracle
+    rows = compare_rows(T)
     if rows.size == 0:
         return
     ref_q, ref_kc, ref_vc = oracle.rope_kv_write(

@@ -2,14 +2,14 @@
 
 Covers the Llama-3-8B MLP workload (I = 14336, per-group 128, T in {1, 64,
 1024, 8192}), group 64, static scale, a tensor-parallel shard width, ragged
-widths, strided views and T = 0.  At T = 8192 the oracle checks sampled rows;
-the amax-448 rule is checked on every group."""
+widths, strided views and T = 0.  Every row is compared with the oracle at
+every T; the amax-448 rule is checked on every group."""
 import numpy as np
 import pytest
 
 import workloads
 from gpu_util import (assert_codes, assert_scales, dev_bf16, host_f32, host_u8, require_gpu,
-                      sample_rows, say)
+                      compare_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,7 @@ def run(rra, oracle, T, I, mode, g=128, static=0.05, strided=False):
     ss = torch.tensor([static], dtype=torch.float32, device="cuda") if mode == 1 else None
     out, scales = rra.silu_mul_quant(inp, mode, g if mode == 3 else 0, ss, out=out)
     torch.cuda.synchronize()
-    rows = sample_rows(T)
+    rows = compare_rows(T)
     ref_codes, ref_scales = oracle.silu_mul_quant(d["inp"][rows], mode, g if mode == 3 else 0,
                                                   static)
     assert_codes(host_u8(out)[rows], ref_codes, f"codes T={T} I={I}")
