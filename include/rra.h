@@ -60,7 +60,8 @@
 extern "C" {
 #endif
 
-#define RRA_ABI_VERSION 4
+/* 5: qk_norm_rope_kv_write refuses write_k = 0 without a cache. */
+#define RRA_ABI_VERSION 5
 
 enum rra_status {
   RRA_OK = 0,

@@ -207,8 +207,14 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double rho, floa
   }
 }
 
-// Residual add + RMSNorm + quant.  Workgroup = kBlock lanes = kWavesPerBlock /
-// kW rows; each row lane holds NV vectors of x, residual and weight.
+// Waves per workgroup of the residual-add norm: four (kWavesPerBlock / kW
+// rows per workgroup), or kW where a row spans more than four waves (the
+// decode-size launches, one vector per lane: 8 waves for H = 4096).
+constexpr int norm_block_waves(int kW) { return kW > kWavesPerBlock ? kW : kWavesPerBlock; }
+
+// Residual add + RMSNorm + quant.  Workgroup = norm_block_waves(kW) waves =
+// norm_block_waves(kW) / kW rows; each row lane holds NV vectors of x,
+// residual and weight.
 // kMode NONE writes the norm to out (uint16_t, element type E) and +0 to its
 // columns [H, H_pad) (the padding variant); the quantizing modes write FP8
 // codes (uint8_t) from bf16 inputs and take H_pad = H.
@@ -222,10 +228,11 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
                                                  void* __restrict__ out, int64_t out_stride,
                                                  float* __restrict__ scales, int64_t T, int H,
                                                  int H_pad) {
-  constexpr int kRowsPerBlock = kWavesPerBlock / kW;
+  constexpr int kBlockWaves = norm_block_waves(kW);
+  constexpr int kRowsPerBlock = kBlockWaves / kW;
   constexpr int kStride = kW * kWave;
-  __shared__ double lds_ss[kWavesPerBlock];
-  __shared__ float lds_m[kWavesPerBlock];
+  __shared__ double lds_ss[kBlockWaves];
+  __shared__ float lds_m[kBlockWaves];
   const int wave = wave_id();
   const int wave_in_row = wave % kW;
   const int rl = wave_in_row * kWave + lane_id();
@@ -281,7 +288,7 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
 // Two entry kernels over the same body, so that profiles tell the quantizing
 // op from the padding op.
 template <int NV, int kW, bool kResidual, int kMode, int kGroup, bool kFull>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(norm_block_waves(kW) * kWave)
     add_rmsnorm_quant_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                              uint16_t* __restrict__ residual, int64_t res_stride,
                              const uint16_t* __restrict__ weight, float eps,
@@ -294,7 +301,7 @@ __global__ void __launch_bounds__(kBlock)
 }
 
 template <int NV, int kW, bool kResidual, bool kFull, typename E>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(norm_block_waves(kW) * kWave)
     add_rmsnorm_pad_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                            uint16_t* __restrict__ residual, int64_t res_stride,
                            const uint16_t* __restrict__ weight, float eps,
@@ -384,6 +391,69 @@ __global__ void __launch_bounds__(kBlock)
   rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, rho_q, m_q, nq, rl, kWave, 0.0f, qo, scale_row);
 }
 
+// MLA dual RMSNorm at decode sizes: one token per workgroup of NVQ + NVKV
+// waves, each wave one 512-column vector of one row (waves 0 .. NVQ - 1 the q
+// latent, the rest kv), so a wave's dependent chain covers one vector instead
+// of the whole token.  Each wave reduces its partials with DPP; one LDS
+// exchange and one barrier give every wave its row's sum of squares (and, for
+// per-token scales, the q amax), combined in a fixed order.
+template <int NVQ, int NVKV, int kMode, int kGroup, bool kFull>
+__global__ void __launch_bounds__((NVQ + NVKV) * kWave)
+    dual_rmsnorm_split_kernel(int64_t T, int Hq, int Hkv, const uint16_t* __restrict__ q,
+                              int64_t q_stride, const uint16_t* __restrict__ kv,
+                              int64_t kv_stride, const uint16_t* __restrict__ q_w,
+                              const uint16_t* __restrict__ kv_w, float eps_q, float eps_kv,
+                              void* __restrict__ q_out, int64_t q_out_stride,
+                              float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
+                              int64_t kv_out_stride) {
+  constexpr int kW = NVQ + NVKV;
+  __shared__ double lds_ss[kW];
+  __shared__ float lds_m[kW];
+  const int wave = wave_id(), lane = lane_id();
+  const int64_t row = blockIdx.x;  // the grid has exactly T workgroups
+  const bool is_q = wave < NVQ;    // wave-uniform
+  const int rl = (is_q ? wave : wave - NVQ) * kWave + lane;  // this lane's vector of its row
+  const int nvec = is_q ? (Hq >> 3) : (Hkv >> 3);
+
+  RowVecs<1> z, w;
+  load_row<1, true, kFull>(z, is_q ? q + row * q_stride : kv + row * kv_stride, nvec, rl, kWave,
+                           true);
+  load_row<1, false, kFull>(w, is_q ? q_w : kv_w, nvec, rl, kWave, true);
+  RowT<1> t;
+  double ss;
+  float m;
+  row_prepare(z, w, kMode == RRA_Q_PER_TOKEN, t, ss, m);
+  ss = wave_sum_f64(ss);
+  if (kMode == RRA_Q_PER_TOKEN) m = wave_max(m);
+  if (lane == 0) {
+    lds_ss[wave] = ss;
+    lds_m[wave] = m;
+  }
+  __syncthreads();
+  const int first = is_q ? 0 : NVQ, count = is_q ? NVQ : NVKV;
+  ss = lds_ss[first];
+  m = lds_m[first];
+  for (int j = 1; j < count; ++j) {
+    ss += lds_ss[first + j];
+    m = fmaxf(m, lds_m[first + j]);
+  }
+  const double rho = row_rho(ss, is_q ? Hq : Hkv, is_q ? eps_q : eps_kv);
+  if (!is_q) {
+    rmsnorm_emit<1, RRA_Q_NONE, 0, kFull>(t, rho, 0.0f, nvec, rl, kWave, 0.0f,
+                                          kv_out + row * kv_out_stride, nullptr);
+    return;
+  }
+  void* qo;
+  float* scale_row = nullptr;
+  if constexpr (kMode == RRA_Q_NONE) {
+    qo = static_cast<uint16_t*>(q_out) + row * q_out_stride;
+  } else {
+    qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
+    scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
+  }
+  rmsnorm_emit<1, kMode, kGroup, kFull>(t, rho, m, nvec, rl, kWave, 0.0f, qo, scale_row);
+}
+
 // Waves per row for the residual-add norm: enough that each lane holds at
 // most two vectors of a row up to H = 4096 (four up to 8192).
 inline int norm_waves_per_row(int64_t H) { return H <= 1024 ? 1 : (H <= 2048 ? 2 : 4); }
@@ -409,14 +479,14 @@ struct NormLaunch {
 template <int N, int W, bool kResidual, bool kFull, int kMode, int kGroup>
 static void launch_norm_quant(const NormLaunch& a) {
   hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual, kMode, kGroup, kFull>), a.grid,
-                     dim3(kBlock), 0, a.st, a.x, a.xs, a.res, a.rs, a.w, a.eps, a.sscale,
+                     dim3(norm_block_waves(W) * kWave), 0, a.st, a.x, a.xs, a.res, a.rs, a.w, a.eps, a.sscale,
                      static_cast<uint8_t*>(a.out), a.os, a.scales, a.T, a.H);
 }
 
 template <int N, int W, bool kResidual, bool kFull, typename E>
 static void launch_norm_pad(const NormLaunch& a) {
-  hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, kFull, E>), a.grid, dim3(kBlock), 0,
-                     a.st,
+  hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, kFull, E>), a.grid,
+                     dim3(norm_block_waves(W) * kWave), 0, a.st,
                      a.x, a.xs, a.res, a.rs, a.w, a.eps, static_cast<uint16_t*>(a.out), a.os,
                      a.T, a.H, a.H_pad);
 }
@@ -452,15 +522,36 @@ static void launch_norm_case(const NormLaunch& a, int mode, int group, int dtype
     launch_norm_mode<N, W, kResidual, false>(a, mode, group, dtype);
 }
 
+// Up to this many rows, the residual-add norm runs one vector per lane (a row
+// over up to 16 waves, one row per workgroup), which shortens each wave's
+// chain of loads, double-precision statistics, scale and codes.  Above it,
+// rows of up to 4096 columns take four waves with two vectors per lane.
+// Measured on MI355X at H = 4096 (profiler medians, cold): the split shape is
+// 0.1-0.16 us faster at T = 32 ... 512, equal at 1024, 3% slower at 2048.
+constexpr int64_t kNormSplitMaxT = 512;
+
+// (vectors per lane, waves per row) for a launch of T rows of width H.
+inline void norm_shape(int64_t T, int64_t H, int& nv, int& kw) {
+  if (T <= kNormSplitMaxT) {
+    const int64_t need = ceil_div(H, 8 * kWave);  // waves at one vector per lane
+    kw = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+    nv = 1;
+  } else {
+    kw = norm_waves_per_row(H);
+    nv = static_cast<int>(ceil_div(H, 8 * kWave * kw));
+  }
+}
+
 template <bool kResidual>
 static int launch_add_rmsnorm(int64_t T, int H, int H_pad, hipStream_t st, const uint16_t* x,
                               int64_t xs, uint16_t* res, int64_t rs, const uint16_t* w, float eps,
                               int mode, int group, const float* sscale, void* out, int64_t os,
                               float* scales, int dtype) {
-  const int kw = norm_waves_per_row(H);
-  const int nv = static_cast<int>(ceil_div(H, 8 * kWave * kw));
-  RRA_REQUIRE(ceil_div(T, kWavesPerBlock / kw) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);  // grid.x
-  const NormLaunch a{dim3(static_cast<unsigned>(ceil_div(T, kWavesPerBlock / kw))),
+  int nv, kw;
+  norm_shape(T, H, nv, kw);
+  const int rows_per_block = norm_block_waves(kw) / kw;
+  RRA_REQUIRE(ceil_div(T, rows_per_block) <= 0x7FFFFFFF, RRA_ERR_UNSUPPORTED);  // grid.x
+  const NormLaunch a{dim3(static_cast<unsigned>(ceil_div(T, rows_per_block))),
                      st, x, xs, res, rs, w, eps, sscale, out, os, scales, T, H, H_pad};
 #define RRA_NORM_CASE(N, W)                                   \
   if (nv == N && kw == W) {                                   \
@@ -469,10 +560,14 @@ static int launch_add_rmsnorm(int64_t T, int H, int H_pad, hipStream_t st, const
   }
   RRA_NORM_CASE(1, 1)
   RRA_NORM_CASE(2, 1)
+  RRA_NORM_CASE(1, 2)
   RRA_NORM_CASE(2, 2)
+  RRA_NORM_CASE(1, 4)
   RRA_NORM_CASE(2, 4)
   RRA_NORM_CASE(3, 4)
   RRA_NORM_CASE(4, 4)
+  RRA_NORM_CASE(1, 8)
+  RRA_NORM_CASE(1, 16)
 #undef RRA_NORM_CASE
   return RRA_ERR_UNSUPPORTED;
 }
@@ -498,8 +593,22 @@ struct DualLaunch {
   int Hq, Hkv;
 };
 
+// Up to this many tokens the MLA norm runs one wave per 512-column vector
+// (dual_rmsnorm_split_kernel); above, one wave per token.  Measured on MI355X
+// at the DeepSeek-V3 shape (profiler medians, cold): the split is 0.5 us
+// (13-15%) faster at T = 32 ... 512 and 5% at 1024, equal at 2048, and 8-12%
+// slower from 4096 (four times the waves, a barrier per token).
+constexpr int64_t kDualSplitMaxT = 1024;
+
 template <int A, int B, bool kFull, int kMode, int kGroup>
 static void launch_dual(const DualLaunch& a) {
+  if (a.T <= kDualSplitMaxT) {
+    hipLaunchKernelGGL((dual_rmsnorm_split_kernel<A, B, kMode, kGroup, kFull>),
+                       dim3(static_cast<unsigned>(a.T)), dim3((A + B) * kWave), 0, a.st, a.T, a.Hq,
+                       a.Hkv, a.q, a.qs, a.kv, a.kvs, a.qw, a.kvw, a.eps_q, a.eps_kv, a.q_out,
+                       a.qos, a.q_scales, a.kv_out, a.kvos);
+    return;
+  }
   hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, kMode, kGroup, kFull>), a.grid,
                      dim3(kBlock), 0,
                      a.st, a.T, a.Hq, a.Hkv, a.q, a.qs, a.kv, a.kvs, a.qw, a.kvw, a.eps_q,

@@ -74,6 +74,22 @@ def test_modes(rra, oracle, mode, g):
     run(rra, oracle, 37, mode, g)
 
 
+# Up to 1024 tokens one wave per 512-column vector (four waves per token at
+# the DeepSeek-V3 shape), above that one wave per token: both sides of the
+# switch in every mode, and ragged widths on both paths.
+@pytest.mark.parametrize("T", [1023, 1024, 1025])
+@pytest.mark.parametrize("mode,g", [(0, 0), (2, 0), (3, 128), (3, 64)])
+def test_decode_shape_switch(rra, oracle, T, mode, g):
+    run(rra, oracle, T, mode, g)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(1024, 512), (2048, 1024), (1000, 520), (512, 8)])
+def test_decode_shape_widths(rra, oracle, Hq, Hkv):
+    mode, g = (3, 64) if Hq % 64 == 0 else (2, 0)
+    run(rra, oracle, 9, mode, g, Hq=Hq, Hkv=Hkv)
+    run(rra, oracle, 1100, mode, g, Hq=Hq, Hkv=Hkv)
+
+
 def test_split_views(rra, oracle):
     run(rra, oracle, 21, split_views=True)
 

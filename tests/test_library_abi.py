@@ -54,7 +54,7 @@ def test_library_exports_every_declared_function(rra):
 
 
 def test_version_and_status_strings(rra):
-    assert rra.abi_version() == rra.ABI_VERSION == 4
+    assert rra.abi_version() == rra.ABI_VERSION == 5
     for s in (OK, ENULL, ESHAPE, EALIGN, EUNSUP, -5):
         assert rra.status_string(s) and rra.status_string(s) != "unknown status"
     assert rra.status_string(-99) == "unknown status"
