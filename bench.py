@@ -18,10 +18,15 @@ launch).  Per-kernel durations come from HIP events (created without a system
 fence) recorded on the stream the kernels run on, around every launch of the
 timed region.
 
-Prints ONE JSON line on stdout (everything else goes to stderr).  With
---sweep it also times each kernel alone at several token counts, rotating
-over enough buffer sets that every launch reads cold data, and adds the table
-under "sweep".
+Prints ONE JSON line on stdout (everything else goes to stderr).  Beside the
+step it reports, each timed alone and cold (rotating buffer sets) next to a
+streaming copy of the same bytes: the next-row kernels ("next_rows"), the
+other quantization modes ("modes": static and per-group-128 norm, static
+SiLU), and the fusion's effect ("fusion": fused against unfused bytes, and the
+MLA norm's two-launch form timed against its one launch).  "target" lists the
+kernels at or below 75% of peak HBM bandwidth; "cpu_baseline" times the
+oracle.  With --sweep it also times each kernel alone at several token counts
+and adds the table under "sweep".
 """
 from __future__ import annotations
 
@@ -36,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+TARGET_FRAC = 0.75  # the bar: each kernel at >= 75% of peak HBM bandwidth
 METRIC = "achieved HBM GB/s (% of MI355X peak) and tokens/s per fused kernel, T=8192"
 
 
@@ -91,28 +97,103 @@ BYTES_PER_LAUNCH.update({
 NEXT_KERNELS = ("qk_norm_rope_kv_write", "fused_add_rmsnorm_pad", "mla_rope_kv_write",
                 "rope_kv_write_f16", "fused_add_rmsnorm_pad_f16")
 
+# The other quantization modes the pages list, timed beside the step (not part
+# of it): the residual-add norm with a static scale at the small config's width
+# (H = 1024, eps 1e-6, scale 0.05) and with per-group-128 scales at the
+# Llama-3-8B width, and SiLU-and-Mul with a static scale.
+H_STATIC = 1024
+BYTES_PER_TOKEN.update({
+    "fused_add_rmsnorm_quant_static": 7 * H_STATIC,
+    "fused_add_rmsnorm_quant_g128": 7 * H_NORM + 4 * (H_NORM // G),
+    "silu_mul_quant_static": 5 * I_SILU,
+})
+BYTES_PER_LAUNCH.update({
+    "fused_add_rmsnorm_quant_static": 2 * H_STATIC + 4,
+    "fused_add_rmsnorm_quant_g128": 2 * H_NORM,
+    "silu_mul_quant_static": 4,
+})
+MODE_KERNELS = ("fused_add_rmsnorm_quant_static", "fused_add_rmsnorm_quant_g128",
+                "silu_mul_quant_static")
+
+# Bytes the unfused form of each pattern moves per token (the pages' "without
+# the fusion" pipelines, each step reading its inputs and writing its outputs):
+#   norm: fused_add_rms_norm (x, residual in; residual and a bf16 y out), then
+#         the quant (y in; codes and the scale out): 11H + 4;
+#   SiLU: silu_and_mul (gate|up in, bf16 activation out), then the quant: 9I + 4I/128;
+#   RoPE: rotary (q, k and the position in; q and k out), then the cache write
+#         (k, v and the slot in; both cache rows out);
+#   MLA norm: the same bytes as the fused op, in two launches.
+UNFUSED_BYTES_PER_TOKEN = {
+    "fused_add_rmsnorm_quant": 11 * H_NORM + 4,
+    "silu_mul_quant": 9 * I_SILU + 4 * (I_SILU // G),
+    "rope_kv_write": 2 * 2 * ROPE_HQ * ROPE_D + 2 * 2 * ROPE_HKV * ROPE_D + 8
+    + 2 * 2 * ROPE_HKV * ROPE_D + 2 * 2 * ROPE_HKV * ROPE_D + 8,
+    "dual_rmsnorm_quant": BYTES_PER_TOKEN["dual_rmsnorm_quant"],
+}
+
 
 def algo_bytes(name: str, T: int) -> int:
     return BYTES_PER_TOKEN[name] * T + BYTES_PER_LAUNCH[name]
 
 
 # Work-items per launch at T tokens, as the library launches these workloads
-# (256-lane workgroups): one row per workgroup for the residual-add norms (four
-# waves per row at widths above 2048), one wave per 512 SiLU outputs, one wave
-# per token for the MLA norm, and for the RoPE family as many waves per token
-# as its units need at one unit per lane (Llama-3-8B / Qwen3-8B attention: 48
-# heads x 8 two-vector units, six waves; DeepSeek-V3 MLA: 129 heads x 8
-# one-vector units + 64 kv_c vectors, eighteen).  Used only to tell the sweep's
-# launches apart in a kernel trace.
+# (used only to tell the sweep's launches apart in a kernel trace):
+#  - residual-add norms: up to 512 rows, one vector per lane and one row per
+#    workgroup of max(4, waves per row) waves (H = 4096: 8 waves; H = 1024: two
+#    rows of 2 waves); above, four waves per row at widths above 2048 (one
+#    workgroup per row), one wave per row up to 1024 (four rows per workgroup);
+#  - SiLU: one wave per 512 outputs;
+#  - MLA norm: up to 1024 tokens one workgroup of 4 waves per token (one wave
+#    per 512-column vector at 1536 / 512), above one wave per token;
+#  - the RoPE family: as many waves per token as its units need at one unit per
+#    lane (Llama-3-8B / Qwen3-8B attention: 48 heads x 8 two-vector units, six
+#    waves; DeepSeek-V3 MLA: 129 heads x 8 one-vector units + 64 kv_c vectors,
+#    eighteen).
+NORM_SPLIT_MAX_T, DUAL_SPLIT_MAX_T = 512, 1024
+
+
 def _rope_waves_per_token(units: int) -> int:
     ku = max(1, -(-units // 2048))
     return -(-(-(-units // ku)) // 64)
 
 
+def _norm_shape(T: int, H: int) -> tuple:
+    """(vectors per lane, waves per row) of the residual-add norms' launch."""
+    need = -(-H // 512)
+    if T <= NORM_SPLIT_MAX_T:
+        return 1, next(w for w in (1, 2, 4, 8, 16) if w >= need)
+    kw = 1 if H <= 1024 else (2 if H <= 2048 else 4)
+    return -(-H // (512 * kw)), kw
+
+
+def _norm_threads(T: int, H: int) -> int:
+    _, kw = _norm_shape(T, H)
+    block_waves = max(4, kw)
+    return 64 * block_waves * -(-T // (block_waves // kw))
+
+
+def launch_symbol(name: str, T: int):
+    """A fragment of the demangled symbol the library launches for the kernel
+    at T, where its launch shape depends on T (the decode-size shapes), so that
+    trace rows of equal grid size but different shape are told apart; None
+    where one symbol serves every T."""
+    if name == "dual_rmsnorm_quant":
+        return ("rra::dual_rmsnorm_split_kernel<" if T <= DUAL_SPLIT_MAX_T
+                else "rra::dual_rmsnorm_quant_kernel<")
+    H = {"fused_add_rmsnorm_quant": H_NORM, "fused_add_rmsnorm_quant_g128": H_NORM,
+         "fused_add_rmsnorm_quant_static": H_STATIC, "fused_add_rmsnorm_pad": PAD_H,
+         "fused_add_rmsnorm_pad_f16": PAD_H}.get(name)
+    if H is None:
+        return None
+    nv, kw = _norm_shape(T, H)
+    sym = "add_rmsnorm_pad_kernel" if "pad" in name else "add_rmsnorm_quant_kernel"
+    return f"rra::{sym}<{nv}, {kw}, "
+
+
 def grid_threads(name: str, T: int) -> int:
     import workloads
 
-    if name == "silu_mul_quant":
+    if name in ("silu_mul_quant", "silu_mul_quant_static"):
         waves = T * -(-I_SILU // 512)
     elif name in ("rope_kv_write", "rope_kv_write_f16"):
         cfg = workloads.ROPE
@@ -126,9 +207,13 @@ def grid_threads(name: str, T: int) -> int:
         per_head = cfg.rope_dim // 16 if cfg.is_neox else cfg.rope_dim // 8
         waves = T * _rope_waves_per_token((cfg.Hq + 1) * per_head + cfg.kv_lora // 8)
     elif name == "dual_rmsnorm_quant":
-        waves = T
+        return 256 * T if T <= DUAL_SPLIT_MAX_T else 256 * -(-T // 4)
+    elif name == "fused_add_rmsnorm_quant_static":
+        return _norm_threads(T, H_STATIC)
+    elif name in ("fused_add_rmsnorm_pad", "fused_add_rmsnorm_pad_f16"):
+        return _norm_threads(T, PAD_H)
     else:
-        waves = 4 * T
+        return _norm_threads(T, H_NORM)
     return 64 * 4 * -(-waves // 4)
 
 
@@ -140,23 +225,29 @@ def copy_half_bytes(nbytes_moved: int) -> int:
 # ---- kernel identity: symbols and sources ----------------------------------------
 
 CSRC = os.path.join(ROOT, "rope_residual_add_amd", "csrc")
-KERNEL_SYMBOL = {
-    "fused_add_rmsnorm_quant": "add_rmsnorm_quant_kernel",
-    "silu_mul_quant": "silu_mul_quant_kernel",
-    "rope_kv_write": "rope_kv_write_kernel",
-    "dual_rmsnorm_quant": "dual_rmsnorm_quant_kernel",
-    "qk_norm_rope_kv_write": "qk_norm_rope_kv_kernel",
-    "fused_add_rmsnorm_pad": "add_rmsnorm_pad_kernel",
-    "mla_rope_kv_write": "mla_rope_kv_kernel",
-    "rope_kv_write_f16": "rope_kv_write_kernel",
-    "fused_add_rmsnorm_pad_f16": "add_rmsnorm_pad_kernel",
+# The demangled kernel names of each measured kernel: symbol and the template
+# arguments that tell modes and element types apart (quant mode 1 static, 2
+# per token, 3 per group; rows of the MLA norm take its one-wave-per-token or
+# its decode-size kernel).
+KERNEL_NAME_RE = {
+    "fused_add_rmsnorm_quant": r"rra::add_rmsnorm_quant_kernel<\d+, \d+, true, 2, 0, \w+>",
+    "fused_add_rmsnorm_quant_static": r"rra::add_rmsnorm_quant_kernel<\d+, \d+, true, 1, 0, \w+>",
+    "fused_add_rmsnorm_quant_g128": r"rra::add_rmsnorm_quant_kernel<\d+, \d+, true, 3, 128, \w+>",
+    "silu_mul_quant": r"rra::silu_mul_quant_kernel<3, 128, \w+>",
+    "silu_mul_quant_static": r"rra::silu_mul_quant_kernel<1, 0, \w+>",
+    "rope_kv_write": r"rra::rope_kv_write_kernel<\d+, \w+, \d+, rra::ElemBf16>",
+    "rope_kv_write_f16": r"rra::rope_kv_write_kernel<\d+, \w+, \d+, rra::ElemF16>",
+    "dual_rmsnorm_quant": r"rra::dual_rmsnorm_(quant|split)_kernel<",
+    "qk_norm_rope_kv_write": r"rra::qk_norm_rope_kv_kernel<",
+    "fused_add_rmsnorm_pad": r"rra::add_rmsnorm_pad_kernel<\d+, \d+, true, \w+, rra::ElemBf16>",
+    "fused_add_rmsnorm_pad_f16": r"rra::add_rmsnorm_pad_kernel<\d+, \d+, true, \w+, rra::ElemF16>",
+    "mla_rope_kv_write": r"rra::mla_rope_kv_kernel<",
 }
-# Kernels that share a symbol with another and differ in a template argument:
-# the argument's text in the demangled name.  Names of the plain kernel must not
-# contain it.
-KERNEL_TAG = {"rope_kv_write_f16": "ElemF16", "fused_add_rmsnorm_pad_f16": "ElemF16"}
 KERNEL_SOURCES = {
     "fused_add_rmsnorm_quant": ("norm_quant.hip",),
+    "fused_add_rmsnorm_quant_static": ("norm_quant.hip",),
+    "fused_add_rmsnorm_quant_g128": ("norm_quant.hip",),
+    "silu_mul_quant_static": ("silu_mul_quant.hip",),
     "dual_rmsnorm_quant": ("norm_quant.hip",),
     "silu_mul_quant": ("silu_mul_quant.hip",),
     "rope_kv_write": ("rope_kv.hip",),
@@ -356,6 +447,32 @@ def make_launchers(T: int, salt: int = 0, shared=None, only=KERNELS):
             cfg.rope_dim, cfg.nope + cfg.rope_dim, cfg.nope, is_neox=cfg.is_neox)
         io["mla_rope_kv_write"] = dict(d, kv_cache=cache)
 
+    if "fused_add_rmsnorm_quant_static" in only:
+        d = workloads.device_norm_inputs(T, H_STATIC, dev, salt)
+        sc0 = torch.full((1,), 0.05, dtype=torch.float32, device=dev)
+        out = torch.empty((T, H_STATIC), dtype=torch.float8_e4m3fn, device=dev)
+        L["fused_add_rmsnorm_quant_static"] = lambda d=d, out=out, sc0=sc0: (
+            rra.fused_add_rmsnorm_quant(d["x"], d["residual"], d["weight"], 1e-6, rra.Q_STATIC,
+                                        0, sc0, out))
+        io["fused_add_rmsnorm_quant_static"] = dict(d, out=out, static_scale=sc0)
+
+    if "fused_add_rmsnorm_quant_g128" in only:
+        d = workloads.device_norm_inputs(T, H_NORM, dev, salt)
+        out = torch.empty((T, H_NORM), dtype=torch.float8_e4m3fn, device=dev)
+        sc = torch.empty((T, H_NORM // G), dtype=torch.float32, device=dev)
+        L["fused_add_rmsnorm_quant_g128"] = lambda d=d, out=out, sc=sc: (
+            rra.fused_add_rmsnorm_quant(d["x"], d["residual"], d["weight"], 1e-5,
+                                        rra.Q_PER_GROUP, G, None, out, sc))
+        io["fused_add_rmsnorm_quant_g128"] = dict(d, out=out, scales=sc)
+
+    if "silu_mul_quant_static" in only:
+        d = workloads.device_silu_inputs(T, I_SILU, dev, salt)
+        sc0 = torch.full((1,), 0.05, dtype=torch.float32, device=dev)
+        out = torch.empty((T, I_SILU), dtype=torch.float8_e4m3fn, device=dev)
+        L["silu_mul_quant_static"] = lambda d=d, out=out, sc0=sc0: rra.silu_mul_quant(
+            d["inp"], rra.Q_STATIC, 0, sc0, out)
+        io["silu_mul_quant_static"] = dict(d, out=out, static_scale=sc0)
+
     if "dual_rmsnorm_quant" in only:
         d = workloads.device_mla_inputs(T, workloads.MLA, dev, salt)
         qo = torch.empty((T, MLA_HQ), dtype=torch.float8_e4m3fn, device=dev)
@@ -547,6 +664,87 @@ def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS, with_copy: bool = T
     return rows
 
 
+def dual_two_launch(Ts, launches: int = 60) -> dict:
+    """The MLA norm as the pages' unfused form runs it, two launches (q: RMSNorm
+    + per-group-128 FP8 quant with fused_add_rmsnorm_quant and no residual; kv:
+    RMSNorm to bf16 with fused_add_rmsnorm_pad and no padding), against the
+    one-launch dual_rmsnorm_quant, at each T: median of event intervals around
+    the one launch or the pair, queued behind a spin kernel, cold (rotating
+    buffer sets of at least 1 GiB, at most 256).  Both forms move the same
+    bytes; the difference is the second launch."""
+    import torch
+
+    import rope_residual_add_amd as rra
+    import workloads
+
+    cyc = _blocker_cycles()
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for T in Ts:
+        b = algo_bytes("dual_rmsnorm_quant", T)
+        n_sets = max(2, min(256, -(-(1 << 30) // b)))
+        sets = []
+        for salt in range(n_sets):
+            d = workloads.device_mla_inputs(T, workloads.MLA, "cuda", salt)
+            sets.append((d, torch.empty((T, MLA_HQ), dtype=torch.float8_e4m3fn, device="cuda"),
+                         torch.empty((T, MLA_HQ // G), dtype=torch.float32, device="cuda"),
+                         torch.empty((T, MLA_HKV), dtype=torch.bfloat16, device="cuda")))
+
+        def one(d, qo, qs, kvo):
+            rra.dual_rmsnorm_quant(d["q"], d["q_w"], 1e-6, d["kv"], d["kv_w"], 1e-6,
+                                   rra.Q_PER_GROUP, G, qo, qs, kvo)
+
+        def two(d, qo, qs, kvo):
+            rra.fused_add_rmsnorm_quant(d["q"], None, d["q_w"], 1e-6, rra.Q_PER_GROUP, G, None,
+                                        qo, qs)
+            rra.fused_add_rmsnorm_pad(d["kv"], None, d["kv_w"], 1e-6, MLA_HKV, kvo)
+
+        # the two forms give the same outputs (scales can differ in the last bit
+        # only where a sum of squares is added in another order)
+        for f in (one, two):
+            for a in sets:
+                f(*a)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in sets[0][1:]]
+        two(*sets[0])
+        torch.cuda.synchronize()
+        same = dict(q_codes=int((ref[0].view(torch.uint8) != sets[0][1].view(torch.uint8))
+                                .sum().item()),
+                    q_scales=int((ref[1] != sets[0][2]).sum().item()),
+                    kv=int((ref[2].view(torch.int16) != sets[0][3].view(torch.int16)).sum().item()))
+        ms1 = _timed_launches(hip, stream, cyc, [lambda a=a: one(*a) for a in sets], launches)
+        ms2 = _timed_launches(hip, stream, cyc, [lambda a=a: two(*a) for a in sets], launches)
+        out[str(T)] = dict(one_launch_us=round(ms1 * 1e3, 2), two_launch_us=round(ms2 * 1e3, 2),
+                           saved_us=round((ms2 - ms1) * 1e3, 2), bytes=b,
+                           outputs_differing=same)
+        log(f"MLA norm T={T}: one launch {ms1 * 1e3:.2f} us, two launches {ms2 * 1e3:.2f} us "
+            f"(differing outputs {same})")
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
+def fusion_report(kern: dict, T: int, dual: dict) -> dict:
+    """Fused against unfused bytes per launch at T, with the unfused form's
+    time projected at the fused kernel's own measured bandwidth (the unfused
+    kernels are not part of this library), and the MLA norm's measured one- and
+    two-launch times."""
+    rep = {}
+    for k in ("fused_add_rmsnorm_quant", "silu_mul_quant", "rope_kv_write"):
+        fused = algo_bytes(k, T)
+        unfused = UNFUSED_BYTES_PER_TOKEN[k] * T + BYTES_PER_LAUNCH[k]
+        rep[k] = dict(fused_bytes=fused, unfused_bytes=unfused,
+                      unfused_over_fused=round(unfused / fused, 4), fused_us=kern[k]["us"],
+                      unfused_us_projected=round(kern[k]["us"] * unfused / fused, 2))
+    rep["dual_rmsnorm_quant"] = dict(fused_bytes=algo_bytes("dual_rmsnorm_quant", T),
+                                     unfused_bytes=algo_bytes("dual_rmsnorm_quant", T),
+                                     launches_measured=dual)
+    rep["note"] = ("unfused_us_projected = fused time x unfused/fused bytes (the fused kernel's "
+                   "own bandwidth); the MLA norm's two-launch form is measured")
+    return rep
+
+
 def environment() -> dict:
     """Versions and device facts recorded beside the numbers."""
     import platform
@@ -573,33 +771,51 @@ def environment() -> dict:
 
 # ---- CPU baseline: the oracle on a bounded sample --------------------------------
 
-def _oracle_calls(n: int) -> dict:
-    """{kernel: zero-argument oracle call} on n tokens of each kernel's workload."""
+def _oracle_call(name: str, n: int):
+    """Zero-argument oracle call on n tokens of a kernel's workload."""
     import oracle
     import workloads
 
-    cfg = workloads.ROPE
-    dn = workloads.norm_inputs(n, H_NORM)
-    ds = workloads.silu_inputs(n, I_SILU)
-    dr = workloads.rope_inputs(n, cfg)
-    dm = workloads.mla_inputs(n)
-    return {
-        "fused_add_rmsnorm_quant": lambda: oracle.fused_add_rmsnorm_quant(
-            dn["x"], dn["residual"], dn["weight"], 1e-5, oracle.Q_PER_TOKEN),
-        "silu_mul_quant": lambda: oracle.silu_mul_quant(ds["inp"], oracle.Q_PER_GROUP, G),
-        "rope_kv_write": lambda: oracle.rope_kv_write(
-            dr["positions"], dr["q"], dr["k"], dr["v"], cfg.theta, cfg.max_pos,
-            dr["slot_mapping"], dr["key_cache"], dr["value_cache"], cfg.Hq, cfg.Hkv, cfg.D),
-        "dual_rmsnorm_quant": lambda: oracle.dual_rmsnorm_quant(
-            dm["q"], dm["q_w"], 1e-6, dm["kv"], dm["kv_w"], 1e-6, oracle.Q_PER_GROUP, G),
-    }
+    if name in ("fused_add_rmsnorm_quant", "fused_add_rmsnorm_quant_g128"):
+        d = workloads.norm_inputs(n, H_NORM)
+        mode, g = ((oracle.Q_PER_TOKEN, 0) if name == "fused_add_rmsnorm_quant"
+                   else (oracle.Q_PER_GROUP, G))
+        return lambda: oracle.fused_add_rmsnorm_quant(d["x"], d["residual"], d["weight"], 1e-5,
+                                                      mode, g)
+    if name == "fused_add_rmsnorm_quant_static":
+        d = workloads.norm_inputs(n, H_STATIC)
+        return lambda: oracle.fused_add_rmsnorm_quant(d["x"], d["residual"], d["weight"], 1e-6,
+                                                      oracle.Q_STATIC, 0, 0.05)
+    if name in ("silu_mul_quant", "silu_mul_quant_static"):
+        d = workloads.silu_inputs(n, I_SILU)
+        if name == "silu_mul_quant":
+            return lambda: oracle.silu_mul_quant(d["inp"], oracle.Q_PER_GROUP, G)
+        return lambda: oracle.silu_mul_quant(d["inp"], oracle.Q_STATIC, 0, 0.05)
+    if name == "rope_kv_write":
+        cfg = workloads.ROPE
+        d = workloads.rope_inputs(n, cfg)
+        return lambda: oracle.rope_kv_write(
+            d["positions"], d["q"], d["k"], d["v"], cfg.theta, cfg.max_pos, d["slot_mapping"],
+            d["key_cache"], d["value_cache"], cfg.Hq, cfg.Hkv, cfg.D)
+    if name == "dual_rmsnorm_quant":
+        d = workloads.mla_inputs(n)
+        return lambda: oracle.dual_rmsnorm_quant(d["q"], d["q_w"], 1e-6, d["kv"], d["kv_w"], 1e-6,
+                                                 oracle.Q_PER_GROUP, G)
+    raise KeyError(name)
+
+
+# Each config's largest token count beside the step's T (the RoPE and MLA
+# configs go to 16384), and the other quantization modes at the step's T.
+ORACLE_LARGEST_T = {"rope_kv_write": 16384, "dual_rmsnorm_quant": 16384}
+ORACLE_REPS = 5
 
 
 def cpu_baseline(T: int, one_core_T: int = 1024) -> dict:
-    """The oracle as it stands, timed on the host's cores: all of them (up to
-    16) on the GPU step's own workload at T tokens, and one core on one_core_T
-    tokens.  Reported in GB/s of the same algorithmic bytes as the GPU, with
-    tokens/s per kernel."""
+    """The oracle as it stands, timed on the host's cores (up to 16): the GPU
+    step's own workload at T tokens, each config's largest T, and the other
+    quantization modes at T; plus one core on one_core_T tokens.  One warm-up,
+    then the median of five calls each.  Reported in GB/s of the same
+    algorithmic bytes as the GPU, with tokens/s per kernel."""
     import oracle
 
     try:
@@ -608,21 +824,23 @@ def cpu_baseline(T: int, one_core_T: int = 1024) -> dict:
         cores = os.cpu_count() or 1
     cores = max(1, min(cores, 16))
 
-    def timed(n, threads):
-        calls = _oracle_calls(n)
+    def timed(name, n, threads):
+        f = _oracle_call(name, n)
         oracle.set_threads(threads)
-        secs = {}
-        for name, f in calls.items():
-            f()  # warm-up
-            ts = []
-            for _ in range(3):
-                t0 = time.perf_counter()
-                f()
-                ts.append(time.perf_counter() - t0)
-            secs[name] = statistics.median(ts)
-            log(f"oracle {name:26s} T={n} {secs[name] * 1e3:8.1f} ms on {oracle.get_threads()} "
-                f"threads")
-        return secs, int(oracle.get_threads())
+        f()  # warm-up
+        ts = []
+        for _ in range(ORACLE_REPS):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        sec = statistics.median(ts)
+        log(f"oracle {name:32s} T={n:6d} {sec * 1e3:8.1f} ms on {oracle.get_threads()} threads")
+        return sec, int(oracle.get_threads())
+
+    def point(name, n, sec):
+        b = algo_bytes(name, n)
+        return dict(T=n, ms=round(sec * 1e3, 2), gbps=round(b / sec / 1e9, 4),
+                    tokens_per_s=round(n / sec, 1))
 
     def summary(n, secs):
         total_bytes = sum(algo_bytes(k, n) for k in KERNELS)
@@ -630,15 +848,22 @@ def cpu_baseline(T: int, one_core_T: int = 1024) -> dict:
                     per_kernel_ms={k: round(v * 1e3, 2) for k, v in secs.items()},
                     tokens_per_s={k: round(n / v, 1) for k, v in secs.items()})
 
-    one, _ = timed(one_core_T, 1)
-    secs, used = timed(T, cores)
+    one = {k: timed(k, one_core_T, 1)[0] for k in KERNELS}
+    secs, used = {}, 1
+    for k in KERNELS:
+        secs[k], used = timed(k, T, cores)
     out = summary(T, secs)
     out.update(cores=used, kind="oracle",
                sample=f"the GPU step's workload, T={T} tokens of each of the four kernels; "
-                      f"fp64 C oracle, OpenMP over rows, median of 3 calls after one warm-up; "
-                      f"bytes counted as for the GPU; one_core: T={one_core_T} on one thread. "
-                      f"The RoPE oracle returns fresh copies of both 128 MiB caches on every "
-                      f"call, which is a large part of its time")
+                      f"fp64 C oracle, OpenMP over rows, median of {ORACLE_REPS} calls after "
+                      f"one warm-up; bytes counted as for the GPU; largest_T: the RoPE and MLA "
+                      f"configs at T=16384; modes: the other quantization modes at T={T}; "
+                      f"one_core: T={one_core_T} on one thread. The RoPE oracle returns fresh "
+                      f"copies of both 128 MiB caches on every call, which is a large part of "
+                      f"its time")
+    out["largest_T"] = {k: point(k, n, timed(k, n, cores)[0])
+                        for k, n in ORACLE_LARGEST_T.items()}
+    out["modes"] = {k: point(k, T, timed(k, T, cores)[0]) for k in MODE_KERNELS}
     out["one_core"] = dict(summary(one_core_T, one), T=one_core_T)
     return out
 
@@ -646,34 +871,44 @@ def cpu_baseline(T: int, one_core_T: int = 1024) -> dict:
 # ---- profile summaries (rocprofv3 CSV -> profiles/*.md) ----------------------------
 
 def _kernel_of(symbol_name: str):
-    tags = set(KERNEL_TAG.values())
-    for k, sym in KERNEL_SYMBOL.items():
-        if f"rra::{sym}<" not in symbol_name and f"rra::{sym}(" not in symbol_name:
-            continue
-        tag = KERNEL_TAG.get(k)
-        if tag is not None and tag in symbol_name:
-            return k
-        if tag is None and not any(t in symbol_name for t in tags):
+    """The measured kernel a demangled kernel name belongs to, or None."""
+    import re
+
+    for k, pat in KERNEL_NAME_RE.items():
+        if re.search(pat, symbol_name):
             return k
     return None
 
 
+def _launch_of(symbol_name: str, grid_items: int, T: int):
+    """The measured kernel a dispatch belongs to when it ran that kernel's
+    workload at T tokens (its grid has grid_threads(kernel, T) work-items), or
+    None.  Other launches of the same symbol (the MLA norm's decode-size
+    timings, a different T) are left out."""
+    k = _kernel_of(symbol_name)
+    if k is None or grid_items != grid_threads(k, T):
+        return None
+    frag = launch_symbol(k, T)
+    return k if frag is None or frag in symbol_name else None
+
+
 def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=None) -> None:
-    """Kernel-trace summary: per-kernel average duration and GB/s (and p10 /
-    median / p90 from the per-dispatch trace next to the stats file); with
-    bench_json (the JSON line the traced run printed), the run's own
-    event-timed average per kernel beside the profiler's."""
+    """Kernel-trace summary of a traced bench run: per kernel, the profiler's
+    durations of its launches at T (average, min, max, p10 / median / p90, from
+    the per-dispatch trace next to the stats file, launches told apart by grid
+    size) and GB/s; with bench_json (the JSON line the traced run printed), the
+    run's own event-timed average per kernel beside the profiler's."""
     import collections
     import csv
 
-    # per-dispatch durations from the kernel trace beside the stats file, if present
     per = collections.defaultdict(list)
+    sym = {}
     trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
-    if trace_csv != stats_csv and os.path.exists(trace_csv):
-        for r in csv.DictReader(open(trace_csv)):
-            k = _kernel_of(r["Kernel_Name"])
-            if k is not None:
-                per[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    for r in csv.DictReader(open(trace_csv)):
+        k = _launch_of(r["Kernel_Name"], int(r["Grid_Size_X"]), T)
+        if k is not None and k in KERNELS:
+            per[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            sym[k] = r["Kernel_Name"].split("(")[0].replace("void ", "")
     events = {}
     if bench_json:
         line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
@@ -682,27 +917,25 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=N
     lines = [f"# Kernel trace: the four fused kernels at T={T}", "",
              "Produced by (from the repository root, after `cd /tmp && export TMPDIR=/tmp` for "
              "the profiler):", "", "```", command, "```", "",
-             "Durations are the profiler's kernel times (AverageNs etc. of "
-             "`--stats` kernel_stats.csv). GB/s = algorithmic bytes per launch / average.", "",
+             "Durations are the profiler's kernel times of every launch of each kernel at "
+             f"T={T} in the traced run (the step, and for the MLA norm also the one-launch side "
+             "of the bench's two-launch comparison; launches told apart by grid size). "
+             "GB/s = algorithmic bytes per launch / average.", "",
              "| kernel | symbol | calls | avg us | min us | max us | p10 / median / p90 us | "
              "algorithmic bytes | GB/s (avg) | % of 8 TB/s |"
              + (" bench.py events avg us |" if events else ""),
              "|---|---|---|---|---|---|---|---|---|---|" + ("---|" if events else "")]
-    for r in csv.DictReader(open(stats_csv)):
-        k = _kernel_of(r["Name"])
-        if k is None or k not in KERNELS:
+    for k in KERNELS:
+        d = per.get(k)
+        if not d:
             continue
-        avg, mn, mx = (float(r[c]) for c in ("AverageNs", "MinNs", "MaxNs"))
+        avg = statistics.fmean(d)
         b = algo_bytes(k, T)
         gbps = b / avg
-        sym = r["Name"].split("(")[0].replace("void ", "")
-        pct = "-"
-        if per.get(k):
-            q = statistics.quantiles(per[k], n=10)
-            pct = f"{q[0] / 1e3:.2f} / {statistics.median(per[k]) / 1e3:.2f} / {q[-1] / 1e3:.2f}"
-        lines.append(f"| {k} | `{sym}` | {r['Calls']} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
-                     f"{mx / 1e3:.2f} | {pct} | {b} | {gbps:.0f} | "
-                     f"{100 * gbps / PEAK_HBM_GBPS:.1f}% |"
+        q = statistics.quantiles(d, n=10) if len(d) > 1 else [avg, avg]
+        lines.append(f"| {k} | `{sym[k]}` | {len(d)} | {avg / 1e3:.2f} | {min(d) / 1e3:.2f} | "
+                     f"{max(d) / 1e3:.2f} | {q[0] / 1e3:.2f} / {statistics.median(d) / 1e3:.2f} / "
+                     f"{q[-1] / 1e3:.2f} | {b} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f}% |"
                      + (f" {events[k]:.2f} |" if events else ""))
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -718,12 +951,17 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out: str, commands: str, T
     def load(path, counter):
         d = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] == counter:
-                d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            if "rra::stream_copy_kernel" in name:
+                d[name].append(float(r["Counter_Value"]))
+            elif _launch_of(name, int(r["Grid_Size"]), T) is not None:
+                d[name, "at T"].append(float(r["Counter_Value"]))
         return d
 
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
-    copy = [n for n in fetch if "rra::stream_copy_kernel" in n]
+    copy = [n for n in fetch if isinstance(n, str) and "rra::stream_copy_kernel" in n]
     if not copy:
         raise SystemExit("no streaming copy in the counter run")
     gib_kib = float(1 << 20)
@@ -742,7 +980,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out: str, commands: str, T
              "| kernel | source | FETCH_SIZE KiB | WRITE_SIZE KiB | launches | traffic bytes | "
              "algorithmic bytes | traffic / algorithmic |", "|---|---|---|---|---|---|---|---|"]
     for k in KERNELS + NEXT_KERNELS:
-        names = [n for n in fetch if _kernel_of(n) == k]
+        names = [n for n in fetch if isinstance(n, tuple) and _kernel_of(n[0]) == k]
         if not names:
             continue
         fv = [v for n in names for v in fetch[n]]
@@ -752,6 +990,62 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out: str, commands: str, T
         b = algo_bytes(k, T)
         lines.append(f"| {k} | `{source_hash(k)}` | {fk:.0f} | {wk:.0f} | {len(fv)} | {traffic} | "
                      f"{b} | {traffic / b:.4f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+WAVE_COUNTERS = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY",
+                 "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU")
+
+
+def summarize_waves(counter_csv: str, out: str, command: str, T: int) -> None:
+    """Per-wave instruction and cycle counters (one rocprofv3 --pmc pass of the
+    eight SQ counters in WAVE_COUNTERS) per kernel at T: VALU instructions per
+    wave, and how a wave's cycles split between waiting on data or
+    dependencies (SQ_WAIT_ANY), waiting for an issue slot (SQ_WAIT_INST_ANY)
+    and issuing (SQ_ACTIVE_INST_ANY); the VALU time per SIMD is instructions x
+    4 cycles (a wave64 instruction on a 16-lane SIMD) x waves / 1024 SIMDs at
+    2.4 GHz.  `source` hashes the kernel's code as in the traffic summary."""
+    import collections
+    import csv
+
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(counter_csv)):
+        name = r["Kernel_Name"]
+        k = ("copy (1 vector per lane)" if "rra::stream_copy_kernel<1>" in name
+             else _launch_of(name, int(r["Grid_Size"]), T))
+        if k is None:
+            continue
+        vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"# Per-wave counters at T={T} (rocprofv3 --pmc, SQ block)", "",
+             "Produced by (from the repository root, after `cd /tmp && export TMPDIR=/tmp` for "
+             "the profiler):", "", "```", command, "```", "",
+             f"Medians over the run's launches of each kernel at T={T} (told apart by grid "
+             "size). Cycles per wave: `waiting on data` "
+             "= SQ_WAIT_ANY (waiting on memory or a dependency), `waiting for issue` = "
+             "SQ_WAIT_INST_ANY, `issuing` = SQ_ACTIVE_INST_ANY. VALU time per SIMD = VALU per "
+             "wave x 4 cycles x waves / 1024 SIMDs / 2.4 GHz. `source` is the hash of the "
+             "kernel's code (comments and layout excluded) when the counters were taken.", "",
+             "| kernel | source | launches | waves | VALU / wave | VALU time per SIMD us | "
+             "wave cycles | waiting on data | waiting for issue | issuing |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    order = [k for k in KERNELS + MODE_KERNELS + NEXT_KERNELS if k in vals]
+    order += [k for k in vals if k not in order]
+    for k in order:
+        c = vals[k]
+        if not c.get("SQ_WAVES"):
+            continue
+        m = {n: statistics.median(v) for n, v in c.items()}
+        w = m["SQ_WAVES"]
+        per = {n: m.get(n, 0.0) / w for n in WAVE_COUNTERS}
+        cyc = per["SQ_WAVE_CYCLES"] or 1.0
+        valu_us = per["SQ_INSTS_VALU"] * 4 * w / 1024 / 2.4e3
+        src = f"`{source_hash(k)}`" if k in KERNEL_SOURCES else "-"
+        lines.append(
+            f"| {k} | {src} | {len(c['SQ_WAVES'])} | {w:.0f} | {per['SQ_INSTS_VALU']:.0f} | "
+            f"{valu_us:.1f} | {cyc:.0f} | {per['SQ_WAIT_ANY']:.0f} "
+            f"({100 * per['SQ_WAIT_ANY'] / cyc:.0f}%) | {per['SQ_WAIT_INST_ANY']:.0f} "
+            f"({100 * per['SQ_WAIT_INST_ANY'] / cyc:.0f}%) | {per['SQ_ACTIVE_INST_ANY']:.0f} |")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -766,13 +1060,16 @@ def summarize_sweep(trace_csv: str, out: str, command: str, Ts, kernels=KERNELS)
     import re
 
     dur = collections.defaultdict(list)  # (kernel or ("copy", V), grid work-items) -> ns
+    launches = collections.defaultdict(list)  # (kernel, grid) -> [(symbol, ns)]
     for r in csv.DictReader(open(trace_csv)):
         name = r["Kernel_Name"]
         m = re.search(r"rra::stream_copy_kernel<(\d+)>", name)
         k = ("copy", int(m.group(1))) if m else _kernel_of(name)
         if k is None:
             continue
-        dur[(k, int(r["Grid_Size_X"]))].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        dur[(k, int(r["Grid_Size_X"]))].append(ns)
+        launches[(k, int(r["Grid_Size_X"]))].append((name, ns))
 
     def copy_best(nbytes_moved):
         """(median ns, vectors per lane) of the fastest copy of that size."""
@@ -797,7 +1094,9 @@ def summarize_sweep(trace_csv: str, out: str, command: str, Ts, kernels=KERNELS)
              "% of copy |", "|---|---|---|---|---|---|---|---|---|"]
     for T in Ts:
         for k in kernels:
-            d = dur.get((k, grid_threads(k, T)))
+            frag = launch_symbol(k, T)
+            d = [ns for name, ns in launches.get((k, grid_threads(k, T)), ())
+                 if frag is None or frag in name]
             if not d:
                 continue
             med = statistics.median(d)
@@ -837,6 +1136,12 @@ def main() -> int:
                                                 "per-kernel cold-cache sweep")
     ap.add_argument("--next-rows", type=int, default=1,
                     help="1 = also time the next-row kernels alone at T (cold, rotating sets)")
+    ap.add_argument("--modes", type=int, default=1,
+                    help="1 = also time the other quantization modes alone at T (static and "
+                         "per-group-128 norm, static SiLU)")
+    ap.add_argument("--fusion", type=int, default=1,
+                    help="1 = also report fused against unfused bytes and time the MLA norm's "
+                         "two-launch form against its one launch")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="write a profiles/ summary from a rocprofv3 --stats run and exit")
     ap.add_argument("--sweep-kernels", default=",".join(KERNELS),
@@ -848,6 +1153,9 @@ def main() -> int:
                     help="write a profiles/ summary of a traced --sweep-only run and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write a profiles/ summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-waves", metavar="COUNTER_CSV",
+                    help="write a profiles/ summary of a rocprofv3 --pmc run of the SQ wave "
+                         "counters and exit")
     ap.add_argument("--out", help="output file for --summarize-*")
     ap.add_argument("--bench-json", help="with --summarize-trace: the traced run's JSON output")
     ap.add_argument("--command", default="", help="command line recorded in the summary")
@@ -858,6 +1166,9 @@ def main() -> int:
         return 0
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.out, args.command, args.T)
+        return 0
+    if args.summarize_waves:
+        summarize_waves(args.summarize_waves, args.out, args.command, args.T)
         return 0
     if args.summarize_sweep:
         summarize_sweep(args.summarize_sweep, args.out, args.command,
@@ -895,11 +1206,15 @@ def main() -> int:
         ms = statistics.fmean(per[n])
         b = algo_bytes(n, T)
         gbps = b / (ms * 1e-3) / 1e9
+        q = statistics.quantiles(per[n], n=10) if len(per[n]) > 1 else [ms, ms]
+        frac = gbps / PEAK_HBM_GBPS
         kern[n] = dict(us=round(ms * 1e3, 2), us_median=round(statistics.median(per[n]) * 1e3, 2),
-                       bytes=b, gbps=round(gbps, 1), frac_of_peak=round(gbps / PEAK_HBM_GBPS, 4),
-                       tokens_per_s=round(T / (ms * 1e-3), 1))
+                       us_p10=round(q[0] * 1e3, 2), us_p90=round(q[-1] * 1e3, 2),
+                       bytes=b, gbps=round(gbps, 1), frac_of_peak=round(frac, 4),
+                       meets_target=frac >= TARGET_FRAC, tokens_per_s=round(T / (ms * 1e-3), 1))
         log(f"{n:26s} {ms * 1e3:9.2f} us  {gbps:8.1f} GB/s  "
-            f"{100 * gbps / PEAK_HBM_GBPS:5.1f}% of 8 TB/s  {T / (ms * 1e-3):.3e} tokens/s")
+            f"{100 * frac:5.1f}% of 8 TB/s  {T / (ms * 1e-3):.3e} tokens/s  "
+            f"{'meets' if frac >= TARGET_FRAC else 'misses'} the {100 * TARGET_FRAC:.0f}% target")
 
     step_bytes = sum(algo_bytes(n, T) for n in KERNELS)
     ms_per_step = wall / args.steps * 1e3
@@ -920,6 +1235,10 @@ def main() -> int:
                     T=T, io="bf16 in; e4m3fn codes + fp32 scales / bf16 out; fp32 arithmetic",
                     step_bytes=step_bytes),
         kernels=kern, roofline=roofline, env=environment(),
+        target=dict(frac_of_peak=TARGET_FRAC,
+                    met=[n for n in KERNELS if kern[n]["meets_target"]],
+                    missed=[n for n in KERNELS if not kern[n]["meets_target"]],
+                    timing="HIP events around each launch of the timed steps (mean)"),
     )
     ceiling = copy_ceiling()
     for n in KERNELS:
@@ -928,6 +1247,11 @@ def main() -> int:
     if args.next_rows:
         result["next_rows"] = {r["kernel"]: {k: v for k, v in r.items() if k != "kernel"}
                                for r in sweep([T], kernels=NEXT_KERNELS)}
+    if args.modes:
+        result["modes"] = {r["kernel"]: {k: v for k, v in r.items() if k != "kernel"}
+                           for r in sweep([T], kernels=MODE_KERNELS)}
+    if args.fusion:
+        result["fusion"] = fusion_report(kern, T, dual_two_launch(sorted({64, 1024, T})))
     if args.sweep:
         result["sweep"] = sweep([int(t) for t in args.sweep.split(",") if t],
                                 kernels=_sweep_kernels(args))
