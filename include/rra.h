@@ -48,8 +48,10 @@
  *   rho NaN (or 0) and every value of the row NaN or +-0, so each dynamic
  *   scale of that row is 0 and its codes are +0; any slice whose scale comes
  *   out 0 gets +0 codes; NaN activations (SiLU) are left out of their group's
- *   amax and code as NaN; a static scale saturates infinities to +-448 and
- *   keeps NaN.  The sign bit of a NaN result is unspecified.
+ *   amax and code as NaN; an infinite activation makes its group's scale
+ *   infinite and the group's finite values code as +-0; a static scale
+ *   saturates infinities to +-448 and keeps NaN.  The sign bit of a NaN
+ *   result is unspecified.
  */
 #ifndef RRA_H
 #define RRA_H
@@ -133,6 +135,11 @@ int fused_add_rmsnorm_quant(const uint16_t* x, int64_t x_stride, uint16_t* resid
  * with s = *static_scale (RRA_Q_STATIC) or one scale per group of group_size
  * columns, s = fp32(amax/448), written to scales[t * (I / group_size) + k]
  * (RRA_Q_PER_GROUP).
+ *
+ * Activations whose magnitude exceeds the fp32 range (silu(g) * u beyond
+ * ~3.4e38, which bf16 inputs allow) are finite values: a group holding one is
+ * taken in double, and its scale is the fp32 rounding of amax/448 (infinite
+ * where that exceeds fp32, so that the group's codes are +-0).
  *
  * in     [T, 2I] bf16 (gate half, then up half), row stride in_stride.
  * out    [T, I] e4m3fn, row stride out_stride.
@@ -229,8 +236,10 @@ int dual_rmsnorm_quant(const uint16_t* q, int64_t q_stride, const uint16_t* q_we
  *
  *   q_h <- rope(q_h / sqrt(mean(q_h^2) + eps) * q_weight)   for every q head
  *   k_h  = rope(k_h / sqrt(mean(k_h^2) + eps) * k_weight)   for every k head
- * computed in fp32 and rounded once to bf16.  q is overwritten in place in
- * qkv.  With slot_mapping != NULL, token t with s = slot_mapping[t] >= 0
+ * computed in fp32 and rounded once to bf16, for heads of any finite
+ * magnitude (a head whose fp32 mean square falls outside [2^-100, 2^100) is
+ * normalized from values rescaled by 2^100 or 2^-100).  q is overwritten in
+ * place in qkv.  With slot_mapping != NULL, token t with s = slot_mapping[t] >= 0
  * writes k_h and the unchanged v_h to key_cache / value_cache[s / block_size,
  * s % block_size, h, :] (layout and slot rules as rope_kv_write).  write_k = 1
  * also writes k_h back into qkv, for every token, with or without a slot.
