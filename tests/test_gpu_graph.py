@@ -21,14 +21,15 @@ def rra():
     return r
 
 
-def test_graph_replays_match_eager(rra):
+# T = 96 runs the norms' decode-size launch shapes, T = 1100 their wider ones.
+@pytest.mark.parametrize("T,num_blocks", [(96, 64), (1100, 128)])
+def test_graph_replays_match_eager(rra, T, num_blocks):
     import dataclasses
 
     import torch
 
-    say("[graph] capture four kernels, replay with fresh inputs")
-    T = 96
-    rcfg = dataclasses.replace(workloads.ROPE, num_blocks=64)
+    say(f"[graph] capture four kernels at T={T}, replay with fresh inputs")
+    rcfg = dataclasses.replace(workloads.ROPE, num_blocks=num_blocks)
 
     def load(salt):
         """Host inputs for one replay (seeded by salt)."""
