@@ -619,7 +619,11 @@ def copy_yardstick(nbytes_moved: int, launches: int, hip, stream, cyc):
     return best
 
 
-def sweep(Ts, launches_per_point: int = 30, kernels=KERNELS, with_copy: bool = True):
+# Timed launches per sweep point (after one warm-up launch per buffer set).
+SWEEP_LAUNCHES = 30
+
+
+def sweep(Ts, launches_per_point: int = SWEEP_LAUNCHES, kernels=KERNELS, with_copy: bool = True):
     """Each kernel alone at each T, rotating over buffer sets of that kernel
     that total at least 1 GiB of algorithmic traffic (four times the 256 MB
     last-level cache), so every launch reads cold data.  With with_copy, each
@@ -1085,7 +1089,14 @@ def summarize_sweep(trace_csv: str, out: str, command: str, Ts, kernels=KERNELS)
              "Produced by (from the repository root, after `cd /tmp && export TMPDIR=/tmp` for "
              "the profiler):", "", "```", command, "```", "",
              "Each point rotates over buffer sets holding at least 1 GiB, so every launch reads "
-             "cold data. Durations are the profiler's (median over the point's launches). "
+             "cold data. Durations are the profiler's (median over the point's launches: one "
+             "warm-up launch per buffer set, which the host issues one at a time with the GPU "
+             "otherwise idle, then the timed launches, queued behind a spin kernel with an event "
+             f"pair around each, {SWEEP_LAUNCHES} of them). Where `launches` exceeds "
+             f"{2 * SWEEP_LAUNCHES}, the warm-up launches are most of them, and the median is "
+             "the duration of an isolated launch: queued back to back with events between them, "
+             "any kernel of a few microseconds, the copy included, reads about 3.5 us in the "
+             "profiler. "
              "`copy` is the fastest of the library's streaming copies (`rra_stream_copy`, the "
              "fused kernels' own loads and stores, with 1, 2, 4 or 8 vectors per lane: `vpl`) "
              "moving the same number of bytes, half read and half written, timed the same way; "

@@ -98,9 +98,12 @@ __device__ __forceinline__ void row_prepare(const RowVecs<NV>& z, const RowVecs<
   for (int i = 1; i < NV; ++i) ss += acc[i];
 }
 
-// rho = 1/sqrt(ss / H + eps) of a row, in double.
-__device__ __forceinline__ double row_rho(double ss, int H, float eps) {
-  return rsqrt_f64(ss / static_cast<double>(H) + static_cast<double>(eps));
+// rho = 1/sqrt(ss / H + eps) of a row, in double, with ss / H correctly
+// rounded from r = 1/H (itself correctly rounded): a product and one
+// correction rather than a full division, which would lengthen the chain that
+// every wave of the row waits on.
+__device__ __forceinline__ double row_rho(double ss, double H, double r, float eps) {
+  return rsqrt_f64(div_rn(ss, H, r) + static_cast<double>(eps));
 }
 
 // Combine the partials of the kW waves of a row: wave-level DPP reductions,
@@ -130,20 +133,14 @@ __device__ __forceinline__ void row_reduce(double& ss, float& m, double* lds_ss,
 // The row's output from rho = 1/sqrt(ss / H + eps):
 //   y = t * rho
 // mode NONE writes y rounded to the element type E to out (uint16_t*); the
-// quantizing modes (E = bf16 inputs only) write
-// e4m3fn(y / s) to out (uint8_t*) and s to scale_row (row lane 0 for a
-// per-token scale, the first lane of each group for per-group scales).
-// Because rho > 0 is one number per row, max|y| = max|t| * rho, so the amax
-// needs no second pass over y, and the codes are e4m3fn(t * rho / s) (quant8
-// rounds them as the exact quotient would).  kMode and kGroup (64 or 128 for
-// per-group scales, else 0) are compile-time, so group indexing is a shift.
-template <int NV, int kMode, int kGroup, bool kFull, typename E = ElemBf16>
-__device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double rho, float m_row,
-                                             int nvec, int rl, int stride, float static_scale,
-                                             void* out, float* scale_row) {
-  static_assert(kMode != RRA_Q_PER_GROUP || kGroup == 64 || kGroup == 128, "group size");
-  const int lane = lane_id();
-
+// static mode (E = bf16 inputs only) writes e4m3fn(y / s) to out (uint8_t*),
+// rounded as the exact quotient would be (quant8).  The dynamic modes use
+// dyn_prepare and dyn_emit: because rho > 0 is one number per row,
+// max|y| = max|t| * rho, so the amax needs no second pass over y and the
+// codes need no rho at all.
+template <int NV, int kMode, bool kFull, typename E = ElemBf16>
+__device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double rho, int nvec, int rl,
+                                             int stride, float static_scale, void* out) {
   if constexpr (kMode == RRA_Q_NONE) {
     const float rho_f = static_cast<float>(rho);
     uint16_t* o = static_cast<uint16_t*>(out);
@@ -165,45 +162,90 @@ __device__ __forceinline__ void rmsnorm_emit(const RowT<NV>& t, double rho, floa
                          E::pack(y[6], y[7])};
       if (kFull || idx < nvec) st_stream(o + idx * 8, packed);
     }
-    return;
-  }
-
-  uint8_t* o = static_cast<uint8_t*>(out);
-  const double rho448 = rho_448(rho);
-  if constexpr (kMode == RRA_Q_PER_GROUP) {
-    constexpr int kLanesPerGroup = kGroup / 8;
+  } else {
+    static_assert(kMode == RRA_Q_STATIC, "dynamic scales go through dyn_prepare / dyn_emit");
+    uint8_t* o = static_cast<uint8_t*>(out);
+    // |y / s| is unbounded, so codes saturate.
+    const QuantStep qs = quant_step(rho, static_scale);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = i * stride + rl;
-      float m = 0.0f;
+      if (kFull || idx < nvec) st_stream(o + idx * 8, quant8<true>(t.t[i], qs));
+    }
+  }
+}
+
+// Dynamic scales (per-token, per-group) in two halves.  dyn_prepare takes the
+// amaxes (per-group slices their group's, a DPP max over the group's 16 or 8
+// lanes, so every lane of the wave must be active; a per-token row the row's
+// m_row) and, with kBrackets, forms a row lane's codes from them alone (rho
+// cancels in y / s; see dyn_step).  It needs no rho, so it runs while rho is
+// computed, or before the row's barrier.  dyn_emit then takes rho, forms and
+// stores the scales, settles the codes the brackets leave open and stores the
+// codes.  Held brackets cost 5 VGPRs per vector until the codes are stored;
+// with three or more vectors per lane that drops the kernels below 8 waves per
+// SIMD, so there (kBrackets = false) each vector's bracket is formed just
+// before it is settled, still without a reciprocal of s on the way.
+template <int NV, bool kBrackets>
+struct DynCodes {
+  Bracket8 b[kBrackets ? NV : 1];
+  float m[NV];
+};
+
+// Brackets are held for at most this many vectors per lane.
+constexpr bool dyn_brackets(int nv) { return nv <= 2; }
+
+template <int NV, int kMode, int kGroup, bool kBrackets>
+__device__ __forceinline__ void dyn_prepare(const RowT<NV>& t, float m_row,
+                                            DynCodes<NV, kBrackets>& dc) {
+  static_assert(kMode == RRA_Q_PER_TOKEN || (kMode == RRA_Q_PER_GROUP &&
+                                             (kGroup == 64 || kGroup == 128)), "mode");
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float m = m_row;
+    if constexpr (kMode == RRA_Q_PER_GROUP) {
+      m = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t.t[i][j]));
       m = kGroup == 128 ? max16(m) : max8(m);
-      const QuantStep qs = quant_step(rho, dynamic_scale(m, rho448));
-      if (kFull || idx < nvec) {
-        if ((lane & (kLanesPerGroup - 1)) == 0) scale_row[idx / kLanesPerGroup] = qs.s;
-        st_stream(o + idx * 8, quant8<false>(t.t[i], qs));
-      }
     }
-    return;
+    dc.m[i] = m;
+    if constexpr (kBrackets) {
+      const DynStep ds = dyn_step(m);
+      dc.b[i] = bracket8<false>(t.t[i], ds.f_dn, ds.f_up);
+    }
   }
+}
 
+template <int NV, int kMode, int kGroup, bool kFull, bool kBrackets>
+__device__ __forceinline__ void dyn_emit(const RowT<NV>& t, const DynCodes<NV, kBrackets>& dc,
+                                         double rho,
+                                         int nvec, int rl, int stride, uint8_t* out,
+                                         float* scale_row) {
+  constexpr int kLanesPerGroup = kGroup / 8;
+  const double rho448 = rho_448(rho);
+  // A scale that is not positive is stored as +0 (NaN where rho is NaN).
+  float s = 0.0f;
   if constexpr (kMode == RRA_Q_PER_TOKEN) {
-    const QuantStep qs = quant_step(rho, dynamic_scale(m_row, rho448));
-    if (rl == 0) scale_row[0] = qs.s;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int idx = i * stride + rl;
-      if (kFull || idx < nvec) st_stream(o + idx * 8, quant8<false>(t.t[i], qs));
-    }
-    return;
+    s = dynamic_scale(dc.m[0], rho448);
+    s = s > 0.0f ? s : 0.0f;
+    if (rl == 0) scale_row[0] = s;
   }
-  // RRA_Q_STATIC: |y / s| is unbounded, so codes saturate.
-  const QuantStep qs = quant_step(rho, static_scale);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = i * stride + rl;
-    if (kFull || idx < nvec) st_stream(o + idx * 8, quant8<true>(t.t[i], qs));
+    if constexpr (kMode == RRA_Q_PER_GROUP) {
+      s = dynamic_scale(dc.m[i], rho448);
+      s = s > 0.0f ? s : 0.0f;
+    }
+    if (kFull || idx < nvec) {
+      if (kMode == RRA_Q_PER_GROUP && (lane_id() & (kLanesPerGroup - 1)) == 0)
+        scale_row[idx / kLanesPerGroup] = s;
+      const DynStep ds = dyn_step(dc.m[i]);
+      const Bracket8 b = kBrackets ? dc.b[kBrackets ? i : 0] : bracket8<false>(t.t[i], ds.f_dn,
+                                                                                ds.f_up);
+      st_stream(out + idx * 8, dyn_settle(t.t[i], b, ds, s, rho));
+    }
   }
 }
 
@@ -227,7 +269,7 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
                                                  const float* __restrict__ static_scale,
                                                  void* __restrict__ out, int64_t out_stride,
                                                  float* __restrict__ scales, int64_t T, int H,
-                                                 int H_pad) {
+                                                 int H_pad, double inv_h) {
   constexpr int kBlockWaves = norm_block_waves(kW);
   constexpr int kRowsPerBlock = kBlockWaves / kW;
   constexpr int kStride = kW * kWave;
@@ -266,22 +308,35 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   double ss;
   float m;
   row_prepare<NV, E>(a, w, kMode == RRA_Q_PER_TOKEN, t, ss, m);
+  // Per-group codes need only this lane's groups: where they are held
+  // (kBr) they are formed before the row's barrier; per-token codes, and the
+  // amaxes of rows too wide to hold codes for, follow it.
+  constexpr bool kDyn = kMode == RRA_Q_PER_TOKEN || kMode == RRA_Q_PER_GROUP;
+  constexpr bool kBr = dyn_brackets(NV);
+  DynCodes<NV, kBr> dc;
+  if constexpr (kMode == RRA_Q_PER_GROUP && kBr) dyn_prepare<NV, kMode, kGroup, kBr>(t, 0.0f, dc);
   row_reduce<kW>(ss, m, lds_ss, lds_m, (wave / kW) * kW, wave_in_row);
   if (!active) return;
-  const double rho = row_rho(ss, H, eps);
+  if constexpr (kMode == RRA_Q_PER_TOKEN || (kMode == RRA_Q_PER_GROUP && !kBr))
+    dyn_prepare<NV, kMode, kGroup, kBr>(t, m, dc);
+  // With kFull the width is NV * kStride * 8, known here.
+  constexpr double kH = static_cast<double>(NV * kStride * 8);
+  const double rho = row_rho(ss, kFull ? kH : static_cast<double>(H), kFull ? 1.0 / kH : inv_h,
+                             eps);
 
   if constexpr (kMode == RRA_Q_NONE) {
     uint16_t* o = static_cast<uint16_t*>(out) + row * out_stride;
-    rmsnorm_emit<NV, RRA_Q_NONE, 0, kFull, E>(t, rho, m, nvec, rl, kStride, 0.0f, o, nullptr);
+    rmsnorm_emit<NV, RRA_Q_NONE, kFull, E>(t, rho, nvec, rl, kStride, 0.0f, o);
     for (int idx = nvec + rl; idx < (H_pad >> 3); idx += kStride)
       st_stream(o + idx * 8, u32x4{0u, 0u, 0u, 0u});
+  } else if constexpr (kMode == RRA_Q_STATIC) {
+    rmsnorm_emit<NV, kMode, kFull>(t, rho, nvec, rl, kStride, sscale,
+                                   static_cast<uint8_t*>(out) + row * out_stride);
   } else {
-    float* scale_row = nullptr;
-    if (kMode == RRA_Q_PER_TOKEN) scale_row = scales + row;
-    if (kMode == RRA_Q_PER_GROUP) scale_row = scales + row * (H / kGroup);
-    rmsnorm_emit<NV, kMode, kGroup, kFull>(t, rho, m, nvec, rl, kStride, sscale,
-                                           static_cast<uint8_t*>(out) + row * out_stride,
-                                           scale_row);
+    static_assert(kDyn, "mode");
+    float* scale_row = kMode == RRA_Q_PER_TOKEN ? scales + row : scales + row * (H / kGroup);
+    dyn_emit<NV, kMode, kGroup, kFull, kBr>(t, dc, rho, nvec, rl, kStride,
+                                       static_cast<uint8_t*>(out) + row * out_stride, scale_row);
   }
 }
 
@@ -294,10 +349,10 @@ __global__ void __launch_bounds__(norm_block_waves(kW) * kWave)
                              const uint16_t* __restrict__ weight, float eps,
                              const float* __restrict__ static_scale,
                              uint8_t* __restrict__ out, int64_t out_stride,
-                             float* __restrict__ scales, int64_t T, int H) {
+                             float* __restrict__ scales, int64_t T, int H, double inv_h) {
   add_rmsnorm_body<NV, kW, kResidual, kMode, kGroup, kFull>(x, x_stride, residual, res_stride,
                                                             weight, eps, static_scale, out,
-                                                            out_stride, scales, T, H, H);
+                                                            out_stride, scales, T, H, H, inv_h);
 }
 
 template <int NV, int kW, bool kResidual, bool kFull, typename E>
@@ -306,11 +361,11 @@ __global__ void __launch_bounds__(norm_block_waves(kW) * kWave)
                            uint16_t* __restrict__ residual, int64_t res_stride,
                            const uint16_t* __restrict__ weight, float eps,
                            uint16_t* __restrict__ out, int64_t out_stride, int64_t T, int H,
-                           int H_pad) {
+                           int H_pad, double inv_h) {
   add_rmsnorm_body<NV, kW, kResidual, RRA_Q_NONE, 0, kFull, E>(x, x_stride, residual,
                                                                res_stride, weight, eps, nullptr,
                                                                out, out_stride, nullptr, T, H,
-                                                               H_pad);
+                                                               H_pad, inv_h);
 }
 
 // MLA dual RMSNorm: one wave per token handles both of its rows, the q latent
@@ -326,8 +381,18 @@ __global__ void __launch_bounds__(norm_block_waves(kW) * kWave)
 // weight lead the argument list, so they are among the preloaded arguments;
 // 1/Hq and 1/Hkv (double) come last and are used only when the widths are not
 // the compile-time ones of kFull.
+// Waves per SIMD the one-wave kernel is held to: with all its waves resident
+// in one round up to 8192 tokens, a ninth VGPR block would leave a second
+// round.  Rows of up to four vectors per lane fit 64 VGPRs without spilling,
+// except with a per-token scale (12 bytes of spill at the DeepSeek-V3 shape),
+// which is left to the compiler.
+constexpr int dual_min_waves(int nvq, int nvkv, int mode) {
+  return nvq + nvkv <= 4 && mode != RRA_Q_PER_TOKEN ? 8 : 1;
+}
+
 template <int NVQ, int NVKV, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
+    __attribute__((amdgpu_waves_per_eu(dual_min_waves(NVQ, NVKV, kMode))))
     dual_rmsnorm_quant_kernel(int64_t T, int Hq, int Hkv, const uint16_t* __restrict__ q,
                               int64_t q_stride, const uint16_t* __restrict__ kv,
                               int64_t kv_stride, const uint16_t* __restrict__ q_w,
@@ -358,10 +423,8 @@ __global__ void __launch_bounds__(kBlock)
   row_prepare(zq, wq, kMode == RRA_Q_PER_TOKEN, tq, ss_q, m_q);
 
   // Lanes 0-31 finish with q's row, lanes 32-63 with kv's.  ms = ss / H is
-  // taken correctly rounded: the product with the rounded reciprocal of H,
-  // corrected once by its residual ss - ms0 * H, which an fma gives exactly
-  // (Markstein's final division step).  An infinite ss (an infinite value in
-  // the row) keeps ms = inf, hence rho = 0.
+  // taken correctly rounded from the rounded reciprocal of H (div_rn).  An
+  // infinite ss (an infinite value in the row) keeps ms = inf, hence rho = 0.
   const double ss = pair_sum_f64(ss_q, ss_kv);
   const bool kv_half = rl >= 32;
   double h, r;
@@ -372,23 +435,29 @@ __global__ void __launch_bounds__(kBlock)
     h = static_cast<double>(kv_half ? Hkv : Hq);
     r = kv_half ? inv_hkv : inv_hq;
   }
-  const double ms0 = ss * r;
-  const double ms = __builtin_isfinite(ms0) ? fma(fma(-ms0, h, ss), r, ms0) : ms0;
-  const double rho = rsqrt_f64(ms + static_cast<double>(kv_half ? eps_kv : eps_q));
+  const double rho = rsqrt_f64(div_rn(ss, h, r) + static_cast<double>(kv_half ? eps_kv : eps_q));
   const double rho_q = readlane_f64(rho, 31), rho_kv = readlane_f64(rho, 63);
-  if (kMode == RRA_Q_PER_TOKEN) m_q = wave_max(m_q);
+  // q's amaxes (and for short rows its codes) need no rho.  They follow kv's
+  // stores in program order, where the scheduler interleaves them with the
+  // statistics chain as far as registers allow (placed before kv's output,
+  // they cost the DeepSeek-V3 shape two waves per SIMD).
+  constexpr bool kBr = dyn_brackets(NVQ + NVKV);
+  DynCodes<NVQ, kBr> dc;
 
-  rmsnorm_emit<NVKV, RRA_Q_NONE, 0, kFull>(tkv, rho_kv, 0.0f, nkv, rl, kWave, 0.0f,
-                                           kv_out + row * kv_out_stride, nullptr);
-  void* qo;
-  float* scale_row = nullptr;
+  rmsnorm_emit<NVKV, RRA_Q_NONE, kFull>(tkv, rho_kv, nkv, rl, kWave, 0.0f,
+                                        kv_out + row * kv_out_stride);
+  if constexpr (kMode != RRA_Q_NONE)
+    dyn_prepare<NVQ, kMode, kGroup, kBr>(tq, kMode == RRA_Q_PER_TOKEN ? wave_max(m_q) : 0.0f,
+                                         dc);
   if constexpr (kMode == RRA_Q_NONE) {
-    qo = static_cast<uint16_t*>(q_out) + row * q_out_stride;
+    rmsnorm_emit<NVQ, kMode, kFull>(tq, rho_q, nq, rl, kWave, 0.0f,
+                                    static_cast<uint16_t*>(q_out) + row * q_out_stride);
   } else {
-    qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
-    scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
+    float* scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
+    dyn_emit<NVQ, kMode, kGroup, kFull, kBr>(tq, dc, rho_q, nq, rl, kWave,
+                                        static_cast<uint8_t*>(q_out) + row * q_out_stride,
+                                        scale_row);
   }
-  rmsnorm_emit<NVQ, kMode, kGroup, kFull>(tq, rho_q, m_q, nq, rl, kWave, 0.0f, qo, scale_row);
 }
 
 // MLA dual RMSNorm at decode sizes: one token per workgroup of NVQ + NVKV
@@ -405,7 +474,7 @@ __global__ void __launch_bounds__((NVQ + NVKV) * kWave)
                               const uint16_t* __restrict__ kv_w, float eps_q, float eps_kv,
                               void* __restrict__ q_out, int64_t q_out_stride,
                               float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
-                              int64_t kv_out_stride) {
+                              int64_t kv_out_stride, double inv_hq, double inv_hkv) {
   constexpr int kW = NVQ + NVKV;
   __shared__ double lds_ss[kW];
   __shared__ float lds_m[kW];
@@ -423,6 +492,10 @@ __global__ void __launch_bounds__((NVQ + NVKV) * kWave)
   double ss;
   float m;
   row_prepare(z, w, kMode == RRA_Q_PER_TOKEN, t, ss, m);
+  // Per-group codes are formed before the barrier (the kv wave forms some it
+  // never stores, which costs it nothing it waits for).
+  DynCodes<1, true> dc;
+  if constexpr (kMode == RRA_Q_PER_GROUP) dyn_prepare<1, kMode, kGroup, true>(t, 0.0f, dc);
   ss = wave_sum_f64(ss);
   if (kMode == RRA_Q_PER_TOKEN) m = wave_max(m);
   if (lane == 0) {
@@ -437,21 +510,30 @@ __global__ void __launch_bounds__((NVQ + NVKV) * kWave)
     ss += lds_ss[first + j];
     m = fmaxf(m, lds_m[first + j]);
   }
-  const double rho = row_rho(ss, is_q ? Hq : Hkv, is_q ? eps_q : eps_kv);
+  if constexpr (kMode == RRA_Q_PER_TOKEN) dyn_prepare<1, kMode, kGroup, true>(t, m, dc);
+  double h, r;
+  if constexpr (kFull) {
+    h = is_q ? NVQ * 512.0 : NVKV * 512.0;
+    r = is_q ? 1.0 / (NVQ * 512.0) : 1.0 / (NVKV * 512.0);
+  } else {
+    h = static_cast<double>(is_q ? Hq : Hkv);
+    r = is_q ? inv_hq : inv_hkv;
+  }
+  const double rho = row_rho(ss, h, r, is_q ? eps_q : eps_kv);
   if (!is_q) {
-    rmsnorm_emit<1, RRA_Q_NONE, 0, kFull>(t, rho, 0.0f, nvec, rl, kWave, 0.0f,
-                                          kv_out + row * kv_out_stride, nullptr);
+    rmsnorm_emit<1, RRA_Q_NONE, kFull>(t, rho, nvec, rl, kWave, 0.0f,
+                                       kv_out + row * kv_out_stride);
     return;
   }
-  void* qo;
-  float* scale_row = nullptr;
   if constexpr (kMode == RRA_Q_NONE) {
-    qo = static_cast<uint16_t*>(q_out) + row * q_out_stride;
+    rmsnorm_emit<1, kMode, kFull>(t, rho, nvec, rl, kWave, 0.0f,
+                                  static_cast<uint16_t*>(q_out) + row * q_out_stride);
   } else {
-    qo = static_cast<uint8_t*>(q_out) + row * q_out_stride;
-    scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
+    float* scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
+    dyn_emit<1, kMode, kGroup, kFull, true>(t, dc, rho, nvec, rl, kWave,
+                                      static_cast<uint8_t*>(q_out) + row * q_out_stride,
+                                      scale_row);
   }
-  rmsnorm_emit<1, kMode, kGroup, kFull>(t, rho, m, nvec, rl, kWave, 0.0f, qo, scale_row);
 }
 
 // Waves per row for the residual-add norm: enough that each lane holds at
@@ -480,7 +562,8 @@ template <int N, int W, bool kResidual, bool kFull, int kMode, int kGroup>
 static void launch_norm_quant(const NormLaunch& a) {
   hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual, kMode, kGroup, kFull>), a.grid,
                      dim3(norm_block_waves(W) * kWave), 0, a.st, a.x, a.xs, a.res, a.rs, a.w, a.eps, a.sscale,
-                     static_cast<uint8_t*>(a.out), a.os, a.scales, a.T, a.H);
+                     static_cast<uint8_t*>(a.out), a.os, a.scales, a.T, a.H,
+                     1.0 / static_cast<double>(a.H));
 }
 
 template <int N, int W, bool kResidual, bool kFull, typename E>
@@ -488,7 +571,7 @@ static void launch_norm_pad(const NormLaunch& a) {
   hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, kFull, E>), a.grid,
                      dim3(norm_block_waves(W) * kWave), 0, a.st,
                      a.x, a.xs, a.res, a.rs, a.w, a.eps, static_cast<uint16_t*>(a.out), a.os,
-                     a.T, a.H, a.H_pad);
+                     a.T, a.H, a.H_pad, 1.0 / static_cast<double>(a.H));
 }
 
 // One (vectors per lane, waves per row) case: mode NONE launches the padding
@@ -606,7 +689,8 @@ static void launch_dual(const DualLaunch& a) {
     hipLaunchKernelGGL((dual_rmsnorm_split_kernel<A, B, kMode, kGroup, kFull>),
                        dim3(static_cast<unsigned>(a.T)), dim3((A + B) * kWave), 0, a.st, a.T, a.Hq,
                        a.Hkv, a.q, a.qs, a.kv, a.kvs, a.qw, a.kvw, a.eps_q, a.eps_kv, a.q_out,
-                       a.qos, a.q_scales, a.kv_out, a.kvos);
+                       a.qos, a.q_scales, a.kv_out, a.kvos, 1.0 / static_cast<double>(a.Hq),
+                       1.0 / static_cast<double>(a.Hkv));
     return;
   }
   hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, kMode, kGroup, kFull>), a.grid,

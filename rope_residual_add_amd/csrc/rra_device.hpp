@@ -200,44 +200,109 @@ __device__ __forceinline__ QuantStep quant_step(double rho, float s) {
   return QuantStep{f * (1.0f - 0x1p-20f), f * (1.0f + 0x1p-20f), s, rho};
 }
 
-// Eight codes e4m3fn(t[j] * rho / s).  kClamp = false when s is a dynamic
-// scale (|t * rho / s| <= 448 within rounding; the conversion rounds up to
-// 464 to 448 by itself).
+// Eight codes from a bracket [f_dn, f_up] around the multiplier rho / s:
+// c = e4m3fn(t[j] * f_dn) for j = 0..7 and d = c ^ e4m3fn(t[j] * f_up), so a
+// nonzero byte of d flags a code the bracket leaves open.  kClamp = false when
+// s is a dynamic scale (|t * rho / s| <= 448 within rounding; the conversion
+// rounds up to 464 to 448 by itself).
+struct Bracket8 {
+  u32x2 c;
+  u32x2 d;
+};
+
 template <bool kClamp>
-__device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
-  if (!(qs.s > 0.0f)) return u32x2{0u, 0u};
+__device__ __forceinline__ Bracket8 bracket8(const float t[8], float f_dn, float f_up) {
   float lo[8], hi[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    lo[j] = t[j] * qs.f_dn;
-    hi[j] = t[j] * qs.f_up;
+    lo[j] = t[j] * f_dn;
+    hi[j] = t[j] * f_up;
   }
-  u32x2 c{pack_e4m3x4<kClamp>(lo[0], lo[1], lo[2], lo[3]),
-          pack_e4m3x4<kClamp>(lo[4], lo[5], lo[6], lo[7])};
-  const uint32_t d0 = c[0] ^ pack_e4m3x4<kClamp>(hi[0], hi[1], hi[2], hi[3]);
-  const uint32_t d1 = c[1] ^ pack_e4m3x4<kClamp>(hi[4], hi[5], hi[6], hi[7]);
-  if ((d0 | d1) != 0u) {
-    // q = p / s for p = t * rho, correctly rounded: q0 = p * y with y the
-    // rounded reciprocal of s, then one correction with the residual
-    // p - q0 * s, which an fma gives exactly (Markstein's final division
-    // step).  Taking p * (rho / s) instead can miss an exact midpoint by an
-    // ulp of the double, and the round-to-odd narrowing would then move a
-    // true tie off it.  The quotient takes t's sign: the correction cannot
-    // flip a nonzero q0, but for t = -0 the residual sum +0 + -0 is +0.
-    const double sd = static_cast<double>(qs.s);
-    const double y = 1.0 / sd;
+  const u32x2 c{pack_e4m3x4<kClamp>(lo[0], lo[1], lo[2], lo[3]),
+                pack_e4m3x4<kClamp>(lo[4], lo[5], lo[6], lo[7])};
+  return Bracket8{c, u32x2{c[0] ^ pack_e4m3x4<kClamp>(hi[0], hi[1], hi[2], hi[3]),
+                           c[1] ^ pack_e4m3x4<kClamp>(hi[4], hi[5], hi[6], hi[7])}};
+}
+
+// The codes of a bracket with its open ones settled: each flagged code is
+// recomputed from the exact quotient q = (t * rho) / s, correctly rounded in
+// double: q0 = p * y with y the rounded reciprocal of s, then one correction
+// with the residual p - q0 * s, which an fma gives exactly (Markstein's final
+// division step), narrowed to fp32 with round-to-odd.  Taking p * (rho / s)
+// instead can miss an exact midpoint by an ulp of the double, and the
+// round-to-odd narrowing would then move a true tie off it.  The quotient
+// takes t's sign: the correction cannot flip a nonzero q0, but for t = -0 the
+// residual sum +0 + -0 is +0.  Requires s > 0.
+template <bool kClamp>
+__device__ __forceinline__ u32x2 settle8(const float t[8], const Bracket8& b, float f_dn, float s,
+                                         double rho) {
+  if ((b.d[0] | b.d[1]) == 0u) return b.c;
+  float lo[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if ((((j < 4 ? d0 : d1) >> (8 * (j & 3))) & 0xFFu) != 0u) {
-        const double p = static_cast<double>(t[j]) * qs.rho;
-        const double q0 = p * y;
-        lo[j] = copysignf(f32_round_odd(fma(fma(-q0, sd, p), y, q0)), t[j]);
-      }
+  for (int j = 0; j < 8; ++j) lo[j] = t[j] * f_dn;
+  const double sd = static_cast<double>(s);
+  const double y = 1.0 / sd;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if ((((j < 4 ? b.d[0] : b.d[1]) >> (8 * (j & 3))) & 0xFFu) != 0u) {
+      const double p = static_cast<double>(t[j]) * rho;
+      const double q0 = p * y;
+      lo[j] = copysignf(f32_round_odd(fma(fma(-q0, sd, p), y, q0)), t[j]);
     }
-    c = u32x2{pack_e4m3x4<kClamp>(lo[0], lo[1], lo[2], lo[3]),
-              pack_e4m3x4<kClamp>(lo[4], lo[5], lo[6], lo[7])};
   }
-  return c;
+  return u32x2{pack_e4m3x4<kClamp>(lo[0], lo[1], lo[2], lo[3]),
+               pack_e4m3x4<kClamp>(lo[4], lo[5], lo[6], lo[7])};
+}
+
+// Eight codes e4m3fn(t[j] * rho / s) for a quantization step.
+template <bool kClamp>
+__device__ __forceinline__ u32x2 quant8(const float t[8], const QuantStep& qs) {
+  if (!(qs.s > 0.0f)) return u32x2{0u, 0u};
+  return settle8<kClamp>(t, bracket8<kClamp>(t, qs.f_dn, qs.f_up), qs.f_dn, qs.s, qs.rho);
+}
+
+// Dynamic scales before rho is known.  With s = fp32(m * rho / 448) for a
+// slice of amax m * rho (m = max |t|), the multiplier is rho / s =
+// 448 / (m (1 + e)), where e (|e| <= 2^-24 for a normal s) is the rounding of
+// s; the row's rho cancels.  So f = fp32(448 * rcp(m)) (the hardware
+// reciprocal is within 1 ulp) lies within 2^-21.6 of rho / s, the same
+// distance as the multiplier of quant_step, and the same bracket f (1 -+ 2^-20)
+// encloses every quotient of the slice.  Its codes can be formed while rho is
+// still being computed; once rho is known, dyn_settle takes s and settles
+// what the bracket leaves open.  Where m or f is not a normal fp32 number
+// (an amax near the fp32 subnormal range; m = 0, infinite or NaN) the bracket
+// is [0, inf] and every code is recomputed, as in quant_step.
+struct DynStep {
+  float f_dn;
+  float f_up;
+};
+
+__device__ __forceinline__ DynStep dyn_step(float m) {
+  const float f = 448.0f * __builtin_amdgcn_rcpf(m);
+  const bool in_range = m >= 0x1p-126f && f < 0x1p127f && f >= 0x1p-126f;
+  if (!in_range) return DynStep{0.0f, __builtin_inff()};
+  return DynStep{f * (1.0f - 0x1p-20f), f * (1.0f + 0x1p-20f)};
+}
+
+// A slice's codes with a dynamic scale s, from its bracket (dyn_step(m)).  A
+// scale that is not positive (an all-zero slice, or a row whose rho is 0 or
+// NaN because it holds an infinite or NaN value) gives +0 codes; a scale that
+// is not a normal fp32 number breaks the bound on e, so every code is then
+// recomputed.
+__device__ __forceinline__ u32x2 dyn_settle(const float t[8], Bracket8 b, const DynStep& ds,
+                                            float s, double rho) {
+  if (!(s > 0.0f)) return u32x2{0u, 0u};
+  if (!(s >= 0x1p-126f && s < __builtin_inff())) b.d = u32x2{~0u, ~0u};
+  return settle8<false>(t, b, ds.f_dn, s, rho);
+}
+
+// a / b correctly rounded, given r = 1/b correctly rounded: the product
+// q0 = a * r, corrected once by its residual a - q0 * b, which an fma gives
+// exactly (Markstein's final division step).  A non-finite q0 (a infinite) is
+// returned as it is.
+__device__ __forceinline__ double div_rn(double a, double b, double r) {
+  const double q0 = a * r;
+  return __builtin_isfinite(q0) ? fma(fma(-q0, b, a), r, q0) : q0;
 }
 
 // ---- wavefront reductions ---------------------------------------------------

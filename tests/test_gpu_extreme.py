@@ -40,15 +40,20 @@ def _bf16(a) -> np.ndarray:
 NORM_ROWS = [  # (magnitude of x, eps)
     (1e-20, 0.0), (1e-30, 1e-6), (1e-38, 1e-5), (1e-39, 0.0), (1e36, 1e-6)]
 
+# (T, H) reaching each launch shape of the residual-add norm: one vector per
+# lane (T <= 512), two vectors per lane, and three (H = 6144, where the codes
+# of a dynamic scale are formed vector by vector rather than held).
+NORM_SHAPES = [(64, 1024), (600, 1024), (520, 6144)]
 
+
+@pytest.mark.parametrize("T,H", NORM_SHAPES)
 @pytest.mark.parametrize("mode,g", [(1, 0), (2, 0), (3, 64), (3, 128)])
 @pytest.mark.parametrize("mag,eps", NORM_ROWS)
-def test_norm_extreme_rows(rra, oracle, mag, eps, mode, g):
+def test_norm_extreme_rows(rra, oracle, mag, eps, mode, g, T, H):
     import torch
 
-    say(f"[extreme] norm |x|~{mag:g} eps={eps:g} mode={mode} g={g}")
+    say(f"[extreme] norm |x|~{mag:g} eps={eps:g} mode={mode} g={g} T={T} H={H}")
     rng = np.random.default_rng(11)
-    T, H = 64, 1024
     x = _bf16(rng.standard_normal((T, H)) * mag)
     w = _bf16(1 + 0.1 * rng.standard_normal(H))
     static = 0.05
@@ -84,15 +89,16 @@ def test_norm_negative_zero(rra, oracle):
         assert_codes(codes, ref, f"-0 codes mode={mode}")
 
 
+@pytest.mark.parametrize("T", [32, 1100])  # one wave per vector; one wave per token
 @pytest.mark.parametrize("mag,eps", [(1e-20, 0.0), (1e-39, 0.0), (1e36, 1e-6)])
-def test_dual_extreme_rows(rra, oracle, mag, eps):
+def test_dual_extreme_rows(rra, oracle, mag, eps, T):
     """MLA dual norm: bf16 kv output (rho beyond fp32 for the 1e-39 rows) and
     per-group FP8 q."""
     import torch
 
-    say(f"[extreme] dual |x|~{mag:g} eps={eps:g}")
+    say(f"[extreme] dual |x|~{mag:g} eps={eps:g} T={T}")
     rng = np.random.default_rng(13)
-    T, Hq, Hkv = 32, 1536, 512
+    Hq, Hkv = 1536, 512
     q = _bf16(rng.standard_normal((T, Hq)) * mag)
     kv = _bf16(rng.standard_normal((T, Hkv)) * mag)
     qw = _bf16(1 + 0.1 * rng.standard_normal(Hq))
@@ -263,17 +269,17 @@ def _special_norm_rows(rng, T, H):
     return _bf16(x), [1, 2, 3, 4, 5]
 
 
+@pytest.mark.parametrize("T,H", [(16, 1024), (600, 6144)])
 @pytest.mark.parametrize("mode,g", [(1, 0), (2, 0), (3, 64), (3, 128)])
-def test_norm_non_finite_rows(rra, oracle, mode, g):
+def test_norm_non_finite_rows(rra, oracle, mode, g, T, H):
     """A row holding a NaN or an infinity: rho is NaN or 0, and the oracle's
     reading gives scale 0 and +0 codes for every dynamic slice of it (the amax
     of NaN values is 0), NaN codes (static scale) where a value is NaN.  Zero
     rows with -0.0 entries get scale 0 and +0 codes."""
     import torch
 
-    say(f"[extreme] norm non-finite rows mode={mode} g={g}")
+    say(f"[extreme] norm non-finite rows mode={mode} g={g} T={T} H={H}")
     rng = np.random.default_rng(16)
-    T, H = 16, 1024
     x, special = _special_norm_rows(rng, T, H)
     w = _bf16(1 + 0.1 * rng.standard_normal(H))
     ss = torch.tensor([0.05], dtype=torch.float32, device="cuda") if mode == 1 else None
@@ -291,12 +297,13 @@ def test_norm_non_finite_rows(rra, oracle, mode, g):
         assert_scales(got[ordinary], ref_scales[ordinary], "ordinary scales")
 
 
-def test_dual_non_finite_rows(rra, oracle):
+@pytest.mark.parametrize("T", [16, 1100])
+def test_dual_non_finite_rows(rra, oracle, T):
     import torch
 
-    say("[extreme] dual non-finite rows")
+    say(f"[extreme] dual non-finite rows T={T}")
     rng = np.random.default_rng(17)
-    T, Hq, Hkv = 16, 1536, 512
+    Hq, Hkv = 1536, 512
     q, special = _special_norm_rows(rng, T, Hq)
     kv, _ = _special_norm_rows(rng, T, Hkv)
     qw = _bf16(1 + 0.1 * rng.standard_normal(Hq))
