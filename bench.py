@@ -138,7 +138,7 @@ def algo_bytes(name: str, T: int) -> int:
 
 # Work-items per launch at T tokens, as the library launches these workloads
 # (used only to tell the sweep's launches apart in a kernel trace):
-#  - residual-add norms: up to 512 rows, one vector per lane and one row per
+#  - residual-add norms: up to 1024 rows, one vector per lane and one row per
 #    workgroup of max(4, waves per row) waves (H = 4096: 8 waves; H = 1024: two
 #    rows of 2 waves); above, four waves per row at widths above 2048 (one
 #    workgroup per row), one wave per row up to 1024 (four rows per workgroup);
@@ -149,7 +149,7 @@ def algo_bytes(name: str, T: int) -> int:
 #    lane (Llama-3-8B / Qwen3-8B attention: 48 heads x 8 two-vector units, six
 #    waves; DeepSeek-V3 MLA: 129 heads x 8 one-vector units + 64 kv_c vectors,
 #    eighteen).
-NORM_SPLIT_MAX_T, DUAL_SPLIT_MAX_T = 512, 1024
+NORM_SPLIT_MAX_T, DUAL_SPLIT_MAX_T = 1024, 1024
 
 
 def _rope_waves_per_token(units: int) -> int:

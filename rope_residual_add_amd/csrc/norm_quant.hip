@@ -610,8 +610,9 @@ static void launch_norm_case(const NormLaunch& a, int mode, int group, int dtype
 // chain of loads, double-precision statistics, scale and codes.  Above it,
 // rows of up to 4096 columns take four waves with two vectors per lane.
 // Measured on MI355X at H = 4096 (profiler medians, cold): the split shape is
-// 0.1-0.16 us faster at T = 32 ... 512, equal at 1024, 3% slower at 2048.
-constexpr int64_t kNormSplitMaxT = 512;
+// 0.1-0.16 us faster at T = 32 ... 512 and 3% faster at 1024, equal at 2048,
+// 1% slower at 4096.
+constexpr int64_t kNormSplitMaxT = 1024;
 
 // (vectors per lane, waves per row) for a launch of T rows of width H.
 inline void norm_shape(int64_t T, int64_t H, int& nv, int& kw) {

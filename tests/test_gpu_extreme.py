@@ -41,9 +41,9 @@ NORM_ROWS = [  # (magnitude of x, eps)
     (1e-20, 0.0), (1e-30, 1e-6), (1e-38, 1e-5), (1e-39, 0.0), (1e36, 1e-6)]
 
 # (T, H) reaching each launch shape of the residual-add norm: one vector per
-# lane (T <= 512), two vectors per lane, and three (H = 6144, where the codes
+# lane (T <= 1024), two vectors per lane, and three (H = 6144, where the codes
 # of a dynamic scale are formed vector by vector rather than held).
-NORM_SHAPES = [(64, 1024), (600, 1024), (520, 6144)]
+NORM_SHAPES = [(64, 1024), (1100, 1024), (1030, 6144)]
 
 
 @pytest.mark.parametrize("T,H", NORM_SHAPES)
@@ -269,7 +269,7 @@ def _special_norm_rows(rng, T, H):
     return _bf16(x), [1, 2, 3, 4, 5]
 
 
-@pytest.mark.parametrize("T,H", [(16, 1024), (600, 6144)])
+@pytest.mark.parametrize("T,H", [(16, 1024), (1030, 6144)])
 @pytest.mark.parametrize("mode,g", [(1, 0), (2, 0), (3, 64), (3, 128)])
 def test_norm_non_finite_rows(rra, oracle, mode, g, T, H):
     """A row holding a NaN or an infinity: rho is NaN or 0, and the oracle's

@@ -90,10 +90,10 @@ def test_per_group(rra, oracle, T, g):
     run(rra, oracle, T, 4096, 3, g)
 
 
-# Up to 512 rows the kernel runs one vector per lane (a row over up to 16
+# Up to 1024 rows the kernel runs one vector per lane (a row over up to 16
 # waves), above that four waves per row with two vectors per lane (H = 4096):
 # both sides of the switch, every mode, and widths of 1 to 16 waves per row.
-@pytest.mark.parametrize("T", [511, 512, 513])
+@pytest.mark.parametrize("T", [1023, 1024, 1025])
 @pytest.mark.parametrize("mode,g", [(1, 0), (2, 0), (3, 128), (3, 64)])
 def test_decode_shape_switch(rra, oracle, T, mode, g):
     run(rra, oracle, T, 4096, mode, g)
@@ -102,7 +102,7 @@ def test_decode_shape_switch(rra, oracle, T, mode, g):
 @pytest.mark.parametrize("H", [512, 1024, 2048, 3072, 6144, 8192])
 def test_decode_shape_widths(rra, oracle, H):
     run(rra, oracle, 24, H, 3, 64)
-    run(rra, oracle, 600, H, 2)
+    run(rra, oracle, 1100, H, 2)
 
 
 @pytest.mark.parametrize("mode,g", [(1, 0), (2, 0), (3, 128)])
