@@ -489,7 +489,7 @@ def run_steps(launch, steps: int, warmup: int):
     """Warm up, then time `steps` passes over the four kernels (launch: the
     dict of make_launchers) twice: first with nothing between the launches,
     for the whole step's wall time, then with HIP events around every launch,
-    for each kernel's duration.  Returns
+    queued behind a spin kernel, for each kernel's duration.  Returns
     (wall seconds for the first timed steps, {kernel: [per-launch ms]})."""
     import torch
 
@@ -508,7 +508,13 @@ def run_steps(launch, steps: int, warmup: int):
     stream = torch.cuda.current_stream().cuda_stream
     nk = len(KERNELS)
     ev = hip.create(steps * (nk + 1))
+    # All launches and events of the pass are queued behind a spin kernel
+    # (long enough for the host to issue them, ~15 us each), so that each
+    # interval holds the GPU's own time between two launches and never a
+    # wait for the host.
+    cyc = _blocker_cycles(max(5.0, 0.03 * steps * (2 * nk + 1)))
     torch.cuda.synchronize()
+    torch.cuda._sleep(cyc)
     for s in range(steps):
         base = s * (nk + 1)
         hip.record(ev[base], stream)
