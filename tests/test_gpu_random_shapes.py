@@ -2,7 +2,8 @@
 over widths, head counts, head sizes, block sizes, strides, quant modes,
 pairings, element types and padding drawn at random within the documented
 limits (ragged widths that leave lanes and vectors partly used, one- and
-many-pass tokens, T from 1 to a few hundred).  The cases are fixed by the
+many-pass tokens, T from 1 to a few hundred, and for the two norms a few
+cases above their 1024-token switch of launch shape).  The cases are fixed by the
 seed, so a failure names a reproducible shape.  Each case reuses the checks
 of the op's own GPU test (codes within 1 ULP on at most 1e-4 of them, scales
 and bf16/fp16 outputs within rtol 1e-2, caches exact outside the written
@@ -114,6 +115,24 @@ def _mla_rope(rng):
     return dict(T=T, cfg=cfg, pad_every=int(rng.choice([0, 5])))
 
 
+# The norms switch launch shape above 1024 rows (tokens): a few cases each
+# above the switch, so that ragged widths reach the wide-row shapes too.
+N_LARGE = max(1, N_CASES // 4)
+
+
+def _large(draw):
+    def f(rng):
+        c = draw(rng)
+        c["T"] = int(rng.integers(1025, 1400))
+        return c
+    return f
+
+
+def _cases_large(tag, draw):
+    rng = np.random.default_rng([20261202, sum(map(ord, tag)), 1])
+    return [_large(draw)(rng) for _ in range(N_LARGE)]
+
+
 @pytest.mark.parametrize("c", _cases("norm", _norm), ids=lambda c: f"T{c['T']}-H{c['H']}-m{c['mode']}")
 def test_norm_random(rra, oracle, c):
     run_norm(rra, oracle, c["T"], c["H"], c["mode"], c["g"], eps=c["eps"],
@@ -154,3 +173,16 @@ def test_pad_random(rra, oracle, c):
                          ids=lambda c: f"T{c['T']}-{c['cfg'].Hq}x{c['cfg'].nope}+{c['cfg'].rope_dim}")
 def test_mla_rope_random(rra, oracle, c):
     run_mla_rope(rra, oracle, c["T"], c["cfg"], pad_every=c["pad_every"])
+
+
+@pytest.mark.parametrize("c", _cases_large("norm", _norm),
+                         ids=lambda c: f"T{c['T']}-H{c['H']}-m{c['mode']}")
+def test_norm_random_large_T(rra, oracle, c):
+    run_norm(rra, oracle, c["T"], c["H"], c["mode"], c["g"], eps=c["eps"],
+             residual=c["residual"], strided=c["strided"])
+
+
+@pytest.mark.parametrize("c", _cases_large("dual", _dual), ids=lambda c: f"T{c['T']}-{c['Hq']}-{c['Hkv']}")
+def test_dual_random_large_T(rra, oracle, c):
+    run_dual(rra, oracle, c["T"], c["mode"], c["g"], c["eps_q"], c["eps_kv"], c["split_views"],
+             Hq=c["Hq"], Hkv=c["Hkv"])
