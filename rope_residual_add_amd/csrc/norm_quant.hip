@@ -192,7 +192,7 @@ struct DynCodes {
   float m[NV];
 };
 
-// Brackets are held for at most this many vectors per lane.
+// Whether a lane holds the brackets of all its nv vectors (up to two).
 constexpr bool dyn_brackets(int nv) { return nv <= 2; }
 
 template <int NV, int kMode, int kGroup, bool kBrackets>
@@ -219,12 +219,12 @@ __device__ __forceinline__ void dyn_prepare(const RowT<NV>& t, float m_row,
 
 template <int NV, int kMode, int kGroup, bool kFull, bool kBrackets>
 __device__ __forceinline__ void dyn_emit(const RowT<NV>& t, const DynCodes<NV, kBrackets>& dc,
-                                         double rho,
-                                         int nvec, int rl, int stride, uint8_t* out,
+                                         double rho, int nvec, int rl, int stride, uint8_t* out,
                                          float* scale_row) {
   constexpr int kLanesPerGroup = kGroup / 8;
   const double rho448 = rho_448(rho);
-  // A scale that is not positive is stored as +0 (NaN where rho is NaN).
+  // A scale that is not positive (0 for an all-zero slice, NaN where rho is
+  // NaN) is stored as +0.
   float s = 0.0f;
   if constexpr (kMode == RRA_Q_PER_TOKEN) {
     s = dynamic_scale(dc.m[0], rho448);
@@ -242,8 +242,11 @@ __device__ __forceinline__ void dyn_emit(const RowT<NV>& t, const DynCodes<NV, k
       if (kMode == RRA_Q_PER_GROUP && (lane_id() & (kLanesPerGroup - 1)) == 0)
         scale_row[idx / kLanesPerGroup] = s;
       const DynStep ds = dyn_step(dc.m[i]);
-      const Bracket8 b = kBrackets ? dc.b[kBrackets ? i : 0] : bracket8<false>(t.t[i], ds.f_dn,
-                                                                                ds.f_up);
+      Bracket8 b;
+      if constexpr (kBrackets)
+        b = dc.b[i];
+      else
+        b = bracket8<false>(t.t[i], ds.f_dn, ds.f_up);
       st_stream(out + idx * 8, dyn_settle(t.t[i], b, ds, s, rho));
     }
   }
@@ -437,10 +440,10 @@ __global__ void __launch_bounds__(kBlock)
   }
   const double rho = rsqrt_f64(div_rn(ss, h, r) + static_cast<double>(kv_half ? eps_kv : eps_q));
   const double rho_q = readlane_f64(rho, 31), rho_kv = readlane_f64(rho, 63);
-  // q's amaxes (and for short rows its codes) need no rho.  They follow kv's
-  // stores in program order, where the scheduler interleaves them with the
-  // statistics chain as far as registers allow (placed before kv's output,
-  // they cost the DeepSeek-V3 shape two waves per SIMD).
+  // q's amaxes (and for short rows its codes) need no rho, but they follow
+  // kv's output: formed before it, alongside the statistics, their live
+  // values cost the DeepSeek-V3 shape two waves per SIMD, or spills when held
+  // to eight.
   constexpr bool kBr = dyn_brackets(NVQ + NVKV);
   DynCodes<NVQ, kBr> dc;
 
