@@ -1,6 +1,7 @@
 """Host logic of bench.py, on the CPU: the one-GPU refusal, the code-only
-source hash, and that the committed HBM-traffic summary was taken on the
-kernel sources as they stand (bench.py reports `traffic` only then)."""
+source hash, that the committed HBM-traffic summary was taken on the kernel
+sources as they stand (bench.py reports `traffic` only then), and that the
+launch shapes bench.py expects are the library's."""
 import os
 import re
 import subprocess
@@ -42,3 +43,21 @@ def test_traffic_summary_matches_the_sources():
     stale = {k: (h, bench.source_hash(k)) for k, h in rows.items()
              if k in bench.KERNEL_SOURCES and bench.source_hash(k) != h}
     assert not stale, f"counters taken on other code (re-take them): {stale}"
+
+
+def test_launch_shapes_match_the_library():
+    """bench.py tells a kernel trace's launches apart by the grid and symbol the
+    library uses at each T; its switch points must be the library's."""
+    import bench
+
+    src = open(os.path.join(ROOT, "rope_residual_add_amd", "csrc", "norm_quant.hip"),
+               encoding="utf-8").read()
+    lib = {name: int(v) for name, v in
+           re.findall(r"constexpr int64_t (kNormSplitMaxT|kDualSplitMaxT) = (\d+);", src)}
+    assert lib == {"kNormSplitMaxT": bench.NORM_SPLIT_MAX_T,
+                   "kDualSplitMaxT": bench.DUAL_SPLIT_MAX_T}
+    # one vector per lane up to the switch, then the four-wave (H > 2048) shape
+    T = bench.NORM_SPLIT_MAX_T
+    assert bench._norm_shape(T, 4096) == (1, 8)
+    assert bench._norm_shape(T + 1, 4096) == (2, 4)
+    assert bench._norm_shape(T + 1, 1024) == (2, 1)
