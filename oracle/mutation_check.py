@@ -136,9 +136,20 @@ BOTH_MUTANTS = [
 ALL = [(n, o, r, False) for n, o, r in MUTANTS] + [(n, o, r, True) for n, o, r in BOTH_MUTANTS]
 
 
+# What the oracle's tests need: the oracle itself, the tests, the seeded input
+# generators and the pytest configuration.
+COPIED = ("oracle", "tests", "workloads.py", "pytest.ini")
+
+
 def _copy_tree(dst: str) -> None:
-    shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(
-        ".git", "_work", "gpurun_out", "__pycache__", "*.so", ".pytest_cache", "profiles"))
+    os.makedirs(dst)
+    skip = shutil.ignore_patterns("__pycache__", "*.so", ".pytest_cache")
+    for name in COPIED:
+        src = os.path.join(ROOT, name)
+        if os.path.isdir(src):
+            shutil.copytree(src, os.path.join(dst, name), ignore=skip)
+        else:
+            shutil.copy2(src, os.path.join(dst, name))
 
 
 def run_one(i: int) -> tuple:

@@ -4,8 +4,8 @@ and how many differ from the oracle's (all by one code at most, or the test
 fails), and the fraction of scales and bf16/fp16 outputs that are bit-identical
 to the oracle's.
 
-    RRA_PARITY_LOG=gpurun_out/parity.jsonl python -m pytest tests -m gpu -q
-    python tests/parity_summary.py gpurun_out/parity.jsonl --out profiles/parity_every_row.md
+    RRA_PARITY_LOG=/tmp/parity.jsonl python -m pytest tests -m gpu -q
+    python tests/parity_summary.py /tmp/parity.jsonl --out profiles/parity_every_row.md
 
 Not a test module (pytest collects test_*.py only)."""
 from __future__ import annotations
@@ -89,13 +89,13 @@ def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("log")
     ap.add_argument("--out")
-    ap.add_argument("--command", default=(
-        "RRA_PARITY_LOG=gpurun_out/parity.jsonl timeout -k 10 1000 python -u -m pytest tests "
+    ap.add_argument("--command", help="the commands that produced the log, for the summary's "
+                    "header (default: the usual two, with the log at {log})", default=(
+        "RRA_PARITY_LOG={log} timeout -k 10 1000 python -u -m pytest tests "
         "-m gpu -x -q --timeout 300 --timeout-method thread\n"
-        "python tests/parity_summary.py gpurun_out/parity.jsonl --out "
-        "profiles/parity_every_row.md"))
+        "python tests/parity_summary.py {log} --out profiles/parity_every_row.md"))
     a = ap.parse_args()
-    text = summarize(load(a.log), a.command)
+    text = summarize(load(a.log), a.command.replace("{log}", a.log))
     if a.out:
         with open(a.out, "w", encoding="utf-8") as f:
             f.write(text)
