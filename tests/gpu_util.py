@@ -75,7 +75,13 @@ def host_f32(t) -> np.ndarray:
     return t.contiguous().cpu().numpy()
 
 
-def assert_codes(gpu: np.ndarray, ref: np.ndarray, what: str) -> dict:
+def assert_codes(gpu: np.ndarray, ref: np.ndarray, what: str, exact: bool = False) -> dict:
+    """FP8 codes against the oracle's.  exact: every code must be the oracle's
+    (the norm kernels round each code as the exact quotient would).
+    Otherwise (SiLU, whose activation is formed in fp32) codes may differ by
+    one code on at most CODE_MISMATCH_BUDGET of them; a case of fewer codes
+    than 1 / CODE_MISMATCH_BUDGET may have one, the least whole count that
+    fraction can mean at that size."""
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     d = code_ulp_diff(gpu, ref)
     n = d.size
@@ -83,8 +89,10 @@ def assert_codes(gpu: np.ndarray, ref: np.ndarray, what: str) -> dict:
     stats = dict(what=what, codes=n, mismatches=bad, max_ulp=int(d.max()) if n else 0)
     print(stats, flush=True)
     _record("codes", stats)
+    if exact:
+        assert bad == 0, stats
     assert stats["max_ulp"] <= 1, stats
-    assert bad <= CODE_MISMATCH_BUDGET * n, stats
+    assert bad <= max(1.0, CODE_MISMATCH_BUDGET * n), stats
     return stats
 
 

@@ -54,7 +54,7 @@ def run(rra, oracle, T, mode=3, g=128, eps_q=1e-6, eps_kv=1e-6, split_views=Fals
     if mode == 0:
         assert_bf16(host_bf16(q_out)[rows], ref_q, f"q_out T={T}")
     else:
-        assert_codes(host_u8(q_out)[rows], ref_q, f"q codes T={T}")
+        assert_codes(host_u8(q_out)[rows], ref_q, f"q codes T={T}", exact=True)
         assert_scales(host_f32(q_scales)[rows], ref_s, "q scales")
         if T:
             gg = Hq if mode == 2 else g
