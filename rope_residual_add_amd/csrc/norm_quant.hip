@@ -19,6 +19,12 @@
 // of one vector, so group amaxes are DPP row reductions with no exchange.
 // Rows past the end are predicated off rather than returned from, so that
 // every wave of a workgroup reaches the barrier.
+//
+// Statistics and scales are in double, and codes are rounded as the exact
+// quotient would be (rra_device.hpp).  With a dynamic scale the row's rho
+// cancels in y / s, so the codes are bracketed from the amaxes alone while rho
+// is still being computed; after rho only the scales, a range check and the
+// rare exact-quotient path remain (dyn_prepare, dyn_emit).
 #include "rra_device.hpp"
 #include "rra_host.hpp"
 
