@@ -62,8 +62,8 @@
 extern "C" {
 #endif
 
-/* 5: qk_norm_rope_kv_write refuses write_k = 0 without a cache. */
-#define RRA_ABI_VERSION 5
+/* 6: rope_kv_write refuses q or k token strides of 2^35 elements or more. */
+#define RRA_ABI_VERSION 6
 
 enum rra_status {
   RRA_OK = 0,
@@ -192,7 +192,8 @@ int rope_cos_sin_cache(float* cos_sin, int64_t max_pos, int rot_dim, double thet
  * key_cache, value_cache [num_blocks, block_size, Hkv, D] dtype, contiguous.
  * Limits: D in {64, 128, 256}; rot_dim == D; is_neox 1 (GPT-NeoX pairs
  * (i, i + D/2)) or 0 (GPT-J pairs (2i, 2i + 1)); 1 <= Hq, Hkv <= 65536;
- * block_size >= 1; dtype RRA_BF16 or RRA_F16 (else RRA_ERR_UNSUPPORTED).
+ * q_stride and k_stride below 2^35 elements; block_size >= 1; dtype RRA_BF16
+ * or RRA_F16 (else RRA_ERR_UNSUPPORTED).
  */
 int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_t q_stride,
                   uint16_t* q_out, int64_t q_out_stride, const uint16_t* k, int64_t k_stride,

@@ -33,7 +33,7 @@ class RRAError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 5  # RRA_ABI_VERSION of include/rra.h
+ABI_VERSION = 6  # RRA_ABI_VERSION of include/rra.h
 BF16, F16 = 0, 1  # enum rra_dtype
 _ELEM = {torch.bfloat16: BF16, torch.float16: F16}
 

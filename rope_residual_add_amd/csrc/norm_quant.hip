@@ -290,14 +290,20 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave / kW;
   // With one row per workgroup the grid has exactly T blocks.
   const bool active = kRowsPerBlock == 1 || row < T;
-  const int nvec = H >> 3;
+  // With kFull the row width is known here, and H (past the preloaded
+  // arguments) is not needed.
+  constexpr int kWidth = NV * kStride * 8;
+  const int nvec = kFull ? kWidth / 8 : H >> 3;
 
   RowVecs<NV> a, r, w;
   load_row<NV, true, kFull>(a, x + row * x_stride, nvec, rl, kStride, active);
   if (kResidual)
     load_row<NV, true, kFull>(r, residual + row * res_stride, nvec, rl, kStride, active);
   load_row<NV, false, kFull>(w, weight, nvec, rl, kStride, true);
+  args_ready(out, out_stride, scales);
+  if constexpr (!kFull || kMode == RRA_Q_NONE) args_ready(H, H_pad, inv_h);
   const float sscale = kMode == RRA_Q_STATIC ? static_scale[0] : 0.0f;
+  if constexpr (kMode == RRA_Q_STATIC) arg_ready(sscale);
 
   if (kResidual) {
     // z = E(x + residual): fp32 carries at least 2p + 2 significand bits for
@@ -328,8 +334,7 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
   if (!active) return;
   if constexpr (kMode == RRA_Q_PER_TOKEN || (kMode == RRA_Q_PER_GROUP && !kBr))
     dyn_prepare<NV, kMode, kGroup, kBr>(t, m, dc);
-  // With kFull the width is NV * kStride * 8, known here.
-  constexpr double kH = static_cast<double>(NV * kStride * 8);
+  constexpr double kH = static_cast<double>(kWidth);
   const double rho = row_rho(ss, kFull ? kH : static_cast<double>(H), kFull ? 1.0 / kH : inv_h,
                              eps);
 
@@ -343,7 +348,8 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
                                    static_cast<uint8_t*>(out) + row * out_stride);
   } else {
     static_assert(kDyn, "mode");
-    float* scale_row = kMode == RRA_Q_PER_TOKEN ? scales + row : scales + row * (H / kGroup);
+    float* scale_row =
+        kMode == RRA_Q_PER_TOKEN ? scales + row : scales + row * ((kFull ? kWidth : H) / kGroup);
     dyn_emit<NV, kMode, kGroup, kFull, kBr>(t, dc, rho, nvec, rl, kStride,
                                        static_cast<uint8_t*>(out) + row * out_stride, scale_row);
   }
@@ -355,10 +361,10 @@ template <int NV, int kW, bool kResidual, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(norm_block_waves(kW) * kWave)
     add_rmsnorm_quant_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                              uint16_t* __restrict__ residual, int64_t res_stride,
-                             const uint16_t* __restrict__ weight, float eps,
+                             const uint16_t* __restrict__ weight, int64_t T, float eps,
                              const float* __restrict__ static_scale,
                              uint8_t* __restrict__ out, int64_t out_stride,
-                             float* __restrict__ scales, int64_t T, int H, double inv_h) {
+                             float* __restrict__ scales, int H, double inv_h) {
   add_rmsnorm_body<NV, kW, kResidual, kMode, kGroup, kFull>(x, x_stride, residual, res_stride,
                                                             weight, eps, static_scale, out,
                                                             out_stride, scales, T, H, H, inv_h);
@@ -368,9 +374,9 @@ template <int NV, int kW, bool kResidual, bool kFull, typename E>
 __global__ void __launch_bounds__(norm_block_waves(kW) * kWave)
     add_rmsnorm_pad_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
                            uint16_t* __restrict__ residual, int64_t res_stride,
-                           const uint16_t* __restrict__ weight, float eps,
-                           uint16_t* __restrict__ out, int64_t out_stride, int64_t T, int H,
-                           int H_pad, double inv_h) {
+                           const uint16_t* __restrict__ weight, int64_t T, float eps,
+                           uint16_t* __restrict__ out, int64_t out_stride, int H, int H_pad,
+                           double inv_h) {
   add_rmsnorm_body<NV, kW, kResidual, RRA_Q_NONE, 0, kFull, E>(x, x_stride, residual,
                                                                res_stride, weight, eps, nullptr,
                                                                out, out_stride, nullptr, T, H,
@@ -386,10 +392,11 @@ __global__ void __launch_bounds__(norm_block_waves(kW) * kWave)
 // than the extra vectors per lane.  The two rows share their statistics work:
 // one paired reduction leaves q's sum of squares in lane 31 and kv's in lane
 // 63, and one vector pass takes both mean squares and both rsqrts (each lane
-// with its half's width and epsilon).  The row count, both rows and the q
-// weight lead the argument list, so they are among the preloaded arguments;
-// 1/Hq and 1/Hkv (double) come last and are used only when the widths are not
-// the compile-time ones of kFull.
+// with its half's width and epsilon).  The row count, both rows and both
+// weights are the first 14 argument dwords, which a wave starts with in
+// registers, so the loads need no argument fetch; the widths and their
+// reciprocals come last and are used only when they are not the compile-time
+// ones of kFull.
 // Waves per SIMD the one-wave kernel is held to: with all its waves resident
 // in one round up to 8192 tokens, a ninth VGPR block would leave a second
 // round.  Rows of up to four vectors per lane fit 64 VGPRs without spilling,
@@ -402,17 +409,18 @@ constexpr int dual_min_waves(int nvq, int nvkv, int mode) {
 template <int NVQ, int NVKV, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(kBlock)
     __attribute__((amdgpu_waves_per_eu(dual_min_waves(NVQ, NVKV, kMode))))
-    dual_rmsnorm_quant_kernel(int64_t T, int Hq, int Hkv, const uint16_t* __restrict__ q,
-                              int64_t q_stride, const uint16_t* __restrict__ kv,
-                              int64_t kv_stride, const uint16_t* __restrict__ q_w,
+    dual_rmsnorm_quant_kernel(int64_t T, const uint16_t* __restrict__ q, int64_t q_stride,
+                              const uint16_t* __restrict__ kv, int64_t kv_stride,
+                              const uint16_t* __restrict__ q_w,
                               const uint16_t* __restrict__ kv_w, float eps_q, float eps_kv,
                               void* __restrict__ q_out, int64_t q_out_stride,
                               float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
-                              int64_t kv_out_stride, double inv_hq, double inv_hkv) {
+                              int64_t kv_out_stride, int Hq, int Hkv, double inv_hq,
+                              double inv_hkv) {
   const int rl = lane_id();
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
   if (row >= T) return;
-  const int nq = Hq >> 3, nkv = Hkv >> 3;
+  const int nq = kFull ? NVQ * kWave : Hq >> 3, nkv = kFull ? NVKV * kWave : Hkv >> 3;
 
   // Every load of the token is issued before either row is touched, kv's
   // first (in-order returns then let kv's products start while q's vectors
@@ -423,6 +431,8 @@ __global__ void __launch_bounds__(kBlock)
   load_row<NVKV, false, kFull>(wkv, kv_w, nkv, rl, kWave, true);
   load_row<NVQ, true, kFull>(zq, q + row * q_stride, nq, rl, kWave, true);
   load_row<NVQ, false, kFull>(wq, q_w, nq, rl, kWave, true);
+  args_ready(eps_q, eps_kv, q_out, q_out_stride, q_scales, kv_out, kv_out_stride);
+  if constexpr (!kFull) args_ready(Hq, Hkv, inv_hq, inv_hkv);
 
   RowT<NVKV> tkv;
   RowT<NVQ> tq;
@@ -462,7 +472,7 @@ __global__ void __launch_bounds__(kBlock)
     rmsnorm_emit<NVQ, kMode, kFull>(tq, rho_q, nq, rl, kWave, 0.0f,
                                     static_cast<uint16_t*>(q_out) + row * q_out_stride);
   } else {
-    float* scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
+    float* scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (nq * 8 / kGroup);
     dyn_emit<NVQ, kMode, kGroup, kFull, kBr>(tq, dc, rho_q, nq, rl, kWave,
                                         static_cast<uint8_t*>(q_out) + row * q_out_stride,
                                         scale_row);
@@ -477,13 +487,14 @@ __global__ void __launch_bounds__(kBlock)
 // per-token scales, the q amax), combined in a fixed order.
 template <int NVQ, int NVKV, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__((NVQ + NVKV) * kWave)
-    dual_rmsnorm_split_kernel(int64_t T, int Hq, int Hkv, const uint16_t* __restrict__ q,
-                              int64_t q_stride, const uint16_t* __restrict__ kv,
-                              int64_t kv_stride, const uint16_t* __restrict__ q_w,
+    dual_rmsnorm_split_kernel(int64_t T, const uint16_t* __restrict__ q, int64_t q_stride,
+                              const uint16_t* __restrict__ kv, int64_t kv_stride,
+                              const uint16_t* __restrict__ q_w,
                               const uint16_t* __restrict__ kv_w, float eps_q, float eps_kv,
                               void* __restrict__ q_out, int64_t q_out_stride,
                               float* __restrict__ q_scales, uint16_t* __restrict__ kv_out,
-                              int64_t kv_out_stride, double inv_hq, double inv_hkv) {
+                              int64_t kv_out_stride, int Hq, int Hkv, double inv_hq,
+                              double inv_hkv) {
   constexpr int kW = NVQ + NVKV;
   __shared__ double lds_ss[kW];
   __shared__ float lds_m[kW];
@@ -491,12 +502,15 @@ __global__ void __launch_bounds__((NVQ + NVKV) * kWave)
   const int64_t row = blockIdx.x;  // the grid has exactly T workgroups
   const bool is_q = wave < NVQ;    // wave-uniform
   const int rl = (is_q ? wave : wave - NVQ) * kWave + lane;  // this lane's vector of its row
-  const int nvec = is_q ? (Hq >> 3) : (Hkv >> 3);
+  const int nq = kFull ? NVQ * kWave : Hq >> 3, nkv = kFull ? NVKV * kWave : Hkv >> 3;
+  const int nvec = is_q ? nq : nkv;
 
   RowVecs<1> z, w;
   load_row<1, true, kFull>(z, is_q ? q + row * q_stride : kv + row * kv_stride, nvec, rl, kWave,
                            true);
   load_row<1, false, kFull>(w, is_q ? q_w : kv_w, nvec, rl, kWave, true);
+  args_ready(eps_q, eps_kv, q_out, q_out_stride, q_scales, kv_out, kv_out_stride);
+  if constexpr (!kFull) args_ready(inv_hq, inv_hkv);
   RowT<1> t;
   double ss;
   float m;
@@ -538,7 +552,7 @@ __global__ void __launch_bounds__((NVQ + NVKV) * kWave)
     rmsnorm_emit<1, kMode, kFull>(t, rho, nvec, rl, kWave, 0.0f,
                                   static_cast<uint16_t*>(q_out) + row * q_out_stride);
   } else {
-    float* scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (Hq / kGroup);
+    float* scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (nq * 8 / kGroup);
     dyn_emit<1, kMode, kGroup, kFull, true>(t, dc, rho, nvec, rl, kWave,
                                       static_cast<uint8_t*>(q_out) + row * q_out_stride,
                                       scale_row);
@@ -570,8 +584,8 @@ struct NormLaunch {
 template <int N, int W, bool kResidual, bool kFull, int kMode, int kGroup>
 static void launch_norm_quant(const NormLaunch& a) {
   hipLaunchKernelGGL((add_rmsnorm_quant_kernel<N, W, kResidual, kMode, kGroup, kFull>), a.grid,
-                     dim3(norm_block_waves(W) * kWave), 0, a.st, a.x, a.xs, a.res, a.rs, a.w, a.eps, a.sscale,
-                     static_cast<uint8_t*>(a.out), a.os, a.scales, a.T, a.H,
+                     dim3(norm_block_waves(W) * kWave), 0, a.st, a.x, a.xs, a.res, a.rs, a.w,
+                     a.T, a.eps, a.sscale, static_cast<uint8_t*>(a.out), a.os, a.scales, a.H,
                      1.0 / static_cast<double>(a.H));
 }
 
@@ -579,8 +593,8 @@ template <int N, int W, bool kResidual, bool kFull, typename E>
 static void launch_norm_pad(const NormLaunch& a) {
   hipLaunchKernelGGL((add_rmsnorm_pad_kernel<N, W, kResidual, kFull, E>), a.grid,
                      dim3(norm_block_waves(W) * kWave), 0, a.st,
-                     a.x, a.xs, a.res, a.rs, a.w, a.eps, static_cast<uint16_t*>(a.out), a.os,
-                     a.T, a.H, a.H_pad, 1.0 / static_cast<double>(a.H));
+                     a.x, a.xs, a.res, a.rs, a.w, a.T, a.eps, static_cast<uint16_t*>(a.out),
+                     a.os, a.H, a.H_pad, 1.0 / static_cast<double>(a.H));
 }
 
 // One (vectors per lane, waves per row) case: mode NONE launches the padding
@@ -697,16 +711,16 @@ template <int A, int B, bool kFull, int kMode, int kGroup>
 static void launch_dual(const DualLaunch& a) {
   if (a.T <= kDualSplitMaxT) {
     hipLaunchKernelGGL((dual_rmsnorm_split_kernel<A, B, kMode, kGroup, kFull>),
-                       dim3(static_cast<unsigned>(a.T)), dim3((A + B) * kWave), 0, a.st, a.T, a.Hq,
-                       a.Hkv, a.q, a.qs, a.kv, a.kvs, a.qw, a.kvw, a.eps_q, a.eps_kv, a.q_out,
-                       a.qos, a.q_scales, a.kv_out, a.kvos, 1.0 / static_cast<double>(a.Hq),
-                       1.0 / static_cast<double>(a.Hkv));
+                       dim3(static_cast<unsigned>(a.T)), dim3((A + B) * kWave), 0, a.st, a.T,
+                       a.q, a.qs, a.kv, a.kvs, a.qw, a.kvw, a.eps_q, a.eps_kv, a.q_out, a.qos,
+                       a.q_scales, a.kv_out, a.kvos, a.Hq, a.Hkv,
+                       1.0 / static_cast<double>(a.Hq), 1.0 / static_cast<double>(a.Hkv));
     return;
   }
   hipLaunchKernelGGL((dual_rmsnorm_quant_kernel<A, B, kMode, kGroup, kFull>), a.grid,
                      dim3(kBlock), 0,
-                     a.st, a.T, a.Hq, a.Hkv, a.q, a.qs, a.kv, a.kvs, a.qw, a.kvw, a.eps_q,
-                     a.eps_kv, a.q_out, a.qos, a.q_scales, a.kv_out, a.kvos,
+                     a.st, a.T, a.q, a.qs, a.kv, a.kvs, a.qw, a.kvw, a.eps_q, a.eps_kv,
+                     a.q_out, a.qos, a.q_scales, a.kv_out, a.kvos, a.Hq, a.Hkv,
                      1.0 / static_cast<double>(a.Hq), 1.0 / static_cast<double>(a.Hkv));
 }
 

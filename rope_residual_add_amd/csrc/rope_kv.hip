@@ -43,6 +43,7 @@ namespace rra {
 
 constexpr int kRopeMaxWaves = 32;                 // waves per token at most
 constexpr int kRopeMaxHeads = 1 << 16;            // head counts accepted (unit indices fit int)
+constexpr int64_t kRopeMaxStride8 = 0xFFFFFFFF;   // rope_kv_write: q, k token strides / 8
 constexpr int kRopeMaxUnitsPerPass = 4;           // units a lane loads before storing
 
 // Most units per lane and pass: 4 two-vector (NeoX) or 8 one-vector (GPT-J)
@@ -178,17 +179,25 @@ __device__ __forceinline__ float group_sum(float v) {
 // before the table row and the slot arrive.  Each lane reads a q unit before
 // writing it back, so q_out may alias q.  E is the element type of q, k, v and
 // the caches (bf16 or fp16).
+// The token's position and slot head the kernel's longest chains (the
+// position, then its table row; the slot, then every cache store), so their
+// loads leave first, ahead of the row loads, and the arguments they and the
+// row loads need fill the 14 argument dwords a wave starts with in registers:
+// the divider without its shift (fast_div_of), the head counts packed as
+// (Hq - 1) | (Hkv - 1) << 16, and the q and k token strides in units of 8
+// elements.  The remaining arguments are fetched while the row loads leave.
 template <int D, bool kNeox, int kU, typename E>
 __global__ void __launch_bounds__(kBlock)
-    rope_kv_write_kernel(uint32_t tw_d, uint32_t tw_magic, uint32_t tw_shift, uint32_t T, int Hq,
-                         int Hkv, const uint16_t* q, int64_t q_stride,
-                         const uint16_t* __restrict__ k, int64_t k_stride,
-                         const uint16_t* __restrict__ v, int64_t v_stride, uint16_t* q_out,
-                         int64_t q_out_stride, const int64_t* __restrict__ positions,
-                         const float* __restrict__ cos_sin,
-                         const int64_t* __restrict__ slot_mapping,
+    rope_kv_write_kernel(uint32_t tw_d, uint32_t tw_magic, uint32_t T, uint32_t heads,
+                         const int64_t* __restrict__ positions,
+                         const int64_t* __restrict__ slot_mapping, const uint16_t* q,
+                         const uint16_t* __restrict__ k, uint32_t q_stride8, uint32_t k_stride8,
+                         const float* __restrict__ cos_sin, const uint16_t* __restrict__ v,
+                         int64_t v_stride, uint16_t* q_out, int64_t q_out_stride,
                          uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache) {
-  const FastDiv tw{tw_d, tw_magic, tw_shift};
+  const FastDiv tw = fast_div_of(tw_d, tw_magic);
+  const int Hq = static_cast<int>(heads & 0xFFFFu) + 1, Hkv = static_cast<int>(heads >> 16) + 1;
+  const int64_t q_stride = int64_t(q_stride8) * 8, k_stride = int64_t(k_stride8) * 8;
   using U = RotUnit<D, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
@@ -196,6 +205,11 @@ __global__ void __launch_bounds__(kBlock)
   int rl;
   token_lane(tw, T, t, rl);
   if (t >= T) return;  // whole waves; no barrier in this kernel
+  const int64_t pos = positions[t];
+  const int64_t slot = slot_mapping[t];
+  // A compiler barrier (no instruction) keeps both loads above the row loads;
+  // without it they are placed next to their first use.
+  asm volatile("" ::: "memory");
   const int lanes = static_cast<int>(tw.d) * kWave;
 
   const int c = rl % kUnitsPerHead;
@@ -204,9 +218,7 @@ __global__ void __launch_bounds__(kBlock)
   const int ukv = Hkv * kUnitsPerHead;
   const int total = uq + 2 * ukv;
   const uint16_t* qt = q + t * q_stride;
-  uint16_t* qo = q_out + t * q_out_stride;
   const uint16_t* kt = k + t * k_stride;
-  const uint16_t* vt = v + t * v_stride;
 
   float cs[8], sn[8];
   for (int u0 = 0; u0 < total; u0 += kU * lanes) {
@@ -222,6 +234,11 @@ __global__ void __launch_bounds__(kBlock)
         if (kNeox) hi[j] = ld_stream(p + hi_off);
       }
     }
+    // The other arguments, fetched while the row loads leave, then the table
+    // row and v.
+    args_ready(cos_sin, v, v_stride, q_out, q_out_stride, key_cache, value_cache);
+    if (u0 == 0) unit_cos_sin<D, kNeox>(cos_sin + pos * D, c, cs, sn);
+    const uint16_t* vt = v + t * v_stride;
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
       const int u = u0 + j * lanes + rl;
@@ -231,11 +248,10 @@ __global__ void __launch_bounds__(kBlock)
         if (kNeox) hi[j] = ld_stream(p + hi_off);
       }
     }
-    if (u0 == 0) unit_cos_sin<D, kNeox>(cos_sin + positions[t] * D, c, cs, sn);
-    const int64_t slot = slot_mapping[t];
     // The cache is [num_blocks, block_size, Hkv, D] and contiguous, so slot
     // block * block_size + offset starts at element slot * Hkv * D.
     const int64_t cache_row = (slot >= 0 ? slot : 0) * Hkv * D;
+    uint16_t* qo = q_out + t * q_out_stride;
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
       const int u = u0 + j * lanes + rl;
@@ -587,6 +603,9 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   RRA_REQUIRE(aligned(key_cache, 16) && aligned(value_cache, 16) && aligned(cos_sin, 16),
               RRA_ERR_ALIGN);
   RRA_REQUIRE(aligned(positions, 8) && aligned(slot_mapping, 8), RRA_ERR_ALIGN);
+  // The kernel takes the q and k token strides as 32-bit counts of 8 elements.
+  RRA_REQUIRE(q_stride / 8 <= kRopeMaxStride8 && k_stride / 8 <= kRopeMaxStride8,
+              RRA_ERR_UNSUPPORTED);
   if (T == 0) return RRA_OK;
   const hipStream_t st = as_stream(stream);
   const RopeLaunch shape =
@@ -595,13 +614,16 @@ extern "C" int rope_kv_write(const int64_t* positions, const uint16_t* q, int64_
   RRA_REQUIRE(blocks > 0, RRA_ERR_UNSUPPORTED);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
   const uint32_t T32 = static_cast<uint32_t>(T);  // below 2^31: rope_blocks refuses larger T
+  const uint32_t heads = static_cast<uint32_t>(Hq - 1) | static_cast<uint32_t>(Hkv - 1) << 16;
+  const uint32_t q_stride8 = static_cast<uint32_t>(q_stride / 8);
+  const uint32_t k_stride8 = static_cast<uint32_t>(k_stride / 8);
 #define RRA_ROPE_CASE(DD, NEOX, DT, EL)                                                        \
   if (D == DD && is_neox == NEOX && dtype == DT) {                                             \
     with_units_per_pass<rope_max_units(NEOX)>(shape.ku, [&](auto units) {                      \
       hipLaunchKernelGGL((rope_kv_write_kernel<DD, NEOX, decltype(units)::value, EL>), grid,   \
-                         block, 0, st, shape.tw.d, shape.tw.magic, shape.tw.shift, T32, Hq,    \
-                         Hkv, q, q_stride, k, k_stride, v, v_stride, q_out, q_out_stride,      \
-                         positions, cos_sin, slot_mapping, key_cache, value_cache);            \
+                         block, 0, st, shape.tw.d, shape.tw.magic, T32, heads, positions,      \
+                         slot_mapping, q, k, q_stride8, k_stride8, cos_sin, v, v_stride,       \
+                         q_out, q_out_stride, key_cache, value_cache);                         \
     });                                                                                        \
     return launch_status();                                                                    \
   }

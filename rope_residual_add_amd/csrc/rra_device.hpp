@@ -36,6 +36,13 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
   return static_cast<uint32_t>((static_cast<uint64_t>(n) * f.magic) >> f.shift);
 }
 
+// The same constants with the shift, 31 + ceil(log2 d), recomputed from d (for
+// kernels whose first argument words are too precious to carry it).
+__device__ __forceinline__ FastDiv fast_div_of(uint32_t d, uint32_t magic) {
+  const uint32_t l = d > 1u ? 32u - static_cast<uint32_t>(__clz(d - 1u)) : 0u;
+  return FastDiv{d, magic, 31u + l};
+}
+
 // Workgroups are dispatched to the 8 XCDs (each with its own L2) in turn:
 // workgroup x runs on XCD x % 8.  xcd_block() renumbers them so that runs of
 // kXcdRun consecutive numbers share an XCD while the runs still go round the
@@ -460,6 +467,23 @@ __device__ __forceinline__ int wave_id() {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Kernel arguments: gfx950 starts a wave with the first 14 dwords of its
+// arguments in scalar registers (with the library's preload build flag); the
+// rest are fetched by scalar loads, which the compiler issues where a value is
+// first used, so an argument first used by a kernel's last stores costs a
+// memory round trip at the end of the wave's chain.  args_ready(a, ...) makes
+// the arguments resident at the point of the call: placed right after a
+// kernel's first vector loads are issued, their fetch runs under those loads.
+template <typename V>
+__device__ __forceinline__ void arg_ready(V v) {
+  asm volatile("" ::"s"(v));
+}
+
+template <typename... A>
+__device__ __forceinline__ void args_ready(A... a) {
+  (arg_ready(a), ...);
+}
 
 // Dynamic scale from an amax given as m * rho (m >= 0 exact in fp32, rho in
 // double): s = fp32(m * rho / 448), 448 being e4m3fn's largest finite value,

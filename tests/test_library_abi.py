@@ -54,7 +54,7 @@ def test_library_exports_every_declared_function(rra):
 
 
 def test_version_and_status_strings(rra):
-    assert rra.abi_version() == rra.ABI_VERSION == 5
+    assert rra.abi_version() == rra.ABI_VERSION == 6
     for s in (OK, ENULL, ESHAPE, EALIGN, EUNSUP, -5):
         assert rra.status_string(s) and rra.status_string(s) != "unknown status"
     assert rra.status_string(-99) == "unknown status"
@@ -143,6 +143,9 @@ def test_rope_validation(rra):
     assert f(kc=A + 2) == EALIGN
     assert f(pos=A + 4) == EALIGN
     assert f(bs=0) == ESHAPE
+    # the kernel carries the q and k token strides as 32-bit counts of 8 elements
+    assert f(qs=8 << 32, T=0) == EUNSUP and f(ks=8 << 32, T=0) == EUNSUP
+    assert f(qs=(8 << 32) - 8, ks=(8 << 32) - 8, T=0) == OK
     # six waves per token at this shape (384 units, one per lane): a launch of
     # 2^31 waves or more is refused before anything is enqueued
     assert f(T=(1 << 31) // 6 + 1) == EUNSUP
