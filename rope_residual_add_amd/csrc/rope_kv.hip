@@ -43,7 +43,7 @@ namespace rra {
 
 constexpr int kRopeMaxWaves = 32;                 // waves per token at most
 constexpr int kRopeMaxHeads = 1 << 16;            // head counts accepted (unit indices fit int)
-constexpr int64_t kRopeMaxStride8 = 0xFFFFFFFF;   // rope_kv_write: q, k token strides / 8
+constexpr int64_t kRopeMaxStride8 = 0xFFFFFFFF;   // token strides / 8 passed as 32 bits
 constexpr int kRopeMaxUnitsPerPass = 4;           // units a lane loads before storing
 
 // Most units per lane and pass: 4 two-vector (NeoX) or 8 one-vector (GPT-J)
@@ -281,19 +281,24 @@ __global__ void __launch_bounds__(kBlock)
 // when there is a cache.  A head's units sit on consecutive lanes of one wave,
 // so its sum of squares is a DPP group sum; every lane runs the group sums
 // (lanes without a q or k unit add zeros).  As in rope_kv_write_kernel the
-// loads leave before the position, slot and weights are needed.  The norm and
-// the rotation are applied in fp32 and rounded once to bf16.
+// loads leave before the position, slot and weights are needed, the position
+// and slot loads leave first, and the first 14 argument dwords hold what those
+// loads need (the divider without its shift, the head counts packed as
+// (Hq - 1) | (Hkv - 1) << 16, the position and slot pointers, the row, its
+// stride, eps and write_k).  The norm and the rotation are applied in fp32 and
+// rounded once to bf16.
 template <int D, bool kNeox, int kU>
 __global__ void __launch_bounds__(kBlock)
-    qk_norm_rope_kv_kernel(uint32_t tw_d, uint32_t tw_magic, uint32_t tw_shift, uint32_t T,
-                           int Hq, int Hkv, uint16_t* qkv, int64_t qkv_stride, int write_k,
-                           float eps, const uint16_t* __restrict__ q_weight,
-                           const uint16_t* __restrict__ k_weight,
+    qk_norm_rope_kv_kernel(uint32_t tw_d, uint32_t tw_magic, uint32_t T, uint32_t heads,
                            const int64_t* __restrict__ positions,
-                           const float* __restrict__ cos_sin,
-                           const int64_t* __restrict__ slot_mapping,
-                           uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache) {
-  const FastDiv tw{tw_d, tw_magic, tw_shift};
+                           const int64_t* __restrict__ slot_mapping, uint16_t* qkv,
+                           int64_t qkv_stride, float eps, int write_k,
+                           const uint16_t* __restrict__ q_weight,
+                           const uint16_t* __restrict__ k_weight,
+                           const float* __restrict__ cos_sin, uint16_t* __restrict__ key_cache,
+                           uint16_t* __restrict__ value_cache) {
+  const FastDiv tw = fast_div_of(tw_d, tw_magic);
+  const int Hq = static_cast<int>(heads & 0xFFFFu) + 1, Hkv = static_cast<int>(heads >> 16) + 1;
   using U = RotUnit<D, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   constexpr int kVals = kNeox ? 16 : 8;  // values of a rotation unit
@@ -302,9 +307,13 @@ __global__ void __launch_bounds__(kBlock)
   int rl;
   token_lane(tw, T, t, rl);
   if (t >= T) return;  // whole waves; no barrier in this kernel
+  const bool cached = slot_mapping != nullptr;
+  const int64_t pos = positions[t];
+  const int64_t slot = cached ? slot_mapping[t] : -1;
+  // A compiler barrier (no instruction) keeps both loads above the row loads.
+  asm volatile("" ::: "memory");
   const int lanes = static_cast<int>(tw.d) * kWave;
 
-  const bool cached = slot_mapping != nullptr;
   const int c = rl % kUnitsPerHead;
   const int lo_off = U::lo(c), hi_off = lo_off + U::kHi;
   const int uq = Hq * kUnitsPerHead;
@@ -332,8 +341,12 @@ __global__ void __launch_bounds__(kBlock)
       lo[j] = ld_stream(p + lo_off);
       if (kNeox) hi[j] = ld_stream(p + hi_off);
     }
+    // The remaining arguments, fetched under the row loads (the scheduling
+    // barrier keeps the loads above the wait).
+    __builtin_amdgcn_sched_barrier(0);
+    args_ready(q_weight, k_weight, cos_sin, key_cache, value_cache);
     if (u0 == 0) {
-      unit_cos_sin<D, kNeox>(cos_sin + positions[t] * D, c, cs, sn);
+      unit_cos_sin<D, kNeox>(cos_sin + pos * D, c, cs, sn);
       const uint16_t* w0 = (kU == 1 && rl >= uq) ? k_weight : q_weight;
       wq[0] = ld_cached(w0 + lo_off);
       if (kNeox) wq[1] = ld_cached(w0 + hi_off);
@@ -342,7 +355,6 @@ __global__ void __launch_bounds__(kBlock)
         if (kNeox) wk[1] = ld_cached(k_weight + hi_off);
       }
     }
-    const int64_t slot = cached ? slot_mapping[t] : -1;
     const int64_t cache_row = (slot >= 0 ? slot : 0) * Hkv * D;
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
@@ -428,16 +440,21 @@ __global__ void __launch_bounds__(kBlock)
 // kv_lora + R].  As in rope_kv_write_kernel the loads depend on t alone: they
 // leave before the position and slot are needed (a padding token's k_pe and
 // kv_c are read but not stored; a lane past the last unit re-reads the
-// token's first kv_c vector).
+// token's first kv_c vector), the position and slot loads leave first, and the
+// first 14 argument dwords hold what those loads and q_pe's need (the divider
+// without its shift, the position and slot pointers, q_pe and its token and
+// head strides in units of 8 elements).
 template <int R, bool kNeox, int kU>
 __global__ void __launch_bounds__(kBlock)
-    mla_rope_kv_kernel(uint32_t tw_d, uint32_t tw_magic, uint32_t tw_shift, uint32_t T, int Hq,
-                       int kv_lora, uint16_t* q_pe, int64_t q_stride, int64_t q_head_stride,
+    mla_rope_kv_kernel(uint32_t tw_d, uint32_t tw_magic, uint32_t T, int Hq, int kv_lora,
+                       const int64_t* __restrict__ positions,
+                       const int64_t* __restrict__ slot_mapping, uint16_t* q_pe,
+                       uint32_t q_stride8, uint32_t q_head_stride8,
                        const uint16_t* __restrict__ k_pe, int64_t k_pe_stride,
                        const uint16_t* __restrict__ kv_c, int64_t kv_c_stride,
-                       const int64_t* __restrict__ positions, const float* __restrict__ cos_sin,
-                       const int64_t* __restrict__ slot_mapping, uint16_t* __restrict__ kv_cache) {
-  const FastDiv tw{tw_d, tw_magic, tw_shift};
+                       const float* __restrict__ cos_sin, uint16_t* __restrict__ kv_cache) {
+  const FastDiv tw = fast_div_of(tw_d, tw_magic);
+  const int64_t q_stride = int64_t(q_stride8) * 8, q_head_stride = int64_t(q_head_stride8) * 8;
   using U = RotUnit<R, kNeox>;
   constexpr int kUnitsPerHead = U::kPerHead;
   static_assert(kWave % kUnitsPerHead == 0, "a lane must keep one column");
@@ -445,6 +462,10 @@ __global__ void __launch_bounds__(kBlock)
   int rl;
   token_lane(tw, T, t, rl);
   if (t >= T) return;  // whole waves; no barrier in this kernel
+  const int64_t pos = positions[t];
+  const int64_t slot = slot_mapping[t];
+  // A compiler barrier (no instruction) keeps both loads above the row loads.
+  asm volatile("" ::: "memory");
   const int lanes = static_cast<int>(tw.d) * kWave;
 
   const int c = rl % kUnitsPerHead;
@@ -453,8 +474,6 @@ __global__ void __launch_bounds__(kBlock)
   const int ur = uq + kUnitsPerHead;  // rotation units (q_pe and k_pe)
   const int total = ur + kv_lora / 8;
   uint16_t* qt = q_pe + t * q_stride;
-  const uint16_t* kt = k_pe + t * k_pe_stride;
-  const uint16_t* ct = kv_c + t * kv_c_stride;
 
   float cs[8], sn[8];
   for (int u0 = 0; u0 < total; u0 += kU * lanes) {
@@ -469,6 +488,14 @@ __global__ void __launch_bounds__(kBlock)
         if (kNeox) hi[j] = ld_stream(p + hi_off);
       }
     }
+    // The remaining arguments, fetched under the q_pe loads (the scheduling
+    // barrier keeps those loads above the wait), then the table row, k_pe and
+    // kv_c.
+    __builtin_amdgcn_sched_barrier(0);
+    args_ready(k_pe, k_pe_stride, kv_c, kv_c_stride, cos_sin, kv_cache);
+    if (u0 == 0) unit_cos_sin<R, kNeox>(cos_sin + pos * R, c, cs, sn);
+    const uint16_t* kt = k_pe + t * k_pe_stride;
+    const uint16_t* ct = kv_c + t * kv_c_stride;
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
       const int u = u0 + j * lanes + rl;
@@ -486,8 +513,6 @@ __global__ void __launch_bounds__(kBlock)
         if (kNeox) hi[j] = ld_stream(ph);
       }
     }
-    if (u0 == 0) unit_cos_sin<R, kNeox>(cos_sin + positions[t] * R, c, cs, sn);
-    const int64_t slot = slot_mapping[t];
     uint16_t* dst = kv_cache + (slot >= 0 ? slot : 0) * static_cast<int64_t>(kv_lora + R);
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
@@ -678,13 +703,14 @@ extern "C" int qk_norm_rope_kv_write(const int64_t* positions, uint16_t* qkv, in
   RRA_REQUIRE(blocks > 0, RRA_ERR_UNSUPPORTED);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
   const uint32_t T32 = static_cast<uint32_t>(T);  // below 2^31: rope_blocks refuses larger T
+  const uint32_t heads = static_cast<uint32_t>(Hq - 1) | static_cast<uint32_t>(Hkv - 1) << 16;
 #define RRA_QKN_CASE(DD, NEOX)                                                                 \
   if (D == DD && is_neox == NEOX) {                                                            \
     with_units_per_pass<rope_max_units(NEOX)>(shape.ku, [&](auto units) {                      \
       hipLaunchKernelGGL((qk_norm_rope_kv_kernel<DD, NEOX, decltype(units)::value>), grid,     \
-                         block, 0, st, shape.tw.d, shape.tw.magic, shape.tw.shift, T32, Hq,    \
-                         Hkv, qkv, qkv_stride, write_k, eps, q_weight, k_weight, positions,    \
-                         cos_sin, slot_mapping, key_cache, value_cache);                       \
+                         block, 0, st, shape.tw.d, shape.tw.magic, T32, heads, positions,      \
+                         slot_mapping, qkv, qkv_stride, eps, write_k, q_weight, k_weight,      \
+                         cos_sin, key_cache, value_cache);                                     \
     });                                                                                        \
     return launch_status();                                                                    \
   }
@@ -724,6 +750,9 @@ extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64
   RRA_REQUIRE(aligned(kv_cache, 16) && aligned(cos_sin, 16) && aligned(positions, 8) &&
                   aligned(slot_mapping, 8),
               RRA_ERR_ALIGN);
+  // The kernel takes the q_pe strides as 32-bit counts of 8 elements
+  // (q_head_stride < q_stride).
+  RRA_REQUIRE(q_stride / 8 <= kRopeMaxStride8, RRA_ERR_UNSUPPORTED);
   if (T == 0) return RRA_OK;
   const hipStream_t st = as_stream(stream);
   const RopeLaunch shape = rope_launch(
@@ -732,13 +761,15 @@ extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64
   RRA_REQUIRE(blocks > 0, RRA_ERR_UNSUPPORTED);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
   const uint32_t T32 = static_cast<uint32_t>(T);  // below 2^31: rope_blocks refuses larger T
+  const uint32_t q_stride8 = static_cast<uint32_t>(q_stride / 8);
+  const uint32_t q_head_stride8 = static_cast<uint32_t>(q_head_stride / 8);
 #define RRA_MLA_CASE(RR, NEOX)                                                                 \
   if (rope_dim == RR && is_neox == NEOX) {                                                     \
     with_units_per_pass<rope_max_units(NEOX)>(shape.ku, [&](auto units) {                      \
       hipLaunchKernelGGL((mla_rope_kv_kernel<RR, NEOX, decltype(units)::value>), grid, block,  \
-                         0, st, shape.tw.d, shape.tw.magic, shape.tw.shift, T32, Hq, kv_lora,  \
-                         q_pe, q_stride, q_head_stride, k_pe, k_pe_stride, kv_c, kv_c_stride,  \
-                         positions, cos_sin, slot_mapping, kv_cache);                          \
+                         0, st, shape.tw.d, shape.tw.magic, T32, Hq, kv_lora, positions,       \
+                         slot_mapping, q_pe, q_stride8, q_head_stride8, k_pe, k_pe_stride,     \
+                         kv_c, kv_c_stride, cos_sin, kv_cache);                                \
     });                                                                                        \
     return launch_status();                                                                    \
   }

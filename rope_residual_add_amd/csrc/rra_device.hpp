@@ -475,6 +475,9 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 // memory round trip at the end of the wave's chain.  args_ready(a, ...) makes
 // the arguments resident at the point of the call: placed right after a
 // kernel's first vector loads are issued, their fetch runs under those loads.
+// The scheduler may still move ordinary loads across it; where it would hoist
+// the wait above them, a __builtin_amdgcn_sched_barrier(0) before the call
+// keeps the loads first.
 template <typename V>
 __device__ __forceinline__ void arg_ready(V v) {
   asm volatile("" ::"s"(v));

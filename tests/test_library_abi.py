@@ -258,6 +258,9 @@ def test_mla_rope_validation(rra):
     assert f(hs=1 << 62) == ESHAPE  # (Hq - 1) * head stride past the row, without overflow
     assert f(hs=196, qs=25088) == EALIGN  # head stride not a multiple of 8
     assert f(kv=A + 4) == EALIGN
+    # the kernel carries the q_pe strides as 32-bit counts of 8 elements
+    assert f(qs=8 << 32, T=0) == EUNSUP
+    assert f(qs=(8 << 32) - 8, T=0) == OK
 
 
 def test_e4m3_diag_validation(rra):
