@@ -127,6 +127,15 @@ def test_qknorm_multi_pass_tokens(rra, oracle, neox):
     run_qknorm(rra, oracle, 5, cfg, is_neox=neox, write_k=True, pad_every=3)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(65536, 1), (1, 65536)])
+def test_qknorm_largest_head_counts(rra, oracle, Hq, Hkv):
+    """Head counts of 65536, the most the entry point takes (packed for the
+    kernel as (Hq - 1) | (Hkv - 1) << 16), with a cache and k written back."""
+    cfg = dataclasses.replace(workloads.QKNORM, Hq=Hq, Hkv=Hkv, D=64, num_blocks=1, block_size=4,
+                              max_pos=4096)
+    run_qknorm(rra, oracle, 3, cfg, cache=True, write_k=True, pad_every=3)
+
+
 def test_qknorm_empty(rra):
     import torch
 

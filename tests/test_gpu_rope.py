@@ -177,6 +177,16 @@ def test_multi_pass_tokens(rra, oracle, neox):
     run(rra, oracle, 6, cfg, pad_every=4)
 
 
+@pytest.mark.parametrize("Hq,Hkv,neox", [(65536, 1, True), (65536, 1, False), (1, 65536, True)])
+def test_largest_head_counts(rra, oracle, Hq, Hkv, neox):
+    """The largest head counts the entry point takes, which the kernel receives
+    packed as (Hq - 1) | (Hkv - 1) << 16: 65536 heads of 64 fill both 16-bit
+    fields and give each lane many passes at the most units per pass."""
+    cfg = dataclasses.replace(workloads.ROPE, Hq=Hq, Hkv=Hkv, D=64, rot_dim=64, is_neox=neox,
+                              num_blocks=1, block_size=4, max_pos=4096)
+    run(rra, oracle, 3, cfg, pad_every=3)
+
+
 def test_position_zero_is_identity(rra):
     """At position 0 the rotation is the identity: q_out == q, cache == k."""
     import torch
