@@ -356,7 +356,9 @@ __device__ __forceinline__ void add_rmsnorm_body(const uint16_t* __restrict__ x,
 }
 
 // Two entry kernels over the same body, so that profiles tell the quantizing
-// op from the padding op.
+// op from the padding op.  The rows, the weight, T (which bounds the row loads
+// when a workgroup holds several rows) and eps are the first 14 argument
+// dwords, which a wave starts with in registers.
 template <int NV, int kW, bool kResidual, int kMode, int kGroup, bool kFull>
 __global__ void __launch_bounds__(norm_block_waves(kW) * kWave)
     add_rmsnorm_quant_kernel(const uint16_t* __restrict__ x, int64_t x_stride,
@@ -472,7 +474,8 @@ __global__ void __launch_bounds__(kBlock)
     rmsnorm_emit<NVQ, kMode, kFull>(tq, rho_q, nq, rl, kWave, 0.0f,
                                     static_cast<uint16_t*>(q_out) + row * q_out_stride);
   } else {
-    float* scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (nq * 8 / kGroup);
+    float* scale_row =
+        kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (nq * 8 / kGroup);
     dyn_emit<NVQ, kMode, kGroup, kFull, kBr>(tq, dc, rho_q, nq, rl, kWave,
                                         static_cast<uint8_t*>(q_out) + row * q_out_stride,
                                         scale_row);
@@ -552,7 +555,8 @@ __global__ void __launch_bounds__((NVQ + NVKV) * kWave)
     rmsnorm_emit<1, kMode, kFull>(t, rho, nvec, rl, kWave, 0.0f,
                                   static_cast<uint16_t*>(q_out) + row * q_out_stride);
   } else {
-    float* scale_row = kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (nq * 8 / kGroup);
+    float* scale_row =
+        kMode == RRA_Q_PER_TOKEN ? q_scales + row : q_scales + row * (nq * 8 / kGroup);
     dyn_emit<1, kMode, kGroup, kFull, true>(t, dc, rho, nvec, rl, kWave,
                                       static_cast<uint8_t*>(q_out) + row * q_out_stride,
                                       scale_row);
