@@ -307,7 +307,8 @@ int fused_add_rmsnorm_pad(const uint16_t* x, int64_t x_stride, uint16_t* residua
  * cos_sin   [max_pos, rope_dim] fp32 (see rope_cos_sin_cache).
  * kv_cache  [num_blocks, block_size, kv_lora + rope_dim] bf16, contiguous.
  * Limits: rope_dim in {64, 128}; kv_lora % 8 == 0, kv_lora <= 2^24;
- * q_head_stride % 8 == 0; q_stride below 2^35 elements; 1 <= Hq <= 65536;
+ * q_head_stride % 8 == 0; q_stride and q_head_stride below 2^35 elements;
+ * 1 <= Hq <= 65536;
  * is_neox 0 (GPT-J pairs, as DeepSeek) or 1.
  */
 int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64_t q_stride,

@@ -750,9 +750,9 @@ extern "C" int mla_rope_kv_write(const int64_t* positions, uint16_t* q_pe, int64
   RRA_REQUIRE(aligned(kv_cache, 16) && aligned(cos_sin, 16) && aligned(positions, 8) &&
                   aligned(slot_mapping, 8),
               RRA_ERR_ALIGN);
-  // The kernel takes the q_pe strides as 32-bit counts of 8 elements
-  // (q_head_stride < q_stride).
-  RRA_REQUIRE(q_stride / 8 <= kRopeMaxStride8, RRA_ERR_UNSUPPORTED);
+  // The kernel takes the q_pe strides as 32-bit counts of 8 elements.
+  RRA_REQUIRE(q_stride / 8 <= kRopeMaxStride8 && q_head_stride / 8 <= kRopeMaxStride8,
+              RRA_ERR_UNSUPPORTED);
   if (T == 0) return RRA_OK;
   const hipStream_t st = as_stream(stream);
   const RopeLaunch shape = rope_launch(

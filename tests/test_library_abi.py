@@ -261,6 +261,7 @@ def test_mla_rope_validation(rra):
     # the kernel carries the q_pe strides as 32-bit counts of 8 elements
     assert f(qs=8 << 32, T=0) == EUNSUP
     assert f(qs=(8 << 32) - 8, T=0) == OK
+    assert f(Hq=1, hs=8 << 32, T=0) == EUNSUP  # one head: its stride is otherwise unbounded
 
 
 def test_e4m3_diag_validation(rra):
