@@ -9,7 +9,9 @@ One step is one pass over the whole fused path at T tokens (default 8192):
   dual_rmsnorm_quant       MLA q (1536, per-group-128 FP8) / kv (512, bf16) RMSNorm (DeepSeek-V3)
 on seeded synthetic inputs already resident in HBM.  The step streams about
 1.1 GB, several times the 256 MB last-level cache, so every kernel starts on
-cold data.
+cold data.  The K timed steps follow --settle-ms of untimed steps and then the
+W warm-up steps, so that they run at the clocks the GPU holds under sustained
+load; "settle" also reports the same K steps timed straight after set-up.
 
 Bandwidth is counted in ALGORITHMIC bytes: each input read once and each
 output written once (per token: 7H + 4 for the norm, 5I + 4I/128 for SiLU,
@@ -485,12 +487,9 @@ def make_launchers(T: int, salt: int = 0, shared=None, only=KERNELS):
     return L
 
 
-def run_steps(launch, steps: int, warmup: int):
-    """Warm up, then time `steps` passes over the four kernels (launch: the
-    dict of make_launchers) twice: first with nothing between the launches,
-    for the whole step's wall time, then with HIP events around every launch,
-    queued behind a spin kernel, for each kernel's duration.  Returns
-    (wall seconds for the first timed steps, {kernel: [per-launch ms]})."""
+def _timed_pass(launch, steps: int, warmup: int) -> float:
+    """`warmup` untimed steps, then the wall time of `steps` steps, each timed
+    region bracketed by a device synchronization."""
     import torch
 
     for _ in range(warmup):
@@ -502,7 +501,41 @@ def run_steps(launch, steps: int, warmup: int):
         for n in KERNELS:
             launch[n]()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    return time.perf_counter() - t0
+
+
+def settle(launch, ms: float) -> int:
+    """Untimed steps until the GPU has run them for at least `ms` milliseconds.
+    An MI355X raises its clocks only under sustained load: the first ~10 ms of
+    steps after an idle spell run about 4% slower than the steady state.
+    Returns the number of steps run."""
+    import torch
+
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(20):
+            for k in KERNELS:
+                launch[k]()
+        n += 20
+        torch.cuda.synchronize()
+    return n
+
+
+def run_steps(launch, steps: int, warmup: int, settle_ms: float = 0.0):
+    """Time `steps` passes over the four kernels (launch: the dict of
+    make_launchers), three ways:
+      - from idle: `warmup` steps, then `steps` timed, straight after set-up;
+      - steady: untimed steps for `settle_ms` (settle), `warmup` steps, then
+        `steps` timed, for the whole step's wall time at loaded clocks;
+      - per kernel: HIP events around every launch, queued behind a spin
+        kernel, for each kernel's duration.
+    Returns (steady wall seconds, from-idle wall seconds, settle steps,
+    {kernel: [per-launch ms]})."""
+    import torch
+
+    idle_wall = _timed_pass(launch, steps, warmup)
+    settled = settle(launch, settle_ms) if settle_ms > 0 else 0
+    wall = _timed_pass(launch, steps, warmup)
 
     hip = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
@@ -525,7 +558,7 @@ def run_steps(launch, steps: int, warmup: int):
     per = {n: [hip.ms(ev[s * (nk + 1) + i], ev[s * (nk + 1) + i + 1]) for s in range(steps)]
            for i, n in enumerate(KERNELS)}
     hip.destroy(ev)
-    return wall, per
+    return wall, idle_wall, settled, per
 
 
 def _blocker_cycles(target_ms: float = 5.0) -> int:
@@ -1146,6 +1179,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps for this long before the warmup, so that the timed "
+                         "steps run at the clocks the GPU holds under sustained load")
     ap.add_argument("--T", type=int, default=8192, help="tokens per step")
     ap.add_argument("--cpu-sample", type=int, default=8192,
                     help="tokens per kernel for the oracle baseline (0 = skip)")
@@ -1216,7 +1252,7 @@ def main() -> int:
     log(f"device: {torch.cuda.get_device_name(0)}; T={T}; steps={args.steps}; "
         f"warmup={args.warmup}")
     launch = make_launchers(T)
-    wall, per = run_steps(launch, args.steps, args.warmup)
+    wall, idle_wall, settled, per = run_steps(launch, args.steps, args.warmup, args.settle_ms)
 
     kern = {}
     for n in KERNELS:
@@ -1251,6 +1287,9 @@ def main() -> int:
                              f"(1536 FP8 group-128 / 512 bf16)",
                     T=T, io="bf16 in; e4m3fn codes + fp32 scales / bf16 out; fp32 arithmetic",
                     step_bytes=step_bytes),
+        settle=dict(ms=args.settle_ms, steps=settled,
+                    from_idle_ms_per_step=round(idle_wall / args.steps * 1e3, 4),
+                    from_idle_value=round(step_bytes / (idle_wall / args.steps) / 1e9, 1)),
         kernels=kern, roofline=roofline, env=environment(),
         target=dict(frac_of_peak=TARGET_FRAC,
                     met=[n for n in KERNELS if kern[n]["meets_target"]],
