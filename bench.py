@@ -961,8 +961,9 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=N
              "Produced by (from the repository root, after `cd /tmp && export TMPDIR=/tmp` for "
              "the profiler):", "", "```", command, "```", "",
              "Durations are the profiler's kernel times of every launch of each kernel at "
-             f"T={T} in the traced run (the step, and for the MLA norm also the one-launch side "
-             "of the bench's two-launch comparison; launches told apart by grid size). "
+             f"T={T} in the traced run (the step's passes: from idle, the settle steps, the timed "
+             "steps and the event-timed steps; for the MLA norm also the one-launch side of the "
+             "bench's two-launch comparison; launches told apart by grid size). "
              "GB/s = algorithmic bytes per launch / average.", "",
              "| kernel | symbol | calls | avg us | min us | max us | p10 / median / p90 us | "
              "algorithmic bytes | GB/s (avg) | % of 8 TB/s |"
