@@ -119,6 +119,30 @@ MUTANTS = [
     ("MLA RoPE: k_pe pairing flipped",
      "rotate_head(k_pe + t * k_pe_stride, dst + kv_lora, c, s, rope_dim, rope_dim, is_neox,",
      "rotate_head(k_pe + t * k_pe_stride, dst + kv_lora, c, s, rope_dim, rope_dim, !is_neox,"),
+    # codecs and element types
+    ("E4M3 ties away from zero", "    k = (lo % 2 == 0) ? lo : hi;", "    k = hi;"),
+    ("E4M3 overflows to NaN above 464", "  if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);",
+     "  if (a > 464.0) return (uint8_t)(sign | 0x7Fu);\n"
+     "  if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);"),
+    ("E4M3 subnormal step 2^-10", "    mag = ldexp((double)m, -9);",
+     "    mag = ldexp((double)m, -10);"),
+    ("bf16 rounding truncates", "  const double n = nearbyint(a / quantum);",
+     "  const double n = floor(a / quantum);"),
+    ("fp16 rounding truncates",
+     "  const double r = nearbyint(a / ldexp(1.0, E - 10)) * ldexp(1.0, E - 10);",
+     "  const double r = floor(a / ldexp(1.0, E - 10)) * ldexp(1.0, E - 10);"),
+    ("fp16 subnormal binade clamped at -15", "  if (E < -14) E = -14;",
+     "  if (E < -15) E = -15;"),
+    ("fp16 exponent bias 14", "    mag = ldexp(1.0 + (double)f / 1024.0, e - 15);",
+     "    mag = ldexp(1.0 + (double)f / 1024.0, e - 14);"),
+    ("fp16 elements read as bf16",
+     "  return dtype == ORC_DT_F16 ? orc_f16_decode(h) : orc_bf16_decode(h);",
+     "  return orc_bf16_decode(h);"),
+    # quantization and RoPE, further slips
+    ("quantize multiplies by the scale", "orc_e4m3fn_encode(y / (double)s)",
+     "orc_e4m3fn_encode(y * (double)s)"),
+    ("RoPE tail zeroed past rot_dim", "  for (int d = rot_dim; d < D; ++d) out[d] = keep[d];",
+     "  for (int d = rot_dim; d < D; ++d) out[d] = 0;"),
 ]
 
 
