@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # (the unfused compositions and the other ops follow it in the file).  The
 # entries of BOTH_MUTANTS replace every occurrence, so that the fused and the
 # unfused function carry the same mistake and the fused == unfused pins cannot
-# see it.
+# see it; an entry whose text and replacement are tuples plants each pair.
 MUTANTS = [
     # residual add + RMSNorm + FP8 quant
     ("eps outside the root", "1.0 / sqrt(ss / (double)H + (double)eps)",
@@ -153,9 +153,13 @@ BOTH_MUTANTS = [
     ("MLA, fused and unfused: kv uses the q weight",
      "norm_emit_row(kv + t * kv_stride, kv_w, eps_kv,",
      "norm_emit_row(kv + t * kv_stride, q_w, eps_kv,"),
+    # The unfused form normalizes a quantized q through the residual-add norm's
+    # function, so the mistake is planted at that call too.
     ("MLA, fused and unfused: q uses the kv epsilon",
-     "norm_emit_row(q + t * q_stride, q_w, eps_q, Hq,",
-     "norm_emit_row(q + t * q_stride, q_w, eps_kv, Hq,"),
+     ("norm_emit_row(q + t * q_stride, q_w, eps_q, Hq,",
+      "orc_fused_add_rmsnorm_quant(q, q_stride, NULL, 0, q_w, eps_q, q_quant_mode"),
+     ("norm_emit_row(q + t * q_stride, q_w, eps_kv, Hq,",
+      "orc_fused_add_rmsnorm_quant(q, q_stride, NULL, 0, q_w, eps_kv, q_quant_mode")),
 ]
 ALL = [(n, o, r, False) for n, o, r in MUTANTS] + [(n, o, r, True) for n, o, r in BOTH_MUTANTS]
 
@@ -183,10 +187,12 @@ def run_one(i: int) -> tuple:
         _copy_tree(d)
         src = os.path.join(d, "oracle", "rra_oracle.c")
         text = open(src, encoding="utf-8").read()
-        n = text.count(old)
-        if n == 0:
-            return i, name, "text not found (not applied)"
-        open(src, "w", encoding="utf-8").write(text.replace(old, new, -1 if every else 1))
+        pairs = zip(old, new) if isinstance(old, tuple) else [(old, new)]
+        for o, r in pairs:
+            if o not in text:
+                return i, name, "text not found (not applied)"
+            text = text.replace(o, r, -1 if every else 1)
+        open(src, "w", encoding="utf-8").write(text)
         r = subprocess.run([sys.executable, "-c", "import oracle; oracle.build()"], cwd=d,
                            capture_output=True, text=True)
         if r.returncode:
