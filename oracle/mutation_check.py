@@ -153,6 +153,19 @@ BOTH_MUTANTS = [
     ("MLA, fused and unfused: kv uses the q weight",
      "norm_emit_row(kv + t * kv_stride, kv_w, eps_kv,",
      "norm_emit_row(kv + t * kv_stride, q_w, eps_kv,"),
+    ("residual-add norm, fused and unfused: norm input is the unrounded sum",
+     ("        const uint16_t zb = orc_bf16_encode(xv + orc_bf16_decode(residual[t * res_stride + j]));\n"
+      "        residual[t * res_stride + j] = zb;\n"
+      "        z[j] = orc_bf16_decode(zb);",
+      "        const uint16_t zb = orc_bf16_encode(v + orc_bf16_decode(residual[t * res_stride + j]));\n"
+      "        residual[t * res_stride + j] = zb;\n"
+      "        v = orc_bf16_decode(zb);"),
+     ("        const double ex = xv + orc_bf16_decode(residual[t * res_stride + j]);\n"
+      "        residual[t * res_stride + j] = orc_bf16_encode(ex);\n"
+      "        z[j] = ex;",
+      "        const double ex = v + orc_bf16_decode(residual[t * res_stride + j]);\n"
+      "        residual[t * res_stride + j] = orc_bf16_encode(ex);\n"
+      "        v = ex;")),
     # The unfused form normalizes a quantized q through the residual-add norm's
     # function, so the mistake is planted at that call too.
     ("MLA, fused and unfused: q uses the kv epsilon",

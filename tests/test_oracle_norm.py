@@ -81,6 +81,30 @@ def test_residual_sum_matches_torch(oracle):
     assert np.array_equal(r_out, ref)
 
 
+def test_norm_reads_the_rounded_sum(oracle):
+    """The residual is updated in place and the norm normalizes that updated
+    residual ([FUSION] section "RMSNorm + Quantization"): its input is
+    z = bf16(x + r), not the exact sum.  So every row must give exactly the
+    codes and scales of normalizing bf16(x + r), rounded here by torch, passed
+    as x with no residual.  A residual column in three is scaled up so that
+    most sums need rounding.  (The fused == unfused pins cannot see this
+    reading: both compositions share it.)"""
+    d = workloads.norm_inputs(64, 1024, salt=3)
+    d["residual"][:, ::3] = workloads.to_bf16_bits(
+        bf16_to_f64(d["residual"][:, ::3]).astype(np.float32) * np.float32(37.0))
+    tx = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).float()
+    tr = torch.from_numpy(d["residual"].view(np.int16)).view(torch.bfloat16).float()
+    z = (tx + tr).to(torch.bfloat16)  # the float32 sum is exact here; one rounding to bf16
+    assert np.count_nonzero(z.double().numpy() != (tx.double() + tr.double()).numpy()) > 1000
+    z_bits = z.view(torch.int16).numpy().view(np.uint16)
+    for mode, g in ((oracle.Q_PER_TOKEN, 0), (oracle.Q_PER_GROUP, 128)):
+        fused = oracle.fused_add_rmsnorm_quant(d["x"], d["residual"].copy(), d["weight"], 1e-6,
+                                               mode, g)
+        plain = oracle.fused_add_rmsnorm_quant(z_bits, None, d["weight"], 1e-6, mode, g)
+        assert np.array_equal(fused[0], plain[0])
+        assert np.array_equal(fused[1].view(np.uint32), plain[1].view(np.uint32))
+
+
 def test_no_residual_equals_zero_residual(oracle):
     d = workloads.norm_inputs(8, 512)
     zero = np.zeros_like(d["residual"])
