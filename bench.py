@@ -25,7 +25,9 @@ step it reports, each timed alone and cold (rotating buffer sets) next to a
 streaming copy of the same bytes: the next-row kernels ("next_rows"), the
 other quantization modes ("modes": static and per-group-128 norm, static
 SiLU), and the fusion's effect ("fusion": fused against unfused bytes, and the
-MLA norm's two-launch form timed against its one launch).  "target" lists the
+MLA norm's two-launch form timed against its one launch), and the step at
+decode-size token counts launched one by one against replayed from a HIP graph
+("decode").  "target" lists the
 kernels at or below 75% of peak HBM bandwidth; "cpu_baseline" times the
 oracle.  With --sweep it also times each kernel alone at several token counts
 and adds the table under "sweep".
@@ -768,6 +770,66 @@ def dual_two_launch(Ts, launches: int = 60) -> dict:
     return out
 
 
+def decode_steps(Ts, steps: int = 200, per_graph: int = 10) -> dict:
+    """The step's four kernels at decode-size token counts, timed per step two
+    ways: launched one by one through the binding (its host cost included, as
+    an eager serving loop pays it) and replayed from a HIP graph captured over
+    `per_graph` steps (torch.cuda.CUDAGraph; the library allocates nothing and
+    only enqueues, so its calls capture as they are).  After the timed
+    replays, the outputs that each step rewrites from unchanged inputs (SiLU's
+    codes, the key cache, the MLA norm's q codes and scales) are checked
+    against the eager ones.  Returns
+    {T: {eager_us_per_step, graph_us_per_step, outputs_equal}}."""
+    import torch
+
+    rows = {}
+    for T in Ts:
+        launch = make_launchers(T, salt=5)
+
+        def step():
+            for n in KERNELS:
+                launch[n]()
+
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        eager = (time.perf_counter() - t0) / steps
+        # Outputs that every step rewrites from unchanged inputs (the norm's
+        # residual and RoPE's q are updated in place, so theirs move on).
+        io = launch["_io"]
+        outs = [io["silu_mul_quant"]["out"], io["rope_kv_write"]["key_cache"],
+                io["dual_rmsnorm_quant"]["q_out"], io["dual_rmsnorm_quant"]["q_scales"]]
+        eager_out = [o.clone() for o in outs]
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(per_graph):
+                    step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // per_graph)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        replayed = (time.perf_counter() - t0) / (reps * per_graph)
+        same = all(torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+                   for a, b in zip(outs, eager_out))
+        rows[str(T)] = dict(eager_us_per_step=round(eager * 1e6, 2),
+                            graph_us_per_step=round(replayed * 1e6, 2), outputs_equal=same)
+        log(f"decode T={T}: {eager * 1e6:.1f} us per step launched one by one, "
+            f"{replayed * 1e6:.1f} us replayed from a graph (outputs equal: {same})")
+        del graph, launch
+    return rows
+
+
 def fusion_report(kern: dict, T: int, dual: dict) -> dict:
     """Fused against unfused bytes per launch at T, with the unfused form's
     time projected at the fused kernel's own measured bandwidth (the unfused
@@ -1193,6 +1255,9 @@ def main() -> int:
     ap.add_argument("--modes", type=int, default=1,
                     help="1 = also time the other quantization modes alone at T (static and "
                          "per-group-128 norm, static SiLU)")
+    ap.add_argument("--decode", default="1,16,64",
+                    help="token counts at which the step is also timed launched one by one "
+                         "and replayed from a HIP graph (empty = skip)")
     ap.add_argument("--fusion", type=int, default=1,
                     help="1 = also report fused against unfused bytes and time the MLA norm's "
                          "two-launch form against its one launch")
@@ -1309,6 +1374,12 @@ def main() -> int:
                            for r in sweep([T], kernels=MODE_KERNELS)}
     if args.fusion:
         result["fusion"] = fusion_report(kern, T, dual_two_launch(sorted({64, 1024, T})))
+    if args.decode:
+        try:
+            result["decode"] = decode_steps([int(t) for t in args.decode.split(",") if t])
+        except Exception as e:  # a measurement beside the step: record it, keep the line
+            result["decode"] = dict(error=f"{type(e).__name__}: {e}")
+            log(f"decode timing failed: {e}")
     if args.sweep:
         result["sweep"] = sweep([int(t) for t in args.sweep.split(",") if t],
                                 kernels=_sweep_kernels(args))
