@@ -1055,23 +1055,32 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=N
         if k is not None and k in KERNELS:
             per[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
             sym[k] = r["Kernel_Name"].split("(")[0].replace("void ", "")
-    events = {}
+    events, b2b = {}, {}
     if bench_json:
         line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
-        events = {k: v["us"] for k, v in json.loads(line)["kernels"].items()}
+        kern = json.loads(line)["kernels"]
+        events = {k: v["us"] for k, v in kern.items()}
+        b2b = {k: v["back_to_back"]["us"] for k, v in kern.items() if "back_to_back" in v}
 
     lines = [f"# Kernel trace: the four fused kernels at T={T}", "",
              "Produced by (from the repository root, after `cd /tmp && export TMPDIR=/tmp` for "
              "the profiler):", "", "```", command, "```", "",
              "Durations are the profiler's kernel times of every launch of each kernel at "
              f"T={T} in the traced run (the step's passes: from idle, the settle steps, the timed "
-             "steps and the event-timed steps; for the MLA norm also the one-launch side of the "
-             "bench's two-launch comparison; launches told apart by grid size). "
-             "GB/s = algorithmic bytes per launch / average.", "",
+             "steps and the event-timed steps; the back-to-back launches of each kernel alone; "
+             "for the MLA norm also the one-launch side of the bench's two-launch comparison; "
+             "launches told apart by grid size). "
+             "GB/s = algorithmic bytes per launch / average."
+             + (" `bench.py events avg us` is the traced run's own mean of the event pairs "
+                "around each launch of its timed steps" if events else "")
+             + ("; `bench.py back-to-back us` its average over 40 launches of the kernel alone "
+                "between one event pair." if b2b else ("." if events else "")), "",
              "| kernel | symbol | calls | avg us | min us | max us | p10 / median / p90 us | "
              "algorithmic bytes | GB/s (avg) | % of 8 TB/s |"
-             + (" bench.py events avg us |" if events else ""),
-             "|---|---|---|---|---|---|---|---|---|---|" + ("---|" if events else "")]
+             + (" bench.py events avg us |" if events else "")
+             + (" bench.py back-to-back us |" if b2b else ""),
+             "|---|---|---|---|---|---|---|---|---|---|" + ("---|" if events else "")
+             + ("---|" if b2b else "")]
     for k in KERNELS:
         d = per.get(k)
         if not d:
@@ -1083,7 +1092,8 @@ def summarize_trace(stats_csv: str, out: str, command: str, T: int, bench_json=N
         lines.append(f"| {k} | `{sym[k]}` | {len(d)} | {avg / 1e3:.2f} | {min(d) / 1e3:.2f} | "
                      f"{max(d) / 1e3:.2f} | {q[0] / 1e3:.2f} / {statistics.median(d) / 1e3:.2f} / "
                      f"{q[-1] / 1e3:.2f} | {b} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f}% |"
-                     + (f" {events[k]:.2f} |" if events else ""))
+                     + (f" {events[k]:.2f} |" if events else "")
+                     + (f" {b2b[k]:.2f} |" if b2b else ""))
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
