@@ -61,3 +61,46 @@ def test_launch_shapes_match_the_library():
     assert bench._norm_shape(T, 4096) == (1, 8)
     assert bench._norm_shape(T + 1, 4096) == (2, 4)
     assert bench._norm_shape(T + 1, 1024) == (2, 1)
+
+
+def test_trace_summary_columns(tmp_path):
+    """summarize_trace: the profiler's average per kernel from the per-dispatch
+    trace, with the traced run's own event-timed and back-to-back figures
+    beside it (read from the run's JSON line)."""
+    import csv
+    import json
+
+    import bench
+
+    T = 8192
+    symbols = {
+        "fused_add_rmsnorm_quant": "void rra::add_rmsnorm_quant_kernel<2, 4, true, 2, 0, true>(x)",
+        "silu_mul_quant": "void rra::silu_mul_quant_kernel<3, 128, true>(x)",
+        "rope_kv_write": "void rra::rope_kv_write_kernel<128, true, 1, rra::ElemBf16>(x)",
+        "dual_rmsnorm_quant": "void rra::dual_rmsnorm_quant_kernel<3, 1, 3, 128, true>(x)",
+    }
+    durations_ns = {k: [10_000 * (i + 1), 10_000 * (i + 1) + 2_000]
+                    for i, k in enumerate(bench.KERNELS)}
+    trace = tmp_path / "t_kernel_trace.csv"
+    with open(trace, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"])
+        for k in bench.KERNELS:
+            for d in durations_ns[k]:
+                w.writerow([symbols[k], bench.grid_threads(k, T), 1000, 1000 + d])
+            # a launch of the same kernel at another T is left out
+            w.writerow([symbols[k], bench.grid_threads(k, 64), 0, 999_999])
+    kern = {k: dict(us=1.5 + i, back_to_back=dict(us=0.5 + i)) for i, k in enumerate(bench.KERNELS)}
+    js = tmp_path / "bench.json"
+    js.write_text("log line\n" + json.dumps(dict(kernels=kern)) + "\n")
+    out = tmp_path / "summary.md"
+    bench.summarize_trace(str(tmp_path / "t_kernel_stats.csv"), str(out), "cmd", T, str(js))
+    text = out.read_text()
+    assert "bench.py events avg us | bench.py back-to-back us |" in text
+    for i, k in enumerate(bench.KERNELS):
+        row = [ln for ln in text.splitlines() if ln.startswith(f"| {k} |")]
+        assert len(row) == 1, (k, text)
+        cells = [c.strip() for c in row[0].strip("|").split("|")]
+        assert cells[2] == "2"  # calls: the launch at T = 64 is not counted
+        assert float(cells[3]) == (10_000 * (i + 1) + 1_000) / 1e3  # average us
+        assert float(cells[-2]) == 1.5 + i and float(cells[-1]) == 0.5 + i
